@@ -1,0 +1,32 @@
+// Host-side launchers shared between translation units of libgsmi (not part of the ABI).
+#pragma once
+
+#include "common.h"
+
+namespace gsi {
+
+gs_status check_gaussians(const gs_gaussians *g);
+
+// Backward through projection and colour evaluation (defined in project.hip).
+gs_status launch_project_bwd(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                             const float *grads2d, gs_param_grads *out, hipStream_t stream);
+
+// Device-wide exclusive scan of m uint32 values (in place allowed).  If total != NULL
+// the 64-bit sum is written there.  partials: scan_partials_len(m) uint32.
+int64_t scan_partials_len(int64_t m);
+gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint32_t *partials,
+                             unsigned long long *total, hipStream_t stream);
+
+// Stable LSD radix sort of (key, value) uint32 pairs on the low `bits` bits of the key,
+// 8 bits per pass, ping-ponging between (ka, va) and (kb, vb).  Returns in *in_b whether
+// the sorted result ended in (kb, vb).  hist: radix_hist_len(m) uint32,
+// partials: scan_partials_len(radix_hist_len(m)) uint32.
+int64_t radix_hist_len(int64_t m);
+gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
+                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream);
+
+// Fills n int32 values with `value` (a kernel, not a memset, so it may be captured in graphs).
+gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream);
+gs_status fill_f32(float *p, int64_t n, float value, hipStream_t stream);
+
+}  // namespace gsi

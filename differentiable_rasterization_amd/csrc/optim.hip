@@ -1,0 +1,188 @@
+// L1 loss and Adam.
+//
+// Loss: the L1 term of the objective (ByteSplat, section 2.1, Eq. 2; "Scaling 3D
+// Gaussian Splatting with Distributed Compute", loss of section "Why gsplat Cannot
+// Just Use DDP"), as the mean over all colour values, and its gradient.
+// Adam: textbook bias-corrected Adam with the settings of that page's
+// create_splats_with_optimizers excerpt at batch size 1 (eps 1e-15, betas 0.9 / 0.999).
+// Both kernels are pure HBM streams: float4 loads and stores, grid-stride loops.
+#include <cmath>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_loss_l1(const float *__restrict__ c, const float *__restrict__ t,
+                                                      int64_t m, float inv, float *__restrict__ grad,
+                                                      double *__restrict__ partials)
+{
+    __shared__ double red[kThreads / 64];
+    double acc = 0.0;
+    const int64_t m4 = m / 4;
+    const float4 *c4 = reinterpret_cast<const float4 *>(c);
+    const float4 *t4 = reinterpret_cast<const float4 *>(t);
+    float4 *g4 = reinterpret_cast<float4 *>(grad);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    auto sgn = [](float d) { return d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f); };
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < m4; i += stride) {
+        const float4 a = c4[i], b = t4[i];
+        const float d0 = a.x - b.x, d1 = a.y - b.y, d2 = a.z - b.z, d3 = a.w - b.w;
+        acc += (double)(fabsf(d0) + fabsf(d1)) + (double)(fabsf(d2) + fabsf(d3));
+        g4[i] = make_float4(sgn(d0) * inv, sgn(d1) * inv, sgn(d2) * inv, sgn(d3) * inv);
+    }
+    for (int64_t i = 4 * m4 + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < m; i += stride) {
+        const float d = c[i] - t[i];
+        acc += (double)fabsf(d);
+        grad[i] = sgn(d) * inv;
+    }
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_down(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(kThreads) void k_loss_final(const double *__restrict__ partials, int nb, double inv,
+                                                         float *__restrict__ loss)
+{
+    __shared__ double red[kThreads / 64];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < nb; i += kThreads) acc += partials[i];
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_down(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) *loss = (float)((red[0] + red[1] + red[2] + red[3]) * inv);
+}
+
+constexpr int kMaxGroups = 16;
+
+struct AdamArgs {
+    float *p[kMaxGroups];
+    const float *g[kMaxGroups];
+    float *m[kMaxGroups];
+    float *v[kMaxGroups];
+    int64_t begin[kMaxGroups + 1];   // prefix of group sizes, in float4 units
+    float step[kMaxGroups];          // lr / (1 - b1^t)
+    bool vec[kMaxGroups];            // group is float4-aligned and a multiple of 4 long
+    int64_t n[kMaxGroups];
+    int ng;
+    float b1, b2, inv_bc2, eps;
+};
+
+__device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, float b1, float b2, float inv_bc2,
+                                      float eps, float step)
+{
+    m = fmaf(b1, m, (1.0f - b1) * g);
+    v = fmaf(b2, v, (1.0f - b2) * g * g);
+    p -= step * m / (__fsqrt_rn(v * inv_bc2) + eps);
+}
+
+__global__ __launch_bounds__(kThreads) void k_adam(AdamArgs a)
+{
+    const int64_t total = a.begin[a.ng];
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+        int gi = 0;
+        while (gi + 1 < a.ng && i >= a.begin[gi + 1]) ++gi;
+        const int64_t j = i - a.begin[gi];
+        const float st = a.step[gi];
+        if (a.vec[gi]) {
+            float4 p = reinterpret_cast<float4 *>(a.p[gi])[j];
+            const float4 g = reinterpret_cast<const float4 *>(a.g[gi])[j];
+            float4 m = reinterpret_cast<float4 *>(a.m[gi])[j];
+            float4 v = reinterpret_cast<float4 *>(a.v[gi])[j];
+            adam1(p.x, g.x, m.x, v.x, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            adam1(p.y, g.y, m.y, v.y, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            adam1(p.z, g.z, m.z, v.z, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            adam1(p.w, g.w, m.w, v.w, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            reinterpret_cast<float4 *>(a.p[gi])[j] = p;
+            reinterpret_cast<float4 *>(a.m[gi])[j] = m;
+            reinterpret_cast<float4 *>(a.v[gi])[j] = v;
+        } else {
+            for (int64_t e = 4 * j; e < min(4 * j + 4, a.n[gi]); ++e) {
+                float p = a.p[gi][e], m = a.m[gi][e], v = a.v[gi][e];
+                adam1(p, a.g[gi][e], m, v, a.b1, a.b2, a.inv_bc2, a.eps, st);
+                a.p[gi][e] = p;
+                a.m[gi][e] = m;
+                a.v[gi][e] = v;
+            }
+        }
+    }
+}
+
+int stream_blocks(int64_t work)
+{
+    // enough blocks to fill 256 CUs several times over, grid-stride beyond that
+    const int64_t b = gsi::ceil_div(work, kThreads);
+    return (int)std::min<int64_t>(std::max<int64_t>(b, 1), 256 * 16);
+}
+
+}  // namespace
+
+extern "C" size_t gs_loss_workspace_bytes(int64_t n_px)
+{
+    (void)n_px;
+    return sizeof(double) * 256 * 16;
+}
+
+extern "C" gs_status gs_loss_l1(const float *color, const float *target, int64_t n_px, float *loss_out,
+                                float *dL_dcolor, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    using namespace gsi;
+    if (n_px < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n_px < 0");
+    if (n_px == 0) {
+        if (loss_out) return fill_f32(loss_out, 1, 0.0f, stream);
+        return GS_OK;
+    }
+    if (!color || !target || !dL_dcolor) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!aligned(color, 16) || !aligned(target, 16) || !aligned(dL_dcolor, 16))
+        return fail(GS_ERR_INVALID_ARGUMENT, "color / target / dL_dcolor must be 16-byte aligned");
+    if (!workspace || workspace_bytes < gs_loss_workspace_bytes(n_px) || !aligned(workspace, 8))
+        return fail(GS_ERR_INVALID_ARGUMENT, "workspace too small");
+    const int64_t m = 3 * n_px;
+    const int nb = stream_blocks(m / 4 + 1);
+    double *part = static_cast<double *>(workspace);
+    k_loss_l1<<<nb, kThreads, 0, stream>>>(color, target, m, (float)(1.0 / (double)m), dL_dcolor, part);
+    GS_LAUNCH_CHECK("k_loss_l1");
+    if (loss_out) {
+        k_loss_final<<<1, kThreads, 0, stream>>>(part, nb, 1.0 / (double)m, loss_out);
+        GS_LAUNCH_CHECK("k_loss_final");
+    }
+    return GS_OK;
+}
+
+extern "C" gs_status gs_adam_step(const gs_adam_group *groups, int32_t n_groups, int32_t step, float beta1,
+                                  float beta2, float eps, hipStream_t stream)
+{
+    using namespace gsi;
+    if (n_groups < 0 || n_groups > kMaxGroups) return fail(GS_ERR_INVALID_ARGUMENT, "n_groups must lie in [0, 16]");
+    if (n_groups > 0 && !groups) return fail(GS_ERR_INVALID_ARGUMENT, "groups is NULL");
+    if (step < 1) return fail(GS_ERR_INVALID_ARGUMENT, "step must be >= 1");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f && eps >= 0.0f))
+        return fail(GS_ERR_INVALID_ARGUMENT, "bad Adam hyper-parameters");
+    AdamArgs a = {};
+    a.ng = n_groups;
+    a.b1 = beta1;
+    a.b2 = beta2;
+    a.eps = eps;
+    const double bc1 = 1.0 - std::pow((double)beta1, step), bc2 = 1.0 - std::pow((double)beta2, step);
+    a.inv_bc2 = (float)(1.0 / bc2);
+    int64_t acc = 0;
+    for (int i = 0; i < n_groups; ++i) {
+        const gs_adam_group &gr = groups[i];
+        if (gr.n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "group %d: n < 0", i);
+        if (gr.n > 0 && (!gr.p || !gr.g || !gr.m || !gr.v))
+            return fail(GS_ERR_INVALID_ARGUMENT, "group %d: NULL pointer", i);
+        a.p[i] = gr.p; a.g[i] = gr.g; a.m[i] = gr.m; a.v[i] = gr.v; a.n[i] = gr.n;
+        a.step[i] = (float)((double)gr.lr / bc1);
+        a.vec[i] = gr.n % 4 == 0 && aligned(gr.p, 16) && aligned(gr.g, 16) && aligned(gr.m, 16) && aligned(gr.v, 16);
+        a.begin[i] = acc;
+        acc += ceil_div(gr.n, 4);
+    }
+    a.begin[n_groups] = acc;
+    if (acc == 0) return GS_OK;
+    k_adam<<<stream_blocks(acc), kThreads, 0, stream>>>(a);
+    GS_LAUNCH_CHECK("k_adam");
+    return GS_OK;
+}

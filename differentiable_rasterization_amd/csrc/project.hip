@@ -1,0 +1,470 @@
+// Projection of 3D Gaussians to 2D records with SH colour (forward), and its
+// backward through projection and colour evaluation.
+//
+// Forward, per Gaussian (one thread each, coalesced structure-of-arrays loads):
+//   s = exp(log_s), o = sigmoid(logit), q^ = q / |q|, R = R(q^)
+//   Sigma = M M^T, M = R diag(s)                       (Splaxel, section 2)
+//   p = W mu + t;  u = fx X/Z + cx, v = fy Y/Z + cy     (frustum culling by the mean)
+//   Sigma2D = T Sigma T^T, T = J W, J the pinhole Jacobian at p   (Splaxel, section 2)
+//   conic = Sigma2D^-1; radii from the alpha >= alpha_min ellipse
+//   colour = sum_k sh_k Y_k(v^), v^ the unit vector from the camera centre to mu
+//     ("Scaling 3D Gaussian Splatting with Distributed Compute", walkthrough step 4)
+// The geometric chain runs in double (it is memory bound, so this costs no time on
+// MI355X) and is rounded once to the float32 record.  SH evaluation runs in float.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+struct CamD {
+    double R[9];
+    double t[3];
+    double fx, fy, cx, cy;
+    double campos[3];
+    double near_z;
+    float r20, r21, r22, t2;
+    int W, H;
+};
+
+CamD make_cam(const gs_camera *c)
+{
+    CamD d;
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 3; ++j) d.R[3 * i + j] = c->viewmat[4 * i + j];
+        d.t[i] = c->viewmat[4 * i + 3];
+    }
+    d.fx = c->fx; d.fy = c->fy; d.cx = c->cx; d.cy = c->cy;
+    for (int j = 0; j < 3; ++j)
+        d.campos[j] = -(d.R[0 * 3 + j] * d.t[0] + d.R[1 * 3 + j] * d.t[1] + d.R[2 * 3 + j] * d.t[2]);
+    d.near_z = c->near_z;
+    d.r20 = c->viewmat[8]; d.r21 = c->viewmat[9]; d.r22 = c->viewmat[10]; d.t2 = c->viewmat[11];
+    d.W = c->width; d.H = c->height;
+    return d;
+}
+
+// Real orthonormal SH basis up to degree 3 as Cartesian polynomials on the unit
+// sphere (no Condon-Shortley phase), index k = l*l + l + m.  Normalisations:
+//   l=0: 1/(2 sqrt(pi));  l=1: sqrt(3/(4 pi))
+//   l=2: sqrt(15/pi)/2 (xy, yz, xz), sqrt(5/pi)/4 (3z^2-1), sqrt(15/pi)/4 (x^2-y^2)
+//   l=3: sqrt(35/(2 pi))/4 (y(3x^2-y^2), x(x^2-3y^2)), sqrt(105/pi)/2 (xyz),
+//        sqrt(21/(2 pi))/4 (y(5z^2-1), x(5z^2-1)), sqrt(7/pi)/4 (z(5z^2-3)),
+//        sqrt(105/pi)/4 (z(x^2-y^2))
+constexpr float kSH0 = 0.28209479177387814f;
+constexpr float kSH1 = 0.48860251190291992f;
+constexpr float kSH2a = 1.0925484305920792f;
+constexpr float kSH2b = 0.31539156525252005f;
+constexpr float kSH2c = 0.54627421529603959f;
+constexpr float kSH3a = 0.59004358992664352f;
+constexpr float kSH3b = 2.8906114426405538f;
+constexpr float kSH3c = 0.45704579946446572f;
+constexpr float kSH3d = 0.37317633259011540f;
+constexpr float kSH3e = 1.4453057213202769f;
+
+template <int DEG>
+__device__ __forceinline__ void sh_basis(float x, float y, float z, float *Y)
+{
+    Y[0] = kSH0;
+    if (DEG >= 1) { Y[1] = kSH1 * y; Y[2] = kSH1 * z; Y[3] = kSH1 * x; }
+    if (DEG >= 2) {
+        const float xx = x * x, yy = y * y, zz = z * z;
+        Y[4] = kSH2a * x * y; Y[5] = kSH2a * y * z; Y[6] = kSH2b * (3.0f * zz - 1.0f);
+        Y[7] = kSH2a * x * z; Y[8] = kSH2c * (xx - yy);
+        if (DEG >= 3) {
+            Y[9] = kSH3a * y * (3.0f * xx - yy);
+            Y[10] = kSH3b * x * y * z;
+            Y[11] = kSH3c * y * (5.0f * zz - 1.0f);
+            Y[12] = kSH3d * z * (5.0f * zz - 3.0f);
+            Y[13] = kSH3c * x * (5.0f * zz - 1.0f);
+            Y[14] = kSH3e * z * (xx - yy);
+            Y[15] = kSH3a * x * (xx - 3.0f * yy);
+        }
+    }
+}
+
+// Gradient of sum_k w_k Y_k(x, y, z) with respect to (x, y, z) (polynomial extension;
+// its tangential part is the derivative on the sphere).
+template <int DEG>
+__device__ __forceinline__ void sh_grad(float x, float y, float z, const float *w, float &gx, float &gy, float &gz)
+{
+    gx = gy = gz = 0.0f;
+    if (DEG >= 1) { gy += kSH1 * w[1]; gz += kSH1 * w[2]; gx += kSH1 * w[3]; }
+    if (DEG >= 2) {
+        gx += kSH2a * (y * w[4] + z * w[7]) + 2.0f * kSH2c * x * w[8];
+        gy += kSH2a * (x * w[4] + z * w[5]) - 2.0f * kSH2c * y * w[8];
+        gz += kSH2a * (y * w[5] + x * w[7]) + 6.0f * kSH2b * z * w[6];
+        if (DEG >= 3) {
+            const float xx = x * x, yy = y * y, zz = z * z;
+            gx += kSH3a * 6.0f * x * y * w[9] + kSH3b * y * z * w[10] + kSH3c * (5.0f * zz - 1.0f) * w[13]
+                + kSH3e * 2.0f * x * z * w[14] + kSH3a * 3.0f * (xx - yy) * w[15];
+            gy += kSH3a * 3.0f * (xx - yy) * w[9] + kSH3b * x * z * w[10] + kSH3c * (5.0f * zz - 1.0f) * w[11]
+                - kSH3e * 2.0f * y * z * w[14] - kSH3a * 6.0f * x * y * w[15];
+            gz += kSH3b * x * y * w[10] + kSH3c * 10.0f * y * z * w[11] + kSH3d * (15.0f * zz - 3.0f) * w[12]
+                + kSH3c * 10.0f * x * z * w[13] + kSH3e * (xx - yy) * w[14];
+        }
+    }
+}
+
+// Everything the forward computes for one Gaussian, kept for the backward.
+struct Proj {
+    bool vis;
+    float key;
+    double mu[3], s[3], q[4], qnorm, o;
+    double Rq[9];        // rotation of q^
+    double M[9];         // Rq diag(s)
+    double Sig[6];       // xx, xy, xz, yy, yz, zz
+    double X, Y, Z, u, v;
+    double T[6];         // J W, 2x3
+    double a, b, c, det, A, B, C;
+    double dist;
+    float dir[3];        // unit view direction
+    int rx, ry;
+};
+
+__device__ __forceinline__ bool finite_d(double x) { return __builtin_isfinite(x); }
+
+__device__ __forceinline__ void project_core(const CamD &cam, double mx, double my, double mz, float fmx,
+                                             float fmy, float fmz, double l0, double l1, double l2, double q0,
+                                             double q1, double q2, double q3, double logit, bool sh_finite,
+                                             double alpha_min, float depth_lo, float depth_hi, Proj &P)
+{
+    P.vis = false;
+    P.rx = P.ry = 0;
+    // camera-space depth as the float32 key: each step rounded explicitly
+    P.key = __fadd_rn(__fmaf_rn(cam.r22, fmz, __fmaf_rn(cam.r21, fmy, __fmul_rn(cam.r20, fmx))), cam.t2);
+    if (!(finite_d(mx) && finite_d(my) && finite_d(mz) && finite_d(l0) && finite_d(l1) && finite_d(l2) &&
+          finite_d(q0) && finite_d(q1) && finite_d(q2) && finite_d(q3) && finite_d(logit) && sh_finite))
+        return;
+    P.qnorm = sqrt(q0 * q0 + q1 * q1 + q2 * q2 + q3 * q3);
+    if (!(P.qnorm > 0.0)) return;
+    if (!(P.key >= depth_lo && P.key < depth_hi)) return;
+    P.mu[0] = mx; P.mu[1] = my; P.mu[2] = mz;
+    P.X = cam.R[0] * mx + cam.R[1] * my + cam.R[2] * mz + cam.t[0];
+    P.Y = cam.R[3] * mx + cam.R[4] * my + cam.R[5] * mz + cam.t[1];
+    P.Z = cam.R[6] * mx + cam.R[7] * my + cam.R[8] * mz + cam.t[2];
+    if (!(P.Z > cam.near_z)) return;
+    P.u = cam.fx * P.X / P.Z + cam.cx;
+    P.v = cam.fy * P.Y / P.Z + cam.cy;
+    if (!(P.u >= 0.0 && P.u < (double)cam.W && P.v >= 0.0 && P.v < (double)cam.H)) return;
+
+    const double iq = 1.0 / P.qnorm;
+    const double w = q0 * iq, x = q1 * iq, y = q2 * iq, z = q3 * iq;
+    P.q[0] = w; P.q[1] = x; P.q[2] = y; P.q[3] = z;
+    double *R = P.Rq;
+    R[0] = 1.0 - 2.0 * (y * y + z * z); R[1] = 2.0 * (x * y - w * z);       R[2] = 2.0 * (x * z + w * y);
+    R[3] = 2.0 * (x * y + w * z);       R[4] = 1.0 - 2.0 * (x * x + z * z); R[5] = 2.0 * (y * z - w * x);
+    R[6] = 2.0 * (x * z - w * y);       R[7] = 2.0 * (y * z + w * x);       R[8] = 1.0 - 2.0 * (x * x + y * y);
+    P.s[0] = exp(l0); P.s[1] = exp(l1); P.s[2] = exp(l2);
+    for (int r = 0; r < 3; ++r)
+        for (int c = 0; c < 3; ++c) P.M[3 * r + c] = R[3 * r + c] * P.s[c];
+    const double *M = P.M;
+    P.Sig[0] = M[0] * M[0] + M[1] * M[1] + M[2] * M[2];
+    P.Sig[1] = M[0] * M[3] + M[1] * M[4] + M[2] * M[5];
+    P.Sig[2] = M[0] * M[6] + M[1] * M[7] + M[2] * M[8];
+    P.Sig[3] = M[3] * M[3] + M[4] * M[4] + M[5] * M[5];
+    P.Sig[4] = M[3] * M[6] + M[4] * M[7] + M[5] * M[8];
+    P.Sig[5] = M[6] * M[6] + M[7] * M[7] + M[8] * M[8];
+
+    const double iz = 1.0 / P.Z;
+    const double j00 = cam.fx * iz, j02 = -cam.fx * P.X * iz * iz;
+    const double j11 = cam.fy * iz, j12 = -cam.fy * P.Y * iz * iz;
+    double *T = P.T;
+    for (int c = 0; c < 3; ++c) {
+        T[c] = j00 * cam.R[c] + j02 * cam.R[6 + c];
+        T[3 + c] = j11 * cam.R[3 + c] + j12 * cam.R[6 + c];
+    }
+    const double *S = P.Sig;
+    // (T Sigma) rows
+    double ts0[3], ts1[3];
+    ts0[0] = T[0] * S[0] + T[1] * S[1] + T[2] * S[2];
+    ts0[1] = T[0] * S[1] + T[1] * S[3] + T[2] * S[4];
+    ts0[2] = T[0] * S[2] + T[1] * S[4] + T[2] * S[5];
+    ts1[0] = T[3] * S[0] + T[4] * S[1] + T[5] * S[2];
+    ts1[1] = T[3] * S[1] + T[4] * S[3] + T[5] * S[4];
+    ts1[2] = T[3] * S[2] + T[4] * S[4] + T[5] * S[5];
+    P.a = ts0[0] * T[0] + ts0[1] * T[1] + ts0[2] * T[2];
+    P.b = ts0[0] * T[3] + ts0[1] * T[4] + ts0[2] * T[5];
+    P.c = ts1[0] * T[3] + ts1[1] * T[4] + ts1[2] * T[5];
+    P.det = P.a * P.c - P.b * P.b;
+    if (!(P.det > 0.0)) return;
+    const double idet = 1.0 / P.det;
+    P.A = P.c * idet; P.B = -P.b * idet; P.C = P.a * idet;
+
+    P.o = 1.0 / (1.0 + exp(-logit));
+    const double o32 = (double)(float)P.o;
+    if (!(o32 >= alpha_min)) return;
+    const double lnr = 2.0 * log(o32 / alpha_min);
+    double ex = ceil(sqrt(lnr * P.a)), ey = ceil(sqrt(lnr * P.c));
+    ex = fmin(fmax(ex, 1.0), (double)GS_RADIUS_CAP);
+    ey = fmin(fmax(ey, 1.0), (double)GS_RADIUS_CAP);
+    P.rx = (int)ex; P.ry = (int)ey;
+
+    const double dx = mx - cam.campos[0], dy = my - cam.campos[1], dz = mz - cam.campos[2];
+    P.dist = sqrt(dx * dx + dy * dy + dz * dz);
+    const double id = 1.0 / P.dist;
+    P.dir[0] = (float)(dx * id); P.dir[1] = (float)(dy * id); P.dir[2] = (float)(dz * id);
+    P.vis = true;
+}
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project(const float *__restrict__ means, const float *__restrict__ log_scales,
+                                                 const float *__restrict__ quats, const float *__restrict__ logits,
+                                                 const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+                                                 float depth_lo, float depth_hi, float2 *__restrict__ means2d,
+                                                 float4 *__restrict__ conic_o, float *__restrict__ color,
+                                                 float *__restrict__ depth, int2 *__restrict__ radii)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float fmx = means[i], fmy = means[n + i], fmz = means[2 * n + i];
+    float shc[3 * K];
+    bool shf = true;
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) {
+        shc[k] = sh[(int64_t)k * n + i];
+        shf = shf && __builtin_isfinite(shc[k]);
+    }
+    Proj P;
+    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, log_scales[i], log_scales[n + i], log_scales[2 * n + i],
+                 quats[i], quats[n + i], quats[2 * n + i], quats[3 * n + i], logits[i], shf, (double)alpha_min,
+                 depth_lo, depth_hi, P);
+    depth[i] = P.key;
+    radii[i] = make_int2(P.rx, P.ry);
+    if (!P.vis) return;
+    means2d[i] = make_float2((float)P.u, (float)P.v);
+    conic_o[i] = make_float4((float)P.A, (float)P.B, (float)P.C, (float)P.o);
+    float Y[K];
+    sh_basis<DEG>(P.dir[0], P.dir[1], P.dir[2], Y);
+    float r = 0.0f, g = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        r = fmaf(shc[3 * k + 0], Y[k], r);
+        g = fmaf(shc[3 * k + 1], Y[k], g);
+        b = fmaf(shc[3 * k + 2], Y[k], b);
+    }
+    color[3 * i + 0] = r;
+    color[3 * i + 1] = g;
+    color[3 * i + 2] = b;
+}
+
+// Backward through projection and colour evaluation (ByteSplat, section 2.1: the
+// aggregated screen-space gradients are propagated through projection and colour
+// evaluation to the 3D parameters).  Exact chain rule of project_core; the float
+// rounding of the record is treated as the identity.
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project_bwd(
+    const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+    float depth_lo, float depth_hi, const float *__restrict__ g2, float *__restrict__ d_means,
+    float *__restrict__ d_ls, float *__restrict__ d_q, float *__restrict__ d_logit, float *__restrict__ d_sh)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float fmx = means[i], fmy = means[n + i], fmz = means[2 * n + i];
+    float shc[3 * K];
+    bool shf = true;
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) {
+        shc[k] = sh[(int64_t)k * n + i];
+        shf = shf && __builtin_isfinite(shc[k]);
+    }
+    Proj P;
+    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, log_scales[i], log_scales[n + i], log_scales[2 * n + i],
+                 quats[i], quats[n + i], quats[2 * n + i], quats[3 * n + i], logits[i], shf, (double)alpha_min,
+                 depth_lo, depth_hi, P);
+    if (!P.vis) {
+        for (int j = 0; j < 3; ++j) { d_means[j * n + i] = 0.0f; d_ls[j * n + i] = 0.0f; }
+        for (int j = 0; j < 4; ++j) d_q[j * n + i] = 0.0f;
+        d_logit[i] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 3 * K; ++k) d_sh[(int64_t)k * n + i] = 0.0f;
+        return;
+    }
+    const double gu = g2[i], gv = g2[n + i], gA = g2[2 * n + i], gB = g2[3 * n + i], gC = g2[4 * n + i];
+    const double go = g2[5 * n + i];
+    const float gc[3] = {g2[6 * n + i], g2[7 * n + i], g2[8 * n + i]};
+
+    // conic = Sigma2D^-1:  G_S2 = -Q G_Q Q with G_Q = [[gA, gB/2], [gB/2, gC]]
+    const double A = P.A, B = P.B, C = P.C;
+    const double hb = 0.5 * gB;
+    const double p00 = A * gA + B * hb, p01 = A * hb + B * gC;
+    const double p10 = B * gA + C * hb, p11 = B * hb + C * gC;
+    const double s00 = -(p00 * A + p01 * B);
+    const double s01 = -(p00 * B + p01 * C);
+    const double s11 = -(p10 * B + p11 * C);
+
+    // Sigma2D = T Sigma T^T:  G_T = 2 G_S2 T Sigma,  G_Sigma = T^T G_S2 T
+    const double *T = P.T, *S = P.Sig;
+    double ts[6];
+    for (int r = 0; r < 2; ++r) {
+        const double *t = T + 3 * r;
+        ts[3 * r + 0] = t[0] * S[0] + t[1] * S[1] + t[2] * S[2];
+        ts[3 * r + 1] = t[0] * S[1] + t[1] * S[3] + t[2] * S[4];
+        ts[3 * r + 2] = t[0] * S[2] + t[1] * S[4] + t[2] * S[5];
+    }
+    double GT[6];
+    for (int c = 0; c < 3; ++c) {
+        GT[c] = 2.0 * (s00 * ts[c] + s01 * ts[3 + c]);
+        GT[3 + c] = 2.0 * (s01 * ts[c] + s11 * ts[3 + c]);
+    }
+    double gsT[6];   // G_S2 T
+    for (int c = 0; c < 3; ++c) {
+        gsT[c] = s00 * T[c] + s01 * T[3 + c];
+        gsT[3 + c] = s01 * T[c] + s11 * T[3 + c];
+    }
+    double GS[9];
+    for (int r = 0; r < 3; ++r)
+        for (int c = 0; c < 3; ++c) GS[3 * r + c] = T[r] * gsT[c] + T[3 + r] * gsT[3 + c];
+
+    // T = J W:  G_J = G_T W^T; only J00, J02, J11, J12 are non-zero
+    const double *W = cam.R;
+    const double gj00 = GT[0] * W[0] + GT[1] * W[1] + GT[2] * W[2];
+    const double gj02 = GT[0] * W[6] + GT[1] * W[7] + GT[2] * W[8];
+    const double gj11 = GT[3] * W[3] + GT[4] * W[4] + GT[5] * W[5];
+    const double gj12 = GT[3] * W[6] + GT[4] * W[7] + GT[5] * W[8];
+    const double iz = 1.0 / P.Z, iz2 = iz * iz, iz3 = iz2 * iz;
+    const double fx = cam.fx, fy = cam.fy, X = P.X, Yc = P.Y;
+    const double dX = -gj02 * fx * iz2 + gu * fx * iz;
+    const double dY = -gj12 * fy * iz2 + gv * fy * iz;
+    const double dZ = -gj00 * fx * iz2 + gj02 * 2.0 * fx * X * iz3 - gj11 * fy * iz2 + gj12 * 2.0 * fy * Yc * iz3
+                    - gu * fx * X * iz2 - gv * fy * Yc * iz2;
+    double dmu[3];
+    for (int j = 0; j < 3; ++j) dmu[j] = W[j] * dX + W[3 + j] * dY + W[6 + j] * dZ;
+
+    // Sigma = M M^T: G_M = 2 G_Sigma M;  M = R diag(s)
+    const double *M = P.M, *R = P.Rq;
+    double GR[9];
+    for (int k = 0; k < 3; ++k) {
+        double ds = 0.0;
+        for (int r = 0; r < 3; ++r) {
+            const double gm = 2.0 * (GS[3 * r + 0] * M[k] + GS[3 * r + 1] * M[3 + k] + GS[3 * r + 2] * M[6 + k]);
+            ds += gm * R[3 * r + k];
+            GR[3 * r + k] = gm * P.s[k];
+        }
+        d_ls[k * n + i] = (float)(ds * P.s[k]);
+    }
+    // R(q^) -> q^ -> q
+    const double w = P.q[0], x = P.q[1], y = P.q[2], z = P.q[3];
+    double dq[4];
+    dq[0] = 2.0 * (-z * GR[1] + y * GR[2] + z * GR[3] - x * GR[5] - y * GR[6] + x * GR[7]);
+    dq[1] = 2.0 * (y * GR[1] + z * GR[2] + y * GR[3] - 2.0 * x * GR[4] - w * GR[5] + z * GR[6] + w * GR[7]
+                   - 2.0 * x * GR[8]);
+    dq[2] = 2.0 * (-2.0 * y * GR[0] + x * GR[1] + w * GR[2] + x * GR[3] + z * GR[5] - w * GR[6] + z * GR[7]
+                   - 2.0 * y * GR[8]);
+    dq[3] = 2.0 * (-2.0 * z * GR[0] - w * GR[1] + x * GR[2] + w * GR[3] - 2.0 * z * GR[4] + y * GR[5] + x * GR[6]
+                   + y * GR[7]);
+    const double qd = w * dq[0] + x * dq[1] + y * dq[2] + z * dq[3];
+    const double iq = 1.0 / P.qnorm;
+    for (int j = 0; j < 4; ++j) d_q[j * n + i] = (float)((dq[j] - P.q[j] * qd) * iq);
+
+    d_logit[i] = (float)(go * P.o * (1.0 - P.o));
+
+    // colour: d sh_k = Y_k dc;  d v^ = sum_k (sh_k . dc) grad Y_k
+    float Y[K], wk[K];
+    sh_basis<DEG>(P.dir[0], P.dir[1], P.dir[2], Y);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        d_sh[(int64_t)(3 * k + 0) * n + i] = Y[k] * gc[0];
+        d_sh[(int64_t)(3 * k + 1) * n + i] = Y[k] * gc[1];
+        d_sh[(int64_t)(3 * k + 2) * n + i] = Y[k] * gc[2];
+        wk[k] = shc[3 * k] * gc[0] + shc[3 * k + 1] * gc[1] + shc[3 * k + 2] * gc[2];
+    }
+    float gx, gy, gz;
+    sh_grad<DEG>(P.dir[0], P.dir[1], P.dir[2], wk, gx, gy, gz);
+    const double vd = (double)P.dir[0] * gx + (double)P.dir[1] * gy + (double)P.dir[2] * gz;
+    const double idist = 1.0 / P.dist;
+    dmu[0] += (gx - P.dir[0] * vd) * idist;
+    dmu[1] += (gy - P.dir[1] * vd) * idist;
+    dmu[2] += (gz - P.dir[2] * vd) * idist;
+    for (int j = 0; j < 3; ++j) d_means[j * n + i] = (float)dmu[j];
+}
+
+}  // namespace
+
+namespace gsi {
+
+gs_status check_gaussians(const gs_gaussians *g)
+{
+    if (!g) return fail(GS_ERR_INVALID_ARGUMENT, "gaussians is NULL");
+    if (g->n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
+    if (g->n > (int64_t(1) << 31) - 1) return fail(GS_ERR_UNSUPPORTED, "n >= 2^31");
+    if (g->n > 0 && (!g->means || !g->log_scales || !g->quats || !g->opacity_logits || !g->sh))
+        return fail(GS_ERR_INVALID_ARGUMENT, "a parameter pointer is NULL");
+    return GS_OK;
+}
+
+gs_status launch_project_bwd(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                             const float *grads2d, gs_param_grads *out, hipStream_t stream)
+{
+    const int64_t n = g->n;
+    if (n == 0) return GS_OK;
+    if (!out->means || !out->log_scales || !out->quats || !out->opacity_logits || !out->sh)
+        return fail(GS_ERR_INVALID_ARGUMENT, "a grads3d pointer is NULL");
+    const CamD cd = make_cam(cam);
+    const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+#define GS_PB(D)                                                                                              \
+    k_project_bwd<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, \
+                                                 n, cd, p->alpha_min, p->depth_lo, p->depth_hi, grads2d,      \
+                                                 out->means, out->log_scales, out->quats, out->opacity_logits, \
+                                                 out->sh)
+    switch (p->sh_degree) {
+    case 0: GS_PB(0); break;
+    case 1: GS_PB(1); break;
+    case 2: GS_PB(2); break;
+    default: GS_PB(3); break;
+    }
+#undef GS_PB
+    GS_LAUNCH_CHECK("k_project_bwd");
+    return GS_OK;
+}
+
+}  // namespace gsi
+
+extern "C" gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                                gs_projected *out, hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if ((s = check_gaussians(g)) != GS_OK) return s;
+    if ((s = check_camera(cam)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "out is NULL");
+    const int64_t n = g->n;
+    if (n == 0) return GS_OK;
+    if (!out->means2d || !out->conic_opacity || !out->color || !out->depth || !out->radii)
+        return fail(GS_ERR_INVALID_ARGUMENT, "a projected-record pointer is NULL");
+    if (!aligned(out->conic_opacity, 16) || !aligned(out->means2d, 8) || !aligned(out->radii, 8))
+        return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity must be 16-byte, means2d/radii 8-byte aligned");
+    const CamD cd = make_cam(cam);
+    const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+    float2 *m2 = reinterpret_cast<float2 *>(out->means2d);
+    float4 *co = reinterpret_cast<float4 *>(out->conic_opacity);
+    int2 *rr = reinterpret_cast<int2 *>(out->radii);
+#define GS_PF(D)                                                                                        \
+    k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
+                                             cd, p->alpha_min, p->depth_lo, p->depth_hi, m2, co, out->color,  \
+                                             out->depth, rr)
+    switch (p->sh_degree) {
+    case 0: GS_PF(0); break;
+    case 1: GS_PF(1); break;
+    case 2: GS_PF(2); break;
+    default: GS_PF(3); break;
+    }
+#undef GS_PF
+    GS_LAUNCH_CHECK("k_project");
+    return GS_OK;
+}
+
+extern "C" gs_status gs_project_bwd(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                                    const float *grads2d, gs_param_grads *grads3d, hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if ((s = check_gaussians(g)) != GS_OK) return s;
+    if ((s = check_camera(cam)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    if (!grads3d) return fail(GS_ERR_INVALID_ARGUMENT, "grads3d is NULL");
+    if (g->n > 0 && !grads2d) return fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
+    return launch_project_bwd(g, cam, p, grads2d, grads3d, stream);
+}

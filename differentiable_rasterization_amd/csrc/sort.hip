@@ -1,0 +1,303 @@
+// Device-wide exclusive scan and stable LSD radix sort for gfx950.
+//
+// Radix pass (8-bit digit, reduce-then-scan, stable):
+//   hist    : each 256-thread block counts the digits of its 4096-element tile
+//             (per-wave LDS histograms) and writes them digit-major, so that one
+//             exclusive scan over [digit][block] gives every (digit, block) its
+//             global output offset;
+//   scatter : each wave ranks its 1024 consecutive elements round by round with a
+//             64-lane digit match (8 ballots), giving a stable rank per digit; the
+//             block then places its tile in LDS in sorted order and writes it out in
+//             runs of equal digits (coalesced).
+// No look-back between blocks, so no forward-progress assumption is needed.
+#include "kernels.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kItems = 16;
+constexpr int kTile = kThreads * kItems;      // 4096 elements per block
+constexpr int kWaveSpan = 64 * kItems;        // 1024 consecutive elements per wave
+
+// Exclusive scan of one value per thread across a 256-thread block.  `scratch`
+// holds 4 words.  Returns the exclusive prefix; *block_total receives the sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch, uint32_t *block_total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) scratch[w] = x;
+    __syncthreads();
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t s = scratch[k];
+        if (k < w) pre += s;
+        tot += s;
+    }
+    __syncthreads();
+    *block_total = tot;
+    return pre + x - v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_reduce(const uint32_t *__restrict__ in, int64_t m,
+                                                          uint32_t *__restrict__ partials)
+{
+    __shared__ uint32_t scratch[4];
+    const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
+    uint32_t s = 0;
+    if (base + kItems <= m) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(in + base);
+#pragma unroll
+        for (int k = 0; k < kItems / 4; ++k) {
+            const uint4 q = p[k];
+            s += q.x + q.y + q.z + q.w;
+        }
+    } else {
+        for (int k = 0; k < kItems; ++k)
+            if (base + k < m) s += in[base + k];
+    }
+    uint32_t tot;
+    block_exclusive_scan(s, scratch, &tot);
+    if (threadIdx.x == 0) partials[blockIdx.x] = tot;
+}
+
+// Single block: exclusive scan of the block partials, carrying across chunks.
+__global__ __launch_bounds__(kThreads) void k_scan_partials(uint32_t *__restrict__ partials, int64_t nb,
+                                                            unsigned long long *__restrict__ total)
+{
+    __shared__ uint32_t scratch[4];
+    unsigned long long carry = 0;
+    for (int64_t c = 0; c < nb; c += kThreads) {
+        const int64_t i = c + threadIdx.x;
+        const uint32_t v = i < nb ? partials[i] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan(v, scratch, &tot);
+        if (i < nb) partials[i] = (uint32_t)(carry + ex);
+        carry += tot;
+    }
+    if (threadIdx.x == 0 && total) *total = carry;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t *__restrict__ in, uint32_t *__restrict__ out,
+                                                        int64_t m, const uint32_t *__restrict__ partials)
+{
+    __shared__ uint32_t scratch[4];
+    const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)threadIdx.x * kItems;
+    uint32_t v[kItems];
+    const bool full = base + kItems <= m;
+    if (full) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(in + base);
+#pragma unroll
+        for (int k = 0; k < kItems / 4; ++k) {
+            const uint4 q = p[k];
+            v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) v[k] = base + k < m ? in[base + k] : 0u;
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) s += v[k];
+    uint32_t tot;
+    uint32_t run = block_exclusive_scan(s, scratch, &tot) + partials[blockIdx.x];
+    if (full) {
+        uint4 *p = reinterpret_cast<uint4 *>(out + base);
+#pragma unroll
+        for (int k = 0; k < kItems / 4; ++k) {
+            uint4 q;
+            q.x = run; run += v[4 * k];
+            q.y = run; run += v[4 * k + 1];
+            q.z = run; run += v[4 * k + 2];
+            q.w = run; run += v[4 * k + 3];
+            p[k] = q;
+        }
+    } else {
+        for (int k = 0; k < kItems; ++k)
+            if (base + k < m) { out[base + k] = run; run += v[k]; }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restrict__ keys, int64_t m, int shift,
+                                                         uint32_t *__restrict__ hist, int64_t nb)
+{
+    __shared__ uint32_t h[4][256];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&h[0][0])[i] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)w * kWaveSpan + lane;
+#pragma unroll 4
+    for (int r = 0; r < kItems; ++r) {
+        const int64_t e = base + r * 64;
+        if (e < m) atomicAdd(&h[w][(keys[e] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const int d = threadIdx.x;
+    hist[(int64_t)d * nb + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+}
+
+__global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__restrict__ kin,
+                                                            const uint32_t *__restrict__ vin,
+                                                            uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+                                                            int64_t m, int shift, const uint32_t *__restrict__ offs,
+                                                            int64_t nb)
+{
+    __shared__ uint32_t wcnt[4][256];
+    __shared__ uint32_t bstart[256];
+    __shared__ uint32_t gbase[256];
+    __shared__ uint32_t scratch[4];
+    __shared__ uint32_t skey[kTile];
+    __shared__ uint32_t sval[kTile];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int64_t tile0 = (int64_t)blockIdx.x * kTile;
+    const int64_t base = tile0 + (int64_t)w * kWaveSpan + lane;
+    const uint64_t below_mask = (1ull << lane) - 1ull;
+    uint32_t key[kItems], val[kItems], rank[kItems];
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const int64_t e = base + r * 64;
+        const bool valid = e < m;
+        const uint32_t k = valid ? kin[e] : 0u;
+        const uint32_t v = valid ? vin[e] : 0u;
+        const uint32_t d = (k >> shift) & 255u;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (d >> b) & 1u;
+            const uint64_t bb = __ballot(bit);
+            same &= bit ? bb : ~bb;
+        }
+        const uint32_t below = (uint32_t)__popcll(same & below_mask);
+        const uint32_t cnt = (uint32_t)__popcll(same);
+        const uint32_t prev = wcnt[w][d];
+        __builtin_amdgcn_wave_barrier();
+        if (valid && below == 0) wcnt[w][d] = prev + cnt;
+        __builtin_amdgcn_wave_barrier();
+        key[r] = k;
+        val[r] = v;
+        rank[r] = prev + below;
+    }
+    __syncthreads();
+    {
+        const int d = threadIdx.x;
+        const uint32_t c0 = wcnt[0][d], c1 = wcnt[1][d], c2 = wcnt[2][d], c3 = wcnt[3][d];
+        wcnt[0][d] = 0;
+        wcnt[1][d] = c0;
+        wcnt[2][d] = c0 + c1;
+        wcnt[3][d] = c0 + c1 + c2;
+        uint32_t tot;
+        bstart[d] = block_exclusive_scan(c0 + c1 + c2 + c3, scratch, &tot);
+        gbase[d] = offs[(int64_t)d * nb + blockIdx.x];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+        const int64_t e = base + r * 64;
+        if (e < m) {
+            const uint32_t d = (key[r] >> shift) & 255u;
+            const uint32_t p = bstart[d] + wcnt[w][d] + rank[r];
+            skey[p] = key[r];
+            sval[p] = val[r];
+        }
+    }
+    __syncthreads();
+    const int cnt = (int)min((int64_t)kTile, m - tile0);
+    for (int i = threadIdx.x; i < cnt; i += kThreads) {
+        const uint32_t k = skey[i];
+        const uint32_t d = (k >> shift) & 255u;
+        const uint32_t dst = gbase[d] + ((uint32_t)i - bstart[d]);
+        if (dst < (uint64_t)m) {   // always true for a consistent ranking; keeps a bug from writing out of bounds
+            kout[dst] = k;
+            vout[dst] = sval[i];
+        }
+    }
+}
+
+__global__ void k_fill_i32(int32_t *__restrict__ p, int64_t n, int32_t value)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = value;
+}
+
+__global__ void k_fill_f32(float *__restrict__ p, int64_t n, float value)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = value;
+}
+
+}  // namespace
+
+namespace gsi {
+
+int64_t scan_partials_len(int64_t m) { return ceil_div(m > 0 ? m : 1, kTile); }
+
+gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint32_t *partials,
+                             unsigned long long *total, hipStream_t stream)
+{
+    if (m <= 0) {
+        if (total) {   // a kernel, not a memset: keeps the call capturable in a graph
+            k_scan_partials<<<1, kThreads, 0, stream>>>(partials, 0, total);
+            GS_LAUNCH_CHECK("k_scan_partials");
+        }
+        return GS_OK;
+    }
+    const int64_t nb = scan_partials_len(m);
+    if (nb > 0x7fffffff) return fail(GS_ERR_UNSUPPORTED, "scan too large");
+    k_scan_reduce<<<(unsigned)nb, kThreads, 0, stream>>>(in, m, partials);
+    GS_LAUNCH_CHECK("k_scan_reduce");
+    k_scan_partials<<<1, kThreads, 0, stream>>>(partials, nb, total);
+    GS_LAUNCH_CHECK("k_scan_partials");
+    k_scan_down<<<(unsigned)nb, kThreads, 0, stream>>>(in, out, m, partials);
+    GS_LAUNCH_CHECK("k_scan_down");
+    return GS_OK;
+}
+
+int64_t radix_hist_len(int64_t m) { return 256 * ceil_div(m > 0 ? m : 1, kTile); }
+
+gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
+                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream)
+{
+    *in_b = false;
+    if (m <= 1 || bits <= 0) return GS_OK;
+    const int64_t nb = ceil_div(m, kTile);
+    const int passes = (bits + 7) / 8;
+    uint32_t *sk = ka, *sv = va, *dk = kb, *dv = vb;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        k_radix_hist<<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, shift, hist, nb);
+        GS_LAUNCH_CHECK("k_radix_hist");
+        gs_status s = exclusive_scan_u32(hist, hist, 256 * nb, partials, nullptr, stream);
+        if (s != GS_OK) return s;
+        k_radix_scatter<<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, shift, hist, nb);
+        GS_LAUNCH_CHECK("k_radix_scatter");
+        uint32_t *tk = sk, *tv = sv;
+        sk = dk; sv = dv; dk = tk; dv = tv;
+        *in_b = !*in_b;
+    }
+    return GS_OK;
+}
+
+gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream)
+{
+    if (n <= 0) return GS_OK;
+    k_fill_i32<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(p, n, value);
+    GS_LAUNCH_CHECK("k_fill_i32");
+    return GS_OK;
+}
+
+gs_status fill_f32(float *p, int64_t n, float value, hipStream_t stream)
+{
+    if (n <= 0) return GS_OK;
+    k_fill_f32<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(p, n, value);
+    GS_LAUNCH_CHECK("k_fill_f32");
+    return GS_OK;
+}
+
+}  // namespace gsi

@@ -1,0 +1,44 @@
+"""Memory planning for one GPU (MI355X: 288 GB of HBM3E).
+
+Per-Gaussian float32 scalars: mean 3, scale 3 + quaternion 4, opacity 1, SH
+3*(degree+1)^2 ("Scaling 3D Gaussian Splatting with Distributed Compute",
+section "Where the Memory Goes": 38 learnable scalars and 456 bytes with the
+two Adam moments at SH degree 2, 59 scalars and about 708 bytes at degree 3).
+This library adds the gradient copy, the projected record, the screen-space
+gradients and the binning workspace; those are counted separately.
+"""
+from __future__ import annotations
+
+MI355X_HBM_BYTES = 288e9
+
+
+def learnable_scalars(sh_degree: int) -> int:
+    return 3 + 3 + 4 + 1 + 3 * (sh_degree + 1) ** 2
+
+
+def bytes_per_gaussian(sh_degree: int, adam: bool = True, grads: bool = False) -> int:
+    """Parameters (+ Adam moments) (+ a gradient copy), float32."""
+    copies = 1 + (2 if adam else 0) + (1 if grads else 0)
+    return 4 * learnable_scalars(sh_degree) * copies
+
+
+def step_bytes_per_gaussian(sh_degree: int) -> int:
+    """Everything this library keeps per Gaussian during a training step: parameters,
+    gradients, Adam moments, the projected record (means2d 8, conic+opacity 16, colour 12,
+    depth 4, radii 8), screen-space gradients (36) and the binning workspace (24)."""
+    return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 48 + 36 + 24
+
+
+def step_bytes_per_intersection() -> int:
+    """Intersection lists: ids (4) plus the workspace's two key buffers and one value
+    buffer (12)."""
+    return 16
+
+
+def max_gaussians(hbm_bytes: float, sh_degree: int, adam: bool = True) -> int:
+    return int(hbm_bytes // bytes_per_gaussian(sh_degree, adam=adam))
+
+
+def max_gaussians_training(hbm_bytes: float, sh_degree: int, intersections_per_gaussian: float) -> int:
+    per = step_bytes_per_gaussian(sh_degree) + intersections_per_gaussian * step_bytes_per_intersection()
+    return int(hbm_bytes // per)

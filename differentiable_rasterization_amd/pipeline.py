@@ -1,0 +1,180 @@
+"""Device buffers and the call sequence of one training step.
+
+Allocation (torch, on the GPU) and the order of the C-ABI calls only; every step
+of the computation runs in libgsmi's kernels:
+
+    gs_project -> gs_bin_sort -> gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd -> gs_adam_step
+
+Parameters, gradients and the two Adam moments each live in one contiguous
+[planes][N] float32 buffer (structure of arrays), so every kernel streams
+coalesced planes and Adam runs as one launch over six parameter groups.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as B
+
+# reading: the pages give Adam's eps and betas but no learning rates; these are
+# per-group defaults of the common 3DGS recipe
+DEFAULT_LR = dict(means=1.6e-4, log_scales=5e-3, quats=1e-3, opacity_logits=5e-2, sh_dc=2.5e-3, sh_rest=1.25e-4)
+
+
+class GaussianParams:
+    """Learnable parameters plus gradients and Adam moments, structure of arrays."""
+
+    def __init__(self, n: int, sh_degree: int, device="cuda"):
+        self.n, self.sh_degree = n, sh_degree
+        self.k_sh = (sh_degree + 1) ** 2
+        self.planes = 11 + 3 * self.k_sh
+        self.data = torch.zeros(self.planes, n, dtype=torch.float32, device=device)
+        self.grad = torch.zeros_like(self.data)
+        self.m = torch.zeros_like(self.data)
+        self.v = torch.zeros_like(self.data)
+        self.step_count = 0
+
+    _SLICES = (("means", 0, 3), ("log_scales", 3, 6), ("quats", 6, 10), ("opacity_logits", 10, 11))
+
+    def view(self, buf, name):
+        for nm, a, b in self._SLICES:
+            if nm == name:
+                return buf[a:b] if b - a > 1 else buf[a]
+        if name == "sh":
+            return buf[11:]
+        raise KeyError(name)
+
+    @classmethod
+    def from_scene(cls, scene, device="cuda"):
+        p = cls(scene.n, scene.sh_degree, device)
+        for name in ("means", "log_scales", "quats", "opacity_logits", "sh"):
+            p.view(p.data, name).copy_(getattr(scene, name).to(device))
+        return p
+
+    def gaussians(self) -> B.Gaussians:
+        v = lambda nm: self.view(self.data, nm)
+        return B.gaussians(v("means"), v("log_scales"), v("quats"), v("opacity_logits"), v("sh"))
+
+    def param_grads(self) -> B.ParamGrads:
+        v = lambda nm: self.view(self.grad, nm)
+        return B.param_grads(v("means"), v("log_scales"), v("quats"), v("opacity_logits"), v("sh"))
+
+    def adam_groups(self, lr=DEFAULT_LR):
+        bounds = [("means", 0, 3), ("log_scales", 3, 6), ("quats", 6, 10), ("opacity_logits", 10, 11),
+                  ("sh_dc", 11, 14), ("sh_rest", 14, self.planes)]
+        out = []
+        for name, a, b in bounds:
+            if b <= a:
+                continue
+            out.append((self.data[a:b], self.grad[a:b], self.m[a:b], self.v[a:b], lr[name]))
+        return out
+
+
+class Projection:
+    def __init__(self, n, device="cuda"):
+        self.means2d = torch.zeros(n, 2, dtype=torch.float32, device=device)
+        self.conic_opacity = torch.zeros(n, 4, dtype=torch.float32, device=device)
+        self.color = torch.zeros(n, 3, dtype=torch.float32, device=device)
+        self.depth = torch.zeros(n, dtype=torch.float32, device=device)
+        self.radii = torch.zeros(n, 2, dtype=torch.int32, device=device)
+
+    def abi(self) -> B.Projected:
+        return B.projected(self.means2d, self.conic_opacity, self.color, self.depth, self.radii)
+
+
+class Binning:
+    """Intersection lists and the sort workspace; grows on demand."""
+
+    def __init__(self, n, width, height, capacity=0, device="cuda", with_keys=False, with_touched=False):
+        self.n, self.width, self.height, self.device = n, width, height, device
+        self.tiles = ((width + 15) // 16) * ((height + 15) // 16)
+        self.tile_ranges = torch.zeros(self.tiles + 1, dtype=torch.int32, device=device)
+        self.with_keys, self.with_touched = with_keys, with_touched
+        self.tiles_touched = torch.zeros(n, dtype=torch.int32, device=device) if with_touched else None
+        self.n_isect = 0
+        self._alloc(max(capacity, 1))
+
+    def _alloc(self, capacity):
+        self.capacity = int(capacity)
+        self.ids = torch.zeros(self.capacity, dtype=torch.int32, device=self.device)
+        self.keys = torch.zeros(self.capacity, dtype=torch.int64, device=self.device) if self.with_keys else None
+        ws = B.gs_bin_sort_workspace_bytes(self.n, self.capacity, self.width, self.height)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
+
+    def abi(self) -> B.Bins:
+        return B.bins(self.ids, self.tile_ranges, self.keys, self.tiles_touched)
+
+    def sort(self, proj: Projection, cam: B.Camera, stream=None) -> int:
+        try:
+            k = B.gs_bin_sort(proj.abi(), self.n, cam, self.abi(), self.workspace, stream)
+        except B.GsCapacityError as e:
+            self._alloc(int(math.ceil(e.required * 1.25)) + 1024)
+            k = B.gs_bin_sort(proj.abi(), self.n, cam, self.abi(), self.workspace, stream)
+        self.n_isect = k
+        return k
+
+
+class Frame:
+    """Per-image buffers: render, transmittance, traversal counts, loss gradient."""
+
+    def __init__(self, width, height, device="cuda"):
+        self.width, self.height = width, height
+        self.n_px = width * height
+        self.color = torch.zeros(height, width, 3, dtype=torch.float32, device=device)
+        self.t_final = torch.zeros(height, width, dtype=torch.float32, device=device)
+        self.n_trav = torch.zeros(height, width, dtype=torch.int32, device=device)
+        self.dL_dcolor = torch.zeros(height, width, 3, dtype=torch.float32, device=device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=device)
+        # running sum of N_p (Gaussian-pixel evaluations) over forward passes; cleared by the caller
+        self.n_trav_sum = torch.zeros(1, dtype=torch.int64, device=device)
+        self.loss_ws = torch.empty(max(B.gs_loss_workspace_bytes(self.n_px), 8), dtype=torch.uint8, device=device)
+
+
+class TrainStep:
+    """One-view training step on one GPU: forward, L1 loss, backward, Adam."""
+
+    def __init__(self, params: GaussianParams, width, height, device="cuda", raster=None, lr=DEFAULT_LR,
+                 capacity=0):
+        self.params = params
+        self.raster = raster if raster is not None else B.make_params(params.sh_degree)
+        self.proj = Projection(params.n, device)
+        self.bins = Binning(params.n, width, height, capacity=capacity, device=device)
+        self.frame = Frame(width, height, device)
+        self.grads2d = torch.zeros(9, params.n, dtype=torch.float32, device=device)
+        self.lr = lr
+
+    def forward(self, cam: B.Camera, stream=None):
+        B.gs_project(self.params.gaussians(), cam, self.raster, self.proj.abi(), stream)
+        self.bins.sort(self.proj, cam, stream)
+        f = self.frame
+        B.gs_raster_fwd(self.proj.abi(), self.bins.abi(), cam, self.raster, f.color, f.t_final, f.n_trav,
+                        f.n_trav_sum, stream)
+
+    def loss(self, target, stream=None):
+        f = self.frame
+        B.gs_loss_l1(f.color, target, f.n_px, f.loss, f.dL_dcolor, f.loss_ws, stream)
+
+    def backward_raster(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):
+        f = self.frame
+        B.gs_raster_bwd(self.params.gaussians(), self.proj.abi(), self.bins.abi(), cam, self.raster, f.t_final,
+                        f.n_trav, f.dL_dcolor if dL_dcolor is None else dL_dcolor, dL_dt, self.grads2d, None,
+                        stream)
+
+    def backward_project(self, cam: B.Camera, stream=None):
+        B.gs_project_bwd(self.params.gaussians(), cam, self.raster, self.grads2d, self.params.param_grads(), stream)
+
+    def backward(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None, grads3d=True):
+        self.backward_raster(cam, dL_dcolor, dL_dt, stream)
+        if grads3d:
+            self.backward_project(cam, stream)
+
+    def adam(self, stream=None):
+        self.params.step_count += 1
+        B.gs_adam_step(self.params.adam_groups(self.lr), self.params.step_count, 0.9, 0.999, 1e-15, stream)
+
+    def step(self, cam: B.Camera, target, stream=None):
+        self.forward(cam, stream)
+        self.loss(target, stream)
+        self.backward(cam, stream=stream)
+        self.adam(stream)

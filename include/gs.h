@@ -1,0 +1,252 @@
+/*
+ * gs.h -- C ABI of libgsmi, the one-GPU 3D Gaussian splatting training step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The step, as the sources describe it (page titles; sections / equations):
+ *   projection + SH colour  -> gs_project     "Splaxel: Efficient Distributed Training of 3D
+ *                                             Gaussian Splatting for Large-scale Scene
+ *                                             Reconstruction via Pixel-level Communication",
+ *                                             section 2 ("Projection"); "Scaling 3D Gaussian
+ *                                             Splatting with Distributed Compute" (ROCm blog),
+ *                                             walkthrough steps 3-4
+ *   tile binning + depth sort -> gs_bin_sort  "ByteSplat: Efficient Distributed 3D Gaussian
+ *                                             Splatting Training via Intra- and Inter-GPU
+ *                                             communication reduction", section 2.1
+ *                                             ("Projection", "Sorting")
+ *   front-to-back compositing -> gs_raster_fwd  ByteSplat section 2.1, Eq. 1
+ *   L1 loss                   -> gs_loss_l1      ByteSplat Eq. 2 (L1 term); ROCm blog, loss
+ *   backward rasterization    -> gs_raster_bwd   ByteSplat section 2.1, Eq. 3 and Eq. 4, then
+ *                                                the backward through projection and colour
+ *   parameter update          -> gs_adam_step    ROCm blog, create_splats_with_optimizers
+ *   partial renders of depth slabs, their over-composition and the compaction of non-zero
+ *   gradient records -> gs_composite_over(_bwd), gs_compact_grads  (Splaxel sections 4.2-4.3;
+ *   ByteSplat section 3 Insight 4 and section 6)
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument that names device memory must be a device (or managed)
+ *     allocation owned by the caller; the library never allocates or frees memory.
+ *     Host pointers are marked "host".
+ *   - All calls enqueue work on `stream` and return without waiting, except where a
+ *     function says it reads a count back to the host (it then synchronises `stream`).
+ *   - Arrays are float32/int32 unless stated; "[a][b]" is row-major (b fastest).
+ *   - Errors: arguments are checked on the host before anything is launched; a non-OK
+ *     status leaves outputs unspecified and gs_last_error() describes the problem.
+ *     HIP runtime failures return GS_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Thread safety: calls are reentrant; the only global state is the thread-local
+ *     error message.  Calls on different streams may run concurrently if their
+ *     buffers do not overlap.
+ */
+#ifndef GS_H
+#define GS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, negative size, bad image size ... */
+    GS_ERR_UNSUPPORTED = 2,      /* e.g. SH degree > 3, more tiles than the sort supports */
+    GS_ERR_CAPACITY = 3,         /* an output list is too small; the required size is reported */
+    GS_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} gs_status;
+
+#define GS_TILE 16          /* tiles are 16x16 pixels (ByteSplat section 2.2) */
+#define GS_MAX_SH_DEGREE 3
+#define GS_RADIUS_CAP (1 << 20)
+
+/* Pinhole camera, OpenCV axes (x right, y down, z forward).  viewmat is the
+ * row-major 4x4 world->camera matrix (rows 0..2 = [R | t]); pixel (i, j) has its
+ * centre at (i + 0.5, j + 0.5). */
+typedef struct {
+    float viewmat[16];
+    float fx, fy, cx, cy;
+    int32_t width, height;   /* 1 .. 65536, at most 2^24 tiles */
+    float near_z;            /* Gaussians with camera depth <= near_z are culled */
+} gs_camera;
+
+typedef struct {
+    int32_t sh_degree;  /* 0..3: (sh_degree+1)^2 coefficients per colour channel */
+    float alpha_min;    /* alpha-check: entries with alpha < alpha_min are skipped (1/255) */
+    float alpha_max;    /* alpha is clamped to at most alpha_max (0.99); must be < 1 */
+    float t_min;        /* compositing stops before an entry once T < t_min (1e-4); 0 disables */
+    float depth_lo;     /* only Gaussians whose depth key d satisfies depth_lo <= d < depth_hi */
+    float depth_hi;     /*   are projected (depth slab of a partial render); 0, +inf = all */
+} gs_raster_params;
+
+/* Learnable parameters, structure of arrays (planes of n floats):
+ *   means [3][n], log_scales [3][n] (scale = exp), quats [4][n] (w, x, y, z; normalised
+ *   in the forward), opacity_logits [n] (opacity = sigmoid), sh [K*3][n] with
+ *   K = (sh_degree+1)^2 and plane k*3 + c holding coefficient k of channel c
+ *   (k = l*l + l + m, real orthonormal basis without Condon-Shortley phase). */
+typedef struct {
+    const float *means, *log_scales, *quats, *opacity_logits, *sh;
+    int64_t n;
+} gs_gaussians;
+
+/* Projected 2D records, one per Gaussian.
+ *   means2d [n][2]        pixel coordinates (u, v) of the mean
+ *   conic_opacity [n][4]  (A, B, C, o): inverse 2D covariance [[A, B], [B, C]] and opacity
+ *                         (16-byte aligned)
+ *   color [n][3]          RGB from the SH coefficients (no offset, no clamp)
+ *   depth [n]             camera-space depth as a float32 key:
+ *                         fma(R22, z, fma(R21, y, R20 * x)) + t2, each step rounded
+ *   radii [n][2]          half-extents in pixels of the alpha >= alpha_min ellipse box,
+ *                         rounded up, >= 1; (0, 0) marks a culled Gaussian.  For culled
+ *                         Gaussians only radii and depth are written. */
+typedef struct {
+    float *means2d, *conic_opacity, *color, *depth;
+    int32_t *radii;
+} gs_projected;
+
+/* Tile-Gaussian intersection lists.
+ *   ids [capacity]            Gaussian index of each entry, sorted by (tile, depth key, index)
+ *   tile_ranges [tiles + 1]   entries of tile t are ids[tile_ranges[t] .. tile_ranges[t+1])
+ *   keys [capacity]           optional (may be NULL): tile << 32 | depth key bits per entry
+ *   tiles_touched [n]         optional (may be NULL): number of tiles of each Gaussian
+ * tiles = ceil(W/16) * ceil(H/16), tile id = row * ceil(W/16) + column. */
+typedef struct {
+    uint32_t *ids;
+    int32_t *tile_ranges;
+    uint64_t *keys;
+    int32_t *tiles_touched;
+    int64_t capacity;
+} gs_bins;
+
+/* Gradients of the learnable parameters, same shapes as gs_gaussians. */
+typedef struct {
+    float *means, *log_scales, *quats, *opacity_logits, *sh;
+} gs_param_grads;
+
+/* One Adam parameter group: n scalars of parameters p, gradients g, moments m, v. */
+typedef struct {
+    float *p;
+    const float *g;
+    float *m, *v;
+    int64_t n;
+    float lr;
+} gs_adam_group;
+
+/* Projection and colour evaluation, one thread per Gaussian (Splaxel section 2:
+ * Sigma = R S S^T R^T, frustum culling by the mean, Sigma2D = J W Sigma W^T J^T;
+ * ROCm blog step 4: SH evaluated to RGB per camera).  Culls a Gaussian if an input is
+ * not finite, |q| = 0, its depth key is outside [depth_lo, depth_hi), its camera depth
+ * is <= near_z, its projected mean lies outside [0, W) x [0, H), det(Sigma2D) <= 0, or
+ * its opacity < alpha_min.  The geometric chain runs in double and is rounded to
+ * the float32 record.  Inputs: g (n >= 0), cam, p.  Outputs: out (n records). */
+gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                     gs_projected *out, hipStream_t stream);
+
+/* Workspace bytes gs_bin_sort needs for n Gaussians, `capacity` list entries and the
+ * camera's image size. */
+size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
+
+/* Tile binning and depth sort (ByteSplat section 2.1, "Projection" and "Sorting").
+ * Every Gaussian with radii > 0 emits one entry per 16x16 tile its box
+ * [u - rx, u + rx] x [v - ry, v + ry] touches (float32 arithmetic:
+ * x0 = clamp(floor((u - rx)/16), 0, TX), x1 = clamp(floor((u + rx)/16) + 1, 0, TX), same
+ * for y).  Entries are ordered by (tile, depth key bits, Gaussian index): a stable LSD
+ * radix sort of the Gaussians by depth key, a scan of their tile counts in that order,
+ * emission, and a stable radix sort of the entries by tile id.
+ * Reads the total K back to the host (synchronises `stream`) and stores it in
+ * *n_isect_out (host).  If K > bins->capacity returns GS_ERR_CAPACITY with K in
+ * *n_isect_out and the lists unspecified.  workspace: device memory of at least
+ * gs_bin_sort_workspace_bytes(n, capacity, W, H) bytes, 256-byte aligned. */
+gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, gs_bins *bins,
+                      int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Front-to-back alpha compositing per 16x16 tile (ByteSplat Eq. 1): for each pixel,
+ * T = 1; for each entry of its tile list in order: stop if T < t_min; alpha =
+ * min(alpha_max, o exp(-A dx^2/2 - B dx dy - C dy^2/2)); skip if alpha < alpha_min;
+ * C += T alpha c; T *= 1 - alpha.  Outputs color [H][W][3], t_final [H][W] (T after the
+ * last accepted entry) and n_trav [H][W] (number of list entries the pixel traversed,
+ * N_p of Eq. 1).  If n_trav_sum (device, may be NULL) is given, sum_p N_p -- the number of
+ * Gaussian-pixel evaluations -- is added to it (the caller clears it).  No background is
+ * added. */
+gs_status gs_raster_fwd(const gs_projected *proj, const gs_bins *bins, const gs_camera *cam,
+                        const gs_raster_params *p, float *color, float *t_final, int32_t *n_trav,
+                        unsigned long long *n_trav_sum, hipStream_t stream);
+
+/* Workspace bytes gs_loss_l1 needs for n_px pixels. */
+size_t gs_loss_workspace_bytes(int64_t n_px);
+
+/* L1 term of the loss (ByteSplat Eq. 2): loss = mean over the 3*n_px colour values of
+ * |color - target|; dL_dcolor = sign(color - target) / (3 n_px) with sign(0) = 0.
+ * loss_out: device float (may be NULL); dL_dcolor [n_px][3].  The sum is accumulated in
+ * double.  workspace: gs_loss_workspace_bytes(n_px) bytes of device memory. */
+gs_status gs_loss_l1(const float *color, const float *target, int64_t n_px, float *loss_out,
+                     float *dL_dcolor, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward rasterization (ByteSplat Eq. 3 and Eq. 4): per tile, each pixel walks its
+ * traversed entries back to front, recovers T_i = T_{i+1} / (1 - alpha_i), and adds its
+ * partial gradient to the Gaussian's 9 screen-space fields, in the order
+ * (u, v, A, B, C, o, r, g, b) of grads2d [9][n] (float32 atomics, so the summation order
+ * is not deterministic).  grads2d is cleared by the call before accumulation.
+ * dL_dcolor [H][W][3]; dL_dt [H][W] is the gradient of t_final (may be NULL).  t_final
+ * and n_trav come from gs_raster_fwd on the same inputs.  If grads3d is non-NULL the
+ * aggregated screen-space gradients are then propagated through projection and colour
+ * evaluation into grads3d (every entry overwritten; zero for culled Gaussians). */
+gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                        const gs_camera *cam, const gs_raster_params *p, const float *t_final,
+                        const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt,
+                        float *grads2d, gs_param_grads *grads3d, hipStream_t stream);
+
+/* Backward through projection and colour evaluation alone (ByteSplat section 2.1: the
+ * aggregated screen-space gradients are propagated through projection and colour
+ * evaluation): from grads2d [9][n] (fields u, v, A, B, C, o, r, g, b) to grads3d (every
+ * entry overwritten; zero for Gaussians the projection culls).  Same g, cam and p as the
+ * gs_project call that produced the records.  Lets the caller aggregate screen-space
+ * gradients from several partial renders before one projection backward. */
+gs_status gs_project_bwd(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                         const float *grads2d, gs_param_grads *grads3d, hipStream_t stream);
+
+/* Bias-corrected Adam over up to 16 parameter groups in one launch (ROCm blog,
+ * create_splats_with_optimizers: eps 1e-15, betas (0.9, 0.999) at batch size 1):
+ * m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2; p -= lr (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps).
+ * step t >= 1.  The gradients are read, not modified. */
+gs_status gs_adam_step(const gs_adam_group *groups, int32_t n_groups, int32_t step, float beta1,
+                       float beta2, float eps, hipStream_t stream);
+
+/* Over-composition of k depth-ordered partial renders along each pixel ray (Splaxel
+ * sections 3.4 and 4.2; saturation skip of section 4.3): A = 1, C = 0; for each partition:
+ * if A < t_min it is skipped, else C += A C_k and A *= T_k.  t_out = A.
+ * c_k: host array of k device pointers to [n_px][3]; t_k: host array of k pointers to
+ * [n_px]; 1 <= k <= 16. */
+gs_status gs_composite_over(const float *const *c_k, const float *const *t_k, int32_t k,
+                            int64_t n_px, float t_min, float *c_out, float *t_out,
+                            hipStream_t stream);
+
+/* Backward of gs_composite_over: dL/dC_k = A_k dL/dC; dL/dT_k = A_k (U_k . dL/dC) +
+ * (prod_{m != k} T_m) dL/dT with U_k the composite of the partitions behind k; skipped
+ * partitions get zeros.  dL_dt may be NULL.  dL_dc_k / dL_dt_k: host arrays of k device
+ * pointers. */
+gs_status gs_composite_over_bwd(const float *const *c_k, const float *const *t_k, int32_t k,
+                                int64_t n_px, float t_min, const float *dL_dc, const float *dL_dt,
+                                float *const *dL_dc_k, float *const *dL_dt_k, hipStream_t stream);
+
+/* Workspace bytes gs_compact_grads needs for n Gaussians. */
+size_t gs_compact_workspace_bytes(int64_t n);
+
+/* Zero-gradient elision (ByteSplat section 3 Insight 4, section 6): keeps the Gaussians
+ * whose 9 screen-space gradient fields are not all exactly zero (-0.0 counts as zero)
+ * and writes records {uint32 index_base + i, float g[9]} (40 bytes each) in ascending
+ * index order to `records` (capacity n records), sets bit i%32 of bitmap[i/32] for each
+ * kept Gaussian (bitmap [ceil(n/32)]), and reads the record count back to the host
+ * (*r_out, host; synchronises `stream`). */
+gs_status gs_compact_grads(const float *grads2d, int64_t n, uint32_t index_base, void *records,
+                           uint32_t *bitmap, int64_t *r_out, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* Message describing the last non-OK status returned on the calling thread. */
+const char *gs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_H */

@@ -1,0 +1,313 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded
+synthetic inputs.  GPU only.
+
+Tolerances: projected records within a few float32 ulps (both sides project in
+double and round once); binning and compaction bit-exact; images and final
+transmittance within 1e-4 max |difference| outside tie pixels; screen-space and
+parameter gradients within relative L2 error 1e-3 per tensor (float32 atomics);
+Adam within 1e-6 relative per tensor.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differentiable_rasterization_amd import binding as B
+from differentiable_rasterization_amd import pipeline as PL
+from differentiable_rasterization_amd import scenes
+from tests.gpu_util import DEV, compare_images, gpu_forward, log, oracle_params, rel_l2, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": lambda: scenes.scene_tiny(),
+    "ragged_sh1": lambda: scenes.scene_small_random(11, 600, 77, 53, 1, extent=1.2, distance=3.0),
+    "ragged_sh2": lambda: scenes.scene_small_random(12, 3000, 130, 33, 2, extent=1.5, distance=3.0,
+                                                    log_scale_mean=-3.0),
+    "offscreen_sh3": lambda: scenes.scene_small_random(13, 2000, 96, 80, 3, extent=4.0, distance=3.0,
+                                                       log_scale_mean=-2.5, logit_mean=1.0),
+}
+
+
+def _scene(name):
+    if name == "100k":
+        return scenes.scene_100k()
+    return SMALL[name]()
+
+
+# ------------------------------------------------------------------ projection
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "ragged_sh2", "offscreen_sh3", "100k"])
+def test_project_parity(name):
+    log(f"project parity {name}")
+    sc = _scene(name)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    st = gpu_forward(sc, cam, rp)
+    P = oracle.project(sc, cam, oracle_params(rp))
+    radii = st.proj.radii.cpu().numpy()
+    vis_g = (radii[:, 0] > 0) & (radii[:, 1] > 0)
+    marg = P.marginal.astype(bool)
+    assert np.array_equal(vis_g[~marg], P.vis[~marg].astype(bool))
+    assert 0 < vis_g.sum() <= sc.n
+    dk = st.proj.depth.cpu().numpy()
+    assert np.array_equal(dk.view(np.uint32), P.dkey.view(np.uint32)), "depth keys must be bit-identical"
+    v = vis_g & P.vis.astype(bool)
+    assert np.array_equal(radii[v], P.radii[v])
+    m2 = st.proj.means2d.cpu().numpy()[v]
+    co = st.proj.conic_opacity.cpu().numpy()[v]
+    col = st.proj.color.cpu().numpy()[v]
+    rec = P.rec[v]
+    assert ulp_diff(m2, rec[:, :2].astype(np.float32)).max() <= 2
+    assert ulp_diff(co[:, 3], rec[:, 5].astype(np.float32)).max() <= 1
+    # conic: both sides invert Sigma2D in double; allow a few ulps of the larger entry
+    scale = np.abs(rec[:, 2:5]).max(axis=1, keepdims=True)
+    assert (np.abs(co[:, :3] - rec[:, 2:5]) / scale).max() < 1e-6
+    assert np.abs(col - rec[:, 6:9]).max() < 2e-6 * max(1.0, np.abs(rec[:, 6:9]).max())
+
+
+def test_project_culls_nonfinite_and_window():
+    sc = scenes.scene_small_random(14, 256, 64, 48, 1, extent=1.0)
+    sc.means[0, 3] = float("nan")
+    sc.log_scales[1, 5] = float("inf")
+    sc.quats[:, 7] = 0.0
+    sc.sh[2, 9] = float("nan")
+    cam = sc.cameras[0]
+    lo, hi = float(np.float32(2.7)), float(np.float32(3.3))
+    rp = B.make_params(1, depth_lo=lo, depth_hi=hi)
+    st = gpu_forward(sc, cam, rp)
+    P = oracle.project(sc, cam, oracle_params(rp))
+    radii = st.proj.radii.cpu().numpy()
+    vis_g = (radii[:, 0] > 0)
+    for i in (3, 5, 7, 9):
+        assert not vis_g[i]
+    assert np.array_equal(vis_g, P.vis.astype(bool))
+    dk = st.proj.depth.cpu().numpy()
+    assert np.all((dk[vis_g] >= lo) & (dk[vis_g] < hi))
+
+
+# ------------------------------------------------------------------ binning (bit-exact)
+
+def _bin_gpu(m2, r, d, W, H, capacity=None):
+    n = d.numel()
+    cam = B.make_camera([1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1], 1.0, 1.0, 0.0, 0.0, W, H)
+    proj = PL.Projection(max(n, 1), DEV)
+    if n:
+        proj.means2d[:n].copy_(m2.to(DEV))
+        proj.radii[:n].copy_(r.to(DEV))
+        proj.depth[:n].copy_(d.to(DEV))
+    bins = PL.Binning(n, W, H, capacity=capacity or 0, device=DEV, with_keys=True, with_touched=True)
+    k = bins.sort(proj, cam)
+    torch.cuda.synchronize()
+    return k, bins
+
+
+@pytest.mark.parametrize("n,W,H,maxr,seed", [
+    (0, 64, 64, 8, 1), (1, 64, 64, 8, 2), (7, 16, 16, 3, 3), (3000, 100, 70, 30, 4), (20000, 257, 129, 60, 5),
+    (200000, 1920, 1080, 24, 6), (50000, 3840, 2160, 300, 7), (5000, 4096, 4096, 2000, 8),
+])
+def test_bin_sort_bit_exact(n, W, H, maxr, seed):
+    log(f"bin sort n={n} {W}x{H}")
+    m2, r, d = scenes.projected_for_binning(seed, n, W, H, max_radius=maxr)
+    k, bins = _bin_gpu(m2, r, d, W, H)
+    tt, keys, ids, ranges = oracle.bin_f32(m2, r, d, W, H)
+    assert k == len(ids)
+    assert np.array_equal(bins.tile_ranges.cpu().numpy(), ranges)
+    if n:
+        assert np.array_equal(bins.tiles_touched.cpu().numpy(), tt)
+    if k:
+        assert np.array_equal(bins.ids[:k].cpu().numpy().view(np.uint32), ids)
+        assert np.array_equal(bins.keys[:k].cpu().numpy().view(np.uint64), keys)
+
+
+def test_bin_sort_all_culled_and_capacity():
+    m2, r, d = scenes.projected_for_binning(9, 4000, 200, 150, max_radius=20)
+    r0 = torch.zeros_like(r)
+    k, bins = _bin_gpu(m2, r0, d, 200, 150)
+    assert k == 0 and int(bins.tile_ranges.abs().sum()) == 0
+    # capacity error reports the required size and leaves the caller to grow
+    tt, keys, ids, ranges = oracle.bin_f32(m2, r, d, 200, 150)
+    cam = B.make_camera([1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1], 1.0, 1.0, 0.0, 0.0, 200, 150)
+    proj = PL.Projection(4000, DEV)
+    proj.means2d.copy_(m2.to(DEV)); proj.radii.copy_(r.to(DEV)); proj.depth.copy_(d.to(DEV))
+    small = PL.Binning(4000, 200, 150, capacity=10, device=DEV)
+    with pytest.raises(B.GsCapacityError) as ei:
+        B.gs_bin_sort(proj.abi(), 4000, cam, small.abi(), small.workspace)
+    assert ei.value.required == len(ids)
+
+
+# ------------------------------------------------------------------ forward compositing
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "ragged_sh2", "offscreen_sh3", "100k"])
+@pytest.mark.parametrize("t_min", [1e-4, 0.0])
+def test_forward_parity(name, t_min):
+    log(f"forward parity {name} t_min={t_min}")
+    sc = _scene(name)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree, t_min=t_min)
+    st = gpu_forward(sc, cam, rp)
+    op = oracle_params(rp)
+    P = oracle.project(sc, cam, op)
+    c, tf, nt, tie = oracle.render(P, op)
+    stats = compare_images(st.frame.color.cpu().numpy(), st.frame.t_final.cpu().numpy(), c, tf, tie)
+    ng = st.frame.n_trav.cpu().numpy()
+    mism = (ng != nt) & ~tie
+    assert mism.sum() <= max(2, 1e-4 * ng.size), (int(mism.sum()), stats)
+    log(f"  {stats} n_trav sum gpu={int(ng.sum())} orc={int(nt.sum())}")
+
+
+# ------------------------------------------------------------------ loss
+
+@pytest.mark.parametrize("h,w", [(64, 64), (37, 41), (1, 1), (1080, 1920)])
+def test_loss_l1_parity(h, w):
+    g = torch.Generator().manual_seed(h * 7 + w)
+    c = torch.rand(h, w, 3, generator=g)
+    t = torch.rand(h, w, 3, generator=g)
+    t.view(-1)[::97] = c.view(-1)[::97]          # exact ties -> zero gradient
+    loss_o, G_o = oracle.loss_l1(c, t)
+    cg, tg = c.to(DEV), t.to(DEV)
+    dl = torch.zeros_like(cg)
+    loss = torch.zeros(1, device=DEV)
+    ws = torch.empty(B.gs_loss_workspace_bytes(h * w), dtype=torch.uint8, device=DEV)
+    B.gs_loss_l1(cg, tg, h * w, loss, dl, ws)
+    torch.cuda.synchronize()
+    assert abs(loss.item() - loss_o) <= 1e-6 * loss_o
+    assert np.array_equal(dl.cpu().numpy().reshape(-1), G_o.astype(np.float32))
+
+
+# ------------------------------------------------------------------ backward
+
+def _oracle_G(c_orc, target):
+    """dL/dC of the L1 loss on the oracle's image, as the float32 input both sides use."""
+    _, G = oracle.loss_l1(c_orc.astype(np.float32), target)
+    return G.astype(np.float32).reshape(c_orc.shape)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "ragged_sh2", "offscreen_sh3", "100k"])
+@pytest.mark.parametrize("with_gt", [False, True])
+def test_backward_parity(name, with_gt):
+    log(f"backward parity {name} with_gt={with_gt}")
+    sc = _scene(name)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    op = oracle_params(rp)
+    st = gpu_forward(sc, cam, rp)
+    P = oracle.project(sc, cam, op)
+    c, tf, nt, tie = oracle.render(P, op)
+    G = _oracle_G(c, sc.targets[0].numpy())
+    GT = None
+    if with_gt:
+        GT = (np.random.default_rng(5).normal(size=tf.shape) * 1e-4).astype(np.float32)
+    g2_o = oracle.raster_backward(P, G.astype(np.float64), None if GT is None else GT.astype(np.float64), op)
+    g3_o = oracle.project_backward(sc, cam, g2_o, op)
+    Gd = torch.from_numpy(G).to(DEV)
+    GTd = torch.from_numpy(GT).to(DEV) if GT is not None else None
+    st.backward(B.camera_from(cam), dL_dcolor=Gd, dL_dt=GTd)
+    torch.cuda.synchronize()
+    g2 = st.grads2d.cpu().numpy()
+    errs = {oracle.G_FIELDS[f]: rel_l2(g2[f], g2_o[f]) for f in range(9)}
+    log(f"  grads2d rel-L2 {errs}")
+    assert max(errs.values()) <= 1e-3, errs
+    gp = st.params
+    errs3 = {nm: rel_l2(gp.view(gp.grad, nm).cpu().numpy(), g3_o[nm]) for nm in
+             ("means", "log_scales", "quats", "opacity_logits", "sh")}
+    log(f"  grads3d rel-L2 {errs3}")
+    assert max(errs3.values()) <= 1e-3, errs3
+    # repeat: only the atomic summation order may differ
+    first = st.grads2d.clone()
+    st.backward(B.camera_from(cam), dL_dcolor=Gd, dL_dt=GTd)
+    torch.cuda.synchronize()
+    assert rel_l2(st.grads2d.cpu().numpy(), first.cpu().numpy()) <= 1e-6
+
+
+# ------------------------------------------------------------------ Adam
+
+@pytest.mark.parametrize("n,step", [(1, 1), (1001, 1), (4096, 7), (250_001, 3)])
+def test_adam_parity(n, step):
+    host = [(scenes.adam_state(n + step, n, step), 1e-3), (scenes.adam_state(n + step + 1, n + 3, step), 5e-2)]
+    dev = [([t.to(DEV).contiguous() for t in st], lr) for st, lr in host]
+    B.gs_adam_step([(p, g, m, v, lr) for (p, g, m, v), lr in dev], step, 0.9, 0.999, 1e-15)
+    torch.cuda.synchronize()
+    for ((p, g, m, v), lr), ((dp, _, dm, dv), _) in zip(host, dev):
+        po, mo, vo = oracle.adam(p, g, m, v, float(np.float32(lr)), float(np.float32(0.9)),
+                                 float(np.float32(0.999)), float(np.float32(1e-15)), step)
+        assert rel_l2(dp.cpu().numpy(), po) <= 1e-6
+        assert rel_l2(dm.cpu().numpy(), mo) <= 1e-6
+        assert rel_l2(dv.cpu().numpy(), vo) <= 1e-6
+        # the update itself, not only the parameters
+        upd_o = po - p.double().numpy()
+        upd = dp.cpu().numpy().astype(np.float64) - p.double().numpy()
+        assert rel_l2(upd, upd_o) <= 1e-4
+
+
+# ------------------------------------------------------------------ partial renders
+
+@pytest.mark.parametrize("parts,n_px,t_min", [(4, 5000, 1e-4), (4, 5000, 0.0), (1, 777, 1e-4), (3, 1, 1e-4)])
+def test_composite_parity(parts, n_px, t_min):
+    cs, ts = scenes.partial_images(20 + parts, parts, n_px)
+    c_o, t_o = oracle.composite(cs, ts, float(np.float32(t_min)))
+    cg = [c.to(DEV) for c in cs]
+    tg = [t.to(DEV) for t in ts]
+    c_out = torch.zeros(n_px, 3, device=DEV)
+    t_out = torch.zeros(n_px, device=DEV)
+    B.gs_composite_over(cg, tg, n_px, t_min, c_out, t_out)
+    rng = np.random.default_rng(parts)
+    G = rng.normal(size=(n_px, 3)).astype(np.float32)
+    GT = rng.normal(size=n_px).astype(np.float32)
+    dcs = [torch.zeros(n_px, 3, device=DEV) for _ in range(parts)]
+    dts = [torch.zeros(n_px, device=DEV) for _ in range(parts)]
+    B.gs_composite_over_bwd(cg, tg, n_px, t_min, torch.from_numpy(G).to(DEV), torch.from_numpy(GT).to(DEV), dcs, dts)
+    torch.cuda.synchronize()
+    assert np.abs(c_out.cpu().numpy() - c_o).max() <= 1e-6
+    assert np.abs(t_out.cpu().numpy() - t_o).max() <= 1e-6
+    dc_o, dt_o = oracle.composite_bwd(cs, ts, float(np.float32(t_min)), G, GT)
+    for k in range(parts):
+        assert np.abs(dcs[k].cpu().numpy() - dc_o[k]).max() <= 1e-5 * max(1, np.abs(dc_o[k]).max())
+        assert np.abs(dts[k].cpu().numpy() - dt_o[k]).max() <= 1e-5 * max(1, np.abs(dt_o[k]).max())
+
+
+@pytest.mark.parametrize("n,base", [(1, 0), (63, 5), (5000, 1000), (1_000_003, 7)])
+def test_compact_bit_exact(n, base):
+    g = scenes.sparse_grads(30 + n % 97, n)
+    rec_o, bm_o = oracle.compact(g, base)
+    gd = g.to(DEV)
+    records = torch.zeros(n, 10, dtype=torch.int32, device=DEV)
+    bitmap = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    ws = torch.empty(B.gs_compact_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    R = B.gs_compact_grads(gd, n, base, records, bitmap, ws)
+    assert R == rec_o.shape[0]
+    assert np.array_equal(records[:R].cpu().numpy().view(np.uint32), rec_o)
+    assert np.array_equal(bitmap.cpu().numpy().view(np.uint32), bm_o)
+
+
+# ------------------------------------------------------------------ whole step, edge cases
+
+def test_empty_scene_and_train_step():
+    sc = scenes.scene_small_random(40, 0, 40, 24, 0)
+    cam = sc.cameras[0]
+    params = PL.GaussianParams.from_scene(sc, DEV)
+    st = PL.TrainStep(params, cam.width, cam.height, DEV)
+    st.step(B.camera_from(cam), sc.targets[0].to(DEV))
+    torch.cuda.synchronize()
+    assert st.bins.n_isect == 0
+    assert float(st.frame.t_final.min()) == 1.0 and float(st.frame.color.abs().max()) == 0.0
+
+
+def test_train_step_composition():
+    """step() is exactly forward + loss + backward + adam (same kernels, same order)."""
+    sc = scenes.scene_small_random(41, 800, 80, 64, 2, extent=1.0)
+    cam = B.camera_from(sc.cameras[0])
+    tgt = sc.targets[0].to(DEV)
+    a = PL.TrainStep(PL.GaussianParams.from_scene(sc, DEV), 80, 64, DEV)
+    b = PL.TrainStep(PL.GaussianParams.from_scene(sc, DEV), 80, 64, DEV)
+    for _ in range(3):
+        a.step(cam, tgt)
+        b.forward(cam)
+        b.loss(tgt)
+        b.backward(cam)
+        b.adam()
+    torch.cuda.synchronize()
+    assert rel_l2(a.params.data.cpu().numpy(), b.params.data.cpu().numpy()) <= 1e-6
+    assert a.frame.loss.item() > 0
