@@ -170,7 +170,7 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
     if ((s = check_raster_inputs(proj, bins)) != GS_OK) return s;
-    if (!t_final || !n_trav || !dL_dcolor || !grads2d)
+    if (!t_final || !n_trav || !dL_dcolor || (g->n > 0 && !grads2d))
         return fail(GS_ERR_INVALID_ARGUMENT, "t_final / n_trav / dL_dcolor / grads2d is NULL");
     if (bins->capacity > 0 && !bins->ids) return fail(GS_ERR_INVALID_ARGUMENT, "ids is NULL");
     const int64_t n = g->n;

@@ -73,6 +73,7 @@ class GaussianParams:
 
 class Projection:
     def __init__(self, n, device="cuda"):
+        n = max(n, 1)   # the raster entry points take the record pointers even for an empty scene
         self.means2d = torch.zeros(n, 2, dtype=torch.float32, device=device)
         self.conic_opacity = torch.zeros(n, 4, dtype=torch.float32, device=device)
         self.color = torch.zeros(n, 3, dtype=torch.float32, device=device)
@@ -141,7 +142,7 @@ class TrainStep:
         self.proj = Projection(params.n, device)
         self.bins = Binning(params.n, width, height, capacity=capacity, device=device)
         self.frame = Frame(width, height, device)
-        self.grads2d = torch.zeros(9, params.n, dtype=torch.float32, device=device)
+        self.grads2d = torch.zeros(9, max(params.n, 1), dtype=torch.float32, device=device)
         self.lr = lr
 
     def forward(self, cam: B.Camera, stream=None):
