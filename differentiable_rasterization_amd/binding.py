@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP = range(5)
 TILE = 16
-EXPORTED = ("gs_project", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_raster_fwd", "gs_loss_workspace_bytes",
+EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_raster_fwd", "gs_loss_workspace_bytes",
             "gs_loss_l1", "gs_raster_bwd", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_last_error")
 
@@ -63,12 +63,12 @@ class Gaussians(ctypes.Structure):
 
 class Projected(ctypes.Structure):
     _fields_ = [("means2d", ctypes.c_void_p), ("conic_opacity", ctypes.c_void_p), ("color", ctypes.c_void_p),
-                ("depth", ctypes.c_void_p), ("radii", ctypes.c_void_p)]
+                ("depth", ctypes.c_void_p), ("radii", ctypes.c_void_p), ("rec", ctypes.c_void_p)]
 
 
 class Bins(ctypes.Structure):
     _fields_ = [("ids", ctypes.c_void_p), ("tile_ranges", ctypes.c_void_p), ("keys", ctypes.c_void_p),
-                ("tiles_touched", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+                ("tiles_touched", ctypes.c_void_p), ("capacity", ctypes.c_int64), ("raster", ctypes.c_void_p)]
 
 
 class ParamGrads(ctypes.Structure):
@@ -85,6 +85,7 @@ _P = ctypes.POINTER
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "gs_project": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _P(Projected), _vp]),
+    "gs_bins_raster_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "gs_bin_sort_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "gs_bin_sort": (_i32, [_P(Projected), _i64, _P(Camera), _P(Bins), _P(_i64), _vp, _sz, _vp]),
     "gs_raster_fwd": (_i32, [_P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp]),
@@ -153,12 +154,14 @@ def gaussians(means, log_scales, quats, opacity_logits, sh) -> Gaussians:
     return Gaussians(_ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh), n)
 
 
-def projected(means2d, conic_opacity, color, depth, radii) -> Projected:
-    return Projected(_ptr(means2d), _ptr(conic_opacity), _ptr(color), _ptr(depth), _ptr(radii))
+def projected(means2d, conic_opacity, color, depth, radii, rec) -> Projected:
+    return Projected(_ptr(means2d), _ptr(conic_opacity), _ptr(color), _ptr(depth), _ptr(radii), _ptr(rec))
 
 
-def bins(ids, tile_ranges, keys=None, tiles_touched=None) -> Bins:
-    return Bins(_ptr(ids), _ptr(tile_ranges), _ptr(keys), _ptr(tiles_touched), ids.numel())
+def bins(ids, tile_ranges, raster, keys=None, tiles_touched=None) -> Bins:
+    """ids [capacity] int32/uint32, tile_ranges [tiles+1] int32, raster: a uint8 device buffer of
+    gs_bins_raster_bytes(n, capacity, W, H) bytes."""
+    return Bins(_ptr(ids), _ptr(tile_ranges), _ptr(keys), _ptr(tiles_touched), ids.numel(), _ptr(raster))
 
 
 def param_grads(means, log_scales, quats, opacity_logits, sh) -> ParamGrads:
@@ -169,6 +172,10 @@ def param_grads(means, log_scales, quats, opacity_logits, sh) -> ParamGrads:
 
 def gs_project(g: Gaussians, cam: Camera, p: RasterParams, out: Projected, stream=None):
     _check(_lib.gs_project(ctypes.byref(g), ctypes.byref(cam), ctypes.byref(p), ctypes.byref(out), _stream(stream)))
+
+
+def gs_bins_raster_bytes(n, capacity, width, height) -> int:
+    return int(_lib.gs_bins_raster_bytes(n, capacity, width, height))
 
 
 def gs_bin_sort_workspace_bytes(n, capacity, width, height) -> int:

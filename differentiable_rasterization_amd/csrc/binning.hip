@@ -9,6 +9,7 @@
 // (1-2 eight-bit passes for up to 65536 tiles) leaves every tile's list in
 // (depth key, index) order.  Same result, roughly a quarter of the bytes.
 #include "kernels.h"
+#include "raster.h"
 
 namespace {
 
@@ -24,16 +25,18 @@ __global__ __launch_bounds__(256) void k_depth_keys(const int2 *__restrict__ rad
     vals[i] = (uint32_t)i;
 }
 
-// Tile counts of the Gaussians in depth order (0 for culled ones).
+// Tile counts of the Gaussians in depth order (0 for culled ones); also keeps the depth
+// order for the backward's per-Gaussian reduction.
 __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skeys, const uint32_t *__restrict__ svals,
                                                const float2 *__restrict__ means2d, const int2 *__restrict__ radii,
-                                               int64_t n, int tx, int ty, uint32_t *__restrict__ cnt)
+                                               int64_t n, int tx, int ty, uint32_t *__restrict__ cnt,
+                                               uint32_t *__restrict__ dsv)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n) return;
     uint32_t c = 0;
+    const uint32_t g = svals[j];
     if (skeys[j] != kCulledKey) {
-        const uint32_t g = svals[j];
         const float2 m = means2d[g];
         const int2 r = radii[g];
         int x0, x1, y0, y1;
@@ -41,13 +44,17 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skey
         c = (uint32_t)((x1 - x0) * (y1 - y0));
     }
     cnt[j] = c;
+    dsv[j] = g;
 }
 
-// Entries (tile id, Gaussian) of each Gaussian in depth order, tiles row-major.
+// Entries of each Gaussian in depth order, tiles row-major.  Entry p gets the key
+// tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at), the
+// value p (its emit position) and gauss[p] = its Gaussian.
 __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
                                               const uint32_t *__restrict__ off, const float2 *__restrict__ means2d,
                                               const int2 *__restrict__ radii, int64_t n, int tx, int ty,
-                                              uint32_t *__restrict__ tkeys, uint32_t *__restrict__ tvals)
+                                              uint32_t *__restrict__ tkeys, uint32_t *__restrict__ tvals,
+                                              uint32_t *__restrict__ gauss)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n || cnt[j] == 0) return;
@@ -59,23 +66,81 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
     uint32_t p = off[j];
     for (int y = y0; y < y1; ++y)
         for (int x = x0; x < x1; ++x) {
-            tkeys[p] = (uint32_t)(y * tx + x);
-            tvals[p] = g;
+            const uint32_t qm = gsr::quad_mask(m.x, m.y, r.x, r.y, (float)(x * GS_TILE), (float)(y * GS_TILE));
+            tkeys[p] = (uint32_t)(y * tx + x) | (qm << gsr::kMaskShift);
+            tvals[p] = p;
+            gauss[p] = g;
             ++p;
         }
 }
 
-// tile_ranges[t] = first entry of tile t (entries sorted by tile); ranges[T] = K.
-__global__ __launch_bounds__(256) void k_ranges(const uint32_t *__restrict__ tkeys, int64_t K, int32_t T,
-                                                int32_t *__restrict__ ranges)
+// Finishes the sorted lists in one pass over the entries: the Gaussian index of each
+// entry, tile_ranges[t] = first entry of tile t (entries are sorted by tile; ranges[T] =
+// K), and the quadrant bitmaps with their per-word bit counts (one 64-bit word per wave and
+// quadrant; block bases are multiples of 64).  `wcnt` [4][words + 1] must be zero
+// beforehand; its exclusive scan gives the positions of the quadrant records.
+__global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
+                                                const uint32_t *__restrict__ gauss, int64_t K, int32_t T,
+                                                uint32_t *__restrict__ ids, int32_t *__restrict__ ranges,
+                                                int64_t words, uint64_t *__restrict__ bitmap,
+                                                uint32_t *__restrict__ wcnt)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t qm = 0;
+    if (k < K) {
+        const uint32_t key = tkeys[k];
+        const int32_t t = (int32_t)(key & gsr::kTileMask);
+        qm = key >> gsr::kMaskShift;
+        ids[k] = gauss[spos[k]];
+        const int32_t prev = k > 0 ? (int32_t)(tkeys[k - 1] & gsr::kTileMask) : -1;
+        for (int32_t u = prev + 1; u <= t; ++u) ranges[u] = (int32_t)k;
+        if (k == K - 1)
+            for (int32_t u = t + 1; u <= T; ++u) ranges[u] = (int32_t)K;
+    }
+    const int64_t wbase = k - (threadIdx.x & 63);
+#pragma unroll
+    for (int q = 0; q < gsr::kQuads; ++q) {
+        const uint64_t b = __ballot((qm >> q) & 1u);
+        if ((threadIdx.x & 63) == 0 && wbase < K) {
+            bitmap[(int64_t)q * words + (wbase >> 6)] = b;
+            wcnt[(int64_t)q * (words + 1) + (wbase >> 6)] = (uint32_t)__popcll(b);
+        }
+    }
+}
+
+// Copies the projected record of every list entry into the record list of each quadrant
+// its box reaches, at the position given by the scanned bit counts, stamps the entry index
+// into it, and records that position in jmap under the entry's emit position.
+__global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
+                                                    const uint32_t *__restrict__ ids, int64_t K, int64_t words,
+                                                    const uint64_t *__restrict__ bitmap,
+                                                    const uint32_t *__restrict__ wpre,
+                                                    const float4 *__restrict__ prec, float4 *__restrict__ qrec,
+                                                    uint4 *__restrict__ jmap)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= K) return;
-    const int32_t t = (int32_t)tkeys[k];
-    const int32_t prev = k > 0 ? (int32_t)tkeys[k - 1] : -1;
-    for (int32_t u = prev + 1; u <= t; ++u) ranges[u] = (int32_t)k;
-    if (k == K - 1)
-        for (int32_t u = t + 1; u <= T; ++u) ranges[u] = (int32_t)K;
+    const uint32_t qm = tkeys[k] >> gsr::kMaskShift;
+    uint32_t pos[gsr::kQuads];
+#pragma unroll
+    for (int q = 0; q < gsr::kQuads; ++q)
+        pos[q] = ((qm >> q) & 1u) ? gsr::quad_prefix(bitmap + (int64_t)q * words, wpre + (int64_t)q * (words + 1),
+                                                      (uint32_t)k)
+                                  : ~0u;
+    jmap[spos[k]] = make_uint4(pos[0], pos[1], pos[2], pos[3]);
+    if (!qm) return;
+    const uint32_t g = ids[k];
+    const float4 a = prec[gsr::kRecF4 * (size_t)g], b = prec[gsr::kRecF4 * (size_t)g + 1];
+    float4 c = prec[gsr::kRecF4 * (size_t)g + 2];
+    c.z = __uint_as_float((uint32_t)k);
+#pragma unroll
+    for (int q = 0; q < gsr::kQuads; ++q) {
+        if (pos[q] == ~0u) continue;
+        float4 *d = qrec + gsr::kRecF4 * (size_t)pos[q];
+        d[0] = a;
+        d[1] = b;
+        d[2] = c;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_keys64(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ ids,
@@ -83,7 +148,7 @@ __global__ __launch_bounds__(256) void k_keys64(const uint32_t *__restrict__ tke
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= K) return;
-    keys[k] = ((uint64_t)tkeys[k] << 32) | (uint64_t)__float_as_uint(depth[ids[k]]);
+    keys[k] = ((uint64_t)(tkeys[k] & gsr::kTileMask) << 32) | (uint64_t)__float_as_uint(depth[ids[k]]);
 }
 
 __global__ __launch_bounds__(256) void k_touched(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
@@ -94,8 +159,37 @@ __global__ __launch_bounds__(256) void k_touched(const uint32_t *__restrict__ sv
     touched[svals[j]] = (int32_t)cnt[j];
 }
 
+// Tiles ordered by decreasing list length (bucketed by the bit length of the count, so
+// the order is heaviest first up to a factor of two), so that the longest tiles start
+// first and the short ones fill in behind them.  One workgroup.
+__global__ __launch_bounds__(1024) void k_tile_order(const int32_t *__restrict__ ranges, int T, int32_t *__restrict__ order)
+{
+    __shared__ uint32_t hist[33];
+    __shared__ uint32_t pos[33];
+    if (threadIdx.x < 33) hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int t = threadIdx.x; t < T; t += blockDim.x) {
+        const uint32_t c = (uint32_t)(ranges[t + 1] - ranges[t]);
+        atomicAdd(&hist[c ? 32 - __clz(c) : 0], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t acc = 0;
+        for (int b = 32; b >= 0; --b) {
+            pos[b] = acc;
+            acc += hist[b];
+        }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < T; t += blockDim.x) {
+        const uint32_t c = (uint32_t)(ranges[t + 1] - ranges[t]);
+        const uint32_t p = atomicAdd(&pos[c ? 32 - __clz(c) : 0], 1u);
+        order[p] = t;
+    }
+}
+
 struct Layout {
-    size_t dkA, dvA, dkB, dvB, cnt, off, total, tkA, tkB, tv, hist, part, bytes;
+    size_t dkA, dvA, dkB, dvB, cnt, total, tkA, tkB, tvA, tvB, gauss, hist, part, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -107,12 +201,13 @@ Layout layout(int64_t n, int64_t cap)
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     const size_t nn = (size_t)(n > 0 ? n : 1), cc = (size_t)(cap > 0 ? cap : 1);
     L.dkA = take(4 * nn); L.dvA = take(4 * nn); L.dkB = take(4 * nn); L.dvB = take(4 * nn);
-    L.cnt = take(4 * nn); L.off = take(4 * nn); L.total = take(8);
-    L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tv = take(4 * cc);
+    L.cnt = take(4 * nn); L.total = take(8);
+    L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(4 * cc); L.tvB = take(4 * cc); L.gauss = take(4 * cc);
     const int64_t mmax = std::max<int64_t>(n, cap);
     const int64_t hl = gsi::radix_hist_len(mmax);
     L.hist = take(4 * (size_t)hl);
-    const int64_t pl = std::max(gsi::scan_partials_len(hl), gsi::scan_partials_len(mmax));
+    const int64_t qwords = gsr::kQuads * (gsr::raster_layout(n, cap, 1).words + 1);   // quadrant bit-count scan
+    const int64_t pl = std::max({gsi::scan_partials_len(hl), gsi::scan_partials_len(mmax), gsi::scan_partials_len(qwords)});
     L.part = take(4 * (size_t)pl);
     L.bytes = o;
     return L;
@@ -126,6 +221,12 @@ int bits_for(int64_t maxval)
 }
 
 }  // namespace
+
+extern "C" size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height)
+{
+    if (n < 0 || capacity < 0 || width <= 0 || height <= 0) return 0;
+    return gsr::raster_layout(n, capacity, gsi::tiles_x(width) * gsi::tiles_y(height)).bytes;
+}
 
 extern "C" size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height)
 {
@@ -143,27 +244,40 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     if (!proj || !bins || !n_isect_out) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
     if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
     if (n > (int64_t(1) << 31) - 1) return fail(GS_ERR_UNSUPPORTED, "n >= 2^31");
-    if (bins->capacity < 0 || bins->capacity > 0xFFFFFFFFll)
-        return fail(GS_ERR_INVALID_ARGUMENT, "capacity out of range");
+    if (bins->capacity < 0 || bins->capacity > 0x3FFFFFFFll)
+        return fail(GS_ERR_INVALID_ARGUMENT, "capacity out of range (at most 2^30 entries)");
     if (!bins->tile_ranges || (bins->capacity > 0 && !bins->ids))
         return fail(GS_ERR_INVALID_ARGUMENT, "ids / tile_ranges is NULL");
+    if (!bins->raster || !aligned(bins->raster, 256))
+        return fail(GS_ERR_INVALID_ARGUMENT, "raster buffer is NULL or not 256-byte aligned");
     const int tx = tiles_x(cam->width), ty = tiles_y(cam->height);
     const int32_t T = tx * ty;
+    const gsr::RasterLayout RL = gsr::raster_layout(n, bins->capacity, T);
+    char *rb = static_cast<char *>(bins->raster);
+    int32_t *order = reinterpret_cast<int32_t *>(rb + RL.order);
+    uint32_t *dsv = reinterpret_cast<uint32_t *>(rb + RL.dsv), *doff = reinterpret_cast<uint32_t *>(rb + RL.doff);
     *n_isect_out = 0;
-    if (n == 0) return fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream);
+    if (n == 0) {
+        if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
+        k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
+        GS_LAUNCH_CHECK("k_tile_order");
+        return GS_OK;
+    }
     if (!proj->means2d || !proj->depth || !proj->radii)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected means2d / depth / radii is NULL");
-    if (!aligned(proj->means2d, 8) || !aligned(proj->radii, 8))
-        return fail(GS_ERR_INVALID_ARGUMENT, "means2d / radii must be 8-byte aligned");
+    if (!proj->rec) return fail(GS_ERR_INVALID_ARGUMENT, "projected rec is NULL");
+    if (!aligned(proj->means2d, 8) || !aligned(proj->radii, 8) || !aligned(proj->rec, 16))
+        return fail(GS_ERR_INVALID_ARGUMENT, "means2d / radii must be 8-byte, rec 16-byte aligned");
     const Layout L = layout(n, bins->capacity);
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.bytes)
         return fail(GS_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, 256-byte aligned", L.bytes);
     char *ws = static_cast<char *>(workspace);
     uint32_t *dkA = (uint32_t *)(ws + L.dkA), *dvA = (uint32_t *)(ws + L.dvA);
     uint32_t *dkB = (uint32_t *)(ws + L.dkB), *dvB = (uint32_t *)(ws + L.dvB);
-    uint32_t *cnt = (uint32_t *)(ws + L.cnt), *off = (uint32_t *)(ws + L.off);
+    uint32_t *cnt = (uint32_t *)(ws + L.cnt);
     unsigned long long *total = (unsigned long long *)(ws + L.total);
-    uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB), *tv = (uint32_t *)(ws + L.tv);
+    uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB);
+    uint32_t *tvA = (uint32_t *)(ws + L.tvA), *tvB = (uint32_t *)(ws + L.tvB), *gauss = (uint32_t *)(ws + L.gauss);
     uint32_t *hist = (uint32_t *)(ws + L.hist), *part = (uint32_t *)(ws + L.part);
     const float2 *m2 = reinterpret_cast<const float2 *>(proj->means2d);
     const int2 *rr = reinterpret_cast<const int2 *>(proj->radii);
@@ -176,15 +290,14 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     if ((s = radix_sort_u32(dkA, dvA, dkB, dvB, n, 32, hist, part, &in_b, stream)) != GS_OK) return s;
     const uint32_t *sk = in_b ? dkB : dkA, *sv = in_b ? dvB : dvA;
 
-    // 2. tile counts in depth order, their exclusive scan, and the total K
-    k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, n, tx, ty, cnt);
+    // 2. tile counts in depth order, their exclusive scan (the emit offsets) and the total K
+    k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, n, tx, ty, cnt, dsv);
     GS_LAUNCH_CHECK("k_count");
-    if ((s = exclusive_scan_u32(cnt, off, n, part, total, stream)) != GS_OK) return s;
+    if ((s = exclusive_scan_u32(cnt, doff, n, part, total, stream)) != GS_OK) return s;
     unsigned long long K = 0;
     GS_HIP(hipMemcpyAsync(&K, total, sizeof(K), hipMemcpyDeviceToHost, stream));
     GS_HIP(hipStreamSynchronize(stream));
     *n_isect_out = (int64_t)K;
-    if (K > 0xFFFFFFFFull) return fail(GS_ERR_UNSUPPORTED, "more than 2^32 intersections");
     if ((int64_t)K > bins->capacity)
         return fail(GS_ERR_CAPACITY, "%llu intersections exceed the capacity %lld", K, (long long)bins->capacity);
 
@@ -192,29 +305,42 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
         k_touched<<<gn, 256, 0, stream>>>(sv, cnt, n, bins->tiles_touched);
         GS_LAUNCH_CHECK("k_touched");
     }
-    if (K == 0) return fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream);
-
-    // 3. emit entries in depth order, then a stable sort by tile id
-    const int tbits = std::max(1, bits_for(T - 1));
-    const int passes = (tbits + 7) / 8;
-    uint32_t *ev = (passes % 2 == 1) ? tv : bins->ids;     // the last pass lands in bins->ids
-    uint32_t *ov = (passes % 2 == 1) ? bins->ids : tv;
-    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, off, m2, rr, n, tx, ty, tkA, ev);
-    GS_LAUNCH_CHECK("k_emit");
-    if ((s = radix_sort_u32(tkA, ev, tkB, ov, (int64_t)K, tbits, hist, part, &in_b, stream)) != GS_OK) return s;
-    const uint32_t *tk = in_b ? tkB : tkA;
-    if (K == 1 && ev != bins->ids) {
-        // a single entry is not moved by the sort
-        GS_HIP(hipMemcpyAsync(bins->ids, ev, 4, hipMemcpyDeviceToDevice, stream));
+    if (K == 0) {
+        if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
+        k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
+        GS_LAUNCH_CHECK("k_tile_order");
+        return GS_OK;
     }
 
-    // 4. per-tile ranges, optional 64-bit keys
+    // 3. emit entries in depth order, then a stable sort of (tile key, emit position) by tile
+    const int tbits = std::max(1, bits_for(T - 1));
+    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, m2, rr, n, tx, ty, tkA, tvA, gauss);
+    GS_LAUNCH_CHECK("k_emit");
+    if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, (int64_t)K, tbits, hist, part, &in_b, stream)) != GS_OK) return s;
+    const uint32_t *tk = in_b ? tkB : tkA, *spos = in_b ? tvB : tvA;
+
+    // 4. ids, per-tile ranges, quadrant bitmaps and their scanned bit counts, the quadrant
+    //    record lists and the emit-position map; optional 64-bit keys
     const unsigned gk = (unsigned)ceil_div((int64_t)K, 256);
-    k_ranges<<<gk, 256, 0, stream>>>(tk, (int64_t)K, T, bins->tile_ranges);
-    GS_LAUNCH_CHECK("k_ranges");
+    uint64_t *bm = reinterpret_cast<uint64_t *>(rb + RL.bitmap);
+    uint32_t *wpre = reinterpret_cast<uint32_t *>(rb + RL.wpre);
+    const int64_t nw = gsr::kQuads * (RL.words + 1);
+    if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre), nw, 0, stream)) != GS_OK) return s;
+    k_finish<<<gk, 256, 0, stream>>>(tk, spos, gauss, (int64_t)K, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
+    GS_LAUNCH_CHECK("k_finish");
+    if ((s = exclusive_scan_u32(wpre, wpre, nw, part, nullptr, stream)) != GS_OK) return s;
+    k_quad_lists<<<gk, 256, 0, stream>>>(tk, spos, bins->ids, (int64_t)K, RL.words, bm, wpre,
+                                         reinterpret_cast<const float4 *>(proj->rec),
+                                         reinterpret_cast<float4 *>(rb + RL.qrec),
+                                         reinterpret_cast<uint4 *>(rb + RL.jmap));
+    GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {
         k_keys64<<<gk, 256, 0, stream>>>(tk, bins->ids, proj->depth, (int64_t)K, bins->keys);
         GS_LAUNCH_CHECK("k_keys64");
     }
+
+    // 5. the order in which tiles are rasterized
+    k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
+    GS_LAUNCH_CHECK("k_tile_order");
     return GS_OK;
 }

@@ -211,7 +211,8 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
                                                  const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
                                                  float depth_lo, float depth_hi, float2 *__restrict__ means2d,
                                                  float4 *__restrict__ conic_o, float *__restrict__ color,
-                                                 float *__restrict__ depth, int2 *__restrict__ radii)
+                                                 float *__restrict__ depth, int2 *__restrict__ radii,
+                                                 float4 *__restrict__ rec)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -245,6 +246,12 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
     color[3 * i + 0] = r;
     color[3 * i + 1] = g;
     color[3 * i + 2] = b;
+    // raster-ready copy: conic scaled for exp2, log2 of the stored opacity
+    constexpr double kL2e = 1.4426950408889634;
+    const double o32 = (double)(float)P.o;
+    rec[3 * i + 0] = make_float4((float)P.u, (float)P.v, (float)(-0.5 * kL2e * P.A), (float)(-kL2e * P.B));
+    rec[3 * i + 1] = make_float4((float)(-0.5 * kL2e * P.C), (float)log2(o32), r, g);
+    rec[3 * i + 2] = make_float4(b, __uint_as_float((uint32_t)i), 0.0f, 0.0f);
 }
 
 // Backward through projection and colour evaluation (ByteSplat, section 2.1: the
@@ -432,10 +439,11 @@ extern "C" gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, con
     if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "out is NULL");
     const int64_t n = g->n;
     if (n == 0) return GS_OK;
-    if (!out->means2d || !out->conic_opacity || !out->color || !out->depth || !out->radii)
+    if (!out->means2d || !out->conic_opacity || !out->color || !out->depth || !out->radii || !out->rec)
         return fail(GS_ERR_INVALID_ARGUMENT, "a projected-record pointer is NULL");
-    if (!aligned(out->conic_opacity, 16) || !aligned(out->means2d, 8) || !aligned(out->radii, 8))
-        return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity must be 16-byte, means2d/radii 8-byte aligned");
+    if (!aligned(out->conic_opacity, 16) || !aligned(out->rec, 16) || !aligned(out->means2d, 8) ||
+        !aligned(out->radii, 8))
+        return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity/rec must be 16-byte, means2d/radii 8-byte aligned");
     const CamD cd = make_cam(cam);
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
     float2 *m2 = reinterpret_cast<float2 *>(out->means2d);
@@ -444,7 +452,7 @@ extern "C" gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, con
 #define GS_PF(D)                                                                                        \
     k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
                                              cd, p->alpha_min, p->depth_lo, p->depth_hi, m2, co, out->color,  \
-                                             out->depth, rr)
+                                             out->depth, rr, reinterpret_cast<float4 *>(out->rec))
     switch (p->sh_degree) {
     case 0: GS_PF(0); break;
     case 1: GS_PF(1); break;

@@ -1,51 +1,132 @@
-// Shared definitions of the forward and backward rasterization kernels.
+// Shared definitions of the binning's raster-ready lists and the forward / backward
+// rasterization kernels.
 //
-// Layout: one 64-lane wave per 16x16 tile.  Lane l owns the four pixels of column
-// l % 16, rows 4*(l / 16) .. 4*(l / 16) + 3 of the tile.  The tile's list is staged
-// through LDS 64 entries at a time (one gather per lane); every lane then walks the
-// batch reading each entry as an LDS broadcast, so one LDS read serves four pixels.
+// Raster-ready lists (the gs_bins.raster buffer, written by gs_bin_sort):
+//   qrec   [4 * capacity] Rec     for each 8x8 quadrant q of every tile (qx = q & 1,
+//                                 qy = q >> 1), the records of the tile's entries whose
+//                                 alpha >= alpha_min box reaches the quadrant, in list
+//                                 order; quadrant 0's lists of all tiles in tile order, then
+//                                 quadrant 1's, ...
+//   bitmap [4][words] uint64      bit k of bitmap q is set if list entry k is in quadrant q
+//   wpre   [4][words + 1] uint32  exclusive prefix count over all four bitmaps, word by
+//                                 word, so the records of tile t in quadrant q are
+//                                 qrec[P_q(start_t) .. P_q(end_t)), P_q(x) = wpre[q][x / 64]
+//                                 + set bits of bitmap q below entry x in its word
+//   order  [tiles] int32          tiles by decreasing list length (heaviest first)
+//   dsv    [n] uint32             Gaussians in depth order (culled ones last)
+//   doff   [n] uint32             first emitted entry of each Gaussian in that order: the
+//                                 entries of Gaussian dsv[r] were emitted at positions
+//                                 doff[r] .. doff[r + 1] (doff[n] = K)
+//   jmap   [4 * capacity] uint32  position in qrec of emitted entry p's record in quadrant q
+//                                 (index 4 p + q), or ~0 if the entry is not in quadrant q
+//   qgrad  [4 * capacity][9] f32  the backward's per-record partial gradients
+//
+// Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
+// (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of records with
+// scalar loads, several records per load batch: the records are uniform across the wave,
+// so they live in SGPRs and feed the vector ALU as operands, with no LDS traffic and no
+// per-entry relevance test.
 #pragma once
 
 #include "common.h"
 
 namespace gsr {
 
-constexpr int kBatch = 64;
-constexpr int kPix = 4;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQuads = 4;
 
-// One list entry in the form the inner loop uses.  The alpha exponent is evaluated
-// base 2: with (dx, dy) = pixel centre - mean,
-//   o exp(-A dx^2/2 - B dx dy - C dy^2/2) = exp2(a dx^2 + b dx dy + c dy^2 + l)
-// where a = -log2(e) A / 2, b = -log2(e) B, c = -log2(e) C / 2, l = log2(o).
-struct Entry {
-    float4 p0;   // u, v, a, b
-    float4 p1;   // c, l, r, g
-    float4 p2;   // blue, A, B, C
-    float4 p3;   // 1/o, -, -, -
+// Record layout (48 bytes; written per Gaussian by the projection, copied per quadrant
+// list entry by the binning).  With (dx, dy) = pixel centre - mean, the alpha exponent is
+// evaluated base 2:  o exp(-A dx^2/2 - B dx dy - C dy^2/2) = exp2(a dx^2 + b dx dy + c dy^2 + l)
+// with a = -log2(e) A / 2, b = -log2(e) B, c = -log2(e) C / 2, l = log2(o).
+//   p0 = (u, v, a, b)   p1 = (c, l, red, green)   p2 = (blue, index bits, entry bits, 0)
+// "entry" is the record's position k in the 16x16 tile lists (set by the binning).
+// The backward recovers A = -2 ln(2) a, B = -ln(2) b, C = -2 ln(2) c and 1/o = exp2(-l).
+struct Rec {
+    float4 p0, p1, p2;
 };
+constexpr int kRecF4 = 3;   // float4 words per record
+constexpr float kLn2 = 0.69314718055994531f;
 
-__device__ __forceinline__ Entry make_entry(uint32_t g, const float2 *__restrict__ means2d,
-                                            const float4 *__restrict__ conic_o, const float *__restrict__ color)
+// Quadrant mask of an entry lives in bits 24..27 of its 32-bit tile key during the sort
+// (tile ids use at most 24 bits and only those are sorted).
+constexpr int kMaskShift = 24;
+constexpr uint32_t kTileMask = (1u << kMaskShift) - 1u;
+
+// Bit q of the result is set if the box [u - rx, u + rx] x [v - ry, v + ry] reaches a pixel
+// centre of 8x8 quadrant q (qx = q & 1, qy = q >> 1) of the tile with pixel origin
+// (x0, y0).  Outside that box alpha < alpha_min exactly; the margin is far above rounding.
+__device__ __forceinline__ uint32_t quad_mask(float u, float v, int rx, int ry, float x0, float y0)
 {
-    const float2 m = means2d[g];
-    const float4 co = conic_o[g];
-    const float r = color[3 * (size_t)g], gg = color[3 * (size_t)g + 1], b = color[3 * (size_t)g + 2];
-    Entry e;
-    e.p0 = make_float4(m.x, m.y, -0.5f * kLog2e * co.x, -kLog2e * co.y);
-    e.p1 = make_float4(-0.5f * kLog2e * co.z, __builtin_amdgcn_logf(co.w), r, gg);
-    e.p2 = make_float4(b, co.x, co.y, co.z);
-    e.p3 = make_float4(__builtin_amdgcn_rcpf(co.w), 0.0f, 0.0f, 0.0f);
-    return e;
+    const float margin = 0.01f;
+    bool mx[2], my[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float lo = 8.0f * h + 0.5f - margin, hi = 8.0f * h + 7.5f + margin;
+        mx[h] = (u - (float)rx) - x0 <= hi && (u + (float)rx) - x0 >= lo;
+        my[h] = (v - (float)ry) - y0 <= hi && (v + (float)ry) - y0 >= lo;
+    }
+    return (uint32_t)(mx[0] && my[0]) | ((uint32_t)(mx[1] && my[0]) << 1) | ((uint32_t)(mx[0] && my[1]) << 2) |
+           ((uint32_t)(mx[1] && my[1]) << 3);
 }
 
-// exp2 exponent of entry (p0, p1) at a pixel: `base` = a dx^2 + l and `bdx` = b dx are
-// shared by the four pixels of a lane (same column).
-__device__ __forceinline__ float exponent(float base, float bdx, float c, float dy)
+struct RasterLayout {
+    size_t qrec, bitmap, wpre, order, dsv, doff, jmap, qgrad, bytes;
+    int64_t cap, words;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
 {
-    return fmaf(c * dy, dy, fmaf(bdx, dy, base));
+    RasterLayout L;
+    L.cap = capacity > 0 ? capacity : 1;
+    L.words = (L.cap + 63) / 64;
+    const size_t nn = (size_t)(n > 0 ? n : 1), q4 = (size_t)kQuads * (size_t)L.cap;
+    size_t o = 0;
+    L.qrec = o;   o += align256(q4 * sizeof(Rec));
+    L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
+    L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);
+    L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);
+    L.dsv = o;    o += align256(nn * 4);
+    L.doff = o;   o += align256(nn * 4);
+    L.jmap = o;   o += align256(q4 * 4);
+    L.qgrad = o;  o += align256(q4 * 9 * 4);
+    L.bytes = o;
+    return L;
+}
+
+// Number of entries below x (0 <= x <= K) that belong to quadrant q: the position in
+// qrec[q] of the first record at or after entry x.  bq = bitmap + q * words,
+// wq = wpre + q * (words + 1).
+__device__ __forceinline__ uint32_t quad_prefix(const uint64_t *__restrict__ bq, const uint32_t *__restrict__ wq,
+                                                uint32_t x)
+{
+    const uint32_t w = x >> 6, r = x & 63u;
+    uint32_t p = wq[w];
+    if (r) p += (uint32_t)__popcll(bq[w] & ((1ull << r) - 1ull));
+    return p;
+}
+
+// Launch geometry shared by both raster kernels: 4 consecutive "slots" on the same XCD
+// are the 4 quadrants of one tile; tiles are interleaved over the 8 XCDs (block b runs
+// on XCD b mod 8) so that heavy tiles, which cluster spatially, spread over the chip.
+inline int64_t raster_grid(int tiles) { return (int64_t)gsi::kXcds * kQuads * gsi::ceil_div(tiles, gsi::kXcds); }
+
+__device__ __forceinline__ void raster_block(int &tile_idx, int &quad)
+{
+    const int b = blockIdx.x;
+    const int slot = b >> 3;
+    tile_idx = (b & 7) + 8 * (slot >> 2);
+    quad = slot & 3;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2 exponent of a record at pixel offset (dx, dy).
+__device__ __forceinline__ float exponent(const float4 &p0, const float4 &p1, float dx, float dy)
+{
+    return fmaf(p0.z * dx, dx, fmaf(p0.w * dx, dy, fmaf(p1.x * dy, dy, p1.y)));
+}
 
 }  // namespace gsr

@@ -6,13 +6,27 @@
 //   dL/dalpha_i = T_i (c_i - B_i) . G - G_T T_final / (1 - alpha_i),
 //                 B_i = colour composited behind i (B = 0 after the last entry,
 //                 B_{i-1} = alpha_i c_i + (1 - alpha_i) B_i)
-//   unclamped alpha only: dL/do = dL/dalpha alpha / o, dL/dpower = dL/dalpha alpha,
+//   unclamped alpha only: dL/dpower = dL/dalpha alpha, dL/do = dL/dpower / o,
 //   dA = -dx^2/2 dpower, dB = -dx dy dpower, dC = -dy^2/2 dpower,
 //   du = (A dx + B dy) dpower, dv = (B dx + C dy) dpower.
-// Aggregation over pixels (Eq. 4): the four pixels of a lane share dx, so their
-// contributions are first folded in registers, then summed over the wave with DPP
-// (skipped when no lane of the wave touched the entry), and one lane per tile adds
-// the tile's total for each entry to global memory with float atomics.
+// Aggregation over pixels (Eq. 4), without atomics: each lane forms the per-pixel moments
+//   S0 = dpower, Sx = dx S0, Sy = dy S0, Sxx = dx Sx, Sxy = dy Sx, Syy = dy Sy and the
+//   colour terms T_i alpha_i G for 4 records at a time, the wave sums the 36 values in one
+//   transpose-reduction (v_permlane32_swap, v_permlane16_swap, then a 4-step DPP butterfly
+//   within each 16-lane row, so row e ends with the totals of record e), and lane (e, f)
+//   turns them into field f of record e,
+//   du = A Sx + B Sy, dv = B Sx + C Sy, dA = -Sxx/2, dB = -Sxy, dC = -Syy/2, do = S0 / o,
+//   and stores it in the record's slot of the per-record gradient buffer (one store
+//   instruction for the 36 values).  A second kernel then sums, for every Gaussian, the
+//   slots of its records (found through the emit-position map): the sum of Eq. 4 in a
+//   fixed order, so the gradients are deterministic.
+//
+// Lanes that do not take an entry run the same instructions with alpha = 0, which leaves
+// T and the colour behind unchanged and contributes zeros (no divergent branches).
+//
+// One wave per 8x8 quadrant (see raster.h), walking its tile's record list for the
+// quadrant back to front from the furthest entry any of its pixels traversed; the slots
+// of the records behind that point are set to zero.
 #include "kernels.h"
 #include "raster.h"
 
@@ -20,143 +34,202 @@ namespace {
 
 using namespace gsr;
 
-template <bool HAS_GT>
-__global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ ranges, const uint32_t *__restrict__ ids,
-                                                   const float2 *__restrict__ means2d,
-                                                   const float4 *__restrict__ conic_o, const float *__restrict__ color,
-                                                   int W, int H, int TX, int T, int per_xcd, float alpha_min,
-                                                   float alpha_max, const float *__restrict__ t_final,
-                                                   const int32_t *__restrict__ n_trav,
-                                                   const float *__restrict__ dL_dc, const float *__restrict__ dL_dt,
-                                                   float *__restrict__ grads2d, int64_t n)
+constexpr int kBwdBatch = 4;   // entries per transpose-reduction (4 x 9 values -> 4 rows of 16 lanes)
+constexpr int kFields = 9;
+
+__device__ __forceinline__ float swap_add32(float &x, float &y)
 {
-    __shared__ float4 s0[kBatch], s1[kBatch], s2[kBatch], s3[kBatch];
-    __shared__ float sacc[9][kBatch];
-    __shared__ int sflag[kBatch];
-    __shared__ uint32_t sid[kBatch];
-    const int tile = (blockIdx.x % gsi::kXcds) * per_xcd + blockIdx.x / gsi::kXcds;
-    if (tile >= T) return;
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float swap_add16(float &x, float &y)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the 16 lanes of each row, result in every lane of the row.
+__device__ __forceinline__ float row_sum16(float v)
+{
+    using namespace gsd;
+    // old = 0 (the identity of +) lets the compiler fold each move into a DPP add
+    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kQuadSwap1, 0xF, 0xF, false));
+    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kQuadSwap2, 0xF, 0xF, false));
+    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kRowHalfMirror, 0xF, 0xF, false));
+    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kRowMirror, 0xF, 0xF, false));
+    return v;
+}
+
+// v[e * 9 + f] holds this lane's value of field f of entry e (e < 4).  Afterwards v[f]
+// (f < 9) holds, in every lane of row e, the sum over all 64 lanes of field f of entry e.
+__device__ __forceinline__ void reduce_4x9(float (&v)[kBwdBatch * kFields])
+{
+#pragma unroll
+    for (int i = 0; i < 18; ++i) v[i] = swap_add32(v[i], v[i + 18]);   // lanes < 32: slot i, else slot i + 18
+#pragma unroll
+    for (int i = 0; i < 9; ++i) v[i] = swap_add16(v[i], v[i + 9]);     // row r: slot i + 9 r
+#pragma unroll
+    for (int i = 0; i < 9; ++i) v[i] = row_sum16(v[i]);
+}
+
+// Per-lane choice of one of four wave-uniform values by the lane's row (lane >> 4).
+__device__ __forceinline__ float by_row(int row, float a0, float a1, float a2, float a3)
+{
+    const float lo = (row & 1) ? a1 : a0, hi = (row & 1) ? a3 : a2;
+    return (row & 2) ? hi : lo;
+}
+
+template <bool HAS_GT>
+__global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ ranges, const int32_t *__restrict__ order,
+                                                   const float4 *__restrict__ qrec, const uint64_t *__restrict__ bitmap,
+                                                   const uint32_t *__restrict__ wpre, int64_t words, int W, int H,
+                                                   int TX, int T, float alpha_min, float alpha_max,
+                                                   const float *__restrict__ t_final, const int32_t *__restrict__ n_trav,
+                                                   const float *__restrict__ dL_dc, const float *__restrict__ dL_dt,
+                                                   float *__restrict__ qgrad)
+{
+    int tidx, q;
+    raster_block(tidx, q);
+    if (tidx >= T) return;
+    const int tile = order[tidx];
     const int lane = threadIdx.x;
-    const int px = (tile % TX) * GS_TILE + (lane & 15);
-    const int py0 = (tile / TX) * GS_TILE + (lane >> 4) * kPix;
-    const float fx = (float)px + 0.5f;
-    float fy[kPix], Tr[kPix], Tf[kPix], G0[kPix], G1[kPix], G2[kPix], GT[kPix], B0[kPix], B1[kPix], B2[kPix];
-    int np[kPix];
-    int nmax = 0;
-#pragma unroll
-    for (int k = 0; k < kPix; ++k) {
-        const int py = py0 + k;
-        fy[k] = (float)py + 0.5f;
-        B0[k] = B1[k] = B2[k] = 0.0f;
-        if (px < W && py < H) {
-            const size_t idx = (size_t)py * W + px;
-            Tr[k] = Tf[k] = t_final[idx];
-            np[k] = n_trav[idx];
-            G0[k] = dL_dc[3 * idx];
-            G1[k] = dL_dc[3 * idx + 1];
-            G2[k] = dL_dc[3 * idx + 2];
-            GT[k] = HAS_GT ? dL_dt[idx] : 0.0f;
-        } else {
-            Tr[k] = Tf[k] = 1.0f;
-            np[k] = 0;
-            G0[k] = G1[k] = G2[k] = GT[k] = 0.0f;
-        }
-        nmax = max(nmax, np[k]);
+    const int px = (tile % TX) * GS_TILE + (q & 1) * 8 + (lane & 7);
+    const int py = (tile / TX) * GS_TILE + (q >> 1) * 8 + (lane >> 3);
+    const bool inside = px < W && py < H;
+    const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
+    float Tr = 1.0f, G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, gtf = 0.0f;
+    int np = 0;
+    if (inside) {
+        const size_t idx = (size_t)py * W + px;
+        Tr = t_final[idx];
+        np = n_trav[idx];
+        G0 = dL_dc[3 * idx];
+        G1 = dL_dc[3 * idx + 1];
+        G2 = dL_dc[3 * idx + 2];
+        if (HAS_GT) gtf = dL_dt[idx] * Tr;
     }
-    nmax = gsd::wave_max_i32(nmax);
-    const int start = ranges[tile];
-    nmax = min(nmax, ranges[tile + 1] - start);   // n_trav never exceeds the list; guard against misuse
-    for (int bend = start + nmax; bend > start; bend -= kBatch) {
-        const int b0 = max(start, bend - kBatch);
-        const int cnt = bend - b0;
-        if (lane < cnt) {
-            const uint32_t gid = ids[b0 + lane];
-            const Entry en = make_entry(gid, means2d, conic_o, color);
-            sid[lane] = gid;
-            s0[lane] = en.p0;
-            s1[lane] = en.p1;
-            s2[lane] = en.p2;
-            s3[lane] = en.p3;
+    const int start = ranges[tile], end = ranges[tile + 1];
+    // the wave walks back from the furthest entry any of its pixels traversed
+    const int nmax = max(0, min(gsd::wave_max_i32(np), end - start));
+    const uint64_t *bq = bitmap + (int64_t)q * words;
+    const uint32_t *wq = wpre + (int64_t)q * (words + 1);
+    const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)(start + nmax));
+    const uint32_t jend = quad_prefix(bq, wq, (uint32_t)end);
+    // records never reached by any pixel of the quadrant contribute nothing
+    for (size_t z = (size_t)j1 * kFields + lane; z < (size_t)jend * kFields; z += 64) qgrad[z] = 0.0f;
+    const int row = lane >> 4, field = lane & 15;
+    float B0 = 0.0f, B1 = 0.0f, B2 = 0.0f;
+    for (uint32_t jt = j1; jt > j0;) {
+        // records jt-1, jt-2, ... (back to front); one wait per batch
+        float4 p0[kBwdBatch], p1[kBwdBatch];
+        float blue[kBwdBatch], kent[kBwdBatch];
+#pragma unroll
+        for (int i = 0; i < kBwdBatch; ++i) {
+            const uint32_t r = jt - 1u - min((uint32_t)i, jt - 1u - j0);   // before j0: repeat the first (unused)
+            p0[i] = qrec[kRecF4 * (size_t)r];
+            p1[i] = qrec[kRecF4 * (size_t)r + 1];
+            const float4 p2 = qrec[kRecF4 * (size_t)r + 2];
+            blue[i] = p2.x;
+            kent[i] = p2.z;
         }
-        __syncthreads();
-        for (int j = cnt - 1; j >= 0; --j) {
-            const int rel = b0 + j - start;
-            const float4 p0 = s0[j], p1 = s1[j], p2 = s2[j];
-            const float inv_o = s3[j].x;
-            const float dx = fx - p0.x;
-            const float base = fmaf(p0.z * dx, dx, p1.y);
-            const float bdx = p0.w * dx;
-            float sum0 = 0.0f, sum1 = 0.0f, sum2 = 0.0f, s_o = 0.0f, s_r = 0.0f, s_g = 0.0f, s_b = 0.0f;
-            bool touched = false;
 #pragma unroll
-            for (int k = 0; k < kPix; ++k) {
-                const float dy = fy[k] - p0.y;
-                const float raw = exp2_fast(exponent(base, bdx, p1.x, dy));
-                const float alpha = fminf(alpha_max, raw);
-                if (rel < np[k] && alpha >= alpha_min) {
-                    const float om = 1.0f - alpha;
-                    const float Ti = Tr[k] * __builtin_amdgcn_rcpf(om);
-                    const float w = Ti * alpha;
-                    s_r = fmaf(w, G0[k], s_r);
-                    s_g = fmaf(w, G1[k], s_g);
-                    s_b = fmaf(w, G2[k], s_b);
-                    float dal = Ti * ((p1.z - B0[k]) * G0[k] + (p1.w - B1[k]) * G1[k] + (p2.x - B2[k]) * G2[k]);
-                    if (HAS_GT) dal -= GT[k] * Tf[k] * __builtin_amdgcn_rcpf(om);
-                    if (raw < alpha_max) {
-                        const float dpow = dal * alpha;
-                        s_o = fmaf(dpow, inv_o, s_o);
-                        sum0 += dpow;
-                        sum1 = fmaf(dy, dpow, sum1);
-                        sum2 = fmaf(dy * dy, dpow, sum2);
-                    }
-                    B0[k] = fmaf(alpha, p1.z - B0[k], B0[k]);
-                    B1[k] = fmaf(alpha, p1.w - B1[k], B1[k]);
-                    B2[k] = fmaf(alpha, p2.x - B2[k], B2[k]);
-                    Tr[k] = Ti;
-                    touched = true;
-                }
-            }
-            if (__ballot(touched) == 0) {
-                if (lane == 63) sflag[j] = 0;
-                continue;
-            }
-            // fold the four pixels into the 9 fields: (u, v, A, B, C, o, r, g, b)
-            const float A = p2.y, Bc = p2.z, C = p2.w;
-            float f[9];
-            f[0] = fmaf(A * dx, sum0, Bc * sum1);
-            f[1] = fmaf(Bc * dx, sum0, C * sum1);
-            f[2] = -0.5f * dx * dx * sum0;
-            f[3] = -dx * sum1;
-            f[4] = -0.5f * sum2;
-            f[5] = s_o;
-            f[6] = s_r;
-            f[7] = s_g;
-            f[8] = s_b;
+        for (int i = 0; i < kBwdBatch; ++i)
+            asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
+                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]));
+        const uint32_t cnt = min((uint32_t)kBwdBatch, jt - j0);
+        float v[kBwdBatch * kFields];
+        bool any = false;
 #pragma unroll
-            for (int q = 0; q < 9; ++q) f[q] = gsd::wave_sum_to_lane63(f[q]);
-            if (lane == 63) {
-#pragma unroll
-                for (int q = 0; q < 9; ++q) sacc[q][j] = f[q];
-                sflag[j] = 1;
-            }
+        for (int i = 0; i < kBwdBatch; ++i) {
+            float *o = v + kFields * i;
+            const int rel = (int)__float_as_uint(kent[i]) - start;
+            const float dx = fx - p0[i].x, dy = fy - p0[i].y;
+            const float raw = exp2_fast(exponent(p0[i], p1[i], dx, dy));
+            const bool acc = (uint32_t)i < cnt && rel < np && raw >= alpha_min;   // alpha >= alpha_min
+            const float alpha = acc ? fminf(alpha_max, raw) : 0.0f;
+            const float ro = __builtin_amdgcn_rcpf(1.0f - alpha);
+            const float Ti = Tr * ro;
+            const float w = Ti * alpha;
+            o[6] = w * G0;
+            o[7] = w * G1;
+            o[8] = w * G2;
+            float dal = Ti * ((p1[i].z - B0) * G0 + (p1[i].w - B1) * G1 + (blue[i] - B2) * G2);
+            if (HAS_GT) dal -= gtf * ro;
+            const float s0 = raw < alpha_max ? dal * alpha : 0.0f;   // clamped alpha has no power gradient
+            o[0] = s0;
+            o[1] = dx * s0;
+            o[2] = dy * s0;
+            o[3] = dx * o[1];
+            o[4] = dy * o[1];
+            o[5] = dy * o[2];
+            B0 = fmaf(alpha, p1[i].z - B0, B0);
+            B1 = fmaf(alpha, p1[i].w - B1, B1);
+            B2 = fmaf(alpha, blue[i] - B2, B2);
+            Tr = acc ? Ti : Tr;
+            any |= acc;
         }
-        __syncthreads();
-        if (lane < cnt && sflag[lane]) {
-            const uint32_t g = sid[lane];
-#pragma unroll
-            for (int q = 0; q < 9; ++q) {
-                const float v = sacc[q][lane];
-                if (v != 0.0f) atomicAdd(grads2d + (size_t)q * n + g, v);
-            }
+        // slot of the batch's record e = row: record jt - 1 - e, field f = lane & 15
+        float *dst = qgrad + ((size_t)(jt - 1u - (uint32_t)min(row, (int)cnt - 1))) * kFields + field;
+        const bool writer = (uint32_t)row < cnt && field < kFields;
+        jt -= cnt;
+        if (__ballot(any) == 0) {
+            if (writer) *dst = 0.0f;
+            continue;
         }
-        __syncthreads();
+        reduce_4x9(v);
+        const float a = by_row(row, p0[0].z, p0[1].z, p0[2].z, p0[3].z);
+        const float b = by_row(row, p0[0].w, p0[1].w, p0[2].w, p0[3].w);
+        const float c = by_row(row, p1[0].x, p1[1].x, p1[2].x, p1[3].x);
+        const float l = by_row(row, p1[0].y, p1[1].y, p1[2].y, p1[3].y);
+        const float A = -2.0f * kLn2 * a, B = -kLn2 * b, C = -2.0f * kLn2 * c;
+        float val = fmaf(A, v[1], B * v[2]);                        // du
+        val = field == 1 ? fmaf(B, v[1], C * v[2]) : val;           // dv
+        val = field == 2 ? -0.5f * v[3] : val;                      // dA
+        val = field == 3 ? -v[4] : val;                             // dB
+        val = field == 4 ? -0.5f * v[5] : val;                      // dC
+        val = field == 5 ? v[0] * exp2_fast(-l) : val;              // do
+        val = field == 6 ? v[6] : val;                              // red
+        val = field == 7 ? v[7] : val;                              // green
+        val = field == 8 ? v[8] : val;                              // blue
+        if (writer) *dst = val;
     }
+}
+
+// Eq. 4: the gradient of Gaussian dsv[r] is the sum of the per-record slots of its
+// entries (emit positions doff[r] .. doff[r+1], up to four quadrant records each).
+// Every Gaussian is written, culled ones with zeros.  One thread per Gaussian.
+__global__ __launch_bounds__(256) void k_grad_reduce(const uint32_t *__restrict__ dsv, const uint32_t *__restrict__ doff,
+                                                     const int32_t *__restrict__ ranges, int T,
+                                                     const uint4 *__restrict__ jmap, const float *__restrict__ qgrad,
+                                                     int64_t n, float *__restrict__ grads2d)
+{
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= n) return;
+    const uint32_t g = dsv[r];
+    const uint32_t p0 = doff[r], p1 = r + 1 < n ? doff[r + 1] : (uint32_t)ranges[T];
+    float acc[kFields];
+#pragma unroll
+    for (int f = 0; f < kFields; ++f) acc[f] = 0.0f;
+    for (uint32_t p = p0; p < p1; ++p) {
+        const uint4 j = jmap[p];
+        const uint32_t js[kQuads] = {j.x, j.y, j.z, j.w};
+#pragma unroll
+        for (int qd = 0; qd < kQuads; ++qd) {
+            if (js[qd] == ~0u) continue;
+            const float *s = qgrad + (size_t)js[qd] * kFields;
+#pragma unroll
+            for (int f = 0; f < kFields; ++f) acc[f] += s[f];
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < kFields; ++f) grads2d[(size_t)f * n + g] = acc[f];
 }
 
 }  // namespace
 
 namespace gsi {
-gs_status check_raster_inputs(const gs_projected *proj, const gs_bins *bins);
+gs_status check_raster_inputs(const gs_bins *bins, const gs_camera *cam);
 }
 
 extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
@@ -165,32 +238,38 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
                                    gs_param_grads *grads3d, hipStream_t stream)
 {
     using namespace gsi;
+    (void)proj;   // the lists carry raster-ready copies of the projected records
     gs_status s;
     if ((s = check_gaussians(g)) != GS_OK) return s;
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
-    if ((s = check_raster_inputs(proj, bins)) != GS_OK) return s;
+    if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
     if (!t_final || !n_trav || !dL_dcolor || (g->n > 0 && !grads2d))
         return fail(GS_ERR_INVALID_ARGUMENT, "t_final / n_trav / dL_dcolor / grads2d is NULL");
-    if (bins->capacity > 0 && !bins->ids) return fail(GS_ERR_INVALID_ARGUMENT, "ids is NULL");
     const int64_t n = g->n;
-    if ((s = fill_f32(grads2d, 9 * n, 0.0f, stream)) != GS_OK) return s;
     const int TX = tiles_x(cam->width), T = TX * tiles_y(cam->height);
-    const int per = xcd_per(T);
-    const dim3 grid((unsigned)(per * kXcds)), block(64);
-    const float2 *m2 = reinterpret_cast<const float2 *>(proj->means2d);
-    const float4 *co = reinterpret_cast<const float4 *>(proj->conic_opacity);
+    const RasterLayout L = raster_layout(n, bins->capacity, T);
+    char *rb = static_cast<char *>(bins->raster);
+    const int32_t *order = reinterpret_cast<const int32_t *>(rb + L.order);
+    const float4 *rc = reinterpret_cast<const float4 *>(rb + L.qrec);
+    const uint64_t *bm = reinterpret_cast<const uint64_t *>(rb + L.bitmap);
+    const uint32_t *wp = reinterpret_cast<const uint32_t *>(rb + L.wpre);
+    float *qg = reinterpret_cast<float *>(rb + L.qgrad);
+    const unsigned grid = (unsigned)raster_grid(T);
     if (n > 0) {
         if (dL_dt)
-            k_raster_bwd<true><<<grid, block, 0, stream>>>(bins->tile_ranges, bins->ids, m2, co, proj->color,
-                                                           cam->width, cam->height, TX, T, per, p->alpha_min,
-                                                           p->alpha_max, t_final, n_trav, dL_dcolor, dL_dt, grads2d, n);
+            k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
+                                                        cam->height, TX, T, p->alpha_min, p->alpha_max, t_final,
+                                                        n_trav, dL_dcolor, dL_dt, qg);
         else
-            k_raster_bwd<false><<<grid, block, 0, stream>>>(bins->tile_ranges, bins->ids, m2, co, proj->color,
-                                                            cam->width, cam->height, TX, T, per, p->alpha_min,
-                                                            p->alpha_max, t_final, n_trav, dL_dcolor, nullptr,
-                                                            grads2d, n);
+            k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
+                                                         cam->height, TX, T, p->alpha_min, p->alpha_max, t_final,
+                                                         n_trav, dL_dcolor, nullptr, qg);
         GS_LAUNCH_CHECK("k_raster_bwd");
+        k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
+            reinterpret_cast<const uint32_t *>(rb + L.dsv), reinterpret_cast<const uint32_t *>(rb + L.doff),
+            bins->tile_ranges, T, reinterpret_cast<const uint4 *>(rb + L.jmap), qg, n, grads2d);
+        GS_LAUNCH_CHECK("k_grad_reduce");
     }
     if (grads3d) return launch_project_bwd(g, cam, p, grads2d, grads3d, stream);
     return GS_OK;

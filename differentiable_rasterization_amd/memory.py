@@ -25,14 +25,17 @@ def bytes_per_gaussian(sh_degree: int, adam: bool = True, grads: bool = False) -
 def step_bytes_per_gaussian(sh_degree: int) -> int:
     """Everything this library keeps per Gaussian during a training step: parameters,
     gradients, Adam moments, the projected record (means2d 8, conic+opacity 16, colour 12,
-    depth 4, radii 8), screen-space gradients (36) and the binning workspace (24)."""
-    return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 48 + 36 + 24
+    depth 4, radii 8), its 48-byte raster-ready copy, screen-space gradients (36) and the
+    binning workspace (24)."""
+    return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 48 + 48 + 36 + 24
 
 
 def step_bytes_per_intersection() -> int:
-    """Intersection lists: ids (4) plus the workspace's two key buffers and one value
-    buffer (12)."""
-    return 16
+    """Intersection lists: ids (4); the raster-ready lists, sized for the worst case of an
+    entry in all four 8x8 quadrants of its tile: records (4 x 48), map words (4 x 4) and
+    per-record gradient slots (4 x 36), plus quadrant bits (1); and the sort workspace's
+    key, value and Gaussian buffers (20)."""
+    return 4 + 4 * (48 + 4 + 36) + 1 + 20
 
 
 def max_gaussians(hbm_bytes: float, sh_degree: int, adam: bool = True) -> int:

@@ -79,9 +79,10 @@ class Projection:
         self.color = torch.zeros(n, 3, dtype=torch.float32, device=device)
         self.depth = torch.zeros(n, dtype=torch.float32, device=device)
         self.radii = torch.zeros(n, 2, dtype=torch.int32, device=device)
+        self.rec = torch.zeros(n, 12, dtype=torch.float32, device=device)   # raster-ready copy
 
     def abi(self) -> B.Projected:
-        return B.projected(self.means2d, self.conic_opacity, self.color, self.depth, self.radii)
+        return B.projected(self.means2d, self.conic_opacity, self.color, self.depth, self.radii, self.rec)
 
 
 class Binning:
@@ -102,9 +103,11 @@ class Binning:
         self.keys = torch.zeros(self.capacity, dtype=torch.int64, device=self.device) if self.with_keys else None
         ws = B.gs_bin_sort_workspace_bytes(self.n, self.capacity, self.width, self.height)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
+        rb = B.gs_bins_raster_bytes(self.n, self.capacity, self.width, self.height)
+        self.raster = torch.empty(max(rb, 256), dtype=torch.uint8, device=self.device)
 
     def abi(self) -> B.Bins:
-        return B.bins(self.ids, self.tile_ranges, self.keys, self.tiles_touched)
+        return B.bins(self.ids, self.tile_ranges, self.raster, self.keys, self.tiles_touched)
 
     def sort(self, proj: Projection, cam: B.Camera, stream=None) -> int:
         try:

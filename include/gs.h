@@ -96,11 +96,16 @@ typedef struct {
  *   depth [n]             camera-space depth as a float32 key:
  *                         fma(R22, z, fma(R21, y, R20 * x)) + t2, each step rounded
  *   radii [n][2]          half-extents in pixels of the alpha >= alpha_min ellipse box,
- *                         rounded up, >= 1; (0, 0) marks a culled Gaussian.  For culled
- *                         Gaussians only radii and depth are written. */
+ *                         rounded up, >= 1; (0, 0) marks a culled Gaussian.
+ *   rec [n][12]           raster-ready copy of the same record (16-byte aligned): u, v, the
+ *                         conic pre-scaled for a base-2 exponential (-A log2(e)/2,
+ *                         -B log2(e), -C log2(e)/2), log2(o), red, green, blue, the index as
+ *                         uint32 bits, two zero words.  gs_bin_sort gathers it per list entry.
+ * For culled Gaussians only radii and depth are written. */
 typedef struct {
     float *means2d, *conic_opacity, *color, *depth;
     int32_t *radii;
+    float *rec;
 } gs_projected;
 
 /* Tile-Gaussian intersection lists.
@@ -108,13 +113,23 @@ typedef struct {
  *   tile_ranges [tiles + 1]   entries of tile t are ids[tile_ranges[t] .. tile_ranges[t+1])
  *   keys [capacity]           optional (may be NULL): tile << 32 | depth key bits per entry
  *   tiles_touched [n]         optional (may be NULL): number of tiles of each Gaussian
- * tiles = ceil(W/16) * ceil(H/16), tile id = row * ceil(W/16) + column. */
+ *   raster                    gs_bins_raster_bytes(n, capacity, W, H) bytes of device memory,
+ *                             256-byte aligned, written by gs_bin_sort and read (and, for the
+ *                             per-record gradient slots, written) by the raster entry points:
+ *                             for each 8x8 quadrant of every tile, the records of the tile's
+ *                             entries whose box reaches it, the maps the backward needs to sum
+ *                             each Gaussian's contributions, and the order in which tiles are
+ *                             rasterized.  Its layout is private to the library; the caller
+ *                             only owns the memory.  The raster calls must use the same n,
+ *                             capacity and image size as the gs_bin_sort call that filled it.
+ * tiles = ceil(W/16) * ceil(H/16), tile id = row * ceil(W/16) + column; capacity <= 2^30. */
 typedef struct {
     uint32_t *ids;
     int32_t *tile_ranges;
     uint64_t *keys;
     int32_t *tiles_touched;
     int64_t capacity;
+    void *raster;
 } gs_bins;
 
 /* Gradients of the learnable parameters, same shapes as gs_gaussians. */
@@ -141,6 +156,11 @@ typedef struct {
 gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
                      gs_projected *out, hipStream_t stream);
 
+/* Bytes of the gs_bins.raster buffer for n Gaussians, `capacity` list entries and a W x H
+ * image: at most 4 quadrant records (48 B), 4 map words and 4 gradient slots (36 B) per
+ * entry, plus 8 B per Gaussian and 4 B per tile. */
+size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
+
 /* Workspace bytes gs_bin_sort needs for n Gaussians, `capacity` list entries and the
  * camera's image size. */
 size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
@@ -151,7 +171,8 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, i
  * x0 = clamp(floor((u - rx)/16), 0, TX), x1 = clamp(floor((u + rx)/16) + 1, 0, TX), same
  * for y).  Entries are ordered by (tile, depth key bits, Gaussian index): a stable LSD
  * radix sort of the Gaussians by depth key, a scan of their tile counts in that order,
- * emission, and a stable radix sort of the entries by tile id.
+ * emission, and a stable radix sort of the entries by tile id.  Then fills bins->raster
+ * from the projected records (every field of `proj` is read).
  * Reads the total K back to the host (synchronises `stream`) and stores it in
  * *n_isect_out (host).  If K > bins->capacity returns GS_ERR_CAPACITY with K in
  * *n_isect_out and the lists unspecified.  workspace: device memory of at least
@@ -183,10 +204,11 @@ gs_status gs_loss_l1(const float *color, const float *target, int64_t n_px, floa
                      float *dL_dcolor, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward rasterization (ByteSplat Eq. 3 and Eq. 4): per tile, each pixel walks its
- * traversed entries back to front, recovers T_i = T_{i+1} / (1 - alpha_i), and adds its
- * partial gradient to the Gaussian's 9 screen-space fields, in the order
- * (u, v, A, B, C, o, r, g, b) of grads2d [9][n] (float32 atomics, so the summation order
- * is not deterministic).  grads2d is cleared by the call before accumulation.
+ * traversed entries back to front, recovers T_i = T_{i+1} / (1 - alpha_i), and forms its
+ * partial gradient of the Gaussian's 9 screen-space fields, in the order
+ * (u, v, A, B, C, o, r, g, b) of grads2d [9][n].  The partial gradients are summed per
+ * tile quadrant and then per Gaussian in a fixed order (no atomics): repeated calls give
+ * bit-identical results.  Every entry of grads2d is written (zero for culled Gaussians).
  * dL_dcolor [H][W][3]; dL_dt [H][W] is the gradient of t_final (may be NULL).  t_final
  * and n_trav come from gs_raster_fwd on the same inputs.  If grads3d is non-NULL the
  * aggregated screen-space gradients are then propagated through projection and colour

@@ -39,8 +39,8 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.Camera) == 16 * 4 + 4 * 4 + 2 * 4 + 4
     assert ctypes.sizeof(B.RasterParams) == 24
     assert ctypes.sizeof(B.Gaussians) == 5 * 8 + 8
-    assert ctypes.sizeof(B.Projected) == 5 * 8
-    assert ctypes.sizeof(B.Bins) == 4 * 8 + 8
+    assert ctypes.sizeof(B.Projected) == 6 * 8
+    assert ctypes.sizeof(B.Bins) == 4 * 8 + 8 + 8
     assert ctypes.sizeof(B.AdamGroup) == 4 * 8 + 8 + 8
 
 
@@ -50,7 +50,7 @@ def _cam(w=64, h=48):
 
 def test_argument_errors_before_launch():
     g = B.Gaussians(None, None, None, None, None, 10)
-    out = B.Projected(None, None, None, None, None)
+    out = B.Projected(None, None, None, None, None, None)
     with pytest.raises(B.GsError) as e:
         B.gs_project(g, _cam(), B.make_params(0), out, stream=_NullStream())
     assert e.value.status == B.GS_ERR_INVALID_ARGUMENT and "NULL" in str(e.value)
@@ -83,7 +83,7 @@ class _NullStream:
 
 
 def test_empty_inputs_return_ok_without_launch():
-    out = B.Projected(None, None, None, None, None)
+    out = B.Projected(None, None, None, None, None, None)
     B.gs_project(B.Gaussians(None, None, None, None, None, 0), _cam(), B.make_params(3), out, _NullStream())
     assert B._lib.gs_adam_step(None, 0, 1, 0.9, 0.999, 1e-15, None) == B.GS_OK
 
@@ -93,11 +93,19 @@ def test_workspace_sizes():
     b = B.gs_bin_sort_workspace_bytes(2000, 5000, 64, 64)
     c = B.gs_bin_sort_workspace_bytes(1000, 50000, 64, 64)
     assert 0 < a < b and a < c
-    # O(24 B per Gaussian + 12 B per entry) plus histograms
-    assert c - a < 12 * 45000 * 1.2 + 4 * 256 * 16 + 4096
+    # O(24 B per Gaussian + 20 B per entry: two key and two value buffers for the tile
+    # sort, the Gaussian of each emitted entry) plus histograms
+    assert 20 * 45000 <= c - a < 20 * 45000 * 1.2 + 4 * 256 * 16 + 4096
     assert B.gs_bin_sort_workspace_bytes(-1, 0, 1, 1) == 0
     assert B.gs_compact_workspace_bytes(10**6) >= 4 * (10**6 // 256)
     assert B.gs_loss_workspace_bytes(100) >= 8
+    # raster-ready lists: per entry up to 4 quadrant records (48 B), map words (4 B) and
+    # gradient slots (36 B); 4 quadrant bits and 4 prefix counts per 64 entries; 8 B per
+    # Gaussian; 4 B per tile
+    r0 = B.gs_bins_raster_bytes(5000, 64 * 1000, 1920, 1080)
+    lo = 4 * (48 + 4 + 36) * 64000 + 4 * 8 * 1000 + 4 * 4 * 1001 + 8 * 5000 + 4 * 8160
+    assert lo <= r0 <= lo + 8 * 256
+    assert B.gs_bins_raster_bytes(0, 0, 16, 16) > 0 and B.gs_bins_raster_bytes(0, -1, 16, 16) == 0
 
 
 def test_memory_planner_matches_page_figures():
