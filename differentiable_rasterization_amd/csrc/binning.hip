@@ -25,12 +25,12 @@ __global__ __launch_bounds__(256) void k_depth_keys(const int2 *__restrict__ rad
     vals[i] = (uint32_t)i;
 }
 
-// Tile counts of the Gaussians in depth order (0 for culled ones); also keeps the depth
-// order for the backward's per-Gaussian reduction.
+// Tile counts of the Gaussians in depth order (0 for culled ones); also records each
+// Gaussian's depth rank for the backward's per-Gaussian reduction.
 __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skeys, const uint32_t *__restrict__ svals,
                                                const float2 *__restrict__ means2d, const int2 *__restrict__ radii,
                                                int64_t n, int tx, int ty, uint32_t *__restrict__ cnt,
-                                               uint32_t *__restrict__ dsv)
+                                               uint32_t *__restrict__ drank)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n) return;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skey
         c = (uint32_t)((x1 - x0) * (y1 - y0));
     }
     cnt[j] = c;
-    dsv[j] = g;
+    drank[g] = (uint32_t)j;
 }
 
 // Entries of each Gaussian in depth order, tiles row-major.  Entry p gets the key
@@ -255,7 +255,7 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     const gsr::RasterLayout RL = gsr::raster_layout(n, bins->capacity, T);
     char *rb = static_cast<char *>(bins->raster);
     int32_t *order = reinterpret_cast<int32_t *>(rb + RL.order);
-    uint32_t *dsv = reinterpret_cast<uint32_t *>(rb + RL.dsv), *doff = reinterpret_cast<uint32_t *>(rb + RL.doff);
+    uint32_t *drank = reinterpret_cast<uint32_t *>(rb + RL.drank), *doff = reinterpret_cast<uint32_t *>(rb + RL.doff);
     *n_isect_out = 0;
     if (n == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
@@ -291,7 +291,7 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     const uint32_t *sk = in_b ? dkB : dkA, *sv = in_b ? dvB : dvA;
 
     // 2. tile counts in depth order, their exclusive scan (the emit offsets) and the total K
-    k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, n, tx, ty, cnt, dsv);
+    k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, n, tx, ty, cnt, drank);
     GS_LAUNCH_CHECK("k_count");
     if ((s = exclusive_scan_u32(cnt, doff, n, part, total, stream)) != GS_OK) return s;
     unsigned long long K = 0;

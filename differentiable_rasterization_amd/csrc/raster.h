@@ -13,13 +13,14 @@
 //                                 qrec[P_q(start_t) .. P_q(end_t)), P_q(x) = wpre[q][x / 64]
 //                                 + set bits of bitmap q below entry x in its word
 //   order  [tiles] int32          tiles by decreasing list length (heaviest first)
-//   dsv    [n] uint32             Gaussians in depth order (culled ones last)
-//   doff   [n] uint32             first emitted entry of each Gaussian in that order: the
-//                                 entries of Gaussian dsv[r] were emitted at positions
+//   drank  [n] uint32             depth rank of each Gaussian (culled ones rank last)
+//   doff   [n] uint32             first emitted entry of each Gaussian by depth rank: the
+//                                 entries of the Gaussian of rank r were emitted at positions
 //                                 doff[r] .. doff[r + 1] (doff[n] = K)
 //   jmap   [4 * capacity] uint32  position in qrec of emitted entry p's record in quadrant q
 //                                 (index 4 p + q), or ~0 if the entry is not in quadrant q
-//   qgrad  [4 * capacity][9] f32  the backward's per-record partial gradients
+//   qgrad  [4 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
+//                                 padded to 48 bytes)
 //
 // Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
 // (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of records with
@@ -46,6 +47,7 @@ struct Rec {
     float4 p0, p1, p2;
 };
 constexpr int kRecF4 = 3;   // float4 words per record
+constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
 constexpr float kLn2 = 0.69314718055994531f;
 
 // Quadrant mask of an entry lives in bits 24..27 of its 32-bit tile key during the sort
@@ -71,7 +73,7 @@ __device__ __forceinline__ uint32_t quad_mask(float u, float v, int rx, int ry, 
 }
 
 struct RasterLayout {
-    size_t qrec, bitmap, wpre, order, dsv, doff, jmap, qgrad, bytes;
+    size_t qrec, bitmap, wpre, order, drank, doff, jmap, qgrad, bytes;
     int64_t cap, words;
 };
 
@@ -88,10 +90,10 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
     L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);
     L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);
-    L.dsv = o;    o += align256(nn * 4);
+    L.drank = o;  o += align256(nn * 4);
     L.doff = o;   o += align256(nn * 4);
     L.jmap = o;   o += align256(q4 * 4);
-    L.qgrad = o;  o += align256(q4 * 9 * 4);
+    L.qgrad = o;  o += align256(q4 * kGradSlot * 4);
     L.bytes = o;
     return L;
 }
@@ -119,6 +121,17 @@ __device__ __forceinline__ void raster_block(int &tile_idx, int &quad)
     const int slot = b >> 3;
     tile_idx = (b & 7) + 8 * (slot >> 2);
     quad = slot & 3;
+}
+
+// Pulls the cache lines of records [j, min(j + 64, jlim)) into L2 with one vector load
+// (lane l touches record j + l), so that the wave's scalar loads of those records hit L2
+// rather than memory.  The loaded word is only folded into a sink one chunk later (by
+// then the load has landed, so that wait costs nothing) and the sink is consumed once at
+// the end of the kernel: an ordinary load the compiler tracks, kept in flight meanwhile.
+__device__ __forceinline__ uint32_t prefetch_records(const float4 *__restrict__ qrec, uint32_t j, uint32_t jlim)
+{
+    const uint32_t r = j + (uint32_t)threadIdx.x;
+    return r < jlim ? __float_as_uint(qrec[kRecF4 * (size_t)r].x) : 0u;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

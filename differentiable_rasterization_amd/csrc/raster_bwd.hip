@@ -117,10 +117,18 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)(start + nmax));
     const uint32_t jend = quad_prefix(bq, wq, (uint32_t)end);
     // records never reached by any pixel of the quadrant contribute nothing
-    for (size_t z = (size_t)j1 * kFields + lane; z < (size_t)jend * kFields; z += 64) qgrad[z] = 0.0f;
+    for (size_t z = (size_t)j1 * kGradSlot + lane; z < (size_t)jend * kGradSlot; z += 64) qgrad[z] = 0.0f;
     const int row = lane >> 4, field = lane & 15;
     float B0 = 0.0f, B1 = 0.0f, B2 = 0.0f;
+    // L2 prefetch of the next chunk of 64 records ahead of the (descending) scalar reads
+    auto chunk = [&](uint32_t hi) { return hi > j0 + 64u ? hi - 64u : j0; };
+    uint32_t sink = prefetch_records(qrec, chunk(j1), j1);
+    uint32_t pend = prefetch_records(qrec, chunk(chunk(j1)), chunk(j1));
     for (uint32_t jt = j1; jt > j0;) {
+        if (((j1 - jt) & 63u) == 0u && jt < j1) {
+            sink ^= pend;
+            pend = prefetch_records(qrec, chunk(chunk(jt)), chunk(jt));
+        }
         // records jt-1, jt-2, ... (back to front); one wait per batch
         float4 p0[kBwdBatch], p1[kBwdBatch];
         float blue[kBwdBatch], kent[kBwdBatch];
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
             any |= acc;
         }
         // slot of the batch's record e = row: record jt - 1 - e, field f = lane & 15
-        float *dst = qgrad + ((size_t)(jt - 1u - (uint32_t)min(row, (int)cnt - 1))) * kFields + field;
+        float *dst = qgrad + ((size_t)(jt - 1u - (uint32_t)min(row, (int)cnt - 1))) * kGradSlot + field;
         const bool writer = (uint32_t)row < cnt && field < kFields;
         jt -= cnt;
         if (__ballot(any) == 0) {
@@ -194,20 +202,23 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         val = field == 8 ? v[8] : val;                              // blue
         if (writer) *dst = val;
     }
+    sink ^= pend;
+    asm volatile("" ::"v"(sink));
 }
 
-// Eq. 4: the gradient of Gaussian dsv[r] is the sum of the per-record slots of its
-// entries (emit positions doff[r] .. doff[r+1], up to four quadrant records each).
-// Every Gaussian is written, culled ones with zeros.  One thread per Gaussian.
-__global__ __launch_bounds__(256) void k_grad_reduce(const uint32_t *__restrict__ dsv, const uint32_t *__restrict__ doff,
+// Eq. 4: the gradient of Gaussian g is the sum of the per-record slots of its entries
+// (emit positions doff[r] .. doff[r+1] with r its depth rank, up to four quadrant records
+// each), added in a fixed order.  Every Gaussian is written, culled ones with zeros.  One
+// thread per Gaussian, in index order so that the stores coalesce.
+__global__ __launch_bounds__(256) void k_grad_reduce(const uint32_t *__restrict__ drank, const uint32_t *__restrict__ doff,
                                                      const int32_t *__restrict__ ranges, int T,
-                                                     const uint4 *__restrict__ jmap, const float *__restrict__ qgrad,
+                                                     const uint4 *__restrict__ jmap, const float4 *__restrict__ qgrad,
                                                      int64_t n, float *__restrict__ grads2d)
 {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= n) return;
-    const uint32_t g = dsv[r];
-    const uint32_t p0 = doff[r], p1 = r + 1 < n ? doff[r + 1] : (uint32_t)ranges[T];
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n) return;
+    const uint32_t r = drank[g];
+    const uint32_t p0 = doff[r], p1 = (int64_t)r + 1 < n ? doff[r + 1] : (uint32_t)ranges[T];
     float acc[kFields];
 #pragma unroll
     for (int f = 0; f < kFields; ++f) acc[f] = 0.0f;
@@ -217,9 +228,11 @@ __global__ __launch_bounds__(256) void k_grad_reduce(const uint32_t *__restrict_
 #pragma unroll
         for (int qd = 0; qd < kQuads; ++qd) {
             if (js[qd] == ~0u) continue;
-            const float *s = qgrad + (size_t)js[qd] * kFields;
-#pragma unroll
-            for (int f = 0; f < kFields; ++f) acc[f] += s[f];
+            const float4 *sl = qgrad + (size_t)js[qd] * (kGradSlot / 4);
+            const float4 a = sl[0], b = sl[1], c = sl[2];
+            acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+            acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+            acc[8] += c.x;
         }
     }
 #pragma unroll
@@ -267,8 +280,9 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
                                                          n_trav, dL_dcolor, nullptr, qg);
         GS_LAUNCH_CHECK("k_raster_bwd");
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
-            reinterpret_cast<const uint32_t *>(rb + L.dsv), reinterpret_cast<const uint32_t *>(rb + L.doff),
-            bins->tile_ranges, T, reinterpret_cast<const uint4 *>(rb + L.jmap), qg, n, grads2d);
+            reinterpret_cast<const uint32_t *>(rb + L.drank), reinterpret_cast<const uint32_t *>(rb + L.doff),
+            bins->tile_ranges, T, reinterpret_cast<const uint4 *>(rb + L.jmap), reinterpret_cast<const float4 *>(qg),
+            n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }
     if (grads3d) return launch_project_bwd(g, cam, p, grads2d, grads3d, stream);

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
                                                    const uint32_t *__restrict__ wpre, int64_t words, int W, int H,
                                                    int TX, int T, float alpha_min, float alpha_max, float t_min,
                                                    float *__restrict__ out_c, float *__restrict__ out_t,
-                                                   int32_t *__restrict__ out_n, unsigned long long *__restrict__ n_sum)
+                                                   int32_t *__restrict__ out_n)
 {
     int tidx, q;
     raster_block(tidx, q);
@@ -40,7 +40,13 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
     float Tr = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
     int np = end - start;
     bool live = inside;
+    // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
+    uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
     for (uint32_t j = j0; j < j1; j += kFwdBatch) {
+        if (((j - j0) & 63u) == 0u && j > j0) {
+            sink ^= pend;
+            pend = prefetch_records(qrec, j + 64u, j1);
+        }
         // Scalar loads complete out of order: one wait per batch of records.
         float4 p0[kFwdBatch], p1[kFwdBatch];
         float blue[kFwdBatch], kent[kFwdBatch];
@@ -76,7 +82,8 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
         }
         if (__ballot(live) == 0) break;
     }
-    unsigned tot = 0;
+    sink ^= pend;
+    asm volatile("" ::"v"(sink));
     if (inside) {
         const size_t idx = (size_t)py * W + px;
         out_c[3 * idx] = cr;
@@ -84,11 +91,24 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
         out_c[3 * idx + 2] = cb;
         out_t[idx] = Tr;
         out_n[idx] = np;
-        tot = (unsigned)np;
     }
-    if (n_sum) {
-        tot = gsd::wave_sum_u32_to_lane63(tot);
-        if (lane == 63 && tot > 0u) atomicAdd(n_sum, (unsigned long long)tot);
+}
+
+// sum over the image of N_p, added to *n_sum: one 64-bit atomic per block (a device-wide
+// counter updated once per raster wave would serialise ~10^4 atomics on one address)
+__global__ __launch_bounds__(256) void k_sum_ntrav(const int32_t *__restrict__ n_trav, int64_t n_px,
+                                                   unsigned long long *__restrict__ n_sum)
+{
+    __shared__ unsigned long long part[4];
+    unsigned long long acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_px; i += (int64_t)gridDim.x * 256)
+        acc += (unsigned)n_trav[i];
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_down(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned long long t = part[0] + part[1] + part[2] + part[3];
+        if (t) atomicAdd(n_sum, t);
     }
 }
 
@@ -126,7 +146,13 @@ extern "C" gs_status gs_raster_fwd(const gs_projected *proj, const gs_bins *bins
     k_raster_fwd<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
         bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order), reinterpret_cast<const float4 *>(rb + L.qrec),
         reinterpret_cast<const uint64_t *>(rb + L.bitmap), reinterpret_cast<const uint32_t *>(rb + L.wpre), L.words,
-        cam->width, cam->height, TX, T, p->alpha_min, p->alpha_max, p->t_min, color, t_final, n_trav, n_trav_sum);
+        cam->width, cam->height, TX, T, p->alpha_min, p->alpha_max, p->t_min, color, t_final, n_trav);
     GS_LAUNCH_CHECK("k_raster_fwd");
+    if (n_trav_sum) {
+        const int64_t n_px = (int64_t)cam->width * cam->height;
+        k_sum_ntrav<<<(unsigned)std::min<int64_t>(ceil_div(n_px, 256 * 8), 1024), 256, 0, stream>>>(n_trav, n_px,
+                                                                                                   n_trav_sum);
+        GS_LAUNCH_CHECK("k_sum_ntrav");
+    }
     return GS_OK;
 }

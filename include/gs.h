@@ -157,7 +157,7 @@ gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raste
                      gs_projected *out, hipStream_t stream);
 
 /* Bytes of the gs_bins.raster buffer for n Gaussians, `capacity` list entries and a W x H
- * image: at most 4 quadrant records (48 B), 4 map words and 4 gradient slots (36 B) per
+ * image: at most 4 quadrant records (48 B), 4 map words and 4 gradient slots (48 B) per
  * entry, plus 8 B per Gaussian and 4 B per tile. */
 size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
 
