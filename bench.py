@@ -133,7 +133,7 @@ def main():
         rec(0)
         B.gs_project(params.gaussians(), c, st.raster, st.proj.abi())
         rec(1)
-        st.bins.sort(st.proj, c)
+        st.bins.sort(st.proj, c, st.raster)
         rec(2)
         f = st.frame
         B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.n_trav_sum)

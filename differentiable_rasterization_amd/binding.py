@@ -87,7 +87,7 @@ _SIGS = {
     "gs_project": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _P(Projected), _vp]),
     "gs_bins_raster_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "gs_bin_sort_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
-    "gs_bin_sort": (_i32, [_P(Projected), _i64, _P(Camera), _P(Bins), _P(_i64), _vp, _sz, _vp]),
+    "gs_bin_sort": (_i32, [_P(Projected), _i64, _P(Camera), _P(RasterParams), _P(Bins), _P(_i64), _vp, _sz, _vp]),
     "gs_raster_fwd": (_i32, [_P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp]),
     "gs_loss_workspace_bytes": (_sz, [_i64]),
     "gs_loss_l1": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -182,10 +182,10 @@ def gs_bin_sort_workspace_bytes(n, capacity, width, height) -> int:
     return int(_lib.gs_bin_sort_workspace_bytes(n, capacity, width, height))
 
 
-def gs_bin_sort(proj: Projected, n, cam: Camera, b: Bins, workspace, stream=None) -> int:
+def gs_bin_sort(proj: Projected, n, cam: Camera, p: RasterParams, b: Bins, workspace, stream=None) -> int:
     """Returns K.  Raises GsCapacityError (with .required = K) if the lists are too small."""
     k = _i64(0)
-    st = _lib.gs_bin_sort(ctypes.byref(proj), n, ctypes.byref(cam), ctypes.byref(b), ctypes.byref(k),
+    st = _lib.gs_bin_sort(ctypes.byref(proj), n, ctypes.byref(cam), ctypes.byref(p), ctypes.byref(b), ctypes.byref(k),
                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, required=k.value)
     return k.value

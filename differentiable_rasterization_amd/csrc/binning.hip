@@ -52,7 +52,8 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skey
 // value p (its emit position) and gauss[p] = its Gaussian.
 __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
                                               const uint32_t *__restrict__ off, const float2 *__restrict__ means2d,
-                                              const int2 *__restrict__ radii, int64_t n, int tx, int ty,
+                                              const int2 *__restrict__ radii, const float4 *__restrict__ conic_o,
+                                              float alpha_min, int64_t n, int tx, int ty,
                                               uint32_t *__restrict__ tkeys, uint32_t *__restrict__ tvals,
                                               uint32_t *__restrict__ gauss)
 {
@@ -61,12 +62,15 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
     const uint32_t g = svals[j];
     const float2 m = means2d[g];
     const int2 r = radii[g];
+    const float4 co = conic_o[g];
+    const float thr = 2.0f * __logf(co.w / alpha_min);
     int x0, x1, y0, y1;
     gsd::tile_rect(m.x, m.y, r.x, r.y, tx, ty, x0, x1, y0, y1);
     uint32_t p = off[j];
     for (int y = y0; y < y1; ++y)
         for (int x = x0; x < x1; ++x) {
-            const uint32_t qm = gsr::quad_mask(m.x, m.y, r.x, r.y, (float)(x * GS_TILE), (float)(y * GS_TILE));
+            const uint32_t qm =
+                gsr::quad_mask(m.x, m.y, co.x, co.y, co.z, thr, (float)(x * GS_TILE), (float)(y * GS_TILE));
             tkeys[p] = (uint32_t)(y * tx + x) | (qm << gsr::kMaskShift);
             tvals[p] = p;
             gauss[p] = g;
@@ -119,6 +123,9 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
                                                     uint4 *__restrict__ jmap)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // the spare records in front of the lists are read (never used) by the backward's
+    // batches: keep them finite
+    if (k < gsr::kRecPad * gsr::kRecF4) qrec[k - gsr::kRecPad * gsr::kRecF4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (k >= K) return;
     const uint32_t qm = tkeys[k] >> gsr::kMaskShift;
     uint32_t pos[gsr::kQuads];
@@ -235,12 +242,15 @@ extern "C" size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32
     return layout(n, capacity).bytes;
 }
 
-extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, gs_bins *bins,
-                                 int64_t *n_isect_out, void *workspace, size_t workspace_bytes, hipStream_t stream)
+extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, const gs_raster_params *p,
+                                 gs_bins *bins, int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream)
 {
     using namespace gsi;
     gs_status s;
     if ((s = check_camera(cam)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    const float alpha_min = p->alpha_min;
     if (!proj || !bins || !n_isect_out) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
     if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
     if (n > (int64_t(1) << 31) - 1) return fail(GS_ERR_UNSUPPORTED, "n >= 2^31");
@@ -265,7 +275,9 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     }
     if (!proj->means2d || !proj->depth || !proj->radii)
         return fail(GS_ERR_INVALID_ARGUMENT, "projected means2d / depth / radii is NULL");
-    if (!proj->rec) return fail(GS_ERR_INVALID_ARGUMENT, "projected rec is NULL");
+    if (!proj->rec || !proj->conic_opacity)
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected rec / conic_opacity is NULL");
+    if (!aligned(proj->conic_opacity, 16)) return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity must be 16-byte aligned");
     if (!aligned(proj->means2d, 8) || !aligned(proj->radii, 8) || !aligned(proj->rec, 16))
         return fail(GS_ERR_INVALID_ARGUMENT, "means2d / radii must be 8-byte, rec 16-byte aligned");
     const Layout L = layout(n, bins->capacity);
@@ -314,7 +326,8 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
 
     // 3. emit entries in depth order, then a stable sort of (tile key, emit position) by tile
     const int tbits = std::max(1, bits_for(T - 1));
-    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, m2, rr, n, tx, ty, tkA, tvA, gauss);
+    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity),
+                                   alpha_min, n, tx, ty, tkA, tvA, gauss);
     GS_LAUNCH_CHECK("k_emit");
     if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, (int64_t)K, tbits, hist, part, &in_b, stream)) != GS_OK) return s;
     const uint32_t *tk = in_b ? tkB : tkA, *spos = in_b ? tvB : tvA;
@@ -331,7 +344,7 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     if ((s = exclusive_scan_u32(wpre, wpre, nw, part, nullptr, stream)) != GS_OK) return s;
     k_quad_lists<<<gk, 256, 0, stream>>>(tk, spos, bins->ids, (int64_t)K, RL.words, bm, wpre,
                                          reinterpret_cast<const float4 *>(proj->rec),
-                                         reinterpret_cast<float4 *>(rb + RL.qrec),
+                                         reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4,
                                          reinterpret_cast<uint4 *>(rb + RL.jmap));
     GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {

@@ -57,15 +57,17 @@ __global__ __launch_bounds__(kThreads) void k_loss_final(const double *__restric
 
 constexpr int kMaxGroups = 16;
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 struct AdamArgs {
     float *p[kMaxGroups];
     const float *g[kMaxGroups];
     float *m[kMaxGroups];
     float *v[kMaxGroups];
-    int64_t begin[kMaxGroups + 1];   // prefix of group sizes, in float4 units
-    float step[kMaxGroups];          // lr / (1 - b1^t)
-    bool vec[kMaxGroups];            // group is float4-aligned and a multiple of 4 long
     int64_t n[kMaxGroups];
+    uint32_t block0[kMaxGroups + 1];   // first block of each group (256 float4 per block)
+    float step[kMaxGroups];            // lr / (1 - b1^t)
+    bool vec[kMaxGroups];              // group is float4-aligned and a multiple of 4 long
     int ng;
     float b1, b2, inv_bc2, eps;
 };
@@ -78,35 +80,43 @@ __device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, flo
     p -= step * m / (__fsqrt_rn(v * inv_bc2) + eps);
 }
 
+// One float4 of one group per thread; every block lies inside one group.  The four
+// streams are read and written once, so the accesses are non-temporal (they would only
+// evict other data from the caches).
 __global__ __launch_bounds__(kThreads) void k_adam(AdamArgs a)
 {
-    const int64_t total = a.begin[a.ng];
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
-        int gi = 0;
-        while (gi + 1 < a.ng && i >= a.begin[gi + 1]) ++gi;
-        const int64_t j = i - a.begin[gi];
-        const float st = a.step[gi];
-        if (a.vec[gi]) {
-            float4 p = reinterpret_cast<float4 *>(a.p[gi])[j];
-            const float4 g = reinterpret_cast<const float4 *>(a.g[gi])[j];
-            float4 m = reinterpret_cast<float4 *>(a.m[gi])[j];
-            float4 v = reinterpret_cast<float4 *>(a.v[gi])[j];
-            adam1(p.x, g.x, m.x, v.x, a.b1, a.b2, a.inv_bc2, a.eps, st);
-            adam1(p.y, g.y, m.y, v.y, a.b1, a.b2, a.inv_bc2, a.eps, st);
-            adam1(p.z, g.z, m.z, v.z, a.b1, a.b2, a.inv_bc2, a.eps, st);
-            adam1(p.w, g.w, m.w, v.w, a.b1, a.b2, a.inv_bc2, a.eps, st);
-            reinterpret_cast<float4 *>(a.p[gi])[j] = p;
-            reinterpret_cast<float4 *>(a.m[gi])[j] = m;
-            reinterpret_cast<float4 *>(a.v[gi])[j] = v;
-        } else {
-            for (int64_t e = 4 * j; e < min(4 * j + 4, a.n[gi]); ++e) {
-                float p = a.p[gi][e], m = a.m[gi][e], v = a.v[gi][e];
-                adam1(p, a.g[gi][e], m, v, a.b1, a.b2, a.inv_bc2, a.eps, st);
-                a.p[gi][e] = p;
-                a.m[gi][e] = m;
-                a.v[gi][e] = v;
-            }
+    const uint32_t b = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < a.ng && b >= a.block0[gi + 1]) ++gi;
+    const int64_t j = (int64_t)(b - a.block0[gi]) * kThreads + threadIdx.x;   // float4 index in the group
+    const int64_t n = a.n[gi];
+    if (4 * j >= n) return;
+    const float st = a.step[gi];
+    if (a.vec[gi]) {
+        v4f *pp = reinterpret_cast<v4f *>(a.p[gi]) + j;
+        const v4f *gp = reinterpret_cast<const v4f *>(a.g[gi]) + j;
+        v4f *mp = reinterpret_cast<v4f *>(a.m[gi]) + j;
+        v4f *vp = reinterpret_cast<v4f *>(a.v[gi]) + j;
+        v4f p = __builtin_nontemporal_load(pp), g = __builtin_nontemporal_load(gp);
+        v4f m = __builtin_nontemporal_load(mp), v = __builtin_nontemporal_load(vp);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float pc = p[c], mc = m[c], vc = v[c];
+            adam1(pc, g[c], mc, vc, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            p[c] = pc;
+            m[c] = mc;
+            v[c] = vc;
+        }
+        __builtin_nontemporal_store(p, pp);
+        __builtin_nontemporal_store(m, mp);
+        __builtin_nontemporal_store(v, vp);
+    } else {
+        for (int64_t e = 4 * j; e < min(4 * j + 4, n); ++e) {
+            float p = a.p[gi][e], m = a.m[gi][e], v = a.v[gi][e];
+            adam1(p, a.g[gi][e], m, v, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            a.p[gi][e] = p;
+            a.m[gi][e] = m;
+            a.v[gi][e] = v;
         }
     }
 }
@@ -168,7 +178,7 @@ extern "C" gs_status gs_adam_step(const gs_adam_group *groups, int32_t n_groups,
     a.eps = eps;
     const double bc1 = 1.0 - std::pow((double)beta1, step), bc2 = 1.0 - std::pow((double)beta2, step);
     a.inv_bc2 = (float)(1.0 / bc2);
-    int64_t acc = 0;
+    int64_t blocks = 0;
     for (int i = 0; i < n_groups; ++i) {
         const gs_adam_group &gr = groups[i];
         if (gr.n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "group %d: n < 0", i);
@@ -177,12 +187,13 @@ extern "C" gs_status gs_adam_step(const gs_adam_group *groups, int32_t n_groups,
         a.p[i] = gr.p; a.g[i] = gr.g; a.m[i] = gr.m; a.v[i] = gr.v; a.n[i] = gr.n;
         a.step[i] = (float)((double)gr.lr / bc1);
         a.vec[i] = gr.n % 4 == 0 && aligned(gr.p, 16) && aligned(gr.g, 16) && aligned(gr.m, 16) && aligned(gr.v, 16);
-        a.begin[i] = acc;
-        acc += ceil_div(gr.n, 4);
+        a.block0[i] = (uint32_t)blocks;
+        blocks += ceil_div(ceil_div(gr.n, 4), kThreads);
+        if (blocks > 0x7fffffff) return fail(GS_ERR_UNSUPPORTED, "parameter groups too large");
     }
-    a.begin[n_groups] = acc;
-    if (acc == 0) return GS_OK;
-    k_adam<<<stream_blocks(acc), kThreads, 0, stream>>>(a);
+    a.block0[n_groups] = (uint32_t)blocks;
+    if (blocks == 0) return GS_OK;
+    k_adam<<<(unsigned)blocks, kThreads, 0, stream>>>(a);
     GS_LAUNCH_CHECK("k_adam");
     return GS_OK;
 }

@@ -2,7 +2,8 @@
 // rasterization kernels.
 //
 // Raster-ready lists (the gs_bins.raster buffer, written by gs_bin_sort):
-//   qrec   [4 * capacity] Rec     for each 8x8 quadrant q of every tile (qx = q & 1,
+//   qrec   [4 * capacity] Rec     (plus kRecPad spare records at each end)
+//                                 for each 8x8 quadrant q of every tile (qx = q & 1,
 //                                 qy = q >> 1), the records of the tile's entries whose
 //                                 alpha >= alpha_min box reaches the quadrant, in list
 //                                 order; quadrant 0's lists of all tiles in tile order, then
@@ -48,6 +49,10 @@ struct Rec {
 };
 constexpr int kRecF4 = 3;   // float4 words per record
 constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
+// The record array has kRecPad spare records before and after the lists, so that a batch
+// of consecutive records can always be loaded from one base address (records outside the
+// lists are loaded but never used).
+constexpr int kRecPad = 4;
 constexpr float kLn2 = 0.69314718055994531f;
 
 // Quadrant mask of an entry lives in bits 24..27 of its 32-bit tile key during the sort
@@ -55,21 +60,44 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kMaskShift = 24;
 constexpr uint32_t kTileMask = (1u << kMaskShift) - 1u;
 
-// Bit q of the result is set if the box [u - rx, u + rx] x [v - ry, v + ry] reaches a pixel
-// centre of 8x8 quadrant q (qx = q & 1, qy = q >> 1) of the tile with pixel origin
-// (x0, y0).  Outside that box alpha < alpha_min exactly; the margin is far above rounding.
-__device__ __forceinline__ uint32_t quad_mask(float u, float v, int rx, int ry, float x0, float y0)
+// Minimum of the quadratic form A x^2 + 2 B x y + C y^2 (positive definite) over the
+// rectangle [xa, xb] x [ya, yb] of offsets from the mean: 0 if the rectangle holds the
+// mean, otherwise the smallest of the four edge minima (each a clamped 1-D quadratic).
+// bA = B / A and bC = B / C are passed in precomputed.
+__device__ __forceinline__ float conic_rect_min(float A, float B, float C, float bA, float bC, float xa, float xb,
+                                                float ya, float yb)
 {
-    const float margin = 0.01f;
-    bool mx[2], my[2];
+    if (xa <= 0.0f && xb >= 0.0f && ya <= 0.0f && yb >= 0.0f) return 0.0f;
+    float m = INFINITY;
+    const float xs[2] = {xa, xb}, ys[2] = {ya, yb};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const float lo = 8.0f * h + 0.5f - margin, hi = 8.0f * h + 7.5f + margin;
-        mx[h] = (u - (float)rx) - x0 <= hi && (u + (float)rx) - x0 >= lo;
-        my[h] = (v - (float)ry) - y0 <= hi && (v + (float)ry) - y0 >= lo;
+    for (int e = 0; e < 2; ++e) {
+        const float x = xs[e], y = fminf(fmaxf(-bC * x, ya), yb);
+        m = fminf(m, fmaf(A * x, x, fmaf(2.0f * B * x, y, C * y * y)));
+        const float y2 = ys[e], x2 = fminf(fmaxf(-bA * y2, xa), xb);
+        m = fminf(m, fmaf(A * x2, x2, fmaf(2.0f * B * x2, y2, C * y2 * y2)));
     }
-    return (uint32_t)(mx[0] && my[0]) | ((uint32_t)(mx[1] && my[0]) << 1) | ((uint32_t)(mx[0] && my[1]) << 2) |
-           ((uint32_t)(mx[1] && my[1]) << 3);
+    return m;
+}
+
+// Bit q of the result is set if the alpha >= alpha_min ellipse of a Gaussian (conic A, B,
+// C; alpha >= alpha_min  <=>  A dx^2 + 2 B dx dy + C dy^2 <= thr = 2 ln(o / alpha_min))
+// can reach a pixel centre of 8x8 quadrant q (qx = q & 1, qy = q >> 1) of the tile with
+// pixel origin (x0, y0): its minimum over the rectangle spanned by the quadrant's pixel
+// centres is at most thr.  The absolute margin of 1e-3 on a form of order 10 (a 0.05 %
+// band of alpha below alpha_min) keeps the test conservative against float rounding;
+// entries it admits in error are rejected by the per-pixel alpha test.
+__device__ __forceinline__ uint32_t quad_mask(float u, float v, float A, float B, float C, float thr, float x0, float y0)
+{
+    const float lim = thr + 1e-3f;
+    const float bA = B / A, bC = B / C;
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float xa = x0 + 8.0f * (q & 1) + 0.5f - u, ya = y0 + 8.0f * (q >> 1) + 0.5f - v;
+        if (conic_rect_min(A, B, C, bA, bC, xa, xa + 7.0f, ya, ya + 7.0f) <= lim) m |= 1u << q;
+    }
+    return m;
 }
 
 struct RasterLayout {
@@ -86,7 +114,7 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.words = (L.cap + 63) / 64;
     const size_t nn = (size_t)(n > 0 ? n : 1), q4 = (size_t)kQuads * (size_t)L.cap;
     size_t o = 0;
-    L.qrec = o;   o += align256(q4 * sizeof(Rec));
+    L.qrec = o;   o += align256((q4 + 2 * kRecPad) * sizeof(Rec));   // kRecPad spare records at each end
     L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
     L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);
     L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);

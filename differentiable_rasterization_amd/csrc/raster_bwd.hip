@@ -132,12 +132,13 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         // records jt-1, jt-2, ... (back to front); one wait per batch
         float4 p0[kBwdBatch], p1[kBwdBatch];
         float blue[kBwdBatch], kent[kBwdBatch];
+        // records jt-1, jt-2, jt-3, jt-4 from one base (before j0: spare, unused)
+        const float4 *rb = qrec + kRecF4 * ((int64_t)jt - kBwdBatch);
 #pragma unroll
         for (int i = 0; i < kBwdBatch; ++i) {
-            const uint32_t r = jt - 1u - min((uint32_t)i, jt - 1u - j0);   // before j0: repeat the first (unused)
-            p0[i] = qrec[kRecF4 * (size_t)r];
-            p1[i] = qrec[kRecF4 * (size_t)r + 1];
-            const float4 p2 = qrec[kRecF4 * (size_t)r + 2];
+            p0[i] = rb[kRecF4 * (kBwdBatch - 1 - i)];
+            p1[i] = rb[kRecF4 * (kBwdBatch - 1 - i) + 1];
+            const float4 p2 = rb[kRecF4 * (kBwdBatch - 1 - i) + 2];
             blue[i] = p2.x;
             kent[i] = p2.z;
         }
@@ -264,7 +265,7 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
     const RasterLayout L = raster_layout(n, bins->capacity, T);
     char *rb = static_cast<char *>(bins->raster);
     const int32_t *order = reinterpret_cast<const int32_t *>(rb + L.order);
-    const float4 *rc = reinterpret_cast<const float4 *>(rb + L.qrec);
+    const float4 *rc = reinterpret_cast<const float4 *>(rb + L.qrec) + kRecPad * kRecF4;
     const uint64_t *bm = reinterpret_cast<const uint64_t *>(rb + L.bitmap);
     const uint32_t *wp = reinterpret_cast<const uint32_t *>(rb + L.wpre);
     float *qg = reinterpret_cast<float *>(rb + L.qgrad);

@@ -50,12 +50,12 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
         // Scalar loads complete out of order: one wait per batch of records.
         float4 p0[kFwdBatch], p1[kFwdBatch];
         float blue[kFwdBatch], kent[kFwdBatch];
+        const float4 *rb = qrec + kRecF4 * (size_t)j;   // records j .. j+3 (past j1: spare, unused)
 #pragma unroll
         for (int i = 0; i < kFwdBatch; ++i) {
-            const uint32_t r = min(j + (uint32_t)i, j1 - 1u);   // past the end: repeat the last (unused)
-            p0[i] = qrec[kRecF4 * (size_t)r];
-            p1[i] = qrec[kRecF4 * (size_t)r + 1];
-            const float4 p2 = qrec[kRecF4 * (size_t)r + 2];
+            p0[i] = rb[kRecF4 * i];
+            p1[i] = rb[kRecF4 * i + 1];
+            const float4 p2 = rb[kRecF4 * i + 2];
             blue[i] = p2.x;
             kent[i] = p2.z;
         }
@@ -63,22 +63,23 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
         for (int i = 0; i < kFwdBatch; ++i)
             asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
                          "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]));
+        // branch-free per entry: lanes that do not take it blend with alpha = 0 (T and C
+        // unchanged exactly); termination is a mask update
 #pragma unroll
         for (int i = 0; i < kFwdBatch; ++i) {
             if (j + (uint32_t)i >= j1) break;
             const float dx = fx - p0[i].x, dy = fy - p0[i].y;
             const float alpha = fminf(alpha_max, exp2_fast(exponent(p0[i], p1[i], dx, dy)));
-            if (live && alpha >= alpha_min) {
-                const float w = Tr * alpha;
-                cr = fmaf(w, p1[i].z, cr);
-                cg = fmaf(w, p1[i].w, cg);
-                cb = fmaf(w, blue[i], cb);
-                Tr = Tr * (1.0f - alpha);
-                if (Tr < t_min) {
-                    live = false;
-                    np = (int)__float_as_uint(kent[i]) - start + 1;
-                }
-            }
+            const bool take = live && alpha >= alpha_min;
+            const float a = take ? alpha : 0.0f;
+            const float w = Tr * a;
+            cr = fmaf(w, p1[i].z, cr);
+            cg = fmaf(w, p1[i].w, cg);
+            cb = fmaf(w, blue[i], cb);
+            Tr = Tr * (1.0f - a);
+            const bool stop = take && Tr < t_min;
+            np = stop ? (int)__float_as_uint(kent[i]) - start + 1 : np;
+            live = live && !stop;
         }
         if (__ballot(live) == 0) break;
     }
@@ -144,7 +145,8 @@ extern "C" gs_status gs_raster_fwd(const gs_projected *proj, const gs_bins *bins
     const RasterLayout L = raster_layout(0, bins->capacity, T);   // the fields read here do not depend on n
     const char *rb = static_cast<const char *>(bins->raster);
     k_raster_fwd<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
-        bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order), reinterpret_cast<const float4 *>(rb + L.qrec),
+        bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order),
+        reinterpret_cast<const float4 *>(rb + L.qrec) + kRecPad * kRecF4,
         reinterpret_cast<const uint64_t *>(rb + L.bitmap), reinterpret_cast<const uint32_t *>(rb + L.wpre), L.words,
         cam->width, cam->height, TX, T, p->alpha_min, p->alpha_max, p->t_min, color, t_final, n_trav);
     GS_LAUNCH_CHECK("k_raster_fwd");

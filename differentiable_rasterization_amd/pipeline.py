@@ -109,12 +109,12 @@ class Binning:
     def abi(self) -> B.Bins:
         return B.bins(self.ids, self.tile_ranges, self.raster, self.keys, self.tiles_touched)
 
-    def sort(self, proj: Projection, cam: B.Camera, stream=None) -> int:
+    def sort(self, proj: Projection, cam: B.Camera, params: B.RasterParams, stream=None) -> int:
         try:
-            k = B.gs_bin_sort(proj.abi(), self.n, cam, self.abi(), self.workspace, stream)
+            k = B.gs_bin_sort(proj.abi(), self.n, cam, params, self.abi(), self.workspace, stream)
         except B.GsCapacityError as e:
             self._alloc(int(math.ceil(e.required * 1.25)) + 1024)
-            k = B.gs_bin_sort(proj.abi(), self.n, cam, self.abi(), self.workspace, stream)
+            k = B.gs_bin_sort(proj.abi(), self.n, cam, params, self.abi(), self.workspace, stream)
         self.n_isect = k
         return k
 
@@ -150,7 +150,7 @@ class TrainStep:
 
     def forward(self, cam: B.Camera, stream=None):
         B.gs_project(self.params.gaussians(), cam, self.raster, self.proj.abi(), stream)
-        self.bins.sort(self.proj, cam, stream)
+        self.bins.sort(self.proj, cam, self.raster, stream)
         f = self.frame
         B.gs_raster_fwd(self.proj.abi(), self.bins.abi(), cam, self.raster, f.color, f.t_final, f.n_trav,
                         f.n_trav_sum, stream)

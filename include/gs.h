@@ -172,13 +172,15 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, i
  * for y).  Entries are ordered by (tile, depth key bits, Gaussian index): a stable LSD
  * radix sort of the Gaussians by depth key, a scan of their tile counts in that order,
  * emission, and a stable radix sort of the entries by tile id.  Then fills bins->raster
- * from the projected records (every field of `proj` is read).
+ * from the projected records (every field of `proj` is read): an entry joins the list of
+ * an 8x8 quadrant of its tile if its alpha >= p->alpha_min ellipse can reach one of the
+ * quadrant's pixel centres.  p must be the parameters given to gs_project.
  * Reads the total K back to the host (synchronises `stream`) and stores it in
  * *n_isect_out (host).  If K > bins->capacity returns GS_ERR_CAPACITY with K in
  * *n_isect_out and the lists unspecified.  workspace: device memory of at least
  * gs_bin_sort_workspace_bytes(n, capacity, W, H) bytes, 256-byte aligned. */
-gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, gs_bins *bins,
-                      int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
+gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, const gs_raster_params *p,
+                      gs_bins *bins, int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
 /* Front-to-back alpha compositing per 16x16 tile (ByteSplat Eq. 1): for each pixel,

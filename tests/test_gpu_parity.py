@@ -99,7 +99,7 @@ def _bin_gpu(m2, r, d, W, H, capacity=None):
         proj.radii[:n].copy_(r.to(DEV))
         proj.depth[:n].copy_(d.to(DEV))
     bins = PL.Binning(n, W, H, capacity=capacity or 0, device=DEV, with_keys=True, with_touched=True)
-    k = bins.sort(proj, cam)
+    k = bins.sort(proj, cam, B.make_params(0))
     torch.cuda.synchronize()
     return k, bins
 
@@ -134,7 +134,7 @@ def test_bin_sort_all_culled_and_capacity():
     proj.means2d.copy_(m2.to(DEV)); proj.radii.copy_(r.to(DEV)); proj.depth.copy_(d.to(DEV))
     small = PL.Binning(4000, 200, 150, capacity=10, device=DEV)
     with pytest.raises(B.GsCapacityError) as ei:
-        B.gs_bin_sort(proj.abi(), 4000, cam, small.abi(), small.workspace)
+        B.gs_bin_sort(proj.abi(), 4000, cam, B.make_params(0), small.abi(), small.workspace)
     assert ei.value.required == len(ids)
 
 
