@@ -92,7 +92,7 @@ _SIGS = {
     "gs_loss_workspace_bytes": (_sz, [_i64]),
     "gs_loss_l1": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "gs_raster_bwd": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp,
-                             _vp, _vp, _P(ParamGrads), _vp]),
+                             _vp, _vp, _vp, _P(ParamGrads), _vp]),
     "gs_project_bwd": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
     "gs_adam_step": (_i32, [_P(AdamGroup), _i32, _i32, _f32, _f32, _f32, _vp]),
     "gs_composite_over": (_i32, [_P(_vp), _P(_vp), _i32, _i64, _f32, _vp, _vp, _vp]),
@@ -183,7 +183,8 @@ def gs_bin_sort_workspace_bytes(n, capacity, width, height) -> int:
 
 
 def gs_bin_sort(proj: Projected, n, cam: Camera, p: RasterParams, b: Bins, workspace, stream=None) -> int:
-    """Returns K.  Raises GsCapacityError (with .required = K) if the lists are too small."""
+    """Returns K.  Raises GsCapacityError (with .required = the capacity needed) if the lists
+    are too small."""
     k = _i64(0)
     st = _lib.gs_bin_sort(ctypes.byref(proj), n, ctypes.byref(cam), ctypes.byref(p), ctypes.byref(b), ctypes.byref(k),
                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
@@ -206,10 +207,10 @@ def gs_loss_l1(color, target, n_px, loss_out, dL_dcolor, workspace, stream=None)
                            workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def gs_raster_bwd(g: Gaussians, proj: Projected, b: Bins, cam: Camera, p: RasterParams, t_final, n_trav, dL_dcolor,
-                  dL_dt, grads2d, grads3d: ParamGrads | None, stream=None):
+def gs_raster_bwd(g: Gaussians, proj: Projected, b: Bins, cam: Camera, p: RasterParams, color, t_final, n_trav,
+                  dL_dcolor, dL_dt, grads2d, grads3d: ParamGrads | None, stream=None):
     _check(_lib.gs_raster_bwd(ctypes.byref(g), ctypes.byref(proj), ctypes.byref(b), ctypes.byref(cam),
-                              ctypes.byref(p), _ptr(t_final), _ptr(n_trav), _ptr(dL_dcolor), _ptr(dL_dt),
+                              ctypes.byref(p), _ptr(color), _ptr(t_final), _ptr(n_trav), _ptr(dL_dcolor), _ptr(dL_dt),
                               _ptr(grads2d), ctypes.byref(grads3d) if grads3d is not None else None,
                               _stream(stream)))
 

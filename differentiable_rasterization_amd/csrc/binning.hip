@@ -25,26 +25,50 @@ __global__ __launch_bounds__(256) void k_depth_keys(const int2 *__restrict__ rad
     vals[i] = (uint32_t)i;
 }
 
-// Tile counts of the Gaussians in depth order (0 for culled ones); also records each
-// Gaussian's depth rank for the backward's per-Gaussian reduction.
+// Tile counts of the Gaussians in depth order (0 for culled ones) and the number of
+// (tile, 8x8 quadrant) pairs their ellipse reaches; also records each Gaussian's depth
+// rank for the backward's per-Gaussian reduction.
 __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skeys, const uint32_t *__restrict__ svals,
                                                const float2 *__restrict__ means2d, const int2 *__restrict__ radii,
-                                               int64_t n, int tx, int ty, uint32_t *__restrict__ cnt,
+                                               const float4 *__restrict__ conic_o, float alpha_min, int64_t n,
+                                               int tx, int ty, uint32_t *__restrict__ cnt, uint32_t *__restrict__ qcnt,
                                                uint32_t *__restrict__ drank)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n) return;
-    uint32_t c = 0;
+    uint32_t c = 0, qc = 0;
     const uint32_t g = svals[j];
     if (skeys[j] != kCulledKey) {
         const float2 m = means2d[g];
         const int2 r = radii[g];
+        const float4 co = conic_o[g];
+        const float thr = 2.0f * __logf(co.w / alpha_min);
         int x0, x1, y0, y1;
         gsd::tile_rect(m.x, m.y, r.x, r.y, tx, ty, x0, x1, y0, y1);
         c = (uint32_t)((x1 - x0) * (y1 - y0));
+        for (int y = y0; y < y1; ++y)
+            for (int x = x0; x < x1; ++x)
+                qc += __popc(gsr::quad_mask(m.x, m.y, co.x, co.y, co.z, thr, (float)(x * GS_TILE), (float)(y * GS_TILE)));
     }
     cnt[j] = c;
+    qcnt[j] = qc;
     drank[g] = (uint32_t)j;
+}
+
+// Sum of the quadrant-pair counts (one 64-bit atomic per block).
+__global__ __launch_bounds__(256) void k_sum_u32(const uint32_t *__restrict__ v, int64_t n,
+                                                 unsigned long long *__restrict__ total)
+{
+    __shared__ unsigned long long part[4];
+    unsigned long long acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) acc += v[i];
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_down(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned long long t = part[0] + part[1] + part[2] + part[3];
+        if (t) atomicAdd(total, t);
+    }
 }
 
 // Entries of each Gaussian in depth order, tiles row-major.  Entry p gets the key
@@ -196,7 +220,7 @@ __global__ __launch_bounds__(1024) void k_tile_order(const int32_t *__restrict__
 }
 
 struct Layout {
-    size_t dkA, dvA, dkB, dvB, cnt, total, tkA, tkB, tvA, tvB, gauss, hist, part, bytes;
+    size_t dkA, dvA, dkB, dvB, cnt, qcnt, total, tkA, tkB, tvA, tvB, gauss, hist, part, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -208,7 +232,7 @@ Layout layout(int64_t n, int64_t cap)
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     const size_t nn = (size_t)(n > 0 ? n : 1), cc = (size_t)(cap > 0 ? cap : 1);
     L.dkA = take(4 * nn); L.dvA = take(4 * nn); L.dkB = take(4 * nn); L.dvB = take(4 * nn);
-    L.cnt = take(4 * nn); L.total = take(8);
+    L.cnt = take(4 * nn); L.qcnt = take(4 * nn); L.total = take(16);   // K, then the quadrant pairs
     L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(4 * cc); L.tvB = take(4 * cc); L.gauss = take(4 * cc);
     const int64_t mmax = std::max<int64_t>(n, cap);
     const int64_t hl = gsi::radix_hist_len(mmax);
@@ -286,7 +310,7 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     char *ws = static_cast<char *>(workspace);
     uint32_t *dkA = (uint32_t *)(ws + L.dkA), *dvA = (uint32_t *)(ws + L.dvA);
     uint32_t *dkB = (uint32_t *)(ws + L.dkB), *dvB = (uint32_t *)(ws + L.dvB);
-    uint32_t *cnt = (uint32_t *)(ws + L.cnt);
+    uint32_t *cnt = (uint32_t *)(ws + L.cnt), *qcnt = (uint32_t *)(ws + L.qcnt);
     unsigned long long *total = (unsigned long long *)(ws + L.total);
     uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB);
     uint32_t *tvA = (uint32_t *)(ws + L.tvA), *tvB = (uint32_t *)(ws + L.tvB), *gauss = (uint32_t *)(ws + L.gauss);
@@ -303,15 +327,25 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     const uint32_t *sk = in_b ? dkB : dkA, *sv = in_b ? dvB : dvA;
 
     // 2. tile counts in depth order, their exclusive scan (the emit offsets) and the total K
-    k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, n, tx, ty, cnt, drank);
+    k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity), alpha_min,
+                                    n, tx, ty, cnt, qcnt, drank);
     GS_LAUNCH_CHECK("k_count");
     if ((s = exclusive_scan_u32(cnt, doff, n, part, total, stream)) != GS_OK) return s;
-    unsigned long long K = 0;
-    GS_HIP(hipMemcpyAsync(&K, total, sizeof(K), hipMemcpyDeviceToHost, stream));
+    if ((s = fill_i32(reinterpret_cast<int32_t *>(total + 1), 2, 0, stream)) != GS_OK) return s;
+    k_sum_u32<<<(unsigned)std::min<int64_t>(ceil_div(n, 256 * 8), 1024), 256, 0, stream>>>(qcnt, n, total + 1);
+    GS_LAUNCH_CHECK("k_sum_u32");
+    unsigned long long KQ[2] = {0, 0};
+    GS_HIP(hipMemcpyAsync(KQ, total, sizeof(KQ), hipMemcpyDeviceToHost, stream));
     GS_HIP(hipStreamSynchronize(stream));
+    const unsigned long long K = KQ[0];
+    // the quadrant records need kQuadFactor * capacity >= their count
+    const int64_t need = std::max<int64_t>((int64_t)K, ceil_div((int64_t)KQ[1], gsr::kQuadFactor));
     *n_isect_out = (int64_t)K;
-    if ((int64_t)K > bins->capacity)
-        return fail(GS_ERR_CAPACITY, "%llu intersections exceed the capacity %lld", K, (long long)bins->capacity);
+    if (need > bins->capacity) {
+        *n_isect_out = need;
+        return fail(GS_ERR_CAPACITY, "%llu intersections (%llu quadrant records) need a capacity of %lld, have %lld",
+                    K, KQ[1], (long long)need, (long long)bins->capacity);
+    }
 
     if (bins->tiles_touched) {
         k_touched<<<gn, 256, 0, stream>>>(sv, cnt, n, bins->tiles_touched);

@@ -2,7 +2,7 @@
 // rasterization kernels.
 //
 // Raster-ready lists (the gs_bins.raster buffer, written by gs_bin_sort):
-//   qrec   [4 * capacity] Rec     (plus kRecPad spare records at each end)
+//   qrec   [2 * capacity] Rec     (plus kRecPad spare records at each end)
 //                                 for each 8x8 quadrant q of every tile (qx = q & 1,
 //                                 qy = q >> 1), the records of the tile's entries whose
 //                                 alpha >= alpha_min box reaches the quadrant, in list
@@ -20,7 +20,7 @@
 //                                 doff[r] .. doff[r + 1] (doff[n] = K)
 //   jmap   [4 * capacity] uint32  position in qrec of emitted entry p's record in quadrant q
 //                                 (index 4 p + q), or ~0 if the entry is not in quadrant q
-//   qgrad  [4 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
+//   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
 //                                 padded to 48 bytes)
 //
 // Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
@@ -53,6 +53,9 @@ constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
 // of consecutive records can always be loaded from one base address (records outside the
 // lists are loaded but never used).
 constexpr int kRecPad = 4;
+// Quadrant records are stored for up to kQuadFactor * capacity (entry, quadrant) pairs
+// (an entry reaches 1.4 - 2 quadrants on average); more is reported as a capacity error.
+constexpr int kQuadFactor = 2;
 constexpr float kLn2 = 0.69314718055994531f;
 
 // Quadrant mask of an entry lives in bits 24..27 of its 32-bit tile key during the sort
@@ -112,7 +115,7 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     RasterLayout L;
     L.cap = capacity > 0 ? capacity : 1;
     L.words = (L.cap + 63) / 64;
-    const size_t nn = (size_t)(n > 0 ? n : 1), q4 = (size_t)kQuads * (size_t)L.cap;
+    const size_t nn = (size_t)(n > 0 ? n : 1), q4 = (size_t)kQuadFactor * (size_t)L.cap;
     size_t o = 0;
     L.qrec = o;   o += align256((q4 + 2 * kRecPad) * sizeof(Rec));   // kRecPad spare records at each end
     L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
@@ -120,7 +123,7 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);
     L.drank = o;  o += align256(nn * 4);
     L.doff = o;   o += align256(nn * 4);
-    L.jmap = o;   o += align256(q4 * 4);
+    L.jmap = o;   o += align256((size_t)kQuads * (size_t)L.cap * 4);
     L.qgrad = o;  o += align256(q4 * kGradSlot * 4);
     L.bytes = o;
     return L;

@@ -1,14 +1,17 @@
 // Backward rasterization (ByteSplat, section 2.1, Eq. 3 and Eq. 4).  Each pixel walks
-// the entries it traversed in the forward pass back to front, recovering
-// T_i = T_{i+1} / (1 - alpha_i) from the final transmittance, and forms the partial
+// the entries it traversed in the forward pass front to back, recomputing T_i exactly as
+// the forward pass did (T_1 = 1, T_{i+1} = T_i (1 - alpha_i)), and forms the partial
 // gradient of its loss with respect to the entry's screen-space fields:
 //   dL/dc_i     = T_i alpha_i G
-//   dL/dalpha_i = T_i (c_i - B_i) . G - G_T T_final / (1 - alpha_i),
-//                 B_i = colour composited behind i (B = 0 after the last entry,
-//                 B_{i-1} = alpha_i c_i + (1 - alpha_i) B_i)
+//   dL/dalpha_i = T_i c_i . G - (T_i B_i . G + G_T T_final) / (1 - alpha_i)
+//                 with T_i B_i = sum_{j>i} T_j alpha_j c_j / (1 - alpha_i) the colour
+//                 composited behind i, so T_i B_i . G (1 - alpha_i) = C . G - sum_{j<=i}
+//                 T_j alpha_j c_j . G, C the pixel's final colour from the forward pass
 //   unclamped alpha only: dL/dpower = dL/dalpha alpha, dL/do = dL/dpower / o,
 //   dA = -dx^2/2 dpower, dB = -dx dy dpower, dC = -dy^2/2 dpower,
 //   du = (A dx + B dy) dpower, dv = (B dx + C dy) dpower.
+// Walking front to back keeps T_i exact where T_final underflows (theta_T = 0 with deep
+// lists), which the back-to-front recovery T_i = T_{i+1} / (1 - alpha_i) cannot.
 // Aggregation over pixels (Eq. 4), without atomics: each lane forms the per-pixel moments
 //   S0 = dpower, Sx = dx S0, Sy = dy S0, Sxx = dx Sx, Sxy = dy Sx, Syy = dy Sy and the
 //   colour terms T_i alpha_i G for 4 records at a time, the wave sums the 36 values in one
@@ -22,10 +25,10 @@
 //   fixed order, so the gradients are deterministic.
 //
 // Lanes that do not take an entry run the same instructions with alpha = 0, which leaves
-// T and the colour behind unchanged and contributes zeros (no divergent branches).
+// T unchanged and contributes zeros (no divergent branches).
 //
 // One wave per 8x8 quadrant (see raster.h), walking its tile's record list for the
-// quadrant back to front from the furthest entry any of its pixels traversed; the slots
+// quadrant front to back up to the furthest entry any of its pixels traversed; the slots
 // of the records behind that point are set to zero.
 #include "kernels.h"
 #include "raster.h"
@@ -85,9 +88,9 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
                                                    const float4 *__restrict__ qrec, const uint64_t *__restrict__ bitmap,
                                                    const uint32_t *__restrict__ wpre, int64_t words, int W, int H,
                                                    int TX, int T, float alpha_min, float alpha_max,
-                                                   const float *__restrict__ t_final, const int32_t *__restrict__ n_trav,
-                                                   const float *__restrict__ dL_dc, const float *__restrict__ dL_dt,
-                                                   float *__restrict__ qgrad)
+                                                   const float *__restrict__ color, const float *__restrict__ t_final,
+                                                   const int32_t *__restrict__ n_trav, const float *__restrict__ dL_dc,
+                                                   const float *__restrict__ dL_dt, float *__restrict__ qgrad)
 {
     int tidx, q;
     raster_block(tidx, q);
@@ -98,19 +101,20 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const int py = (tile / TX) * GS_TILE + (q >> 1) * 8 + (lane >> 3);
     const bool inside = px < W && py < H;
     const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
-    float Tr = 1.0f, G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, gtf = 0.0f;
+    // Z = C . G + G_T T_final - sum_{j<=i} T_j alpha_j c_j . G  =  (T_i B_i . G + G_T T_final) (1 - alpha_i)
+    float G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, Z = 0.0f;
     int np = 0;
     if (inside) {
         const size_t idx = (size_t)py * W + px;
-        Tr = t_final[idx];
         np = n_trav[idx];
         G0 = dL_dc[3 * idx];
         G1 = dL_dc[3 * idx + 1];
         G2 = dL_dc[3 * idx + 2];
-        if (HAS_GT) gtf = dL_dt[idx] * Tr;
+        Z = fmaf(color[3 * idx], G0, fmaf(color[3 * idx + 1], G1, color[3 * idx + 2] * G2));
+        if (HAS_GT) Z = fmaf(dL_dt[idx], t_final[idx], Z);
     }
     const int start = ranges[tile], end = ranges[tile + 1];
-    // the wave walks back from the furthest entry any of its pixels traversed
+    // the wave walks up to the furthest entry any of its pixels traversed
     const int nmax = max(0, min(gsd::wave_max_i32(np), end - start));
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
@@ -119,26 +123,23 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     // records never reached by any pixel of the quadrant contribute nothing
     for (size_t z = (size_t)j1 * kGradSlot + lane; z < (size_t)jend * kGradSlot; z += 64) qgrad[z] = 0.0f;
     const int row = lane >> 4, field = lane & 15;
-    float B0 = 0.0f, B1 = 0.0f, B2 = 0.0f;
-    // L2 prefetch of the next chunk of 64 records ahead of the (descending) scalar reads
-    auto chunk = [&](uint32_t hi) { return hi > j0 + 64u ? hi - 64u : j0; };
-    uint32_t sink = prefetch_records(qrec, chunk(j1), j1);
-    uint32_t pend = prefetch_records(qrec, chunk(chunk(j1)), chunk(j1));
-    for (uint32_t jt = j1; jt > j0;) {
-        if (((j1 - jt) & 63u) == 0u && jt < j1) {
+    float Tr = 1.0f;
+    // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
+    uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
+    for (uint32_t jt = j0; jt < j1;) {
+        if (((jt - j0) & 63u) == 0u && jt > j0) {
             sink ^= pend;
-            pend = prefetch_records(qrec, chunk(chunk(jt)), chunk(jt));
+            pend = prefetch_records(qrec, jt + 64u, j1);
         }
-        // records jt-1, jt-2, ... (back to front); one wait per batch
+        // records jt .. jt+3 (past j1: spare, unused); one wait per batch
         float4 p0[kBwdBatch], p1[kBwdBatch];
         float blue[kBwdBatch], kent[kBwdBatch];
-        // records jt-1, jt-2, jt-3, jt-4 from one base (before j0: spare, unused)
-        const float4 *rb = qrec + kRecF4 * ((int64_t)jt - kBwdBatch);
+        const float4 *rb = qrec + kRecF4 * (size_t)jt;
 #pragma unroll
         for (int i = 0; i < kBwdBatch; ++i) {
-            p0[i] = rb[kRecF4 * (kBwdBatch - 1 - i)];
-            p1[i] = rb[kRecF4 * (kBwdBatch - 1 - i) + 1];
-            const float4 p2 = rb[kRecF4 * (kBwdBatch - 1 - i) + 2];
+            p0[i] = rb[kRecF4 * i];
+            p1[i] = rb[kRecF4 * i + 1];
+            const float4 p2 = rb[kRecF4 * i + 2];
             blue[i] = p2.x;
             kent[i] = p2.z;
         }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         for (int i = 0; i < kBwdBatch; ++i)
             asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
                          "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]));
-        const uint32_t cnt = min((uint32_t)kBwdBatch, jt - j0);
+        const uint32_t cnt = min((uint32_t)kBwdBatch, j1 - jt);
         float v[kBwdBatch * kFields];
         bool any = false;
 #pragma unroll
@@ -155,33 +156,33 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
             const int rel = (int)__float_as_uint(kent[i]) - start;
             const float dx = fx - p0[i].x, dy = fy - p0[i].y;
             const float raw = exp2_fast(exponent(p0[i], p1[i], dx, dy));
-            const bool acc = (uint32_t)i < cnt && rel < np && raw >= alpha_min;   // alpha >= alpha_min
-            const float alpha = acc ? fminf(alpha_max, raw) : 0.0f;
-            const float ro = __builtin_amdgcn_rcpf(1.0f - alpha);
-            const float Ti = Tr * ro;
-            const float w = Ti * alpha;
+            // the forward pass's alpha and T, bit for bit
+            const float alpha = fminf(alpha_max, raw);
+            const bool take = (uint32_t)i < cnt && rel < np && alpha >= alpha_min;
+            const float a = take ? alpha : 0.0f;
+            const float om = 1.0f - a;
+            const float ro = __builtin_amdgcn_rcpf(om);
+            const float w = Tr * a;
             o[6] = w * G0;
             o[7] = w * G1;
             o[8] = w * G2;
-            float dal = Ti * ((p1[i].z - B0) * G0 + (p1[i].w - B1) * G1 + (blue[i] - B2) * G2);
-            if (HAS_GT) dal -= gtf * ro;
-            const float s0 = raw < alpha_max ? dal * alpha : 0.0f;   // clamped alpha has no power gradient
+            const float cg = fmaf(p1[i].z, G0, fmaf(p1[i].w, G1, blue[i] * G2));
+            Z = fmaf(-w, cg, Z);
+            const float dal = fmaf(Tr, cg, -ro * Z);
+            const float s0 = dal * (raw < alpha_max ? a : 0.0f);   // clamped alpha has no power gradient
             o[0] = s0;
             o[1] = dx * s0;
             o[2] = dy * s0;
             o[3] = dx * o[1];
             o[4] = dy * o[1];
             o[5] = dy * o[2];
-            B0 = fmaf(alpha, p1[i].z - B0, B0);
-            B1 = fmaf(alpha, p1[i].w - B1, B1);
-            B2 = fmaf(alpha, blue[i] - B2, B2);
-            Tr = acc ? Ti : Tr;
-            any |= acc;
+            Tr = Tr * om;
+            any |= take;
         }
-        // slot of the batch's record e = row: record jt - 1 - e, field f = lane & 15
-        float *dst = qgrad + ((size_t)(jt - 1u - (uint32_t)min(row, (int)cnt - 1))) * kGradSlot + field;
+        // slot of the batch's record e = row: record jt + e, field f = lane & 15
+        float *dst = qgrad + ((size_t)(jt + (uint32_t)min(row, (int)cnt - 1))) * kGradSlot + field;
         const bool writer = (uint32_t)row < cnt && field < kFields;
-        jt -= cnt;
+        jt += cnt;
         if (__ballot(any) == 0) {
             if (writer) *dst = 0.0f;
             continue;
@@ -247,8 +248,9 @@ gs_status check_raster_inputs(const gs_bins *bins, const gs_camera *cam);
 }
 
 extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
-                                   const gs_camera *cam, const gs_raster_params *p, const float *t_final,
-                                   const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt, float *grads2d,
+                                   const gs_camera *cam, const gs_raster_params *p, const float *color,
+                                   const float *t_final, const int32_t *n_trav, const float *dL_dcolor,
+                                   const float *dL_dt, float *grads2d,
                                    gs_param_grads *grads3d, hipStream_t stream)
 {
     using namespace gsi;
@@ -258,8 +260,8 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
     if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
-    if (!t_final || !n_trav || !dL_dcolor || (g->n > 0 && !grads2d))
-        return fail(GS_ERR_INVALID_ARGUMENT, "t_final / n_trav / dL_dcolor / grads2d is NULL");
+    if (!color || !t_final || !n_trav || !dL_dcolor || (g->n > 0 && !grads2d))
+        return fail(GS_ERR_INVALID_ARGUMENT, "color / t_final / n_trav / dL_dcolor / grads2d is NULL");
     const int64_t n = g->n;
     const int TX = tiles_x(cam->width), T = TX * tiles_y(cam->height);
     const RasterLayout L = raster_layout(n, bins->capacity, T);
@@ -273,12 +275,12 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
     if (n > 0) {
         if (dL_dt)
             k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
-                                                        cam->height, TX, T, p->alpha_min, p->alpha_max, t_final,
-                                                        n_trav, dL_dcolor, dL_dt, qg);
+                                                        cam->height, TX, T, p->alpha_min, p->alpha_max, color,
+                                                        t_final, n_trav, dL_dcolor, dL_dt, qg);
         else
             k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
-                                                         cam->height, TX, T, p->alpha_min, p->alpha_max, t_final,
-                                                         n_trav, dL_dcolor, nullptr, qg);
+                                                         cam->height, TX, T, p->alpha_min, p->alpha_max, color,
+                                                         t_final, n_trav, dL_dcolor, nullptr, qg);
         GS_LAUNCH_CHECK("k_raster_bwd");
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
             reinterpret_cast<const uint32_t *>(rb + L.drank), reinterpret_cast<const uint32_t *>(rb + L.doff),

@@ -31,11 +31,10 @@ def step_bytes_per_gaussian(sh_degree: int) -> int:
 
 
 def step_bytes_per_intersection() -> int:
-    """Intersection lists: ids (4); the raster-ready lists, sized for the worst case of an
-    entry in all four 8x8 quadrants of its tile: records (4 x 48), map words (4 x 4) and
-    per-record gradient slots (4 x 48), plus quadrant bits (1); and the sort workspace's
-    key, value and Gaussian buffers (20)."""
-    return 4 + 4 * (48 + 4 + 48) + 1 + 20
+    """Intersection lists: ids (4); the raster-ready lists with room for two 8x8-quadrant
+    records per entry (2 x 48) and their gradient slots (2 x 48), map words (4 x 4) and
+    quadrant bits (1); and the sort workspace's key, value and Gaussian buffers (20)."""
+    return 4 + 2 * (48 + 48) + 16 + 1 + 20
 
 
 def max_gaussians(hbm_bytes: float, sh_degree: int, adam: bool = True) -> int:

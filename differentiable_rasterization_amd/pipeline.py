@@ -161,8 +161,8 @@ class TrainStep:
 
     def backward_raster(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):
         f = self.frame
-        B.gs_raster_bwd(self.params.gaussians(), self.proj.abi(), self.bins.abi(), cam, self.raster, f.t_final,
-                        f.n_trav, f.dL_dcolor if dL_dcolor is None else dL_dcolor, dL_dt, self.grads2d, None,
+        B.gs_raster_bwd(self.params.gaussians(), self.proj.abi(), self.bins.abi(), cam, self.raster, f.color,
+                        f.t_final, f.n_trav, f.dL_dcolor if dL_dcolor is None else dL_dcolor, dL_dt, self.grads2d, None,
                         stream)
 
     def backward_project(self, cam: B.Camera, stream=None):

@@ -157,8 +157,8 @@ gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raste
                      gs_projected *out, hipStream_t stream);
 
 /* Bytes of the gs_bins.raster buffer for n Gaussians, `capacity` list entries and a W x H
- * image: at most 4 quadrant records (48 B), 4 map words and 4 gradient slots (48 B) per
- * entry, plus 8 B per Gaussian and 4 B per tile. */
+ * image: 2 quadrant records (48 B) and 2 gradient slots (48 B), 4 map words and 4 quadrant bits
+ * per entry, plus 8 B per Gaussian and 4 B per tile. */
 size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
 
 /* Workspace bytes gs_bin_sort needs for n Gaussians, `capacity` list entries and the
@@ -176,8 +176,9 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, i
  * an 8x8 quadrant of its tile if its alpha >= p->alpha_min ellipse can reach one of the
  * quadrant's pixel centres.  p must be the parameters given to gs_project.
  * Reads the total K back to the host (synchronises `stream`) and stores it in
- * *n_isect_out (host).  If K > bins->capacity returns GS_ERR_CAPACITY with K in
- * *n_isect_out and the lists unspecified.  workspace: device memory of at least
+ * *n_isect_out (host).  The quadrant records take up to 2 * capacity slots, so a capacity
+ * below max(K, ceil(Q / 2)) (Q = the number of (entry, quadrant) pairs) returns
+ * GS_ERR_CAPACITY with that required capacity in *n_isect_out and the lists unspecified.  workspace: device memory of at least
  * gs_bin_sort_workspace_bytes(n, capacity, W, H) bytes, 256-byte aligned. */
 gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, const gs_raster_params *p,
                       gs_bins *bins, int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
@@ -206,18 +207,20 @@ gs_status gs_loss_l1(const float *color, const float *target, int64_t n_px, floa
                      float *dL_dcolor, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward rasterization (ByteSplat Eq. 3 and Eq. 4): per tile, each pixel walks its
- * traversed entries back to front, recovers T_i = T_{i+1} / (1 - alpha_i), and forms its
- * partial gradient of the Gaussian's 9 screen-space fields, in the order
- * (u, v, A, B, C, o, r, g, b) of grads2d [9][n].  The partial gradients are summed per
- * tile quadrant and then per Gaussian in a fixed order (no atomics): repeated calls give
- * bit-identical results.  Every entry of grads2d is written (zero for culled Gaussians).
- * dL_dcolor [H][W][3]; dL_dt [H][W] is the gradient of t_final (may be NULL).  t_final
- * and n_trav come from gs_raster_fwd on the same inputs.  If grads3d is non-NULL the
- * aggregated screen-space gradients are then propagated through projection and colour
- * evaluation into grads3d (every entry overwritten; zero for culled Gaussians). */
+ * traversed entries front to back, recomputing T_i as the forward pass did, takes the
+ * colour composited behind entry i from the forward pass's final colour (T_i B_i (1 -
+ * alpha_i) = C - sum_{j<=i} T_j alpha_j c_j), and forms its partial gradient of the
+ * Gaussian's 9 screen-space fields, in the order (u, v, A, B, C, o, r, g, b) of grads2d
+ * [9][n].  The partial gradients are summed per tile quadrant and then per Gaussian in a
+ * fixed order (no atomics): repeated calls give bit-identical results.  Every entry of
+ * grads2d is written (zero for culled Gaussians).  dL_dcolor [H][W][3]; dL_dt [H][W] is
+ * the gradient of t_final (may be NULL).  color, t_final and n_trav come from
+ * gs_raster_fwd on the same inputs.  If grads3d is non-NULL the aggregated screen-space
+ * gradients are then propagated through projection and colour evaluation into grads3d
+ * (every entry overwritten; zero for culled Gaussians). */
 gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
-                        const gs_camera *cam, const gs_raster_params *p, const float *t_final,
-                        const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt,
+                        const gs_camera *cam, const gs_raster_params *p, const float *color,
+                        const float *t_final, const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt,
                         float *grads2d, gs_param_grads *grads3d, hipStream_t stream);
 
 /* Backward through projection and colour evaluation alone (ByteSplat section 2.1: the

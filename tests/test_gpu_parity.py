@@ -223,6 +223,34 @@ def test_backward_parity(name, with_gt):
     assert torch.equal(st.grads2d, first) and torch.equal(gp.grad, first3)
 
 
+@pytest.mark.parametrize("with_gt", [False, True])
+def test_backward_deep_stack_no_termination(with_gt):
+    """theta_T = 0 over lists of ~1300 near-opaque entries: T_final is exactly 0 in float32
+    at about 30% of the pixels (the oracle's, in double, is as small as 1e-231), so the
+    front entries' T_i cannot be recovered from T_final; the backward must still match."""
+    log(f"backward deep stack theta_T=0 with_gt={with_gt}")
+    sc = scenes.scene_small_random(15, 3000, 72, 40, 1, extent=0.6, distance=3.0, log_scale_mean=-2.0,
+                                   logit_mean=4.0)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree, t_min=0.0)
+    op = oracle_params(rp)
+    st = gpu_forward(sc, cam, rp)
+    P = oracle.project(sc, cam, op)
+    c, tf, nt, tie = oracle.render(P, op)
+    assert (tf.astype(np.float32) == 0).mean() > 0.2     # the case this test is about
+    compare_images(st.frame.color.cpu().numpy(), st.frame.t_final.cpu().numpy(), c, tf, tie)
+    G = _oracle_G(c, sc.targets[0].numpy())
+    GT = (np.random.default_rng(6).normal(size=tf.shape)).astype(np.float32) if with_gt else None
+    g2_o = oracle.raster_backward(P, G.astype(np.float64), None if GT is None else GT.astype(np.float64), op)
+    st.backward(B.camera_from(cam), dL_dcolor=torch.from_numpy(G).to(DEV),
+                dL_dt=torch.from_numpy(GT).to(DEV) if GT is not None else None, grads3d=False)
+    torch.cuda.synchronize()
+    g2 = st.grads2d.cpu().numpy()
+    errs = {oracle.G_FIELDS[f]: rel_l2(g2[f], g2_o[f]) for f in range(9)}
+    log(f"  grads2d rel-L2 {errs}")
+    assert max(errs.values()) <= 1e-3, errs
+
+
 # ------------------------------------------------------------------ Adam
 
 @pytest.mark.parametrize("n,step", [(1, 1), (1001, 1), (4096, 7), (250_001, 3)])

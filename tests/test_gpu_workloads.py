@@ -1,0 +1,271 @@
+"""Parity of the HIP path with the CPU oracle at the sizes of the measured workloads.
+GPU only.
+
+* 1M Gaussians, SH3, 1080p (two of its four views) and 10M Gaussians, SH3, skewed
+  clusters, 4K: binning bit-exact from identical projected inputs (the oracle's float
+  records are loaded into both binnings); images, final transmittance and N_p on bands of
+  rows the oracle renders pixel by pixel; screen-space gradients with the loss gradient
+  restricted to those rows (so both sides sum the same pixels).
+* 20M Gaussians in four depth slabs, 4K (full size): properties that hold at any size --
+  the over-composited partial renders equal the unpartitioned render (Splaxel, section 4.2),
+  the gradients through the composite equal the unpartitioned gradients, and the
+  compacted records scatter back to the dense gradients (ByteSplat, section 6).
+* The same partitioned recipe at 200K Gaussians: partial renders, composite, composite
+  backward and per-slab gradients against the oracle.
+"""
+import gc
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from differentiable_rasterization_amd import binding as B
+from differentiable_rasterization_amd import pipeline as PL
+from differentiable_rasterization_amd import scenes
+from tests.gpu_util import DEV, compare_images, log, oracle_params, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _band(width, y0, rows):
+    return np.stack([np.tile(np.arange(width, dtype=np.int32), rows),
+                     np.repeat(np.arange(y0, y0 + rows, dtype=np.int32), width)], axis=1).copy()
+
+
+def _upload_projected(P, n):
+    """The oracle's float32 projected records as the input of the GPU binning."""
+    proj = PL.Projection(n, DEV)
+    proj.means2d.copy_(torch.from_numpy(P.rec[:, :2].astype(np.float32)))
+    proj.radii.copy_(torch.from_numpy(P.radii))
+    proj.depth.copy_(torch.from_numpy(P.dkey))
+    co = np.zeros((n, 4), np.float32)
+    co[:, :3] = P.rec[:, 2:5]
+    co[:, 3] = P.rec[:, 5]
+    proj.conic_opacity.copy_(torch.from_numpy(co))
+    return proj
+
+
+def _check_binning(P, cam, n, rp):
+    tt, keys, ids, ranges = oracle.bin_f32(P.rec[:, :2].astype(np.float32), P.radii, P.dkey, cam.width,
+                                           cam.height)
+    proj = _upload_projected(P, n)
+    bins = PL.Binning(n, cam.width, cam.height, capacity=len(ids), device=DEV, with_keys=True,
+                      with_touched=True)
+    k = bins.sort(proj, B.camera_from(cam), rp)
+    torch.cuda.synchronize()
+    assert k == len(ids)
+    assert np.array_equal(bins.tile_ranges.cpu().numpy(), ranges)
+    assert np.array_equal(bins.tiles_touched.cpu().numpy(), tt)
+    assert np.array_equal(bins.ids[:k].cpu().numpy().view(np.uint32), ids)
+    assert np.array_equal(bins.keys[:k].cpu().numpy().view(np.uint64), keys)
+    del proj, bins
+    return k
+
+
+def _band_parity(sc, view, bands, check_bins=True):
+    """Forward on the whole image, compared on bands of rows; backward with the L1
+    gradient of those rows only."""
+    cam = sc.cameras[view]
+    W, H = cam.width, cam.height
+    rp = B.make_params(sc.sh_degree)
+    op = oracle_params(rp)
+    log(f"  oracle projection of {sc.n} Gaussians, view {view}")
+    P = oracle.project(sc, cam, op)
+    if check_bins:
+        k = _check_binning(P, cam, sc.n, rp)
+        log(f"  binning bit-exact, K = {k}")
+    params = PL.GaussianParams.from_scene(sc, DEV)
+    st = PL.TrainStep(params, W, H, DEV, raster=rp)
+    c = B.camera_from(cam)
+    st.forward(c)
+    torch.cuda.synchronize()
+    pix = np.concatenate([_band(W, y0, rows) for y0, rows in bands])
+    log(f"  oracle render of {len(pix)} pixels")
+    col, tf, nt, tie = oracle.render(P, op, pixels=pix)
+    gc_ = st.frame.color.cpu().numpy()[pix[:, 1], pix[:, 0]]
+    gt_ = st.frame.t_final.cpu().numpy()[pix[:, 1], pix[:, 0]]
+    gn_ = st.frame.n_trav.cpu().numpy()[pix[:, 1], pix[:, 0]]
+    stats = compare_images(gc_, gt_, col, tf, tie)
+    mism = (gn_ != nt) & ~tie
+    assert mism.sum() <= max(2, 1e-4 * len(pix)), (int(mism.sum()), stats)
+    log(f"  image {stats}")
+    # backward: L1 gradient of the band pixels (oracle image), zero elsewhere
+    target = sc.targets[view].numpy()[pix[:, 1], pix[:, 0]]
+    _, G = oracle.loss_l1(col.astype(np.float32), target)
+    G = G.astype(np.float32).reshape(-1, 3)
+    Gfull = np.zeros((H, W, 3), np.float32)
+    Gfull[pix[:, 1], pix[:, 0]] = G
+    st.backward(c, dL_dcolor=torch.from_numpy(Gfull).to(DEV), grads3d=False)
+    torch.cuda.synchronize()
+    log("  oracle backward of the band")
+    g2o = oracle.raster_backward(P, G.astype(np.float64), None, op, pixels=pix)
+    g2 = st.grads2d.cpu().numpy()
+    errs = {oracle.G_FIELDS[f]: rel_l2(g2[f], g2o[f]) for f in range(9)}
+    log(f"  grads2d rel-L2 {errs}")
+    assert max(errs.values()) <= 1e-3, errs
+    del st, params, P
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_1m_1080p_sampled_parity():
+    log("1M 1080p")
+    sc = scenes.scene_1m_1080p()
+    _band_parity(sc, 0, [(500, 48), (100, 8)])
+    _band_parity(sc, 2, [(540, 32)], check_bins=False)
+
+
+def test_10m_4k_skewed_sampled_parity():
+    log("10M 4K skewed")
+    sc = scenes.scene_skewed_4k()
+    # rows through the dense centre of the image and one off-centre band
+    _band_parity(sc, 0, [(1072, 8), (300, 4)])
+
+
+def _partition_run(sc, t_min, G=None):
+    """Unpartitioned and partitioned renders of view 0 on the GPU (depth windows in
+    gs_project), the composite, and (if G is given) the backward of both with dL/dC = G."""
+    cam = sc.cameras[0]
+    W, H = cam.width, cam.height
+    n_px = W * H
+    c = B.camera_from(cam)
+    params = PL.GaussianParams.from_scene(sc, DEV)
+    out = {}
+    st = PL.TrainStep(params, W, H, DEV, raster=B.make_params(sc.sh_degree, t_min=t_min))
+    st.forward(c)
+    out["full"] = (st.frame.color.clone(), st.frame.t_final.clone())
+    if G is not None:
+        st.backward(c, dL_dcolor=G, grads3d=False)
+        out["full_g2"] = st.grads2d.clone()
+    del st
+    torch.cuda.empty_cache()
+    slabs = []
+    for lo, hi in sc.depth_slabs:
+        rp = B.make_params(sc.sh_degree, t_min=t_min, depth_lo=lo, depth_hi=hi)
+        s = PL.TrainStep(params, W, H, DEV, raster=rp)
+        s.forward(c)
+        slabs.append(s)
+    cs = [s.frame.color for s in slabs]
+    ts = [s.frame.t_final for s in slabs]
+    comp_c = torch.zeros(H, W, 3, device=DEV)
+    comp_t = torch.zeros(H, W, device=DEV)
+    B.gs_composite_over(cs, ts, n_px, t_min, comp_c, comp_t)
+    out["comp"] = (comp_c, comp_t)
+    out["slabs"] = slabs
+    if G is not None:
+        dcs = [torch.zeros(H, W, 3, device=DEV) for _ in slabs]
+        dts = [torch.zeros(H, W, device=DEV) for _ in slabs]
+        B.gs_composite_over_bwd(cs, ts, n_px, t_min, G, None, dcs, dts)
+        g2 = torch.zeros_like(out["full_g2"])
+        for s, dc, dt in zip(slabs, dcs, dts):
+            s.backward(c, dL_dcolor=dc, dL_dt=dt, grads3d=False)
+            g2 += s.grads2d     # each Gaussian lies in one slab; the others give it zeros
+        out["part_g2"] = g2
+        out["dcs"], out["dts"] = dcs, dts
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_records(g2):
+    """ByteSplat section 6: the compacted records are exactly the Gaussians with a
+    non-zero field, in ascending order, and scatter back to the dense gradients."""
+    n = g2.shape[1]
+    records = torch.zeros(n, 10, dtype=torch.int32, device=DEV)
+    bitmap = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    ws = torch.empty(B.gs_compact_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    R = B.gs_compact_grads(g2, n, 0, records, bitmap, ws)
+    dense = g2.cpu().numpy()
+    nz = (dense != 0).any(axis=0)
+    assert R == int(nz.sum())
+    rec = records[:R].cpu().numpy().view(np.uint32)
+    idx = rec[:, 0].astype(np.int64)
+    assert np.array_equal(idx, np.nonzero(nz)[0])
+    assert np.array_equal(rec[:, 1:].view(np.float32).T.view(np.uint32), dense[:, idx].view(np.uint32))
+    bits = np.unpackbits(bitmap.cpu().numpy().view(np.uint8), bitorder="little")[:n].astype(bool)
+    assert np.array_equal(bits, nz)
+    return R
+
+
+def test_20m_4k_partitioned_properties():
+    log("20M 4K, 4 depth slabs")
+    sc = scenes.scene_partitioned_4k()
+    cam = sc.cameras[0]
+    H, W = cam.height, cam.width
+    # theta_T = 0: the partitions are an exact split, composite == unpartitioned up to fp32
+    tgt = sc.targets[0].to(DEV)
+    probe = _partition_run(sc, 0.0)
+    comp_c, comp_t = probe["comp"]
+    G = (torch.sign(comp_c - tgt) / (3 * H * W)).contiguous()
+    del probe
+    torch.cuda.empty_cache()
+    out = _partition_run(sc, 0.0, G)
+    fc, ft = out["full"]
+    cc, ct = out["comp"]
+    dc = float((fc - cc).abs().max())
+    dt = float((ft - ct).abs().max())
+    log(f"  theta_T = 0: composite vs unpartitioned max |dC| {dc:.2e} |dT| {dt:.2e}")
+    assert dc <= 2e-5 and dt <= 2e-5
+    e = rel_l2(out["part_g2"].cpu().numpy(), out["full_g2"].cpu().numpy())
+    log(f"  gradients through the composite vs unpartitioned rel-L2 {e:.2e}")
+    assert e <= 1e-4
+    for k, s in enumerate(out["slabs"]):
+        R = _check_records(s.grads2d)
+        log(f"  slab {k}: {R} non-zero records of {s.params.n}")
+    del out
+    torch.cuda.empty_cache()
+    # theta_T = 1e-4: termination inside a slab differs from the global one by at most
+    # theta_T times a colour
+    out = _partition_run(sc, 1e-4)
+    fc, ft = out["full"]
+    cc, ct = out["comp"]
+    cmax = float(fc.abs().max())
+    dc = float((fc - cc).abs().max())
+    log(f"  theta_T = 1e-4: composite vs unpartitioned max |dC| {dc:.2e} (bound {1e-4 * max(1.0, cmax):.2e})")
+    assert dc <= 1e-4 * max(1.0, cmax) + 2e-5
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_partitioned_small_against_oracle():
+    log("partitioned recipe at 200K, 960x540")
+    sc = scenes.scene_partitioned_4k(n=200_000, width=960, height=540)
+    cam = sc.cameras[0]
+    H, W = cam.height, cam.width
+    t_min = 1e-4
+    # oracle: partial renders, composite, composite backward, per-slab gradients
+    orc = []
+    for lo, hi in sc.depth_slabs:
+        rp = B.make_params(sc.sh_degree, t_min=t_min, depth_lo=lo, depth_hi=hi)
+        op = oracle_params(rp)
+        P = oracle.project(sc, cam, op)
+        col, tf, nt, tie = oracle.render(P, op)
+        orc.append((P, op, col, tf, tie))
+    cs_o = [o[2].astype(np.float32) for o in orc]
+    ts_o = [o[3].astype(np.float32) for o in orc]
+    comp_o, compt_o = oracle.composite(cs_o, ts_o, float(np.float32(t_min)))
+    _, G = oracle.loss_l1(comp_o.astype(np.float32), sc.targets[0].numpy())
+    G = G.astype(np.float32).reshape(H, W, 3)
+    dcs_o, dts_o = oracle.composite_bwd(cs_o, ts_o, float(np.float32(t_min)), G)
+    out = _partition_run(sc, t_min, torch.from_numpy(G).to(DEV))
+    tie_any = np.zeros((H, W), bool)
+    for k, (P, op, col, tf, tie) in enumerate(orc):
+        s = out["slabs"][k]
+        stats = compare_images(s.frame.color.cpu().numpy(), s.frame.t_final.cpu().numpy(), col, tf, tie)
+        log(f"  slab {k} partial render {stats}")
+        tie_any |= tie
+    comp_c, comp_t = out["comp"]
+    compare_images(comp_c.cpu().numpy(), comp_t.cpu().numpy(), comp_o.reshape(H, W, 3), compt_o.reshape(H, W),
+                   tie_any)
+    for k, (P, op, col, tf, tie) in enumerate(orc):
+        # the composite backward on the GPU partials matches the oracle's on its own partials
+        assert np.abs(out["dcs"][k].cpu().numpy().reshape(-1, 3) - dcs_o[k])[~tie_any.reshape(-1)].max() <= 1e-5
+        dts_g = out["dts"][k].cpu().numpy().reshape(-1)
+        assert np.abs(dts_g - dts_o[k])[~tie_any.reshape(-1)].max() <= 1e-4 * max(1.0, np.abs(dts_o[k]).max())
+        g2o = oracle.raster_backward(P, dcs_o[k].reshape(H, W, 3), dts_o[k].reshape(H, W), op)
+        g2 = out["slabs"][k].grads2d.cpu().numpy()
+        errs = {oracle.G_FIELDS[f]: rel_l2(g2[f], g2o[f]) for f in range(9)}
+        log(f"  slab {k} grads2d rel-L2 {errs}")
+        assert max(errs.values()) <= 1e-3, errs
+        _check_records(out["slabs"][k].grads2d)
