@@ -1,10 +1,11 @@
 """Benchmark of the one-GPU 3D Gaussian splatting training step on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m|100k|10m] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m|100k|10m|tiny] [--no-cpu-baseline]
+                    [--cpu-rows R] [--copy-calibration-mib M]
 
 A step is one training iteration on one view: gs_project -> gs_bin_sort ->
-gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd -> gs_project_bwd -> gs_adam_step,
-on seeded synthetic data already resident in HBM.  The default workload is 1M
+gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd (gs_raster_bwd_partials, gs_grad_aggregate)
+-> gs_project_bwd -> gs_adam_step, on seeded synthetic data already resident in HBM.  The default workload is 1M
 Gaussians (SH degree 3, 64 clusters in a 20 m cube) at 1920x1080 with four
 cameras on a sphere of radius 25; steps cycle through the four views.
 
@@ -12,6 +13,14 @@ Prints one JSON line: value = Gaussian-pixel intersections (sum over pixels of t
 number of list entries each pixel composites, N_p of Eq. 1 in ByteSplat section 2.1)
 per second of whole training step; ms_per_step = train-step milliseconds.  Per-kernel
 times come from HIP events recorded on the stream the kernels run on.
+
+roofline: the dominant kernel, k_raster_bwd (one launch per step), is bound by VALU
+arithmetic; its algorithmic work is FLOP_PER_PAIR["raster_bwd"] floating-point
+operations per Gaussian-pixel pair.  roofline.traffic is the HBM traffic of one launch
+from the stored counter summary (profiles/), or null if the kernel's sources changed
+since those counters were taken.  --copy-calibration-mib runs a plain copy-like kernel of
+known size before the timed steps, for the counter runs that normalise FETCH_SIZE and
+WRITE_SIZE.
 """
 from __future__ import annotations
 
@@ -29,25 +38,26 @@ HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3          # published MI355X vector fp32 (packed FMA)
 FP32_NONPACKED_TFLOPS = 78.6             # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
 
-# Algorithmic floating-point work per Gaussian-pixel evaluation (a fused multiply-add
-# counts 2, exp2 / reciprocal 1), from the operations of Eq. 1 and Eq. 3:
-#  forward  : dx, dy (2); exponent a dx^2 + b dx dy + c dy^2 + log2 o (8); exp2 (1);
-#             clamp (1); alpha-check (1); w = T alpha (1); C += w c (6); T *= 1 - alpha (2)
-#  backward : forward's exponent, exp2, clamp, check (13); T recovery (2); w (1);
-#             colour grads (6); dL/dalpha (3 sub + 3 fma + 1 mul = 10); dpower (1);
-#             opacity grad (2); conic / mean moment sums (5); B update (9)
-FWD_FLOP_PER_ISECT = 22
-BWD_FLOP_PER_ISECT = 49
+# Algorithmic floating-point work per Gaussian-pixel pair, from the operation lists of
+# ByteSplat Eq. 1 (forward: offset, quadratic form, exp, clamp and alpha-check, blend,
+# transmittance update: 26 flop + 1 exp) and Eq. 3 / Eq. 4 (backward: the forward's alpha,
+# T recovery, colour and alpha gradients, colour-behind update, power / conic / mean /
+# opacity gradients and their per-Gaussian sums: 61 flop + 1 exp + 1 reciprocal).  The
+# kernels compute the same quantities with fewer instructions (per-wave moment sums).
+FLOP_PER_PAIR = {"raster_fwd": 27, "raster_bwd": 63}
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_raster_bwd_1m_1080p_traffic.txt")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="1m", choices=["1m", "100k", "10m", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="image rows the oracle baseline composites")
+    ap.add_argument("--cpu-rows", type=int, default=1080, help="image rows the oracle baseline composites")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a copy-like kernel over this many MiB before timing (counter normalisation)")
     return ap.parse_args()
 
 
@@ -75,6 +85,8 @@ def hbm_bytes(kernel, n, n_vis, k_sh, n_isect, n_px):
         return n_px * 36
     if kernel == "bin_sort":
         return 8 * n + 24 * n_vis + 44 * n_isect
+    if kernel == "grad_aggregate":
+        return 36 * n_isect + 36 * n                                # one partial per (tile, Gaussian); grads2d
     return None
 
 
@@ -110,6 +122,7 @@ def main():
     import torch
     from differentiable_rasterization_amd import binding as B
     from differentiable_rasterization_amd import pipeline as PL
+    from differentiable_rasterization_amd.profiling import read_stored_traffic
 
     dev = "cuda"
     scene, desc = make_scene(args.workload)
@@ -125,32 +138,43 @@ def main():
     st.bins._alloc(int(st.bins.capacity * 1.3) + 4096)
     torch.cuda.synchronize()
 
-    names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "project_bwd", "adam"]
+    names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
+    g = params.gaussians()
 
     def one_step(i, ev=None):
         c, t = cams[i % nviews], targets[i % nviews]
         rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        f = st.frame
         rec(0)
-        B.gs_project(params.gaussians(), c, st.raster, st.proj.abi())
+        B.gs_project(g, c, st.raster, st.proj.abi())
         rec(1)
         st.bins.sort(st.proj, c, st.raster)
         rec(2)
-        f = st.frame
         B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.n_trav_sum)
         rec(3)
         B.gs_loss_l1(f.color, t, f.n_px, f.loss, f.dL_dcolor, f.loss_ws)
         rec(4)
-        st.backward_raster(c)
+        B.gs_raster_bwd_partials(g, st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.dL_dcolor, None)
         rec(5)
-        st.backward_project(c)
+        B.gs_grad_aggregate(g, st.bins.abi(), c, st.raster, st.grads2d, None)
         rec(6)
-        st.adam()
+        st.backward_project(c)
         rec(7)
+        st.adam()
+        rec(8)
 
+    if args.copy_calibration_mib > 0:
+        # a copy-like kernel of known size (reads and writes M MiB) for counter normalisation
+        src = torch.ones(args.copy_calibration_mib << 18, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     st.frame.n_trav_sum.zero_()
     k_isect = []
     torch.cuda.synchronize()
@@ -164,6 +188,7 @@ def main():
     isect_total = int(st.frame.n_trav_sum.item())
     per_kernel = {nm: sum(events[s][j].elapsed_time(events[s][j + 1]) for s in range(args.steps)) / args.steps
                   for j, nm in enumerate(names)}
+    step_ms = sorted(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps))
     ms_step = wall * 1e3 / args.steps
     isect_step = isect_total / args.steps
     n = scene.n
@@ -177,22 +202,20 @@ def main():
         if by is not None:
             entry.update(bound="hbm", algorithmic_bytes=int(by), achieved_GBs=round(by / (ms * 1e-3) / 1e9, 1),
                          frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
-        elif nm in ("raster_fwd", "raster_bwd"):
-            fl = (FWD_FLOP_PER_ISECT if nm == "raster_fwd" else BWD_FLOP_PER_ISECT) * isect_step
+        elif nm in FLOP_PER_PAIR:
+            fl = FLOP_PER_PAIR[nm] * isect_step
             tf = fl / (ms * 1e-3) / 1e12
             entry.update(bound="alu", algorithmic_flop=int(fl), achieved_TFLOPs=round(tf, 3),
                          frac=round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
                          frac_nonpacked=round(tf / FP32_NONPACKED_TFLOPS, 4),
                          isect_per_s=round(isect_step / (ms * 1e-3), 1))
         kernels[nm] = entry
-    dom = max(per_kernel, key=per_kernel.get)
-    d = kernels[dom]
-    if d.get("bound") == "hbm":
-        roof = {"kernel": dom, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": d["frac"], "traffic": None}
-    else:
-        roof = {"kernel": dom, "bound": "alu", "achieved": d["achieved_TFLOPs"], "peak": FP32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": d["frac"], "traffic": None}
+    d = kernels["raster_bwd"]
+    roof = {"kernel": "k_raster_bwd", "bound": "alu", "achieved": d["achieved_TFLOPs"],
+            "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["frac"],
+            "traffic": read_stored_traffic(TRAFFIC_SUMMARY, "k_raster_bwd") if args.workload == "1m" else None,
+            "flop_per_pair": FLOP_PER_PAIR["raster_bwd"], "pairs_per_launch": round(isect_step, 1),
+            "launch_ms": d["ms"], "frac_nonpacked_peak": d["frac_nonpacked"]}
     out = {
         "metric": METRIC, "value": round(isect_total / wall, 1), "unit": "Gaussian-pixel intersections/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -200,10 +223,13 @@ def main():
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
                    "views": nviews, "step": "one view: fwd + L1 + bwd + Adam"},
         "roofline": roof,
+        "step_stream_ms": {"median": round(step_ms[len(step_ms) // 2], 4),
+                           "p90": round(step_ms[min(len(step_ms) - 1, int(0.9 * len(step_ms)))], 4)},
         "intersections_per_step": round(isect_step, 1),
         "tile_entries_per_step": round(kmean, 1),
         "visible_gaussians": n_vis,
-        "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]) * 1e-3), 1),
+        "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]
+                                                   + per_kernel["grad_aggregate"]) * 1e-3), 1),
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
     }

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP = range(5)
 TILE = 16
 EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_raster_fwd", "gs_loss_workspace_bytes",
-            "gs_loss_l1", "gs_raster_bwd", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
+            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_last_error")
 
 
@@ -93,6 +93,9 @@ _SIGS = {
     "gs_loss_l1": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "gs_raster_bwd": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp,
                              _vp, _vp, _vp, _P(ParamGrads), _vp]),
+    "gs_raster_bwd_partials": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp,
+                                      _vp, _vp]),
+    "gs_grad_aggregate": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
     "gs_project_bwd": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
     "gs_adam_step": (_i32, [_P(AdamGroup), _i32, _i32, _f32, _f32, _f32, _vp]),
     "gs_composite_over": (_i32, [_P(_vp), _P(_vp), _i32, _i64, _f32, _vp, _vp, _vp]),
@@ -213,6 +216,20 @@ def gs_raster_bwd(g: Gaussians, proj: Projected, b: Bins, cam: Camera, p: Raster
                               ctypes.byref(p), _ptr(color), _ptr(t_final), _ptr(n_trav), _ptr(dL_dcolor), _ptr(dL_dt),
                               _ptr(grads2d), ctypes.byref(grads3d) if grads3d is not None else None,
                               _stream(stream)))
+
+
+def gs_raster_bwd_partials(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, color, t_final, n_trav, dL_dcolor,
+                           dL_dt, stream=None):
+    _check(_lib.gs_raster_bwd_partials(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
+                                       _ptr(color), _ptr(t_final), _ptr(n_trav), _ptr(dL_dcolor), _ptr(dL_dt),
+                                       _stream(stream)))
+
+
+def gs_grad_aggregate(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, grads2d, grads3d: ParamGrads | None,
+                      stream=None):
+    _check(_lib.gs_grad_aggregate(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
+                                  _ptr(grads2d), ctypes.byref(grads3d) if grads3d is not None else None,
+                                  _stream(stream)))
 
 
 def gs_project_bwd(g: Gaussians, cam: Camera, p: RasterParams, grads2d, grads3d: ParamGrads, stream=None):

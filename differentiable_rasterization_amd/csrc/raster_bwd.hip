@@ -247,22 +247,21 @@ namespace gsi {
 gs_status check_raster_inputs(const gs_bins *bins, const gs_camera *cam);
 }
 
-extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
-                                   const gs_camera *cam, const gs_raster_params *p, const float *color,
-                                   const float *t_final, const int32_t *n_trav, const float *dL_dcolor,
-                                   const float *dL_dt, float *grads2d,
-                                   gs_param_grads *grads3d, hipStream_t stream)
+extern "C" gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                            const gs_raster_params *p, const float *color, const float *t_final,
+                                            const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt,
+                                            hipStream_t stream)
 {
     using namespace gsi;
-    (void)proj;   // the lists carry raster-ready copies of the projected records
     gs_status s;
     if ((s = check_gaussians(g)) != GS_OK) return s;
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
     if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
-    if (!color || !t_final || !n_trav || !dL_dcolor || (g->n > 0 && !grads2d))
-        return fail(GS_ERR_INVALID_ARGUMENT, "color / t_final / n_trav / dL_dcolor / grads2d is NULL");
+    if (!color || !t_final || !n_trav || !dL_dcolor)
+        return fail(GS_ERR_INVALID_ARGUMENT, "color / t_final / n_trav / dL_dcolor is NULL");
     const int64_t n = g->n;
+    if (n == 0) return GS_OK;
     const int TX = tiles_x(cam->width), T = TX * tiles_y(cam->height);
     const RasterLayout L = raster_layout(n, bins->capacity, T);
     char *rb = static_cast<char *>(bins->raster);
@@ -272,22 +271,52 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
     const uint32_t *wp = reinterpret_cast<const uint32_t *>(rb + L.wpre);
     float *qg = reinterpret_cast<float *>(rb + L.qgrad);
     const unsigned grid = (unsigned)raster_grid(T);
+    if (dL_dt)
+        k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
+                                                    cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
+                                                    n_trav, dL_dcolor, dL_dt, qg);
+    else
+        k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
+                                                     cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
+                                                     n_trav, dL_dcolor, nullptr, qg);
+    GS_LAUNCH_CHECK("k_raster_bwd");
+    return GS_OK;
+}
+
+extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                       const gs_raster_params *p, float *grads2d, gs_param_grads *grads3d,
+                                       hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if ((s = check_gaussians(g)) != GS_OK) return s;
+    if ((s = check_camera(cam)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
+    if (g->n > 0 && !grads2d) return fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
+    const int64_t n = g->n;
     if (n > 0) {
-        if (dL_dt)
-            k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
-                                                        cam->height, TX, T, p->alpha_min, p->alpha_max, color,
-                                                        t_final, n_trav, dL_dcolor, dL_dt, qg);
-        else
-            k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
-                                                         cam->height, TX, T, p->alpha_min, p->alpha_max, color,
-                                                         t_final, n_trav, dL_dcolor, nullptr, qg);
-        GS_LAUNCH_CHECK("k_raster_bwd");
+        const int T = tiles_x(cam->width) * tiles_y(cam->height);
+        const RasterLayout L = raster_layout(n, bins->capacity, T);
+        const char *rb = static_cast<const char *>(bins->raster);
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
             reinterpret_cast<const uint32_t *>(rb + L.drank), reinterpret_cast<const uint32_t *>(rb + L.doff),
-            bins->tile_ranges, T, reinterpret_cast<const uint4 *>(rb + L.jmap), reinterpret_cast<const float4 *>(qg),
-            n, grads2d);
+            bins->tile_ranges, T, reinterpret_cast<const uint4 *>(rb + L.jmap),
+            reinterpret_cast<const float4 *>(rb + L.qgrad), n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }
     if (grads3d) return launch_project_bwd(g, cam, p, grads2d, grads3d, stream);
     return GS_OK;
+}
+
+extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                                   const gs_camera *cam, const gs_raster_params *p, const float *color,
+                                   const float *t_final, const int32_t *n_trav, const float *dL_dcolor,
+                                   const float *dL_dt, float *grads2d, gs_param_grads *grads3d, hipStream_t stream)
+{
+    (void)proj;   // the lists carry raster-ready copies of the projected records
+    if (g && g->n > 0 && !grads2d) return gsi::fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
+    const gs_status s = gs_raster_bwd_partials(g, bins, cam, p, color, t_final, n_trav, dL_dcolor, dL_dt, stream);
+    if (s != GS_OK) return s;
+    return gs_grad_aggregate(g, bins, cam, p, grads2d, grads3d, stream);
 }

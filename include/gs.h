@@ -223,6 +223,22 @@ gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const g
                         const float *t_final, const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt,
                         float *grads2d, gs_param_grads *grads3d, hipStream_t stream);
 
+/* The two halves of gs_raster_bwd, for callers that time or schedule them separately;
+ * gs_raster_bwd is gs_raster_bwd_partials followed by gs_grad_aggregate on the same
+ * stream.  gs_raster_bwd_partials: ByteSplat Eq. 3 per pixel and the per-quadrant part of
+ * the Eq. 4 sum, written to per-record slots inside bins->raster (nothing outside it is
+ * written; same arguments and checks as gs_raster_bwd).  gs_grad_aggregate: the
+ * per-Gaussian part of the Eq. 4 sum over those slots into grads2d [9][n] (every entry
+ * written), then, if grads3d is non-NULL, the projection backward as in gs_raster_bwd.
+ * Between the two calls the bins must not be re-sorted. */
+gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                 const gs_raster_params *p, const float *color, const float *t_final,
+                                 const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt,
+                                 hipStream_t stream);
+gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                            const gs_raster_params *p, float *grads2d, gs_param_grads *grads3d,
+                            hipStream_t stream);
+
 /* Backward through projection and colour evaluation alone (ByteSplat section 2.1: the
  * aggregated screen-space gradients are propagated through projection and colour
  * evaluation): from grads2d [9][n] (fields u, v, A, B, C, o, r, g, b) to grads3d (every

@@ -251,6 +251,27 @@ def test_backward_deep_stack_no_termination(with_gt):
     assert max(errs.values()) <= 1e-3, errs
 
 
+def test_backward_split_matches_whole():
+    """gs_raster_bwd_partials then gs_grad_aggregate gives gs_raster_bwd's gradients, bit for bit."""
+    sc = SMALL["ragged_sh2"]()
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    st = gpu_forward(sc, cam, rp)
+    c = B.camera_from(cam)
+    G = torch.rand(cam.height, cam.width, 3, device=DEV) - 0.5
+    GT = torch.rand(cam.height, cam.width, device=DEV) - 0.5
+    st.backward(c, dL_dcolor=G, dL_dt=GT)
+    whole2, whole3 = st.grads2d.clone(), st.params.grad.clone()
+    st.grads2d.fill_(float("nan"))
+    st.params.grad.fill_(float("nan"))
+    f = st.frame
+    g = st.params.gaussians()
+    B.gs_raster_bwd_partials(g, st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, G, GT)
+    B.gs_grad_aggregate(g, st.bins.abi(), c, st.raster, st.grads2d, st.params.param_grads())
+    torch.cuda.synchronize()
+    assert torch.equal(st.grads2d, whole2) and torch.equal(st.params.grad, whole3)
+
+
 # ------------------------------------------------------------------ Adam
 
 @pytest.mark.parametrize("n,step", [(1, 1), (1001, 1), (4096, 7), (250_001, 3)])
