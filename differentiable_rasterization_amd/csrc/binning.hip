@@ -26,8 +26,9 @@ __global__ __launch_bounds__(256) void k_depth_keys(const int2 *__restrict__ rad
 }
 
 // Tile counts of the Gaussians in depth order (0 for culled ones) and the number of
-// (tile, 8x8 quadrant) pairs their ellipse reaches; also records each Gaussian's depth
-// rank for the backward's per-Gaussian reduction.
+// (tile, 8x8 quadrant) pairs their ellipse reaches (qcnt [n + 1], qcnt[n] = 0, so that its
+// exclusive scan ends with the total); also records each Gaussian's depth rank for the
+// backward's per-Gaussian reduction.
 __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skeys, const uint32_t *__restrict__ svals,
                                                const float2 *__restrict__ means2d, const int2 *__restrict__ radii,
                                                const float4 *__restrict__ conic_o, float alpha_min, int64_t n,
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skey
                                                uint32_t *__restrict__ drank)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j == 0) qcnt[n] = 0;
     if (j >= n) return;
     uint32_t c = 0, qc = 0;
     const uint32_t g = svals[j];
@@ -55,31 +57,17 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skey
     drank[g] = (uint32_t)j;
 }
 
-// Sum of the quadrant-pair counts (one 64-bit atomic per block).
-__global__ __launch_bounds__(256) void k_sum_u32(const uint32_t *__restrict__ v, int64_t n,
-                                                 unsigned long long *__restrict__ total)
-{
-    __shared__ unsigned long long part[4];
-    unsigned long long acc = 0;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) acc += v[i];
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_down(acc, o, 64);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned long long t = part[0] + part[1] + part[2] + part[3];
-        if (t) atomicAdd(total, t);
-    }
-}
-
 // Entries of each Gaussian in depth order, tiles row-major.  Entry p gets the key
 // tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at), the
-// value p (its emit position) and gauss[p] = its Gaussian.
+// value p (its emit position), gauss[p] = its Gaussian and soff[p] = the gradient slot of
+// its first quadrant record (the Gaussian's slots follow its entries in order).
 __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
-                                              const uint32_t *__restrict__ off, const float2 *__restrict__ means2d,
+                                              const uint32_t *__restrict__ off, const uint32_t *__restrict__ qoff,
+                                              const float2 *__restrict__ means2d,
                                               const int2 *__restrict__ radii, const float4 *__restrict__ conic_o,
                                               float alpha_min, int64_t n, int tx, int ty,
                                               uint32_t *__restrict__ tkeys, uint32_t *__restrict__ tvals,
-                                              uint32_t *__restrict__ gauss)
+                                              uint32_t *__restrict__ gauss, uint32_t *__restrict__ soff)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n || cnt[j] == 0) return;
@@ -90,7 +78,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
     const float thr = 2.0f * __logf(co.w / alpha_min);
     int x0, x1, y0, y1;
     gsd::tile_rect(m.x, m.y, r.x, r.y, tx, ty, x0, x1, y0, y1);
-    uint32_t p = off[j];
+    uint32_t p = off[j], sl = qoff[j];
     for (int y = y0; y < y1; ++y)
         for (int x = x0; x < x1; ++x) {
             const uint32_t qm =
@@ -98,6 +86,8 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
             tkeys[p] = (uint32_t)(y * tx + x) | (qm << gsr::kMaskShift);
             tvals[p] = p;
             gauss[p] = g;
+            soff[p] = sl;
+            sl += (uint32_t)__popc(qm);
             ++p;
         }
 }
@@ -137,37 +127,37 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
 }
 
 // Copies the projected record of every list entry into the record list of each quadrant
-// its box reaches, at the position given by the scanned bit counts, stamps the entry index
-// into it, and records that position in jmap under the entry's emit position.
+// its box reaches, at the position given by the scanned bit counts, and stamps the entry
+// index and the record's gradient slot into it.  The spare records around the lists are
+// read (never used) by the raster kernels' batches: they are zeroed, so they stay finite.
 __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
                                                     const uint32_t *__restrict__ ids, int64_t K, int64_t words,
                                                     const uint64_t *__restrict__ bitmap,
-                                                    const uint32_t *__restrict__ wpre,
-                                                    const float4 *__restrict__ prec, float4 *__restrict__ qrec,
-                                                    uint4 *__restrict__ jmap)
+                                                    const uint32_t *__restrict__ wpre, const uint32_t *__restrict__ soff,
+                                                    const float4 *__restrict__ prec, float4 *__restrict__ qrec)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // the spare records in front of the lists are read (never used) by the backward's
-    // batches: keep them finite
-    if (k < gsr::kRecPad * gsr::kRecF4) qrec[k - gsr::kRecPad * gsr::kRecF4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    constexpr int kPadF4 = gsr::kRecPad * gsr::kRecF4;
+    if (k < 2 * kPadF4) {
+        // leading pad, then the pad after the last record (the scan's total)
+        const int64_t q_total = wpre[(int64_t)gsr::kQuads * (words + 1) - 1];
+        const int64_t at = k < kPadF4 ? k - kPadF4 : gsr::kRecF4 * q_total + (k - kPadF4);
+        qrec[at] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
     if (k >= K) return;
     const uint32_t qm = tkeys[k] >> gsr::kMaskShift;
-    uint32_t pos[gsr::kQuads];
-#pragma unroll
-    for (int q = 0; q < gsr::kQuads; ++q)
-        pos[q] = ((qm >> q) & 1u) ? gsr::quad_prefix(bitmap + (int64_t)q * words, wpre + (int64_t)q * (words + 1),
-                                                      (uint32_t)k)
-                                  : ~0u;
-    jmap[spos[k]] = make_uint4(pos[0], pos[1], pos[2], pos[3]);
     if (!qm) return;
     const uint32_t g = ids[k];
     const float4 a = prec[gsr::kRecF4 * (size_t)g], b = prec[gsr::kRecF4 * (size_t)g + 1];
     float4 c = prec[gsr::kRecF4 * (size_t)g + 2];
     c.z = __uint_as_float((uint32_t)k);
+    uint32_t slot = soff[spos[k]];
 #pragma unroll
     for (int q = 0; q < gsr::kQuads; ++q) {
-        if (pos[q] == ~0u) continue;
-        float4 *d = qrec + gsr::kRecF4 * (size_t)pos[q];
+        if (!((qm >> q) & 1u)) continue;
+        const uint32_t pos = gsr::quad_prefix(bitmap + (int64_t)q * words, wpre + (int64_t)q * (words + 1), (uint32_t)k);
+        float4 *d = qrec + gsr::kRecF4 * (size_t)pos;
+        c.w = __uint_as_float(slot++);
         d[0] = a;
         d[1] = b;
         d[2] = c;
@@ -220,7 +210,7 @@ __global__ __launch_bounds__(1024) void k_tile_order(const int32_t *__restrict__
 }
 
 struct Layout {
-    size_t dkA, dvA, dkB, dvB, cnt, qcnt, total, tkA, tkB, tvA, tvB, gauss, hist, part, bytes;
+    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, tkA, tkB, tvA, tvB, gauss, soff, hist, part, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -232,9 +222,11 @@ Layout layout(int64_t n, int64_t cap)
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     const size_t nn = (size_t)(n > 0 ? n : 1), cc = (size_t)(cap > 0 ? cap : 1);
     L.dkA = take(4 * nn); L.dvA = take(4 * nn); L.dkB = take(4 * nn); L.dvB = take(4 * nn);
-    L.cnt = take(4 * nn); L.qcnt = take(4 * nn); L.total = take(16);   // K, then the quadrant pairs
+    L.cnt = take(4 * nn); L.qcnt = take(4 * (nn + 1)); L.doff = take(4 * nn);
+    L.total = take(16);   // K, then the quadrant records
     L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(4 * cc); L.tvB = take(4 * cc); L.gauss = take(4 * cc);
-    const int64_t mmax = std::max<int64_t>(n, cap);
+    L.soff = take(4 * cc);
+    const int64_t mmax = std::max<int64_t>(n + 1, cap);
     const int64_t hl = gsi::radix_hist_len(mmax);
     L.hist = take(4 * (size_t)hl);
     const int64_t qwords = gsr::kQuads * (gsr::raster_layout(n, cap, 1).words + 1);   // quadrant bit-count scan
@@ -289,7 +281,7 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     const gsr::RasterLayout RL = gsr::raster_layout(n, bins->capacity, T);
     char *rb = static_cast<char *>(bins->raster);
     int32_t *order = reinterpret_cast<int32_t *>(rb + RL.order);
-    uint32_t *drank = reinterpret_cast<uint32_t *>(rb + RL.drank), *doff = reinterpret_cast<uint32_t *>(rb + RL.doff);
+    uint32_t *drank = reinterpret_cast<uint32_t *>(rb + RL.drank), *qoff = reinterpret_cast<uint32_t *>(rb + RL.qoff);
     *n_isect_out = 0;
     if (n == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
@@ -310,10 +302,11 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     char *ws = static_cast<char *>(workspace);
     uint32_t *dkA = (uint32_t *)(ws + L.dkA), *dvA = (uint32_t *)(ws + L.dvA);
     uint32_t *dkB = (uint32_t *)(ws + L.dkB), *dvB = (uint32_t *)(ws + L.dvB);
-    uint32_t *cnt = (uint32_t *)(ws + L.cnt), *qcnt = (uint32_t *)(ws + L.qcnt);
+    uint32_t *cnt = (uint32_t *)(ws + L.cnt), *qcnt = (uint32_t *)(ws + L.qcnt), *doff = (uint32_t *)(ws + L.doff);
     unsigned long long *total = (unsigned long long *)(ws + L.total);
     uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB);
     uint32_t *tvA = (uint32_t *)(ws + L.tvA), *tvB = (uint32_t *)(ws + L.tvB), *gauss = (uint32_t *)(ws + L.gauss);
+    uint32_t *soff = (uint32_t *)(ws + L.soff);
     uint32_t *hist = (uint32_t *)(ws + L.hist), *part = (uint32_t *)(ws + L.part);
     const float2 *m2 = reinterpret_cast<const float2 *>(proj->means2d);
     const int2 *rr = reinterpret_cast<const int2 *>(proj->radii);
@@ -326,14 +319,13 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     if ((s = radix_sort_u32(dkA, dvA, dkB, dvB, n, 32, hist, part, &in_b, stream)) != GS_OK) return s;
     const uint32_t *sk = in_b ? dkB : dkA, *sv = in_b ? dvB : dvA;
 
-    // 2. tile counts in depth order, their exclusive scan (the emit offsets) and the total K
+    // 2. tile and quadrant-record counts in depth order, their exclusive scans (the emit
+    //    offsets and the first gradient slot of each Gaussian) and the totals K and Q
     k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity), alpha_min,
                                     n, tx, ty, cnt, qcnt, drank);
     GS_LAUNCH_CHECK("k_count");
     if ((s = exclusive_scan_u32(cnt, doff, n, part, total, stream)) != GS_OK) return s;
-    if ((s = fill_i32(reinterpret_cast<int32_t *>(total + 1), 2, 0, stream)) != GS_OK) return s;
-    k_sum_u32<<<(unsigned)std::min<int64_t>(ceil_div(n, 256 * 8), 1024), 256, 0, stream>>>(qcnt, n, total + 1);
-    GS_LAUNCH_CHECK("k_sum_u32");
+    if ((s = exclusive_scan_u32(qcnt, qoff, n + 1, part, total + 1, stream)) != GS_OK) return s;
     unsigned long long KQ[2] = {0, 0};
     GS_HIP(hipMemcpyAsync(KQ, total, sizeof(KQ), hipMemcpyDeviceToHost, stream));
     GS_HIP(hipStreamSynchronize(stream));
@@ -360,14 +352,14 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
 
     // 3. emit entries in depth order, then a stable sort of (tile key, emit position) by tile
     const int tbits = std::max(1, bits_for(T - 1));
-    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity),
-                                   alpha_min, n, tx, ty, tkA, tvA, gauss);
+    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, qoff, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity),
+                                   alpha_min, n, tx, ty, tkA, tvA, gauss, soff);
     GS_LAUNCH_CHECK("k_emit");
     if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, (int64_t)K, tbits, hist, part, &in_b, stream)) != GS_OK) return s;
     const uint32_t *tk = in_b ? tkB : tkA, *spos = in_b ? tvB : tvA;
 
     // 4. ids, per-tile ranges, quadrant bitmaps and their scanned bit counts, the quadrant
-    //    record lists and the emit-position map; optional 64-bit keys
+    //    record lists; optional 64-bit keys
     const unsigned gk = (unsigned)ceil_div((int64_t)K, 256);
     uint64_t *bm = reinterpret_cast<uint64_t *>(rb + RL.bitmap);
     uint32_t *wpre = reinterpret_cast<uint32_t *>(rb + RL.wpre);
@@ -376,10 +368,9 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     k_finish<<<gk, 256, 0, stream>>>(tk, spos, gauss, (int64_t)K, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
     GS_LAUNCH_CHECK("k_finish");
     if ((s = exclusive_scan_u32(wpre, wpre, nw, part, nullptr, stream)) != GS_OK) return s;
-    k_quad_lists<<<gk, 256, 0, stream>>>(tk, spos, bins->ids, (int64_t)K, RL.words, bm, wpre,
-                                         reinterpret_cast<const float4 *>(proj->rec),
-                                         reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4,
-                                         reinterpret_cast<uint4 *>(rb + RL.jmap));
+    k_quad_lists<<<(unsigned)std::max<int64_t>(gk, 1), 256, 0, stream>>>(
+        tk, spos, bins->ids, (int64_t)K, RL.words, bm, wpre, soff, reinterpret_cast<const float4 *>(proj->rec),
+        reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4);
     GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {
         k_keys64<<<gk, 256, 0, stream>>>(tk, bins->ids, proj->depth, (int64_t)K, bins->keys);

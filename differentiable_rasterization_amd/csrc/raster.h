@@ -15,13 +15,13 @@
 //                                 + set bits of bitmap q below entry x in its word
 //   order  [tiles] int32          tiles by decreasing list length (heaviest first)
 //   drank  [n] uint32             depth rank of each Gaussian (culled ones rank last)
-//   doff   [n] uint32             first emitted entry of each Gaussian by depth rank: the
-//                                 entries of the Gaussian of rank r were emitted at positions
-//                                 doff[r] .. doff[r + 1] (doff[n] = K)
-//   jmap   [4 * capacity] uint32  position in qrec of emitted entry p's record in quadrant q
-//                                 (index 4 p + q), or ~0 if the entry is not in quadrant q
+//   qoff   [n + 1] uint32         first gradient slot of the Gaussian of depth rank r: its
+//                                 quadrant records own slots qoff[r] .. qoff[r + 1], in the
+//                                 order of its entries and, within an entry, of the quadrants
+//                                 (qoff[n] = the number of quadrant records)
 //   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
-//                                 padded to 48 bytes)
+//                                 padded to 48 bytes), one slot per quadrant record, at the
+//                                 slot index its record carries
 //
 // Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
 // (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of records with
@@ -41,8 +41,9 @@ constexpr int kQuads = 4;
 // list entry by the binning).  With (dx, dy) = pixel centre - mean, the alpha exponent is
 // evaluated base 2:  o exp(-A dx^2/2 - B dx dy - C dy^2/2) = exp2(a dx^2 + b dx dy + c dy^2 + l)
 // with a = -log2(e) A / 2, b = -log2(e) B, c = -log2(e) C / 2, l = log2(o).
-//   p0 = (u, v, a, b)   p1 = (c, l, red, green)   p2 = (blue, index bits, entry bits, 0)
-// "entry" is the record's position k in the 16x16 tile lists (set by the binning).
+//   p0 = (u, v, a, b)   p1 = (c, l, red, green)   p2 = (blue, index bits, entry bits, slot bits)
+// "entry" is the record's position k in the 16x16 tile lists and "slot" the index of its
+// gradient slot (both set by the binning).
 // The backward recovers A = -2 ln(2) a, B = -ln(2) b, C = -2 ln(2) c and 1/o = exp2(-l).
 struct Rec {
     float4 p0, p1, p2;
@@ -104,7 +105,7 @@ __device__ __forceinline__ uint32_t quad_mask(float u, float v, float A, float B
 }
 
 struct RasterLayout {
-    size_t qrec, bitmap, wpre, order, drank, doff, jmap, qgrad, bytes;
+    size_t qrec, bitmap, wpre, order, drank, qoff, qgrad, bytes;
     int64_t cap, words;
 };
 
@@ -122,8 +123,7 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);
     L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);
     L.drank = o;  o += align256(nn * 4);
-    L.doff = o;   o += align256(nn * 4);
-    L.jmap = o;   o += align256((size_t)kQuads * (size_t)L.cap * 4);
+    L.qoff = o;   o += align256((nn + 1) * 4);
     L.qgrad = o;  o += align256(q4 * kGradSlot * 4);
     L.bytes = o;
     return L;

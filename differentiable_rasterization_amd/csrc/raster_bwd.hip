@@ -19,10 +19,10 @@
 //   within each 16-lane row, so row e ends with the totals of record e), and lane (e, f)
 //   turns them into field f of record e,
 //   du = A Sx + B Sy, dv = B Sx + C Sy, dA = -Sxx/2, dB = -Sxy, dC = -Syy/2, do = S0 / o,
-//   and stores it in the record's slot of the per-record gradient buffer (one store
-//   instruction for the 36 values).  A second kernel then sums, for every Gaussian, the
-//   slots of its records (found through the emit-position map): the sum of Eq. 4 in a
-//   fixed order, so the gradients are deterministic.
+//   and stores it in the record's gradient slot (one store instruction for the 36
+//   values).  The binning gives each Gaussian's quadrant records consecutive slots, so a
+//   second kernel sums, for every Gaussian, one contiguous run of slots: the sum of Eq. 4
+//   in a fixed order, so the gradients are deterministic.
 //
 // Lanes that do not take an entry run the same instructions with alpha = 0, which leaves
 // T unchanged and contributes zeros (no divergent branches).
@@ -120,8 +120,14 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)(start + nmax));
     const uint32_t jend = quad_prefix(bq, wq, (uint32_t)end);
-    // records never reached by any pixel of the quadrant contribute nothing
-    for (size_t z = (size_t)j1 * kGradSlot + lane; z < (size_t)jend * kGradSlot; z += 64) qgrad[z] = 0.0f;
+    // records never reached by any pixel of the quadrant contribute nothing: one lane per
+    // record clears its slot
+    for (uint32_t j = j1 + (uint32_t)lane; j < jend; j += 64u) {
+        float4 *z = reinterpret_cast<float4 *>(qgrad + (size_t)__float_as_uint(qrec[kRecF4 * (size_t)j + 2].w) * kGradSlot);
+        z[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        z[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        z[2] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
     const int row = lane >> 4, field = lane & 15;
     float Tr = 1.0f;
     // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         }
         // records jt .. jt+3 (past j1: spare, unused); one wait per batch
         float4 p0[kBwdBatch], p1[kBwdBatch];
-        float blue[kBwdBatch], kent[kBwdBatch];
+        float blue[kBwdBatch], kent[kBwdBatch], slot[kBwdBatch];
         const float4 *rb = qrec + kRecF4 * (size_t)jt;
 #pragma unroll
         for (int i = 0; i < kBwdBatch; ++i) {
@@ -142,11 +148,12 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
             const float4 p2 = rb[kRecF4 * i + 2];
             blue[i] = p2.x;
             kent[i] = p2.z;
+            slot[i] = p2.w;
         }
 #pragma unroll
         for (int i = 0; i < kBwdBatch; ++i)
             asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
-                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]));
+                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]), "s"(slot[i]));
         const uint32_t cnt = min((uint32_t)kBwdBatch, j1 - jt);
         float v[kBwdBatch * kFields];
         bool any = false;
@@ -179,8 +186,9 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
             Tr = Tr * om;
             any |= take;
         }
-        // slot of the batch's record e = row: record jt + e, field f = lane & 15
-        float *dst = qgrad + ((size_t)(jt + (uint32_t)min(row, (int)cnt - 1))) * kGradSlot + field;
+        // gradient slot of the batch's record e = row (record jt + e), field f = lane & 15
+        const uint32_t my_slot = __float_as_uint(by_row(row, slot[0], slot[1], slot[2], slot[3]));
+        float *dst = qgrad + (size_t)my_slot * kGradSlot + field;
         const bool writer = (uint32_t)row < cnt && field < kFields;
         jt += cnt;
         if (__ballot(any) == 0) {
@@ -208,34 +216,27 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     asm volatile("" ::"v"(sink));
 }
 
-// Eq. 4: the gradient of Gaussian g is the sum of the per-record slots of its entries
-// (emit positions doff[r] .. doff[r+1] with r its depth rank, up to four quadrant records
-// each), added in a fixed order.  Every Gaussian is written, culled ones with zeros.  One
-// thread per Gaussian, in index order so that the stores coalesce.
-__global__ __launch_bounds__(256) void k_grad_reduce(const uint32_t *__restrict__ drank, const uint32_t *__restrict__ doff,
-                                                     const int32_t *__restrict__ ranges, int T,
-                                                     const uint4 *__restrict__ jmap, const float4 *__restrict__ qgrad,
-                                                     int64_t n, float *__restrict__ grads2d)
+// Eq. 4: the gradient of Gaussian g is the sum of the slots of its quadrant records,
+// slots qoff[r] .. qoff[r + 1] for its depth rank r, added in order.  Every Gaussian is
+// written, culled ones (no records) with zeros.  One thread per Gaussian, in index order
+// so that the stores coalesce.
+__global__ __launch_bounds__(256) void k_grad_reduce(const uint32_t *__restrict__ drank, const uint32_t *__restrict__ qoff,
+                                                     const float4 *__restrict__ qgrad, int64_t n,
+                                                     float *__restrict__ grads2d)
 {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     const uint32_t r = drank[g];
-    const uint32_t p0 = doff[r], p1 = (int64_t)r + 1 < n ? doff[r + 1] : (uint32_t)ranges[T];
+    const uint32_t s0 = qoff[r], s1 = qoff[r + 1];
     float acc[kFields];
 #pragma unroll
     for (int f = 0; f < kFields; ++f) acc[f] = 0.0f;
-    for (uint32_t p = p0; p < p1; ++p) {
-        const uint4 j = jmap[p];
-        const uint32_t js[kQuads] = {j.x, j.y, j.z, j.w};
-#pragma unroll
-        for (int qd = 0; qd < kQuads; ++qd) {
-            if (js[qd] == ~0u) continue;
-            const float4 *sl = qgrad + (size_t)js[qd] * (kGradSlot / 4);
-            const float4 a = sl[0], b = sl[1], c = sl[2];
-            acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-            acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-            acc[8] += c.x;
-        }
+    for (uint32_t j = s0; j < s1; ++j) {
+        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
+        const float4 a = sl[0], b = sl[1], c = sl[2];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+        acc[8] += c.x;
     }
 #pragma unroll
     for (int f = 0; f < kFields; ++f) grads2d[(size_t)f * n + g] = acc[f];
@@ -300,8 +301,7 @@ extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bin
         const RasterLayout L = raster_layout(n, bins->capacity, T);
         const char *rb = static_cast<const char *>(bins->raster);
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
-            reinterpret_cast<const uint32_t *>(rb + L.drank), reinterpret_cast<const uint32_t *>(rb + L.doff),
-            bins->tile_ranges, T, reinterpret_cast<const uint4 *>(rb + L.jmap),
+            reinterpret_cast<const uint32_t *>(rb + L.drank), reinterpret_cast<const uint32_t *>(rb + L.qoff),
             reinterpret_cast<const float4 *>(rb + L.qgrad), n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }

@@ -26,15 +26,16 @@ def step_bytes_per_gaussian(sh_degree: int) -> int:
     """Everything this library keeps per Gaussian during a training step: parameters,
     gradients, Adam moments, the projected record (means2d 8, conic+opacity 16, colour 12,
     depth 4, radii 8), its 48-byte raster-ready copy, screen-space gradients (36) and the
-    binning workspace (24)."""
-    return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 48 + 48 + 36 + 24
+    binning's per-Gaussian buffers (36: depth keys and values twice, tile and quadrant
+    counts, emit offsets, depth rank, first gradient slot)."""
+    return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 48 + 48 + 36 + 36
 
 
 def step_bytes_per_intersection() -> int:
     """Intersection lists: ids (4); the raster-ready lists with room for two 8x8-quadrant
-    records per entry (2 x 48) and their gradient slots (2 x 48), map words (4 x 4) and
-    quadrant bits (1); and the sort workspace's key, value and Gaussian buffers (20)."""
-    return 4 + 2 * (48 + 48) + 16 + 1 + 20
+    records per entry (2 x 48) and their gradient slots (2 x 48) and quadrant bits (1); and
+    the sort workspace's key, value, Gaussian and first-slot buffers (24)."""
+    return 4 + 2 * (48 + 48) + 1 + 24
 
 
 def max_gaussians(hbm_bytes: float, sh_degree: int, adam: bool = True) -> int:

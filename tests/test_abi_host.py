@@ -93,17 +93,17 @@ def test_workspace_sizes():
     b = B.gs_bin_sort_workspace_bytes(2000, 5000, 64, 64)
     c = B.gs_bin_sort_workspace_bytes(1000, 50000, 64, 64)
     assert 0 < a < b and a < c
-    # O(28 B per Gaussian + 20 B per entry: two key and two value buffers for the tile
-    # sort, the Gaussian of each emitted entry) plus histograms
-    assert 20 * 45000 <= c - a < 20 * 45000 * 1.2 + 4 * 256 * 16 + 4096
+    # O(32 B per Gaussian + 24 B per entry: two key and two value buffers for the tile
+    # sort, the Gaussian and the first gradient slot of each emitted entry) plus histograms
+    assert 24 * 45000 <= c - a < 24 * 45000 * 1.2 + 4 * 256 * 16 + 4096
     assert B.gs_bin_sort_workspace_bytes(-1, 0, 1, 1) == 0
     assert B.gs_compact_workspace_bytes(10**6) >= 4 * (10**6 // 256)
     assert B.gs_loss_workspace_bytes(100) >= 8
-    # raster-ready lists: per entry 2 quadrant records (48 B) and gradient slots (48 B), 4 map
-    # words (4 B); 4 quadrant bits and 4 prefix counts per 64 entries; 8 B per Gaussian;
-    # 4 B per tile
+    # raster-ready lists: per entry 2 quadrant records (48 B) and gradient slots (48 B); 4
+    # quadrant bits and 4 prefix counts per 64 entries; depth rank and first gradient slot
+    # per Gaussian (+ the total); 4 B per tile
     r0 = B.gs_bins_raster_bytes(5000, 64 * 1000, 1920, 1080)
-    lo = 2 * (48 + 48) * 64000 + 4 * 4 * 64000 + 4 * 8 * 1000 + 4 * 4 * 1001 + 8 * 5000 + 4 * 8160
+    lo = 2 * (48 + 48) * 64000 + 4 * 8 * 1000 + 4 * 4 * 1001 + 4 * 5000 + 4 * 5001 + 4 * 8160
     assert lo <= r0 <= lo + 8 * 256
     assert B.gs_bins_raster_bytes(0, 0, 16, 16) > 0 and B.gs_bins_raster_bytes(0, -1, 16, 16) == 0
 
