@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--workload", default="1m", choices=["1m", "100k", "10m", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1080, help="image rows the oracle baseline composites")
+    ap.add_argument("--kernel-events", default="all", choices=["all", "dominant"],
+                    help="HIP events around every call, or only around the dominant kernel's call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a copy-like kernel over this many MiB before timing (counter normalisation)")
     return ap.parse_args()
@@ -141,14 +143,22 @@ def main():
     names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
     g = params.gaussians()
 
-    def one_step(i, ev=None):
+    def one_step(i, ev=None, counts=None):
         c, t = cams[i % nviews], targets[i % nviews]
-        rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        if ev is None:
+            rec = lambda k: None
+        elif args.kernel_events == "all":
+            rec = lambda k: ev[k].record()
+        else:   # step boundaries and the dominant kernel only
+            rec = lambda k: ev[k].record() if k in (0, 4, 5, len(names)) else None
         f = st.frame
         rec(0)
         B.gs_project(g, c, st.raster, st.proj.abi())
         rec(1)
-        st.bins.sort(st.proj, c, st.raster)
+        if counts is None:
+            st.bins.sort(st.proj, c, st.raster)
+        else:   # no host wait inside the step; the counts are checked after the timed steps
+            st.bins.sort_async(st.proj, c, st.raster, counts)
         rec(2)
         B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.n_trav_sum)
         rec(3)
@@ -176,18 +186,22 @@ def main():
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     st.frame.n_trav_sum.zero_()
-    k_isect = []
+    counts = torch.zeros(args.steps, 2, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(args.warmup + i, events[i])
-        k_isect.append(st.bins.n_isect)
+        one_step(args.warmup + i, events[i], counts[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
+    cnt = counts.cpu()
+    if int(cnt[:, 1].max()) != 0:
+        raise RuntimeError(f"intersection lists overflowed during the timed steps (need {int(cnt[:, 1].max())})")
+    k_isect = [int(k) for k in cnt[:, 0]]
     isect_total = int(st.frame.n_trav_sum.item())
-    per_kernel = {nm: sum(events[s][j].elapsed_time(events[s][j + 1]) for s in range(args.steps)) / args.steps
-                  for j, nm in enumerate(names)}
+    timed = range(len(names)) if args.kernel_events == "all" else [names.index("raster_bwd")]
+    per_kernel = {names[j]: sum(events[s][j].elapsed_time(events[s][j + 1]) for s in range(args.steps)) / args.steps
+                  for j in timed}
     step_ms = sorted(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps))
     ms_step = wall * 1e3 / args.steps
     isect_step = isect_total / args.steps
@@ -229,7 +243,9 @@ def main():
         "tile_entries_per_step": round(kmean, 1),
         "visible_gaussians": n_vis,
         "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]
-                                                   + per_kernel["grad_aggregate"]) * 1e-3), 1),
+                                                   + per_kernel["grad_aggregate"]) * 1e-3), 1)
+        if "raster_fwd" in per_kernel else None,
+        "kernel_events": args.kernel_events,
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
     }

@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP = range(5)
 TILE = 16
-EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_raster_fwd", "gs_loss_workspace_bytes",
+EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_bin_sort_async", "gs_raster_fwd", "gs_loss_workspace_bytes",
             "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_last_error")
 
@@ -88,6 +88,7 @@ _SIGS = {
     "gs_bins_raster_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "gs_bin_sort_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "gs_bin_sort": (_i32, [_P(Projected), _i64, _P(Camera), _P(RasterParams), _P(Bins), _P(_i64), _vp, _sz, _vp]),
+    "gs_bin_sort_async": (_i32, [_P(Projected), _i64, _P(Camera), _P(RasterParams), _P(Bins), _vp, _vp, _sz, _vp]),
     "gs_raster_fwd": (_i32, [_P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp]),
     "gs_loss_workspace_bytes": (_sz, [_i64]),
     "gs_loss_l1": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -193,6 +194,14 @@ def gs_bin_sort(proj: Projected, n, cam: Camera, p: RasterParams, b: Bins, works
                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, required=k.value)
     return k.value
+
+
+def gs_bin_sort_async(proj: Projected, n, cam: Camera, p: RasterParams, b: Bins, counts, workspace, stream=None):
+    """Queues the sort without waiting for the device; counts (device int64[2], or None)
+    receives (K, required capacity or 0)."""
+    _check(_lib.gs_bin_sort_async(ctypes.byref(proj), n, ctypes.byref(cam), ctypes.byref(p), ctypes.byref(b),
+                                  _ptr(counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
 
 
 def gs_raster_fwd(proj: Projected, b: Bins, cam: Camera, p: RasterParams, color, t_final, n_trav, n_trav_sum=None,

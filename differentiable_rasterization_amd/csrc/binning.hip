@@ -57,6 +57,13 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skey
     drank[g] = (uint32_t)j;
 }
 
+// Capacity the lists of K entries and Q quadrant records need.
+__device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned long long K, unsigned long long Q)
+{
+    const unsigned long long qc = (Q + gsr::kQuadFactor - 1) / gsr::kQuadFactor;
+    return K > qc ? K : qc;
+}
+
 // Entries of each Gaussian in depth order, tiles row-major.  Entry p gets the key
 // tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at), the
 // value p (its emit position), gauss[p] = its Gaussian and soff[p] = the gradient slot of
@@ -66,11 +73,26 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
                                               const float2 *__restrict__ means2d,
                                               const int2 *__restrict__ radii, const float4 *__restrict__ conic_o,
                                               float alpha_min, int64_t n, int tx, int ty,
+                                              const unsigned long long *__restrict__ tot, int64_t cap,
+                                              unsigned long long *__restrict__ klen, gsr::BinsHeader *__restrict__ hdr,
+                                              int64_t *__restrict__ counts,
                                               uint32_t *__restrict__ tkeys, uint32_t *__restrict__ tvals,
                                               uint32_t *__restrict__ gauss, uint32_t *__restrict__ soff)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= n || cnt[j] == 0) return;
+    const unsigned long long K = tot[0], Q = tot[1];
+    const bool ok = need_capacity(K, Q) <= (unsigned long long)cap;
+    if (j == 0) {
+        *klen = ok ? K : 0ull;
+        hdr->K = K;
+        hdr->Q = Q;
+        hdr->ok = ok ? 1u : 0u;
+        if (counts) {
+            counts[0] = (int64_t)K;
+            counts[1] = ok ? 0 : (int64_t)need_capacity(K, Q);
+        }
+    }
+    if (!ok || j >= n || cnt[j] == 0) return;
     const uint32_t g = svals[j];
     const float2 m = means2d[g];
     const int2 r = radii[g];
@@ -96,14 +118,21 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
 // entry, tile_ranges[t] = first entry of tile t (entries are sorted by tile; ranges[T] =
 // K), and the quadrant bitmaps with their per-word bit counts (one 64-bit word per wave and
 // quadrant; block bases are multiples of 64).  `wcnt` [4][words + 1] must be zero
-// beforehand; its exclusive scan gives the positions of the quadrant records.
+// beforehand; its exclusive scan gives the positions of the quadrant records.  The
+// launch covers max(capacity, T + 1) threads; K is read on the device.
 __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
-                                                const uint32_t *__restrict__ gauss, int64_t K, int32_t T,
+                                                const uint32_t *__restrict__ gauss,
+                                                const unsigned long long *__restrict__ klen, int32_t T,
                                                 uint32_t *__restrict__ ids, int32_t *__restrict__ ranges,
                                                 int64_t words, uint64_t *__restrict__ bitmap,
                                                 uint32_t *__restrict__ wcnt)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t K = (int64_t)*klen;
+    if (K == 0) {   // no entries (or lists that did not fit): every tile list is empty
+        if (k <= T) ranges[k] = 0;
+        return;
+    }
     uint32_t qm = 0;
     if (k < K) {
         const uint32_t key = tkeys[k];
@@ -131,7 +160,8 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
 // index and the record's gradient slot into it.  The spare records around the lists are
 // read (never used) by the raster kernels' batches: they are zeroed, so they stay finite.
 __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
-                                                    const uint32_t *__restrict__ ids, int64_t K, int64_t words,
+                                                    const uint32_t *__restrict__ ids,
+                                                    const unsigned long long *__restrict__ klen, int64_t words,
                                                     const uint64_t *__restrict__ bitmap,
                                                     const uint32_t *__restrict__ wpre, const uint32_t *__restrict__ soff,
                                                     const float4 *__restrict__ prec, float4 *__restrict__ qrec)
@@ -144,7 +174,7 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
         const int64_t at = k < kPadF4 ? k - kPadF4 : gsr::kRecF4 * q_total + (k - kPadF4);
         qrec[at] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    if (k >= K) return;
+    if (k >= (int64_t)*klen) return;
     const uint32_t qm = tkeys[k] >> gsr::kMaskShift;
     if (!qm) return;
     const uint32_t g = ids[k];
@@ -165,10 +195,11 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
 }
 
 __global__ __launch_bounds__(256) void k_keys64(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ ids,
-                                                const float *__restrict__ depth, int64_t K, uint64_t *__restrict__ keys)
+                                                const float *__restrict__ depth,
+                                                const unsigned long long *__restrict__ klen, uint64_t *__restrict__ keys)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= K) return;
+    if (k >= (int64_t)*klen) return;
     keys[k] = ((uint64_t)(tkeys[k] & gsr::kTileMask) << 32) | (uint64_t)__float_as_uint(depth[ids[k]]);
 }
 
@@ -209,8 +240,20 @@ __global__ __launch_bounds__(1024) void k_tile_order(const int32_t *__restrict__
     }
 }
 
+// Counts of an empty scene (n = 0).
+__global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restrict__ counts)
+{
+    hdr->K = 0;
+    hdr->Q = 0;
+    hdr->ok = 1u;
+    if (counts) {
+        counts[0] = 0;
+        counts[1] = 0;
+    }
+}
+
 struct Layout {
-    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, tkA, tkB, tvA, tvB, gauss, soff, hist, part, bytes;
+    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, gauss, soff, hist, part, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -224,6 +267,7 @@ Layout layout(int64_t n, int64_t cap)
     L.dkA = take(4 * nn); L.dvA = take(4 * nn); L.dkB = take(4 * nn); L.dvB = take(4 * nn);
     L.cnt = take(4 * nn); L.qcnt = take(4 * (nn + 1)); L.doff = take(4 * nn);
     L.total = take(16);   // K, then the quadrant records
+    L.klen = take(8);     // K if the lists fit, else 0
     L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(4 * cc); L.tvB = take(4 * cc); L.gauss = take(4 * cc);
     L.soff = take(4 * cc);
     const int64_t mmax = std::max<int64_t>(n + 1, cap);
@@ -258,35 +302,43 @@ extern "C" size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32
     return layout(n, capacity).bytes;
 }
 
-extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, const gs_raster_params *p,
-                                 gs_bins *bins, int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
-                                 hipStream_t stream)
+namespace {
+
+// Both entry points: every launch after the counting is sized by the capacity and reads
+// the entry count on the device, so nothing here waits for the device.
+gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *cam, const gs_raster_params *p,
+                          gs_bins *bins, int64_t *counts, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream)
 {
     using namespace gsi;
     gs_status s;
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
     const float alpha_min = p->alpha_min;
-    if (!proj || !bins || !n_isect_out) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!proj || !bins) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
     if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
-    if (n > (int64_t(1) << 31) - 1) return fail(GS_ERR_UNSUPPORTED, "n >= 2^31");
+    if (n > (int64_t(1) << 31) - 2) return fail(GS_ERR_UNSUPPORTED, "n >= 2^31 - 1");
     if (bins->capacity < 0 || bins->capacity > 0x3FFFFFFFll)
         return fail(GS_ERR_INVALID_ARGUMENT, "capacity out of range (at most 2^30 entries)");
     if (!bins->tile_ranges || (bins->capacity > 0 && !bins->ids))
         return fail(GS_ERR_INVALID_ARGUMENT, "ids / tile_ranges is NULL");
     if (!bins->raster || !aligned(bins->raster, 256))
         return fail(GS_ERR_INVALID_ARGUMENT, "raster buffer is NULL or not 256-byte aligned");
+    if (counts && !aligned(counts, 8)) return fail(GS_ERR_INVALID_ARGUMENT, "counts must be 8-byte aligned");
     const int tx = tiles_x(cam->width), ty = tiles_y(cam->height);
     const int32_t T = tx * ty;
-    const gsr::RasterLayout RL = gsr::raster_layout(n, bins->capacity, T);
+    const int64_t cap = bins->capacity;
+    const gsr::RasterLayout RL = gsr::raster_layout(n, cap, T);
     char *rb = static_cast<char *>(bins->raster);
+    gsr::BinsHeader *hdr = reinterpret_cast<gsr::BinsHeader *>(rb + RL.hdr);
     int32_t *order = reinterpret_cast<int32_t *>(rb + RL.order);
     uint32_t *drank = reinterpret_cast<uint32_t *>(rb + RL.drank), *qoff = reinterpret_cast<uint32_t *>(rb + RL.qoff);
-    *n_isect_out = 0;
     if (n == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
         k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
         GS_LAUNCH_CHECK("k_tile_order");
+        k_bins_empty<<<1, 1, 0, stream>>>(hdr, counts);
+        GS_LAUNCH_CHECK("k_bins_empty");
         return GS_OK;
     }
     if (!proj->means2d || !proj->depth || !proj->radii)
@@ -296,7 +348,7 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     if (!aligned(proj->conic_opacity, 16)) return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity must be 16-byte aligned");
     if (!aligned(proj->means2d, 8) || !aligned(proj->radii, 8) || !aligned(proj->rec, 16))
         return fail(GS_ERR_INVALID_ARGUMENT, "means2d / radii must be 8-byte, rec 16-byte aligned");
-    const Layout L = layout(n, bins->capacity);
+    const Layout L = layout(n, cap);
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.bytes)
         return fail(GS_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, 256-byte aligned", L.bytes);
     char *ws = static_cast<char *>(workspace);
@@ -304,6 +356,7 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     uint32_t *dkB = (uint32_t *)(ws + L.dkB), *dvB = (uint32_t *)(ws + L.dvB);
     uint32_t *cnt = (uint32_t *)(ws + L.cnt), *qcnt = (uint32_t *)(ws + L.qcnt), *doff = (uint32_t *)(ws + L.doff);
     unsigned long long *total = (unsigned long long *)(ws + L.total);
+    unsigned long long *klen = (unsigned long long *)(ws + L.klen);
     uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB);
     uint32_t *tvA = (uint32_t *)(ws + L.tvA), *tvB = (uint32_t *)(ws + L.tvB), *gauss = (uint32_t *)(ws + L.gauss);
     uint32_t *soff = (uint32_t *)(ws + L.soff);
@@ -326,59 +379,81 @@ extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_c
     GS_LAUNCH_CHECK("k_count");
     if ((s = exclusive_scan_u32(cnt, doff, n, part, total, stream)) != GS_OK) return s;
     if ((s = exclusive_scan_u32(qcnt, qoff, n + 1, part, total + 1, stream)) != GS_OK) return s;
-    unsigned long long KQ[2] = {0, 0};
-    GS_HIP(hipMemcpyAsync(KQ, total, sizeof(KQ), hipMemcpyDeviceToHost, stream));
-    GS_HIP(hipStreamSynchronize(stream));
-    const unsigned long long K = KQ[0];
-    // the quadrant records need kQuadFactor * capacity >= their count
-    const int64_t need = std::max<int64_t>((int64_t)K, ceil_div((int64_t)KQ[1], gsr::kQuadFactor));
-    *n_isect_out = (int64_t)K;
-    if (need > bins->capacity) {
-        *n_isect_out = need;
-        return fail(GS_ERR_CAPACITY, "%llu intersections (%llu quadrant records) need a capacity of %lld, have %lld",
-                    K, KQ[1], (long long)need, (long long)bins->capacity);
-    }
-
     if (bins->tiles_touched) {
         k_touched<<<gn, 256, 0, stream>>>(sv, cnt, n, bins->tiles_touched);
         GS_LAUNCH_CHECK("k_touched");
     }
-    if (K == 0) {
+
+    // 3. emit entries in depth order (nothing if the lists do not fit), then a stable sort
+    //    of (tile key, emit position) by tile
+    const int tbits = std::max(1, bits_for(T - 1));
+    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, qoff, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity),
+                                   alpha_min, n, tx, ty, total, cap, klen, hdr, counts, tkA, tvA, gauss, soff);
+    GS_LAUNCH_CHECK("k_emit");
+    if (cap == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
         k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
         GS_LAUNCH_CHECK("k_tile_order");
         return GS_OK;
     }
-
-    // 3. emit entries in depth order, then a stable sort of (tile key, emit position) by tile
-    const int tbits = std::max(1, bits_for(T - 1));
-    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, qoff, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity),
-                                   alpha_min, n, tx, ty, tkA, tvA, gauss, soff);
-    GS_LAUNCH_CHECK("k_emit");
-    if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, (int64_t)K, tbits, hist, part, &in_b, stream)) != GS_OK) return s;
+    if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, cap, tbits, hist, part, &in_b, stream, klen)) != GS_OK) return s;
     const uint32_t *tk = in_b ? tkB : tkA, *spos = in_b ? tvB : tvA;
 
     // 4. ids, per-tile ranges, quadrant bitmaps and their scanned bit counts, the quadrant
     //    record lists; optional 64-bit keys
-    const unsigned gk = (unsigned)ceil_div((int64_t)K, 256);
+    const unsigned gk = (unsigned)ceil_div(cap, 256);
     uint64_t *bm = reinterpret_cast<uint64_t *>(rb + RL.bitmap);
     uint32_t *wpre = reinterpret_cast<uint32_t *>(rb + RL.wpre);
     const int64_t nw = gsr::kQuads * (RL.words + 1);
     if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre), nw, 0, stream)) != GS_OK) return s;
-    k_finish<<<gk, 256, 0, stream>>>(tk, spos, gauss, (int64_t)K, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
+    k_finish<<<(unsigned)ceil_div(std::max<int64_t>(cap, (int64_t)T + 1), 256), 256, 0, stream>>>(
+        tk, spos, gauss, klen, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
     GS_LAUNCH_CHECK("k_finish");
     if ((s = exclusive_scan_u32(wpre, wpre, nw, part, nullptr, stream)) != GS_OK) return s;
-    k_quad_lists<<<(unsigned)std::max<int64_t>(gk, 1), 256, 0, stream>>>(
-        tk, spos, bins->ids, (int64_t)K, RL.words, bm, wpre, soff, reinterpret_cast<const float4 *>(proj->rec),
-        reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4);
+    k_quad_lists<<<gk, 256, 0, stream>>>(tk, spos, bins->ids, klen, RL.words, bm, wpre, soff,
+                                         reinterpret_cast<const float4 *>(proj->rec),
+                                         reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4);
     GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {
-        k_keys64<<<gk, 256, 0, stream>>>(tk, bins->ids, proj->depth, (int64_t)K, bins->keys);
+        k_keys64<<<gk, 256, 0, stream>>>(tk, bins->ids, proj->depth, klen, bins->keys);
         GS_LAUNCH_CHECK("k_keys64");
     }
 
     // 5. the order in which tiles are rasterized
     k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
     GS_LAUNCH_CHECK("k_tile_order");
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" gs_status gs_bin_sort_async(const gs_projected *proj, int64_t n, const gs_camera *cam,
+                                       const gs_raster_params *p, gs_bins *bins, int64_t *counts, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream)
+{
+    return bin_sort_launch(proj, n, cam, p, bins, counts, workspace, workspace_bytes, stream);
+}
+
+extern "C" gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam, const gs_raster_params *p,
+                                 gs_bins *bins, int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream)
+{
+    using namespace gsi;
+    if (!n_isect_out) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
+    *n_isect_out = 0;
+    gs_status s = bin_sort_launch(proj, n, cam, p, bins, nullptr, workspace, workspace_bytes, stream);
+    if (s != GS_OK) return s;
+    const gsr::RasterLayout RL =
+        gsr::raster_layout(n, bins->capacity, tiles_x(cam->width) * tiles_y(cam->height));
+    gsr::BinsHeader h{};
+    GS_HIP(hipMemcpyAsync(&h, static_cast<char *>(bins->raster) + RL.hdr, sizeof(h), hipMemcpyDeviceToHost, stream));
+    GS_HIP(hipStreamSynchronize(stream));
+    *n_isect_out = (int64_t)h.K;
+    if (!h.ok) {
+        const unsigned long long need = need_capacity(h.K, h.Q);
+        *n_isect_out = (int64_t)need;
+        return fail(GS_ERR_CAPACITY, "%llu intersections (%llu quadrant records) need a capacity of %llu, have %lld",
+                    h.K, h.Q, need, (long long)bins->capacity);
+    }
     return GS_OK;
 }

@@ -20,10 +20,12 @@ gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint3
 // Stable LSD radix sort of (key, value) uint32 pairs on the low `bits` bits of the key,
 // 8 bits per pass, ping-ponging between (ka, va) and (kb, vb).  Returns in *in_b whether
 // the sorted result ended in (kb, vb).  hist: radix_hist_len(m) uint32,
-// partials: scan_partials_len(radix_hist_len(m)) uint32.
+// partials: scan_partials_len(radix_hist_len(m)) uint32.  If m_dev is given, the number
+// of elements is min(m, *m_dev), read on the device (m sizes the launches).
 int64_t radix_hist_len(int64_t m);
 gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
-                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream);
+                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream,
+                         const unsigned long long *m_dev = nullptr);
 
 // Fills n int32 values with `value` (a kernel, not a memset, so it may be captured in graphs).
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream);

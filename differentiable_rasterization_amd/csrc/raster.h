@@ -2,6 +2,8 @@
 // rasterization kernels.
 //
 // Raster-ready lists (the gs_bins.raster buffer, written by gs_bin_sort):
+//   hdr    BinsHeader             the counts of the last sort: entries K, quadrant records
+//                                 Q, and whether the lists fit the capacity
 //   qrec   [2 * capacity] Rec     (plus kRecPad spare records at each end)
 //                                 for each 8x8 quadrant q of every tile (qx = q & 1,
 //                                 qy = q >> 1), the records of the tile's entries whose
@@ -104,8 +106,16 @@ __device__ __forceinline__ uint32_t quad_mask(float u, float v, float A, float B
     return m;
 }
 
+// Counts of the last sort, in device memory (the first bytes of the raster buffer).  When
+// the lists did not fit (ok == 0) the sort leaves every tile list empty and the per-Gaussian
+// gradient reduction writes zeros.
+struct BinsHeader {
+    unsigned long long K, Q;   // tile entries and (entry, quadrant) records
+    uint32_t ok, pad;
+};
+
 struct RasterLayout {
-    size_t qrec, bitmap, wpre, order, drank, qoff, qgrad, bytes;
+    size_t hdr, qrec, bitmap, wpre, order, drank, qoff, qgrad, bytes;
     int64_t cap, words;
 };
 
@@ -118,6 +128,7 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.words = (L.cap + 63) / 64;
     const size_t nn = (size_t)(n > 0 ? n : 1), q4 = (size_t)kQuadFactor * (size_t)L.cap;
     size_t o = 0;
+    L.hdr = o;    o += align256(sizeof(BinsHeader));
     L.qrec = o;   o += align256((q4 + 2 * kRecPad) * sizeof(Rec));   // kRecPad spare records at each end
     L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
     L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);

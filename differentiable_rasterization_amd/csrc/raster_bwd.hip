@@ -218,16 +218,19 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
 
 // Eq. 4: the gradient of Gaussian g is the sum of the slots of its quadrant records,
 // slots qoff[r] .. qoff[r + 1] for its depth rank r, added in order.  Every Gaussian is
-// written, culled ones (no records) with zeros.  One thread per Gaussian, in index order
+// written, culled ones (no records) with zeros, and all of them when the lists did not
+// fit the capacity.  One thread per Gaussian, in index order
 // so that the stores coalesce.
-__global__ __launch_bounds__(256) void k_grad_reduce(const uint32_t *__restrict__ drank, const uint32_t *__restrict__ qoff,
-                                                     const float4 *__restrict__ qgrad, int64_t n,
-                                                     float *__restrict__ grads2d)
+__global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
+                                                     const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
+                                                     int64_t n, float *__restrict__ grads2d)
 {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     const uint32_t r = drank[g];
-    const uint32_t s0 = qoff[r], s1 = qoff[r + 1];
+    // lists that did not fit the capacity were left empty: no slots to sum
+    const bool ok = hdr->ok != 0u;
+    const uint32_t s0 = ok ? qoff[r] : 0u, s1 = ok ? qoff[r + 1] : 0u;
     float acc[kFields];
 #pragma unroll
     for (int f = 0; f < kFields; ++f) acc[f] = 0.0f;
@@ -301,7 +304,8 @@ extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bin
         const RasterLayout L = raster_layout(n, bins->capacity, T);
         const char *rb = static_cast<const char *>(bins->raster);
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
-            reinterpret_cast<const uint32_t *>(rb + L.drank), reinterpret_cast<const uint32_t *>(rb + L.qoff),
+            reinterpret_cast<const BinsHeader *>(rb + L.hdr), reinterpret_cast<const uint32_t *>(rb + L.drank),
+            reinterpret_cast<const uint32_t *>(rb + L.qoff),
             reinterpret_cast<const float4 *>(rb + L.qgrad), n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }

@@ -123,10 +123,18 @@ __global__ __launch_bounds__(kThreads) void k_scan_down(const uint32_t *__restri
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restrict__ keys, int64_t m, int shift,
+// m_dev (may be NULL): the element count in device memory, at most m (the launch bound).
+__device__ __forceinline__ int64_t elem_count(int64_t m, const unsigned long long *m_dev)
+{
+    return m_dev ? (int64_t)min((unsigned long long)m, *m_dev) : m;
+}
+
+__global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restrict__ keys, int64_t m_max,
+                                                         const unsigned long long *__restrict__ m_dev, int shift,
                                                          uint32_t *__restrict__ hist, int64_t nb)
 {
     __shared__ uint32_t h[4][256];
+    const int64_t m = elem_count(m_max, m_dev);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&h[0][0])[i] = 0;
     __syncthreads();
@@ -144,9 +152,10 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
 __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__restrict__ kin,
                                                             const uint32_t *__restrict__ vin,
                                                             uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
-                                                            int64_t m, int shift, const uint32_t *__restrict__ offs,
-                                                            int64_t nb)
+                                                            int64_t m_max, const unsigned long long *__restrict__ m_dev,
+                                                            int shift, const uint32_t *__restrict__ offs, int64_t nb)
 {
+    const int64_t m = elem_count(m_max, m_dev);
     __shared__ uint32_t wcnt[4][256];
     __shared__ uint32_t bstart[256];
     __shared__ uint32_t gbase[256];
@@ -262,7 +271,8 @@ gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint3
 int64_t radix_hist_len(int64_t m) { return 256 * ceil_div(m > 0 ? m : 1, kTile); }
 
 gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
-                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream)
+                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream,
+                         const unsigned long long *m_dev)
 {
     *in_b = false;
     if (m <= 1 || bits <= 0) return GS_OK;
@@ -271,11 +281,11 @@ gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb,
     uint32_t *sk = ka, *sv = va, *dk = kb, *dv = vb;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
-        k_radix_hist<<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, shift, hist, nb);
+        k_radix_hist<<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb);
         GS_LAUNCH_CHECK("k_radix_hist");
         gs_status s = exclusive_scan_u32(hist, hist, 256 * nb, partials, nullptr, stream);
         if (s != GS_OK) return s;
-        k_radix_scatter<<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, shift, hist, nb);
+        k_radix_scatter<<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb);
         GS_LAUNCH_CHECK("k_radix_scatter");
         uint32_t *tk = sk, *tv = sv;
         sk = dk; sv = dv; dk = tk; dv = tv;

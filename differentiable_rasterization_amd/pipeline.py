@@ -118,6 +118,11 @@ class Binning:
         self.n_isect = k
         return k
 
+    def sort_async(self, proj: Projection, cam: B.Camera, params: B.RasterParams, counts=None, stream=None):
+        """Queues the sort without a host wait; counts (device int64[2]) receives (K,
+        required capacity or 0).  The caller checks it and repeats the step after growing."""
+        B.gs_bin_sort_async(proj.abi(), self.n, cam, params, self.abi(), counts, self.workspace, stream)
+
 
 class Frame:
     """Per-image buffers: render, transmittance, traversal counts, loss gradient."""

@@ -184,6 +184,19 @@ gs_status gs_bin_sort(const gs_projected *proj, int64_t n, const gs_camera *cam,
                       gs_bins *bins, int64_t *n_isect_out, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* gs_bin_sort without the read-back: nothing in the call waits for the device, so a
+ * training step can be queued (or captured) as a whole.  Every launch after the counting is
+ * sized by bins->capacity and reads the entry count on the device.  counts (device, may be
+ * NULL, 8-byte aligned): receives {K, required capacity} as two int64 when the stream gets
+ * there; required capacity is 0 when the lists fit, else the capacity gs_bin_sort would
+ * report with GS_ERR_CAPACITY.  Lists that do not fit are left empty (every tile range
+ * empty; gs_raster_fwd then renders nothing and gs_raster_bwd / gs_grad_aggregate write zero
+ * gradients): the caller checks counts, grows the buffers and repeats the step.  Otherwise
+ * identical results to gs_bin_sort. */
+gs_status gs_bin_sort_async(const gs_projected *proj, int64_t n, const gs_camera *cam, const gs_raster_params *p,
+                            gs_bins *bins, int64_t *counts, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Front-to-back alpha compositing per 16x16 tile (ByteSplat Eq. 1): for each pixel,
  * T = 1; for each entry of its tile list in order: stop if T < t_min; alpha =
  * min(alpha_max, o exp(-A dx^2/2 - B dx dy - C dy^2/2)); skip if alpha < alpha_min;

@@ -138,6 +138,44 @@ def test_bin_sort_all_culled_and_capacity():
     assert ei.value.required == len(ids)
 
 
+def test_bin_sort_async_matches_sync_and_reports_overflow():
+    """gs_bin_sort_async gives gs_bin_sort's lists and image bit for bit; when the lists do
+    not fit it reports the required capacity in its device counts and leaves every tile
+    list empty (nothing rendered, zero gradients)."""
+    sc = SMALL["ragged_sh2"]()
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    st = gpu_forward(sc, cam, rp)
+    c = B.camera_from(cam)
+    k_sync = st.bins.n_isect
+    ids0, rng0 = st.bins.ids[:k_sync].clone(), st.bins.tile_ranges.clone()
+    col0, t0, n0 = st.frame.color.clone(), st.frame.t_final.clone(), st.frame.n_trav.clone()
+    counts = torch.full((2,), -7, dtype=torch.int64, device=DEV)
+    st.bins.ids.zero_(); st.bins.tile_ranges.fill_(-1)
+    st.bins.sort_async(st.proj, c, rp, counts)
+    f = st.frame
+    B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, rp, f.color, f.t_final, f.n_trav)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [k_sync, 0]
+    assert torch.equal(st.bins.ids[:k_sync], ids0) and torch.equal(st.bins.tile_ranges, rng0)
+    assert torch.equal(f.color, col0) and torch.equal(f.t_final, t0) and torch.equal(f.n_trav, n0)
+    # too small: the sync call's error and the async call's counts agree
+    n = sc.n
+    small = PL.Binning(n, cam.width, cam.height, capacity=16, device=DEV)
+    with pytest.raises(B.GsCapacityError) as ei:
+        B.gs_bin_sort(st.proj.abi(), n, c, rp, small.abi(), small.workspace)
+    small.sort_async(st.proj, c, rp, counts)
+    B.gs_raster_fwd(st.proj.abi(), small.abi(), c, rp, f.color, f.t_final, f.n_trav)
+    g2 = torch.full((9, n), float("nan"), device=DEV)
+    B.gs_raster_bwd(st.params.gaussians(), st.proj.abi(), small.abi(), c, rp, f.color, f.t_final, f.n_trav,
+                    torch.ones_like(f.color), None, g2, None)
+    torch.cuda.synchronize()
+    assert counts.tolist() == [k_sync, ei.value.required] and ei.value.required > 16
+    assert int(small.tile_ranges.abs().sum()) == 0
+    assert float(f.color.abs().max()) == 0.0 and bool((f.t_final == 1.0).all()) and int(f.n_trav.sum()) == 0
+    assert float(g2.abs().max()) == 0.0
+
+
 # ------------------------------------------------------------------ forward compositing
 
 @pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "ragged_sh2", "offscreen_sh3", "100k"])
