@@ -4,8 +4,10 @@
                     [--cpu-rows R] [--copy-calibration-mib M]
 
 A step is one training iteration on one view: gs_project -> gs_bin_sort ->
-gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd (gs_raster_bwd_partials, gs_grad_aggregate)
--> gs_project_bwd -> gs_adam_step, on seeded synthetic data already resident in HBM.  The default workload is 1M
+gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd_partials -> gs_grad_aggregate_adam (the
+per-Gaussian gradient sum, projection backward and Adam in one pass; --unfused runs
+gs_grad_aggregate, gs_project_bwd and gs_adam_step instead), on seeded synthetic data
+already resident in HBM.  The default workload is 1M
 Gaussians (SH degree 3, 64 clusters in a 20 m cube) at 1920x1080 with four
 cameras on a sphere of radius 25; steps cycle through the four views.
 
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--workload", default="1m", choices=["1m", "100k", "10m", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1080, help="image rows the oracle baseline composites")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate gs_grad_aggregate, gs_project_bwd and gs_adam_step calls instead of the fused pass")
     ap.add_argument("--kernel-events", default="all", choices=["all", "dominant"],
                     help="HIP events around every call, or only around the dominant kernel's call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -89,6 +93,8 @@ def hbm_bytes(kernel, n, n_vis, k_sh, n_isect, n_px):
         return 8 * n + 24 * n_vis + 44 * n_isect
     if kernel == "grad_aggregate":
         return 36 * n_isect + 36 * n                                # one partial per (tile, Gaussian); grads2d
+    if kernel == "grad_adam":                                       # partials; p, m, v read and written
+        return 36 * n_isect + n * (11 + 3 * k_sh) * 24
     return None
 
 
@@ -140,7 +146,10 @@ def main():
     st.bins._alloc(int(st.bins.capacity * 1.3) + 4096)
     torch.cuda.synchronize()
 
-    names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
+    if args.unfused:
+        names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
+    else:
+        names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_adam"]
     g = params.gaussians()
 
     def one_step(i, ev=None, counts=None):
@@ -166,12 +175,16 @@ def main():
         rec(4)
         B.gs_raster_bwd_partials(g, st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.dL_dcolor, None)
         rec(5)
-        B.gs_grad_aggregate(g, st.bins.abi(), c, st.raster, st.grads2d, None)
-        rec(6)
-        st.backward_project(c)
-        rec(7)
-        st.adam()
-        rec(8)
+        if args.unfused:
+            B.gs_grad_aggregate(g, st.bins.abi(), c, st.raster, st.grads2d, None)
+            rec(6)
+            st.backward_project(c)
+            rec(7)
+            st.adam()
+            rec(8)
+        else:   # per-Gaussian sum, projection backward and Adam in one pass
+            st.aggregate_adam(c)
+            rec(6)
 
     if args.copy_calibration_mib > 0:
         # a copy-like kernel of known size (reads and writes M MiB) for counter normalisation
@@ -242,8 +255,9 @@ def main():
         "intersections_per_step": round(isect_step, 1),
         "tile_entries_per_step": round(kmean, 1),
         "visible_gaussians": n_vis,
-        "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]
-                                                   + per_kernel["grad_aggregate"]) * 1e-3), 1)
+        # Gaussian-pixel intersections over the two raster kernels' time (forward compositing
+        # and the per-pixel backward with its per-quadrant sums)
+        "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]) * 1e-3), 1)
         if "raster_fwd" in per_kernel else None,
         "kernel_events": args.kernel_events,
         "kernels": kernels,

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP = range(5)
 TILE = 16
 EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_bin_sort_async", "gs_raster_fwd", "gs_loss_workspace_bytes",
-            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
+            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_last_error")
 
 
@@ -76,6 +76,10 @@ class ParamGrads(ctypes.Structure):
                 ("opacity_logits", ctypes.c_void_p), ("sh", ctypes.c_void_p)]
 
 
+class AdamLrs(ctypes.Structure):
+    _fields_ = [(nm, ctypes.c_float) for nm in ("means", "log_scales", "quats", "opacity_logits", "sh_dc", "sh_rest")]
+
+
 class AdamGroup(ctypes.Structure):
     _fields_ = [("p", ctypes.c_void_p), ("g", ctypes.c_void_p), ("m", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("n", ctypes.c_int64), ("lr", ctypes.c_float)]
@@ -97,6 +101,8 @@ _SIGS = {
     "gs_raster_bwd_partials": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp,
                                       _vp, _vp]),
     "gs_grad_aggregate": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
+    "gs_grad_aggregate_adam": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads),
+                                      _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32, _f32, _vp]),
     "gs_project_bwd": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
     "gs_adam_step": (_i32, [_P(AdamGroup), _i32, _i32, _f32, _f32, _f32, _vp]),
     "gs_composite_over": (_i32, [_P(_vp), _P(_vp), _i32, _i64, _f32, _vp, _vp, _vp]),
@@ -239,6 +245,13 @@ def gs_grad_aggregate(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, grads
     _check(_lib.gs_grad_aggregate(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
                                   _ptr(grads2d), ctypes.byref(grads3d) if grads3d is not None else None,
                                   _stream(stream)))
+
+
+def gs_grad_aggregate_adam(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, grads2d, m: ParamGrads, v: ParamGrads,
+                           lr: "AdamLrs", step, beta1, beta2, eps, stream=None):
+    _check(_lib.gs_grad_aggregate_adam(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
+                                       _ptr(grads2d), ctypes.byref(m), ctypes.byref(v), ctypes.byref(lr), step, beta1,
+                                       beta2, eps, _stream(stream)))
 
 
 def gs_project_bwd(g: Gaussians, cam: Camera, p: RasterParams, grads2d, grads3d: ParamGrads, stream=None):

@@ -110,6 +110,16 @@ __device__ __forceinline__ unsigned rank_below(uint64_t mask)
     return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
 }
 
+// One bias-corrected Adam step of one scalar (step = lr / (1 - b1^t), inv_bc2 =
+// 1 / (1 - b2^t)); every Adam path of the library uses this, so they agree bit for bit.
+__device__ __forceinline__ void adam_update(float &p, float g, float &m, float &v, float b1, float b2, float inv_bc2,
+                                            float eps, float step)
+{
+    m = fmaf(b1, m, (1.0f - b1) * g);
+    v = fmaf(b2, v, (1.0f - b2) * g * g);
+    p -= step * m / (__fsqrt_rn(v * inv_bc2) + eps);
+}
+
 // Tile rectangle [x0,x1) x [y0,y1) touched by the box [u-rx, u+rx] x [v-ry, v+ry],
 // float32 arithmetic (division by 16 is exact), clamped to the tile grid.
 __device__ __forceinline__ void tile_rect(float u, float v, int rx, int ry, int tx, int ty,

@@ -72,13 +72,7 @@ struct AdamArgs {
     float b1, b2, inv_bc2, eps;
 };
 
-__device__ __forceinline__ void adam1(float &p, float g, float &m, float &v, float b1, float b2, float inv_bc2,
-                                      float eps, float step)
-{
-    m = fmaf(b1, m, (1.0f - b1) * g);
-    v = fmaf(b2, v, (1.0f - b2) * g * g);
-    p -= step * m / (__fsqrt_rn(v * inv_bc2) + eps);
-}
+using gsd::adam_update;
 
 // One float4 of one group per thread; every block lies inside one group.  The four
 // streams are read and written once, so the accesses are non-temporal (they would only
@@ -102,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void k_adam(AdamArgs a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             float pc = p[c], mc = m[c], vc = v[c];
-            adam1(pc, g[c], mc, vc, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            adam_update(pc, g[c], mc, vc, a.b1, a.b2, a.inv_bc2, a.eps, st);
             p[c] = pc;
             m[c] = mc;
             v[c] = vc;
@@ -113,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_adam(AdamArgs a)
     } else {
         for (int64_t e = 4 * j; e < min(4 * j + 4, n); ++e) {
             float p = a.p[gi][e], m = a.m[gi][e], v = a.v[gi][e];
-            adam1(p, a.g[gi][e], m, v, a.b1, a.b2, a.inv_bc2, a.eps, st);
+            adam_update(p, a.g[gi][e], m, v, a.b1, a.b2, a.inv_bc2, a.eps, st);
             a.p[gi][e] = p;
             a.m[gi][e] = m;
             a.v[gi][e] = v;

@@ -11,8 +11,11 @@
 //     ("Scaling 3D Gaussian Splatting with Distributed Compute", walkthrough step 4)
 // The geometric chain runs in double (it is memory bound, so this costs no time on
 // MI355X) and is rounded once to the float32 record.  SH evaluation runs in float.
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
+#include "raster.h"
 
 namespace {
 
@@ -257,40 +260,136 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
 // Backward through projection and colour evaluation (ByteSplat, section 2.1: the
 // aggregated screen-space gradients are propagated through projection and colour
 // evaluation to the 3D parameters).  Exact chain rule of project_core; the float
-// rounding of the record is treated as the identity.
-template <int DEG>
-__global__ __launch_bounds__(256) void k_project_bwd(
-    const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
-    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
-    float depth_lo, float depth_hi, const float *__restrict__ g2, float *__restrict__ d_means,
-    float *__restrict__ d_ls, float *__restrict__ d_q, float *__restrict__ d_logit, float *__restrict__ d_sh)
+// rounding of the record is treated as the identity.  The gradients of one Gaussian are
+// collected in registers (the SH gradients as Y_k(v^) and dL/dc, their product formed
+// where it is used) and handed with the current parameter values to a sink: GradSink
+// stores them, AdamSink applies the Adam update at once.
+template <int K>
+struct Grad3 {
+    float means[3], ls[3], q[4], logit;
+    float Y[K], gc[3];
+    __device__ float sh(int plane) const { return Y[plane / 3] * gc[plane % 3]; }
+};
+
+template <int K>
+struct Params1 {   // one Gaussian's parameters as loaded
+    float means[3], ls[3], q[4], logit, sh[3 * K];
+};
+
+struct GradSink {
+    float *d_means, *d_ls, *d_q, *d_logit, *d_sh;
+    int64_t n;
+    template <int K>
+    __device__ void flush(int64_t i, const Grad3<K> &g, const Params1<K> &) const
+    {
+        for (int j = 0; j < 3; ++j) d_means[j * n + i] = g.means[j];
+        for (int j = 0; j < 3; ++j) d_ls[j * n + i] = g.ls[j];
+        for (int j = 0; j < 4; ++j) d_q[j * n + i] = g.q[j];
+        d_logit[i] = g.logit;
+#pragma unroll
+        for (int k = 0; k < 3 * K; ++k) d_sh[(int64_t)k * n + i] = g.sh(k);
+    }
+};
+
+// Adam over the parameter scalars of one Gaussian, a chunk of planes at a time: every
+// moment load of a chunk is issued before any store, so the loads overlap.
+struct AdamSink {
+    float *p[5], *m[5], *v[5];   // means, log_scales, quats, opacity_logits, sh
+    int64_t n;
+    float st[6];                 // lr / (1 - b1^t): means, log_scales, quats, opacity, sh DC, sh rest
+    float b1, b2, inv_bc2, eps;
+
+    template <int N>
+    __device__ void chunk(const int (&grp)[N], const int (&plane)[N], const float (&g)[N], const float (&pv)[N],
+                          const float (&step)[N], int64_t i) const
+    {
+        float mv[N], vv[N];
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+            const int64_t idx = (int64_t)plane[c] * n + i;
+            mv[c] = __builtin_nontemporal_load(m[grp[c]] + idx);
+            vv[c] = __builtin_nontemporal_load(v[grp[c]] + idx);
+        }
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+            float pc = pv[c];
+            gsd::adam_update(pc, g[c], mv[c], vv[c], b1, b2, inv_bc2, eps, step[c]);
+            const int64_t idx = (int64_t)plane[c] * n + i;
+            __builtin_nontemporal_store(pc, p[grp[c]] + idx);
+            __builtin_nontemporal_store(mv[c], m[grp[c]] + idx);
+            __builtin_nontemporal_store(vv[c], v[grp[c]] + idx);
+        }
+    }
+
+    template <int K>
+    __device__ void flush(int64_t i, const Grad3<K> &g, const Params1<K> &P) const
+    {
+        {   // means, log_scales, quats, opacity: 11 scalars
+            const int grp[11] = {0, 0, 0, 1, 1, 1, 2, 2, 2, 2, 3};
+            const int pl[11] = {0, 1, 2, 0, 1, 2, 0, 1, 2, 3, 0};
+            const float gg[11] = {g.means[0], g.means[1], g.means[2], g.ls[0], g.ls[1], g.ls[2],
+                                  g.q[0], g.q[1], g.q[2], g.q[3], g.logit};
+            const float pv[11] = {P.means[0], P.means[1], P.means[2], P.ls[0], P.ls[1], P.ls[2],
+                                  P.q[0], P.q[1], P.q[2], P.q[3], P.logit};
+            const float sp[11] = {st[0], st[0], st[0], st[1], st[1], st[1], st[2], st[2], st[2], st[2], st[3]};
+            chunk(grp, pl, gg, pv, sp, i);
+        }
+        constexpr int kChunk = 3 * K < 12 ? 3 * K : 12;
+#pragma unroll
+        for (int c0 = 0; c0 < 3 * K; c0 += kChunk) {
+            int grp[kChunk], pl[kChunk];
+            float gg[kChunk], pv[kChunk], sp[kChunk];
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                grp[c] = 4;
+                pl[c] = c0 + c;
+                gg[c] = g.sh(c0 + c);
+                pv[c] = P.sh[c0 + c];
+                sp[c] = c0 + c < 3 ? st[4] : st[5];
+            }
+            chunk(grp, pl, gg, pv, sp, i);
+        }
+    }
+};
+
+template <int DEG, class Sink>
+__device__ __forceinline__ void project_bwd_one(const float *__restrict__ means, const float *__restrict__ log_scales,
+                                                const float *__restrict__ quats, const float *__restrict__ logits,
+                                                const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
+                                                float alpha_min, float depth_lo, float depth_hi, const float (&g2)[9],
+                                                const Sink &out)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const float fmx = means[i], fmy = means[n + i], fmz = means[2 * n + i];
-    float shc[3 * K];
+    Params1<K> prm;
+    prm.means[0] = means[i]; prm.means[1] = means[n + i]; prm.means[2] = means[2 * n + i];
+    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[n + i]; prm.ls[2] = log_scales[2 * n + i];
+    prm.q[0] = quats[i]; prm.q[1] = quats[n + i]; prm.q[2] = quats[2 * n + i]; prm.q[3] = quats[3 * n + i];
+    prm.logit = logits[i];
+    const float *shc = prm.sh;
     bool shf = true;
 #pragma unroll
     for (int k = 0; k < 3 * K; ++k) {
-        shc[k] = sh[(int64_t)k * n + i];
-        shf = shf && __builtin_isfinite(shc[k]);
+        prm.sh[k] = sh[(int64_t)k * n + i];
+        shf = shf && __builtin_isfinite(prm.sh[k]);
     }
     Proj P;
-    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, log_scales[i], log_scales[n + i], log_scales[2 * n + i],
-                 quats[i], quats[n + i], quats[2 * n + i], quats[3 * n + i], logits[i], shf, (double)alpha_min,
-                 depth_lo, depth_hi, P);
+    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
+    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
+                 prm.q[3], prm.logit, shf, (double)alpha_min, depth_lo, depth_hi, P);
+    Grad3<K> G;
     if (!P.vis) {
-        for (int j = 0; j < 3; ++j) { d_means[j * n + i] = 0.0f; d_ls[j * n + i] = 0.0f; }
-        for (int j = 0; j < 4; ++j) d_q[j * n + i] = 0.0f;
-        d_logit[i] = 0.0f;
+        for (int j = 0; j < 3; ++j) G.means[j] = G.ls[j] = 0.0f;
+        for (int j = 0; j < 4; ++j) G.q[j] = 0.0f;
+        G.logit = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 3 * K; ++k) d_sh[(int64_t)k * n + i] = 0.0f;
+        for (int k = 0; k < K; ++k) G.Y[k] = 0.0f;
+        G.gc[0] = G.gc[1] = G.gc[2] = 0.0f;
+        out.flush(i, G, prm);
         return;
     }
-    const double gu = g2[i], gv = g2[n + i], gA = g2[2 * n + i], gB = g2[3 * n + i], gC = g2[4 * n + i];
-    const double go = g2[5 * n + i];
-    const float gc[3] = {g2[6 * n + i], g2[7 * n + i], g2[8 * n + i]};
+    const double gu = g2[0], gv = g2[1], gA = g2[2], gB = g2[3], gC = g2[4];
+    const double go = g2[5];
+    const float gc[3] = {g2[6], g2[7], g2[8]};
 
     // conic = Sigma2D^-1:  G_S2 = -Q G_Q Q with G_Q = [[gA, gB/2], [gB/2, gC]]
     const double A = P.A, B = P.B, C = P.C;
@@ -349,7 +448,7 @@ __global__ __launch_bounds__(256) void k_project_bwd(
             ds += gm * R[3 * r + k];
             GR[3 * r + k] = gm * P.s[k];
         }
-        d_ls[k * n + i] = (float)(ds * P.s[k]);
+        G.ls[k] = (float)(ds * P.s[k]);
     }
     // R(q^) -> q^ -> q
     const double w = P.q[0], x = P.q[1], y = P.q[2], z = P.q[3];
@@ -363,20 +462,16 @@ __global__ __launch_bounds__(256) void k_project_bwd(
                    + y * GR[7]);
     const double qd = w * dq[0] + x * dq[1] + y * dq[2] + z * dq[3];
     const double iq = 1.0 / P.qnorm;
-    for (int j = 0; j < 4; ++j) d_q[j * n + i] = (float)((dq[j] - P.q[j] * qd) * iq);
+    for (int j = 0; j < 4; ++j) G.q[j] = (float)((dq[j] - P.q[j] * qd) * iq);
 
-    d_logit[i] = (float)(go * P.o * (1.0 - P.o));
+    G.logit = (float)(go * P.o * (1.0 - P.o));
 
     // colour: d sh_k = Y_k dc;  d v^ = sum_k (sh_k . dc) grad Y_k
-    float Y[K], wk[K];
-    sh_basis<DEG>(P.dir[0], P.dir[1], P.dir[2], Y);
+    float wk[K];
+    sh_basis<DEG>(P.dir[0], P.dir[1], P.dir[2], G.Y);
+    G.gc[0] = gc[0]; G.gc[1] = gc[1]; G.gc[2] = gc[2];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        d_sh[(int64_t)(3 * k + 0) * n + i] = Y[k] * gc[0];
-        d_sh[(int64_t)(3 * k + 1) * n + i] = Y[k] * gc[1];
-        d_sh[(int64_t)(3 * k + 2) * n + i] = Y[k] * gc[2];
-        wk[k] = shc[3 * k] * gc[0] + shc[3 * k + 1] * gc[1] + shc[3 * k + 2] * gc[2];
-    }
+    for (int k = 0; k < K; ++k) wk[k] = shc[3 * k] * gc[0] + shc[3 * k + 1] * gc[1] + shc[3 * k + 2] * gc[2];
     float gx, gy, gz;
     sh_grad<DEG>(P.dir[0], P.dir[1], P.dir[2], wk, gx, gy, gz);
     const double vd = (double)P.dir[0] * gx + (double)P.dir[1] * gy + (double)P.dir[2] * gz;
@@ -384,7 +479,43 @@ __global__ __launch_bounds__(256) void k_project_bwd(
     dmu[0] += (gx - P.dir[0] * vd) * idist;
     dmu[1] += (gy - P.dir[1] * vd) * idist;
     dmu[2] += (gz - P.dir[2] * vd) * idist;
-    for (int j = 0; j < 3; ++j) d_means[j * n + i] = (float)dmu[j];
+    for (int j = 0; j < 3; ++j) G.means[j] = (float)dmu[j];
+    out.flush(i, G, prm);
+}
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project_bwd(
+    const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+    float depth_lo, float depth_hi, const float *__restrict__ g2, GradSink out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float g[9];
+#pragma unroll
+    for (int f = 0; f < 9; ++f) g[f] = g2[(int64_t)f * n + i];
+    project_bwd_one<DEG>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, g, out);
+}
+
+// The end of a training step per Gaussian: the per-Gaussian sum of Eq. 4 over its
+// quadrant-record slots (as k_grad_reduce; optionally stored in grads2d), the projection
+// backward, and the Adam update of every parameter scalar.
+template <int DEG>
+__global__ __launch_bounds__(256) void k_grad_adam(
+    const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+    float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
+    const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad, float *__restrict__ grads2d, AdamSink out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float g[9];
+    gsr::sum_slots(hdr, drank, qoff, qgrad, i, g);
+    if (grads2d) {
+#pragma unroll
+        for (int f = 0; f < 9; ++f) grads2d[(int64_t)f * n + i] = g[f];
+    }
+    project_bwd_one<DEG>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, g, out);
 }
 
 }  // namespace
@@ -410,11 +541,10 @@ gs_status launch_project_bwd(const gs_gaussians *g, const gs_camera *cam, const 
         return fail(GS_ERR_INVALID_ARGUMENT, "a grads3d pointer is NULL");
     const CamD cd = make_cam(cam);
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+    const GradSink sink{out->means, out->log_scales, out->quats, out->opacity_logits, out->sh, n};
 #define GS_PB(D)                                                                                              \
     k_project_bwd<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, \
-                                                 n, cd, p->alpha_min, p->depth_lo, p->depth_hi, grads2d,      \
-                                                 out->means, out->log_scales, out->quats, out->opacity_logits, \
-                                                 out->sh)
+                                                 n, cd, p->alpha_min, p->depth_lo, p->depth_hi, grads2d, sink)
     switch (p->sh_degree) {
     case 0: GS_PB(0); break;
     case 1: GS_PB(1); break;
@@ -475,4 +605,67 @@ extern "C" gs_status gs_project_bwd(const gs_gaussians *g, const gs_camera *cam,
     if (!grads3d) return fail(GS_ERR_INVALID_ARGUMENT, "grads3d is NULL");
     if (g->n > 0 && !grads2d) return fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
     return launch_project_bwd(g, cam, p, grads2d, grads3d, stream);
+}
+
+namespace gsi {
+gs_status check_raster_inputs(const gs_bins *bins, const gs_camera *cam);
+}
+
+extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                            const gs_raster_params *p, float *grads2d, const gs_param_grads *m,
+                                            const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1,
+                                            float beta2, float eps, hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if ((s = check_gaussians(g)) != GS_OK) return s;
+    if ((s = check_camera(cam)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
+    if (!m || !v || !lr) return fail(GS_ERR_INVALID_ARGUMENT, "m / v / lr is NULL");
+    if (step < 1) return fail(GS_ERR_INVALID_ARGUMENT, "step must be >= 1");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f && eps >= 0.0f))
+        return fail(GS_ERR_INVALID_ARGUMENT, "bad Adam hyper-parameters");
+    const int64_t n = g->n;
+    if (n == 0) return GS_OK;
+    if (!m->means || !m->log_scales || !m->quats || !m->opacity_logits || !m->sh || !v->means || !v->log_scales ||
+        !v->quats || !v->opacity_logits || !v->sh)
+        return fail(GS_ERR_INVALID_ARGUMENT, "an Adam moment pointer is NULL");
+    AdamSink sink;
+    float *params[5] = {const_cast<float *>(g->means), const_cast<float *>(g->log_scales), const_cast<float *>(g->quats),
+                        const_cast<float *>(g->opacity_logits), const_cast<float *>(g->sh)};
+    float *ms[5] = {m->means, m->log_scales, m->quats, m->opacity_logits, m->sh};
+    float *vs[5] = {v->means, v->log_scales, v->quats, v->opacity_logits, v->sh};
+    for (int a = 0; a < 5; ++a) { sink.p[a] = params[a]; sink.m[a] = ms[a]; sink.v[a] = vs[a]; }
+    sink.n = n;
+    // the same host arithmetic as gs_adam_step, so that both paths agree bit for bit
+    const double bc1 = 1.0 - std::pow((double)beta1, step), bc2 = 1.0 - std::pow((double)beta2, step);
+    const float lrs[6] = {lr->means, lr->log_scales, lr->quats, lr->opacity_logits, lr->sh_dc, lr->sh_rest};
+    for (int a = 0; a < 6; ++a) sink.st[a] = (float)((double)lrs[a] / bc1);
+    sink.b1 = beta1;
+    sink.b2 = beta2;
+    sink.inv_bc2 = (float)(1.0 / bc2);
+    sink.eps = eps;
+    const int T = tiles_x(cam->width) * tiles_y(cam->height);
+    const gsr::RasterLayout L = gsr::raster_layout(n, bins->capacity, T);
+    const char *rb = static_cast<const char *>(bins->raster);
+    const gsr::BinsHeader *hdr = reinterpret_cast<const gsr::BinsHeader *>(rb + L.hdr);
+    const uint32_t *drank = reinterpret_cast<const uint32_t *>(rb + L.drank);
+    const uint32_t *qoff = reinterpret_cast<const uint32_t *>(rb + L.qoff);
+    const float4 *qg = reinterpret_cast<const float4 *>(rb + L.qgrad);
+    const CamD cd = make_cam(cam);
+    const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+#define GS_GA(D)                                                                                                   \
+    k_grad_adam<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, cd, \
+                                               p->alpha_min, p->depth_lo, p->depth_hi, hdr, drank, qoff, qg,      \
+                                               grads2d, sink)
+    switch (p->sh_degree) {
+    case 0: GS_GA(0); break;
+    case 1: GS_GA(1); break;
+    case 2: GS_GA(2); break;
+    default: GS_GA(3); break;
+    }
+#undef GS_GA
+    GS_LAUNCH_CHECK("k_grad_adam");
+    return GS_OK;
 }

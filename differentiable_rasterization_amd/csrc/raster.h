@@ -140,6 +140,27 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     return L;
 }
 
+// ByteSplat Eq. 4 for Gaussian g: the sum of the gradient slots of its quadrant records,
+// slots qoff[r] .. qoff[r + 1] for its depth rank r, added in order (zero when the lists
+// did not fit the capacity).
+__device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
+                                          const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
+                                          int64_t g, float (&acc)[9])
+{
+    const uint32_t r = drank[g];
+    const bool ok = hdr->ok != 0u;
+    const uint32_t s0 = ok ? qoff[r] : 0u, s1 = ok ? qoff[r + 1] : 0u;
+#pragma unroll
+    for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
+    for (uint32_t j = s0; j < s1; ++j) {
+        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
+        const float4 a = sl[0], b = sl[1], c = sl[2];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+        acc[8] += c.x;
+    }
+}
+
 // Number of entries below x (0 <= x <= K) that belong to quadrant q: the position in
 // qrec[q] of the first record at or after entry x.  bq = bitmap + q * words,
 // wq = wpre + q * (words + 1).

@@ -227,20 +227,8 @@ __global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restric
 {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
-    const uint32_t r = drank[g];
-    // lists that did not fit the capacity were left empty: no slots to sum
-    const bool ok = hdr->ok != 0u;
-    const uint32_t s0 = ok ? qoff[r] : 0u, s1 = ok ? qoff[r + 1] : 0u;
     float acc[kFields];
-#pragma unroll
-    for (int f = 0; f < kFields; ++f) acc[f] = 0.0f;
-    for (uint32_t j = s0; j < s1; ++j) {
-        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
-        const float4 a = sl[0], b = sl[1], c = sl[2];
-        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-        acc[8] += c.x;
-    }
+    sum_slots(hdr, drank, qoff, qgrad, g, acc);
 #pragma unroll
     for (int f = 0; f < kFields; ++f) grads2d[(size_t)f * n + g] = acc[f];
 }

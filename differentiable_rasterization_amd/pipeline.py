@@ -60,6 +60,13 @@ class GaussianParams:
         v = lambda nm: self.view(self.grad, nm)
         return B.param_grads(v("means"), v("log_scales"), v("quats"), v("opacity_logits"), v("sh"))
 
+    def moments(self):
+        """(m, v) as ABI parameter sets."""
+        def ps(buf):
+            v = lambda nm: self.view(buf, nm)
+            return B.param_grads(v("means"), v("log_scales"), v("quats"), v("opacity_logits"), v("sh"))
+        return ps(self.m), ps(self.v)
+
     def adam_groups(self, lr=DEFAULT_LR):
         bounds = [("means", 0, 3), ("log_scales", 3, 6), ("quats", 6, 10), ("opacity_logits", 10, 11),
                   ("sh_dc", 11, 14), ("sh_rest", 14, self.planes)]
@@ -181,6 +188,19 @@ class TrainStep:
     def adam(self, stream=None):
         self.params.step_count += 1
         B.gs_adam_step(self.params.adam_groups(self.lr), self.params.step_count, 0.9, 0.999, 1e-15, stream)
+
+    def aggregate_adam(self, cam: B.Camera, grads2d=None, stream=None):
+        """Per-Gaussian gradient sum, projection backward and Adam in one pass (after
+        backward_partials); the 3D gradients are not stored."""
+        self.params.step_count += 1
+        m, v = self.params.moments()
+        B.gs_grad_aggregate_adam(self.params.gaussians(), self.bins.abi(), cam, self.raster, grads2d, m, v,
+                                 B.AdamLrs(**self.lr), self.params.step_count, 0.9, 0.999, 1e-15, stream)
+
+    def backward_partials(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):
+        f = self.frame
+        B.gs_raster_bwd_partials(self.params.gaussians(), self.bins.abi(), cam, self.raster, f.color, f.t_final,
+                                 f.n_trav, f.dL_dcolor if dL_dcolor is None else dL_dcolor, dL_dt, stream)
 
     def step(self, cam: B.Camera, target, stream=None):
         self.forward(cam, stream)

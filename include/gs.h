@@ -252,6 +252,27 @@ gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bins, const gs
                             const gs_raster_params *p, float *grads2d, gs_param_grads *grads3d,
                             hipStream_t stream);
 
+/* Learning rates of the fused step below, per parameter group (the SH coefficients split
+ * into the DC term, planes 0..2, and the rest). */
+typedef struct {
+    float means, log_scales, quats, opacity_logits, sh_dc, sh_rest;
+} gs_adam_lrs;
+
+/* The end of a training step in one pass over the Gaussians, for callers that update
+ * right after each backward (batch size 1): per Gaussian, the per-Gaussian part of the
+ * ByteSplat Eq. 4 sum (as gs_grad_aggregate), the projection backward (as gs_project_bwd)
+ * and the Adam update of every parameter scalar (as gs_adam_step with the groups means,
+ * log_scales, quats, opacity_logits, sh planes 0..2, sh planes 3.., and the learning rates
+ * in lr).  The 3D gradients are never stored.  The results equal gs_grad_aggregate,
+ * gs_project_bwd and gs_adam_step in sequence, bit for bit.  g: the parameters, read and
+ * then updated in place (the arrays must be writable device memory).  m, v: the Adam
+ * moments, same shapes as the parameters, updated in place.  grads2d [9][n] (may be NULL):
+ * receives the screen-space gradients.  bins, cam, p: as for gs_grad_aggregate. */
+gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                 const gs_raster_params *p, float *grads2d, const gs_param_grads *m,
+                                 const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1,
+                                 float beta2, float eps, hipStream_t stream);
+
 /* Backward through projection and colour evaluation alone (ByteSplat section 2.1: the
  * aggregated screen-space gradients are propagated through projection and colour
  * evaluation): from grads2d [9][n] (fields u, v, A, B, C, o, r, g, b) to grads3d (every

@@ -310,6 +310,36 @@ def test_backward_split_matches_whole():
     assert torch.equal(st.grads2d, whole2) and torch.equal(st.params.grad, whole3)
 
 
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "100k"])
+def test_fused_aggregate_adam_matches_separate_calls(name):
+    """gs_grad_aggregate_adam equals gs_grad_aggregate -> gs_project_bwd -> gs_adam_step bit
+    for bit (parameters, moments, screen-space gradients), over two steps."""
+    sc = _scene(name)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    c = B.camera_from(cam)
+    tgt = sc.targets[0].to(DEV)
+    runs = []
+    for fused in (False, True):
+        st = gpu_forward(sc, cam, rp)
+        for step in range(2):
+            if step:
+                st.forward(c)
+            st.loss(tgt)
+            if fused:
+                st.backward_partials(c)
+                st.aggregate_adam(c, grads2d=st.grads2d)
+            else:
+                st.backward(c)
+                st.adam()
+        torch.cuda.synchronize()
+        runs.append((st.params.data.clone(), st.params.m.clone(), st.params.v.clone(), st.grads2d.clone()))
+    (p0, m0, v0, g0), (p1, m1, v1, g1) = runs
+    assert torch.equal(g0, g1)
+    assert torch.equal(p0, p1) and torch.equal(m0, m1) and torch.equal(v0, v1)
+    assert float((m1 != 0).float().mean()) > 0.0
+
+
 # ------------------------------------------------------------------ Adam
 
 @pytest.mark.parametrize("n,step", [(1, 1), (1001, 1), (4096, 7), (250_001, 3)])
