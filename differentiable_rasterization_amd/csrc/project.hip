@@ -352,41 +352,14 @@ struct AdamSink {
     }
 };
 
-template <int DEG, class Sink>
-__device__ __forceinline__ void project_bwd_one(const float *__restrict__ means, const float *__restrict__ log_scales,
-                                                const float *__restrict__ quats, const float *__restrict__ logits,
-                                                const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
-                                                float alpha_min, float depth_lo, float depth_hi, const float (&g2)[9],
-                                                const Sink &out)
+// The chain rule for a Gaussian the projection keeps.
+template <int DEG>
+__device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam, const float (&g2)[9],
+                                                  const Params1<(DEG + 1) * (DEG + 1)> &prm,
+                                                  Grad3<(DEG + 1) * (DEG + 1)> &G)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    Params1<K> prm;
-    prm.means[0] = means[i]; prm.means[1] = means[n + i]; prm.means[2] = means[2 * n + i];
-    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[n + i]; prm.ls[2] = log_scales[2 * n + i];
-    prm.q[0] = quats[i]; prm.q[1] = quats[n + i]; prm.q[2] = quats[2 * n + i]; prm.q[3] = quats[3 * n + i];
-    prm.logit = logits[i];
     const float *shc = prm.sh;
-    bool shf = true;
-#pragma unroll
-    for (int k = 0; k < 3 * K; ++k) {
-        prm.sh[k] = sh[(int64_t)k * n + i];
-        shf = shf && __builtin_isfinite(prm.sh[k]);
-    }
-    Proj P;
-    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
-    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
-                 prm.q[3], prm.logit, shf, (double)alpha_min, depth_lo, depth_hi, P);
-    Grad3<K> G;
-    if (!P.vis) {
-        for (int j = 0; j < 3; ++j) G.means[j] = G.ls[j] = 0.0f;
-        for (int j = 0; j < 4; ++j) G.q[j] = 0.0f;
-        G.logit = 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) G.Y[k] = 0.0f;
-        G.gc[0] = G.gc[1] = G.gc[2] = 0.0f;
-        out.flush(i, G, prm);
-        return;
-    }
     const double gu = g2[0], gv = g2[1], gA = g2[2], gB = g2[3], gC = g2[4];
     const double go = g2[5];
     const float gc[3] = {g2[6], g2[7], g2[8]};
@@ -480,6 +453,41 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
     dmu[1] += (gy - P.dir[1] * vd) * idist;
     dmu[2] += (gz - P.dir[2] * vd) * idist;
     for (int j = 0; j < 3; ++j) G.means[j] = (float)dmu[j];
+}
+
+template <int DEG, class Sink>
+__device__ __forceinline__ void project_bwd_one(const float *__restrict__ means, const float *__restrict__ log_scales,
+                                                const float *__restrict__ quats, const float *__restrict__ logits,
+                                                const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
+                                                float alpha_min, float depth_lo, float depth_hi, const float (&g2)[9],
+                                                const Sink &out)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    Params1<K> prm;
+    prm.means[0] = means[i]; prm.means[1] = means[n + i]; prm.means[2] = means[2 * n + i];
+    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[n + i]; prm.ls[2] = log_scales[2 * n + i];
+    prm.q[0] = quats[i]; prm.q[1] = quats[n + i]; prm.q[2] = quats[2 * n + i]; prm.q[3] = quats[3 * n + i];
+    prm.logit = logits[i];
+    bool shf = true;
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) {
+        prm.sh[k] = sh[(int64_t)k * n + i];
+        shf = shf && __builtin_isfinite(prm.sh[k]);
+    }
+    Proj P;
+    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
+    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
+                 prm.q[3], prm.logit, shf, (double)alpha_min, depth_lo, depth_hi, P);
+    // culled Gaussians get zero gradients; every lane reaches the one flush at the end, so
+    // a wave issues the sink's memory traffic once
+    Grad3<K> G;
+    for (int j = 0; j < 3; ++j) G.means[j] = G.ls[j] = 0.0f;
+    for (int j = 0; j < 4; ++j) G.q[j] = 0.0f;
+    G.logit = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) G.Y[k] = 0.0f;
+    G.gc[0] = G.gc[1] = G.gc[2] = 0.0f;
+    if (P.vis) project_bwd_grads<DEG>(P, cam, g2, prm, G);
     out.flush(i, G, prm);
 }
 
