@@ -60,8 +60,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1080, help="image rows the oracle baseline composites")
     ap.add_argument("--unfused", action="store_true",
                     help="separate gs_grad_aggregate, gs_project_bwd and gs_adam_step calls instead of the fused pass")
-    ap.add_argument("--kernel-events", default="all", choices=["all", "dominant"],
-                    help="HIP events around every call, or only around the dominant kernel's call")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the untimed pass that times every call separately")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a copy-like kernel over this many MiB before timing (counter normalisation)")
     return ap.parse_args()
@@ -152,14 +152,18 @@ def main():
         names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_adam"]
     g = params.gaussians()
 
-    def one_step(i, ev=None, counts=None):
+    i_bwd = names.index("raster_bwd")
+
+    def one_step(i, ev=None, counts=None, every_call=False):
+        """ev: HIP events, recorded around the dominant kernel's call only (each record costs
+        the stream a few microseconds), or around every call if every_call."""
         c, t = cams[i % nviews], targets[i % nviews]
         if ev is None:
             rec = lambda k: None
-        elif args.kernel_events == "all":
+        elif every_call:
             rec = lambda k: ev[k].record()
-        else:   # step boundaries and the dominant kernel only
-            rec = lambda k: ev[k].record() if k in (0, 4, 5, len(names)) else None
+        else:
+            rec = lambda k: ev[k].record() if k in (i_bwd, i_bwd + 1) else None
         f = st.frame
         rec(0)
         B.gs_project(g, c, st.raster, st.proj.abi())
@@ -197,7 +201,9 @@ def main():
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                          for _ in range(args.steps)]
+    events = new_events()
     st.frame.n_trav_sum.zero_()
     counts = torch.zeros(args.steps, 2, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
@@ -212,10 +218,18 @@ def main():
         raise RuntimeError(f"intersection lists overflowed during the timed steps (need {int(cnt[:, 1].max())})")
     k_isect = [int(k) for k in cnt[:, 0]]
     isect_total = int(st.frame.n_trav_sum.item())
-    timed = range(len(names)) if args.kernel_events == "all" else [names.index("raster_bwd")]
-    per_kernel = {names[j]: sum(events[s][j].elapsed_time(events[s][j + 1]) for s in range(args.steps)) / args.steps
-                  for j in timed}
-    step_ms = sorted(events[s][0].elapsed_time(events[s][-1]) for s in range(args.steps))
+    bwd_ms = sum(events[s][i_bwd].elapsed_time(events[s][i_bwd + 1]) for s in range(args.steps)) / args.steps
+    per_kernel, step_ms = {"raster_bwd": bwd_ms}, None
+    if not args.no_breakdown:
+        # untimed: the same steps again with an event around every call
+        ev2 = new_events()
+        for i in range(args.steps):
+            one_step(args.warmup + i, ev2[i], counts[i], every_call=True)
+        torch.cuda.synchronize()
+        per_kernel = {names[j]: sum(ev2[s][j].elapsed_time(ev2[s][j + 1]) for s in range(args.steps)) / args.steps
+                      for j in range(len(names))}
+        per_kernel["raster_bwd"] = bwd_ms
+        step_ms = sorted(ev2[s][0].elapsed_time(ev2[s][-1]) for s in range(args.steps))
     ms_step = wall * 1e3 / args.steps
     isect_step = isect_total / args.steps
     n = scene.n
@@ -250,8 +264,10 @@ def main():
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
                    "views": nviews, "step": "one view: fwd + L1 + bwd + Adam"},
         "roofline": roof,
+        # from the untimed pass with an event around every call
         "step_stream_ms": {"median": round(step_ms[len(step_ms) // 2], 4),
-                           "p90": round(step_ms[min(len(step_ms) - 1, int(0.9 * len(step_ms)))], 4)},
+                           "p90": round(step_ms[min(len(step_ms) - 1, int(0.9 * len(step_ms)))], 4)}
+        if step_ms else None,
         "intersections_per_step": round(isect_step, 1),
         "tile_entries_per_step": round(kmean, 1),
         "visible_gaussians": n_vis,
@@ -259,7 +275,8 @@ def main():
         # and the per-pixel backward with its per-quadrant sums)
         "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]) * 1e-3), 1)
         if "raster_fwd" in per_kernel else None,
-        "kernel_events": args.kernel_events,
+        "kernels_note": "raster_bwd from events in the timed steps; the others from an untimed pass of the "
+                        "same steps with an event around every call",
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
     }

@@ -8,6 +8,8 @@
 // emits its entries in that order, and a stable sort of the entries by tile id
 // (1-2 eight-bit passes for up to 65536 tiles) leaves every tile's list in
 // (depth key, index) order.  Same result, roughly a quarter of the bytes.
+#include <cmath>
+
 #include "kernels.h"
 #include "raster.h"
 
@@ -15,10 +17,14 @@ namespace {
 
 constexpr uint32_t kCulledKey = 0xFFFFFFFFu;
 
+// Depth keys (culled Gaussians last) and their indices; also clears the scans' look-back
+// state for this sort (zero: zero_words uint32).
 __global__ __launch_bounds__(256) void k_depth_keys(const int2 *__restrict__ radii, const float *__restrict__ depth,
-                                                    int64_t n, uint32_t *__restrict__ keys, uint32_t *__restrict__ vals)
+                                                    int64_t n, uint32_t *__restrict__ keys, uint32_t *__restrict__ vals,
+                                                    uint32_t *__restrict__ zero, int64_t zero_words)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t z = i; z < zero_words; z += (int64_t)gridDim.x * blockDim.x) zero[z] = 0u;
     if (i >= n) return;
     const int2 r = radii[i];
     keys[i] = (r.x > 0 && r.y > 0) ? __float_as_uint(depth[i]) : kCulledKey;
@@ -30,8 +36,7 @@ __global__ __launch_bounds__(256) void k_depth_keys(const int2 *__restrict__ rad
 // exclusive scan ends with the total); also records each Gaussian's depth rank for the
 // backward's per-Gaussian reduction.
 __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skeys, const uint32_t *__restrict__ svals,
-                                               const float2 *__restrict__ means2d, const int2 *__restrict__ radii,
-                                               const float4 *__restrict__ conic_o, float alpha_min, int64_t n,
+                                               const float4 *__restrict__ rec, float log2_amin, int64_t n,
                                                int tx, int ty, uint32_t *__restrict__ cnt, uint32_t *__restrict__ qcnt,
                                                uint32_t *__restrict__ drank)
 {
@@ -41,16 +46,14 @@ __global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skey
     uint32_t c = 0, qc = 0;
     const uint32_t g = svals[j];
     if (skeys[j] != kCulledKey) {
-        const float2 m = means2d[g];
-        const int2 r = radii[g];
-        const float4 co = conic_o[g];
-        const float thr = 2.0f * __logf(co.w / alpha_min);
+        const float4 p0 = rec[gsr::kRecF4 * (size_t)g], p1 = rec[gsr::kRecF4 * (size_t)g + 1],
+                     p2 = rec[gsr::kRecF4 * (size_t)g + 2];
         int x0, x1, y0, y1;
-        gsd::tile_rect(m.x, m.y, r.x, r.y, tx, ty, x0, x1, y0, y1);
+        gsd::tile_rect(p0.x, p0.y, __float_as_int(p2.z), __float_as_int(p2.w), tx, ty, x0, x1, y0, y1);
         c = (uint32_t)((x1 - x0) * (y1 - y0));
         for (int y = y0; y < y1; ++y)
             for (int x = x0; x < x1; ++x)
-                qc += __popc(gsr::quad_mask(m.x, m.y, co.x, co.y, co.z, thr, (float)(x * GS_TILE), (float)(y * GS_TILE)));
+                qc += __popc(gsr::quad_mask_rec(p0, p1, log2_amin, (float)(x * GS_TILE), (float)(y * GS_TILE)));
     }
     cnt[j] = c;
     qcnt[j] = qc;
@@ -70,9 +73,8 @@ __device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned lo
 // its first quadrant record (the Gaussian's slots follow its entries in order).
 __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
                                               const uint32_t *__restrict__ off, const uint32_t *__restrict__ qoff,
-                                              const float2 *__restrict__ means2d,
-                                              const int2 *__restrict__ radii, const float4 *__restrict__ conic_o,
-                                              float alpha_min, int64_t n, int tx, int ty,
+                                              const float4 *__restrict__ rec, float log2_amin, int64_t n, int tx,
+                                              int ty,
                                               const unsigned long long *__restrict__ tot, int64_t cap,
                                               unsigned long long *__restrict__ klen, gsr::BinsHeader *__restrict__ hdr,
                                               int64_t *__restrict__ counts,
@@ -94,17 +96,14 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
     }
     if (!ok || j >= n || cnt[j] == 0) return;
     const uint32_t g = svals[j];
-    const float2 m = means2d[g];
-    const int2 r = radii[g];
-    const float4 co = conic_o[g];
-    const float thr = 2.0f * __logf(co.w / alpha_min);
+    const float4 p0 = rec[gsr::kRecF4 * (size_t)g], p1 = rec[gsr::kRecF4 * (size_t)g + 1],
+                 p2 = rec[gsr::kRecF4 * (size_t)g + 2];
     int x0, x1, y0, y1;
-    gsd::tile_rect(m.x, m.y, r.x, r.y, tx, ty, x0, x1, y0, y1);
+    gsd::tile_rect(p0.x, p0.y, __float_as_int(p2.z), __float_as_int(p2.w), tx, ty, x0, x1, y0, y1);
     uint32_t p = off[j], sl = qoff[j];
     for (int y = y0; y < y1; ++y)
         for (int x = x0; x < x1; ++x) {
-            const uint32_t qm =
-                gsr::quad_mask(m.x, m.y, co.x, co.y, co.z, thr, (float)(x * GS_TILE), (float)(y * GS_TILE));
+            const uint32_t qm = gsr::quad_mask_rec(p0, p1, log2_amin, (float)(x * GS_TILE), (float)(y * GS_TILE));
             tkeys[p] = (uint32_t)(y * tx + x) | (qm << gsr::kMaskShift);
             tvals[p] = p;
             gauss[p] = g;
@@ -117,9 +116,10 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
 // Finishes the sorted lists in one pass over the entries: the Gaussian index of each
 // entry, tile_ranges[t] = first entry of tile t (entries are sorted by tile; ranges[T] =
 // K), and the quadrant bitmaps with their per-word bit counts (one 64-bit word per wave and
-// quadrant; block bases are multiples of 64).  `wcnt` [4][words + 1] must be zero
-// beforehand; its exclusive scan gives the positions of the quadrant records.  The
-// launch covers max(capacity, T + 1) threads; K is read on the device.
+// quadrant; block bases are multiples of 64).  Every word of the bitmaps and of `wcnt`
+// [4][words + 1] is written (zero past the entries); the exclusive scan of wcnt gives the
+// positions of the quadrant records.  The launch covers max(capacity, T + 1) threads (all
+// `words` words); K is read on the device.
 __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
                                                 const uint32_t *__restrict__ gauss,
                                                 const unsigned long long *__restrict__ klen, int32_t T,
@@ -129,10 +129,8 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t K = (int64_t)*klen;
-    if (K == 0) {   // no entries (or lists that did not fit): every tile list is empty
-        if (k <= T) ranges[k] = 0;
-        return;
-    }
+    if (k < gsr::kQuads) wcnt[(int64_t)k * (words + 1) + words] = 0u;
+    if (K == 0 && k <= T) ranges[k] = 0;   // no entries (or lists that did not fit): all lists empty
     uint32_t qm = 0;
     if (k < K) {
         const uint32_t key = tkeys[k];
@@ -148,7 +146,7 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
 #pragma unroll
     for (int q = 0; q < gsr::kQuads; ++q) {
         const uint64_t b = __ballot((qm >> q) & 1u);
-        if ((threadIdx.x & 63) == 0 && wbase < K) {
+        if ((threadIdx.x & 63) == 0 && (wbase >> 6) < words) {
             bitmap[(int64_t)q * words + (wbase >> 6)] = b;
             wcnt[(int64_t)q * (words + 1) + (wbase >> 6)] = (uint32_t)__popcll(b);
         }
@@ -253,29 +251,44 @@ __global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restr
 }
 
 struct Layout {
-    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, gauss, soff, hist, part, bytes;
+    // zero region (cleared by k_depth_keys at the start of every sort): tickets and
+    // look-back status words of the scans
+    size_t zero, tickets, stD, stT, scC, scQ, scW, zero_bytes;
+    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, gauss, soff, hist, bytes;
+    int tbits;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Layout layout(int64_t n, int64_t cap)
+int bits_for(int64_t maxval);
+
+// tickets: 0-3 depth sort passes, 4-6 tile sort passes, 8 tile counts, 9 quadrant counts,
+// 10 quadrant bit counts
+constexpr int kTkDepth = 0, kTkTile = 4, kTkCnt = 8, kTkQcnt = 9, kTkWpre = 10;
+
+Layout layout(int64_t n, int64_t cap, int32_t tiles)
 {
     Layout L;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     const size_t nn = (size_t)(n > 0 ? n : 1), cc = (size_t)(cap > 0 ? cap : 1);
+    L.tbits = std::max(1, bits_for((int64_t)tiles - 1));
+    const int64_t nw = gsr::kQuads * (gsr::raster_layout(n, cap, 1).words + 1);
+    L.zero = o;
+    L.tickets = take(16 * 4);
+    L.stD = take(8 * (size_t)gsi::radix_scan_status_len((int64_t)nn, 32));
+    L.stT = take(8 * (size_t)gsi::radix_scan_status_len((int64_t)cc, L.tbits));
+    L.scC = take(8 * (size_t)gsi::lb_scan_tiles((int64_t)nn));
+    L.scQ = take(8 * (size_t)gsi::lb_scan_tiles((int64_t)nn + 1));
+    L.scW = take(8 * (size_t)gsi::lb_scan_tiles(nw));
+    L.zero_bytes = o - L.zero;
     L.dkA = take(4 * nn); L.dvA = take(4 * nn); L.dkB = take(4 * nn); L.dvB = take(4 * nn);
     L.cnt = take(4 * nn); L.qcnt = take(4 * (nn + 1)); L.doff = take(4 * nn);
     L.total = take(16);   // K, then the quadrant records
     L.klen = take(8);     // K if the lists fit, else 0
     L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(4 * cc); L.tvB = take(4 * cc); L.gauss = take(4 * cc);
     L.soff = take(4 * cc);
-    const int64_t mmax = std::max<int64_t>(n + 1, cap);
-    const int64_t hl = gsi::radix_hist_len(mmax);
-    L.hist = take(4 * (size_t)hl);
-    const int64_t qwords = gsr::kQuads * (gsr::raster_layout(n, cap, 1).words + 1);   // quadrant bit-count scan
-    const int64_t pl = std::max({gsi::scan_partials_len(hl), gsi::scan_partials_len(mmax), gsi::scan_partials_len(qwords)});
-    L.part = take(4 * (size_t)pl);
+    L.hist = take(4 * (size_t)gsi::radix_hist_len(std::max<int64_t>((int64_t)nn, (int64_t)cc)));
     L.bytes = o;
     return L;
 }
@@ -297,9 +310,8 @@ extern "C" size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t widt
 
 extern "C" size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height)
 {
-    (void)width; (void)height;
-    if (n < 0 || capacity < 0) return 0;
-    return layout(n, capacity).bytes;
+    if (n < 0 || capacity < 0 || width <= 0 || height <= 0) return 0;
+    return layout(n, capacity, gsi::tiles_x(width) * gsi::tiles_y(height)).bytes;
 }
 
 namespace {
@@ -314,7 +326,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     gs_status s;
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
-    const float alpha_min = p->alpha_min;
+    const float log2_amin = std::log2(p->alpha_min);
     if (!proj || !bins) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
     if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
     if (n > (int64_t(1) << 31) - 2) return fail(GS_ERR_UNSUPPORTED, "n >= 2^31 - 1");
@@ -341,14 +353,11 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
         GS_LAUNCH_CHECK("k_bins_empty");
         return GS_OK;
     }
-    if (!proj->means2d || !proj->depth || !proj->radii)
-        return fail(GS_ERR_INVALID_ARGUMENT, "projected means2d / depth / radii is NULL");
-    if (!proj->rec || !proj->conic_opacity)
-        return fail(GS_ERR_INVALID_ARGUMENT, "projected rec / conic_opacity is NULL");
-    if (!aligned(proj->conic_opacity, 16)) return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity must be 16-byte aligned");
-    if (!aligned(proj->means2d, 8) || !aligned(proj->radii, 8) || !aligned(proj->rec, 16))
-        return fail(GS_ERR_INVALID_ARGUMENT, "means2d / radii must be 8-byte, rec 16-byte aligned");
-    const Layout L = layout(n, cap);
+    if (!proj->depth || !proj->radii || !proj->rec)
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected depth / radii / rec is NULL");
+    if (!aligned(proj->radii, 8) || !aligned(proj->rec, 16))
+        return fail(GS_ERR_INVALID_ARGUMENT, "radii must be 8-byte, rec 16-byte aligned");
+    const Layout L = layout(n, cap, T);
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.bytes)
         return fail(GS_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, 256-byte aligned", L.bytes);
     char *ws = static_cast<char *>(workspace);
@@ -360,25 +369,29 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB);
     uint32_t *tvA = (uint32_t *)(ws + L.tvA), *tvB = (uint32_t *)(ws + L.tvB), *gauss = (uint32_t *)(ws + L.gauss);
     uint32_t *soff = (uint32_t *)(ws + L.soff);
-    uint32_t *hist = (uint32_t *)(ws + L.hist), *part = (uint32_t *)(ws + L.part);
-    const float2 *m2 = reinterpret_cast<const float2 *>(proj->means2d);
+    uint32_t *hist = (uint32_t *)(ws + L.hist), *tickets = (uint32_t *)(ws + L.tickets);
+    unsigned long long *stD = (unsigned long long *)(ws + L.stD), *stT = (unsigned long long *)(ws + L.stT);
+    unsigned long long *scC = (unsigned long long *)(ws + L.scC), *scQ = (unsigned long long *)(ws + L.scQ);
+    unsigned long long *scW = (unsigned long long *)(ws + L.scW);
     const int2 *rr = reinterpret_cast<const int2 *>(proj->radii);
+    const float4 *prec = reinterpret_cast<const float4 *>(proj->rec);
     const unsigned gn = (unsigned)ceil_div(n, 256);
 
     // 1. Gaussians by depth key (stable, so equal keys stay in index order)
-    k_depth_keys<<<gn, 256, 0, stream>>>(rr, proj->depth, n, dkA, dvA);
+    k_depth_keys<<<gn, 256, 0, stream>>>(rr, proj->depth, n, dkA, dvA, (uint32_t *)(ws + L.zero),
+                                         (int64_t)(L.zero_bytes / 4));
     GS_LAUNCH_CHECK("k_depth_keys");
     bool in_b = false;
-    if ((s = radix_sort_u32(dkA, dvA, dkB, dvB, n, 32, hist, part, &in_b, stream)) != GS_OK) return s;
+    if ((s = radix_sort_u32(dkA, dvA, dkB, dvB, n, 32, hist, stD, tickets + kTkDepth, &in_b, stream)) != GS_OK)
+        return s;
     const uint32_t *sk = in_b ? dkB : dkA, *sv = in_b ? dvB : dvA;
 
     // 2. tile and quadrant-record counts in depth order, their exclusive scans (the emit
     //    offsets and the first gradient slot of each Gaussian) and the totals K and Q
-    k_count<<<gn, 256, 0, stream>>>(sk, sv, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity), alpha_min,
-                                    n, tx, ty, cnt, qcnt, drank);
+    k_count<<<gn, 256, 0, stream>>>(sk, sv, prec, log2_amin, n, tx, ty, cnt, qcnt, drank);
     GS_LAUNCH_CHECK("k_count");
-    if ((s = exclusive_scan_u32(cnt, doff, n, part, total, stream)) != GS_OK) return s;
-    if ((s = exclusive_scan_u32(qcnt, qoff, n + 1, part, total + 1, stream)) != GS_OK) return s;
+    if ((s = lb_scan_u32(cnt, doff, n, scC, tickets + kTkCnt, total, stream)) != GS_OK) return s;
+    if ((s = lb_scan_u32(qcnt, qoff, n + 1, scQ, tickets + kTkQcnt, total + 1, stream)) != GS_OK) return s;
     if (bins->tiles_touched) {
         k_touched<<<gn, 256, 0, stream>>>(sv, cnt, n, bins->tiles_touched);
         GS_LAUNCH_CHECK("k_touched");
@@ -386,9 +399,9 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
 
     // 3. emit entries in depth order (nothing if the lists do not fit), then a stable sort
     //    of (tile key, emit position) by tile
-    const int tbits = std::max(1, bits_for(T - 1));
-    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, qoff, m2, rr, reinterpret_cast<const float4 *>(proj->conic_opacity),
-                                   alpha_min, n, tx, ty, total, cap, klen, hdr, counts, tkA, tvA, gauss, soff);
+    const int tbits = L.tbits;
+    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, qoff, prec, log2_amin, n, tx, ty, total, cap, klen, hdr, counts, tkA,
+                                   tvA, gauss, soff);
     GS_LAUNCH_CHECK("k_emit");
     if (cap == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
@@ -396,7 +409,9 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
         GS_LAUNCH_CHECK("k_tile_order");
         return GS_OK;
     }
-    if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, cap, tbits, hist, part, &in_b, stream, klen)) != GS_OK) return s;
+    if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, cap, tbits, hist, stT, tickets + kTkTile, &in_b, stream, klen)) !=
+        GS_OK)
+        return s;
     const uint32_t *tk = in_b ? tkB : tkA, *spos = in_b ? tvB : tvA;
 
     // 4. ids, per-tile ranges, quadrant bitmaps and their scanned bit counts, the quadrant
@@ -405,14 +420,12 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     uint64_t *bm = reinterpret_cast<uint64_t *>(rb + RL.bitmap);
     uint32_t *wpre = reinterpret_cast<uint32_t *>(rb + RL.wpre);
     const int64_t nw = gsr::kQuads * (RL.words + 1);
-    if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre), nw, 0, stream)) != GS_OK) return s;
     k_finish<<<(unsigned)ceil_div(std::max<int64_t>(cap, (int64_t)T + 1), 256), 256, 0, stream>>>(
         tk, spos, gauss, klen, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
     GS_LAUNCH_CHECK("k_finish");
-    if ((s = exclusive_scan_u32(wpre, wpre, nw, part, nullptr, stream)) != GS_OK) return s;
+    if ((s = lb_scan_u32(wpre, wpre, nw, scW, tickets + kTkWpre, nullptr, stream)) != GS_OK) return s;
     k_quad_lists<<<gk, 256, 0, stream>>>(tk, spos, bins->ids, klen, RL.words, bm, wpre, soff,
-                                         reinterpret_cast<const float4 *>(proj->rec),
-                                         reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4);
+                                         prec, reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4);
     GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {
         k_keys64<<<gk, 256, 0, stream>>>(tk, bins->ids, proj->depth, klen, bins->keys);

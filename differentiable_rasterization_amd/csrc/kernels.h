@@ -17,15 +17,25 @@ int64_t scan_partials_len(int64_t m);
 gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint32_t *partials,
                              unsigned long long *total, hipStream_t stream);
 
+// Exclusive scan of m >= 1 uint32 values (in place allowed) in one launch, by look-back
+// over the published sums of earlier tiles.  status [lb_scan_tiles(m)] uint64 and *ticket
+// must be zero on entry (each scan needs its own).  If total != NULL the 64-bit sum is
+// written there.
+int64_t lb_scan_tiles(int64_t m);
+gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
+                      unsigned long long *total, hipStream_t stream);
+
 // Stable LSD radix sort of (key, value) uint32 pairs on the low `bits` bits of the key,
 // 8 bits per pass, ping-ponging between (ka, va) and (kb, vb).  Returns in *in_b whether
-// the sorted result ended in (kb, vb).  hist: radix_hist_len(m) uint32,
-// partials: scan_partials_len(radix_hist_len(m)) uint32.  If m_dev is given, the number
-// of elements is min(m, *m_dev), read on the device (m sizes the launches).
+// the sorted result ended in (kb, vb).  hist: radix_hist_len(m) uint32; scan_status
+// [radix_scan_status_len(m, bits)] uint64 and scan_tickets [passes] must be zero on entry.
+// If m_dev is given, the number of elements is min(m, *m_dev), read on the device (m
+// sizes the launches).
 int64_t radix_hist_len(int64_t m);
+int64_t radix_scan_status_len(int64_t m, int bits);
 gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
-                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream,
-                         const unsigned long long *m_dev = nullptr);
+                         uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
+                         hipStream_t stream, const unsigned long long *m_dev = nullptr);
 
 // Fills n int32 values with `value` (a kernel, not a memset, so it may be captured in graphs).
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream);

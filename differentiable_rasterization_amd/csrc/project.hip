@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
     const double o32 = (double)(float)P.o;
     rec[3 * i + 0] = make_float4((float)P.u, (float)P.v, (float)(-0.5 * kL2e * P.A), (float)(-kL2e * P.B));
     rec[3 * i + 1] = make_float4((float)(-0.5 * kL2e * P.C), (float)log2(o32), r, g);
-    rec[3 * i + 2] = make_float4(b, __uint_as_float((uint32_t)i), 0.0f, 0.0f);
+    rec[3 * i + 2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(P.rx), __int_as_float(P.ry));
 }
 
 // Backward through projection and colour evaluation (ByteSplat, section 2.1: the

@@ -45,7 +45,8 @@ constexpr int kQuads = 4;
 // with a = -log2(e) A / 2, b = -log2(e) B, c = -log2(e) C / 2, l = log2(o).
 //   p0 = (u, v, a, b)   p1 = (c, l, red, green)   p2 = (blue, index bits, entry bits, slot bits)
 // "entry" is the record's position k in the 16x16 tile lists and "slot" the index of its
-// gradient slot (both set by the binning).
+// gradient slot (both set by the binning; in the per-Gaussian records the projection writes,
+// those two words hold the box half-extents rx, ry as int32 bits).
 // The backward recovers A = -2 ln(2) a, B = -ln(2) b, C = -2 ln(2) c and 1/o = exp2(-l).
 struct Rec {
     float4 p0, p1, p2;
@@ -113,6 +114,15 @@ struct BinsHeader {
     unsigned long long K, Q;   // tile entries and (entry, quadrant) records
     uint32_t ok, pad;
 };
+
+// The same test from a raster record (conic pre-scaled for exp2, l = log2 o):
+// alpha >= alpha_min  <=>  a dx^2 + b dx dy + c dy^2 >= log2(alpha_min) - l, i.e. the
+// positive form -a dx^2 - b dx dy - c dy^2 is at most l - log2(alpha_min).
+__device__ __forceinline__ uint32_t quad_mask_rec(const float4 &p0, const float4 &p1, float log2_amin, float x0,
+                                                  float y0)
+{
+    return quad_mask(p0.x, p0.y, -p0.z, -0.5f * p0.w, -p1.x, p1.y - log2_amin, x0, y0);
+}
 
 struct RasterLayout {
     size_t hdr, qrec, bitmap, wpre, order, drank, qoff, qgrad, bytes;

@@ -229,6 +229,111 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
     }
 }
 
+// ------------------------------------------------------------------ single-launch scan
+//
+// Each block takes the next tile of kTile values in arrival order (an atomic ticket: any
+// tile it waits for belongs to a block that has already started), publishes its sum, and
+// finds the sum of everything before it by looking back over the published sums, 64 tiles
+// per step (one wave, one status word per lane), until it meets a tile that has published
+// its inclusive prefix.  64-bit status words: flag in bits 62..63 (0 = not yet published,
+// 1 = the tile's own sum, 2 = its inclusive prefix), the sum below.
+constexpr unsigned long long kFlagSum = 1ull << 62, kFlagIncl = 2ull << 62, kFlagMask = 3ull << 62;
+
+__device__ __forceinline__ unsigned long long status_load(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void status_store(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_scan_lb(const uint32_t *in, uint32_t *out, int64_t m,
+                                                      unsigned long long *__restrict__ status,
+                                                      uint32_t *__restrict__ ticket,
+                                                      unsigned long long *__restrict__ total)
+{
+    __shared__ uint32_t scratch[4];
+    __shared__ uint32_t s_tile;
+    __shared__ unsigned long long s_excl;
+    if (threadIdx.x == 0) s_tile = atomicAdd(ticket, 1u);
+    __syncthreads();
+    const int64_t tile = s_tile;
+    const int64_t base = tile * kTile + (int64_t)threadIdx.x * kItems;
+    uint32_t v[kItems];
+    const bool full = base + kItems <= m;
+    if (full) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(in + base);
+#pragma unroll
+        for (int k = 0; k < kItems / 4; ++k) {
+            const uint4 q = p[k];
+            v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) v[k] = base + k < m ? in[base + k] : 0u;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) sum += v[k];
+    uint32_t tot32;
+    const uint32_t pre = block_exclusive_scan(sum, scratch, &tot32);
+    const unsigned long long tot = tot32;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        if (lane == 0) status_store(status + tile, (tile == 0 ? kFlagIncl : kFlagSum) | tot);
+        unsigned long long excl = 0;
+        if (tile > 0) {
+            for (int64_t hi = tile - 1;; hi -= 64) {
+                const int64_t j = hi - lane;   // lane 0 is the nearest tile
+                // before tile 0 everything is an inclusive prefix of 0
+                unsigned long long x = j >= 0 ? status_load(status + j) : kFlagIncl;
+                while (__ballot((x & kFlagMask) == 0ull)) {   // wait for the window to be published
+                    __builtin_amdgcn_s_sleep(1);
+                    if ((x & kFlagMask) == 0ull) x = status_load(status + j);
+                }
+                const uint64_t incl = __ballot((x & kFlagMask) == kFlagIncl);
+                if (incl) {
+                    const int first = __ffsll((long long)incl) - 1;   // nearest inclusive prefix
+                    excl += wave_sum_u64(lane <= first ? (x & ~kFlagMask) : 0ull);
+                    break;
+                }
+                excl += wave_sum_u64(x & ~kFlagMask);
+            }
+        }
+        if (lane == 0) {
+            if (tile > 0) status_store(status + tile, kFlagIncl | (excl + tot));
+            s_excl = excl;
+            if (total && (tile + 1) * kTile >= m) *total = excl + tot;   // the last tile
+        }
+    }
+    __syncthreads();
+    uint32_t run = (uint32_t)s_excl + pre;
+    if (full) {
+        uint4 *p = reinterpret_cast<uint4 *>(out + base);
+#pragma unroll
+        for (int k = 0; k < kItems / 4; ++k) {
+            uint4 q;
+            q.x = run; run += v[4 * k];
+            q.y = run; run += v[4 * k + 1];
+            q.z = run; run += v[4 * k + 2];
+            q.w = run; run += v[4 * k + 3];
+            p[k] = q;
+        }
+    } else {
+        for (int k = 0; k < kItems; ++k)
+            if (base + k < m) { out[base + k] = run; run += v[k]; }
+    }
+}
+
 __global__ void k_fill_i32(int32_t *__restrict__ p, int64_t n, int32_t value)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -270,9 +375,25 @@ gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint3
 
 int64_t radix_hist_len(int64_t m) { return 256 * ceil_div(m > 0 ? m : 1, kTile); }
 
+int64_t lb_scan_tiles(int64_t m) { return ceil_div(m > 0 ? m : 1, kTile); }
+
+gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
+                      unsigned long long *total, hipStream_t stream)
+{
+    if (m <= 0) return fail(GS_ERR_UNSUPPORTED, "scan of an empty array");
+    k_scan_lb<<<(unsigned)lb_scan_tiles(m), kThreads, 0, stream>>>(in, out, m, status, ticket, total);
+    GS_LAUNCH_CHECK("k_scan_lb");
+    return GS_OK;
+}
+
+int64_t radix_scan_status_len(int64_t m, int bits)
+{
+    return (int64_t)((bits + 7) / 8) * lb_scan_tiles(radix_hist_len(m));
+}
+
 gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
-                         uint32_t *hist, uint32_t *partials, bool *in_b, hipStream_t stream,
-                         const unsigned long long *m_dev)
+                         uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
+                         hipStream_t stream, const unsigned long long *m_dev)
 {
     *in_b = false;
     if (m <= 1 || bits <= 0) return GS_OK;
@@ -283,7 +404,8 @@ gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb,
         const int shift = 8 * p;
         k_radix_hist<<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb);
         GS_LAUNCH_CHECK("k_radix_hist");
-        gs_status s = exclusive_scan_u32(hist, hist, 256 * nb, partials, nullptr, stream);
+        gs_status s = lb_scan_u32(hist, hist, 256 * nb, scan_status + p * lb_scan_tiles(256 * nb), scan_tickets + p,
+                                  nullptr, stream);
         if (s != GS_OK) return s;
         k_radix_scatter<<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb);
         GS_LAUNCH_CHECK("k_radix_scatter");

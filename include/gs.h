@@ -100,7 +100,9 @@ typedef struct {
  *   rec [n][12]           raster-ready copy of the same record (16-byte aligned): u, v, the
  *                         conic pre-scaled for a base-2 exponential (-A log2(e)/2,
  *                         -B log2(e), -C log2(e)/2), log2(o), red, green, blue, the index as
- *                         uint32 bits, two zero words.  gs_bin_sort gathers it per list entry.
+ *                         uint32 bits, rx and ry as int32 bits.  gs_bin_sort takes each
+ *                         Gaussian's tile box and quadrant test from it and copies it per
+ *                         list entry.
  * For culled Gaussians only radii and depth are written. */
 typedef struct {
     float *means2d, *conic_opacity, *color, *depth;
@@ -157,8 +159,8 @@ gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raste
                      gs_projected *out, hipStream_t stream);
 
 /* Bytes of the gs_bins.raster buffer for n Gaussians, `capacity` list entries and a W x H
- * image: 2 quadrant records (48 B) and 2 gradient slots (48 B), 4 map words and 4 quadrant bits
- * per entry, plus 8 B per Gaussian and 4 B per tile. */
+ * image: 2 quadrant records (48 B), 2 gradient slots (48 B) and 4 quadrant bits per entry,
+ * plus 8 B per Gaussian, 4 B per tile and a 256-byte header. */
 size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
 
 /* Workspace bytes gs_bin_sort needs for n Gaussians, `capacity` list entries and the
@@ -172,9 +174,10 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, i
  * for y).  Entries are ordered by (tile, depth key bits, Gaussian index): a stable LSD
  * radix sort of the Gaussians by depth key, a scan of their tile counts in that order,
  * emission, and a stable radix sort of the entries by tile id.  Then fills bins->raster
- * from the projected records (every field of `proj` is read): an entry joins the list of
- * an 8x8 quadrant of its tile if its alpha >= p->alpha_min ellipse can reach one of the
- * quadrant's pixel centres.  p must be the parameters given to gs_project.
+ * from the projected records (proj->depth, radii and rec are read; u, v, rx, ry as stored in
+ * rec): an entry joins the list of an 8x8 quadrant of its tile if its alpha >= p->alpha_min
+ * ellipse can reach one of the quadrant's pixel centres.  p must be the parameters given
+ * to gs_project.
  * Reads the total K back to the host (synchronises `stream`) and stores it in
  * *n_isect_out (host).  The quadrant records take up to 2 * capacity slots, so a capacity
  * below max(K, ceil(Q / 2)) (Q = the number of (entry, quadrant) pairs) returns

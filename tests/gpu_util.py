@@ -26,6 +26,47 @@ def oracle_params(rp: B.RasterParams) -> oracle.Params:
                          depth_lo=float(np.float32(rp.depth_lo)), depth_hi=float(np.float32(rp.depth_hi)))
 
 
+def synthetic_projection(m2, r, d):
+    """Projected records for the binning stage alone: means, radii, depth keys, and the
+    raster records' u, v and box half-extents (conic zero: every quadrant test passes)."""
+    n = d.numel()
+    proj = PL.Projection(max(n, 1), DEV)
+    if n:
+        proj.means2d[:n].copy_(m2.to(DEV))
+        proj.radii[:n].copy_(r.to(DEV))
+        proj.depth[:n].copy_(d.to(DEV))
+        proj.rec[:n, 0:2].copy_(m2.to(DEV))
+        proj.rec[:n, 10:12].copy_(r.to(DEV).view(torch.float32))
+    return proj
+
+
+def oracle_projection(P, n):
+    """The oracle's float32 projected records in the GPU layout (the raster record formed
+    as the projection forms it: conic scaled for exp2, log2 of the float32 opacity)."""
+    l2e = 1.4426950408889634
+    rec = np.zeros((n, 12), np.float32)
+    rec[:, 0:2] = P.rec[:, 0:2]
+    rec[:, 2] = -0.5 * l2e * P.rec[:, 2]
+    rec[:, 3] = -l2e * P.rec[:, 3]
+    rec[:, 4] = -0.5 * l2e * P.rec[:, 4]
+    with np.errstate(divide="ignore"):
+        rec[:, 5] = np.log2(P.rec[:, 5].astype(np.float32).astype(np.float64))
+    rec[:, 6:9] = P.rec[:, 6:9]
+    rec[:, 9] = np.arange(n, dtype=np.uint32).view(np.float32)
+    rec[:, 10:12] = np.ascontiguousarray(P.radii, np.int32).view(np.float32)
+    proj = PL.Projection(n, DEV)
+    proj.means2d.copy_(torch.from_numpy(P.rec[:, :2].astype(np.float32)))
+    proj.radii.copy_(torch.from_numpy(np.ascontiguousarray(P.radii, np.int32)))
+    proj.depth.copy_(torch.from_numpy(P.dkey))
+    co = np.zeros((n, 4), np.float32)
+    co[:, :3] = P.rec[:, 2:5]
+    co[:, 3] = P.rec[:, 5]
+    proj.conic_opacity.copy_(torch.from_numpy(co))
+    proj.color.copy_(torch.from_numpy(P.rec[:, 6:9].astype(np.float32)))
+    proj.rec.copy_(torch.from_numpy(rec))
+    return proj
+
+
 def gpu_forward(scene, cam, rp=None, capacity=0):
     """Project, bin and render one view on the GPU.  Returns the TrainStep holding the buffers."""
     params = PL.GaussianParams.from_scene(scene, DEV)

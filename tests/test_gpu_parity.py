@@ -17,7 +17,8 @@ import oracle
 from differentiable_rasterization_amd import binding as B
 from differentiable_rasterization_amd import pipeline as PL
 from differentiable_rasterization_amd import scenes
-from tests.gpu_util import DEV, compare_images, gpu_forward, log, oracle_params, rel_l2, ulp_diff
+from tests.gpu_util import (DEV, compare_images, gpu_forward, log, oracle_params, rel_l2, synthetic_projection,
+                            ulp_diff)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,11 +94,7 @@ def test_project_culls_nonfinite_and_window():
 def _bin_gpu(m2, r, d, W, H, capacity=None):
     n = d.numel()
     cam = B.make_camera([1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1], 1.0, 1.0, 0.0, 0.0, W, H)
-    proj = PL.Projection(max(n, 1), DEV)
-    if n:
-        proj.means2d[:n].copy_(m2.to(DEV))
-        proj.radii[:n].copy_(r.to(DEV))
-        proj.depth[:n].copy_(d.to(DEV))
+    proj = synthetic_projection(m2, r, d)
     bins = PL.Binning(n, W, H, capacity=capacity or 0, device=DEV, with_keys=True, with_touched=True)
     k = bins.sort(proj, cam, B.make_params(0))
     torch.cuda.synchronize()
@@ -130,12 +127,13 @@ def test_bin_sort_all_culled_and_capacity():
     # capacity error reports the required size and leaves the caller to grow
     tt, keys, ids, ranges = oracle.bin_f32(m2, r, d, 200, 150)
     cam = B.make_camera([1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1, 0, 0, 0, 0, 1], 1.0, 1.0, 0.0, 0.0, 200, 150)
-    proj = PL.Projection(4000, DEV)
-    proj.means2d.copy_(m2.to(DEV)); proj.radii.copy_(r.to(DEV)); proj.depth.copy_(d.to(DEV))
+    proj = synthetic_projection(m2, r, d)
     small = PL.Binning(4000, 200, 150, capacity=10, device=DEV)
     with pytest.raises(B.GsCapacityError) as ei:
         B.gs_bin_sort(proj.abi(), 4000, cam, B.make_params(0), small.abi(), small.workspace)
-    assert ei.value.required == len(ids)
+    # the required capacity is max(K, ceil(Q / 2)); with a zero conic every entry reaches all
+    # four quadrants of its tile, so Q = 4 K
+    assert ei.value.required == 2 * len(ids)
 
 
 def test_bin_sort_async_matches_sync_and_reports_overflow():

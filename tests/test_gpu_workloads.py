@@ -24,7 +24,7 @@ import oracle
 from differentiable_rasterization_amd import binding as B
 from differentiable_rasterization_amd import pipeline as PL
 from differentiable_rasterization_amd import scenes
-from tests.gpu_util import DEV, compare_images, log, oracle_params, rel_l2
+from tests.gpu_util import DEV, compare_images, log, oracle_params, oracle_projection, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -34,23 +34,10 @@ def _band(width, y0, rows):
                      np.repeat(np.arange(y0, y0 + rows, dtype=np.int32), width)], axis=1).copy()
 
 
-def _upload_projected(P, n):
-    """The oracle's float32 projected records as the input of the GPU binning."""
-    proj = PL.Projection(n, DEV)
-    proj.means2d.copy_(torch.from_numpy(P.rec[:, :2].astype(np.float32)))
-    proj.radii.copy_(torch.from_numpy(P.radii))
-    proj.depth.copy_(torch.from_numpy(P.dkey))
-    co = np.zeros((n, 4), np.float32)
-    co[:, :3] = P.rec[:, 2:5]
-    co[:, 3] = P.rec[:, 5]
-    proj.conic_opacity.copy_(torch.from_numpy(co))
-    return proj
-
-
 def _check_binning(P, cam, n, rp):
     tt, keys, ids, ranges = oracle.bin_f32(P.rec[:, :2].astype(np.float32), P.radii, P.dkey, cam.width,
                                            cam.height)
-    proj = _upload_projected(P, n)
+    proj = oracle_projection(P, n)
     bins = PL.Binning(n, cam.width, cam.height, capacity=len(ids), device=DEV, with_keys=True,
                       with_touched=True)
     k = bins.sort(proj, B.camera_from(cam), rp)
