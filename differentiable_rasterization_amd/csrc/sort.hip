@@ -1,23 +1,27 @@
 // Device-wide exclusive scan and stable LSD radix sort for gfx950.
 //
 // Radix pass (8-bit digit, reduce-then-scan, stable):
-//   hist    : each 256-thread block counts the digits of its 4096-element tile
+//   hist    : each 256-thread block counts the digits of its 2048-element tile
 //             (per-wave LDS histograms) and writes them digit-major, so that one
 //             exclusive scan over [digit][block] gives every (digit, block) its
 //             global output offset;
-//   scatter : each wave ranks its 1024 consecutive elements round by round with a
+//   scan    : the single-launch look-back scan below;
+//   scatter : each wave ranks its 512 consecutive elements round by round with a
 //             64-lane digit match (8 ballots), giving a stable rank per digit; the
 //             block then places its tile in LDS in sorted order and writes it out in
 //             runs of equal digits (coalesced).
-// No look-back between blocks, so no forward-progress assumption is needed.
 #include "kernels.h"
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kItems = 16;
-constexpr int kTile = kThreads * kItems;      // 4096 elements per block
-constexpr int kWaveSpan = 64 * kItems;        // 1024 consecutive elements per wave
+constexpr int kTile = kThreads * kItems;      // 4096 elements per scan block
+// radix blocks take 2048 elements, so that a million keys make ~500 blocks and each CU
+// holds two or more of them: the ranking loop is latency-bound
+constexpr int kRxItems = 8;
+constexpr int kRxTile = kThreads * kRxItems;
+constexpr int kRxWaveSpan = 64 * kRxItems;
 
 // Exclusive scan of one value per thread across a 256-thread block.  `scratch`
 // holds 4 words.  Returns the exclusive prefix; *block_total receives the sum.
@@ -138,9 +142,9 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&h[0][0])[i] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)w * kWaveSpan + lane;
+    const int64_t base = (int64_t)blockIdx.x * kRxTile + (int64_t)w * kRxWaveSpan + lane;
 #pragma unroll 4
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < kRxItems; ++r) {
         const int64_t e = base + r * 64;
         if (e < m) atomicAdd(&h[w][(keys[e] >> shift) & 255u], 1u);
     }
@@ -160,17 +164,17 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
     __shared__ uint32_t bstart[256];
     __shared__ uint32_t gbase[256];
     __shared__ uint32_t scratch[4];
-    __shared__ uint32_t skey[kTile];
-    __shared__ uint32_t sval[kTile];
+    __shared__ uint32_t skey[kRxTile];
+    __shared__ uint32_t sval[kRxTile];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
-    const int64_t tile0 = (int64_t)blockIdx.x * kTile;
-    const int64_t base = tile0 + (int64_t)w * kWaveSpan + lane;
+    const int64_t tile0 = (int64_t)blockIdx.x * kRxTile;
+    const int64_t base = tile0 + (int64_t)w * kRxWaveSpan + lane;
     const uint64_t below_mask = (1ull << lane) - 1ull;
-    uint32_t key[kItems], val[kItems], rank[kItems];
+    uint32_t key[kRxItems], val[kRxItems], rank[kRxItems];
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < kRxItems; ++r) {
         const int64_t e = base + r * 64;
         const bool valid = e < m;
         const uint32_t k = valid ? kin[e] : 0u;
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kItems; ++r) {
+    for (int r = 0; r < kRxItems; ++r) {
         const int64_t e = base + r * 64;
         if (e < m) {
             const uint32_t d = (key[r] >> shift) & 255u;
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
         }
     }
     __syncthreads();
-    const int cnt = (int)min((int64_t)kTile, m - tile0);
+    const int cnt = (int)min((int64_t)kRxTile, m - tile0);
     for (int i = threadIdx.x; i < cnt; i += kThreads) {
         const uint32_t k = skey[i];
         const uint32_t d = (k >> shift) & 255u;
@@ -373,7 +377,7 @@ gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint3
     return GS_OK;
 }
 
-int64_t radix_hist_len(int64_t m) { return 256 * ceil_div(m > 0 ? m : 1, kTile); }
+int64_t radix_hist_len(int64_t m) { return 256 * ceil_div(m > 0 ? m : 1, kRxTile); }
 
 int64_t lb_scan_tiles(int64_t m) { return ceil_div(m > 0 ? m : 1, kTile); }
 
@@ -397,7 +401,7 @@ gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb,
 {
     *in_b = false;
     if (m <= 1 || bits <= 0) return GS_OK;
-    const int64_t nb = ceil_div(m, kTile);
+    const int64_t nb = ceil_div(m, kRxTile);
     const int passes = (bits + 7) / 8;
     uint32_t *sk = ka, *sv = va, *dk = kb, *dv = vb;
     for (int p = 0; p < passes; ++p) {
