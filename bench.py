@@ -180,7 +180,7 @@ def main():
         B.gs_raster_bwd_partials(g, st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.dL_dcolor, None)
         rec(5)
         if args.unfused:
-            B.gs_grad_aggregate(g, st.bins.abi(), c, st.raster, st.grads2d, None)
+            B.gs_grad_aggregate(g, st.proj.abi(), st.bins.abi(), c, st.raster, st.grads2d, None)
             rec(6)
             st.backward_project(c)
             rec(7)

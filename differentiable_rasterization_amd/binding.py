@@ -100,8 +100,10 @@ _SIGS = {
                              _vp, _vp, _vp, _P(ParamGrads), _vp]),
     "gs_raster_bwd_partials": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp,
                                       _vp, _vp]),
-    "gs_grad_aggregate": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
-    "gs_grad_aggregate_adam": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads),
+    "gs_grad_aggregate": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp,
+                                 _P(ParamGrads), _vp]),
+    "gs_grad_aggregate_adam": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp,
+                                      _P(ParamGrads),
                                       _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32, _f32, _vp]),
     "gs_project_bwd": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
     "gs_adam_step": (_i32, [_P(AdamGroup), _i32, _i32, _f32, _f32, _f32, _vp]),
@@ -240,16 +242,17 @@ def gs_raster_bwd_partials(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, 
                                        _stream(stream)))
 
 
-def gs_grad_aggregate(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, grads2d, grads3d: ParamGrads | None,
-                      stream=None):
-    _check(_lib.gs_grad_aggregate(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
+def gs_grad_aggregate(g: Gaussians, proj: Projected, b: Bins, cam: Camera, p: RasterParams, grads2d,
+                      grads3d: ParamGrads | None, stream=None):
+    _check(_lib.gs_grad_aggregate(ctypes.byref(g), ctypes.byref(proj), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
                                   _ptr(grads2d), ctypes.byref(grads3d) if grads3d is not None else None,
                                   _stream(stream)))
 
 
-def gs_grad_aggregate_adam(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, grads2d, m: ParamGrads, v: ParamGrads,
-                           lr: "AdamLrs", step, beta1, beta2, eps, stream=None):
-    _check(_lib.gs_grad_aggregate_adam(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
+def gs_grad_aggregate_adam(g: Gaussians, proj: Projected, b: Bins, cam: Camera, p: RasterParams, grads2d,
+                           m: ParamGrads, v: ParamGrads, lr: "AdamLrs", step, beta1, beta2, eps, stream=None):
+    _check(_lib.gs_grad_aggregate_adam(ctypes.byref(g), ctypes.byref(proj), ctypes.byref(b), ctypes.byref(cam),
+                                       ctypes.byref(p),
                                        _ptr(grads2d), ctypes.byref(m), ctypes.byref(v), ctypes.byref(lr), step, beta1,
                                        beta2, eps, _stream(stream)))
 

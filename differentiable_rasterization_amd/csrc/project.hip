@@ -513,12 +513,13 @@ __global__ __launch_bounds__(256) void k_grad_adam(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
     const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
-    const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad, float *__restrict__ grads2d, AdamSink out)
+    const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad, const float4 *__restrict__ rec,
+    float *__restrict__ grads2d, AdamSink out)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     float g[9];
-    gsr::sum_slots(hdr, drank, qoff, qgrad, i, g);
+    gsr::sum_slots(hdr, drank, qoff, qgrad, rec, i, g);
     if (grads2d) {
 #pragma unroll
         for (int f = 0; f < 9; ++f) grads2d[(int64_t)f * n + i] = g[f];
@@ -619,7 +620,8 @@ namespace gsi {
 gs_status check_raster_inputs(const gs_bins *bins, const gs_camera *cam);
 }
 
-extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                                            const gs_camera *cam,
                                             const gs_raster_params *p, float *grads2d, const gs_param_grads *m,
                                             const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1,
                                             float beta2, float eps, hipStream_t stream)
@@ -631,6 +633,8 @@ extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_bins
     if ((s = check_params(p)) != GS_OK) return s;
     if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
     if (!m || !v || !lr) return fail(GS_ERR_INVALID_ARGUMENT, "m / v / lr is NULL");
+    if (g->n > 0 && (!proj || !proj->rec || !aligned(proj->rec, 16)))
+        return fail(GS_ERR_INVALID_ARGUMENT, "proj->rec is NULL or not 16-byte aligned");
     if (step < 1) return fail(GS_ERR_INVALID_ARGUMENT, "step must be >= 1");
     if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f && eps >= 0.0f))
         return fail(GS_ERR_INVALID_ARGUMENT, "bad Adam hyper-parameters");
@@ -666,7 +670,7 @@ extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_bins
 #define GS_GA(D)                                                                                                   \
     k_grad_adam<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, cd, \
                                                p->alpha_min, p->depth_lo, p->depth_hi, hdr, drank, qoff, qg,      \
-                                               grads2d, sink)
+                                               reinterpret_cast<const float4 *>(proj->rec), grads2d, sink)
     switch (p->sh_degree) {
     case 0: GS_GA(0); break;
     case 1: GS_GA(1); break;

@@ -14,15 +14,16 @@
 // lists), which the back-to-front recovery T_i = T_{i+1} / (1 - alpha_i) cannot.
 // Aggregation over pixels (Eq. 4), without atomics: each lane forms the per-pixel moments
 //   S0 = dpower, Sx = dx S0, Sy = dy S0, Sxx = dx Sx, Sxy = dy Sx, Syy = dy Sy and the
-//   colour terms T_i alpha_i G for 4 records at a time, the wave sums the 36 values in one
-//   transpose-reduction (v_permlane32_swap, v_permlane16_swap, then a 4-step DPP butterfly
-//   within each 16-lane row, so row e ends with the totals of record e), and lane (e, f)
-//   turns them into field f of record e,
-//   du = A Sx + B Sy, dv = B Sx + C Sy, dA = -Sxx/2, dB = -Sxy, dC = -Syy/2, do = S0 / o,
-//   and stores it in the record's gradient slot (one store instruction for the 36
-//   values).  The binning gives each Gaussian's quadrant records consecutive slots, so a
-//   second kernel sums, for every Gaussian, one contiguous run of slots: the sum of Eq. 4
-//   in a fixed order, so the gradients are deterministic.
+//   colour terms T_i alpha_i G for 4 records at a time; the wave sums the 36 values in one
+//   transposing reduction (reduce_4x9), after which 9 lanes of row e hold the 9 totals of
+//   record e, and stores them in the record's gradient slot (one store instruction for
+//   the 36 values).  The screen-space gradients are linear in these sums with coefficients
+//   of the Gaussian alone,
+//     du = A Sx + B Sy, dv = B Sx + C Sy, dA = -Sxx/2, dB = -Sxy, dC = -Syy/2, do = S0 / o,
+//   so they are formed once per Gaussian, after its slots are summed (sum_slots in
+//   raster.h).  The binning gives each Gaussian's quadrant records consecutive slots: the
+//   sum of Eq. 4 is one contiguous run of slots added in a fixed order, so the gradients
+//   are deterministic.
 //
 // Lanes that do not take an entry run the same instructions with alpha = 0, which leaves
 // T unchanged and contributes zeros (no divergent branches).
@@ -52,28 +53,33 @@ __device__ __forceinline__ float swap_add16(float &x, float &y)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the 16 lanes of each row, result in every lane of the row.
-__device__ __forceinline__ float row_sum16(float v)
+// v[e * 9 + f] holds this lane's value of field f of entry e (e < 4).  Sums every field
+// of every entry over the 64 lanes, transposing as it goes so that each sum lands in one
+// lane: afterwards lane (e, n) of row e = lane >> 4 (n = lane & 15) holds the total of
+// field F(n) = 4 b1 + 2 b2 + b3 of entry e (b_k = bit k of n; lanes n and n ^ 1 hold the
+// same field) and t8 holds the total of field 8 of entry e.
+//   1. v_permlane32_swap + add: rows 0-1 keep entries 0-1, rows 2-3 entries 2-3
+//   2. v_permlane16_swap + add: row e keeps entry e (9 partial sums per lane)
+//   3. within each 16-lane row, fields 0-7 by a transposing butterfly (partners n ^ 8 by
+//      row_ror:8, n ^ 7 by row_half_mirror, n ^ 2 and n ^ 1 by quad_perm): at each step a
+//      lane keeps one field of each pair, chosen by one bit of n, adds the partner's value
+//      of that field, and passes on the other; field 8 by a plain butterfly.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
 {
     using namespace gsd;
-    // old = 0 (the identity of +) lets the compiler fold each move into a DPP add
-    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kQuadSwap1, 0xF, 0xF, false));
-    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kQuadSwap2, 0xF, 0xF, false));
-    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kRowHalfMirror, 0xF, 0xF, false));
-    v += f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), kRowMirror, 0xF, 0xF, false));
-    return v;
+    // old = 0 (the identity of +) lets the compiler fold the move into the DPP add
+    return f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), CTRL, 0xF, 0xF, false));
 }
 
-// v[e * 9 + f] holds this lane's value of field f of entry e (e < 4).  Afterwards v[f]
-// (f < 9) holds, in every lane of row e, the sum over all 64 lanes of field f of entry e.
-__device__ __forceinline__ void reduce_4x9(float (&v)[kBwdBatch * kFields])
+constexpr int kRowRor8 = 0x128;
+
+// One transposing step: keep x if !bit else y, and add the partner's copy of the same field.
+template <int CTRL>
+__device__ __forceinline__ float tstep(float x, float y, bool bit)
 {
-#pragma unroll
-    for (int i = 0; i < 18; ++i) v[i] = swap_add32(v[i], v[i + 18]);   // lanes < 32: slot i, else slot i + 18
-#pragma unroll
-    for (int i = 0; i < 9; ++i) v[i] = swap_add16(v[i], v[i + 9]);     // row r: slot i + 9 r
-#pragma unroll
-    for (int i = 0; i < 9; ++i) v[i] = row_sum16(v[i]);
+    const float keep = bit ? y : x, send = bit ? x : y;
+    return keep + dpp_f<CTRL>(send);
 }
 
 // Per-lane choice of one of four wave-uniform values by the lane's row (lane >> 4).
@@ -81,6 +87,29 @@ __device__ __forceinline__ float by_row(int row, float a0, float a1, float a2, f
 {
     const float lo = (row & 1) ? a1 : a0, hi = (row & 1) ? a3 : a2;
     return (row & 2) ? hi : lo;
+}
+
+__device__ __forceinline__ void reduce_4x9(float (&v)[kBwdBatch * kFields], int n, float &fz, float &t8)
+{
+    using namespace gsd;
+#pragma unroll
+    for (int i = 0; i < 18; ++i) v[i] = swap_add32(v[i], v[i + 18]);   // lanes < 32: slot i, else slot i + 18
+#pragma unroll
+    for (int i = 0; i < 9; ++i) v[i] = swap_add16(v[i], v[i + 9]);     // row r: slot i + 9 r
+    const bool b3 = (n >> 3) & 1, b2 = (n >> 2) & 1, b1 = (n >> 1) & 1;
+    float w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = tstep<kRowRor8>(v[2 * k], v[2 * k + 1], b3);   // field 2k + b3
+    const float x0 = tstep<kRowHalfMirror>(w[0], w[1], b2);                            // field 2 b2 + b3
+    const float x1 = tstep<kRowHalfMirror>(w[2], w[3], b2);                            // 4 + 2 b2 + b3
+    const float y = tstep<kQuadSwap2>(x0, x1, b1);                                     // 4 b1 + 2 b2 + b3
+    fz = y + dpp_f<kQuadSwap1>(y);
+    float z = v[8];
+    z += dpp_f<kQuadSwap1>(z);
+    z += dpp_f<kQuadSwap2>(z);
+    z += dpp_f<kRowHalfMirror>(z);
+    z += dpp_f<kRowRor8>(z);
+    t8 = z;
 }
 
 template <bool HAS_GT>
@@ -128,7 +157,11 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         z[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         z[2] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    const int row = lane >> 4, field = lane & 15;
+    const int row = lane >> 4, nl = lane & 15;
+    // the reduced field each lane of a row holds (reduce_4x9): even lanes hold fields 0-7,
+    // lane 1 field 8
+    const int my_field = nl == 1 ? 8 : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
+    const bool lane_writes = (nl & 1) == 0 || nl == 1;
     float Tr = 1.0f;
     // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
     uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
@@ -186,31 +219,19 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
             Tr = Tr * om;
             any |= take;
         }
-        // gradient slot of the batch's record e = row (record jt + e), field f = lane & 15
+        // gradient slot of the batch's record e = row (record jt + e); lane n writes field
+        // my_field (see reduce_4x9)
         const uint32_t my_slot = __float_as_uint(by_row(row, slot[0], slot[1], slot[2], slot[3]));
-        float *dst = qgrad + (size_t)my_slot * kGradSlot + field;
-        const bool writer = (uint32_t)row < cnt && field < kFields;
+        float *dst = qgrad + (size_t)my_slot * kGradSlot + my_field;
+        const bool writer = (uint32_t)row < cnt && lane_writes;
         jt += cnt;
         if (__ballot(any) == 0) {
             if (writer) *dst = 0.0f;
             continue;
         }
-        reduce_4x9(v);
-        const float a = by_row(row, p0[0].z, p0[1].z, p0[2].z, p0[3].z);
-        const float b = by_row(row, p0[0].w, p0[1].w, p0[2].w, p0[3].w);
-        const float c = by_row(row, p1[0].x, p1[1].x, p1[2].x, p1[3].x);
-        const float l = by_row(row, p1[0].y, p1[1].y, p1[2].y, p1[3].y);
-        const float A = -2.0f * kLn2 * a, B = -kLn2 * b, C = -2.0f * kLn2 * c;
-        float val = fmaf(A, v[1], B * v[2]);                        // du
-        val = field == 1 ? fmaf(B, v[1], C * v[2]) : val;           // dv
-        val = field == 2 ? -0.5f * v[3] : val;                      // dA
-        val = field == 3 ? -v[4] : val;                             // dB
-        val = field == 4 ? -0.5f * v[5] : val;                      // dC
-        val = field == 5 ? v[0] * exp2_fast(-l) : val;              // do
-        val = field == 6 ? v[6] : val;                              // red
-        val = field == 7 ? v[7] : val;                              // green
-        val = field == 8 ? v[8] : val;                              // blue
-        if (writer) *dst = val;
+        float fz, t8;
+        reduce_4x9(v, nl, fz, t8);
+        if (writer) *dst = nl == 1 ? t8 : fz;
     }
     sink ^= pend;
     asm volatile("" ::"v"(sink));
@@ -223,12 +244,13 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
 // so that the stores coalesce.
 __global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
                                                      const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
-                                                     int64_t n, float *__restrict__ grads2d)
+                                                     const float4 *__restrict__ rec, int64_t n,
+                                                     float *__restrict__ grads2d)
 {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     float acc[kFields];
-    sum_slots(hdr, drank, qoff, qgrad, g, acc);
+    sum_slots(hdr, drank, qoff, qgrad, rec, g, acc);
 #pragma unroll
     for (int f = 0; f < kFields; ++f) grads2d[(size_t)f * n + g] = acc[f];
 }
@@ -275,9 +297,9 @@ extern "C" gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins
     return GS_OK;
 }
 
-extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
-                                       const gs_raster_params *p, float *grads2d, gs_param_grads *grads3d,
-                                       hipStream_t stream)
+extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                                       const gs_camera *cam, const gs_raster_params *p, float *grads2d,
+                                       gs_param_grads *grads3d, hipStream_t stream)
 {
     using namespace gsi;
     gs_status s;
@@ -286,6 +308,8 @@ extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bin
     if ((s = check_params(p)) != GS_OK) return s;
     if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
     if (g->n > 0 && !grads2d) return fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
+    if (g->n > 0 && (!proj || !proj->rec || !aligned(proj->rec, 16)))
+        return fail(GS_ERR_INVALID_ARGUMENT, "proj->rec is NULL or not 16-byte aligned");
     const int64_t n = g->n;
     if (n > 0) {
         const int T = tiles_x(cam->width) * tiles_y(cam->height);
@@ -294,7 +318,7 @@ extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bin
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
             reinterpret_cast<const BinsHeader *>(rb + L.hdr), reinterpret_cast<const uint32_t *>(rb + L.drank),
             reinterpret_cast<const uint32_t *>(rb + L.qoff),
-            reinterpret_cast<const float4 *>(rb + L.qgrad), n, grads2d);
+            reinterpret_cast<const float4 *>(rb + L.qgrad), reinterpret_cast<const float4 *>(proj->rec), n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }
     if (grads3d) return launch_project_bwd(g, cam, p, grads2d, grads3d, stream);
@@ -306,9 +330,8 @@ extern "C" gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *pr
                                    const float *t_final, const int32_t *n_trav, const float *dL_dcolor,
                                    const float *dL_dt, float *grads2d, gs_param_grads *grads3d, hipStream_t stream)
 {
-    (void)proj;   // the lists carry raster-ready copies of the projected records
     if (g && g->n > 0 && !grads2d) return gsi::fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
     const gs_status s = gs_raster_bwd_partials(g, bins, cam, p, color, t_final, n_trav, dL_dcolor, dL_dt, stream);
     if (s != GS_OK) return s;
-    return gs_grad_aggregate(g, bins, cam, p, grads2d, grads3d, stream);
+    return gs_grad_aggregate(g, proj, bins, cam, p, grads2d, grads3d, stream);
 }

@@ -194,7 +194,7 @@ class TrainStep:
         backward_partials); the 3D gradients are not stored."""
         self.params.step_count += 1
         m, v = self.params.moments()
-        B.gs_grad_aggregate_adam(self.params.gaussians(), self.bins.abi(), cam, self.raster, grads2d, m, v,
+        B.gs_grad_aggregate_adam(self.params.gaussians(), self.proj.abi(), self.bins.abi(), cam, self.raster, grads2d, m, v,
                                  B.AdamLrs(**self.lr), self.params.step_count, 0.9, 0.999, 1e-15, stream)
 
     def backward_partials(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):

@@ -243,17 +243,19 @@ gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const g
  * gs_raster_bwd is gs_raster_bwd_partials followed by gs_grad_aggregate on the same
  * stream.  gs_raster_bwd_partials: ByteSplat Eq. 3 per pixel and the per-quadrant part of
  * the Eq. 4 sum, written to per-record slots inside bins->raster (nothing outside it is
- * written; same arguments and checks as gs_raster_bwd).  gs_grad_aggregate: the
- * per-Gaussian part of the Eq. 4 sum over those slots into grads2d [9][n] (every entry
- * written), then, if grads3d is non-NULL, the projection backward as in gs_raster_bwd.
- * Between the two calls the bins must not be re-sorted. */
+ * written; same arguments and checks as gs_raster_bwd).  The slots hold per-record sums of
+ * pixel moments.  gs_grad_aggregate: the per-Gaussian part of the Eq. 4 sum over those slots,
+ * turned into the screen-space gradients with the Gaussian's conic and opacity from
+ * proj->rec, into grads2d [9][n] (every entry written), then, if grads3d is non-NULL, the
+ * projection backward as in gs_raster_bwd.  Between the two calls the bins must not be
+ * re-sorted; proj is the gs_project output the bins were sorted from. */
 gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
                                  const gs_raster_params *p, const float *color, const float *t_final,
                                  const int32_t *n_trav, const float *dL_dcolor, const float *dL_dt,
                                  hipStream_t stream);
-gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
-                            const gs_raster_params *p, float *grads2d, gs_param_grads *grads3d,
-                            hipStream_t stream);
+gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                            const gs_camera *cam, const gs_raster_params *p, float *grads2d,
+                            gs_param_grads *grads3d, hipStream_t stream);
 
 /* Learning rates of the fused step below, per parameter group (the SH coefficients split
  * into the DC term, planes 0..2, and the rest). */
@@ -271,8 +273,9 @@ typedef struct {
  * then updated in place (the arrays must be writable device memory).  m, v: the Adam
  * moments, same shapes as the parameters, updated in place.  grads2d [9][n] (may be NULL):
  * receives the screen-space gradients.  bins, cam, p: as for gs_grad_aggregate. */
-gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
-                                 const gs_raster_params *p, float *grads2d, const gs_param_grads *m,
+gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                                 const gs_camera *cam, const gs_raster_params *p, float *grads2d,
+                                 const gs_param_grads *m,
                                  const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1,
                                  float beta2, float eps, hipStream_t stream);
 

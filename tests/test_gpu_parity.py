@@ -303,7 +303,7 @@ def test_backward_split_matches_whole():
     f = st.frame
     g = st.params.gaussians()
     B.gs_raster_bwd_partials(g, st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, G, GT)
-    B.gs_grad_aggregate(g, st.bins.abi(), c, st.raster, st.grads2d, st.params.param_grads())
+    B.gs_grad_aggregate(g, st.proj.abi(), st.bins.abi(), c, st.raster, st.grads2d, st.params.param_grads())
     torch.cuda.synchronize()
     assert torch.equal(st.grads2d, whole2) and torch.equal(st.params.grad, whole3)
 
