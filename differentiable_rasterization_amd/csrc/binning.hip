@@ -345,8 +345,12 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     gsr::BinsHeader *hdr = reinterpret_cast<gsr::BinsHeader *>(rb + RL.hdr);
     int32_t *order = reinterpret_cast<int32_t *>(rb + RL.order);
     uint32_t *drank = reinterpret_cast<uint32_t *>(rb + RL.drank), *qoff = reinterpret_cast<uint32_t *>(rb + RL.qoff);
+    // the quadrant prefix counts of empty lists: zero
+    uint32_t *wpre0 = reinterpret_cast<uint32_t *>(rb + RL.wpre);
+    const int64_t nw0 = gsr::kQuads * (RL.words + 1);
     if (n == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
+        if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre0), nw0, 0, stream)) != GS_OK) return s;
         k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
         GS_LAUNCH_CHECK("k_tile_order");
         k_bins_empty<<<1, 1, 0, stream>>>(hdr, counts);
@@ -405,6 +409,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     GS_LAUNCH_CHECK("k_emit");
     if (cap == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
+        if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre0), nw0, 0, stream)) != GS_OK) return s;
         k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
         GS_LAUNCH_CHECK("k_tile_order");
         return GS_OK;

@@ -54,9 +54,9 @@ struct Rec {
 constexpr int kRecF4 = 3;   // float4 words per record
 constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
 // The record array has kRecPad spare records before and after the lists, so that a batch
-// of consecutive records can always be loaded from one base address (records outside the
-// lists are loaded but never used).
-constexpr int kRecPad = 4;
+// of consecutive records, and the batch after it, can always be loaded from one base
+// address (records outside the lists are loaded but never used).
+constexpr int kRecPad = 8;
 // Quadrant records are stored for up to kQuadFactor * capacity (entry, quadrant) pairs
 // (an entry reaches 1.4 - 2 quadrants on average); more is reported as a capacity error.
 constexpr int kQuadFactor = 2;

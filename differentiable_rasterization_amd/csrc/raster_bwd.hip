@@ -143,6 +143,7 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         if (HAS_GT) Z = fmaf(dL_dt[idx], t_final[idx], Z);
     }
     const int start = ranges[tile], end = ranges[tile + 1];
+    if (start >= end) return;   // empty list: no records, no slots (the prefix counts may be unset)
     // the wave walks up to the furthest entry any of its pixels traversed
     const int nmax = max(0, min(gsd::wave_max_i32(np), end - start));
     const uint64_t *bq = bitmap + (int64_t)q * words;

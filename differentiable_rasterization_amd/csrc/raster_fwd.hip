@@ -16,6 +16,34 @@ using namespace gsr;
 
 constexpr int kFwdBatch = 4;   // records per scalar-load batch
 
+// One batch of records in scalar registers.
+struct Batch {
+    float4 p0[kFwdBatch], p1[kFwdBatch];
+    float blue[kFwdBatch], kent[kFwdBatch];
+    __device__ __forceinline__ void load(const float4 *__restrict__ qrec, uint32_t j)
+    {
+        const float4 *rb = qrec + kRecF4 * (size_t)j;
+#pragma unroll
+        for (int i = 0; i < kFwdBatch; ++i) {
+            p0[i] = rb[kRecF4 * i];
+            p1[i] = rb[kRecF4 * i + 1];
+            const float4 p2 = rb[kRecF4 * i + 2];
+            blue[i] = p2.x;
+            kent[i] = p2.z;
+        }
+    }
+    // Makes the loaded values available here: the compiler waits for the scalar loads at
+    // this point (the "memory" clobber keeps later loads behind it).
+    __device__ __forceinline__ void wait() const
+    {
+#pragma unroll
+        for (int i = 0; i < kFwdBatch; ++i)
+            asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
+                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i])
+                         : "memory");
+    }
+};
+
 __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ ranges, const int32_t *__restrict__ order,
                                                    const float4 *__restrict__ qrec, const uint64_t *__restrict__ bitmap,
                                                    const uint32_t *__restrict__ wpre, int64_t words, int W, int H,
@@ -34,6 +62,17 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
     if (__ballot(inside) == 0) return;
     const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
     const int start = ranges[tile], end = ranges[tile + 1];
+    if (start >= end) {   // empty list: nothing is read (the quadrant prefix counts may be unset)
+        if (inside) {
+            const size_t idx = (size_t)py * W + px;
+            out_c[3 * idx] = 0.0f;
+            out_c[3 * idx + 1] = 0.0f;
+            out_c[3 * idx + 2] = 0.0f;
+            out_t[idx] = 1.0f;
+            out_n[idx] = 0;
+        }
+        return;
+    }
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)end);
@@ -42,45 +81,48 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
     bool live = inside;
     // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
     uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
-    for (uint32_t j = j0; j < j1; j += kFwdBatch) {
-        if (((j - j0) & 63u) == 0u && j > j0) {
-            sink ^= pend;
-            pend = prefetch_records(qrec, j + 64u, j1);
-        }
-        // Scalar loads complete out of order: one wait per batch of records.
-        float4 p0[kFwdBatch], p1[kFwdBatch];
-        float blue[kFwdBatch], kent[kFwdBatch];
-        const float4 *rb = qrec + kRecF4 * (size_t)j;   // records j .. j+3 (past j1: spare, unused)
-#pragma unroll
-        for (int i = 0; i < kFwdBatch; ++i) {
-            p0[i] = rb[kRecF4 * i];
-            p1[i] = rb[kRecF4 * i + 1];
-            const float4 p2 = rb[kRecF4 * i + 2];
-            blue[i] = p2.x;
-            kent[i] = p2.z;
-        }
-#pragma unroll
-        for (int i = 0; i < kFwdBatch; ++i)
-            asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
-                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]));
+    // Records come in batches of kFwdBatch through scalar loads.  Scalar loads complete out
+    // of order, so the only wait is for all of them: the loop waits for batch b, issues the
+    // loads of batch b + 1 and then blends batch b, so that the loads of b + 1 land while b
+    // is blended.  Two register sets, alternating (the loop body is unrolled twice).
+    Batch A, B;
+    if (j0 < j1) A.load(qrec, j0);
+    auto blend = [&](const Batch &R, uint32_t j) {
         // branch-free per entry: lanes that do not take it blend with alpha = 0 (T and C
         // unchanged exactly); termination is a mask update
 #pragma unroll
         for (int i = 0; i < kFwdBatch; ++i) {
             if (j + (uint32_t)i >= j1) break;
-            const float dx = fx - p0[i].x, dy = fy - p0[i].y;
-            const float alpha = fminf(alpha_max, exp2_fast(exponent(p0[i], p1[i], dx, dy)));
+            const float dx = fx - R.p0[i].x, dy = fy - R.p0[i].y;
+            const float alpha = fminf(alpha_max, exp2_fast(exponent(R.p0[i], R.p1[i], dx, dy)));
             const bool take = live && alpha >= alpha_min;
             const float a = take ? alpha : 0.0f;
             const float w = Tr * a;
-            cr = fmaf(w, p1[i].z, cr);
-            cg = fmaf(w, p1[i].w, cg);
-            cb = fmaf(w, blue[i], cb);
+            cr = fmaf(w, R.p1[i].z, cr);
+            cg = fmaf(w, R.p1[i].w, cg);
+            cb = fmaf(w, R.blue[i], cb);
             Tr = Tr * (1.0f - a);
             const bool stop = take && Tr < t_min;
-            np = stop ? (int)__float_as_uint(kent[i]) - start + 1 : np;
+            np = stop ? (int)__float_as_uint(R.kent[i]) - start + 1 : np;
             live = live && !stop;
         }
+    };
+    auto prefetch = [&](uint32_t j) {
+        if (((j - j0) & 63u) == 0u && j > j0) {
+            sink ^= pend;
+            pend = prefetch_records(qrec, j + 64u, j1);
+        }
+    };
+    for (uint32_t j = j0; j < j1; j += 2 * kFwdBatch) {
+        prefetch(j);
+        A.wait();
+        B.load(qrec, j + kFwdBatch);   // past j1: spare records, loaded but unused
+        blend(A, j);
+        if (j + kFwdBatch >= j1 || __ballot(live) == 0) break;
+        prefetch(j + kFwdBatch);
+        B.wait();
+        A.load(qrec, j + 2 * kFwdBatch);
+        blend(B, j + kFwdBatch);
         if (__ballot(live) == 0) break;
     }
     sink ^= pend;
