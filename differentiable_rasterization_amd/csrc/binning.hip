@@ -68,9 +68,9 @@ __device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned lo
 }
 
 // Entries of each Gaussian in depth order, tiles row-major.  Entry p gets the key
-// tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at), the
-// value p (its emit position), gauss[p] = its Gaussian and soff[p] = the gradient slot of
-// its first quadrant record (the Gaussian's slots follow its entries in order).
+// tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at) and the
+// value (gradient slot of its first quadrant record) << 32 | its Gaussian, carried through
+// the tile sort (the Gaussian's slots follow its entries in order).
 __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
                                               const uint32_t *__restrict__ off, const uint32_t *__restrict__ qoff,
                                               const float4 *__restrict__ rec, float log2_amin, int64_t n, int tx,
@@ -78,8 +78,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
                                               const unsigned long long *__restrict__ tot, int64_t cap,
                                               unsigned long long *__restrict__ klen, gsr::BinsHeader *__restrict__ hdr,
                                               int64_t *__restrict__ counts,
-                                              uint32_t *__restrict__ tkeys, uint32_t *__restrict__ tvals,
-                                              uint32_t *__restrict__ gauss, uint32_t *__restrict__ soff)
+                                              uint32_t *__restrict__ tkeys, uint64_t *__restrict__ tvals)
 {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const unsigned long long K = tot[0], Q = tot[1];
@@ -105,9 +104,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
         for (int x = x0; x < x1; ++x) {
             const uint32_t qm = gsr::quad_mask_rec(p0, p1, log2_amin, (float)(x * GS_TILE), (float)(y * GS_TILE));
             tkeys[p] = (uint32_t)(y * tx + x) | (qm << gsr::kMaskShift);
-            tvals[p] = p;
-            gauss[p] = g;
-            soff[p] = sl;
+            tvals[p] = ((uint64_t)sl << 32) | g;
             sl += (uint32_t)__popc(qm);
             ++p;
         }
@@ -120,8 +117,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
 // [4][words + 1] is written (zero past the entries); the exclusive scan of wcnt gives the
 // positions of the quadrant records.  The launch covers max(capacity, T + 1) threads (all
 // `words` words); K is read on the device.
-__global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
-                                                const uint32_t *__restrict__ gauss,
+__global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tkeys, const uint64_t *__restrict__ tvals,
                                                 const unsigned long long *__restrict__ klen, int32_t T,
                                                 uint32_t *__restrict__ ids, int32_t *__restrict__ ranges,
                                                 int64_t words, uint64_t *__restrict__ bitmap,
@@ -136,7 +132,7 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
         const uint32_t key = tkeys[k];
         const int32_t t = (int32_t)(key & gsr::kTileMask);
         qm = key >> gsr::kMaskShift;
-        ids[k] = gauss[spos[k]];
+        ids[k] = (uint32_t)tvals[k];
         const int32_t prev = k > 0 ? (int32_t)(tkeys[k - 1] & gsr::kTileMask) : -1;
         for (int32_t u = prev + 1; u <= t; ++u) ranges[u] = (int32_t)k;
         if (k == K - 1)
@@ -157,11 +153,10 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
 // its box reaches, at the position given by the scanned bit counts, and stamps the entry
 // index and the record's gradient slot into it.  The spare records around the lists are
 // read (never used) by the raster kernels' batches: they are zeroed, so they stay finite.
-__global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint32_t *__restrict__ spos,
-                                                    const uint32_t *__restrict__ ids,
+__global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint64_t *__restrict__ tvals,
                                                     const unsigned long long *__restrict__ klen, int64_t words,
                                                     const uint64_t *__restrict__ bitmap,
-                                                    const uint32_t *__restrict__ wpre, const uint32_t *__restrict__ soff,
+                                                    const uint32_t *__restrict__ wpre,
                                                     const float4 *__restrict__ prec, float4 *__restrict__ qrec)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -175,11 +170,12 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
     if (k >= (int64_t)*klen) return;
     const uint32_t qm = tkeys[k] >> gsr::kMaskShift;
     if (!qm) return;
-    const uint32_t g = ids[k];
+    const uint64_t tvk = tvals[k];
+    const uint32_t g = (uint32_t)tvk;
     const float4 a = prec[gsr::kRecF4 * (size_t)g], b = prec[gsr::kRecF4 * (size_t)g + 1];
     float4 c = prec[gsr::kRecF4 * (size_t)g + 2];
     c.z = __uint_as_float((uint32_t)k);
-    uint32_t slot = soff[spos[k]];
+    uint32_t slot = (uint32_t)(tvk >> 32);
 #pragma unroll
     for (int q = 0; q < gsr::kQuads; ++q) {
         if (!((qm >> q) & 1u)) continue;
@@ -254,7 +250,7 @@ struct Layout {
     // zero region (cleared by k_depth_keys at the start of every sort): tickets and
     // look-back status words of the scans
     size_t zero, tickets, stD, stT, scC, scQ, scW, zero_bytes;
-    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, gauss, soff, hist, bytes;
+    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, hist, bytes;
     int tbits;
 };
 
@@ -286,8 +282,7 @@ Layout layout(int64_t n, int64_t cap, int32_t tiles)
     L.cnt = take(4 * nn); L.qcnt = take(4 * (nn + 1)); L.doff = take(4 * nn);
     L.total = take(16);   // K, then the quadrant records
     L.klen = take(8);     // K if the lists fit, else 0
-    L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(4 * cc); L.tvB = take(4 * cc); L.gauss = take(4 * cc);
-    L.soff = take(4 * cc);
+    L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(8 * cc); L.tvB = take(8 * cc);
     L.hist = take(4 * (size_t)gsi::radix_hist_len(std::max<int64_t>((int64_t)nn, (int64_t)cc)));
     L.bytes = o;
     return L;
@@ -371,8 +366,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     unsigned long long *total = (unsigned long long *)(ws + L.total);
     unsigned long long *klen = (unsigned long long *)(ws + L.klen);
     uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB);
-    uint32_t *tvA = (uint32_t *)(ws + L.tvA), *tvB = (uint32_t *)(ws + L.tvB), *gauss = (uint32_t *)(ws + L.gauss);
-    uint32_t *soff = (uint32_t *)(ws + L.soff);
+    uint64_t *tvA = (uint64_t *)(ws + L.tvA), *tvB = (uint64_t *)(ws + L.tvB);
     uint32_t *hist = (uint32_t *)(ws + L.hist), *tickets = (uint32_t *)(ws + L.tickets);
     unsigned long long *stD = (unsigned long long *)(ws + L.stD), *stT = (unsigned long long *)(ws + L.stT);
     unsigned long long *scC = (unsigned long long *)(ws + L.scC), *scQ = (unsigned long long *)(ws + L.scQ);
@@ -405,7 +399,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     //    of (tile key, emit position) by tile
     const int tbits = L.tbits;
     k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, qoff, prec, log2_amin, n, tx, ty, total, cap, klen, hdr, counts, tkA,
-                                   tvA, gauss, soff);
+                                   tvA);
     GS_LAUNCH_CHECK("k_emit");
     if (cap == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
@@ -414,10 +408,11 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
         GS_LAUNCH_CHECK("k_tile_order");
         return GS_OK;
     }
-    if ((s = radix_sort_u32(tkA, tvA, tkB, tvB, cap, tbits, hist, stT, tickets + kTkTile, &in_b, stream, klen)) !=
+    if ((s = radix_sort_u32_u64(tkA, tvA, tkB, tvB, cap, tbits, hist, stT, tickets + kTkTile, &in_b, stream, klen)) !=
         GS_OK)
         return s;
-    const uint32_t *tk = in_b ? tkB : tkA, *spos = in_b ? tvB : tvA;
+    const uint32_t *tk = in_b ? tkB : tkA;
+    const uint64_t *tv = in_b ? tvB : tvA;
 
     // 4. ids, per-tile ranges, quadrant bitmaps and their scanned bit counts, the quadrant
     //    record lists; optional 64-bit keys
@@ -426,10 +421,10 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     uint32_t *wpre = reinterpret_cast<uint32_t *>(rb + RL.wpre);
     const int64_t nw = gsr::kQuads * (RL.words + 1);
     k_finish<<<(unsigned)ceil_div(std::max<int64_t>(cap, (int64_t)T + 1), 256), 256, 0, stream>>>(
-        tk, spos, gauss, klen, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
+        tk, tv, klen, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
     GS_LAUNCH_CHECK("k_finish");
     if ((s = lb_scan_u32(wpre, wpre, nw, scW, tickets + kTkWpre, nullptr, stream)) != GS_OK) return s;
-    k_quad_lists<<<gk, 256, 0, stream>>>(tk, spos, bins->ids, klen, RL.words, bm, wpre, soff,
+    k_quad_lists<<<gk, 256, 0, stream>>>(tk, tv, klen, RL.words, bm, wpre,
                                          prec, reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4);
     GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {

@@ -36,6 +36,10 @@ int64_t radix_scan_status_len(int64_t m, int bits);
 gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
                          uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
                          hipStream_t stream, const unsigned long long *m_dev = nullptr);
+// The same with 64-bit values.
+gs_status radix_sort_u32_u64(uint32_t *ka, uint64_t *va, uint32_t *kb, uint64_t *vb, int64_t m, int bits,
+                             uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
+                             hipStream_t stream, const unsigned long long *m_dev = nullptr);
 
 // Fills n int32 values with `value` (a kernel, not a memset, so it may be captured in graphs).
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream);

@@ -153,9 +153,9 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
     hist[(int64_t)d * nb + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
 }
 
-__global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__restrict__ kin,
-                                                            const uint32_t *__restrict__ vin,
-                                                            uint32_t *__restrict__ kout, uint32_t *__restrict__ vout,
+template <typename V>
+__global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__restrict__ kin, const V *__restrict__ vin,
+                                                            uint32_t *__restrict__ kout, V *__restrict__ vout,
                                                             int64_t m_max, const unsigned long long *__restrict__ m_dev,
                                                             int shift, const uint32_t *__restrict__ offs, int64_t nb)
 {
@@ -165,20 +165,21 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
     __shared__ uint32_t gbase[256];
     __shared__ uint32_t scratch[4];
     __shared__ uint32_t skey[kRxTile];
-    __shared__ uint32_t sval[kRxTile];
+    __shared__ V sval[kRxTile];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     const int64_t tile0 = (int64_t)blockIdx.x * kRxTile;
     const int64_t base = tile0 + (int64_t)w * kRxWaveSpan + lane;
     const uint64_t below_mask = (1ull << lane) - 1ull;
-    uint32_t key[kRxItems], val[kRxItems], rank[kRxItems];
+    uint32_t key[kRxItems], rank[kRxItems];
+    V val[kRxItems];
 #pragma unroll
     for (int r = 0; r < kRxItems; ++r) {
         const int64_t e = base + r * 64;
         const bool valid = e < m;
         const uint32_t k = valid ? kin[e] : 0u;
-        const uint32_t v = valid ? vin[e] : 0u;
+        const V v = valid ? vin[e] : V(0);
         const uint32_t d = (k >> shift) & 255u;
         uint64_t same = __ballot(valid);
 #pragma unroll
@@ -395,15 +396,17 @@ int64_t radix_scan_status_len(int64_t m, int bits)
     return (int64_t)((bits + 7) / 8) * lb_scan_tiles(radix_hist_len(m));
 }
 
-gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
-                         uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
-                         hipStream_t stream, const unsigned long long *m_dev)
+template <typename V>
+gs_status radix_sort_kv(uint32_t *ka, V *va, uint32_t *kb, V *vb, int64_t m, int bits, uint32_t *hist,
+                        unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b, hipStream_t stream,
+                        const unsigned long long *m_dev)
 {
     *in_b = false;
     if (m <= 1 || bits <= 0) return GS_OK;
     const int64_t nb = ceil_div(m, kRxTile);
     const int passes = (bits + 7) / 8;
-    uint32_t *sk = ka, *sv = va, *dk = kb, *dv = vb;
+    uint32_t *sk = ka, *dk = kb;
+    V *sv = va, *dv = vb;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
         k_radix_hist<<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb);
@@ -411,13 +414,27 @@ gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb,
         gs_status s = lb_scan_u32(hist, hist, 256 * nb, scan_status + p * lb_scan_tiles(256 * nb), scan_tickets + p,
                                   nullptr, stream);
         if (s != GS_OK) return s;
-        k_radix_scatter<<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb);
+        k_radix_scatter<V><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb);
         GS_LAUNCH_CHECK("k_radix_scatter");
-        uint32_t *tk = sk, *tv = sv;
-        sk = dk; sv = dv; dk = tk; dv = tv;
+        std::swap(sk, dk);
+        std::swap(sv, dv);
         *in_b = !*in_b;
     }
     return GS_OK;
+}
+
+gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
+                         uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
+                         hipStream_t stream, const unsigned long long *m_dev)
+{
+    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev);
+}
+
+gs_status radix_sort_u32_u64(uint32_t *ka, uint64_t *va, uint32_t *kb, uint64_t *vb, int64_t m, int bits,
+                             uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
+                             hipStream_t stream, const unsigned long long *m_dev)
+{
+    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev);
 }
 
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream)

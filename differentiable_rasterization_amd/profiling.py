@@ -32,6 +32,7 @@ KERNEL_SOURCES = {
     "k_raster_bwd": ["raster_bwd.hip", "raster.h", "kernels.h", "common.h"],
     "k_raster_fwd": ["raster_fwd.hip", "raster.h", "common.h"],
     "k_adam": ["optim.hip", "kernels.h", "common.h"],
+    "k_grad_adam": ["project.hip", "raster.h", "kernels.h", "common.h"],
 }
 
 COPY_KERNEL = re.compile(r"vectorized_elementwise_kernel.*MulFunctor")
