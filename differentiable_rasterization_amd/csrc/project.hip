@@ -17,6 +17,12 @@
 #include "kernels.h"
 #include "raster.h"
 
+// No implicit multiply-add contraction in this file: the forward projection, its recomputation
+// in the backward kernels and the fused step must round identically (the same cull
+// decisions and records in every kernel), which per-kernel contraction choices would not
+// guarantee.  Explicit fmaf calls stay fused.
+#pragma clang fp contract(off)
+
 namespace {
 
 struct CamD {
@@ -208,6 +214,19 @@ __device__ __forceinline__ void project_core(const CamD &cam, double mx, double 
     P.vis = true;
 }
 
+// The conic and opacity of the raster record, as float: a = -A log2(e)/2, b = -B log2(e),
+// c = -C log2(e)/2, l = log2 of the float32 opacity.
+struct RecConic {
+    float a, b, c, l;
+};
+
+__device__ __forceinline__ RecConic rec_conic(const Proj &P)
+{
+    constexpr double kL2e = 1.4426950408889634;
+    const double o32 = (double)(float)P.o;
+    return {(float)(-0.5 * kL2e * P.A), (float)(-kL2e * P.B), (float)(-0.5 * kL2e * P.C), (float)log2(o32)};
+}
+
 template <int DEG>
 __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means, const float *__restrict__ log_scales,
                                                  const float *__restrict__ quats, const float *__restrict__ logits,
@@ -250,10 +269,9 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
     color[3 * i + 1] = g;
     color[3 * i + 2] = b;
     // raster-ready copy: conic scaled for exp2, log2 of the stored opacity
-    constexpr double kL2e = 1.4426950408889634;
-    const double o32 = (double)(float)P.o;
-    rec[3 * i + 0] = make_float4((float)P.u, (float)P.v, (float)(-0.5 * kL2e * P.A), (float)(-kL2e * P.B));
-    rec[3 * i + 1] = make_float4((float)(-0.5 * kL2e * P.C), (float)log2(o32), r, g);
+    const RecConic rc = rec_conic(P);
+    rec[3 * i + 0] = make_float4((float)P.u, (float)P.v, rc.a, rc.b);
+    rec[3 * i + 1] = make_float4(rc.c, rc.l, r, g);
     rec[3 * i + 2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(P.rx), __int_as_float(P.ry));
 }
 
@@ -455,12 +473,15 @@ __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam
     for (int j = 0; j < 3; ++j) G.means[j] = (float)dmu[j];
 }
 
-template <int DEG, class Sink>
+// in: the screen-space gradients (u, v, A, B, C, o, r, g, b), or with RAW the per-Gaussian
+// moment sums of the raster backward, turned into those gradients here with the record's
+// conic and opacity as the forward pass rounded them (and stored to grads2d [9][n] if given).
+template <int DEG, bool RAW, class Sink>
 __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means, const float *__restrict__ log_scales,
                                                 const float *__restrict__ quats, const float *__restrict__ logits,
                                                 const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
-                                                float alpha_min, float depth_lo, float depth_hi, const float (&g2)[9],
-                                                const Sink &out)
+                                                float alpha_min, float depth_lo, float depth_hi, const float (&in)[9],
+                                                float *__restrict__ grads2d, const Sink &out)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     Params1<K> prm;
@@ -487,7 +508,19 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
 #pragma unroll
     for (int k = 0; k < K; ++k) G.Y[k] = 0.0f;
     G.gc[0] = G.gc[1] = G.gc[2] = 0.0f;
-    if (P.vis) project_bwd_grads<DEG>(P, cam, g2, prm, G);
+    if (RAW) {
+        float g2[9];
+        RecConic rc{0.0f, 0.0f, 0.0f, 0.0f};
+        if (P.vis) rc = rec_conic(P);
+        gsr::moments_to_grads(in, rc.a, rc.b, rc.c, rc.l, g2);
+        if (grads2d) {
+#pragma unroll
+            for (int f = 0; f < 9; ++f) grads2d[(int64_t)f * n + i] = g2[f];
+        }
+        if (P.vis) project_bwd_grads<DEG>(P, cam, g2, prm, G);
+    } else if (P.vis) {
+        project_bwd_grads<DEG>(P, cam, in, prm, G);
+    }
     out.flush(i, G, prm);
 }
 
@@ -502,7 +535,8 @@ __global__ __launch_bounds__(256) void k_project_bwd(
     float g[9];
 #pragma unroll
     for (int f = 0; f < 9; ++f) g[f] = g2[(int64_t)f * n + i];
-    project_bwd_one<DEG>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, g, out);
+    project_bwd_one<DEG, false>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, g,
+                                nullptr, out);
 }
 
 // The end of a training step per Gaussian: the per-Gaussian sum of Eq. 4 over its
@@ -513,18 +547,14 @@ __global__ __launch_bounds__(256) void k_grad_adam(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
     const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
-    const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad, const float4 *__restrict__ rec,
-    float *__restrict__ grads2d, AdamSink out)
+    const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad, float *__restrict__ grads2d, AdamSink out)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    float g[9];
-    gsr::sum_slots(hdr, drank, qoff, qgrad, rec, i, g);
-    if (grads2d) {
-#pragma unroll
-        for (int f = 0; f < 9; ++f) grads2d[(int64_t)f * n + i] = g[f];
-    }
-    project_bwd_one<DEG>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, g, out);
+    float acc[9];
+    gsr::raw_slot_sums(hdr, drank, qoff, qgrad, i, acc);
+    project_bwd_one<DEG, true>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, acc,
+                               grads2d, out);
 }
 
 }  // namespace
@@ -670,7 +700,7 @@ extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_proj
 #define GS_GA(D)                                                                                                   \
     k_grad_adam<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, cd, \
                                                p->alpha_min, p->depth_lo, p->depth_hi, hdr, drank, qoff, qg,      \
-                                               reinterpret_cast<const float4 *>(proj->rec), grads2d, sink)
+                                               grads2d, sink)
     switch (p->sh_degree) {
     case 0: GS_GA(0); break;
     case 1: GS_GA(1); break;

@@ -153,20 +153,14 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
 // ByteSplat Eq. 4 for Gaussian g: the sum of the gradient slots of its quadrant records,
 // slots qoff[r] .. qoff[r + 1] for its depth rank r, added in order (none when the lists
 // did not fit the capacity).  The slots hold per-record sums of the pixel moments S0 =
-// dpower, Sx, Sy, Sxx, Sxy, Syy and the colour terms; the screen-space gradients
-// (u, v, A, B, C, o, r, g, b) follow from their totals with the Gaussian's own conic and
-// opacity, taken from its raster record rec[g] (conic pre-scaled by -log2(e)/2, l = log2 o):
-//   A = -2 ln2 a, B = -ln2 b, C = -2 ln2 c,
-//   du = A Sx + B Sy, dv = B Sx + C Sy, dA = -Sxx/2, dB = -Sxy, dC = -Syy/2, do = S0 2^-l.
-// A Gaussian without records (culled) gets zeros and its record is not read.
-__device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
-                                          const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
-                                          const float4 *__restrict__ rec, int64_t g, float (&out)[9])
+// dpower, Sx, Sy, Sxx, Sxy, Syy and the colour terms.  Returns whether g has any slot.
+__device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
+                                              const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
+                                              int64_t g, float (&acc)[9])
 {
     const uint32_t r = drank[g];
     const bool ok = hdr->ok != 0u;
     const uint32_t s0 = ok ? qoff[r] : 0u, s1 = ok ? qoff[r + 1] : 0u;
-    float acc[9];
 #pragma unroll
     for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
     for (uint32_t j = s0; j < s1; ++j) {
@@ -176,23 +170,42 @@ __device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, co
         acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
         acc[8] += c.x;
     }
-    float A = 0.0f, B = 0.0f, C = 0.0f, io = 0.0f;
-    if (s1 > s0) {
-        const float4 p0 = rec[kRecF4 * (size_t)g], p1 = rec[kRecF4 * (size_t)g + 1];
-        A = -2.0f * kLn2 * p0.z;
-        B = -kLn2 * p0.w;
-        C = -2.0f * kLn2 * p1.x;
-        io = __builtin_amdgcn_exp2f(-p1.y);
-    }
+    return s1 > s0;
+}
+
+// The screen-space gradients (u, v, A, B, C, o, r, g, b) from the moment sums, with the
+// Gaussian's own conic and opacity as its raster record holds them (conic pre-scaled by
+// -log2(e)/2, l = log2 o):
+//   A = -2 ln2 a, B = -ln2 b, C = -2 ln2 c,
+//   du = A Sx + B Sy, dv = B Sx + C Sy, dA = -Sxx/2, dB = -Sxy, dC = -Syy/2, do = S0 2^-l.
+__device__ __forceinline__ void moments_to_grads(const float (&acc)[9], float a, float b, float c, float l,
+                                                 float (&out)[9])
+{
+    const float A = -2.0f * kLn2 * a, B = -kLn2 * b, C = -2.0f * kLn2 * c;
     out[0] = fmaf(A, acc[1], B * acc[2]);
     out[1] = fmaf(B, acc[1], C * acc[2]);
     out[2] = -0.5f * acc[3];
     out[3] = -acc[4];
     out[4] = -0.5f * acc[5];
-    out[5] = acc[0] * io;
+    out[5] = acc[0] * __builtin_amdgcn_exp2f(-l);
     out[6] = acc[6];
     out[7] = acc[7];
     out[8] = acc[8];
+}
+
+// Both steps, the record read from rec[g]; a Gaussian without records (culled) gets zeros
+// and its record is not read.
+__device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
+                                          const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
+                                          const float4 *__restrict__ rec, int64_t g, float (&out)[9])
+{
+    float acc[9];
+    float a = 0.0f, b = 0.0f, c = 0.0f, l = 0.0f;
+    if (raw_slot_sums(hdr, drank, qoff, qgrad, g, acc)) {
+        const float4 p0 = rec[kRecF4 * (size_t)g], p1 = rec[kRecF4 * (size_t)g + 1];
+        a = p0.z; b = p0.w; c = p1.x; l = p1.y;
+    }
+    moments_to_grads(acc, a, b, c, l, out);
 }
 
 // Number of entries below x (0 <= x <= K) that belong to quadrant q: the position in
