@@ -21,9 +21,10 @@
 //                                 quadrant records own slots qoff[r] .. qoff[r + 1], in the
 //                                 order of its entries and, within an entry, of the quadrants
 //                                 (qoff[n] = the number of quadrant records)
-//   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
-//                                 padded to 48 bytes), one slot per quadrant record, at the
-//                                 slot index its record carries
+//   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields and
+//                                 the stamp of the backward call that wrote them, padded to
+//                                 48 bytes), one slot per quadrant record, at the slot index
+//                                 its record carries
 //
 // Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
 // (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of records with
@@ -109,10 +110,14 @@ __device__ __forceinline__ uint32_t quad_mask(float u, float v, float A, float B
 
 // Counts of the last sort, in device memory (the first bytes of the raster buffer).  When
 // the lists did not fit (ok == 0) the sort leaves every tile list empty and the per-Gaussian
-// gradient reduction writes zeros.
+// gradient reduction writes zeros.  epoch: advanced by every backward call (any start
+// value); the backward stamps each gradient slot it writes with (epoch, ~epoch), and the
+// per-Gaussian sums take only slots stamped by the latest call, so slots of records no
+// pixel reached are never written (a stale or never-written slot matches the stamp with
+// probability 2^-64).
 struct BinsHeader {
     unsigned long long K, Q;   // tile entries and (entry, quadrant) records
-    uint32_t ok, pad;
+    uint32_t ok, epoch;
 };
 
 // The same test from a raster record (conic pre-scaled for exp2, l = log2 o):
@@ -160,12 +165,15 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
 {
     const uint32_t r = drank[g];
     const bool ok = hdr->ok != 0u;
+    const uint32_t epoch = hdr->epoch;
     const uint32_t s0 = ok ? qoff[r] : 0u, s1 = ok ? qoff[r + 1] : 0u;
 #pragma unroll
     for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
     for (uint32_t j = s0; j < s1; ++j) {
         const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
         const float4 a = sl[0], b = sl[1], c = sl[2];
+        // slots the latest backward call did not write hold nothing of this step
+        if (__float_as_uint(c.y) != epoch || __float_as_uint(c.z) != ~epoch) continue;
         acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
         acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
         acc[8] += c.x;

@@ -29,8 +29,10 @@
 // T unchanged and contributes zeros (no divergent branches).
 //
 // One wave per 8x8 quadrant (see raster.h), walking its tile's record list for the
-// quadrant front to back up to the furthest entry any of its pixels traversed; the slots
-// of the records behind that point are set to zero.
+// quadrant front to back up to the furthest entry any of its pixels traversed.  The slots of
+// records behind that point, and of batches no pixel takes, are not written: every slot
+// written carries the call's stamp (BinsHeader::epoch), and the per-Gaussian sums skip the
+// others.
 #include "kernels.h"
 #include "raster.h"
 
@@ -119,7 +121,8 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
                                                    int TX, int T, float alpha_min, float alpha_max,
                                                    const float *__restrict__ color, const float *__restrict__ t_final,
                                                    const int32_t *__restrict__ n_trav, const float *__restrict__ dL_dc,
-                                                   const float *__restrict__ dL_dt, float *__restrict__ qgrad)
+                                                   const float *__restrict__ dL_dt,
+                                                   const BinsHeader *__restrict__ hdr, float *__restrict__ qgrad)
 {
     int tidx, q;
     raster_block(tidx, q);
@@ -149,20 +152,14 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)(start + nmax));
-    const uint32_t jend = quad_prefix(bq, wq, (uint32_t)end);
-    // records never reached by any pixel of the quadrant contribute nothing: one lane per
-    // record clears its slot
-    for (uint32_t j = j1 + (uint32_t)lane; j < jend; j += 64u) {
-        float4 *z = reinterpret_cast<float4 *>(qgrad + (size_t)__float_as_uint(qrec[kRecF4 * (size_t)j + 2].w) * kGradSlot);
-        z[0] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        z[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        z[2] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
+    const uint32_t epoch = hdr->epoch;
     const int row = lane >> 4, nl = lane & 15;
     // the reduced field each lane of a row holds (reduce_4x9): even lanes hold fields 0-7,
-    // lane 1 field 8
-    const int my_field = nl == 1 ? 8 : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
-    const bool lane_writes = (nl & 1) == 0 || nl == 1;
+    // lane 1 field 8; lanes 3 and 5 write the stamp (epoch, ~epoch) into words 9 and 10
+    const int my_field = nl == 1 ? 8 : nl == 3 ? 9 : nl == 5 ? 10
+                                     : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
+    const bool lane_writes = (nl & 1) == 0 || nl == 1 || nl == 3 || nl == 5;
+    const float stamp = __uint_as_float(nl == 3 ? epoch : ~epoch);
     float Tr = 1.0f;
     // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
     uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
@@ -226,17 +223,17 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         float *dst = qgrad + (size_t)my_slot * kGradSlot + my_field;
         const bool writer = (uint32_t)row < cnt && lane_writes;
         jt += cnt;
-        if (__ballot(any) == 0) {
-            if (writer) *dst = 0.0f;
-            continue;
-        }
+        if (__ballot(any) == 0) continue;   // no pixel takes these records: slots left unstamped
         float fz, t8;
         reduce_4x9(v, nl, fz, t8);
-        if (writer) *dst = nl == 1 ? t8 : fz;
+        if (writer) *dst = nl == 1 ? t8 : (nl == 3 || nl == 5) ? stamp : fz;
     }
     sink ^= pend;
     asm volatile("" ::"v"(sink));
 }
+
+// A new stamp for the gradient slots of this backward call.
+__global__ void k_new_epoch(BinsHeader *__restrict__ hdr) { hdr->epoch = hdr->epoch + 1u; }
 
 // Eq. 4: the gradient of Gaussian g is the sum of the slots of its quadrant records,
 // slots qoff[r] .. qoff[r + 1] for its depth rank r, added in order.  Every Gaussian is
@@ -286,14 +283,17 @@ extern "C" gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins
     const uint32_t *wp = reinterpret_cast<const uint32_t *>(rb + L.wpre);
     float *qg = reinterpret_cast<float *>(rb + L.qgrad);
     const unsigned grid = (unsigned)raster_grid(T);
+    BinsHeader *hdr = reinterpret_cast<BinsHeader *>(rb + L.hdr);
+    k_new_epoch<<<1, 1, 0, stream>>>(hdr);
+    GS_LAUNCH_CHECK("k_new_epoch");
     if (dL_dt)
         k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
                                                     cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
-                                                    n_trav, dL_dcolor, dL_dt, qg);
+                                                    n_trav, dL_dcolor, dL_dt, hdr, qg);
     else
         k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
                                                      cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
-                                                     n_trav, dL_dcolor, nullptr, qg);
+                                                     n_trav, dL_dcolor, nullptr, hdr, qg);
     GS_LAUNCH_CHECK("k_raster_bwd");
     return GS_OK;
 }

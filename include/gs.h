@@ -244,7 +244,9 @@ gs_status gs_raster_bwd(const gs_gaussians *g, const gs_projected *proj, const g
  * stream.  gs_raster_bwd_partials: ByteSplat Eq. 3 per pixel and the per-quadrant part of
  * the Eq. 4 sum, written to per-record slots inside bins->raster (nothing outside it is
  * written; same arguments and checks as gs_raster_bwd).  The slots hold per-record sums of
- * pixel moments.  gs_grad_aggregate: the per-Gaussian part of the Eq. 4 sum over those slots,
+ * pixel moments, stamped with a counter the call advances, so gs_grad_aggregate reads only
+ * the slots of the latest gs_raster_bwd_partials call on these bins.  gs_grad_aggregate: the
+ * per-Gaussian part of the Eq. 4 sum over those slots,
  * turned into the screen-space gradients with the Gaussian's conic and opacity from
  * proj->rec, into grads2d [9][n] (every entry written), then, if grads3d is non-NULL, the
  * projection backward as in gs_raster_bwd.  Between the two calls the bins must not be
