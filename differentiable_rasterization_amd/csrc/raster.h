@@ -169,14 +169,23 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
     const uint32_t s0 = ok ? qoff[r] : 0u, s1 = ok ? qoff[r + 1] : 0u;
 #pragma unroll
     for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
-    for (uint32_t j = s0; j < s1; ++j) {
-        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
-        const float4 a = sl[0], b = sl[1], c = sl[2];
-        // slots the latest backward call did not write hold nothing of this step
-        if (__float_as_uint(c.y) != epoch || __float_as_uint(c.z) != ~epoch) continue;
+    // slots the latest backward call did not write hold nothing of this step
+    auto add = [&](const float4 &a, const float4 &b, const float4 &c) {
+        if (__float_as_uint(c.y) != epoch || __float_as_uint(c.z) != ~epoch) return;
         acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
         acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
         acc[8] += c.x;
+    };
+    uint32_t j = s0;
+    for (; j + 2 <= s1; j += 2) {   // two slots' loads in flight at once; summed in slot order
+        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
+        const float4 a0 = sl[0], b0 = sl[1], c0 = sl[2], a1 = sl[3], b1 = sl[4], c1 = sl[5];
+        add(a0, b0, c0);
+        add(a1, b1, c1);
+    }
+    if (j < s1) {
+        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
+        add(sl[0], sl[1], sl[2]);
     }
     return s1 > s0;
 }
