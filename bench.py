@@ -222,6 +222,8 @@ def main():
     if int(cnt[:, 1].max()) != 0:
         raise RuntimeError(f"intersection lists overflowed during the timed steps (need {int(cnt[:, 1].max())})")
     k_isect = [int(k) for k in cnt[:, 0]]
+    # quadrant records of the last sort (the list header: entries, then quadrant records)
+    q_last = int(st.bins.raster[:16].view(torch.int64)[1].item())
     isect_total = int(st.frame.n_trav_sum.item())
     timed_ms = {names[k]: sum(events[s][k].elapsed_time(events[s][k + 1]) for s in range(args.steps)) / args.steps
                 for k in timed_calls}
@@ -288,6 +290,7 @@ def main():
         if step_ms else None,
         "intersections_per_step": round(isect_step, 1),
         "tile_entries_per_step": round(kmean, 1),
+        "quadrant_records_last_step": q_last,
         "visible_gaussians": n_vis,
         # Gaussian-pixel intersections over the two raster kernels' time (forward compositing
         # and the per-pixel backward with its per-quadrant sums)

@@ -17,47 +17,155 @@ namespace {
 
 constexpr uint32_t kCulledKey = 0xFFFFFFFFu;
 
-// Depth keys (culled Gaussians last) and their indices; also clears the scans' look-back
-// state for this sort (zero: zero_words uint32).
-__global__ __launch_bounds__(256) void k_depth_keys(const int2 *__restrict__ radii, const float *__restrict__ depth,
-                                                    int64_t n, uint32_t *__restrict__ keys, uint32_t *__restrict__ vals,
-                                                    uint32_t *__restrict__ zero, int64_t zero_words)
+// ------------------------------------------------------------------ block-cooperative entries
+//
+// A block takes 256 Gaussians and walks their tile entries together, 256 entries per
+// round, so that a Gaussian covering many tiles does not hold up the lanes of Gaussians
+// covering few, and consecutive lanes produce consecutive entries.  Entry e of the block
+// belongs to the Gaussian o with off[o] <= e < off[o + 1] (block-local offsets in tile
+// row-major order); its quadrant mask is tested from o's record.
+
+struct Coop {
+    uint32_t off[257];        // block-local exclusive offsets of the Gaussians' entries; off[256] = total
+    float4 p0[256], p1[256];  // the Gaussians' raster records (centre, conic, opacity)
+    int4 rect[256];           // first tile column and row, width in tiles, Gaussian index
+    uint32_t qbase[256];      // first gradient slot of the Gaussian (emit only)
+    uint32_t qacc[256];       // quadrant records of the Gaussian's entries taken so far
+    uint32_t scan[256];       // inclusive scan of the current round's per-entry record counts
+    uint32_t wsum[4];
+};
+
+// Inclusive scan of one value per thread over the 256-thread block.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *wsum)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (int64_t z = i; z < zero_words; z += (int64_t)gridDim.x * blockDim.x) zero[z] = 0u;
-    if (i >= n) return;
-    const int2 r = radii[i];
-    keys[i] = (r.x > 0 && r.y > 0) ? __float_as_uint(depth[i]) : kCulledKey;
-    vals[i] = (uint32_t)i;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    uint32_t pre = 0;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (k < w) pre += wsum[k];
+    __syncthreads();
+    return pre + x;
 }
 
-// Tile counts of the Gaussians in depth order (0 for culled ones) and the number of
-// (tile, 8x8 quadrant) pairs their ellipse reaches (qcnt [n + 1], qcnt[n] = 0, so that its
-// exclusive scan ends with the total); also records each Gaussian's depth rank for the
-// backward's per-Gaussian reduction.
-__global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ skeys, const uint32_t *__restrict__ svals,
-                                               const float4 *__restrict__ rec, float log2_amin, int64_t n,
-                                               int tx, int ty, uint32_t *__restrict__ cnt, uint32_t *__restrict__ qcnt,
-                                               uint32_t *__restrict__ drank)
+// Loads Gaussian t of the block (valid: it is listed; otherwise it has no entries) into
+// the shared state and sets the block-local offsets.  Returns the block's entry count.
+__device__ __forceinline__ uint32_t coop_load(Coop &S, bool valid, uint32_t g, const float4 *__restrict__ rec,
+                                              int tx, int ty, uint32_t &c_out)
 {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j == 0) qcnt[n] = 0;
-    if (j >= n) return;
-    uint32_t c = 0, qc = 0;
-    const uint32_t g = svals[j];
-    if (skeys[j] != kCulledKey) {
-        const float4 p0 = rec[gsr::kRecF4 * (size_t)g], p1 = rec[gsr::kRecF4 * (size_t)g + 1],
-                     p2 = rec[gsr::kRecF4 * (size_t)g + 2];
-        int x0, x1, y0, y1;
+    const int t = threadIdx.x;
+    uint32_t c = 0;
+    float4 p0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), p1 = p0;
+    int x0 = 0, w = 1;
+    int y0 = 0;
+    if (valid) {
+        p0 = rec[gsr::kRecF4 * (size_t)g];
+        p1 = rec[gsr::kRecF4 * (size_t)g + 1];
+        const float4 p2 = rec[gsr::kRecF4 * (size_t)g + 2];
+        int x1, y1;
         gsd::tile_rect(p0.x, p0.y, __float_as_int(p2.z), __float_as_int(p2.w), tx, ty, x0, x1, y0, y1);
-        c = (uint32_t)((x1 - x0) * (y1 - y0));
-        for (int y = y0; y < y1; ++y)
-            for (int x = x0; x < x1; ++x)
-                qc += __popc(gsr::quad_mask_rec(p0, p1, log2_amin, (float)(x * GS_TILE), (float)(y * GS_TILE)));
+        if (x1 > x0 && y1 > y0) {
+            c = (uint32_t)((x1 - x0) * (y1 - y0));
+            w = x1 - x0;
+        }
     }
-    cnt[j] = c;
-    qcnt[j] = qc;
-    drank[g] = (uint32_t)j;
+    const uint32_t incl = block_incl_scan(c, S.wsum);
+    S.off[t] = incl - c;
+    if (t == 255) S.off[256] = incl;
+    S.p0[t] = p0;
+    S.p1[t] = p1;
+    S.rect[t] = make_int4(x0, y0, w, (int)g);
+    S.qacc[t] = 0u;
+    c_out = c;
+    __syncthreads();
+    return S.off[256];
+}
+
+// One round of entries e0 .. e0 + 255 (e = e0 + threadIdx.x).  For a real entry (e < C):
+// its Gaussian o (block-local), tile (x, y), quadrant mask qm and, in slot_in, the number
+// of quadrant records of o's earlier entries (all rounds).  Advances S.qacc.
+struct CoopEntry {
+    bool real;
+    int o, x, y;
+    uint32_t qm, slot_in;
+};
+
+__device__ __forceinline__ CoopEntry coop_round(Coop &S, uint32_t e0, uint32_t C, float log2_amin)
+{
+    const int t = threadIdx.x;
+    const uint32_t e = e0 + (uint32_t)t;
+    CoopEntry E{e < C, 0, 0, 0, 0u, 0u};
+    if (E.real) {
+        int o = 0;   // the last Gaussian whose offset is <= e (those with no entries share the next one's)
+#pragma unroll
+        for (int step = 128; step > 0; step >>= 1)
+            if (S.off[o + step] <= e) o += step;
+        const int4 R = S.rect[o];
+        const uint32_t local = e - S.off[o];
+        const uint32_t row = local / (uint32_t)R.z;
+        E.o = o;
+        E.x = R.x + (int)(local - row * (uint32_t)R.z);
+        E.y = R.y + (int)row;
+        E.qm = gsr::quad_mask_rec(S.p0[o], S.p1[o], log2_amin, (float)(E.x * GS_TILE), (float)(E.y * GS_TILE));
+    }
+    const uint32_t pc = (uint32_t)__popc(E.qm);
+    const uint32_t incl = block_incl_scan(pc, S.wsum);
+    S.scan[t] = incl;
+    __syncthreads();
+    uint32_t upd = 0;
+    bool last = false;
+    if (E.real) {
+        const uint32_t o_begin = S.off[E.o], o_end = S.off[E.o + 1];
+        const uint32_t first = (o_begin > e0 ? o_begin : e0) - e0;   // o's first entry of this round
+        const uint32_t before = first ? S.scan[first - 1] : 0u;
+        E.slot_in = S.qacc[E.o] + (incl - pc - before);
+        const uint32_t round_end = min(min(o_end, e0 + 256u), C);
+        last = e + 1 == round_end;   // o's last entry of this round
+        upd = incl - before;
+    }
+    __syncthreads();
+    if (last) S.qacc[E.o] += upd;
+    __syncthreads();
+    return E;
+}
+
+// Depth keys (culled Gaussians last) in index order, with the values tile count << 32 |
+// index, each Gaussian's quadrant-record count (qcnt [n + 1], qcnt[n] = 0, so that its
+// exclusive scan ends with the total), optionally the tile counts for the caller
+// (touched); also clears the scans' look-back state for this sort (zero: zero_words
+// uint32).
+__global__ __launch_bounds__(256) void k_keys_count(const int2 *__restrict__ radii, const float *__restrict__ depth,
+                                                    const float4 *__restrict__ rec, float log2_amin, int64_t n,
+                                                    int tx, int ty, uint32_t *__restrict__ keys,
+                                                    uint64_t *__restrict__ vals, uint32_t *__restrict__ qcnt,
+                                                    int32_t *__restrict__ touched, uint32_t *__restrict__ zero,
+                                                    int64_t zero_words)
+{
+    __shared__ Coop S;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t z = i; z < zero_words; z += (int64_t)gridDim.x * blockDim.x) zero[z] = 0u;
+    if (i == 0) qcnt[n] = 0u;
+    bool vis = false;
+    if (i < n) {
+        const int2 r = radii[i];
+        vis = r.x > 0 && r.y > 0;
+        keys[i] = vis ? __float_as_uint(depth[i]) : kCulledKey;
+    }
+    uint32_t c;
+    const uint32_t C = coop_load(S, vis, (uint32_t)i, rec, tx, ty, c);
+    for (uint32_t e0 = 0; e0 < C; e0 += 256u) coop_round(S, e0, C, log2_amin);
+    if (i < n) {
+        vals[i] = ((uint64_t)c << 32) | (uint64_t)i;
+        qcnt[i] = S.qacc[threadIdx.x];
+        if (touched) touched[i] = (int32_t)c;
+    }
 }
 
 // Capacity the lists of K entries and Q quadrant records need.
@@ -67,19 +175,21 @@ __device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned lo
     return K > qc ? K : qc;
 }
 
-// Entries of each Gaussian in depth order, tiles row-major.  Entry p gets the key
+// Entries of the Gaussians in depth order (block b: depth ranks 256 b ..; svals: tile
+// count << 32 | Gaussian), tiles row-major; off: exclusive scan of the tile counts in depth
+// order.  Entry p gets the key
 // tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at) and the
 // value (gradient slot of its first quadrant record) << 32 | its Gaussian, carried through
-// the tile sort (the Gaussian's slots follow its entries in order).
-__global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
-                                              const uint32_t *__restrict__ off, const uint32_t *__restrict__ qoff,
+// the tile sort.  Gaussian g's quadrant records own slots qoff[g] .. qoff[g + 1], in the
+// order of its entries and, within an entry, of the quadrants.
+__global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals, const uint32_t *__restrict__ off, const uint32_t *__restrict__ qoff,
                                               const float4 *__restrict__ rec, float log2_amin, int64_t n, int tx,
-                                              int ty,
-                                              const unsigned long long *__restrict__ tot, int64_t cap,
+                                              int ty, const unsigned long long *__restrict__ tot, int64_t cap,
                                               unsigned long long *__restrict__ klen, gsr::BinsHeader *__restrict__ hdr,
-                                              int64_t *__restrict__ counts,
-                                              uint32_t *__restrict__ tkeys, uint64_t *__restrict__ tvals)
+                                              int64_t *__restrict__ counts, uint32_t *__restrict__ tkeys,
+                                              uint64_t *__restrict__ tvals)
 {
+    __shared__ Coop S;
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const unsigned long long K = tot[0], Q = tot[1];
     const bool ok = need_capacity(K, Q) <= (unsigned long long)cap;
@@ -93,21 +203,26 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t *__restrict__ svals
             counts[1] = ok ? 0 : (int64_t)need_capacity(K, Q);
         }
     }
-    if (!ok || j >= n || cnt[j] == 0) return;
-    const uint32_t g = svals[j];
-    const float4 p0 = rec[gsr::kRecF4 * (size_t)g], p1 = rec[gsr::kRecF4 * (size_t)g + 1],
-                 p2 = rec[gsr::kRecF4 * (size_t)g + 2];
-    int x0, x1, y0, y1;
-    gsd::tile_rect(p0.x, p0.y, __float_as_int(p2.z), __float_as_int(p2.w), tx, ty, x0, x1, y0, y1);
-    uint32_t p = off[j], sl = qoff[j];
-    for (int y = y0; y < y1; ++y)
-        for (int x = x0; x < x1; ++x) {
-            const uint32_t qm = gsr::quad_mask_rec(p0, p1, log2_amin, (float)(x * GS_TILE), (float)(y * GS_TILE));
-            tkeys[p] = (uint32_t)(y * tx + x) | (qm << gsr::kMaskShift);
-            tvals[p] = ((uint64_t)sl << 32) | g;
-            sl += (uint32_t)__popc(qm);
-            ++p;
+    if (!ok) return;   // the whole block agrees
+    const int64_t j0 = (int64_t)blockIdx.x * blockDim.x;
+    const uint64_t sv = j < n ? svals[j] : 0ull;
+    const bool listed = (sv >> 32) != 0u;   // culled Gaussians and those off the image have no tiles
+    const uint32_t g = (uint32_t)sv;
+    uint32_t c;
+    const uint32_t C = coop_load(S, listed, g, rec, tx, ty, c);
+    if (C == 0) return;
+    S.qbase[threadIdx.x] = listed ? qoff[g] : 0u;
+    const uint64_t base = off[j0];
+    __syncthreads();
+    for (uint32_t e0 = 0; e0 < C; e0 += 256u) {
+        const CoopEntry E = coop_round(S, e0, C, log2_amin);
+        const uint64_t p = base + e0 + threadIdx.x;
+        if (E.real && p < (uint64_t)cap) {   // p < K <= cap; the test keeps a bug from writing out of bounds
+            const uint32_t slot = S.qbase[E.o] + E.slot_in;
+            tkeys[p] = (uint32_t)(E.y * tx + E.x) | (E.qm << gsr::kMaskShift);
+            tvals[p] = ((uint64_t)slot << 32) | (uint32_t)S.rect[E.o].w;
         }
+    }
 }
 
 // Finishes the sorted lists in one pass over the entries: the Gaussian index of each
@@ -153,21 +268,37 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
 // its box reaches, at the position given by the scanned bit counts, and stamps the entry
 // index and the record's gradient slot into it.  The spare records around the lists are
 // read (never used) by the raster kernels' batches: they are zeroed, so they stay finite.
+// Blocks reach the 8 XCDs round-robin (block b on XCD b % 8).  The first `active` blocks
+// are renumbered so that each XCD takes one contiguous run of them: the entries of
+// neighbouring tiles, which gather the records of largely the same Gaussians, then share
+// one L2.  Returns -1 for blocks past `active`.
+__device__ __forceinline__ int64_t xcd_contiguous_block(int64_t active)
+{
+    const int64_t b = blockIdx.x;
+    if (b >= active) return -1;
+    const int64_t x = b % gsi::kXcds, per = active / gsi::kXcds, rem = active % gsi::kXcds;
+    return x * per + (x < rem ? x : rem) + b / gsi::kXcds;
+}
+
 __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint64_t *__restrict__ tvals,
                                                     const unsigned long long *__restrict__ klen, int64_t words,
                                                     const uint64_t *__restrict__ bitmap,
                                                     const uint32_t *__restrict__ wpre,
                                                     const float4 *__restrict__ prec, float4 *__restrict__ qrec)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     constexpr int kPadF4 = gsr::kRecPad * gsr::kRecF4;
-    if (k < 2 * kPadF4) {
+    const int64_t kp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (kp < 2 * kPadF4) {
         // leading pad, then the pad after the last record (the scan's total)
         const int64_t q_total = wpre[(int64_t)gsr::kQuads * (words + 1) - 1];
-        const int64_t at = k < kPadF4 ? k - kPadF4 : gsr::kRecF4 * q_total + (k - kPadF4);
+        const int64_t at = kp < kPadF4 ? kp - kPadF4 : gsr::kRecF4 * q_total + (kp - kPadF4);
         qrec[at] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    if (k >= (int64_t)*klen) return;
+    const int64_t K = (int64_t)*klen;
+    const int64_t blk = xcd_contiguous_block((K + 255) / 256);
+    if (blk < 0) return;
+    const int64_t k = blk * 256 + threadIdx.x;
+    if (k >= K) return;
     const uint32_t qm = tkeys[k] >> gsr::kMaskShift;
     if (!qm) return;
     const uint64_t tvk = tvals[k];
@@ -195,14 +326,6 @@ __global__ __launch_bounds__(256) void k_keys64(const uint32_t *__restrict__ tke
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= (int64_t)*klen) return;
     keys[k] = ((uint64_t)(tkeys[k] & gsr::kTileMask) << 32) | (uint64_t)__float_as_uint(depth[ids[k]]);
-}
-
-__global__ __launch_bounds__(256) void k_touched(const uint32_t *__restrict__ svals, const uint32_t *__restrict__ cnt,
-                                                 int64_t n, int32_t *__restrict__ touched)
-{
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= n) return;
-    touched[svals[j]] = (int32_t)cnt[j];
 }
 
 // Tiles ordered by decreasing list length (bucketed by the bit length of the count, so
@@ -247,10 +370,10 @@ __global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restr
 }
 
 struct Layout {
-    // zero region (cleared by k_depth_keys at the start of every sort): tickets and
+    // zero region (cleared by k_keys_count at the start of every sort): tickets and
     // look-back status words of the scans
     size_t zero, tickets, stD, stT, scC, scQ, scW, zero_bytes;
-    size_t dkA, dvA, dkB, dvB, cnt, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, hist, bytes;
+    size_t dkA, dvA, dkB, dvB, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, hist, bytes;
     int tbits;
 };
 
@@ -278,8 +401,8 @@ Layout layout(int64_t n, int64_t cap, int32_t tiles)
     L.scQ = take(8 * (size_t)gsi::lb_scan_tiles((int64_t)nn + 1));
     L.scW = take(8 * (size_t)gsi::lb_scan_tiles(nw));
     L.zero_bytes = o - L.zero;
-    L.dkA = take(4 * nn); L.dvA = take(4 * nn); L.dkB = take(4 * nn); L.dvB = take(4 * nn);
-    L.cnt = take(4 * nn); L.qcnt = take(4 * (nn + 1)); L.doff = take(4 * nn);
+    L.dkA = take(4 * nn); L.dvA = take(8 * nn); L.dkB = take(4 * nn); L.dvB = take(8 * nn);
+    L.qcnt = take(4 * (nn + 1)); L.doff = take(4 * nn);
     L.total = take(16);   // K, then the quadrant records
     L.klen = take(8);     // K if the lists fit, else 0
     L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(8 * cc); L.tvB = take(8 * cc);
@@ -339,7 +462,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     char *rb = static_cast<char *>(bins->raster);
     gsr::BinsHeader *hdr = reinterpret_cast<gsr::BinsHeader *>(rb + RL.hdr);
     int32_t *order = reinterpret_cast<int32_t *>(rb + RL.order);
-    uint32_t *drank = reinterpret_cast<uint32_t *>(rb + RL.drank), *qoff = reinterpret_cast<uint32_t *>(rb + RL.qoff);
+    uint32_t *qoff = reinterpret_cast<uint32_t *>(rb + RL.qoff);
     // the quadrant prefix counts of empty lists: zero
     uint32_t *wpre0 = reinterpret_cast<uint32_t *>(rb + RL.wpre);
     const int64_t nw0 = gsr::kQuads * (RL.words + 1);
@@ -360,9 +483,9 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.bytes)
         return fail(GS_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, 256-byte aligned", L.bytes);
     char *ws = static_cast<char *>(workspace);
-    uint32_t *dkA = (uint32_t *)(ws + L.dkA), *dvA = (uint32_t *)(ws + L.dvA);
-    uint32_t *dkB = (uint32_t *)(ws + L.dkB), *dvB = (uint32_t *)(ws + L.dvB);
-    uint32_t *cnt = (uint32_t *)(ws + L.cnt), *qcnt = (uint32_t *)(ws + L.qcnt), *doff = (uint32_t *)(ws + L.doff);
+    uint32_t *dkA = (uint32_t *)(ws + L.dkA), *dkB = (uint32_t *)(ws + L.dkB);
+    uint64_t *dvA = (uint64_t *)(ws + L.dvA), *dvB = (uint64_t *)(ws + L.dvB);
+    uint32_t *qcnt = (uint32_t *)(ws + L.qcnt), *doff = (uint32_t *)(ws + L.doff);
     unsigned long long *total = (unsigned long long *)(ws + L.total);
     unsigned long long *klen = (unsigned long long *)(ws + L.klen);
     uint32_t *tkA = (uint32_t *)(ws + L.tkA), *tkB = (uint32_t *)(ws + L.tkB);
@@ -375,30 +498,26 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     const float4 *prec = reinterpret_cast<const float4 *>(proj->rec);
     const unsigned gn = (unsigned)ceil_div(n, 256);
 
-    // 1. Gaussians by depth key (stable, so equal keys stay in index order)
-    k_depth_keys<<<gn, 256, 0, stream>>>(rr, proj->depth, n, dkA, dvA, (uint32_t *)(ws + L.zero),
-                                         (int64_t)(L.zero_bytes / 4));
-    GS_LAUNCH_CHECK("k_depth_keys");
-    bool in_b = false;
-    if ((s = radix_sort_u32(dkA, dvA, dkB, dvB, n, 32, hist, stD, tickets + kTkDepth, &in_b, stream)) != GS_OK)
-        return s;
-    const uint32_t *sk = in_b ? dkB : dkA, *sv = in_b ? dvB : dvA;
-
-    // 2. tile and quadrant-record counts in depth order, their exclusive scans (the emit
-    //    offsets and the first gradient slot of each Gaussian) and the totals K and Q
-    k_count<<<gn, 256, 0, stream>>>(sk, sv, prec, log2_amin, n, tx, ty, cnt, qcnt, drank);
-    GS_LAUNCH_CHECK("k_count");
-    if ((s = lb_scan_u32(cnt, doff, n, scC, tickets + kTkCnt, total, stream)) != GS_OK) return s;
+    // 1. depth keys, tile and quadrant-record counts in index order; the first gradient
+    //    slot of each Gaussian (exclusive scan of its record counts) and the total Q
+    k_keys_count<<<gn, 256, 0, stream>>>(rr, proj->depth, prec, log2_amin, n, tx, ty, dkA, dvA, qcnt,
+                                         bins->tiles_touched, (uint32_t *)(ws + L.zero), (int64_t)(L.zero_bytes / 4));
+    GS_LAUNCH_CHECK("k_keys_count");
     if ((s = lb_scan_u32(qcnt, qoff, n + 1, scQ, tickets + kTkQcnt, total + 1, stream)) != GS_OK) return s;
-    if (bins->tiles_touched) {
-        k_touched<<<gn, 256, 0, stream>>>(sv, cnt, n, bins->tiles_touched);
-        GS_LAUNCH_CHECK("k_touched");
-    }
+
+    // 2. Gaussians by depth key (stable, so equal keys stay in index order; the values
+    //    carry the tile counts along), and the emit offsets: the exclusive scan of the tile
+    //    counts in that order, with the total K
+    bool in_b = false;
+    if ((s = radix_sort_u32_u64(dkA, dvA, dkB, dvB, n, 32, hist, stD, tickets + kTkDepth, &in_b, stream)) != GS_OK)
+        return s;
+    const uint64_t *sv = in_b ? dvB : dvA;
+    if ((s = lb_scan_hi32(sv, doff, n, scC, tickets + kTkCnt, total, stream)) != GS_OK) return s;
 
     // 3. emit entries in depth order (nothing if the lists do not fit), then a stable sort
     //    of (tile key, emit position) by tile
     const int tbits = L.tbits;
-    k_emit<<<gn, 256, 0, stream>>>(sv, cnt, doff, qoff, prec, log2_amin, n, tx, ty, total, cap, klen, hdr, counts, tkA,
+    k_emit<<<gn, 256, 0, stream>>>(sv, doff, qoff, prec, log2_amin, n, tx, ty, total, cap, klen, hdr, counts, tkA,
                                    tvA);
     GS_LAUNCH_CHECK("k_emit");
     if (cap == 0) {

@@ -24,6 +24,9 @@ gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint3
 int64_t lb_scan_tiles(int64_t m);
 gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
                       unsigned long long *total, hipStream_t stream);
+// The same over the high 32 bits of m uint64 values (in: 16-byte aligned).
+gs_status lb_scan_hi32(const uint64_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
+                       unsigned long long *total, hipStream_t stream);
 
 // Stable LSD radix sort of (key, value) uint32 pairs on the low `bits` bits of the key,
 // 8 bits per pass, ping-ponging between (ka, va) and (kb, vb).  Returns in *in_b whether

@@ -16,11 +16,10 @@
 //                                 qrec[P_q(start_t) .. P_q(end_t)), P_q(x) = wpre[q][x / 64]
 //                                 + set bits of bitmap q below entry x in its word
 //   order  [tiles] int32          tiles by decreasing list length (heaviest first)
-//   drank  [n] uint32             depth rank of each Gaussian (culled ones rank last)
-//   qoff   [n + 1] uint32         first gradient slot of the Gaussian of depth rank r: its
-//                                 quadrant records own slots qoff[r] .. qoff[r + 1], in the
-//                                 order of its entries and, within an entry, of the quadrants
-//                                 (qoff[n] = the number of quadrant records)
+//   qoff   [n + 1] uint32         first gradient slot of Gaussian g: its quadrant records
+//                                 own slots qoff[g] .. qoff[g + 1], in the order of its
+//                                 entries and, within an entry, of the quadrants (qoff[n] =
+//                                 the number of quadrant records)
 //   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields and
 //                                 the stamp of the backward call that wrote them, padded to
 //                                 48 bytes), one slot per quadrant record, at the slot index
@@ -130,7 +129,7 @@ __device__ __forceinline__ uint32_t quad_mask_rec(const float4 &p0, const float4
 }
 
 struct RasterLayout {
-    size_t hdr, qrec, bitmap, wpre, order, drank, qoff, qgrad, bytes;
+    size_t hdr, qrec, bitmap, wpre, order, qoff, qgrad, bytes;
     int64_t cap, words;
 };
 
@@ -148,7 +147,6 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
     L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);
     L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);
-    L.drank = o;  o += align256(nn * 4);
     L.qoff = o;   o += align256((nn + 1) * 4);
     L.qgrad = o;  o += align256(q4 * kGradSlot * 4);
     L.bytes = o;
@@ -156,17 +154,15 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
 }
 
 // ByteSplat Eq. 4 for Gaussian g: the sum of the gradient slots of its quadrant records,
-// slots qoff[r] .. qoff[r + 1] for its depth rank r, added in order (none when the lists
-// did not fit the capacity).  The slots hold per-record sums of the pixel moments S0 =
-// dpower, Sx, Sy, Sxx, Sxy, Syy and the colour terms.  Returns whether g has any slot.
-__device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
-                                              const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
-                                              int64_t g, float (&acc)[9])
+// slots qoff[g] .. qoff[g + 1], added in order (none when the lists did not fit the
+// capacity).  The slots hold per-record sums of the pixel moments S0 = dpower, Sx, Sy,
+// Sxx, Sxy, Syy and the colour terms.  Returns whether g has any slot.
+__device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
+                                              const float4 *__restrict__ qgrad, int64_t g, float (&acc)[9])
 {
-    const uint32_t r = drank[g];
     const bool ok = hdr->ok != 0u;
     const uint32_t epoch = hdr->epoch;
-    const uint32_t s0 = ok ? qoff[r] : 0u, s1 = ok ? qoff[r + 1] : 0u;
+    const uint32_t s0 = ok ? qoff[g] : 0u, s1 = ok ? qoff[g + 1] : 0u;
 #pragma unroll
     for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
     // slots the latest backward call did not write hold nothing of this step
@@ -212,13 +208,13 @@ __device__ __forceinline__ void moments_to_grads(const float (&acc)[9], float a,
 
 // Both steps, the record read from rec[g]; a Gaussian without records (culled) gets zeros
 // and its record is not read.
-__device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
-                                          const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
-                                          const float4 *__restrict__ rec, int64_t g, float (&out)[9])
+__device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
+                                          const float4 *__restrict__ qgrad, const float4 *__restrict__ rec, int64_t g,
+                                          float (&out)[9])
 {
     float acc[9];
     float a = 0.0f, b = 0.0f, c = 0.0f, l = 0.0f;
-    if (raw_slot_sums(hdr, drank, qoff, qgrad, g, acc)) {
+    if (raw_slot_sums(hdr, qoff, qgrad, g, acc)) {
         const float4 p0 = rec[kRecF4 * (size_t)g], p1 = rec[kRecF4 * (size_t)g + 1];
         a = p0.z; b = p0.w; c = p1.x; l = p1.y;
     }

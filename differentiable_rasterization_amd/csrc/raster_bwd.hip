@@ -236,11 +236,11 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
 __global__ void k_new_epoch(BinsHeader *__restrict__ hdr) { hdr->epoch = hdr->epoch + 1u; }
 
 // Eq. 4: the gradient of Gaussian g is the sum of the slots of its quadrant records,
-// slots qoff[r] .. qoff[r + 1] for its depth rank r, added in order.  Every Gaussian is
+// slots qoff[g] .. qoff[g + 1], added in order.  Every Gaussian is
 // written, culled ones (no records) with zeros, and all of them when the lists did not
 // fit the capacity.  One thread per Gaussian, in index order
 // so that the stores coalesce.
-__global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ drank,
+__global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restrict__ hdr,
                                                      const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
                                                      const float4 *__restrict__ rec, int64_t n,
                                                      float *__restrict__ grads2d)
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restric
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n) return;
     float acc[kFields];
-    sum_slots(hdr, drank, qoff, qgrad, rec, g, acc);
+    sum_slots(hdr, qoff, qgrad, rec, g, acc);
 #pragma unroll
     for (int f = 0; f < kFields; ++f) grads2d[(size_t)f * n + g] = acc[f];
 }
@@ -317,8 +317,7 @@ extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_projected
         const RasterLayout L = raster_layout(n, bins->capacity, T);
         const char *rb = static_cast<const char *>(bins->raster);
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
-            reinterpret_cast<const BinsHeader *>(rb + L.hdr), reinterpret_cast<const uint32_t *>(rb + L.drank),
-            reinterpret_cast<const uint32_t *>(rb + L.qoff),
+            reinterpret_cast<const BinsHeader *>(rb + L.hdr), reinterpret_cast<const uint32_t *>(rb + L.qoff),
             reinterpret_cast<const float4 *>(rb + L.qgrad), reinterpret_cast<const float4 *>(proj->rec), n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }

@@ -138,20 +138,43 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
 }
 
 // sum over the image of N_p, added to *n_sum: one 64-bit atomic per block (a device-wide
-// counter updated once per raster wave would serialise ~10^4 atomics on one address)
+// counter updated once per raster wave would serialise ~10^4 atomics on one address).
+// Each thread reads four 16-byte groups of pixels, independently, when n_trav is 16-byte
+// aligned; otherwise single pixels.
+constexpr int kSumGroups = 4;
+
 __global__ __launch_bounds__(256) void k_sum_ntrav(const int32_t *__restrict__ n_trav, int64_t n_px,
                                                    unsigned long long *__restrict__ n_sum)
 {
     __shared__ unsigned long long part[4];
     unsigned long long acc = 0;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_px; i += (int64_t)gridDim.x * 256)
-        acc += (unsigned)n_trav[i];
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x, stride = (int64_t)gridDim.x * 256;
+    if ((reinterpret_cast<uintptr_t>(n_trav) & 15) == 0) {
+        const int4 *v = reinterpret_cast<const int4 *>(n_trav);
+        const int64_t n4 = n_px >> 2;
+        int4 x[kSumGroups];
+#pragma unroll
+        for (int u = 0; u < kSumGroups; ++u) {
+            const int64_t i = t + u * stride;
+            x[u] = i < n4 ? v[i] : make_int4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kSumGroups; ++u)
+            acc += (unsigned long long)((uint32_t)x[u].x + (uint32_t)x[u].y) + ((uint32_t)x[u].z + (uint32_t)x[u].w);
+        for (int64_t i = t + kSumGroups * stride; i < n4; i += stride) {
+            const int4 y = v[i];
+            acc += (unsigned long long)((uint32_t)y.x + (uint32_t)y.y) + ((uint32_t)y.z + (uint32_t)y.w);
+        }
+        if (t < (n_px & 3)) acc += (uint32_t)n_trav[(n4 << 2) + t];
+    } else {
+        for (int64_t i = t; i < n_px; i += stride) acc += (uint32_t)n_trav[i];
+    }
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_down(acc, o, 64);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned long long t = part[0] + part[1] + part[2] + part[3];
-        if (t) atomicAdd(n_sum, t);
+        const unsigned long long s = part[0] + part[1] + part[2] + part[3];
+        if (s) atomicAdd(n_sum, s);
     }
 }
 
@@ -194,8 +217,8 @@ extern "C" gs_status gs_raster_fwd(const gs_projected *proj, const gs_bins *bins
     GS_LAUNCH_CHECK("k_raster_fwd");
     if (n_trav_sum) {
         const int64_t n_px = (int64_t)cam->width * cam->height;
-        k_sum_ntrav<<<(unsigned)std::min<int64_t>(ceil_div(n_px, 256 * 8), 1024), 256, 0, stream>>>(n_trav, n_px,
-                                                                                                   n_trav_sum);
+        const int64_t blocks = std::min<int64_t>(std::max<int64_t>(ceil_div(n_px, 256 * 4 * kSumGroups), 1), 1024);
+        k_sum_ntrav<<<(unsigned)blocks, 256, 0, stream>>>(n_trav, n_px, n_trav_sum);
         GS_LAUNCH_CHECK("k_sum_ntrav");
     }
     return GS_OK;

@@ -2,7 +2,8 @@
 //
 // Radix pass (8-bit digit, reduce-then-scan, stable):
 //   hist    : each 256-thread block counts the digits of its 2048-element tile
-//             (per-wave LDS histograms) and writes them digit-major, so that one
+//             (per-wave LDS histograms, one add per run of equal digits across the
+//             lanes) and writes them digit-major, so that one
 //             exclusive scan over [digit][block] gives every (digit, block) its
 //             global output offset;
 //   scan    : the single-launch look-back scan below;
@@ -143,10 +144,22 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&h[0][0])[i] = 0;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kRxTile + (int64_t)w * kRxWaveSpan + lane;
+    // Consecutive lanes hold consecutive elements.  Each run of equal digits across the
+    // lanes is counted by its first lane with one LDS add of the run length, so skewed or
+    // presorted keys (long runs of one digit) do not serialise on one LDS address.
 #pragma unroll 4
     for (int r = 0; r < kRxItems; ++r) {
         const int64_t e = base + r * 64;
-        if (e < m) atomicAdd(&h[w][(keys[e] >> shift) & 255u], 1u);
+        const bool valid = e < m;
+        const uint32_t d = valid ? (keys[e] >> shift) & 255u : 0x100u;   // 0x100: no element
+        const uint32_t dp = __shfl_up(d, 1, 64);
+        const bool head = lane == 0 || d != dp;
+        const uint64_t heads = __ballot(head);
+        if (head && valid) {
+            const uint64_t above = lane == 63 ? 0ull : heads >> (lane + 1);
+            const int next = above ? lane + 1 + __builtin_ctzll(above) : 64;
+            atomicAdd(&h[w][d], (uint32_t)(next - lane));
+        }
     }
     __syncthreads();
     const int d = threadIdx.x;
@@ -236,11 +249,15 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
 
 // ------------------------------------------------------------------ single-launch scan
 //
-// Each block takes the next tile of kTile values in arrival order (an atomic ticket: any
+// Each block takes the next tile of values in arrival order (an atomic ticket: any
 // tile it waits for belongs to a block that has already started), publishes its sum, and
 // finds the sum of everything before it by looking back over the published sums, 64 tiles
 // per step (one wave, one status word per lane), until it meets a tile that has published
-// its inclusive prefix.  64-bit status words: flag in bits 62..63 (0 = not yet published,
+// its inclusive prefix.  In the steady state each tile waits for its predecessor's
+// inclusive prefix, a chain of ~45 ns per tile on MI355X (measured; wider windows of 8
+// words per lane were slower), so large scans take larger tiles: 4096 values up to 1.5M,
+// 8192 up to 6M, 16384 above (the chain, not the bandwidth, bounds a scan of 10M values
+// with 4096-value tiles).  64-bit status words: flag in bits 62..63 (0 = not yet published,
 // 1 = the tile's own sum, 2 = its inclusive prefix), the sum below.
 constexpr unsigned long long kFlagSum = 1ull << 62, kFlagIncl = 2ull << 62, kFlagMask = 3ull << 62;
 
@@ -261,34 +278,56 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void k_scan_lb(const uint32_t *in, uint32_t *out, int64_t m,
+// Tile size of the single-launch scan for m values: kThreads * lb_items(m) values.
+__host__ __device__ constexpr int lb_items(int64_t m) { return m <= 1500000 ? 16 : m <= 6000000 ? 32 : 64; }
+
+// HI32: the input is uint64 and the scan takes the high 32 bits of each value.
+template <int ITEMS, bool HI32>
+__global__ __launch_bounds__(kThreads) void k_scan_lb(const void *in_v, uint32_t *out, int64_t m,
                                                       unsigned long long *__restrict__ status,
                                                       uint32_t *__restrict__ ticket,
                                                       unsigned long long *__restrict__ total)
 {
+    constexpr int kT = kThreads * ITEMS;
     __shared__ uint32_t scratch[4];
     __shared__ uint32_t s_tile;
     __shared__ unsigned long long s_excl;
     if (threadIdx.x == 0) s_tile = atomicAdd(ticket, 1u);
     __syncthreads();
     const int64_t tile = s_tile;
-    const int64_t base = tile * kTile + (int64_t)threadIdx.x * kItems;
-    uint32_t v[kItems];
-    const bool full = base + kItems <= m;
-    if (full) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(in + base);
+    const int64_t base = tile * kT + (int64_t)threadIdx.x * ITEMS;
+    uint32_t v[ITEMS];
+    const bool full = base + ITEMS <= m;
+    if (HI32) {
+        const uint64_t *in = static_cast<const uint64_t *>(in_v);
+        if (full) {
+            const ulonglong2 *p = reinterpret_cast<const ulonglong2 *>(in + base);
 #pragma unroll
-        for (int k = 0; k < kItems / 4; ++k) {
-            const uint4 q = p[k];
-            v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
+            for (int k = 0; k < ITEMS / 2; ++k) {
+                const ulonglong2 q = p[k];
+                v[2 * k] = (uint32_t)(q.x >> 32); v[2 * k + 1] = (uint32_t)(q.y >> 32);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < ITEMS; ++k) v[k] = base + k < m ? (uint32_t)(in[base + k] >> 32) : 0u;
         }
     } else {
+        const uint32_t *in = static_cast<const uint32_t *>(in_v);
+        if (full) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(in + base);
 #pragma unroll
-        for (int k = 0; k < kItems; ++k) v[k] = base + k < m ? in[base + k] : 0u;
+            for (int k = 0; k < ITEMS / 4; ++k) {
+                const uint4 q = p[k];
+                v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < ITEMS; ++k) v[k] = base + k < m ? in[base + k] : 0u;
+        }
     }
     uint32_t sum = 0;
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) sum += v[k];
+    for (int k = 0; k < ITEMS; ++k) sum += v[k];
     uint32_t tot32;
     const uint32_t pre = block_exclusive_scan(sum, scratch, &tot32);
     const unsigned long long tot = tot32;
@@ -317,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_lb(const uint32_t *in, uint32
         if (lane == 0) {
             if (tile > 0) status_store(status + tile, kFlagIncl | (excl + tot));
             s_excl = excl;
-            if (total && (tile + 1) * kTile >= m) *total = excl + tot;   // the last tile
+            if (total && (tile + 1) * kT >= m) *total = excl + tot;   // the last tile
         }
     }
     __syncthreads();
@@ -325,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_scan_lb(const uint32_t *in, uint32
     if (full) {
         uint4 *p = reinterpret_cast<uint4 *>(out + base);
 #pragma unroll
-        for (int k = 0; k < kItems / 4; ++k) {
+        for (int k = 0; k < ITEMS / 4; ++k) {
             uint4 q;
             q.x = run; run += v[4 * k];
             q.y = run; run += v[4 * k + 1];
@@ -334,9 +373,26 @@ __global__ __launch_bounds__(kThreads) void k_scan_lb(const uint32_t *in, uint32
             p[k] = q;
         }
     } else {
-        for (int k = 0; k < kItems; ++k)
+        for (int k = 0; k < ITEMS; ++k)
             if (base + k < m) { out[base + k] = run; run += v[k]; }
     }
+}
+
+template <bool HI32>
+gs_status launch_scan_lb(const void *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
+                         unsigned long long *total, hipStream_t stream)
+{
+    if (m <= 0) return gsi::fail(GS_ERR_UNSUPPORTED, "scan of an empty array");
+    const int items = lb_items(m);
+    const unsigned grid = (unsigned)gsi::ceil_div(m, (int64_t)kThreads * items);
+    if (items == 16)
+        k_scan_lb<16, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total);
+    else if (items == 32)
+        k_scan_lb<32, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total);
+    else
+        k_scan_lb<64, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total);
+    GS_LAUNCH_CHECK("k_scan_lb");
+    return GS_OK;
 }
 
 __global__ void k_fill_i32(int32_t *__restrict__ p, int64_t n, int32_t value)
@@ -380,15 +436,19 @@ gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint3
 
 int64_t radix_hist_len(int64_t m) { return 256 * ceil_div(m > 0 ? m : 1, kRxTile); }
 
-int64_t lb_scan_tiles(int64_t m) { return ceil_div(m > 0 ? m : 1, kTile); }
+int64_t lb_scan_tiles(int64_t m) { return ceil_div(m > 0 ? m : 1, (int64_t)kThreads * lb_items(m)); }
 
 gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
                       unsigned long long *total, hipStream_t stream)
 {
-    if (m <= 0) return fail(GS_ERR_UNSUPPORTED, "scan of an empty array");
-    k_scan_lb<<<(unsigned)lb_scan_tiles(m), kThreads, 0, stream>>>(in, out, m, status, ticket, total);
-    GS_LAUNCH_CHECK("k_scan_lb");
-    return GS_OK;
+    return launch_scan_lb<false>(in, out, m, status, ticket, total, stream);
+}
+
+gs_status lb_scan_hi32(const uint64_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
+                       unsigned long long *total, hipStream_t stream)
+{
+    if (!aligned(in, 16)) return fail(GS_ERR_INVALID_ARGUMENT, "scan input must be 16-byte aligned");
+    return launch_scan_lb<true>(in, out, m, status, ticket, total, stream);
 }
 
 int64_t radix_scan_status_len(int64_t m, int bits)

@@ -26,8 +26,8 @@ def step_bytes_per_gaussian(sh_degree: int) -> int:
     """Everything this library keeps per Gaussian during a training step: parameters,
     gradients, Adam moments, the projected record (means2d 8, conic+opacity 16, colour 12,
     depth 4, radii 8), its 48-byte raster-ready copy, screen-space gradients (36) and the
-    binning's per-Gaussian buffers (36: depth keys and values twice, tile and quadrant
-    counts, emit offsets, depth rank, first gradient slot)."""
+    binning's per-Gaussian buffers (36: 32-bit depth keys and 64-bit values (tile count,
+    index) twice, quadrant-record counts, emit offsets, first gradient slot)."""
     return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 48 + 48 + 36 + 36
 
 

@@ -427,3 +427,27 @@ def test_train_step_composition():
     torch.cuda.synchronize()
     assert rel_l2(a.params.data.cpu().numpy(), b.params.data.cpu().numpy()) <= 1e-6
     assert a.frame.loss.item() > 0
+
+
+@pytest.mark.parametrize("name", ["ragged_sh1", "100k"])
+def test_ntrav_sum(name):
+    """The optional device sum of N_p equals the sum of the per-pixel counts, for a
+    16-byte aligned n_trav and for one that is not (an odd pixel count leaves a tail)."""
+    log(f"n_trav sum {name}")
+    sc = _scene(name)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    st = gpu_forward(sc, cam, rp)
+    c = B.camera_from(cam)
+    f = st.frame
+    want = int(f.n_trav.to(torch.int64).sum())
+    assert want > 0
+    tot = torch.zeros(1, dtype=torch.int64, device=DEV)
+    B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, rp, f.color, f.t_final, f.n_trav, tot)
+    buf = torch.full((cam.height * cam.width + 1,), -1, dtype=torch.int32, device=DEV)
+    shifted = buf[1:].view(cam.height, cam.width)   # 4 bytes past a 256-byte boundary
+    tot2 = torch.full((1,), 5, dtype=torch.int64, device=DEV)
+    B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, rp, f.color, f.t_final, shifted, tot2)
+    torch.cuda.synchronize()
+    assert torch.equal(shifted, f.n_trav)
+    assert int(tot) == want and int(tot2) == want + 5
