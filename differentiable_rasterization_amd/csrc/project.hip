@@ -547,12 +547,13 @@ __global__ __launch_bounds__(256) void k_grad_adam(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
     const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
-    const float4 *__restrict__ qgrad, float *__restrict__ grads2d, AdamSink out)
+    const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp, float *__restrict__ grads2d, AdamSink out)
 {
+    __shared__ gsr::SlotStage stage[4];
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
     float acc[9];
-    gsr::raw_slot_sums(hdr, qoff, qgrad, i, acc);
+    gsr::raw_slot_sums(hdr, qoff, qgrad, qstamp, i, n, stage[threadIdx.x >> 6], acc);
+    if (i >= n) return;
     project_bwd_one<DEG, true>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, acc,
                                grads2d, out);
 }
@@ -694,11 +695,12 @@ extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_proj
     const gsr::BinsHeader *hdr = reinterpret_cast<const gsr::BinsHeader *>(rb + L.hdr);
     const uint32_t *qoff = reinterpret_cast<const uint32_t *>(rb + L.qoff);
     const float4 *qg = reinterpret_cast<const float4 *>(rb + L.qgrad);
+    const uint2 *qs = reinterpret_cast<const uint2 *>(rb + L.qstamp);
     const CamD cd = make_cam(cam);
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
 #define GS_GA(D)                                                                                                   \
     k_grad_adam<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, cd, \
-                                               p->alpha_min, p->depth_lo, p->depth_hi, hdr, qoff, qg,             \
+                                               p->alpha_min, p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,         \
                                                grads2d, sink)
     switch (p->sh_degree) {
     case 0: GS_GA(0); break;

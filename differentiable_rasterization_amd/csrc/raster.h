@@ -20,10 +20,12 @@
 //                                 own slots qoff[g] .. qoff[g + 1], in the order of its
 //                                 entries and, within an entry, of the quadrants (qoff[n] =
 //                                 the number of quadrant records)
-//   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields and
-//                                 the stamp of the backward call that wrote them, padded to
-//                                 48 bytes), one slot per quadrant record, at the slot index
-//                                 its record carries
+//   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
+//                                 padded to 48 bytes), one slot per quadrant record, at the
+//                                 slot index its record carries
+//   qstamp [2 * capacity] uint2   the stamp (epoch, ~epoch) of the backward call that wrote
+//                                 each slot, kept apart from the slots so that the
+//                                 per-Gaussian sums read only the slots that were written
 //
 // Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
 // (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of records with
@@ -53,6 +55,7 @@ struct Rec {
 };
 constexpr int kRecF4 = 3;   // float4 words per record
 constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
+constexpr int kStampWords = 2;  // uint32 words per slot stamp
 // The record array has kRecPad spare records before and after the lists, so that a batch
 // of consecutive records, and the batch after it, can always be loaded from one base
 // address (records outside the lists are loaded but never used).
@@ -110,9 +113,9 @@ __device__ __forceinline__ uint32_t quad_mask(float u, float v, float A, float B
 // Counts of the last sort, in device memory (the first bytes of the raster buffer).  When
 // the lists did not fit (ok == 0) the sort leaves every tile list empty and the per-Gaussian
 // gradient reduction writes zeros.  epoch: advanced by every backward call (any start
-// value); the backward stamps each gradient slot it writes with (epoch, ~epoch), and the
-// per-Gaussian sums take only slots stamped by the latest call, so slots of records no
-// pixel reached are never written (a stale or never-written slot matches the stamp with
+// value); the backward stamps each gradient slot it writes with (epoch, ~epoch) in qstamp,
+// and the per-Gaussian sums take only slots stamped by the latest call, so slots of records
+// no pixel reached are never written nor read (a stale or never-written stamp matches with
 // probability 2^-64).
 struct BinsHeader {
     unsigned long long K, Q;   // tile entries and (entry, quadrant) records
@@ -129,7 +132,7 @@ __device__ __forceinline__ uint32_t quad_mask_rec(const float4 &p0, const float4
 }
 
 struct RasterLayout {
-    size_t hdr, qrec, bitmap, wpre, order, qoff, qgrad, bytes;
+    size_t hdr, qrec, bitmap, wpre, order, qoff, qgrad, qstamp, bytes;
     int64_t cap, words;
 };
 
@@ -149,6 +152,7 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);
     L.qoff = o;   o += align256((nn + 1) * 4);
     L.qgrad = o;  o += align256(q4 * kGradSlot * 4);
+    L.qstamp = o; o += align256(q4 * kStampWords * 4);
     L.bytes = o;
     return L;
 }
@@ -157,31 +161,55 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
 // slots qoff[g] .. qoff[g + 1], added in order (none when the lists did not fit the
 // capacity).  The slots hold per-record sums of the pixel moments S0 = dpower, Sx, Sy,
 // Sxx, Sxy, Syy and the colour terms.  Returns whether g has any slot.
+//
+// A wave's 64 consecutive Gaussians own one contiguous run of slots.  The wave reads that
+// run 64 slots at a time, coalesced, into its staging area in LDS (the stamps first; the
+// data of a slot only if the latest backward call wrote it), and each lane then adds its
+// own slots from LDS, in slot order.  All 64 lanes of the wave must call it; a lane past
+// the last Gaussian passes g >= n (an empty range).
+struct SlotStage {
+    float4 d[3][64];   // d[k][l]: float4 k of slot c0 + l of the current chunk
+    uint32_t ok[64];   // slot c0 + l was written by the latest backward call
+};
+
 __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
-                                              const float4 *__restrict__ qgrad, int64_t g, float (&acc)[9])
+                                              const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp,
+                                              int64_t g, int64_t n, SlotStage &S, float (&acc)[9])
 {
+    const int lane = threadIdx.x & 63;
     const bool ok = hdr->ok != 0u;
     const uint32_t epoch = hdr->epoch;
-    const uint32_t s0 = ok ? qoff[g] : 0u, s1 = ok ? qoff[g + 1] : 0u;
+    const int64_t gc = g < n ? g : n;
+    const uint32_t s0 = ok ? qoff[gc] : 0u, s1 = ok && g < n ? qoff[g + 1] : s0;
+    const uint32_t w0 = __shfl(s0, 0, 64), w1 = __shfl(s1, 63, 64);   // the wave's run of slots
 #pragma unroll
     for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
-    // slots the latest backward call did not write hold nothing of this step
-    auto add = [&](const float4 &a, const float4 &b, const float4 &c) {
-        if (__float_as_uint(c.y) != epoch || __float_as_uint(c.z) != ~epoch) return;
-        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-        acc[8] += c.x;
-    };
-    uint32_t j = s0;
-    for (; j + 2 <= s1; j += 2) {   // two slots' loads in flight at once; summed in slot order
-        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
-        const float4 a0 = sl[0], b0 = sl[1], c0 = sl[2], a1 = sl[3], b1 = sl[4], c1 = sl[5];
-        add(a0, b0, c0);
-        add(a1, b1, c1);
-    }
-    if (j < s1) {
-        const float4 *sl = qgrad + (size_t)j * (kGradSlot / 4);
-        add(sl[0], sl[1], sl[2]);
+    for (uint32_t c0 = w0; c0 < w1; c0 += 64u) {
+        const uint32_t sl = c0 + (uint32_t)lane;
+        bool w = false;
+        if (sl < w1) {
+            const uint2 t = qstamp[sl];
+            w = t.x == epoch && t.y == ~epoch;   // slots the latest backward call did not write: not read
+            if (w) {
+                const float4 *p = qgrad + (size_t)sl * (kGradSlot / 4);
+                S.d[0][lane] = p[0];
+                S.d[1][lane] = p[1];
+                S.d[2][lane] = p[2];
+            }
+        }
+        S.ok[lane] = w ? 1u : 0u;
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t lo = s0 > c0 ? s0 : c0, hi = s1 < c0 + 64u ? s1 : c0 + 64u;
+        for (uint32_t x = lo; x < hi; ++x) {
+            const uint32_t l = x - c0;
+            if (S.ok[l]) {
+                const float4 a = S.d[0][l], b = S.d[1][l], c = S.d[2][l];
+                acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+                acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+                acc[8] += c.x;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
     }
     return s1 > s0;
 }
@@ -207,14 +235,15 @@ __device__ __forceinline__ void moments_to_grads(const float (&acc)[9], float a,
 }
 
 // Both steps, the record read from rec[g]; a Gaussian without records (culled) gets zeros
-// and its record is not read.
+// and its record is not read.  Called by all 64 lanes of the wave (see raw_slot_sums).
 __device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
-                                          const float4 *__restrict__ qgrad, const float4 *__restrict__ rec, int64_t g,
+                                          const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp,
+                                          const float4 *__restrict__ rec, int64_t g, int64_t n, SlotStage &S,
                                           float (&out)[9])
 {
     float acc[9];
     float a = 0.0f, b = 0.0f, c = 0.0f, l = 0.0f;
-    if (raw_slot_sums(hdr, qoff, qgrad, g, acc)) {
+    if (raw_slot_sums(hdr, qoff, qgrad, qstamp, g, n, S, acc)) {
         const float4 p0 = rec[kRecF4 * (size_t)g], p1 = rec[kRecF4 * (size_t)g + 1];
         a = p0.z; b = p0.w; c = p1.x; l = p1.y;
     }

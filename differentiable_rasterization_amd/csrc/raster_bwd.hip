@@ -122,7 +122,8 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
                                                    const float *__restrict__ color, const float *__restrict__ t_final,
                                                    const int32_t *__restrict__ n_trav, const float *__restrict__ dL_dc,
                                                    const float *__restrict__ dL_dt,
-                                                   const BinsHeader *__restrict__ hdr, float *__restrict__ qgrad)
+                                                   const BinsHeader *__restrict__ hdr, float *__restrict__ qgrad,
+                                                   uint32_t *__restrict__ qstamp)
 {
     int tidx, q;
     raster_block(tidx, q);
@@ -155,11 +156,11 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const uint32_t epoch = hdr->epoch;
     const int row = lane >> 4, nl = lane & 15;
     // the reduced field each lane of a row holds (reduce_4x9): even lanes hold fields 0-7,
-    // lane 1 field 8; lanes 3 and 5 write the stamp (epoch, ~epoch) into words 9 and 10
-    const int my_field = nl == 1 ? 8 : nl == 3 ? 9 : nl == 5 ? 10
-                                     : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
-    const bool lane_writes = (nl & 1) == 0 || nl == 1 || nl == 3 || nl == 5;
-    const float stamp = __uint_as_float(nl == 3 ? epoch : ~epoch);
+    // lane 1 field 8; lanes 3 and 5 write the slot's stamp (epoch, ~epoch)
+    const bool stamp_lane = nl == 3 || nl == 5;
+    const int my_field = nl == 1 ? 8 : stamp_lane ? (nl == 5) : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
+    const bool lane_writes = (nl & 1) == 0 || nl == 1 || stamp_lane;
+    const uint32_t stamp = nl == 3 ? epoch : ~epoch;
     float Tr = 1.0f;
     // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
     uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
@@ -220,13 +221,14 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         // gradient slot of the batch's record e = row (record jt + e); lane n writes field
         // my_field (see reduce_4x9)
         const uint32_t my_slot = __float_as_uint(by_row(row, slot[0], slot[1], slot[2], slot[3]));
-        float *dst = qgrad + (size_t)my_slot * kGradSlot + my_field;
+        uint32_t *dst = (stamp_lane ? qstamp + (size_t)my_slot * kStampWords
+                                    : reinterpret_cast<uint32_t *>(qgrad) + (size_t)my_slot * kGradSlot) + my_field;
         const bool writer = (uint32_t)row < cnt && lane_writes;
         jt += cnt;
         if (__ballot(any) == 0) continue;   // no pixel takes these records: slots left unstamped
         float fz, t8;
         reduce_4x9(v, nl, fz, t8);
-        if (writer) *dst = nl == 1 ? t8 : (nl == 3 || nl == 5) ? stamp : fz;
+        if (writer) *dst = stamp_lane ? stamp : __float_as_uint(nl == 1 ? t8 : fz);
     }
     sink ^= pend;
     asm volatile("" ::"v"(sink));
@@ -242,13 +244,15 @@ __global__ void k_new_epoch(BinsHeader *__restrict__ hdr) { hdr->epoch = hdr->ep
 // so that the stores coalesce.
 __global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restrict__ hdr,
                                                      const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
+                                                     const uint2 *__restrict__ qstamp,
                                                      const float4 *__restrict__ rec, int64_t n,
                                                      float *__restrict__ grads2d)
 {
+    __shared__ SlotStage stage[4];
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= n) return;
     float acc[kFields];
-    sum_slots(hdr, qoff, qgrad, rec, g, acc);
+    sum_slots(hdr, qoff, qgrad, qstamp, rec, g, n, stage[threadIdx.x >> 6], acc);
+    if (g >= n) return;
 #pragma unroll
     for (int f = 0; f < kFields; ++f) grads2d[(size_t)f * n + g] = acc[f];
 }
@@ -282,6 +286,7 @@ extern "C" gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins
     const uint64_t *bm = reinterpret_cast<const uint64_t *>(rb + L.bitmap);
     const uint32_t *wp = reinterpret_cast<const uint32_t *>(rb + L.wpre);
     float *qg = reinterpret_cast<float *>(rb + L.qgrad);
+    uint32_t *qs = reinterpret_cast<uint32_t *>(rb + L.qstamp);
     const unsigned grid = (unsigned)raster_grid(T);
     BinsHeader *hdr = reinterpret_cast<BinsHeader *>(rb + L.hdr);
     k_new_epoch<<<1, 1, 0, stream>>>(hdr);
@@ -289,11 +294,11 @@ extern "C" gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins
     if (dL_dt)
         k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
                                                     cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
-                                                    n_trav, dL_dcolor, dL_dt, hdr, qg);
+                                                    n_trav, dL_dcolor, dL_dt, hdr, qg, qs);
     else
         k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
                                                      cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
-                                                     n_trav, dL_dcolor, nullptr, hdr, qg);
+                                                     n_trav, dL_dcolor, nullptr, hdr, qg, qs);
     GS_LAUNCH_CHECK("k_raster_bwd");
     return GS_OK;
 }
@@ -318,7 +323,8 @@ extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_projected
         const char *rb = static_cast<const char *>(bins->raster);
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
             reinterpret_cast<const BinsHeader *>(rb + L.hdr), reinterpret_cast<const uint32_t *>(rb + L.qoff),
-            reinterpret_cast<const float4 *>(rb + L.qgrad), reinterpret_cast<const float4 *>(proj->rec), n, grads2d);
+            reinterpret_cast<const float4 *>(rb + L.qgrad), reinterpret_cast<const uint2 *>(rb + L.qstamp),
+            reinterpret_cast<const float4 *>(proj->rec), n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }
     if (grads3d) return launch_project_bwd(g, cam, p, grads2d, grads3d, stream);

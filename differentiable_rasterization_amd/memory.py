@@ -33,9 +33,10 @@ def step_bytes_per_gaussian(sh_degree: int) -> int:
 
 def step_bytes_per_intersection() -> int:
     """Intersection lists: ids (4); the raster-ready lists with room for two 8x8-quadrant
-    records per entry (2 x 48) and their gradient slots (2 x 48) and quadrant bits (1); and
-    the sort workspace's key, value, Gaussian and first-slot buffers (24)."""
-    return 4 + 2 * (48 + 48) + 1 + 24
+    records per entry (2 x 48), their gradient slots (2 x 48) and slot stamps (2 x 8) and
+    quadrant bits (1); and the sort workspace's key, value, Gaussian and first-slot buffers
+    (24)."""
+    return 4 + 2 * (48 + 48 + 8) + 1 + 24
 
 
 def max_gaussians(hbm_bytes: float, sh_degree: int, adam: bool = True) -> int:
