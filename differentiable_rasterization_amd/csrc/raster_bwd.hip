@@ -156,11 +156,11 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const uint32_t epoch = hdr->epoch;
     const int row = lane >> 4, nl = lane & 15;
     // the reduced field each lane of a row holds (reduce_4x9): even lanes hold fields 0-7,
-    // lane 1 field 8; lanes 3 and 5 write the slot's stamp (epoch, ~epoch)
-    const bool stamp_lane = nl == 3 || nl == 5;
-    const int my_field = nl == 1 ? 8 : stamp_lane ? (nl == 5) : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
+    // lane 1 field 8; lane 3 writes the slot's stamp (epoch, ~epoch)
+    const bool stamp_lane = nl == 3;
+    const int my_field = nl == 1 ? 8 : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
     const bool lane_writes = (nl & 1) == 0 || nl == 1 || stamp_lane;
-    const uint32_t stamp = nl == 3 ? epoch : ~epoch;
+    const uint2 stamp = make_uint2(epoch, ~epoch);
     float Tr = 1.0f;
     // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
     uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
@@ -221,14 +221,19 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
         // gradient slot of the batch's record e = row (record jt + e); lane n writes field
         // my_field (see reduce_4x9)
         const uint32_t my_slot = __float_as_uint(by_row(row, slot[0], slot[1], slot[2], slot[3]));
-        uint32_t *dst = (stamp_lane ? qstamp + (size_t)my_slot * kStampWords
-                                    : reinterpret_cast<uint32_t *>(qgrad) + (size_t)my_slot * kGradSlot) + my_field;
+        float *dst = qgrad + (size_t)my_slot * kGradSlot + my_field;
+        uint2 *dst_stamp = reinterpret_cast<uint2 *>(qstamp) + my_slot;
         const bool writer = (uint32_t)row < cnt && lane_writes;
         jt += cnt;
         if (__ballot(any) == 0) continue;   // no pixel takes these records: slots left unstamped
         float fz, t8;
         reduce_4x9(v, nl, fz, t8);
-        if (writer) *dst = stamp_lane ? stamp : __float_as_uint(nl == 1 ? t8 : fz);
+        if (writer) {
+            if (stamp_lane)
+                *dst_stamp = stamp;
+            else
+                *dst = nl == 1 ? t8 : fz;
+        }
     }
     sink ^= pend;
     asm volatile("" ::"v"(sink));
