@@ -3,10 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m|100k|10m|tiny] [--no-cpu-baseline]
                     [--cpu-rows R] [--copy-calibration-mib M]
 
-A step is one training iteration on one view: gs_project -> gs_bin_sort ->
-gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd_partials -> gs_grad_aggregate_adam (the
-per-Gaussian gradient sum, projection backward and Adam in one pass; --unfused runs
-gs_grad_aggregate, gs_project_bwd and gs_adam_step instead), on seeded synthetic data
+A step is one training iteration on one view: projection -> gs_bin_sort ->
+gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd_partials -> gs_grad_aggregate_adam_project
+(the per-Gaussian gradient sum, projection backward, Adam and the projection of the
+updated Gaussians for the next step's view in one pass, so each step's projection is done
+by the step before it; the first step's records come from gs_project before the warm-up).
+--unfused runs gs_project at the start of each step and gs_grad_aggregate,
+gs_project_bwd and gs_adam_step at its end instead.  The data are seeded, synthetic and
 already resident in HBM.  The default workload is 1M
 Gaussians (SH degree 3, 64 clusters in a 20 m cube) at 1920x1080 with four
 cameras on a sphere of radius 25; steps cycle through the four views.
@@ -16,9 +19,9 @@ number of list entries each pixel composites, N_p of Eq. 1 in ByteSplat section 
 per second of whole training step; ms_per_step = train-step milliseconds.  Per-kernel
 times come from HIP events recorded on the stream the kernels run on.
 
-roofline: the dominant kernel, k_raster_bwd (one launch per step), is bound by VALU
-arithmetic; its algorithmic work is FLOP_PER_PAIR["raster_bwd"] floating-point
-operations per Gaussian-pixel pair.  roofline.traffic is the HBM traffic of one launch
+roofline: the longer of k_raster_bwd (bound by VALU arithmetic; its algorithmic work is
+FLOP_PER_PAIR["raster_bwd"] floating-point operations per Gaussian-pixel pair) and
+k_grad_adam (bound by HBM; hbm_bytes), one launch each per step; roofline_next the other.  roofline.traffic is the HBM traffic of one launch
 from the stored counter summary (profiles/), or null if the kernel's sources changed
 since those counters were taken.  --copy-calibration-mib runs a plain copy-like kernel of
 known size before the timed steps, for the counter runs that normalise FETCH_SIZE and
@@ -50,7 +53,7 @@ FLOP_PER_PAIR = {"raster_fwd": 27, "raster_bwd": 63}
 # stored counter traffic of the kernels that can dominate the step (1M / 1080p workload)
 TRAFFIC_SUMMARY = {"k_raster_bwd": os.path.join(ROOT, "profiles", "k_raster_bwd_1m_1080p_traffic.txt"),
                    "k_grad_adam": os.path.join(ROOT, "profiles", "k_grad_adam_1m_1080p_traffic.txt")}
-KERNEL_OF = {"raster_bwd": "k_raster_bwd", "grad_adam": "k_grad_adam"}
+KERNEL_OF = {"raster_bwd": "k_raster_bwd", "grad_adam": "k_grad_adam", "grad_adam_project": "k_grad_adam"}
 
 
 def parse():
@@ -98,6 +101,8 @@ def hbm_bytes(kernel, n, n_vis, k_sh, n_isect, n_px):
         return 36 * n_isect + 36 * n                                # one partial per (tile, Gaussian); grads2d
     if kernel == "grad_adam":                                       # partials; p, m, v read and written
         return 36 * n_isect + n * (11 + 3 * k_sh) * 24
+    if kernel == "grad_adam_project":                               # the same + the next view's records
+        return 36 * n_isect + n * (11 + 3 * k_sh) * 24 + n_vis * 96 + (n - n_vis) * 12
     return None
 
 
@@ -151,18 +156,18 @@ def main():
 
     if args.unfused:
         names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
-    else:
-        names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_adam"]
+    else:   # the projection of each step runs in the previous step's last pass
+        names = ["bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_adam_project"]
     g = params.gaussians()
 
     # the calls timed inside the timed steps: the two kernels that can dominate the step
-    timed_calls = [names.index(nm) for nm in ("raster_bwd", "grad_adam") if nm in names]
+    timed_calls = [names.index(nm) for nm in ("raster_bwd", "grad_adam", "grad_adam_project") if nm in names]
     timed_marks = set(timed_calls) | {k + 1 for k in timed_calls}
 
     def one_step(i, ev=None, counts=None, every_call=False):
         """ev: HIP events, recorded around the dominant kernel's call only (each record costs
         the stream a few microseconds), or around every call if every_call."""
-        c, t = cams[i % nviews], targets[i % nviews]
+        c, t, nc = cams[i % nviews], targets[i % nviews], cams[(i + 1) % nviews]
         if ev is None:
             rec = lambda k: None
         elif every_call:
@@ -170,30 +175,38 @@ def main():
         else:
             rec = lambda k: ev[k].record() if k in timed_marks else None
         f = st.frame
-        rec(0)
-        B.gs_project(g, c, st.raster, st.proj.abi())
-        rec(1)
+        k = 0
+        rec(k)
+        if args.unfused:
+            B.gs_project(g, c, st.raster, st.proj.abi())
+            k += 1
+            rec(k)
         if counts is None:
             st.bins.sort(st.proj, c, st.raster)
         else:   # no host wait inside the step; the counts are checked after the timed steps
             st.bins.sort_async(st.proj, c, st.raster, counts)
-        rec(2)
+        rec(k + 1)
         B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.n_trav_sum)
-        rec(3)
+        rec(k + 2)
         B.gs_loss_l1(f.color, t, f.n_px, f.loss, f.dL_dcolor, f.loss_ws)
-        rec(4)
+        rec(k + 3)
         B.gs_raster_bwd_partials(g, st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.dL_dcolor, None)
-        rec(5)
+        rec(k + 4)
         if args.unfused:
             B.gs_grad_aggregate(g, st.proj.abi(), st.bins.abi(), c, st.raster, st.grads2d, None)
-            rec(6)
+            rec(k + 5)
             st.backward_project(c)
-            rec(7)
+            rec(k + 6)
             st.adam()
-            rec(8)
-        else:   # per-Gaussian sum, projection backward and Adam in one pass
-            st.aggregate_adam(c)
-            rec(6)
+            rec(k + 7)
+        else:   # per-Gaussian sum, projection backward, Adam and the next view's projection in one pass
+            st.aggregate_adam_project(c, nc)
+            rec(k + 5)
+
+    def project_for(i):
+        """The records step i starts from (the fused pass projects for the step after it)."""
+        if not args.unfused:
+            B.gs_project(g, cams[i % nviews], st.raster, st.proj.abi())
 
     if args.copy_calibration_mib > 0:
         # a copy-like kernel of known size (reads and writes M MiB) for counter normalisation
@@ -203,6 +216,7 @@ def main():
             torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    project_for(0)
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
@@ -230,6 +244,7 @@ def main():
     per_kernel, step_ms = dict(timed_ms), None
     if not args.no_breakdown:
         # untimed: the same steps again with an event around every call
+        project_for(args.warmup)
         ev2 = new_events()
         for i in range(args.steps):
             one_step(args.warmup + i, ev2[i], counts[i], every_call=True)
@@ -281,7 +296,9 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
-                   "views": nviews, "step": "one view: fwd + L1 + bwd + Adam"},
+                   "views": nviews,
+                   "step": "one view: projection + fwd + L1 + bwd + Adam" + (
+                       "" if args.unfused else " (each view's projection fused into the previous step's Adam pass)")},
         "roofline": roof,
         "roofline_next": roof_next,
         # from the untimed pass with an event around every call
@@ -296,7 +313,7 @@ def main():
         # and the per-pixel backward with its per-quadrant sums)
         "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]) * 1e-3), 1)
         if "raster_fwd" in per_kernel else None,
-        "kernels_note": "raster_bwd and grad_adam from events in the timed steps; the others from an untimed "
+        "kernels_note": "raster_bwd and grad_adam(_project) from events in the timed steps; the others from an untimed "
                         "pass of the same steps with an event around every call",
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP = range(5)
 TILE = 16
 EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_bin_sort_async", "gs_raster_fwd", "gs_loss_workspace_bytes",
-            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
+            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_last_error")
 
 
@@ -105,6 +105,9 @@ _SIGS = {
     "gs_grad_aggregate_adam": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp,
                                       _P(ParamGrads),
                                       _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32, _f32, _vp]),
+    "gs_grad_aggregate_adam_project": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams),
+                                              _vp, _P(ParamGrads), _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32,
+                                              _f32, _P(Camera), _P(Projected), _vp]),
     "gs_project_bwd": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
     "gs_adam_step": (_i32, [_P(AdamGroup), _i32, _i32, _f32, _f32, _f32, _vp]),
     "gs_composite_over": (_i32, [_P(_vp), _P(_vp), _i32, _i64, _f32, _vp, _vp, _vp]),
@@ -255,6 +258,15 @@ def gs_grad_aggregate_adam(g: Gaussians, proj: Projected, b: Bins, cam: Camera, 
                                        ctypes.byref(p),
                                        _ptr(grads2d), ctypes.byref(m), ctypes.byref(v), ctypes.byref(lr), step, beta1,
                                        beta2, eps, _stream(stream)))
+
+
+def gs_grad_aggregate_adam_project(g: Gaussians, proj: Projected, b: Bins, cam: Camera, p: RasterParams, grads2d,
+                                   m: ParamGrads, v: ParamGrads, lr: "AdamLrs", step, beta1, beta2, eps,
+                                   next_cam: Camera, next_proj: Projected, stream=None):
+    _check(_lib.gs_grad_aggregate_adam_project(ctypes.byref(g), ctypes.byref(proj), ctypes.byref(b),
+                                               ctypes.byref(cam), ctypes.byref(p), _ptr(grads2d), ctypes.byref(m),
+                                               ctypes.byref(v), ctypes.byref(lr), step, beta1, beta2, eps,
+                                               ctypes.byref(next_cam), ctypes.byref(next_proj), _stream(stream)))
 
 
 def gs_project_bwd(g: Gaussians, cam: Camera, p: RasterParams, grads2d, grads3d: ParamGrads, stream=None):

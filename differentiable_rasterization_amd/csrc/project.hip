@@ -227,52 +227,91 @@ __device__ __forceinline__ RecConic rec_conic(const Proj &P)
     return {(float)(-0.5 * kL2e * P.A), (float)(-kL2e * P.B), (float)(-0.5 * kL2e * P.C), (float)log2(o32)};
 }
 
+template <int K>
+struct Params1 {   // one Gaussian's parameters as loaded
+    float means[3], ls[3], q[4], logit, sh[3 * K];
+};
+
+template <int K>
+__device__ __forceinline__ void load_params(const float *__restrict__ means, const float *__restrict__ log_scales,
+                                            const float *__restrict__ quats, const float *__restrict__ logits,
+                                            const float *__restrict__ sh, int64_t n, int64_t i, Params1<K> &prm)
+{
+    prm.means[0] = means[i]; prm.means[1] = means[n + i]; prm.means[2] = means[2 * n + i];
+    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[n + i]; prm.ls[2] = log_scales[2 * n + i];
+    prm.q[0] = quats[i]; prm.q[1] = quats[n + i]; prm.q[2] = quats[2 * n + i]; prm.q[3] = quats[3 * n + i];
+    prm.logit = logits[i];
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) prm.sh[k] = sh[(int64_t)k * n + i];
+}
+
+template <int K>
+__device__ __forceinline__ bool sh_finite(const Params1<K> &prm)
+{
+    bool f = true;
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) f = f && __builtin_isfinite(prm.sh[k]);
+    return f;
+}
+
+// The projection's outputs (gs_projected).
+struct ProjOut {
+    float2 *means2d;
+    float4 *conic_o;
+    float *color, *depth;
+    int2 *radii;
+    float4 *rec;
+};
+
+// Projects Gaussian i with parameters prm and stores its projected record: the one
+// definition both gs_project and the projection fused into the end of a step use.
 template <int DEG>
-__global__ __launch_bounds__(256) void k_project(const float *__restrict__ means, const float *__restrict__ log_scales,
-                                                 const float *__restrict__ quats, const float *__restrict__ logits,
-                                                 const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
-                                                 float depth_lo, float depth_hi, float2 *__restrict__ means2d,
-                                                 float4 *__restrict__ conic_o, float *__restrict__ color,
-                                                 float *__restrict__ depth, int2 *__restrict__ radii,
-                                                 float4 *__restrict__ rec)
+__device__ __forceinline__ void project_store(const Params1<(DEG + 1) * (DEG + 1)> &prm, const CamD &cam,
+                                              float alpha_min, float depth_lo, float depth_hi, int64_t i,
+                                              const ProjOut &po)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const float fmx = means[i], fmy = means[n + i], fmz = means[2 * n + i];
-    float shc[3 * K];
-    bool shf = true;
-#pragma unroll
-    for (int k = 0; k < 3 * K; ++k) {
-        shc[k] = sh[(int64_t)k * n + i];
-        shf = shf && __builtin_isfinite(shc[k]);
-    }
+    const bool shf = sh_finite(prm);
     Proj P;
-    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, log_scales[i], log_scales[n + i], log_scales[2 * n + i],
-                 quats[i], quats[n + i], quats[2 * n + i], quats[3 * n + i], logits[i], shf, (double)alpha_min,
-                 depth_lo, depth_hi, P);
-    depth[i] = P.key;
-    radii[i] = make_int2(P.rx, P.ry);
+    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
+    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
+                 prm.q[3], prm.logit, shf, (double)alpha_min, depth_lo, depth_hi, P);
+    po.depth[i] = P.key;
+    po.radii[i] = make_int2(P.rx, P.ry);
     if (!P.vis) return;
-    means2d[i] = make_float2((float)P.u, (float)P.v);
-    conic_o[i] = make_float4((float)P.A, (float)P.B, (float)P.C, (float)P.o);
+    po.means2d[i] = make_float2((float)P.u, (float)P.v);
+    po.conic_o[i] = make_float4((float)P.A, (float)P.B, (float)P.C, (float)P.o);
     float Y[K];
     sh_basis<DEG>(P.dir[0], P.dir[1], P.dir[2], Y);
     float r = 0.0f, g = 0.0f, b = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        r = fmaf(shc[3 * k + 0], Y[k], r);
-        g = fmaf(shc[3 * k + 1], Y[k], g);
-        b = fmaf(shc[3 * k + 2], Y[k], b);
+        r = fmaf(prm.sh[3 * k + 0], Y[k], r);
+        g = fmaf(prm.sh[3 * k + 1], Y[k], g);
+        b = fmaf(prm.sh[3 * k + 2], Y[k], b);
     }
-    color[3 * i + 0] = r;
-    color[3 * i + 1] = g;
-    color[3 * i + 2] = b;
+    po.color[3 * i + 0] = r;
+    po.color[3 * i + 1] = g;
+    po.color[3 * i + 2] = b;
     // raster-ready copy: conic scaled for exp2, log2 of the stored opacity
     const RecConic rc = rec_conic(P);
-    rec[3 * i + 0] = make_float4((float)P.u, (float)P.v, rc.a, rc.b);
-    rec[3 * i + 1] = make_float4(rc.c, rc.l, r, g);
-    rec[3 * i + 2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(P.rx), __int_as_float(P.ry));
+    po.rec[3 * i + 0] = make_float4((float)P.u, (float)P.v, rc.a, rc.b);
+    po.rec[3 * i + 1] = make_float4(rc.c, rc.l, r, g);
+    po.rec[3 * i + 2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(P.rx), __int_as_float(P.ry));
+}
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project(const float *__restrict__ means, const float *__restrict__ log_scales,
+                                                 const float *__restrict__ quats, const float *__restrict__ logits,
+                                                 const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+                                                 float depth_lo, float depth_hi, ProjOut po)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    Params1<K> prm;
+    load_params(means, log_scales, quats, logits, sh, n, i, prm);
+    project_store<DEG>(prm, cam, alpha_min, depth_lo, depth_hi, i, po);
 }
 
 // Backward through projection and colour evaluation (ByteSplat, section 2.1: the
@@ -287,11 +326,6 @@ struct Grad3 {
     float means[3], ls[3], q[4], logit;
     float Y[K], gc[3];
     __device__ float sh(int plane) const { return Y[plane / 3] * gc[plane % 3]; }
-};
-
-template <int K>
-struct Params1 {   // one Gaussian's parameters as loaded
-    float means[3], ls[3], q[4], logit, sh[3 * K];
 };
 
 struct GradSink {
@@ -309,6 +343,15 @@ struct GradSink {
     }
 };
 
+// Planes per chunk of the SH update: the largest divisor of the plane count up to 12 (3,
+// 12, 9 and 12 planes for degrees 0-3), so that the chunks tile the planes exactly.
+constexpr int sh_chunk(int planes)
+{
+    for (int c = 12; c > 1; --c)
+        if (planes % c == 0) return c;
+    return 1;
+}
+
 // Adam over the parameter scalars of one Gaussian, a chunk of planes at a time: every
 // moment load of a chunk is issued before any store, so the loads overlap.
 struct AdamSink {
@@ -317,8 +360,9 @@ struct AdamSink {
     float st[6];                 // lr / (1 - b1^t): means, log_scales, quats, opacity, sh DC, sh rest
     float b1, b2, inv_bc2, eps;
 
+    // pv: the parameter values in, the updated values out
     template <int N>
-    __device__ void chunk(const int (&grp)[N], const int (&plane)[N], const float (&g)[N], const float (&pv)[N],
+    __device__ void chunk(const int (&grp)[N], const int (&plane)[N], const float (&g)[N], float (&pv)[N],
                           const float (&step)[N], int64_t i) const
     {
         float mv[N], vv[N];
@@ -330,29 +374,35 @@ struct AdamSink {
         }
 #pragma unroll
         for (int c = 0; c < N; ++c) {
-            float pc = pv[c];
-            gsd::adam_update(pc, g[c], mv[c], vv[c], b1, b2, inv_bc2, eps, step[c]);
+            gsd::adam_update(pv[c], g[c], mv[c], vv[c], b1, b2, inv_bc2, eps, step[c]);
             const int64_t idx = (int64_t)plane[c] * n + i;
-            __builtin_nontemporal_store(pc, p[grp[c]] + idx);
+            __builtin_nontemporal_store(pv[c], p[grp[c]] + idx);
             __builtin_nontemporal_store(mv[c], m[grp[c]] + idx);
             __builtin_nontemporal_store(vv[c], v[grp[c]] + idx);
         }
     }
 
+    // Updates and stores every parameter scalar of Gaussian i; P holds the updated values
+    // afterwards.
     template <int K>
-    __device__ void flush(int64_t i, const Grad3<K> &g, const Params1<K> &P) const
+    __device__ void flush(int64_t i, const Grad3<K> &g, Params1<K> &P) const
     {
         {   // means, log_scales, quats, opacity: 11 scalars
             const int grp[11] = {0, 0, 0, 1, 1, 1, 2, 2, 2, 2, 3};
             const int pl[11] = {0, 1, 2, 0, 1, 2, 0, 1, 2, 3, 0};
             const float gg[11] = {g.means[0], g.means[1], g.means[2], g.ls[0], g.ls[1], g.ls[2],
                                   g.q[0], g.q[1], g.q[2], g.q[3], g.logit};
-            const float pv[11] = {P.means[0], P.means[1], P.means[2], P.ls[0], P.ls[1], P.ls[2],
-                                  P.q[0], P.q[1], P.q[2], P.q[3], P.logit};
+            float pv[11] = {P.means[0], P.means[1], P.means[2], P.ls[0], P.ls[1], P.ls[2],
+                            P.q[0], P.q[1], P.q[2], P.q[3], P.logit};
             const float sp[11] = {st[0], st[0], st[0], st[1], st[1], st[1], st[2], st[2], st[2], st[2], st[3]};
             chunk(grp, pl, gg, pv, sp, i);
+            P.means[0] = pv[0]; P.means[1] = pv[1]; P.means[2] = pv[2];
+            P.ls[0] = pv[3]; P.ls[1] = pv[4]; P.ls[2] = pv[5];
+            P.q[0] = pv[6]; P.q[1] = pv[7]; P.q[2] = pv[8]; P.q[3] = pv[9];
+            P.logit = pv[10];
         }
-        constexpr int kChunk = 3 * K < 12 ? 3 * K : 12;
+        constexpr int kChunk = sh_chunk(3 * K);
+        static_assert((3 * K) % kChunk == 0, "the chunks must tile the SH planes exactly");
 #pragma unroll
         for (int c0 = 0; c0 < 3 * K; c0 += kChunk) {
             int grp[kChunk], pl[kChunk];
@@ -366,6 +416,8 @@ struct AdamSink {
                 sp[c] = c0 + c < 3 ? st[4] : st[5];
             }
             chunk(grp, pl, gg, pv, sp, i);
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) P.sh[c0 + c] = pv[c];
         }
     }
 };
@@ -476,25 +528,20 @@ __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam
 // in: the screen-space gradients (u, v, A, B, C, o, r, g, b), or with RAW the per-Gaussian
 // moment sums of the raster backward, turned into those gradients here with the record's
 // conic and opacity as the forward pass rounded them (and stored to grads2d [9][n] if given).
-template <int DEG, bool RAW, class Sink>
+// With NEXT (an AdamSink, which leaves the updated parameters in prm), the updated Gaussian
+// is then projected for the next camera, exactly as gs_project would project it.
+template <int DEG, bool RAW, bool NEXT, class Sink>
 __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means, const float *__restrict__ log_scales,
                                                 const float *__restrict__ quats, const float *__restrict__ logits,
                                                 const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
                                                 float alpha_min, float depth_lo, float depth_hi, const float (&in)[9],
-                                                float *__restrict__ grads2d, const Sink &out)
+                                                float *__restrict__ grads2d, const Sink &out, const CamD &next_cam,
+                                                const ProjOut &next)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     Params1<K> prm;
-    prm.means[0] = means[i]; prm.means[1] = means[n + i]; prm.means[2] = means[2 * n + i];
-    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[n + i]; prm.ls[2] = log_scales[2 * n + i];
-    prm.q[0] = quats[i]; prm.q[1] = quats[n + i]; prm.q[2] = quats[2 * n + i]; prm.q[3] = quats[3 * n + i];
-    prm.logit = logits[i];
-    bool shf = true;
-#pragma unroll
-    for (int k = 0; k < 3 * K; ++k) {
-        prm.sh[k] = sh[(int64_t)k * n + i];
-        shf = shf && __builtin_isfinite(prm.sh[k]);
-    }
+    load_params(means, log_scales, quats, logits, sh, n, i, prm);
+    const bool shf = sh_finite(prm);
     Proj P;
     const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
     project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
@@ -522,6 +569,7 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
         project_bwd_grads<DEG>(P, cam, in, prm, G);
     }
     out.flush(i, G, prm);
+    if constexpr (NEXT) project_store<DEG>(prm, next_cam, alpha_min, depth_lo, depth_hi, i, next);
 }
 
 template <int DEG>
@@ -535,27 +583,29 @@ __global__ __launch_bounds__(256) void k_project_bwd(
     float g[9];
 #pragma unroll
     for (int f = 0; f < 9; ++f) g[f] = g2[(int64_t)f * n + i];
-    project_bwd_one<DEG, false>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, g,
-                                nullptr, out);
+    project_bwd_one<DEG, false, false>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo,
+                                       depth_hi, g, nullptr, out, cam, ProjOut{});
 }
 
 // The end of a training step per Gaussian: the per-Gaussian sum of Eq. 4 over its
 // quadrant-record slots (as k_grad_reduce; optionally stored in grads2d), the projection
-// backward, and the Adam update of every parameter scalar.
-template <int DEG>
+// backward, and the Adam update of every parameter scalar; with NEXT also the projection
+// of the updated Gaussian for the next camera (into next).
+template <int DEG, bool NEXT>
 __global__ __launch_bounds__(256) void k_grad_adam(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
     const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
-    const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp, float *__restrict__ grads2d, AdamSink out)
+    const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp, float *__restrict__ grads2d, AdamSink out,
+    CamD next_cam, ProjOut next)
 {
     __shared__ gsr::SlotStage stage[4];
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     float acc[9];
     gsr::raw_slot_sums(hdr, qoff, qgrad, qstamp, i, n, stage[threadIdx.x >> 6], acc);
     if (i >= n) return;
-    project_bwd_one<DEG, true>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, acc,
-                               grads2d, out);
+    project_bwd_one<DEG, true, NEXT>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi,
+                                     acc, grads2d, out, next_cam, next);
 }
 
 }  // namespace
@@ -570,6 +620,24 @@ gs_status check_gaussians(const gs_gaussians *g)
     if (g->n > 0 && (!g->means || !g->log_scales || !g->quats || !g->opacity_logits || !g->sh))
         return fail(GS_ERR_INVALID_ARGUMENT, "a parameter pointer is NULL");
     return GS_OK;
+}
+
+gs_status check_proj_out(const gs_projected *out, int64_t n)
+{
+    if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "projected output is NULL");
+    if (n == 0) return GS_OK;
+    if (!out->means2d || !out->conic_opacity || !out->color || !out->depth || !out->radii || !out->rec)
+        return fail(GS_ERR_INVALID_ARGUMENT, "a projected-record pointer is NULL");
+    if (!aligned(out->conic_opacity, 16) || !aligned(out->rec, 16) || !aligned(out->means2d, 8) ||
+        !aligned(out->radii, 8))
+        return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity/rec must be 16-byte, means2d/radii 8-byte aligned");
+    return GS_OK;
+}
+
+ProjOut proj_out(const gs_projected *out)
+{
+    return ProjOut{reinterpret_cast<float2 *>(out->means2d), reinterpret_cast<float4 *>(out->conic_opacity),
+                   out->color, out->depth, reinterpret_cast<int2 *>(out->radii), reinterpret_cast<float4 *>(out->rec)};
 }
 
 gs_status launch_project_bwd(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
@@ -606,23 +674,15 @@ extern "C" gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, con
     if ((s = check_gaussians(g)) != GS_OK) return s;
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
-    if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "out is NULL");
     const int64_t n = g->n;
+    if ((s = check_proj_out(out, n)) != GS_OK) return s;
     if (n == 0) return GS_OK;
-    if (!out->means2d || !out->conic_opacity || !out->color || !out->depth || !out->radii || !out->rec)
-        return fail(GS_ERR_INVALID_ARGUMENT, "a projected-record pointer is NULL");
-    if (!aligned(out->conic_opacity, 16) || !aligned(out->rec, 16) || !aligned(out->means2d, 8) ||
-        !aligned(out->radii, 8))
-        return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity/rec must be 16-byte, means2d/radii 8-byte aligned");
     const CamD cd = make_cam(cam);
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
-    float2 *m2 = reinterpret_cast<float2 *>(out->means2d);
-    float4 *co = reinterpret_cast<float4 *>(out->conic_opacity);
-    int2 *rr = reinterpret_cast<int2 *>(out->radii);
+    const ProjOut po = proj_out(out);
 #define GS_PF(D)                                                                                        \
     k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
-                                             cd, p->alpha_min, p->depth_lo, p->depth_hi, m2, co, out->color,  \
-                                             out->depth, rr, reinterpret_cast<float4 *>(out->rec))
+                                             cd, p->alpha_min, p->depth_lo, p->depth_hi, po)
     switch (p->sh_degree) {
     case 0: GS_PF(0); break;
     case 1: GS_PF(1); break;
@@ -651,11 +711,12 @@ namespace gsi {
 gs_status check_raster_inputs(const gs_bins *bins, const gs_camera *cam);
 }
 
-extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
-                                            const gs_camera *cam,
-                                            const gs_raster_params *p, float *grads2d, const gs_param_grads *m,
-                                            const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1,
-                                            float beta2, float eps, hipStream_t stream)
+namespace {
+
+gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins, const gs_camera *cam,
+                           const gs_raster_params *p, float *grads2d, const gs_param_grads *m,
+                           const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1, float beta2,
+                           float eps, const gs_camera *next_cam, gs_projected *next_proj, hipStream_t stream)
 {
     using namespace gsi;
     gs_status s;
@@ -670,6 +731,10 @@ extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_proj
     if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f && eps >= 0.0f))
         return fail(GS_ERR_INVALID_ARGUMENT, "bad Adam hyper-parameters");
     const int64_t n = g->n;
+    if (next_cam) {
+        if ((s = check_camera(next_cam)) != GS_OK) return s;
+        if ((s = check_proj_out(next_proj, n)) != GS_OK) return s;
+    }
     if (n == 0) return GS_OK;
     if (!m->means || !m->log_scales || !m->quats || !m->opacity_logits || !m->sh || !v->means || !v->log_scales ||
         !v->quats || !v->opacity_logits || !v->sh)
@@ -697,11 +762,21 @@ extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_proj
     const float4 *qg = reinterpret_cast<const float4 *>(rb + L.qgrad);
     const uint2 *qs = reinterpret_cast<const uint2 *>(rb + L.qstamp);
     const CamD cd = make_cam(cam);
+    const CamD nd = next_cam ? make_cam(next_cam) : cd;
+    const ProjOut po = next_cam ? proj_out(next_proj) : ProjOut{};
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
 #define GS_GA(D)                                                                                                   \
-    k_grad_adam<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, cd, \
-                                               p->alpha_min, p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,         \
-                                               grads2d, sink)
+    do {                                                                                                           \
+        if (next_cam)                                                                                              \
+            k_grad_adam<D, true><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, \
+                                                             g->sh, n, cd, p->alpha_min, p->depth_lo, p->depth_hi, \
+                                                             hdr, qoff, qg, qs, grads2d, sink, nd, po);            \
+        else                                                                                                       \
+            k_grad_adam<D, false><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,                   \
+                                                              g->opacity_logits, g->sh, n, cd, p->alpha_min,       \
+                                                              p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,         \
+                                                              grads2d, sink, nd, po);                              \
+    } while (0)
     switch (p->sh_degree) {
     case 0: GS_GA(0); break;
     case 1: GS_GA(1); break;
@@ -711,4 +786,28 @@ extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_proj
 #undef GS_GA
     GS_LAUNCH_CHECK("k_grad_adam");
     return GS_OK;
+}
+
+}  // namespace
+
+extern "C" gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                                            const gs_camera *cam, const gs_raster_params *p, float *grads2d,
+                                            const gs_param_grads *m, const gs_param_grads *v, const gs_adam_lrs *lr,
+                                            int32_t step, float beta1, float beta2, float eps, hipStream_t stream)
+{
+    return grad_adam_launch(g, proj, bins, cam, p, grads2d, m, v, lr, step, beta1, beta2, eps, nullptr, nullptr,
+                            stream);
+}
+
+extern "C" gs_status gs_grad_aggregate_adam_project(const gs_gaussians *g, const gs_projected *proj,
+                                                    const gs_bins *bins, const gs_camera *cam,
+                                                    const gs_raster_params *p, float *grads2d,
+                                                    const gs_param_grads *m, const gs_param_grads *v,
+                                                    const gs_adam_lrs *lr, int32_t step, float beta1, float beta2,
+                                                    float eps, const gs_camera *next_cam, gs_projected *next_proj,
+                                                    hipStream_t stream)
+{
+    if (!next_cam) return gsi::fail(GS_ERR_INVALID_ARGUMENT, "next_cam is NULL");
+    return grad_adam_launch(g, proj, bins, cam, p, grads2d, m, v, lr, step, beta1, beta2, eps, next_cam, next_proj,
+                            stream);
 }

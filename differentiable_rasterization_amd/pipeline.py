@@ -162,6 +162,11 @@ class TrainStep:
 
     def forward(self, cam: B.Camera, stream=None):
         B.gs_project(self.params.gaussians(), cam, self.raster, self.proj.abi(), stream)
+        self.forward_projected(cam, stream)
+
+    def forward_projected(self, cam: B.Camera, stream=None):
+        """Binning and forward rasterization of the records already in self.proj (written by
+        gs_project or by aggregate_adam_project for this camera)."""
         self.bins.sort(self.proj, cam, self.raster, stream)
         f = self.frame
         B.gs_raster_fwd(self.proj.abi(), self.bins.abi(), cam, self.raster, f.color, f.t_final, f.n_trav,
@@ -196,6 +201,16 @@ class TrainStep:
         m, v = self.params.moments()
         B.gs_grad_aggregate_adam(self.params.gaussians(), self.proj.abi(), self.bins.abi(), cam, self.raster, grads2d, m, v,
                                  B.AdamLrs(**self.lr), self.params.step_count, 0.9, 0.999, 1e-15, stream)
+
+    def aggregate_adam_project(self, cam: B.Camera, next_cam: B.Camera, grads2d=None, stream=None):
+        """aggregate_adam, then the projection of the updated Gaussians for next_cam into
+        self.proj in the same pass (the next step then starts at the binning)."""
+        self.params.step_count += 1
+        m, v = self.params.moments()
+        pa = self.proj.abi()
+        B.gs_grad_aggregate_adam_project(self.params.gaussians(), pa, self.bins.abi(), cam, self.raster, grads2d, m,
+                                         v, B.AdamLrs(**self.lr), self.params.step_count, 0.9, 0.999, 1e-15,
+                                         next_cam, pa, stream)
 
     def backward_partials(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):
         f = self.frame

@@ -281,6 +281,20 @@ gs_status gs_grad_aggregate_adam(const gs_gaussians *g, const gs_projected *proj
                                  const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1,
                                  float beta2, float eps, hipStream_t stream);
 
+/* gs_grad_aggregate_adam, then the projection of the updated Gaussians for the camera of
+ * the next step, in the same pass: each Gaussian is projected from the updated values the
+ * Adam update leaves in registers, so the parameters are not read a second time.  The
+ * step that follows starts at gs_bin_sort.  next_proj receives exactly what
+ * gs_project(g, next_cam, p, next_proj) would write after gs_grad_aggregate_adam (Splaxel
+ * section 2 "Projection", with the same p); it may be the same buffers as proj, which this
+ * call does not read.  next_cam must not be NULL.  Errors as gs_grad_aggregate_adam and
+ * gs_project. */
+gs_status gs_grad_aggregate_adam_project(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins,
+                                         const gs_camera *cam, const gs_raster_params *p, float *grads2d,
+                                         const gs_param_grads *m, const gs_param_grads *v, const gs_adam_lrs *lr,
+                                         int32_t step, float beta1, float beta2, float eps,
+                                         const gs_camera *next_cam, gs_projected *next_proj, hipStream_t stream);
+
 /* Backward through projection and colour evaluation alone (ByteSplat section 2.1: the
  * aggregated screen-space gradients are propagated through projection and colour
  * evaluation): from grads2d [9][n] (fields u, v, A, B, C, o, r, g, b) to grads3d (every

@@ -308,7 +308,7 @@ def test_backward_split_matches_whole():
     assert torch.equal(st.grads2d, whole2) and torch.equal(st.params.grad, whole3)
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "100k"])
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "ragged_sh2", "offscreen_sh3", "100k"])
 def test_fused_aggregate_adam_matches_separate_calls(name):
     """gs_grad_aggregate_adam equals gs_grad_aggregate -> gs_project_bwd -> gs_adam_step bit
     for bit (parameters, moments, screen-space gradients), over two steps."""
@@ -336,6 +336,58 @@ def test_fused_aggregate_adam_matches_separate_calls(name):
     assert torch.equal(g0, g1)
     assert torch.equal(p0, p1) and torch.equal(m0, m1) and torch.equal(v0, v1)
     assert float((m1 != 0).float().mean()) > 0.0
+
+
+def _moved_camera(cam):
+    """The same camera shifted sideways and back (a second view of the scene)."""
+    vm = cam.viewmat.clone().reshape(4, 4)
+    vm[0, 3] += 0.15
+    vm[2, 3] += 0.4
+    return scenes._camera(vm.reshape(16).contiguous(), cam.width, cam.height)
+
+
+def _proj_fields(pr):
+    return [t.clone() for t in (pr.means2d, pr.conic_opacity, pr.color, pr.depth, pr.radii, pr.rec)]
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "ragged_sh2", "offscreen_sh3", "100k"])
+def test_fused_adam_projection_matches_separate_calls(name):
+    """gs_grad_aggregate_adam_project equals gs_grad_aggregate_adam followed by gs_project of
+    the updated Gaussians for the next camera, bit for bit (every projected field, the
+    parameters and the Adam moments), over two steps on two views."""
+    log(f"fused adam + next projection {name}")
+    sc = _scene(name)
+    cams = [sc.cameras[0], _moved_camera(sc.cameras[0])]
+    rp = B.make_params(sc.sh_degree)
+    tgt = sc.targets[0].to(DEV)
+    runs = []
+    for fused in (False, True):
+        st = gpu_forward(sc, cams[0], rp)
+        projs = []
+        for step in range(2):
+            c, nc = B.camera_from(cams[step % 2]), B.camera_from(cams[(step + 1) % 2])
+            if step:
+                st.forward_projected(c)
+            st.loss(tgt)
+            st.backward_partials(c)
+            for t in (st.proj.means2d, st.proj.conic_opacity, st.proj.color, st.proj.depth, st.proj.rec):
+                t.fill_(-123.0)
+            st.proj.radii.fill_(-5)
+            if fused:
+                st.aggregate_adam_project(c, nc)
+            else:
+                st.aggregate_adam(c)
+                B.gs_project(st.params.gaussians(), nc, rp, st.proj.abi())
+            torch.cuda.synchronize()
+            projs.append(_proj_fields(st.proj))
+        runs.append((projs, st.params.data.clone(), st.params.m.clone(), st.params.v.clone()))
+    (pa, p0, m0, v0), (pb, p1, m1, v1) = runs
+    for sa, sb in zip(pa, pb):
+        for a, b in zip(sa, sb):
+            assert torch.equal(a, b)
+    assert torch.equal(p0, p1) and torch.equal(m0, m1) and torch.equal(v0, v1)
+    # the projection saw the updated parameters: its visible records differ from view 0's
+    assert int((pb[0][4][:, 0] > 0).sum()) > 0
 
 
 # ------------------------------------------------------------------ Adam
