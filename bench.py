@@ -17,7 +17,8 @@ cameras on a sphere of radius 25; steps cycle through the four views.
 Prints one JSON line: value = Gaussian-pixel intersections (sum over pixels of the
 number of list entries each pixel composites, N_p of Eq. 1 in ByteSplat section 2.1)
 per second of whole training step; ms_per_step = train-step milliseconds.  Per-kernel
-times come from HIP events recorded on the stream the kernels run on.
+times come from HIP events recorded on the stream the kernels run on (timing-only events
+without the system-scope fence, see TimingEvent).
 
 roofline: the longer of k_raster_bwd (bound by VALU arithmetic; its algorithmic work is
 FLOP_PER_PAIR["raster_bwd"] floating-point operations per Gaussian-pixel pair) and
@@ -104,6 +105,54 @@ def hbm_bytes(kernel, n, n_vis, k_sh, n_isect, n_px):
     if kernel == "grad_adam_project":                               # the same + the next view's records
         return 36 * n_isect + n * (11 + 3 * k_sh) * 24 + n_vis * 96 + (n - n_vis) * 12
     return None
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: recording it
+    skips the system-scope release fence (a cache writeback and invalidation) that a
+    default event performs, which costs the stream several microseconds per record on this
+    GPU.  Recorded on the current (torch) stream, the stream the kernels are launched on.
+    Uses the HIP runtime torch has loaded."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            import torch
+            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        import torch
+        rc = self._lib().hipEventRecord(self.ev, self._ct.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        ms = self._ct.c_float()
+        rc = self._lib().hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
 
 
 def cpu_baseline(scene, rows):
@@ -220,7 +269,7 @@ def main():
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
-    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    new_events = lambda: [[TimingEvent() for _ in range(len(names) + 1)]
                           for _ in range(args.steps)]
     events = new_events()
     st.frame.n_trav_sum.zero_()
