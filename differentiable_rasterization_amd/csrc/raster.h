@@ -288,10 +288,12 @@ __device__ __forceinline__ uint32_t prefetch_records(const float4 *__restrict__ 
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// exp2 exponent of a record at pixel offset (dx, dy).
+// exp2 exponent of a record at pixel offset (dx, dy), as dx (a dx + b dy) + (c dy^2 + l):
+// two multiplies and three FMAs.  Both raster kernels evaluate it this way, so the
+// backward recomputes the forward's alpha bit for bit.
 __device__ __forceinline__ float exponent(const float4 &p0, const float4 &p1, float dx, float dy)
 {
-    return fmaf(p0.z * dx, dx, fmaf(p0.w * dx, dy, fmaf(p1.x * dy, dy, p1.y)));
+    return fmaf(dx, fmaf(p0.z, dx, p0.w * dy), fmaf(p1.x * dy, dy, p1.y));
 }
 
 }  // namespace gsr
