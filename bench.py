@@ -4,12 +4,14 @@
                     [--cpu-rows R] [--copy-calibration-mib M]
 
 A step is one training iteration on one view: projection -> gs_bin_sort ->
-gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd_partials -> gs_grad_aggregate_adam_project
-(the per-Gaussian gradient sum, projection backward, Adam and the projection of the
-updated Gaussians for the next step's view in one pass, so each step's projection is done
-by the step before it; the first step's records come from gs_project before the warm-up).
---unfused runs gs_project at the start of each step and gs_grad_aggregate,
-gs_project_bwd and gs_adam_step at its end instead.  The data are seeded, synthetic and
+gs_raster_fused_l1 (forward rasterization, L1 loss and backward rasterization in one
+kernel) -> gs_grad_aggregate_adam_project (the per-Gaussian gradient sum, projection
+backward, Adam and the projection of the updated Gaussians for the next step's view in
+one pass, so each step's projection is done by the step before it; the first step's
+records come from gs_project before the warm-up).  --separate-raster runs gs_raster_fwd,
+gs_loss_l1 and gs_raster_bwd_partials in place of the fused kernel; --unfused also runs
+gs_project at the start of each step and gs_grad_aggregate, gs_project_bwd and
+gs_adam_step at its end.  The data are seeded, synthetic and
 already resident in HBM.  The default workload is 1M
 Gaussians (SH degree 3, 64 clusters in a 20 m cube) at 1920x1080 with four
 cameras on a sphere of radius 25; steps cycle through the four views.
@@ -20,9 +22,10 @@ per second of whole training step; ms_per_step = train-step milliseconds.  Per-k
 times come from HIP events recorded on the stream the kernels run on (timing-only events
 without the system-scope fence, see TimingEvent).
 
-roofline: the longer of k_raster_bwd (bound by VALU arithmetic; its algorithmic work is
-FLOP_PER_PAIR["raster_bwd"] floating-point operations per Gaussian-pixel pair) and
-k_grad_adam (bound by HBM; hbm_bytes), one launch each per step; roofline_next the other.  roofline.traffic is the HBM traffic of one launch
+roofline: the longer of the backward raster kernel (k_raster_fused_l1 by default,
+k_raster_bwd with --separate-raster; bound by VALU arithmetic, its algorithmic work is
+FLOP_PER_PAIR floating-point operations per Gaussian-pixel pair) and k_grad_adam (bound by
+HBM; hbm_bytes), one launch each per step; roofline_next the other.  roofline.traffic is the HBM traffic of one launch
 from the stored counter summary (profiles/), or null if the kernel's sources changed
 since those counters were taken.  --copy-calibration-mib runs a plain copy-like kernel of
 known size before the timed steps, for the counter runs that normalise FETCH_SIZE and
@@ -50,11 +53,13 @@ FP32_NONPACKED_TFLOPS = 78.6             # 256 CU x 4 SIMD x 16 lanes x 2 flop x
 # T recovery, colour and alpha gradients, colour-behind update, power / conic / mean /
 # opacity gradients and their per-Gaussian sums: 61 flop + 1 exp + 1 reciprocal).  The
 # kernels compute the same quantities with fewer instructions (per-wave moment sums).
-FLOP_PER_PAIR = {"raster_fwd": 27, "raster_bwd": 63}
+FLOP_PER_PAIR = {"raster_fwd": 27, "raster_bwd": 63, "raster_fused": 27 + 63}
 # stored counter traffic of the kernels that can dominate the step (1M / 1080p workload)
 TRAFFIC_SUMMARY = {"k_raster_bwd": os.path.join(ROOT, "profiles", "k_raster_bwd_1m_1080p_traffic.txt"),
+                   "k_raster_fused_l1": os.path.join(ROOT, "profiles", "k_raster_fused_l1_1m_1080p_traffic.txt"),
                    "k_grad_adam": os.path.join(ROOT, "profiles", "k_grad_adam_1m_1080p_traffic.txt")}
-KERNEL_OF = {"raster_bwd": "k_raster_bwd", "grad_adam": "k_grad_adam", "grad_adam_project": "k_grad_adam"}
+KERNEL_OF = {"raster_bwd": "k_raster_bwd", "grad_adam": "k_grad_adam", "grad_adam_project": "k_grad_adam",
+             "raster_fused": "k_raster_fused_l1"}
 
 
 def parse():
@@ -67,6 +72,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1080, help="image rows the oracle baseline composites")
     ap.add_argument("--unfused", action="store_true",
                     help="separate gs_grad_aggregate, gs_project_bwd and gs_adam_step calls instead of the fused pass")
+    ap.add_argument("--separate-raster", action="store_true",
+                    help="gs_raster_fwd, gs_loss_l1 and gs_raster_bwd_partials instead of gs_raster_fused_l1")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the untimed pass that times every call separately")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -205,12 +212,15 @@ def main():
 
     if args.unfused:
         names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
-    else:   # the projection of each step runs in the previous step's last pass
+    elif args.separate_raster:   # the projection of each step runs in the previous step's last pass
         names = ["bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_adam_project"]
+    else:   # and forward, loss and backward rasterization run as one kernel
+        names = ["bin_sort", "raster_fused", "grad_adam_project"]
     g = params.gaussians()
 
     # the calls timed inside the timed steps: the two kernels that can dominate the step
-    timed_calls = [names.index(nm) for nm in ("raster_bwd", "grad_adam", "grad_adam_project") if nm in names]
+    timed_calls = [names.index(nm) for nm in ("raster_fused", "raster_bwd", "grad_adam", "grad_adam_project")
+                   if nm in names]
     timed_marks = set(timed_calls) | {k + 1 for k in timed_calls}
 
     def one_step(i, ev=None, counts=None, every_call=False):
@@ -235,6 +245,12 @@ def main():
         else:   # no host wait inside the step; the counts are checked after the timed steps
             st.bins.sort_async(st.proj, c, st.raster, counts)
         rec(k + 1)
+        if not args.unfused and not args.separate_raster:   # forward + L1 + backward in one kernel
+            st.fused_l1(c, t)
+            rec(k + 2)
+            st.aggregate_adam_project(c, nc)
+            rec(k + 3)
+            return
         B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.n_trav_sum)
         rec(k + 2)
         B.gs_loss_l1(f.color, t, f.n_px, f.loss, f.dL_dcolor, f.loss_ws)
@@ -347,7 +363,8 @@ def main():
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
                    "views": nviews,
                    "step": "one view: projection + fwd + L1 + bwd + Adam" + (
-                       "" if args.unfused else " (each view's projection fused into the previous step's Adam pass)")},
+                       "" if args.unfused else " (each view's projection fused into the previous step's Adam pass"
+                       + ("" if args.separate_raster else "; fwd + L1 + bwd in one kernel") + ")")},
         "roofline": roof,
         "roofline_next": roof_next,
         # from the untimed pass with an event around every call
@@ -361,8 +378,9 @@ def main():
         # Gaussian-pixel intersections over the two raster kernels' time (forward compositing
         # and the per-pixel backward with its per-quadrant sums)
         "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]) * 1e-3), 1)
-        if "raster_fwd" in per_kernel else None,
-        "kernels_note": "raster_bwd and grad_adam(_project) from events in the timed steps; the others from an untimed "
+        if "raster_fwd" in per_kernel else round(isect_step / (per_kernel["raster_fused"] * 1e-3), 1),
+        "kernels_note": "raster_fused (or raster_bwd) and grad_adam(_project) from events in the timed steps; the others "
+                        "from an untimed "
                         "pass of the same steps with an event around every call",
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),

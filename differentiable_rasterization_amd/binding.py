@@ -27,7 +27,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP = range(5)
 TILE = 16
 EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_bin_sort_async", "gs_raster_fwd", "gs_loss_workspace_bytes",
-            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project", "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
+            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project",
+            "gs_raster_fused_l1", "gs_raster_fused_l1_workspace_bytes", "gs_tile_budget", "gs_tile_budget_report",
+            "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_last_error")
 
 
@@ -108,6 +110,11 @@ _SIGS = {
     "gs_grad_aggregate_adam_project": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams),
                                               _vp, _P(ParamGrads), _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32,
                                               _f32, _P(Camera), _P(Projected), _vp]),
+    "gs_raster_fused_l1": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, ctypes.c_size_t, _vp]),
+    "gs_raster_fused_l1_workspace_bytes": (ctypes.c_size_t, [_i32, _i32]),
+    "gs_tile_budget": (_i64, [_i64, _i64, _i64]),
+    "gs_tile_budget_report": (_i32, [_P(Bins), _P(Camera), _i64, _vp, _vp, _vp, _vp]),
     "gs_project_bwd": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
     "gs_adam_step": (_i32, [_P(AdamGroup), _i32, _i32, _f32, _f32, _f32, _vp]),
     "gs_composite_over": (_i32, [_P(_vp), _P(_vp), _i32, _i64, _f32, _vp, _vp, _vp]),
@@ -267,6 +274,26 @@ def gs_grad_aggregate_adam_project(g: Gaussians, proj: Projected, b: Bins, cam: 
                                                ctypes.byref(cam), ctypes.byref(p), _ptr(grads2d), ctypes.byref(m),
                                                ctypes.byref(v), ctypes.byref(lr), step, beta1, beta2, eps,
                                                ctypes.byref(next_cam), ctypes.byref(next_proj), _stream(stream)))
+
+
+def gs_raster_fused_l1_workspace_bytes(width, height) -> int:
+    return int(_lib.gs_raster_fused_l1_workspace_bytes(width, height))
+
+
+def gs_raster_fused_l1(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, target, color, t_final, n_trav,
+                       loss_out, n_trav_sum, workspace, stream=None):
+    _check(_lib.gs_raster_fused_l1(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p), _ptr(target),
+                                   _ptr(color), _ptr(t_final), _ptr(n_trav), _ptr(loss_out), _ptr(n_trav_sum),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def gs_tile_budget(lds_budget_bytes, fixed_bytes, bytes_per_gaussian) -> int:
+    return int(_lib.gs_tile_budget(lds_budget_bytes, fixed_bytes, bytes_per_gaussian))
+
+
+def gs_tile_budget_report(b: Bins, cam: Camera, budget, excess=None, frac=None, totals=None, stream=None):
+    _check(_lib.gs_tile_budget_report(ctypes.byref(b), ctypes.byref(cam), budget, _ptr(excess), _ptr(frac),
+                                      _ptr(totals), _stream(stream)))
 
 
 def gs_project_bwd(g: Gaussians, cam: Camera, p: RasterParams, grads2d, grads3d: ParamGrads, stream=None):

@@ -34,85 +34,13 @@
 // written carries the call's stamp (BinsHeader::epoch), and the per-Gaussian sums skip the
 // others.
 #include "kernels.h"
-#include "raster.h"
+#include "raster_walk.h"
 
 namespace {
 
 using namespace gsr;
 
-constexpr int kBwdBatch = 4;   // entries per transpose-reduction (4 x 9 values -> 4 rows of 16 lanes)
 constexpr int kFields = 9;
-
-__device__ __forceinline__ float swap_add32(float &x, float &y)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float swap_add16(float &x, float &y)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// v[e * 9 + f] holds this lane's value of field f of entry e (e < 4).  Sums every field
-// of every entry over the 64 lanes, transposing as it goes so that each sum lands in one
-// lane: afterwards lane (e, n) of row e = lane >> 4 (n = lane & 15) holds the total of
-// field F(n) = 4 b1 + 2 b2 + b3 of entry e (b_k = bit k of n; lanes n and n ^ 1 hold the
-// same field) and t8 holds the total of field 8 of entry e.
-//   1. v_permlane32_swap + add: rows 0-1 keep entries 0-1, rows 2-3 entries 2-3
-//   2. v_permlane16_swap + add: row e keeps entry e (9 partial sums per lane)
-//   3. within each 16-lane row, fields 0-7 by a transposing butterfly (partners n ^ 8 by
-//      row_ror:8, n ^ 7 by row_half_mirror, n ^ 2 and n ^ 1 by quad_perm): at each step a
-//      lane keeps one field of each pair, chosen by one bit of n, adds the partner's value
-//      of that field, and passes on the other; field 8 by a plain butterfly.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v)
-{
-    using namespace gsd;
-    // old = 0 (the identity of +) lets the compiler fold the move into the DPP add
-    return f_from_i(__builtin_amdgcn_update_dpp(0, i_from_f(v), CTRL, 0xF, 0xF, false));
-}
-
-constexpr int kRowRor8 = 0x128;
-
-// One transposing step: keep x if !bit else y, and add the partner's copy of the same field.
-template <int CTRL>
-__device__ __forceinline__ float tstep(float x, float y, bool bit)
-{
-    const float keep = bit ? y : x, send = bit ? x : y;
-    return keep + dpp_f<CTRL>(send);
-}
-
-// Per-lane choice of one of four wave-uniform values by the lane's row (lane >> 4).
-__device__ __forceinline__ float by_row(int row, float a0, float a1, float a2, float a3)
-{
-    const float lo = (row & 1) ? a1 : a0, hi = (row & 1) ? a3 : a2;
-    return (row & 2) ? hi : lo;
-}
-
-__device__ __forceinline__ void reduce_4x9(float (&v)[kBwdBatch * kFields], int n, float &fz, float &t8)
-{
-    using namespace gsd;
-#pragma unroll
-    for (int i = 0; i < 18; ++i) v[i] = swap_add32(v[i], v[i + 18]);   // lanes < 32: slot i, else slot i + 18
-#pragma unroll
-    for (int i = 0; i < 9; ++i) v[i] = swap_add16(v[i], v[i + 9]);     // row r: slot i + 9 r
-    const bool b3 = (n >> 3) & 1, b2 = (n >> 2) & 1, b1 = (n >> 1) & 1;
-    float w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = tstep<kRowRor8>(v[2 * k], v[2 * k + 1], b3);   // field 2k + b3
-    const float x0 = tstep<kRowHalfMirror>(w[0], w[1], b2);                            // field 2 b2 + b3
-    const float x1 = tstep<kRowHalfMirror>(w[2], w[3], b2);                            // 4 + 2 b2 + b3
-    const float y = tstep<kQuadSwap2>(x0, x1, b1);                                     // 4 b1 + 2 b2 + b3
-    fz = y + dpp_f<kQuadSwap1>(y);
-    float z = v[8];
-    z += dpp_f<kQuadSwap1>(z);
-    z += dpp_f<kQuadSwap2>(z);
-    z += dpp_f<kRowHalfMirror>(z);
-    z += dpp_f<kRowRor8>(z);
-    t8 = z;
-}
 
 template <bool HAS_GT>
 __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ ranges, const int32_t *__restrict__ order,
@@ -153,90 +81,7 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)(start + nmax));
-    const uint32_t epoch = hdr->epoch;
-    const int row = lane >> 4, nl = lane & 15;
-    // the reduced field each lane of a row holds (reduce_4x9): even lanes hold fields 0-7,
-    // lane 1 field 8; lane 3 writes the slot's stamp (epoch, ~epoch)
-    const bool stamp_lane = nl == 3;
-    const int my_field = nl == 1 ? 8 : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
-    const bool lane_writes = (nl & 1) == 0 || nl == 1 || stamp_lane;
-    const uint2 stamp = make_uint2(epoch, ~epoch);
-    float Tr = 1.0f;
-    // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
-    uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
-    for (uint32_t jt = j0; jt < j1;) {
-        if (((jt - j0) & 63u) == 0u && jt > j0) {
-            sink ^= pend;
-            pend = prefetch_records(qrec, jt + 64u, j1);
-        }
-        // records jt .. jt+3 (past j1: spare, unused); one wait per batch
-        float4 p0[kBwdBatch], p1[kBwdBatch];
-        float blue[kBwdBatch], kent[kBwdBatch], slot[kBwdBatch];
-        const float4 *rb = qrec + kRecF4 * (size_t)jt;
-#pragma unroll
-        for (int i = 0; i < kBwdBatch; ++i) {
-            p0[i] = rb[kRecF4 * i];
-            p1[i] = rb[kRecF4 * i + 1];
-            const float4 p2 = rb[kRecF4 * i + 2];
-            blue[i] = p2.x;
-            kent[i] = p2.z;
-            slot[i] = p2.w;
-        }
-#pragma unroll
-        for (int i = 0; i < kBwdBatch; ++i)
-            asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
-                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]), "s"(slot[i]));
-        const uint32_t cnt = min((uint32_t)kBwdBatch, j1 - jt);
-        float v[kBwdBatch * kFields];
-        bool any = false;
-#pragma unroll
-        for (int i = 0; i < kBwdBatch; ++i) {
-            float *o = v + kFields * i;
-            const int rel = (int)__float_as_uint(kent[i]) - start;
-            const float dx = fx - p0[i].x, dy = fy - p0[i].y;
-            const float raw = exp2_fast(exponent(p0[i], p1[i], dx, dy));
-            // the forward pass's alpha and T, bit for bit
-            const float alpha = fminf(alpha_max, raw);
-            const bool take = (uint32_t)i < cnt && rel < np && alpha >= alpha_min;
-            const float a = take ? alpha : 0.0f;
-            const float om = 1.0f - a;
-            const float ro = __builtin_amdgcn_rcpf(om);
-            const float w = Tr * a;
-            o[6] = w * G0;
-            o[7] = w * G1;
-            o[8] = w * G2;
-            const float cg = fmaf(p1[i].z, G0, fmaf(p1[i].w, G1, blue[i] * G2));
-            Z = fmaf(-w, cg, Z);
-            const float dal = fmaf(Tr, cg, -ro * Z);
-            const float s0 = dal * (raw < alpha_max ? a : 0.0f);   // clamped alpha has no power gradient
-            o[0] = s0;
-            o[1] = dx * s0;
-            o[2] = dy * s0;
-            o[3] = dx * o[1];
-            o[4] = dy * o[1];
-            o[5] = dy * o[2];
-            Tr = Tr * om;
-            any |= take;
-        }
-        // gradient slot of the batch's record e = row (record jt + e); lane n writes field
-        // my_field (see reduce_4x9)
-        const uint32_t my_slot = __float_as_uint(by_row(row, slot[0], slot[1], slot[2], slot[3]));
-        float *dst = qgrad + (size_t)my_slot * kGradSlot + my_field;
-        uint2 *dst_stamp = reinterpret_cast<uint2 *>(qstamp) + my_slot;
-        const bool writer = (uint32_t)row < cnt && lane_writes;
-        jt += cnt;
-        if (__ballot(any) == 0) continue;   // no pixel takes these records: slots left unstamped
-        float fz, t8;
-        reduce_4x9(v, nl, fz, t8);
-        if (writer) {
-            if (stamp_lane)
-                *dst_stamp = stamp;
-            else
-                *dst = nl == 1 ? t8 : fz;
-        }
-    }
-    sink ^= pend;
-    asm volatile("" ::"v"(sink));
+    bwd_walk(qrec, j0, j1, fx, fy, start, np, G0, G1, G2, Z, alpha_min, alpha_max, hdr->epoch, qgrad, qstamp);
 }
 
 // A new stamp for the gradient slots of this backward call.

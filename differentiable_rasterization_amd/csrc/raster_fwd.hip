@@ -8,41 +8,11 @@
 // pixel of the quadrant has terminated.  N_p counts every entry of the 16x16 tile list up
 // to the termination point (the Gaussians the pixel traverses), whether or not the
 // quadrant's list holds them.
-#include "raster.h"
+#include "raster_walk.h"
 
 namespace {
 
 using namespace gsr;
-
-constexpr int kFwdBatch = 4;   // records per scalar-load batch
-
-// One batch of records in scalar registers.
-struct Batch {
-    float4 p0[kFwdBatch], p1[kFwdBatch];
-    float blue[kFwdBatch], kent[kFwdBatch];
-    __device__ __forceinline__ void load(const float4 *__restrict__ qrec, uint32_t j)
-    {
-        const float4 *rb = qrec + kRecF4 * (size_t)j;
-#pragma unroll
-        for (int i = 0; i < kFwdBatch; ++i) {
-            p0[i] = rb[kRecF4 * i];
-            p1[i] = rb[kRecF4 * i + 1];
-            const float4 p2 = rb[kRecF4 * i + 2];
-            blue[i] = p2.x;
-            kent[i] = p2.z;
-        }
-    }
-    // Makes the loaded values available here: the compiler waits for the scalar loads at
-    // this point (the "memory" clobber keeps later loads behind it).
-    __device__ __forceinline__ void wait() const
-    {
-#pragma unroll
-        for (int i = 0; i < kFwdBatch; ++i)
-            asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
-                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i])
-                         : "memory");
-    }
-};
 
 __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ ranges, const int32_t *__restrict__ order,
                                                    const float4 *__restrict__ qrec, const uint64_t *__restrict__ bitmap,
@@ -76,57 +46,9 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)end);
-    float Tr = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
-    int np = end - start;
-    bool live = inside;
-    // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
-    uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
-    // Records come in batches of kFwdBatch through scalar loads.  Scalar loads complete out
-    // of order, so the only wait is for all of them: the loop waits for batch b, issues the
-    // loads of batch b + 1 and then blends batch b, so that the loads of b + 1 land while b
-    // is blended.  Two register sets, alternating (the loop body is unrolled twice).
-    Batch A, B;
-    if (j0 < j1) A.load(qrec, j0);
-    auto blend = [&](const Batch &R, uint32_t j) {
-        // branch-free per entry: lanes that do not take it blend with alpha = 0 (T and C
-        // unchanged exactly); termination is a mask update
-#pragma unroll
-        for (int i = 0; i < kFwdBatch; ++i) {
-            if (j + (uint32_t)i >= j1) break;
-            const float dx = fx - R.p0[i].x, dy = fy - R.p0[i].y;
-            const float alpha = fminf(alpha_max, exp2_fast(exponent(R.p0[i], R.p1[i], dx, dy)));
-            const bool take = live && alpha >= alpha_min;
-            const float a = take ? alpha : 0.0f;
-            const float w = Tr * a;
-            cr = fmaf(w, R.p1[i].z, cr);
-            cg = fmaf(w, R.p1[i].w, cg);
-            cb = fmaf(w, R.blue[i], cb);
-            Tr = Tr * (1.0f - a);
-            const bool stop = take && Tr < t_min;
-            np = stop ? (int)__float_as_uint(R.kent[i]) - start + 1 : np;
-            live = live && !stop;
-        }
-    };
-    auto prefetch = [&](uint32_t j) {
-        if (((j - j0) & 63u) == 0u && j > j0) {
-            sink ^= pend;
-            pend = prefetch_records(qrec, j + 64u, j1);
-        }
-    };
-    for (uint32_t j = j0; j < j1; j += 2 * kFwdBatch) {
-        prefetch(j);
-        A.wait();
-        B.load(qrec, j + kFwdBatch);   // past j1: spare records, loaded but unused
-        blend(A, j);
-        if (j + kFwdBatch >= j1 || __ballot(live) == 0) break;
-        prefetch(j + kFwdBatch);
-        B.wait();
-        A.load(qrec, j + 2 * kFwdBatch);
-        blend(B, j + kFwdBatch);
-        if (__ballot(live) == 0) break;
-    }
-    sink ^= pend;
-    asm volatile("" ::"v"(sink));
+    float Tr, cr, cg, cb;
+    int np;
+    fwd_walk(qrec, j0, j1, fx, fy, start, end, inside, alpha_min, alpha_max, t_min, cr, cg, cb, Tr, np);
     if (inside) {
         const size_t idx = (size_t)py * W + px;
         out_c[3 * idx] = cr;

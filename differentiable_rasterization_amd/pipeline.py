@@ -145,6 +145,9 @@ class Frame:
         # running sum of N_p (Gaussian-pixel evaluations) over forward passes; cleared by the caller
         self.n_trav_sum = torch.zeros(1, dtype=torch.int64, device=device)
         self.loss_ws = torch.empty(max(B.gs_loss_workspace_bytes(self.n_px), 8), dtype=torch.uint8, device=device)
+        # per-wave partial sums of the fused forward + L1 + backward
+        self.fused_ws = torch.empty(max(B.gs_raster_fused_l1_workspace_bytes(width, height), 16),
+                                    dtype=torch.uint8, device=device)
 
 
 class TrainStep:
@@ -211,6 +214,13 @@ class TrainStep:
         B.gs_grad_aggregate_adam_project(self.params.gaussians(), pa, self.bins.abi(), cam, self.raster, grads2d, m,
                                          v, B.AdamLrs(**self.lr), self.params.step_count, 0.9, 0.999, 1e-15,
                                          next_cam, pa, stream)
+
+    def fused_l1(self, cam: B.Camera, target, stream=None):
+        """Forward rasterization, L1 loss and the per-record backward in one kernel (from the
+        current bins); equal to forward rasterization, loss and backward_partials."""
+        f = self.frame
+        B.gs_raster_fused_l1(self.params.gaussians(), self.bins.abi(), cam, self.raster, target, f.color, f.t_final,
+                             f.n_trav, f.loss, f.n_trav_sum, f.fused_ws, stream)
 
     def backward_partials(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):
         f = self.frame

@@ -29,8 +29,9 @@ CSRC = os.path.join(HERE, "csrc")
 # sources each profiled kernel is compiled from (its own file, the headers it includes,
 # and the build flags)
 KERNEL_SOURCES = {
-    "k_raster_bwd": ["raster_bwd.hip", "raster.h", "kernels.h", "common.h"],
-    "k_raster_fwd": ["raster_fwd.hip", "raster.h", "common.h"],
+    "k_raster_bwd": ["raster_bwd.hip", "raster_walk.h", "raster.h", "kernels.h", "common.h"],
+    "k_raster_fwd": ["raster_fwd.hip", "raster_walk.h", "raster.h", "common.h"],
+    "k_raster_fused_l1": ["raster_fused.hip", "raster_walk.h", "raster.h", "kernels.h", "common.h"],
     "k_adam": ["optim.hip", "kernels.h", "common.h"],
     "k_grad_adam": ["project.hip", "raster.h", "kernels.h", "common.h"],
 }

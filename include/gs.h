@@ -259,6 +259,39 @@ gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_projected *proj, con
                             const gs_camera *cam, const gs_raster_params *p, float *grads2d,
                             gs_param_grads *grads3d, hipStream_t stream);
 
+/* Forward rasterization, L1 loss and the per-record part of the backward in one kernel
+ * (ByteSplat section 4.2, "Fused Rasterization Dataflow"): each 8x8 quadrant composites its
+ * pixels (Eq. 1), forms dL/dC = sign(C - target) / (3 W H) per channel at once (the L1 term
+ * of Eq. 2, tile-local) and runs the backward walk of Eq. 3 from registers, so the image,
+ * N_p and dL/dC are not read back.  Equal, bit for bit, to gs_raster_fwd, gs_loss_l1 and
+ * gs_raster_bwd_partials (without dL/dT) in sequence: color [H][W][3], t_final [H][W] and
+ * n_trav [H][W] are written as by gs_raster_fwd, and the gradient slots in bins->raster as by
+ * gs_raster_bwd_partials (follow with gs_grad_aggregate or gs_grad_aggregate_adam(_project)).
+ * target [H][W][3]: the reference image.  loss_out (device, may be NULL): the mean of
+ * |C - target|, equal to gs_loss_l1's up to the order of its double-precision sum.
+ * n_trav_sum (device, may be NULL): sum_p N_p is added to it, as in gs_raster_fwd.
+ * workspace: gs_raster_fused_l1_workspace_bytes(W, H) bytes (16-byte aligned) of per-wave
+ * partial sums.  Every tile takes this path: records stream through registers in batches,
+ * so no tile is too large for it. */
+size_t gs_raster_fused_l1_workspace_bytes(int32_t width, int32_t height);
+gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                             const gs_raster_params *p, const float *target, float *color, float *t_final,
+                             int32_t *n_trav, float *loss_out, unsigned long long *n_trav_sum, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Tile budget diagnostic (ByteSplat section 5.2, Eq. 7-9).  gs_tile_budget: B =
+ * floor((lds_budget_bytes - fixed_bytes) / bytes_per_gaussian), the number of Gaussian
+ * records a tile can keep on chip in a design that holds them there (Eq. 7); -1 for
+ * invalid arguments.  gs_tile_budget_report: for the tile lists in bins, per tile t with
+ * N_t entries, excess[t] = E_t = max(0, N_t - budget) (Eq. 8) and frac[t] = P_t = E_t / N_t,
+ * 0 for an empty tile (Eq. 9) (each may be NULL; tiles-long arrays); totals (device, may be
+ * NULL, 8-byte aligned): totals[0] += the number of tiles with E_t > 0, totals[1] += sum_t
+ * E_t.  The fused kernel above needs no budget (it streams); the report says how tiles
+ * would fare in one that does. */
+int64_t gs_tile_budget(int64_t lds_budget_bytes, int64_t fixed_bytes, int64_t bytes_per_gaussian);
+gs_status gs_tile_budget_report(const gs_bins *bins, const gs_camera *cam, int64_t budget, int32_t *excess,
+                                float *frac, unsigned long long *totals, hipStream_t stream);
+
 /* Learning rates of the fused step below, per parameter group (the SH coefficients split
  * into the DC term, planes 0..2, and the rest). */
 typedef struct {

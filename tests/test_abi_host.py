@@ -137,3 +137,42 @@ def test_scene_generators_are_seeded_and_shaped():
     assert abs(c.cameras[0].fx - 256 / math.tan(math.radians(30))) < 1e-9
     m2, r, d = scenes.projected_for_binning(1, 1000, 100, 50)
     assert (m2[:, 0] < 100).all() and (m2[:, 1] < 50).all() and (d > 0).all()
+
+
+def test_tile_budget_and_fused_workspace():
+    """ByteSplat Eq. 7: B = floor((M_budget - M_fixed) / M_g); -1 for arguments that do not
+    define a budget.  The fused kernel's workspace holds one 16-byte partial per 8x8
+    quadrant wave."""
+    assert B.gs_tile_budget(65536, 10240, 48) == (65536 - 10240) // 48 == 1152
+    assert B.gs_tile_budget(160 * 1024, 0, 48) == 3413
+    assert B.gs_tile_budget(1000, 1000, 48) == 0
+    assert B.gs_tile_budget(1000, 1001, 48) == -1
+    assert B.gs_tile_budget(1000, 0, 0) == -1
+    assert B.gs_tile_budget(-1, 0, 48) == -1
+    # per-wave partials, the final reduction's per-block sums (one per 1024 waves) and its ticket
+    waves = 120 * 68 * 4
+    assert B.gs_raster_fused_l1_workspace_bytes(1920, 1080) == 16 * waves + 16 * -(-waves // 1024) + 16
+    assert B.gs_raster_fused_l1_workspace_bytes(17, 1) == 16 * 8 + 16 + 16
+    assert B.gs_raster_fused_l1_workspace_bytes(0, 10) == 0
+
+
+def test_fused_l1_argument_errors_before_launch():
+    g = B.Gaussians(None, None, None, None, None, 0)
+    bins = B.Bins(None, None, None, None, 0, None)
+    ws = _Buf(16)
+    with pytest.raises(B.GsError) as e:   # no tile lists
+        B._check(B._lib.gs_raster_fused_l1(ctypes.byref(g), ctypes.byref(bins), ctypes.byref(_cam()),
+                                           ctypes.byref(B.make_params(0)), None, None, None, None, None, None,
+                                           ws.ptr, 16, None))
+    assert e.value.status == B.GS_ERR_INVALID_ARGUMENT
+    with pytest.raises(B.GsError) as e:
+        B._check(B._lib.gs_tile_budget_report(ctypes.byref(bins), ctypes.byref(_cam()), -1, None, None, None, None))
+    assert e.value.status == B.GS_ERR_INVALID_ARGUMENT
+
+
+class _Buf:
+    """A host buffer standing in for a device pointer in argument checks (never dereferenced)."""
+
+    def __init__(self, n):
+        self.mem = ctypes.create_string_buffer(n + 16)
+        self.ptr = ctypes.c_void_p((ctypes.addressof(self.mem) + 15) // 16 * 16)

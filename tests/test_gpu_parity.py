@@ -503,3 +503,90 @@ def test_ntrav_sum(name):
     torch.cuda.synchronize()
     assert torch.equal(shifted, f.n_trav)
     assert int(tot) == want and int(tot2) == want + 5
+
+
+# ------------------------------------------------------------------ fused forward + L1 + backward
+
+@pytest.mark.parametrize("name,t_min", [("tiny", 1e-4), ("tiny", 0.0), ("ragged_sh1", 1e-4), ("ragged_sh2", 1e-4),
+                                        ("offscreen_sh3", 1e-4), ("100k", 1e-4)])
+def test_fused_l1_matches_separate_calls(name, t_min):
+    """gs_raster_fused_l1 equals gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd_partials bit for
+    bit: image, T_final, N_p, and the per-Gaussian sums of the gradient slots; the loss up
+    to the order of its double sum; the same sum of N_p."""
+    log(f"fused fwd + L1 + bwd {name} t_min={t_min}")
+    sc = _scene(name)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree, t_min=t_min)
+    c = B.camera_from(cam)
+    tgt = sc.targets[0].to(DEV)
+    st = gpu_forward(sc, cam, rp)
+    f = st.frame
+    g = st.params.gaussians()
+    f.n_trav_sum.zero_()
+    B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, rp, f.color, f.t_final, f.n_trav, f.n_trav_sum)
+    st.loss(tgt)
+    st.backward_partials(c)
+    B.gs_grad_aggregate(g, st.proj.abi(), st.bins.abi(), c, rp, st.grads2d, None)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (f.color, f.t_final, f.n_trav, st.grads2d, f.loss, f.n_trav_sum)]
+    f.color.fill_(float("nan")); f.t_final.fill_(float("nan")); f.n_trav.fill_(-1)
+    f.loss.fill_(float("nan")); f.n_trav_sum.zero_(); st.grads2d.fill_(float("nan"))
+    st.fused_l1(c, tgt)
+    B.gs_grad_aggregate(g, st.proj.abi(), st.bins.abi(), c, rp, st.grads2d, None)
+    torch.cuda.synchronize()
+    for a, b in zip((f.color, f.t_final, f.n_trav, st.grads2d), ref[:4]):
+        assert torch.equal(a, b)
+    assert int(f.n_trav_sum) == int(ref[5]) > 0
+    assert abs(float(f.loss) - float(ref[4])) <= 1e-6 * abs(float(ref[4]))
+    assert float(st.grads2d.abs().max()) > 0.0
+
+
+def test_fused_l1_then_fused_adam_projection_matches_separate_step():
+    """A whole fused step (bin sort, fused forward + L1 + backward, fused end of step with the
+    next view's projection) equals the separate calls over two steps, bit for bit."""
+    sc = _scene("ragged_sh2")
+    cams = [sc.cameras[0], _moved_camera(sc.cameras[0])]
+    rp = B.make_params(sc.sh_degree)
+    tgt = sc.targets[0].to(DEV)
+    out = []
+    for fused in (False, True):
+        st = gpu_forward(sc, cams[0], rp)
+        for step in range(2):
+            c, nc = B.camera_from(cams[step % 2]), B.camera_from(cams[(step + 1) % 2])
+            if fused:
+                if step:
+                    st.bins.sort(st.proj, c, rp)
+                st.fused_l1(c, tgt)
+                st.aggregate_adam_project(c, nc)
+            else:
+                if step:
+                    st.forward(c)
+                st.loss(tgt)
+                st.backward_partials(c)
+                st.aggregate_adam(c)
+        torch.cuda.synchronize()
+        out.append((st.frame.color.clone(), st.params.data.clone(), st.params.m.clone(), st.params.v.clone()))
+    for a, b in zip(*out):
+        assert torch.equal(a, b)
+
+
+def test_tile_budget_report():
+    """ByteSplat Eq. 8 and Eq. 9 per tile against numpy on the tile lists of a sorted scene."""
+    sc = _scene("100k")
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    st = gpu_forward(sc, cam, rp)
+    T = st.bins.tiles
+    rng = st.bins.tile_ranges.cpu().numpy().astype(np.int64)
+    nt = rng[1:] - rng[:-1]
+    budget = int(np.percentile(nt[nt > 0], 60))
+    excess = torch.full((T,), -1, dtype=torch.int32, device=DEV)
+    frac = torch.full((T,), -1.0, dtype=torch.float32, device=DEV)
+    totals = torch.zeros(2, dtype=torch.int64, device=DEV)
+    B.gs_tile_budget_report(st.bins.abi(), B.camera_from(cam), budget, excess, frac, totals)
+    torch.cuda.synchronize()
+    e = np.maximum(0, nt - budget)
+    p = np.where(nt > 0, e / np.maximum(nt, 1), 0.0).astype(np.float32)
+    assert np.array_equal(excess.cpu().numpy(), e.astype(np.int32))
+    assert np.array_equal(frac.cpu().numpy(), p)
+    assert totals.tolist() == [int((e > 0).sum()), int(e.sum())] and int((e > 0).sum()) > 0
