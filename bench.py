@@ -318,6 +318,17 @@ def main():
                       for j in range(len(names))}
         per_kernel.update(timed_ms)
         step_ms = sorted(ev2[s][0].elapsed_time(ev2[s][-1]) for s in range(args.steps))
+    # ByteSplat Eq. 7-9 for the last step's tile lists: how many tiles a design that keeps a
+    # tile's records on chip could hold (64 KiB of LDS per tile, 256 pixels x 32 B of pixel
+    # state, 48-B records); the fused kernel streams records and runs every tile
+    lds_budget, fixed_bytes, rec_bytes = 64 * 1024, 256 * 32, 48
+    budget = B.gs_tile_budget(lds_budget, fixed_bytes, rec_bytes)
+    totals = torch.zeros(2, dtype=torch.int64, device=dev)
+    B.gs_tile_budget_report(st.bins.abi(), cams[(args.warmup + args.steps - 1) % nviews], budget, None, None, totals)
+    tiles_over, excess = (int(x) for x in totals.cpu())
+    tile_budget = {"B": budget, "lds_budget_bytes": lds_budget, "fixed_bytes": fixed_bytes, "bytes_per_gaussian": rec_bytes,
+                   "tiles": st.bins.tiles, "tiles_over_budget": tiles_over,
+                   "frac_tiles_within": round(1.0 - tiles_over / st.bins.tiles, 4), "sum_excess": excess}
     ms_step = wall * 1e3 / args.steps
     isect_step = isect_total / args.steps
     n = scene.n
@@ -375,6 +386,7 @@ def main():
         "tile_entries_per_step": round(kmean, 1),
         "quadrant_records_last_step": q_last,
         "visible_gaussians": n_vis,
+        "tile_budget": tile_budget,
         # Gaussian-pixel intersections over the two raster kernels' time (forward compositing
         # and the per-pixel backward with its per-quadrant sums)
         "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]) * 1e-3), 1)
