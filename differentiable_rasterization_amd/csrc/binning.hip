@@ -328,33 +328,82 @@ __global__ __launch_bounds__(256) void k_keys64(const uint32_t *__restrict__ tke
     keys[k] = ((uint64_t)(tkeys[k] & gsr::kTileMask) << 32) | (uint64_t)__float_as_uint(depth[ids[k]]);
 }
 
-// Tiles ordered by decreasing list length (bucketed by the bit length of the count, so
-// the order is heaviest first up to a factor of two), so that the longest tiles start
-// first and the short ones fill in behind them.  One workgroup.
-__global__ __launch_bounds__(1024) void k_tile_order(const int32_t *__restrict__ ranges, int T, int32_t *__restrict__ order)
+// The raster kernels run one wave per (tile, quadrant), in the order `order` gives (entry
+// w = tile * 4 + quadrant): waves by decreasing length of their quadrant record list,
+// bucketed four buckets per octave (the order within a bucket is arbitrary), so that the
+// longest lists start first and the short ones fill in behind them.  Two passes over the
+// waves: bucket and count (global histogram), then place.  whist and wcur [kWaveBuckets]
+// must be zero before the first pass.
+constexpr int kWaveBuckets = 129;   // 0: empty; 1 + 4 log2(len), 1..128
+
+__device__ __forceinline__ uint32_t wave_bucket(uint32_t len)
 {
-    __shared__ uint32_t hist[33];
-    __shared__ uint32_t pos[33];
-    if (threadIdx.x < 33) hist[threadIdx.x] = 0;
+    if (len == 0) return 0u;
+    return (__float_as_uint((float)len) >> 21) - (127u << 2) + 1u;   // exponent and two mantissa bits
+}
+
+__device__ __forceinline__ uint32_t wave_len(const int32_t *__restrict__ ranges, const uint64_t *__restrict__ bitmap,
+                                             const uint32_t *__restrict__ wpre, int64_t words, uint32_t w)
+{
+    const int t = (int)(w >> 2), q = (int)(w & 3u);
+    const int start = ranges[t], end = ranges[t + 1];
+    if (start >= end) return 0u;   // (the prefix counts of an empty list may be unset)
+    const uint64_t *bq = bitmap + (int64_t)q * words;
+    const uint32_t *wq = wpre + (int64_t)q * (words + 1);
+    return gsr::quad_prefix(bq, wq, (uint32_t)end) - gsr::quad_prefix(bq, wq, (uint32_t)start);
+}
+
+__global__ __launch_bounds__(256) void k_wave_hist(const int32_t *__restrict__ ranges, const uint64_t *__restrict__ bitmap,
+                                                   const uint32_t *__restrict__ wpre, int64_t words, uint32_t waves,
+                                                   uint8_t *__restrict__ wb, uint32_t *__restrict__ whist)
+{
+    __shared__ uint32_t h[kWaveBuckets];
+    for (int i = threadIdx.x; i < kWaveBuckets; i += 256) h[i] = 0;
     __syncthreads();
-    for (int t = threadIdx.x; t < T; t += blockDim.x) {
-        const uint32_t c = (uint32_t)(ranges[t + 1] - ranges[t]);
-        atomicAdd(&hist[c ? 32 - __clz(c) : 0], 1u);
+    const uint32_t w = blockIdx.x * 256 + threadIdx.x;
+    if (w < waves) {
+        const uint32_t bk = wave_bucket(wave_len(ranges, bitmap, wpre, words, w));
+        wb[w] = (uint8_t)bk;
+        atomicAdd(&h[bk], 1u);
     }
     __syncthreads();
+    for (int i = threadIdx.x; i < kWaveBuckets; i += 256)
+        if (h[i]) atomicAdd(&whist[i], h[i]);
+}
+
+__global__ __launch_bounds__(256) void k_wave_place(const uint8_t *__restrict__ wb, uint32_t waves,
+                                                    const uint32_t *__restrict__ whist, uint32_t *__restrict__ wcur,
+                                                    int32_t *__restrict__ order)
+{
+    __shared__ uint32_t first[kWaveBuckets];   // first position of each bucket (heaviest first)
+    __shared__ uint32_t h[kWaveBuckets];
     if (threadIdx.x == 0) {
         uint32_t acc = 0;
-        for (int b = 32; b >= 0; --b) {
-            pos[b] = acc;
-            acc += hist[b];
+        for (int b = kWaveBuckets - 1; b >= 0; --b) {
+            first[b] = acc;
+            acc += whist[b];
         }
     }
+    for (int i = threadIdx.x; i < kWaveBuckets; i += 256) h[i] = 0;
     __syncthreads();
-    for (int t = threadIdx.x; t < T; t += blockDim.x) {
-        const uint32_t c = (uint32_t)(ranges[t + 1] - ranges[t]);
-        const uint32_t p = atomicAdd(&pos[c ? 32 - __clz(c) : 0], 1u);
-        order[p] = t;
+    const uint32_t w = blockIdx.x * 256 + threadIdx.x;
+    uint32_t bk = 0, rank = 0;
+    if (w < waves) {
+        bk = wb[w];
+        rank = atomicAdd(&h[bk], 1u);
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kWaveBuckets; i += 256)
+        if (h[i]) h[i] = first[i] + atomicAdd(&wcur[i], h[i]);   // this block's run in the bucket
+    __syncthreads();
+    if (w < waves) order[h[bk] + rank] = (int32_t)w;
+}
+
+// The waves in index order (every list empty).
+__global__ __launch_bounds__(256) void k_wave_identity(uint32_t waves, int32_t *__restrict__ order)
+{
+    const uint32_t w = blockIdx.x * 256 + threadIdx.x;
+    if (w < waves) order[w] = (int32_t)w;
 }
 
 // Counts of an empty scene (n = 0).
@@ -372,8 +421,8 @@ __global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restr
 struct Layout {
     // zero region (cleared by k_keys_count at the start of every sort): tickets and
     // look-back status words of the scans
-    size_t zero, tickets, stD, stT, scC, scQ, scW, zero_bytes;
-    size_t dkA, dvA, dkB, dvB, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, hist, bytes;
+    size_t zero, tickets, whist, stD, stT, scC, scQ, scW, zero_bytes;
+    size_t dkA, dvA, dkB, dvB, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, hist, wb, bytes;
     int tbits;
 };
 
@@ -395,6 +444,7 @@ Layout layout(int64_t n, int64_t cap, int32_t tiles)
     const int64_t nw = gsr::kQuads * (gsr::raster_layout(n, cap, 1).words + 1);
     L.zero = o;
     L.tickets = take(16 * 4);
+    L.whist = take(2 * 4 * kWaveBuckets);   // wave-order histogram, then placement cursors
     L.stD = take(8 * (size_t)gsi::radix_scan_status_len((int64_t)nn, 32));
     L.stT = take(8 * (size_t)gsi::radix_scan_status_len((int64_t)cc, L.tbits));
     L.scC = take(8 * (size_t)gsi::lb_scan_tiles((int64_t)nn));
@@ -407,6 +457,7 @@ Layout layout(int64_t n, int64_t cap, int32_t tiles)
     L.klen = take(8);     // K if the lists fit, else 0
     L.tkA = take(4 * cc); L.tkB = take(4 * cc); L.tvA = take(8 * cc); L.tvB = take(8 * cc);
     L.hist = take(4 * (size_t)gsi::radix_hist_len(std::max<int64_t>((int64_t)nn, (int64_t)cc)));
+    L.wb = take((size_t)gsr::kQuads * (size_t)(tiles > 0 ? tiles : 1));   // bucket of each raster wave
     L.bytes = o;
     return L;
 }
@@ -462,6 +513,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     char *rb = static_cast<char *>(bins->raster);
     gsr::BinsHeader *hdr = reinterpret_cast<gsr::BinsHeader *>(rb + RL.hdr);
     int32_t *order = reinterpret_cast<int32_t *>(rb + RL.order);
+    const int64_t waves = (int64_t)gsr::kQuads * T;
     uint32_t *qoff = reinterpret_cast<uint32_t *>(rb + RL.qoff);
     // the quadrant prefix counts of empty lists: zero
     uint32_t *wpre0 = reinterpret_cast<uint32_t *>(rb + RL.wpre);
@@ -469,8 +521,8 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     if (n == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
         if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre0), nw0, 0, stream)) != GS_OK) return s;
-        k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
-        GS_LAUNCH_CHECK("k_tile_order");
+        k_wave_identity<<<(unsigned)ceil_div(waves, 256), 256, 0, stream>>>((uint32_t)waves, order);
+        GS_LAUNCH_CHECK("k_wave_identity");
         k_bins_empty<<<1, 1, 0, stream>>>(hdr, counts);
         GS_LAUNCH_CHECK("k_bins_empty");
         return GS_OK;
@@ -523,8 +575,8 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     if (cap == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
         if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre0), nw0, 0, stream)) != GS_OK) return s;
-        k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
-        GS_LAUNCH_CHECK("k_tile_order");
+        k_wave_identity<<<(unsigned)ceil_div(waves, 256), 256, 0, stream>>>((uint32_t)waves, order);
+        GS_LAUNCH_CHECK("k_wave_identity");
         return GS_OK;
     }
     if ((s = radix_sort_u32_u64(tkA, tvA, tkB, tvB, cap, tbits, hist, stT, tickets + kTkTile, &in_b, stream, klen)) !=
@@ -551,9 +603,16 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
         GS_LAUNCH_CHECK("k_keys64");
     }
 
-    // 5. the order in which tiles are rasterized
-    k_tile_order<<<1, 1024, 0, stream>>>(bins->tile_ranges, T, order);
-    GS_LAUNCH_CHECK("k_tile_order");
+    // 5. the order in which the (tile, quadrant) waves are rasterized
+    {
+        uint32_t *whist = (uint32_t *)(ws + L.whist), *wcur = whist + kWaveBuckets;
+        uint8_t *wb = (uint8_t *)(ws + L.wb);
+        const unsigned gw = (unsigned)ceil_div(waves, 256);
+        k_wave_hist<<<gw, 256, 0, stream>>>(bins->tile_ranges, bm, wpre, RL.words, (uint32_t)waves, wb, whist);
+        GS_LAUNCH_CHECK("k_wave_hist");
+        k_wave_place<<<gw, 256, 0, stream>>>(wb, (uint32_t)waves, whist, wcur, order);
+        GS_LAUNCH_CHECK("k_wave_place");
+    }
     return GS_OK;
 }
 

@@ -15,7 +15,8 @@
 //                                 word, so the records of tile t in quadrant q are
 //                                 qrec[P_q(start_t) .. P_q(end_t)), P_q(x) = wpre[q][x / 64]
 //                                 + set bits of bitmap q below entry x in its word
-//   order  [tiles] int32          tiles by decreasing list length (heaviest first)
+//   order  [4 * tiles] int32      the (tile, quadrant) waves, w = tile * 4 + quadrant, by
+//                                 decreasing quadrant record count (heaviest first)
 //   qoff   [n + 1] uint32         first gradient slot of Gaussian g: its quadrant records
 //                                 own slots qoff[g] .. qoff[g + 1], in the order of its
 //                                 entries and, within an entry, of the quadrants (qoff[n] =
@@ -149,7 +150,7 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     L.qrec = o;   o += align256((q4 + 2 * kRecPad) * sizeof(Rec));   // kRecPad spare records at each end
     L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
     L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);
-    L.order = o;  o += align256((size_t)(tiles > 0 ? tiles : 1) * 4);
+    L.order = o;  o += align256((size_t)kQuads * (size_t)(tiles > 0 ? tiles : 1) * 4);
     L.qoff = o;   o += align256((nn + 1) * 4);
     L.qgrad = o;  o += align256(q4 * kGradSlot * 4);
     L.qstamp = o; o += align256(q4 * kStampWords * 4);
@@ -262,17 +263,17 @@ __device__ __forceinline__ uint32_t quad_prefix(const uint64_t *__restrict__ bq,
     return p;
 }
 
-// Launch geometry shared by both raster kernels: 4 consecutive "slots" on the same XCD
-// are the 4 quadrants of one tile; tiles are interleaved over the 8 XCDs (block b runs
-// on XCD b mod 8) so that heavy tiles, which cluster spatially, spread over the chip.
-inline int64_t raster_grid(int tiles) { return (int64_t)gsi::kXcds * kQuads * gsi::ceil_div(tiles, gsi::kXcds); }
+// Launch geometry shared by the raster kernels: one single-wave block per (tile, quadrant),
+// block b running wave order[b], so the heaviest waves start first; consecutive blocks go
+// to the 8 XCDs in turn (block b runs on XCD b mod 8), so heavy waves, which cluster
+// spatially, spread over the chip.
+inline int64_t raster_grid(int tiles) { return (int64_t)kQuads * tiles; }
 
-__device__ __forceinline__ void raster_block(int &tile_idx, int &quad)
+__device__ __forceinline__ void raster_block(const int32_t *__restrict__ order, int &tile, int &quad)
 {
-    const int b = blockIdx.x;
-    const int slot = b >> 3;
-    tile_idx = (b & 7) + 8 * (slot >> 2);
-    quad = slot & 3;
+    const int w = order[blockIdx.x];
+    tile = w >> 2;
+    quad = w & 3;
 }
 
 // Pulls the cache lines of records [j, min(j + 64, jlim)) into L2 with one vector load

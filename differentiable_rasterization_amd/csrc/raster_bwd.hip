@@ -53,10 +53,8 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
                                                    const BinsHeader *__restrict__ hdr, float *__restrict__ qgrad,
                                                    uint32_t *__restrict__ qstamp)
 {
-    int tidx, q;
-    raster_block(tidx, q);
-    if (tidx >= T) return;
-    const int tile = order[tidx];
+    int tile, q;
+    raster_block(order, tile, q);
     const int lane = threadIdx.x;
     const int px = (tile % TX) * GS_TILE + (q & 1) * 8 + (lane & 7);
     const int py = (tile / TX) * GS_TILE + (q >> 1) * 8 + (lane >> 3);

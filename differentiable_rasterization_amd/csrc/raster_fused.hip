@@ -60,12 +60,10 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
     FusedPartial *__restrict__ part, uint32_t *__restrict__ final_ticket, const BinsHeader *__restrict__ hdr,
     float *__restrict__ qgrad, uint32_t *__restrict__ qstamp)
 {
-    int tidx, q;
-    raster_block(tidx, q);
-    if (tidx >= T) return;
-    if (tidx == 0 && q == 0 && threadIdx.x == 0) *final_ticket = 0u;   // for k_fused_final of this call
-    const int slot = tidx * kQuads + q;   // one partial per (tile, quadrant) wave
-    const int tile = order[tidx];
+    int tile, q;
+    raster_block(order, tile, q);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *final_ticket = 0u;   // for k_fused_final of this call
+    const int slot = blockIdx.x;   // one partial per (tile, quadrant) wave
     const int lane = threadIdx.x;
     const int px = (tile % TX) * GS_TILE + (q & 1) * 8 + (lane & 7);
     const int py = (tile / TX) * GS_TILE + (q >> 1) * 8 + (lane >> 3);
@@ -113,14 +111,17 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
     if (!listed) return;
     const int nmax = max(0, min(gsd::wave_max_i32(np), end - start));
     const uint32_t jb = quad_prefix(bq, wq, (uint32_t)(start + nmax));
-    bwd_walk(qrec, j0, jb, fx, fy, start, np, G0, G1, G2, Z, alpha_min, alpha_max, hdr->epoch, qgrad, qstamp);
+    // the stamp of this call: the header's epoch advanced by one (k_fused_final stores it)
+    bwd_walk(qrec, j0, jb, fx, fy, start, np, G0, G1, G2, Z, alpha_min, alpha_max, hdr->epoch + 1u, qgrad, qstamp);
 }
 
 // The loss and sum_p N_p from the per-wave partials.  Each block adds kFinalSpan partials
 // (four independent loads per thread, then a fixed tree) into its block sum; the block that
 // finishes last (by a ticket) adds the block sums in block order and writes the results,
 // so the result does not depend on which block finished last.  The ticket is cleared by
-// k_raster_fused_l1 of the same call.
+// k_raster_fused_l1 of the same call.  The last block also advances the header's epoch to
+// the stamp k_raster_fused_l1 wrote (epoch + 1), so the per-Gaussian sums that follow read
+// this call's slots.
 constexpr int kFinalSpan = 1024;
 
 __device__ __forceinline__ void block_sum(double &l, unsigned long long &c, double *rl, unsigned long long *rn)
@@ -138,7 +139,8 @@ __device__ __forceinline__ void block_sum(double &l, unsigned long long &c, doub
 
 __global__ __launch_bounds__(256) void k_fused_final(const FusedPartial *__restrict__ part, int n, double inv,
                                                      FusedPartial *__restrict__ block_part, uint32_t *__restrict__ ticket,
-                                                     float *__restrict__ loss, unsigned long long *__restrict__ n_sum)
+                                                     BinsHeader *__restrict__ hdr, float *__restrict__ loss,
+                                                     unsigned long long *__restrict__ n_sum)
 {
     __shared__ double rl[4];
     __shared__ unsigned long long rn[4];
@@ -181,6 +183,7 @@ __global__ __launch_bounds__(256) void k_fused_final(const FusedPartial *__restr
     if (threadIdx.x == 0) {
         if (loss) *loss = (float)(l * inv);
         if (n_sum && c) atomicAdd(n_sum, c);
+        hdr->epoch = hdr->epoch + 1u;
     }
 }
 
@@ -208,7 +211,6 @@ __global__ __launch_bounds__(256) void k_tile_budget(const int32_t *__restrict__
     }
 }
 
-__global__ void k_new_epoch_fused(BinsHeader *__restrict__ hdr) { hdr->epoch = hdr->epoch + 1u; }
 
 }  // namespace
 
@@ -266,8 +268,6 @@ extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bi
     FusedPartial *part = reinterpret_cast<FusedPartial *>(wsb + fw.part);
     FusedPartial *block_part = reinterpret_cast<FusedPartial *>(wsb + fw.block_part);
     uint32_t *ticket = reinterpret_cast<uint32_t *>(wsb + fw.ticket);
-    k_new_epoch_fused<<<1, 1, 0, stream>>>(hdr);
-    GS_LAUNCH_CHECK("k_new_epoch_fused");
     k_raster_fused_l1<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
         bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order),
         reinterpret_cast<const float4 *>(rb + L.qrec) + kRecPad * kRecF4,
@@ -276,11 +276,9 @@ extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bi
         color, t_final, n_trav, part, ticket, hdr, reinterpret_cast<float *>(rb + L.qgrad),
         reinterpret_cast<uint32_t *>(rb + L.qstamp));
     GS_LAUNCH_CHECK("k_raster_fused_l1");
-    if (loss_out || n_trav_sum) {
-        k_fused_final<<<(unsigned)fw.blocks, 256, 0, stream>>>(part, fw.waves, 1.0 / (double)m, block_part, ticket,
-                                                              loss_out, n_trav_sum);
-        GS_LAUNCH_CHECK("k_fused_final");
-    }
+    k_fused_final<<<(unsigned)fw.blocks, 256, 0, stream>>>(part, fw.waves, 1.0 / (double)m, block_part, ticket, hdr,
+                                                          loss_out, n_trav_sum);
+    GS_LAUNCH_CHECK("k_fused_final");
     return GS_OK;
 }
 

@@ -21,10 +21,8 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
                                                    float *__restrict__ out_c, float *__restrict__ out_t,
                                                    int32_t *__restrict__ out_n)
 {
-    int tidx, q;
-    raster_block(tidx, q);
-    if (tidx >= T) return;
-    const int tile = order[tidx];
+    int tile, q;
+    raster_block(order, tile, q);
     const int lane = threadIdx.x;
     const int px = (tile % TX) * GS_TILE + (q & 1) * 8 + (lane & 7);
     const int py = (tile / TX) * GS_TILE + (q >> 1) * 8 + (lane >> 3);

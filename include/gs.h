@@ -160,7 +160,7 @@ gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raste
 
 /* Bytes of the gs_bins.raster buffer for n Gaussians, `capacity` list entries and a W x H
  * image: 2 quadrant records (48 B), 2 gradient slots (48 B) with their stamps (8 B) and 4
- * quadrant bits per entry, plus 4 B per Gaussian, 4 B per tile and a 256-byte header. */
+ * quadrant bits per entry, plus 4 B per Gaussian, 16 B per tile and a 256-byte header. */
 size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
 
 /* Workspace bytes gs_bin_sort needs for n Gaussians, `capacity` list entries and the
