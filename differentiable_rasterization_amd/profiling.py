@@ -120,6 +120,10 @@ def counters(path: str, kernels) -> str:
             # SQ_ACTIVE_INST_VALU sums over the CUs; GRBM_GUI_ACTIVE over the 8 XCDs
             busy = 100.0 * c["SQ_ACTIVE_INST_VALU"] / 256.0 / (c["GRBM_GUI_ACTIVE"] / 8.0)
             out.append(f"    VALU busy % (SQ_ACTIVE_INST_VALU / 256 CU / GRBM_GUI_ACTIVE per XCD) {busy:.1f}")
+        if "SQ_INSTS_VALU" in c and "GRBM_GUI_ACTIVE" in c:
+            # a CU's four SIMDs together issue at most one wave64 VALU instruction per cycle
+            issue = 100.0 * c["SQ_INSTS_VALU"] / 256.0 / (c["GRBM_GUI_ACTIVE"] / 8.0)
+            out.append(f"    VALU issue % (SQ_INSTS_VALU / 256 CU / GRBM_GUI_ACTIVE per XCD) {issue:.1f}")
         if "SQ_INSTS_VALU" in c and "SQ_WAVES" in c and c["SQ_WAVES"] > 0:
             out.append(f"    VALU instructions per wave {c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.1f}")
     return "\n".join(out)
