@@ -1,6 +1,6 @@
 """Benchmark of the one-GPU 3D Gaussian splatting training step on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m|100k|10m|tiny] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m|100k|10m|20m|tiny] [--no-cpu-baseline]
                     [--cpu-rows R] [--copy-calibration-mib M]
 
 A step is one training iteration on one view: projection -> gs_bin_sort ->
@@ -21,6 +21,13 @@ number of list entries each pixel composites, N_p of Eq. 1 in ByteSplat section 
 per second of whole training step; ms_per_step = train-step milliseconds.  Per-kernel
 times come from HIP events recorded on the stream the kernels run on (timing-only events
 without the system-scope fence, see TimingEvent).
+
+--workload 20m measures the partitioned step instead (PartitionedStep): 20M Gaussians at
+3840x2160 in four camera-space depth slabs of 5M, each rendered on its own and
+over-composited, L1 on the composite, the composite backward, each slab's backward
+rasterization and per-Gaussian sum, compaction of its non-zero gradient records, their
+decoding into the slab owner's gradient planes, and the owner's projection backward and
+Adam; every call is timed with events and reported in `kernels`.
 
 roofline: the longer of the backward raster kernel (k_raster_fused_l1 by default,
 k_raster_bwd with --separate-raster; bound by VALU arithmetic, its algorithmic work is
@@ -67,7 +74,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="1m", choices=["1m", "100k", "10m", "tiny"])
+    ap.add_argument("--workload", default="1m", choices=["1m", "100k", "10m", "20m", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1080, help="image rows the oracle baseline composites")
     ap.add_argument("--unfused", action="store_true",
@@ -111,6 +118,19 @@ def hbm_bytes(kernel, n, n_vis, k_sh, n_isect, n_px):
         return 36 * n_isect + n * (11 + 3 * k_sh) * 24
     if kernel == "grad_adam_project":                               # the same + the next view's records
         return 36 * n_isect + n * (11 + 3 * k_sh) * 24 + n_vis * 96 + (n - n_vis) * 12
+    return None
+
+
+def partition_bytes(kernel, parts, n_px, n, records):
+    """Algorithmic HBM bytes per call of the partitioned step's own kernels."""
+    if kernel == "composite":          # C_k, T_k read; C, T written
+        return (16 * parts + 16) * n_px
+    if kernel == "composite_bwd":      # C_k, T_k and dL/dC read; dL/dC_k, dL/dT_k written
+        return (32 * parts + 12) * n_px
+    if kernel == "compact":            # grads2d read, records and the bitmap written
+        return 36 * n + 40 * records + n // 8
+    if kernel == "decode":             # records read; 9 fields read and written (zeroing: 36 B per Gaussian)
+        return 40 * records + 72 * records + 36 * n
     return None
 
 
@@ -185,12 +205,164 @@ def cpu_baseline(scene, rows):
                       f"compositing backward of {rows} rows x {W} px ({isect} intersections) in {dt:.1f} s"}
 
 
+class CallTimer:
+    """Timing events around calls, summed by name after a synchronisation."""
+
+    def __init__(self):
+        self.marks = []
+
+    def __call__(self, name):
+        timer = self
+
+        class _Ctx:
+            def __enter__(self):
+                self.a = TimingEvent()
+                self.a.record()
+
+            def __exit__(self, *exc):
+                b = TimingEvent()
+                b.record()
+                timer.marks.append((name, self.a, b))
+        return _Ctx()
+
+    def totals(self):
+        out = {}
+        for name, a, b in self.marks:
+            out[name] = out.get(name, 0.0) + a.elapsed_time(b)
+        return out
+
+
+def main_partitioned(args):
+    """The partitioned step of --workload 20m (see the module docstring)."""
+    import math
+    import torch
+    from differentiable_rasterization_amd import binding as B
+    from differentiable_rasterization_amd import pipeline as PL
+    from differentiable_rasterization_amd import scenes
+
+    dev = "cuda"
+    scene = scenes.scene_partitioned_4k()
+    desc = "20M Gaussians SH3, 256 skewed anisotropic clusters, 3840x2160, 1 view, 4 depth slabs of 5M"
+    subs = scenes.slab_scenes(scene)
+    cam = B.camera_from(scene.cameras[0])
+    target = scene.targets[0].to(dev)
+    W, H = scene.cameras[0].width, scene.cameras[0].height
+    slabs = [PL.GaussianParams.from_scene(s, dev) for s in subs]
+    del subs
+    # the slabs are disjoint and depth-ordered, so each projects without a depth window
+    ps = PL.PartitionedStep(slabs, [(0.0, math.inf)] * len(slabs), W, H, dev, t_min=1e-4)
+    ps.forward(cam)
+    for st in ps.parts:
+        st.bins._alloc(int(st.bins.capacity * 1.3) + 4096)
+    torch.cuda.synchronize()
+
+    def one_step(t):
+        for k, st in enumerate(ps.parts):
+            with t("project"):
+                B.gs_project(st.params.gaussians(), cam, st.raster, st.proj.abi())
+            with t("bin_sort"):
+                st.bins.sort(st.proj, cam, st.raster)
+            with t("raster_fwd"):
+                f = st.frame
+                B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), cam, st.raster, f.color, f.t_final, f.n_trav,
+                                f.n_trav_sum)
+        with t("composite"):
+            ps.composite()
+        with t("loss"):
+            ps.loss(target)
+        with t("composite_bwd"):
+            ps.composite_backward()
+        for k, st in enumerate(ps.parts):
+            with t("raster_bwd"):
+                st.backward_partials(cam, dL_dcolor=ps.dcs[k], dL_dt=ps.dts[k])
+            with t("grad_aggregate"):
+                B.gs_grad_aggregate(st.params.gaussians(), st.proj.abi(), st.bins.abi(), cam, st.raster,
+                                    st.grads2d, None)
+            with t("compact"):
+                ps.compact_part(k)
+            with t("decode"):
+                ps.decode_part(k)
+            with t("project_bwd"):
+                B.gs_project_bwd(st.params.gaussians(), cam, st.raster, ps.owner_g2[k], st.params.param_grads())
+            with t("adam"):
+                st.adam()
+
+    for _ in range(args.warmup):
+        one_step(CallTimer())
+    torch.cuda.synchronize()
+    for st in ps.parts:
+        st.frame.n_trav_sum.zero_()
+    timer = CallTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel = {nm: ms / args.steps for nm, ms in timer.totals().items()}
+    isect_step = sum(int(st.frame.n_trav_sum.item()) for st in ps.parts) / args.steps
+    parts = len(ps.parts)
+    n = sum(st.params.n for st in ps.parts)
+    n_vis = sum(int((st.proj.radii[:, 0] > 0).sum().item()) for st in ps.parts)
+    k_isect = sum(st.bins.n_isect for st in ps.parts)
+    records = sum(ps.r)
+    k_sh = scene.k_sh
+    kernels = {}
+    for nm, ms in per_kernel.items():
+        entry = {"ms": round(ms, 4)}
+        by = partition_bytes(nm, parts, W * H, n, records)
+        if by is None:
+            by = hbm_bytes(nm, n, n_vis, k_sh, k_isect, W * H)
+        if by is not None:
+            entry.update(bound="hbm", algorithmic_bytes=int(by), achieved_GBs=round(by / (ms * 1e-3) / 1e9, 1),
+                         frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        elif nm in FLOP_PER_PAIR:
+            fl = FLOP_PER_PAIR[nm] * isect_step
+            tf = fl / (ms * 1e-3) / 1e12
+            entry.update(bound="alu", algorithmic_flop=int(fl), achieved_TFLOPs=round(tf, 3),
+                         frac=round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         isect_per_s=round(isect_step / (ms * 1e-3), 1))
+        kernels[nm] = entry
+    dom = max(per_kernel, key=per_kernel.get)
+    d = kernels[dom]
+    kern = {"raster_bwd": "k_raster_bwd", "raster_fwd": "k_raster_fwd", "bin_sort": "gs_bin_sort"}.get(dom, dom)
+    if d.get("bound") == "alu":
+        roof = {"kernel": kern, "bound": "alu", "achieved": d["achieved_TFLOPs"], "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": d["frac"], "traffic": None, "flop_per_pair": FLOP_PER_PAIR[dom],
+                "pairs_per_launch": round(isect_step / parts, 1), "launch_ms": round(d["ms"] / parts, 4)}
+    else:
+        roof = {"kernel": kern, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["frac"], "traffic": None, "algorithmic_bytes": d["algorithmic_bytes"],
+                "launch_ms": d["ms"]}
+    out = {
+        "metric": METRIC, "value": round(isect_step * args.steps / wall, 1), "unit": "Gaussian-pixel intersections/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H], "views": 1,
+                   "slabs": parts, "slab_gaussians": [st.params.n for st in ps.parts],
+                   "step": "per slab projection + binning + forward; composite; L1; composite backward; per slab "
+                           "backward raster + per-Gaussian sum + compaction + decoding + projection backward + Adam"},
+        "roofline": roof,
+        "intersections_per_step": round(isect_step, 1),
+        "tile_entries_per_step": k_isect,
+        "records_per_step": records,
+        "visible_gaussians": n_vis,
+        "kernels_note": "every call timed with events in the timed steps; summed over the slabs",
+        "kernels": kernels,
+        "device": torch.cuda.get_device_name(0),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "20m":
+        return main_partitioned(args)
     import torch
     from differentiable_rasterization_amd import binding as B
     from differentiable_rasterization_amd import pipeline as PL

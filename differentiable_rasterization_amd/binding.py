@@ -30,7 +30,7 @@ EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes",
             "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project",
             "gs_raster_fused_l1", "gs_raster_fused_l1_workspace_bytes", "gs_tile_budget", "gs_tile_budget_report",
             "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
-            "gs_compact_workspace_bytes", "gs_compact_grads", "gs_last_error")
+            "gs_compact_workspace_bytes", "gs_compact_grads", "gs_decode_grads", "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -87,6 +87,11 @@ class AdamGroup(ctypes.Structure):
                 ("n", ctypes.c_int64), ("lr", ctypes.c_float)]
 
 
+class GradRecords(ctypes.Structure):
+    _fields_ = [("records", ctypes.c_void_p), ("r", ctypes.c_int64), ("index_base", ctypes.c_uint32),
+                ("owner_index", ctypes.c_void_p), ("n_part", ctypes.c_int64)]
+
+
 _P = ctypes.POINTER
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
@@ -121,6 +126,7 @@ _SIGS = {
     "gs_composite_over_bwd": (_i32, [_P(_vp), _P(_vp), _i32, _i64, _f32, _vp, _vp, _P(_vp), _P(_vp), _vp]),
     "gs_compact_workspace_bytes": (_sz, [_i64]),
     "gs_compact_grads": (_i32, [_vp, _i64, ctypes.c_uint32, _vp, _vp, _P(_i64), _vp, _sz, _vp]),
+    "gs_decode_grads": (_i32, [_P(GradRecords), _i32, _vp, _i64, _vp, _vp]),
     "gs_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -332,3 +338,12 @@ def gs_compact_grads(grads2d, n, index_base, records, bitmap, workspace, stream=
     _check(_lib.gs_compact_grads(_ptr(grads2d), n, index_base, _ptr(records), _ptr(bitmap), ctypes.byref(r),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return r.value
+
+
+def gs_decode_grads(parts, grads2d, n_owner, rejected=None, stream=None):
+    """parts: list of (records, r, index_base, owner_index or None, n_part); adds the
+    records' fields into grads2d [9][n_owner]."""
+    arr = (GradRecords * max(len(parts), 1))()
+    for i, (rec, r, base, owner, n_part) in enumerate(parts):
+        arr[i] = GradRecords(_ptr(rec), int(r), int(base), _ptr(owner), int(n_part))
+    _check(_lib.gs_decode_grads(arr, len(parts), _ptr(grads2d), int(n_owner), _ptr(rejected), _stream(stream)))

@@ -125,6 +125,63 @@ __global__ __launch_bounds__(256) void k_compact_write(const float *__restrict__
     }
 }
 
+// Owner-side decoding of compacted records (ByteSplat section 6.2): each record's
+// partition position is mapped through the forward-communication index of its
+// partition to the owner's Gaussian, and its non-zero fields are added to the owner's
+// gradient planes with fp32 atomics -- a Gaussian sent to several renderers receives
+// one record from each, so the adds may collide.  One block decodes 256 records of one
+// partition; they are staged through LDS so the 40-byte records are read with
+// coalesced dword loads.
+constexpr int kDecodeRecords = 256;
+constexpr int kRecordWords = 10;
+
+struct DecodeParts {
+    const uint32_t *rec[kMaxParts];
+    const uint32_t *map[kMaxParts];   // NULL: identity
+    uint32_t base[kMaxParts];
+    uint32_t n_part[kMaxParts];
+    uint32_t r[kMaxParts];
+    uint32_t first_block[kMaxParts + 1];
+    int k;
+};
+
+__global__ __launch_bounds__(256) void k_decode_grads(DecodeParts D, float *__restrict__ g2, uint32_t n_owner,
+                                                      uint32_t *__restrict__ rejected)
+{
+    __shared__ uint32_t st[kDecodeRecords * kRecordWords];
+    const uint32_t b = blockIdx.x;
+    int p = 0;
+    while (p + 1 < D.k && b >= D.first_block[p + 1]) ++p;   // uniform: kernel arguments live in SGPRs
+    const uint32_t r0 = (b - D.first_block[p]) * kDecodeRecords;
+    const uint32_t cnt = min((uint32_t)kDecodeRecords, D.r[p] - r0);
+    const uint32_t *src = D.rec[p] + (size_t)r0 * kRecordWords;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int w = 0; w < kRecordWords; ++w) {
+        const uint32_t j = (uint32_t)(w * kDecodeRecords + t);
+        if (j < cnt * kRecordWords) st[j] = src[j];
+    }
+    __syncthreads();
+    bool bad = false;
+    if ((uint32_t)t < cnt) {
+        const uint32_t *rw = st + t * kRecordWords;
+        const uint32_t i = rw[0] - D.base[p];   // wraps to a large value below the base
+        uint32_t o = 0xFFFFFFFFu;
+        if (i < D.n_part[p]) o = D.map[p] ? D.map[p][i] : i;
+        if (o < n_owner) {
+#pragma unroll
+            for (int f = 0; f < 9; ++f) {
+                const float v = __uint_as_float(rw[1 + f]);
+                if (v != 0.0f) unsafeAtomicAdd(g2 + (size_t)f * n_owner + o, v);
+            }
+        } else {
+            bad = true;
+        }
+    }
+    const uint64_t m = __ballot(bad);
+    if (rejected && m && (t & 63) == 0) atomicAdd(rejected, (uint32_t)__popcll(m));
+}
+
 gs_status fill_parts(Parts &P, const float *const *c_k, const float *const *t_k, int32_t k, int64_t n_px)
 {
     using namespace gsi;
@@ -222,5 +279,44 @@ extern "C" gs_status gs_compact_grads(const float *grads2d, int64_t n, uint32_t 
     GS_HIP(hipMemcpyAsync(&R, total, sizeof(R), hipMemcpyDeviceToHost, stream));
     GS_HIP(hipStreamSynchronize(stream));
     *r_out = (int64_t)R;
+    return GS_OK;
+}
+
+extern "C" gs_status gs_decode_grads(const gs_grad_records *parts, int32_t k, float *grads2d, int64_t n_owner,
+                                     uint32_t *rejected, hipStream_t stream)
+{
+    using namespace gsi;
+    if (k < 0 || k > kMaxParts) return fail(GS_ERR_INVALID_ARGUMENT, "k must lie in [0, 16]");
+    if (n_owner < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n_owner < 0");
+    if (n_owner >= 0xFFFFFFFFll) return fail(GS_ERR_UNSUPPORTED, "n_owner >= 2^32 - 1");
+    if (k > 0 && !parts) return fail(GS_ERR_INVALID_ARGUMENT, "parts is NULL");
+    DecodeParts D = {};
+    uint64_t blocks = 0;
+    for (int i = 0; i < k; ++i) {
+        const gs_grad_records &q = parts[i];
+        if (q.r < 0 || q.n_part < 0) return fail(GS_ERR_INVALID_ARGUMENT, "partition %d: r or n_part < 0", i);
+        if (q.r > 0xFFFFFFFFll || q.n_part > 0xFFFFFFFFll)
+            return fail(GS_ERR_UNSUPPORTED, "partition %d: r or n_part >= 2^32", i);
+        if (q.r > 0 && !q.records) return fail(GS_ERR_INVALID_ARGUMENT, "partition %d: records is NULL", i);
+        if (!aligned(q.records, 4) || !aligned(q.owner_index, 4))
+            return fail(GS_ERR_INVALID_ARGUMENT, "partition %d: records / owner_index must be 4-byte aligned", i);
+        D.rec[i] = static_cast<const uint32_t *>(q.records);
+        D.map[i] = q.owner_index;
+        D.base[i] = q.index_base;
+        D.n_part[i] = (uint32_t)q.n_part;
+        D.r[i] = (uint32_t)q.r;
+        D.first_block[i] = (uint32_t)blocks;
+        blocks += (uint64_t)ceil_div(q.r, kDecodeRecords);
+    }
+    D.k = k;
+    D.first_block[k] = (uint32_t)blocks;
+    if (blocks == 0) return GS_OK;
+    if (blocks > 0x7FFFFFFFull) return fail(GS_ERR_UNSUPPORTED, "too many records");
+    if (n_owner == 0 && !rejected) return GS_OK;   // every record would be rejected, uncounted
+    if (n_owner > 0 && !grads2d) return fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
+    if (!aligned(grads2d, 4) || !aligned(rejected, 4))
+        return fail(GS_ERR_INVALID_ARGUMENT, "grads2d / rejected must be 4-byte aligned");
+    k_decode_grads<<<(unsigned)blocks, 256, 0, stream>>>(D, grads2d, (uint32_t)n_owner, rejected);
+    GS_LAUNCH_CHECK("k_decode_grads");
     return GS_OK;
 }

@@ -5,6 +5,9 @@ of the computation runs in libgsmi's kernels:
 
     gs_project -> gs_bin_sort -> gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd -> gs_adam_step
 
+and of one training step over depth slabs rendered separately and over-composited
+(PartitionedStep).
+
 Parameters, gradients and the two Adam moments each live in one contiguous
 [planes][N] float32 buffer (structure of arrays), so every kernel streams
 coalesced planes and Adam runs as one launch over six parameter groups.
@@ -232,3 +235,105 @@ class TrainStep:
         self.loss(target, stream)
         self.backward(cam, stream=stream)
         self.adam(stream)
+
+
+class PartitionedStep:
+    """One view's training step over Gaussians split into camera-space depth slabs.
+
+    Forward: each slab projects, bins and composites its own Gaussians into a partial
+    image (C_k, T_k); the partials are over-composited in depth order (Splaxel sections
+    3.4 and 4.2: convex partitions in depth order reproduce the global blending order;
+    section 4.3: partitions behind a saturated pixel are skipped).  Loss: L1 on the
+    composite.  Backward: the composite backward gives each slab (dL/dC_k, dL/dT_k); each
+    slab's backward rasterization and per-Gaussian sum give its screen-space gradients,
+    which are compacted to the records of non-zero Gaussians (ByteSplat section 6.1) and
+    decoded into the owner's gradient planes (section 6.2).  On one GPU a slab's renderer
+    and owner are the same; the exchange between them is left out.  The owner then runs
+    the projection backward and Adam for its Gaussians.
+
+    slabs: one GaussianParams per slab (disjoint Gaussians); windows: the slabs' depth
+    windows [lo, hi) of the projection (Gaussians outside are culled)."""
+
+    def __init__(self, slabs, windows, width, height, device="cuda", t_min=1e-4, lr=DEFAULT_LR, capacity=0):
+        self.width, self.height, self.t_min = width, height, t_min
+        self.n_px = width * height
+        self.parts = []
+        for params, (lo, hi) in zip(slabs, windows):
+            rp = B.make_params(params.sh_degree, t_min=t_min, depth_lo=lo, depth_hi=hi)
+            self.parts.append(TrainStep(params, width, height, device, raster=rp, lr=lr, capacity=capacity))
+        z = lambda *shape: torch.zeros(*shape, dtype=torch.float32, device=device)
+        self.color, self.t_final = z(height, width, 3), z(height, width)
+        self.loss_value, self.dL_dcolor = z(1), z(height, width, 3)
+        self.loss_ws = torch.empty(max(B.gs_loss_workspace_bytes(self.n_px), 8), dtype=torch.uint8, device=device)
+        self.dcs = [z(height, width, 3) for _ in self.parts]
+        self.dts = [z(height, width) for _ in self.parts]
+        self.records, self.bitmaps, self.compact_ws, self.owner_g2, self.r = [], [], [], [], []
+        for st in self.parts:
+            n = max(st.params.n, 1)
+            self.records.append(torch.zeros(n, 10, dtype=torch.int32, device=device))
+            self.bitmaps.append(torch.zeros((n + 31) // 32, dtype=torch.int32, device=device))
+            self.compact_ws.append(torch.empty(max(B.gs_compact_workspace_bytes(n), 256), dtype=torch.uint8,
+                                               device=device))
+            self.owner_g2.append(z(9, n))
+            self.r.append(0)
+
+    # -- forward
+    def render_part(self, k, cam: B.Camera, stream=None):
+        self.parts[k].forward(cam, stream)
+
+    def composite(self, stream=None):
+        B.gs_composite_over([st.frame.color for st in self.parts], [st.frame.t_final for st in self.parts],
+                            self.n_px, self.t_min, self.color, self.t_final, stream)
+
+    def forward(self, cam: B.Camera, stream=None):
+        for k in range(len(self.parts)):
+            self.render_part(k, cam, stream)
+        self.composite(stream)
+
+    def loss(self, target, stream=None):
+        B.gs_loss_l1(self.color, target, self.n_px, self.loss_value, self.dL_dcolor, self.loss_ws, stream)
+
+    # -- backward
+    def composite_backward(self, stream=None):
+        B.gs_composite_over_bwd([st.frame.color for st in self.parts], [st.frame.t_final for st in self.parts],
+                                self.n_px, self.t_min, self.dL_dcolor, None, self.dcs, self.dts, stream)
+
+    def backward_part(self, k, cam: B.Camera, stream=None):
+        """The slab's backward rasterization and per-Gaussian sum into its grads2d."""
+        st = self.parts[k]
+        st.backward_partials(cam, dL_dcolor=self.dcs[k], dL_dt=self.dts[k], stream=stream)
+        B.gs_grad_aggregate(st.params.gaussians(), st.proj.abi(), st.bins.abi(), cam, st.raster, st.grads2d, None,
+                            stream)
+
+    def compact_part(self, k, stream=None) -> int:
+        """Non-zero records of the slab's gradients (reads the count back to the host)."""
+        st = self.parts[k]
+        self.r[k] = B.gs_compact_grads(st.grads2d, st.params.n, 0, self.records[k], self.bitmaps[k],
+                                       self.compact_ws[k], stream)
+        return self.r[k]
+
+    def decode_part(self, k, stream=None):
+        """The owner's side: its gradient planes rebuilt from the slab's records."""
+        n = self.parts[k].params.n
+        self.owner_g2[k].zero_()
+        B.gs_decode_grads([(self.records[k], self.r[k], 0, None, n)], self.owner_g2[k], n, None, stream)
+
+    def update_part(self, k, cam: B.Camera, stream=None):
+        """The owner's projection backward from the decoded gradients, then Adam."""
+        st = self.parts[k]
+        B.gs_project_bwd(st.params.gaussians(), cam, st.raster, self.owner_g2[k], st.params.param_grads(), stream)
+        st.adam(stream)
+
+    def backward(self, cam: B.Camera, stream=None):
+        self.composite_backward(stream)
+        for k in range(len(self.parts)):
+            self.backward_part(k, cam, stream)
+            self.compact_part(k, stream)
+            self.decode_part(k, stream)
+
+    def step(self, cam: B.Camera, target, stream=None):
+        self.forward(cam, stream)
+        self.loss(target, stream)
+        self.backward(cam, stream)
+        for k in range(len(self.parts)):
+            self.update_part(k, cam, stream)

@@ -194,6 +194,21 @@ def _depth_slabs(means, viewmat, parts):
     return [(bounds[k], bounds[k + 1]) for k in range(parts)]
 
 
+def slab_scenes(sc: Scene) -> list:
+    """The scene's Gaussians split by its depth slabs into one scene per slab (camera-space
+    depth of view 0 in double precision, window [lo, hi)); each keeps the cameras and
+    targets.  Slabs are disjoint and ordered front to back."""
+    M = sc.cameras[0].viewmat.double().reshape(4, 4)
+    z = (M[2, :3].unsqueeze(1) * sc.means.double()).sum(0) + M[2, 3]
+    out = []
+    for k, (lo, hi) in enumerate(sc.depth_slabs):
+        idx = torch.nonzero((z >= lo) & (z < hi)).squeeze(1)
+        pick = lambda t: t[..., idx].contiguous()
+        out.append(Scene(f"{sc.name}_slab{k}", sc.sh_degree, pick(sc.means), pick(sc.log_scales), pick(sc.quats),
+                         pick(sc.opacity_logits), pick(sc.sh), sc.cameras, sc.targets, adam=sc.adam))
+    return out
+
+
 # --------------------------------------------------------------------------- configs
 
 def scene_tiny(seed: int = 1) -> Scene:

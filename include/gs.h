@@ -20,7 +20,9 @@
  *   parameter update          -> gs_adam_step    ROCm blog, create_splats_with_optimizers
  *   partial renders of depth slabs, their over-composition and the compaction of non-zero
  *   gradient records -> gs_composite_over(_bwd), gs_compact_grads  (Splaxel sections 4.2-4.3;
- *   ByteSplat section 3 Insight 4 and section 6)
+ *   ByteSplat section 3 Insight 4 and section 6.1)
+ *   owner-side decoding and atomic aggregation of those records -> gs_decode_grads
+ *   (ByteSplat section 6.2)
  *
  * Conventions (all entry points):
  *   - Every pointer argument that names device memory must be a device (or managed)
@@ -373,6 +375,29 @@ size_t gs_compact_workspace_bytes(int64_t n);
 gs_status gs_compact_grads(const float *grads2d, int64_t n, uint32_t index_base, void *records,
                            uint32_t *bitmap, int64_t *r_out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* One renderer partition's compacted records, as gs_compact_grads wrote them, and the
+ * forward-communication index that maps its positions to the owner's Gaussians. */
+typedef struct {
+    const void *records;          /* r records {uint32 index; float g[9]} (40 B), 4-byte aligned */
+    int64_t r;                    /* record count (the r_out of gs_compact_grads) */
+    uint32_t index_base;          /* the index_base the records were written with */
+    const uint32_t *owner_index;  /* [n_part]: owner Gaussian of partition position i; NULL: i itself */
+    int64_t n_part;               /* positions in the partition */
+} gs_grad_records;
+
+/* Owner-side sparse decoding (ByteSplat section 6.2, Fig. 9): for every record of the k
+ * partitions (0 <= k <= 16), position i = index - index_base is mapped through
+ * owner_index to the owner Gaussian o and each non-zero field f is added to
+ * grads2d[f * n_owner + o] with an fp32 atomic add.  grads2d ([9][n_owner], same field
+ * order as gs_raster_bwd) is accumulated, not cleared; records of different partitions
+ * that name the same Gaussian are summed in an unspecified order.  A record whose
+ * position is outside [0, n_part) or whose owner Gaussian is outside [0, n_owner) is
+ * skipped and counted into *rejected (device uint32, accumulated; may be NULL).  The
+ * records and owner_index arrays are device memory, `parts` is a host array.  Calls
+ * whose partitions are decoded into the same grads2d may overlap on different streams. */
+gs_status gs_decode_grads(const gs_grad_records *parts, int32_t k, float *grads2d, int64_t n_owner,
+                          uint32_t *rejected, hipStream_t stream);
 
 /* Message describing the last non-OK status returned on the calling thread. */
 const char *gs_last_error(void);

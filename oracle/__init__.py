@@ -298,6 +298,28 @@ def compact(grads2d, index_base=0):
     return rec[:R].copy(), bm[:(n + 31) // 32].copy()
 
 
+def decode(parts, n_owner, out=None):
+    """parts: list of (records [R][10] uint32, index_base, owner_index [n_part] or None,
+    n_part).  Returns (grads [9][n_owner] float64 accumulated onto `out`, rejected)."""
+    L = lib()
+    k = len(parts)
+    recs = [np.ascontiguousarray(np.asarray(p[0], np.uint32).reshape(-1, 10)) for p in parts]
+    maps = [None if p[2] is None else np.ascontiguousarray(np.asarray(p[2], np.uint32)) for p in parts]
+    res = np.zeros((9, n_owner)) if out is None else np.array(out, np.float64, copy=True).reshape(9, n_owner)
+    res = np.ascontiguousarray(res)
+    R = (ctypes.c_int64 * max(k, 1))(*[x.shape[0] for x in recs])
+    base = (ctypes.c_uint32 * max(k, 1))(*[int(p[1]) for p in parts])
+    npart = (ctypes.c_int64 * max(k, 1))(*[int(p[3]) for p in parts])
+    rp = (ctypes.c_void_p * max(k, 1))(*[x.ctypes.data for x in recs])
+    mp = (ctypes.c_void_p * max(k, 1))(*[None if m is None else m.ctypes.data for m in maps])
+    f = L.orc_decode
+    f.restype = ctypes.c_int64
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    rej = f(k, rp, R, base, mp, npart, n_owner, res.ctypes.data)
+    return res, int(rej)
+
+
 def sh_basis(deg, dirs):
     """Y [m][(deg+1)^2] and dY [m][(deg+1)^2][3] at unit vectors dirs [m][3]."""
     L = lib()

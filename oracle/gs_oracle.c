@@ -1019,3 +1019,38 @@ int64_t orc_compact(int64_t n, const float *grads2d, uint32_t index_base,
     }
     return r;
 }
+
+/* Owner-side aggregation of compacted records [ByteSplat sec. 6.2, Fig. 9]:
+ * every record of partition k names a partition position i = index - base[k];
+ * the forward-communication index maps it to the owner's Gaussian
+ * o = owner_index[k][i] (identity when that array is NULL), and the record's
+ * nine fields are added to field planes out[f][o] (accumulated, double).
+ * Records whose position or owner Gaussian is out of range are skipped and
+ * counted; the count is returned. */
+int64_t orc_decode(int k, const uint32_t *const *records, const int64_t *r, const uint32_t *base,
+                   const uint32_t *const *owner_index, const int64_t *n_part, int64_t n_owner,
+                   double *out /* [9][n_owner] */)
+{
+    int64_t rejected = 0;
+    for (int q = 0; q < k; ++q) {
+        for (int64_t j = 0; j < r[q]; ++j) {
+            const uint32_t *rec = records[q] + 10 * j;
+            const int64_t i = (int64_t)rec[0] - (int64_t)base[q];
+            if (i < 0 || i >= n_part[q]) {
+                ++rejected;
+                continue;
+            }
+            const int64_t o = owner_index[q] ? (int64_t)owner_index[q][i] : i;
+            if (o >= n_owner) {
+                ++rejected;
+                continue;
+            }
+            for (int f = 0; f < 9; ++f) {
+                float v;
+                memcpy(&v, &rec[1 + f], 4);
+                out[f * n_owner + o] += (double)v;
+            }
+        }
+    }
+    return rejected;
+}

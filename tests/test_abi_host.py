@@ -42,6 +42,8 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.Projected) == 6 * 8
     assert ctypes.sizeof(B.Bins) == 4 * 8 + 8 + 8
     assert ctypes.sizeof(B.AdamGroup) == 4 * 8 + 8 + 8
+    assert ctypes.sizeof(B.GradRecords) == 8 + 8 + 8 + 8 + 8      # uint32 index_base padded to 8
+    assert B.GradRecords.owner_index.offset == 24
 
 
 def _cam(w=64, h=48):
@@ -176,3 +178,25 @@ class _Buf:
     def __init__(self, n):
         self.mem = ctypes.create_string_buffer(n + 16)
         self.ptr = ctypes.c_void_p((ctypes.addressof(self.mem) + 15) // 16 * 16)
+
+
+def test_decode_argument_errors_before_launch():
+    """gs_decode_grads checks its partitions on the host; k = 0, empty partitions and an
+    empty owner range with no counter launch nothing."""
+    buf = _Buf(64)
+    one = (B.GradRecords * 1)(B.GradRecords(buf.ptr, 1, 0, None, 1))
+    st = B._lib.gs_decode_grads(one, 17, buf.ptr, 10, None, None)
+    assert st == B.GS_ERR_INVALID_ARGUMENT and "k must" in B.last_error()
+    assert B._lib.gs_decode_grads(None, 1, buf.ptr, 10, None, None) == B.GS_ERR_INVALID_ARGUMENT
+    bad = (B.GradRecords * 1)(B.GradRecords(None, 5, 0, None, 10))
+    assert B._lib.gs_decode_grads(bad, 1, buf.ptr, 10, None, None) == B.GS_ERR_INVALID_ARGUMENT
+    neg = (B.GradRecords * 1)(B.GradRecords(buf.ptr, -1, 0, None, 10))
+    assert B._lib.gs_decode_grads(neg, 1, buf.ptr, 10, None, None) == B.GS_ERR_INVALID_ARGUMENT
+    odd = (B.GradRecords * 1)(B.GradRecords(ctypes.c_void_p(buf.ptr.value + 2), 1, 0, None, 1))
+    assert B._lib.gs_decode_grads(odd, 1, buf.ptr, 10, None, None) == B.GS_ERR_INVALID_ARGUMENT
+    assert B._lib.gs_decode_grads(one, 1, None, 10, None, None) == B.GS_ERR_INVALID_ARGUMENT
+    assert B._lib.gs_decode_grads(one, 1, buf.ptr, -1, None, None) == B.GS_ERR_INVALID_ARGUMENT
+    assert B._lib.gs_decode_grads(None, 0, None, 0, None, None) == B.GS_OK
+    empty = (B.GradRecords * 1)(B.GradRecords(None, 0, 0, None, 0))
+    assert B._lib.gs_decode_grads(empty, 1, None, 0, None, None) == B.GS_OK
+    assert B._lib.gs_decode_grads(one, 1, None, 0, None, None) == B.GS_OK

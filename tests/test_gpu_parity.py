@@ -450,6 +450,105 @@ def test_compact_bit_exact(n, base):
     assert np.array_equal(bitmap.cpu().numpy().view(np.uint32), bm_o)
 
 
+def _shared_partitions(seed, n_owner, k, n_part_max, zero_frac=0.6):
+    """k renderer partitions over an owner's n_owner Gaussians: each holds a random
+    subset (positions in random order, so partitions overlap) with seeded sparse
+    gradients; a few fields are subnormal."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for q in range(k):
+        n_part = int(rng.integers(0, n_part_max + 1)) if q else n_part_max
+        owner = rng.choice(n_owner, size=min(n_part, n_owner), replace=False).astype(np.uint32)
+        g = scenes.sparse_grads(seed * 31 + q, len(owner), zero_frac=zero_frac)
+        sub = torch.from_numpy(rng.random(g.shape) < 0.01) & (g != 0)
+        g[sub] = torch.sign(g[sub]) * 1e-40
+        out.append((g, owner, 1000 * q))
+    return out
+
+
+def _decode_both(parts, n_owner, init):
+    """Compacts each partition on both sides (bit-identical, checked), then decodes on the
+    GPU through the C ABI and in the oracle; returns (gpu [9][n_owner], oracle, count
+    of contributions per owner Gaussian and field, sum of their magnitudes)."""
+    gparts, oparts, keep = [], [], []
+    for g, owner, base in parts:
+        n = len(owner)
+        rec_o, _ = oracle.compact(g, base)
+        records = torch.zeros(max(n, 1), 10, dtype=torch.int32, device=DEV)
+        bitmap = torch.zeros(max((n + 31) // 32, 1), dtype=torch.int32, device=DEV)
+        ws = torch.empty(max(B.gs_compact_workspace_bytes(n), 256), dtype=torch.uint8, device=DEV)
+        R = B.gs_compact_grads(g.to(DEV), n, base, records, bitmap, ws) if n else 0
+        assert R == rec_o.shape[0]
+        assert np.array_equal(records[:R].cpu().numpy().view(np.uint32), rec_o)
+        om = torch.from_numpy(owner.astype(np.int64)).to(torch.int32).to(DEV) if n else None
+        gparts.append((records, R, base, om, n))
+        oparts.append((rec_o, base, owner, n))
+        keep.append(records)
+    out = init.clone().to(DEV)
+    rejected = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.gs_decode_grads(gparts, out, n_owner, rejected)
+    torch.cuda.synchronize()
+    want, rej = oracle.decode(oparts, n_owner, out=init.numpy())
+    assert rej == 0 and int(rejected.item()) == 0
+    cnt = np.zeros((9, n_owner))
+    mag = np.abs(init.numpy()).astype(np.float64)
+    for rec_o, base, owner, n in oparts:
+        pos = rec_o[:, 0].astype(np.int64) - base
+        vals = rec_o[:, 1:].view(np.float32).T.astype(np.float64)
+        np.add.at(cnt, (slice(None), owner[pos]), (vals != 0).astype(np.float64))
+        np.add.at(mag, (slice(None), owner[pos]), np.abs(vals))
+    return out.cpu().numpy(), want, cnt, mag
+
+
+@pytest.mark.parametrize("seed,n_owner,k,n_part_max", [(1, 1, 1, 1), (2, 5000, 3, 4000), (3, 100_003, 5, 60_000),
+                                                        (4, 2000, 16, 2000), (5, 300_000, 2, 300_000)])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_decode_matches_oracle(seed, n_owner, k, n_part_max, accumulate):
+    """ByteSplat section 6.2: the owner's gradients are the sum of every partition's
+    records mapped through its forward index.  Bound: an fp32 sum of m terms onto the
+    initial value errs by at most m u sum|terms| (u = 2^-24), plus 2^-126 per add if the
+    atomic flushes subnormals; a Gaussian with a single normal-valued contribution onto
+    zero is exact."""
+    parts = _shared_partitions(seed, n_owner, k, n_part_max)
+    init = torch.zeros(9, n_owner)
+    if accumulate:
+        init = torch.from_numpy(np.random.default_rng(seed).normal(size=(9, n_owner)).astype(np.float32))
+    got, want, cnt, mag = _decode_both(parts, n_owner, init)
+    m = cnt + (init.numpy() != 0)
+    bound = m * (2.0 ** -24 * mag + 2.0 ** -126)
+    err = np.abs(got.astype(np.float64) - want)
+    assert (err <= bound).all(), float((err - bound).max())
+    single = (cnt == 1) & (init.numpy() == 0) & (np.abs(want) >= 2.0 ** -126)
+    assert np.array_equal(got[single], want[single].astype(np.float32))
+    log(f"  decode k={k} owner={n_owner}: {int(cnt.sum())} adds, max sharing {int(cnt.max(initial=0))}")
+
+
+def test_decode_rejected_and_empty():
+    """Records outside their partition, or mapped outside the owner range, are skipped
+    and counted; empty partitions and k = 0 do nothing."""
+    n = 3000
+    g = scenes.sparse_grads(7, n, zero_frac=0.0)
+    records = torch.zeros(n, 10, dtype=torch.int32, device=DEV)
+    bitmap = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    ws = torch.empty(B.gs_compact_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    R = B.gs_compact_grads(g.to(DEV), n, 500, records, bitmap, ws)
+    assert R == n
+    owner = np.arange(2000, dtype=np.uint32)
+    owner[:7] = 4000                                   # past the owner range
+    om = torch.from_numpy(owner.astype(np.int64)).to(torch.int32).to(DEV)
+    out = torch.zeros(9, 2500, device=DEV)
+    rejected = torch.zeros(1, dtype=torch.int32, device=DEV)
+    empty = torch.zeros(1, 10, dtype=torch.int32, device=DEV)
+    B.gs_decode_grads([(records, R, 500, om, 2000), (empty, 0, 0, None, 0)], out, 2500, rejected)
+    B.gs_decode_grads([], out, 2500, rejected)
+    torch.cuda.synchronize()
+    assert int(rejected.item()) == 1000 + 7
+    rec_o, _ = oracle.compact(g, 500)
+    want, rej = oracle.decode([(rec_o, 500, owner, 2000)], 2500)
+    assert rej == 1007
+    assert np.array_equal(out.cpu().numpy(), want.astype(np.float32))
+
+
 # ------------------------------------------------------------------ whole step, edge cases
 
 def test_empty_scene_and_train_step():

@@ -8,8 +8,12 @@ GPU only.
   restricted to those rows (so both sides sum the same pixels).
 * 20M Gaussians in four depth slabs, 4K (full size): properties that hold at any size --
   the over-composited partial renders equal the unpartitioned render (Splaxel, section 4.2),
-  the gradients through the composite equal the unpartitioned gradients, and the
-  compacted records scatter back to the dense gradients (ByteSplat, section 6).
+  the gradients through the composite equal the unpartitioned gradients, the
+  compacted records scatter back to the dense gradients (ByteSplat, section 6.1), and
+  the owner-side decoding of all four slabs' records rebuilds them (section 6.2).
+* ByteSplat's owner/renderer split at 100K Gaussians, 512x512: four renderers own bands
+  of tile rows; each returns compacted records of the Gaussians sent to it and the
+  owner's decoded sum equals one unsplit backward.
 * The same partitioned recipe at 200K Gaussians: partial renders, composite, composite
   backward and per-slab gradients against the oracle.
 """
@@ -172,7 +176,7 @@ def _check_records(g2):
     assert np.array_equal(rec[:, 1:].view(np.float32).T.view(np.uint32), dense[:, idx].view(np.uint32))
     bits = np.unpackbits(bitmap.cpu().numpy().view(np.uint8), bitorder="little")[:n].astype(bool)
     assert np.array_equal(bits, nz)
-    return R
+    return R, records
 
 
 def test_20m_4k_partitioned_properties():
@@ -197,10 +201,21 @@ def test_20m_4k_partitioned_properties():
     e = rel_l2(out["part_g2"].cpu().numpy(), out["full_g2"].cpu().numpy())
     log(f"  gradients through the composite vs unpartitioned rel-L2 {e:.2e}")
     assert e <= 1e-4
+    parts = []
     for k, s in enumerate(out["slabs"]):
-        R = _check_records(s.grads2d)
+        R, records = _check_records(s.grads2d)
         log(f"  slab {k}: {R} non-zero records of {s.params.n}")
-    del out
+        parts.append((records, R, 0, None, s.params.n))
+    # owner side: every Gaussian lies in one slab, so the decoded sum of the four record
+    # sets is exactly the sum of the dense slab gradients
+    n = out["part_g2"].shape[1]
+    owner = torch.zeros_like(out["part_g2"])
+    rejected = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.gs_decode_grads(parts, owner, n, rejected)
+    torch.cuda.synchronize()
+    assert int(rejected.item()) == 0
+    assert torch.equal(owner, out["part_g2"])
+    del out, parts, owner
     torch.cuda.empty_cache()
     # theta_T = 1e-4: termination inside a slab differs from the global one by at most
     # theta_T times a colour
@@ -256,3 +271,113 @@ def test_partitioned_small_against_oracle():
         log(f"  slab {k} grads2d rel-L2 {errs}")
         assert max(errs.values()) <= 1e-3, errs
         _check_records(out["slabs"][k].grads2d)
+
+
+def test_tile_band_renderers_decode_to_full_gradients():
+    """ByteSplat sections 2.2 and 6: each renderer owns a band of tile rows and receives
+    the Gaussians whose footprint reaches it; Gaussians that reach a band but add nothing
+    there come back with all-zero gradients and are elided.  The owner decodes the four
+    record sets (Gaussians on band borders arrive from two or more renderers) and gets
+    the gradients of one unsplit backward, up to the fp32 summation order."""
+    log("100K 512x512, 4 renderer bands")
+    sc = scenes.scene_100k()
+    cam = sc.cameras[0]
+    W, H = cam.width, cam.height
+    c = B.camera_from(cam)
+    params = PL.GaussianParams.from_scene(sc, DEV)
+    st = PL.TrainStep(params, W, H, DEV)
+    st.forward(c)
+    st.loss(sc.targets[0].to(DEV))
+    G = st.frame.dL_dcolor.clone()
+    st.backward(c, dL_dcolor=G, grads3d=False)
+    full = st.grads2d.clone()
+    n = params.n
+    m2 = st.proj.means2d.cpu().numpy().astype(np.float64)
+    radii = st.proj.radii.cpu().numpy()
+    vis = (radii > 0).all(axis=1)
+    # rows a footprint can reach (one pixel of slack around the bounding box)
+    lo, hi = m2[:, 1] - radii[:, 1] - 1, m2[:, 1] + radii[:, 1] + 1
+    band_rows = 16 * ((H // 16 + 3) // 4)
+    parts, keep, sent_total, recs_total = [], [], 0, 0
+    for y0 in range(0, H, band_rows):
+        y1 = min(H, y0 + band_rows)
+        Gk = torch.zeros_like(G)
+        Gk[y0:y1] = G[y0:y1]
+        st.backward(c, dL_dcolor=Gk, grads3d=False)
+        sent = np.nonzero(vis & (hi >= y0) & (lo < y1))[0]
+        outside = np.ones(n, bool)
+        outside[sent] = False
+        assert not bool(st.grads2d[:, torch.from_numpy(outside).to(DEV)].any())
+        idx = torch.from_numpy(sent).to(DEV)
+        gpart = st.grads2d[:, idx].contiguous()
+        m = len(sent)
+        records = torch.zeros(max(m, 1), 10, dtype=torch.int32, device=DEV)
+        bitmap = torch.zeros(max((m + 31) // 32, 1), dtype=torch.int32, device=DEV)
+        ws = torch.empty(max(B.gs_compact_workspace_bytes(m), 256), dtype=torch.uint8, device=DEV)
+        R = B.gs_compact_grads(gpart, m, 0, records, bitmap, ws) if m else 0
+        parts.append((records, R, 0, idx.to(torch.int32), m))
+        keep.append(gpart)
+        sent_total += m
+        recs_total += R
+        log(f"  rows [{y0}, {y1}): {m} Gaussians sent, {R} non-zero records returned")
+    owner = torch.zeros(9, n, device=DEV)
+    rejected = torch.zeros(1, dtype=torch.int32, device=DEV)
+    B.gs_decode_grads(parts, owner, n, rejected)
+    torch.cuda.synchronize()
+    assert int(rejected.item()) == 0
+    assert recs_total < sent_total
+    got, want = owner.cpu().numpy(), full.cpu().numpy()
+    errs = {oracle.G_FIELDS[f]: rel_l2(got[f], want[f]) for f in range(9)}
+    log(f"  decoded vs unsplit rel-L2 {errs}; {sent_total - recs_total} of {sent_total} records elided")
+    assert max(errs.values()) <= 1e-5, errs
+    # a Gaussian that no band's pixels touch has no record anywhere and stays zero
+    untouched = ~(want != 0).any(axis=0)
+    assert not (got[:, untouched] != 0).any()
+
+
+def test_partitioned_step_matches_unpartitioned():
+    """PartitionedStep on the 4-slab recipe at 200K Gaussians, 960x540, theta_T = 0: the
+    composite equals the unpartitioned render, the gradient planes each slab owner decodes
+    from its records equal the unpartitioned gradients of its Gaussians, and the owners'
+    projection backward gives the unpartitioned 3D gradients (Splaxel section 4.2;
+    ByteSplat section 6)."""
+    log("PartitionedStep, 200K 960x540, 4 slabs")
+    sc = scenes.scene_partitioned_4k(n=200_000, width=960, height=540)
+    subs = scenes.slab_scenes(sc)
+    cam = B.camera_from(sc.cameras[0])
+    W, H = sc.cameras[0].width, sc.cameras[0].height
+    tgt = sc.targets[0].to(DEV)
+    # Gaussian i of slab k is Gaussian idx[k][i] of the whole scene
+    M = sc.cameras[0].viewmat.double().reshape(4, 4)
+    z = (M[2, :3].unsqueeze(1) * sc.means.double()).sum(0) + M[2, 3]
+    idx = [torch.nonzero((z >= lo) & (z < hi)).squeeze(1) for lo, hi in sc.depth_slabs]
+    assert sum(len(i) for i in idx) == sc.n
+    full = PL.TrainStep(PL.GaussianParams.from_scene(sc, DEV), W, H, DEV, raster=B.make_params(sc.sh_degree, t_min=0.0))
+    full.forward(cam)
+    full.loss(tgt)
+    full.backward(cam)
+    g3_full = full.params.grad.clone()
+    slabs = [PL.GaussianParams.from_scene(s, DEV) for s in subs]
+    ps = PL.PartitionedStep(slabs, [(0.0, math.inf)] * 4, W, H, DEV, t_min=0.0)
+    ps.forward(cam)
+    ps.loss(tgt)
+    torch.cuda.synchronize()
+    dc = float((ps.color - full.frame.color).abs().max())
+    dt = float((ps.t_final - full.frame.t_final).abs().max())
+    log(f"  composite vs unpartitioned max |dC| {dc:.2e} |dT| {dt:.2e}")
+    assert dc <= 2e-5 and dt <= 2e-5
+    # the same loss gradient on both sides (pixels whose sign flips between the two renders
+    # would otherwise differ)
+    ps.dL_dcolor.copy_(full.frame.dL_dcolor)
+    ps.backward(cam)
+    for k, st in enumerate(ps.parts):
+        B.gs_project_bwd(st.params.gaussians(), cam, st.raster, ps.owner_g2[k], st.params.param_grads())
+    torch.cuda.synchronize()
+    g2_full = full.grads2d.cpu()
+    g3 = g3_full.cpu()
+    for k, st in enumerate(ps.parts):
+        assert torch.equal(ps.owner_g2[k][:, :st.params.n], st.grads2d)      # decoding is exact
+        e2 = rel_l2(ps.owner_g2[k].cpu().numpy(), g2_full[:, idx[k]].numpy())
+        e3 = rel_l2(st.params.grad.cpu().numpy(), g3[:, idx[k]].numpy())
+        log(f"  slab {k}: {ps.r[k]} records of {st.params.n}; grads2d rel-L2 {e2:.2e}, 3D grads rel-L2 {e3:.2e}")
+        assert e2 <= 1e-4 and e3 <= 1e-4

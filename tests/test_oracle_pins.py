@@ -595,6 +595,74 @@ def test_compaction_invariants():
     assert np.array_equal(bits, nz)
 
 
+def test_decode_round_trip_and_permutation():
+    """[ByteSplat sec. 6.2]: decoding one partition's records through its forward index
+    restores the dense gradients (the elided columns are exactly zero); with a
+    permutation as forward index, position i lands on owner Gaussian perm[i]."""
+    n = 3000
+    g = scenes.sparse_grads(9, n)
+    rec, _ = oracle.compact(g, index_base=77)
+    dense = g.numpy().astype(np.float64)
+    out, rej = oracle.decode([(rec, 77, None, n)], n)
+    assert rej == 0 and np.array_equal(out, dense)
+    perm = np.random.default_rng(3).permutation(n).astype(np.uint32)
+    out, rej = oracle.decode([(rec, 77, perm, n)], n)
+    want = np.zeros_like(dense)
+    want[:, perm] = dense
+    assert rej == 0 and np.array_equal(out, want)
+    # accumulation onto a non-zero buffer
+    prev = np.random.default_rng(4).normal(size=(9, n))
+    out2, _ = oracle.decode([(rec, 77, perm, n)], n, out=prev)
+    assert np.array_equal(out2, prev + want)
+
+
+def test_decode_shared_gaussians_sum_exactly():
+    """A Gaussian sent to several renderers gets one record from each; the owner's
+    result is their sum.  The owner totals are integers split into integer parts across
+    overlapping partitions, so the expected sums are known exactly by construction."""
+    rng = np.random.default_rng(11)
+    n_owner, k = 500, 5
+    total = rng.integers(-50, 51, size=(9, n_owner)).astype(np.float64)
+    members = [[] for _ in range(k)]                 # owner Gaussians of each partition
+    shares = [[] for _ in range(k)]
+    for o in range(n_owner):
+        ks = rng.choice(k, size=int(rng.integers(1, k + 1)), replace=False)
+        part = rng.integers(-20, 21, size=(9, len(ks))).astype(np.float64)
+        part[:, -1] = total[:, o] - part[:, :-1].sum(axis=1)
+        for j, q in enumerate(ks):
+            members[q].append(o)
+            shares[q].append(part[:, j])
+    parts = []
+    for q in range(k):
+        order = rng.permutation(len(members[q]))    # partition positions in arbitrary order
+        idx = np.array(members[q], np.uint32)[order]
+        dense = np.array(shares[q])[order].T.astype(np.float32).copy()
+        dense[:, 0] = 0.0                              # one all-zero column: elided, contributes nothing
+        rec, _ = oracle.compact(torch.from_numpy(dense), index_base=10 * q)
+        parts.append((rec, 10 * q, idx, len(idx)))
+        total[:, idx[0]] -= np.array(shares[q])[order[0]]
+    out, rej = oracle.decode(parts, n_owner)
+    assert rej == 0
+    assert np.array_equal(out, total)
+
+
+def test_decode_rejects_out_of_range_records():
+    """Records outside the partition or mapped outside the owner range are skipped and
+    counted; the rest are decoded as usual."""
+    g = scenes.sparse_grads(12, 200, zero_frac=0.0)
+    rec, _ = oracle.compact(g, index_base=1000)
+    n_part = 150                                       # records 150..199 lie past the partition
+    owner = np.arange(n_part, dtype=np.uint32)
+    owner[:10] = 10_000                                # 10 positions map past the owner range
+    out, rej = oracle.decode([(rec, 1000, owner, n_part)], 400)
+    assert rej == 50 + 10
+    dense = g.numpy().astype(np.float64)
+    assert np.array_equal(out[:, 10:150], dense[:, 10:150])
+    assert not out[:, :10].any() and not out[:, 150:].any()
+    lo, rej = oracle.decode([(rec, 1001, None, 400)], 400)   # index 1000 lies below the base
+    assert rej == 1 and np.array_equal(lo[:, :199], dense[:, 1:])
+
+
 # ------------------------------------------------------------------ golden values from the pages
 
 def test_golden_thresholds_fixture():
