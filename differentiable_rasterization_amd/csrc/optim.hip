@@ -65,54 +65,68 @@ struct AdamArgs {
     float *m[kMaxGroups];
     float *v[kMaxGroups];
     int64_t n[kMaxGroups];
-    uint32_t block0[kMaxGroups + 1];   // first block of each group (256 float4 per block)
+    uint32_t block0[kMaxGroups + 1];   // first block of each group
     float step[kMaxGroups];            // lr / (1 - b1^t)
-    bool vec[kMaxGroups];              // group is float4-aligned and a multiple of 4 long
+    int32_t head[kMaxGroups];          // vector groups: scalars before the first 16-byte boundary
+    bool vec[kMaxGroups];              // the four arrays share their offset from a 16-byte boundary
     int ng;
     float b1, b2, inv_bc2, eps;
 };
 
 using gsd::adam_update;
 
-// One float4 of one group per thread; every block lies inside one group.  The four
-// streams are read and written once, so the accesses are non-temporal (they would only
-// evict other data from the caches).
+__device__ __forceinline__ void adam_scalar(const AdamArgs &a, int gi, int64_t e)
+{
+    float p = a.p[gi][e], m = a.m[gi][e], v = a.v[gi][e];
+    adam_update(p, a.g[gi][e], m, v, a.b1, a.b2, a.inv_bc2, a.eps, a.step[gi]);
+    a.p[gi][e] = p;
+    a.m[gi][e] = m;
+    a.v[gi][e] = v;
+}
+
+// Vector groups: one float4 of the group's aligned body per thread, plus the up to three
+// scalars before and after the body in the group's first block.  Other groups: one scalar
+// per thread.  Every block lies inside one group.  The four streams are read and written
+// once, so the accesses are non-temporal (they would only evict other data from the caches).
 __global__ __launch_bounds__(kThreads) void k_adam(AdamArgs a)
 {
     const uint32_t b = blockIdx.x;
     int gi = 0;
     while (gi + 1 < a.ng && b >= a.block0[gi + 1]) ++gi;
-    const int64_t j = (int64_t)(b - a.block0[gi]) * kThreads + threadIdx.x;   // float4 index in the group
+    const int64_t lb = b - a.block0[gi];
     const int64_t n = a.n[gi];
-    if (4 * j >= n) return;
-    const float st = a.step[gi];
-    if (a.vec[gi]) {
-        v4f *pp = reinterpret_cast<v4f *>(a.p[gi]) + j;
-        const v4f *gp = reinterpret_cast<const v4f *>(a.g[gi]) + j;
-        v4f *mp = reinterpret_cast<v4f *>(a.m[gi]) + j;
-        v4f *vp = reinterpret_cast<v4f *>(a.v[gi]) + j;
-        v4f p = __builtin_nontemporal_load(pp), g = __builtin_nontemporal_load(gp);
-        v4f m = __builtin_nontemporal_load(mp), v = __builtin_nontemporal_load(vp);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float pc = p[c], mc = m[c], vc = v[c];
-            adam_update(pc, g[c], mc, vc, a.b1, a.b2, a.inv_bc2, a.eps, st);
-            p[c] = pc;
-            m[c] = mc;
-            v[c] = vc;
-        }
-        __builtin_nontemporal_store(p, pp);
-        __builtin_nontemporal_store(m, mp);
-        __builtin_nontemporal_store(v, vp);
-    } else {
-        for (int64_t e = 4 * j; e < min(4 * j + 4, n); ++e) {
-            float p = a.p[gi][e], m = a.m[gi][e], v = a.v[gi][e];
-            adam_update(p, a.g[gi][e], m, v, a.b1, a.b2, a.inv_bc2, a.eps, st);
-            a.p[gi][e] = p;
-            a.m[gi][e] = m;
-            a.v[gi][e] = v;
-        }
+    if (!a.vec[gi]) {
+        const int64_t e = lb * kThreads + threadIdx.x;
+        if (e < n) adam_scalar(a, gi, e);
+        return;
     }
+    const int64_t head = a.head[gi];
+    const int64_t n4 = (n - head) >> 2;
+    const int64_t j = lb * kThreads + threadIdx.x;   // float4 index in the body
+    if (lb == 0) {
+        const int64_t tail = n - head - 4 * n4;
+        if ((int64_t)threadIdx.x < head) adam_scalar(a, gi, threadIdx.x);
+        if (threadIdx.x >= 64 && (int64_t)threadIdx.x < 64 + tail) adam_scalar(a, gi, head + 4 * n4 + threadIdx.x - 64);
+    }
+    if (j >= n4) return;
+    const float st = a.step[gi];
+    v4f *pp = reinterpret_cast<v4f *>(a.p[gi] + head) + j;
+    const v4f *gp = reinterpret_cast<const v4f *>(a.g[gi] + head) + j;
+    v4f *mp = reinterpret_cast<v4f *>(a.m[gi] + head) + j;
+    v4f *vp = reinterpret_cast<v4f *>(a.v[gi] + head) + j;
+    v4f p = __builtin_nontemporal_load(pp), g = __builtin_nontemporal_load(gp);
+    v4f m = __builtin_nontemporal_load(mp), v = __builtin_nontemporal_load(vp);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        float pc = p[c], mc = m[c], vc = v[c];
+        adam_update(pc, g[c], mc, vc, a.b1, a.b2, a.inv_bc2, a.eps, st);
+        p[c] = pc;
+        m[c] = mc;
+        v[c] = vc;
+    }
+    __builtin_nontemporal_store(p, pp);
+    __builtin_nontemporal_store(m, mp);
+    __builtin_nontemporal_store(v, vp);
 }
 
 int stream_blocks(int64_t work)
@@ -180,9 +194,17 @@ extern "C" gs_status gs_adam_step(const gs_adam_group *groups, int32_t n_groups,
             return fail(GS_ERR_INVALID_ARGUMENT, "group %d: NULL pointer", i);
         a.p[i] = gr.p; a.g[i] = gr.g; a.m[i] = gr.m; a.v[i] = gr.v; a.n[i] = gr.n;
         a.step[i] = (float)((double)gr.lr / bc1);
-        a.vec[i] = gr.n % 4 == 0 && aligned(gr.p, 16) && aligned(gr.g, 16) && aligned(gr.m, 16) && aligned(gr.v, 16);
+        // float4 body when the four arrays sit at the same offset from a 16-byte boundary
+        // (the case for planes of [planes][N] buffers of any N)
+        const uintptr_t off = reinterpret_cast<uintptr_t>(gr.p) & 15;
+        const bool same = aligned(gr.p, 4) && (reinterpret_cast<uintptr_t>(gr.g) & 15) == off &&
+                          (reinterpret_cast<uintptr_t>(gr.m) & 15) == off &&
+                          (reinterpret_cast<uintptr_t>(gr.v) & 15) == off;
+        a.head[i] = same ? (int32_t)std::min<int64_t>(((16 - off) & 15) / 4, gr.n) : 0;
+        a.vec[i] = same;
         a.block0[i] = (uint32_t)blocks;
-        blocks += ceil_div(ceil_div(gr.n, 4), kThreads);
+        if (gr.n > 0)
+            blocks += same ? std::max<int64_t>(ceil_div((gr.n - a.head[i]) / 4, kThreads), 1) : ceil_div(gr.n, kThreads);
         if (blocks > 0x7fffffff) return fail(GS_ERR_UNSUPPORTED, "parameter groups too large");
     }
     a.block0[n_groups] = (uint32_t)blocks;

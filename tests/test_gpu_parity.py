@@ -410,6 +410,36 @@ def test_adam_parity(n, step):
         assert rel_l2(upd, upd_o) <= 1e-4
 
 
+@pytest.mark.parametrize("n", [1, 2, 5, 1001, 250_003])
+def test_adam_groups_at_any_offset(n):
+    """Parameter groups that are planes of [planes][n] buffers start at every offset from a
+    16-byte boundary (n odd); each array's update still equals the oracle's.  The last
+    group's gradient sits at another offset than its parameters (the scalar path)."""
+    planes = 7
+    st = scenes.adam_state(900 + n, planes * n, 4)
+    bufs = [t.to(DEV).contiguous() for t in st]
+    gshift = torch.zeros(planes * n + 1, device=DEV)
+    gshift[1:] = bufs[1]
+    bounds = [(0, 1), (1, 3), (3, 4), (4, 7)]
+    groups = []
+    for a, b in bounds[:-1]:
+        groups.append((bufs[0][a * n:b * n], bufs[1][a * n:b * n], bufs[2][a * n:b * n], bufs[3][a * n:b * n], 1e-3))
+    a, b = bounds[-1]
+    groups.append((bufs[0][a * n:b * n], gshift[1 + a * n:1 + b * n], bufs[2][a * n:b * n], bufs[3][a * n:b * n], 1e-3))
+    B.gs_adam_step(groups, 4, 0.9, 0.999, 1e-15)
+    torch.cuda.synchronize()
+    p, g, m, v = st
+    po, mo, vo = oracle.adam(p, g, m, v, float(np.float32(1e-3)), float(np.float32(0.9)), float(np.float32(0.999)),
+                             float(np.float32(1e-15)), 4)
+    assert rel_l2(bufs[0].cpu().numpy(), po) <= 1e-6
+    assert rel_l2(bufs[2].cpu().numpy(), mo) <= 1e-6
+    assert rel_l2(bufs[3].cpu().numpy(), vo) <= 1e-6
+    upd = bufs[0].cpu().numpy().astype(np.float64) - p.double().numpy()
+    assert rel_l2(upd, po - p.double().numpy()) <= 1e-4
+    # every element was updated exactly once: the moments match elementwise
+    assert np.abs(bufs[2].cpu().numpy() - mo).max() <= 1e-6 * max(1.0, np.abs(mo).max())
+
+
 # ------------------------------------------------------------------ partial renders
 
 @pytest.mark.parametrize("parts,n_px,t_min", [(4, 5000, 1e-4), (4, 5000, 0.0), (1, 777, 1e-4), (3, 1, 1e-4)])
