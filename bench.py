@@ -1,7 +1,7 @@
 """Benchmark of the one-GPU 3D Gaussian splatting training step on MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m|100k|10m|20m|tiny] [--no-cpu-baseline]
-                    [--cpu-rows R] [--copy-calibration-mib M]
+                    [--cpu-rows R] [--copy-calibration-mib M] [--batch B]
 
 A step is one training iteration on one view: projection -> gs_bin_sort ->
 gs_raster_fused_l1 (forward rasterization, L1 loss and backward rasterization in one
@@ -28,6 +28,12 @@ over-composited, L1 on the composite, the composite backward, each slab's backwa
 rasterization and per-Gaussian sum, compaction of its non-zero gradient records, their
 decoding into the slab owner's gradient planes, and the owner's projection backward and
 Adam; every call is timed with events and reported in `kernels`.
+
+--batch B (2..4) measures BatchTrainStep instead: one optimiser step over B views (the
+workload's views in turn), each binned and rasterized with the fused forward + L1 +
+backward, then one gs_grad_aggregate_adam_batch pass (the views' gradient mean, Adam with
+the batch hyper-parameters of the ROCm blog's "Batching and Hyperparameter Scaling", and
+the next batch's projections).  ms_per_step is per optimiser step (B views).
 
 roofline: the longer of the backward raster kernel (k_raster_fused_l1 by default,
 k_raster_bwd with --separate-raster; bound by VALU arithmetic, its algorithmic work is
@@ -83,6 +89,7 @@ def parse():
                     help="gs_raster_fwd, gs_loss_l1 and gs_raster_bwd_partials instead of gs_raster_fused_l1")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the untimed pass that times every call separately")
+    ap.add_argument("--batch", type=int, default=1, help="views per optimiser step (BatchTrainStep for 2..4)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a copy-like kernel over this many MiB before timing (counter normalisation)")
     return ap.parse_args()
@@ -355,6 +362,113 @@ def main_partitioned(args):
     print(json.dumps(out), flush=True)
 
 
+def main_batch(args):
+    """--batch B: BatchTrainStep over the workload's views (see the module docstring)."""
+    import torch
+    from differentiable_rasterization_amd import binding as B
+    from differentiable_rasterization_amd import pipeline as PL
+
+    dev = "cuda"
+    scene, desc = make_scene(args.workload)
+    cams = [B.camera_from(c) for c in scene.cameras]
+    targets = [t.to(dev) for t in scene.targets]
+    nviews = len(cams)
+    W, H = scene.cameras[0].width, scene.cameras[0].height
+    bs = args.batch
+    params = PL.GaussianParams.from_scene(scene, dev)
+    bt = PL.BatchTrainStep(params, W, H, bs, dev)
+    views_of = lambda i: [(i * bs + k) % nviews for k in range(bs)]
+    # size every view's lists before timing
+    for v in range(nviews):
+        bt.project([cams[v]] * bs)
+        for k in range(bs):
+            bt.sort(k, cams[v])
+    for b in bt.bins:
+        b._alloc(int(b.capacity * 1.3) + 4096)
+    torch.cuda.synchronize()
+
+    def one_step(i, ev=None, counts=None):
+        vs, nv = views_of(i), views_of(i + 1)
+        rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        for k, v in enumerate(vs):
+            if counts is None:
+                bt.sort(k, cams[v])
+            else:
+                bt.bins[k].sort_async(bt.proj[k], cams[v], bt.raster, counts[k])
+            rec(2 * k)
+            bt.render(k, cams[v], targets[v])
+            rec(2 * k + 1)
+        rec(2 * bs)
+        bt.update([cams[v] for v in vs], [cams[v] for v in nv])
+        rec(2 * bs + 1)
+
+    bt.project([cams[v] for v in views_of(0)])
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    for f in bt.frame:
+        f.n_trav_sum.zero_()
+    events = [[TimingEvent() for _ in range(2 * bs + 2)] for _ in range(args.steps)]
+    counts = torch.zeros(args.steps, bs, 2, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i, events[i], counts[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    cnt = counts.cpu()
+    if int(cnt[:, :, 1].max()) != 0:
+        raise RuntimeError("intersection lists overflowed during the timed steps")
+    raster_ms = sum(events[s][2 * k].elapsed_time(events[s][2 * k + 1]) for s in range(args.steps)
+                    for k in range(bs)) / (args.steps * bs)
+    update_ms = sum(events[s][2 * bs].elapsed_time(events[s][2 * bs + 1]) for s in range(args.steps)) / args.steps
+    isect_total = sum(int(f.n_trav_sum.item()) for f in bt.frame)
+    isect_view = isect_total / (args.steps * bs)
+    n = scene.n
+    n_vis = int((bt.proj[0].radii[:, 0] > 0).sum().item())
+    k_mean = float(cnt[:, :, 0].double().mean())
+    by = 36 * k_mean * bs + n * (11 + 3 * scene.k_sh) * 24 + bs * (n_vis * 96 + (n - n_vis) * 12)
+    fl = FLOP_PER_PAIR["raster_fused"] * isect_view
+    kernels = {
+        "raster_fused": {"ms": round(raster_ms, 4), "bound": "alu", "algorithmic_flop": int(fl),
+                         "achieved_TFLOPs": round(fl / (raster_ms * 1e-3) / 1e12, 3),
+                         "frac": round(fl / (raster_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
+                         "note": "per view"},
+        "grad_adam_batch": {"ms": round(update_ms, 4), "bound": "hbm", "algorithmic_bytes": int(by),
+                            "achieved_GBs": round(by / (update_ms * 1e-3) / 1e9, 1),
+                            "frac": round(by / (update_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "note": "per optimiser step"},
+    }
+    if update_ms > raster_ms:
+        d = kernels["grad_adam_batch"]
+        roof = {"kernel": "k_grad_adam_batch", "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": d["frac"], "traffic": None, "algorithmic_bytes": d["algorithmic_bytes"],
+                "launch_ms": d["ms"]}
+    else:
+        d = kernels["raster_fused"]
+        roof = {"kernel": "k_raster_fused_l1", "bound": "alu", "achieved": d["achieved_TFLOPs"],
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["frac"], "traffic": None,
+                "flop_per_pair": FLOP_PER_PAIR["raster_fused"], "pairs_per_launch": round(isect_view, 1),
+                "launch_ms": d["ms"]}
+    out = {
+        "metric": METRIC, "value": round(isect_total / wall, 1), "unit": "Gaussian-pixel intersections/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_view": round(wall * 1e3 / (args.steps * bs), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
+                   "views": nviews, "batch": bs,
+                   "step": f"one optimiser step over {bs} views: per view binning + fwd + L1 + bwd; one pass of "
+                           "gradient mean, Adam (batch hyper-parameters) and the next batch's projections"},
+        "roofline": roof,
+        "intersections_per_view": round(isect_view, 1),
+        "tile_entries_per_view": round(k_mean, 1),
+        "kernels": kernels,
+        "device": torch.cuda.get_device_name(0),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -363,6 +477,11 @@ def main():
         sys.exit(2)
     if args.workload == "20m":
         return main_partitioned(args)
+    if args.batch != 1:
+        if not 2 <= args.batch <= 4:
+            print("--batch takes 1 to 4 views", file=sys.stderr)
+            sys.exit(2)
+        return main_batch(args)
     import torch
     from differentiable_rasterization_amd import binding as B
     from differentiable_rasterization_amd import pipeline as PL

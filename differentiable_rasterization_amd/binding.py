@@ -30,7 +30,8 @@ EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes",
             "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project",
             "gs_raster_fused_l1", "gs_raster_fused_l1_workspace_bytes", "gs_tile_budget", "gs_tile_budget_report",
             "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
-            "gs_compact_workspace_bytes", "gs_compact_grads", "gs_decode_grads", "gs_last_error")
+            "gs_compact_workspace_bytes", "gs_compact_grads", "gs_decode_grads", "gs_project_batch",
+            "gs_grad_aggregate_adam_batch", "gs_adam_batch_hparams", "gs_last_error")
 
 
 class GsError(RuntimeError):
@@ -127,6 +128,12 @@ _SIGS = {
     "gs_compact_workspace_bytes": (_sz, [_i64]),
     "gs_compact_grads": (_i32, [_vp, _i64, ctypes.c_uint32, _vp, _vp, _P(_i64), _vp, _sz, _vp]),
     "gs_decode_grads": (_i32, [_P(GradRecords), _i32, _vp, _i64, _vp, _vp]),
+    "gs_project_batch": (_i32, [_P(Gaussians), _i32, _P(Camera), _P(RasterParams), _P(Projected), _vp]),
+    "gs_grad_aggregate_adam_batch": (_i32, [_P(Gaussians), _i32, _P(Bins), _P(Camera), _P(RasterParams), _f32,
+                                            _P(ParamGrads), _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32, _f32,
+                                            _P(Camera), _P(Projected), _vp]),
+    "gs_adam_batch_hparams": (_i32, [_i32, ctypes.c_double, ctypes.c_double, ctypes.c_double, _P(AdamLrs),
+                                     _P(AdamLrs), _P(_f32), _P(_f32), _P(_f32)]),
     "gs_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -347,3 +354,36 @@ def gs_decode_grads(parts, grads2d, n_owner, rejected=None, stream=None):
     for i, (rec, r, base, owner, n_part) in enumerate(parts):
         arr[i] = GradRecords(_ptr(rec), int(r), int(base), _ptr(owner), int(n_part))
     _check(_lib.gs_decode_grads(arr, len(parts), _ptr(grads2d), int(n_owner), _ptr(rejected), _stream(stream)))
+
+
+def _array(cls, items):
+    arr = (cls * len(items))()
+    for k, it in enumerate(items):
+        arr[k] = it
+    return arr
+
+
+def gs_project_batch(g: Gaussians, cams, p: RasterParams, outs, stream=None):
+    """cams: list of Camera; outs: list of Projected (one per camera)."""
+    _check(_lib.gs_project_batch(ctypes.byref(g), len(cams), _array(Camera, cams), ctypes.byref(p),
+                                 _array(Projected, outs), _stream(stream)))
+
+
+def gs_grad_aggregate_adam_batch(g: Gaussians, bins, cams, p: RasterParams, grad_scale, m: ParamGrads,
+                                 v: ParamGrads, lr: "AdamLrs", step, beta1, beta2, eps, next_cams=None,
+                                 next_projs=None, stream=None):
+    """bins, cams: lists (one per view); next_cams / next_projs: lists or None."""
+    nc = _array(Camera, next_cams) if next_cams is not None else None
+    npj = _array(Projected, next_projs) if next_projs is not None else None
+    _check(_lib.gs_grad_aggregate_adam_batch(ctypes.byref(g), len(cams), _array(Bins, bins), _array(Camera, cams),
+                                             ctypes.byref(p), grad_scale, ctypes.byref(m), ctypes.byref(v),
+                                             ctypes.byref(lr), int(step), beta1, beta2, eps, nc, npj, _stream(stream)))
+
+
+def gs_adam_batch_hparams(batch, lr: "AdamLrs", beta1=0.9, beta2=0.999, eps=1e-15):
+    """(learning rates, beta1, beta2, eps) for a batch of `batch` views."""
+    out = AdamLrs()
+    b1, b2, e = _f32(), _f32(), _f32()
+    _check(_lib.gs_adam_batch_hparams(int(batch), beta1, beta2, eps, ctypes.byref(lr), ctypes.byref(out),
+                                      ctypes.byref(b1), ctypes.byref(b2), ctypes.byref(e)))
+    return out, b1.value, b2.value, e.value

@@ -213,3 +213,24 @@ extern "C" gs_status gs_adam_step(const gs_adam_group *groups, int32_t n_groups,
     GS_LAUNCH_CHECK("k_adam");
     return GS_OK;
 }
+
+extern "C" gs_status gs_adam_batch_hparams(int32_t batch, double beta1, double beta2, double eps,
+                                           const gs_adam_lrs *lr, gs_adam_lrs *lr_out, float *beta1_out,
+                                           float *beta2_out, float *eps_out)
+{
+    using namespace gsi;
+    if (batch < 1) return fail(GS_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+    if (!lr || !lr_out || !beta1_out || !beta2_out || !eps_out) return fail(GS_ERR_INVALID_ARGUMENT, "NULL argument");
+    const double bs = (double)batch, root = std::sqrt(bs);
+    const double b1 = 1.0 - bs * (1.0 - beta1), b2 = 1.0 - bs * (1.0 - beta2);
+    if (!(b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0))
+        return fail(GS_ERR_INVALID_ARGUMENT, "batch %d leaves a momentum coefficient outside [0, 1)", batch);
+    const float in[6] = {lr->means, lr->log_scales, lr->quats, lr->opacity_logits, lr->sh_dc, lr->sh_rest};
+    float o[6];
+    for (int a = 0; a < 6; ++a) o[a] = (float)((double)in[a] * root);
+    *lr_out = gs_adam_lrs{o[0], o[1], o[2], o[3], o[4], o[5]};
+    *beta1_out = (float)b1;
+    *beta2_out = (float)b2;
+    *eps_out = (float)(eps / root);
+    return GS_OK;
+}

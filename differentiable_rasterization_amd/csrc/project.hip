@@ -131,21 +131,44 @@ struct Proj {
 
 __device__ __forceinline__ bool finite_d(double x) { return __builtin_isfinite(x); }
 
-__device__ __forceinline__ void project_core(const CamD &cam, double mx, double my, double mz, float fmx,
-                                             float fmy, float fmz, double l0, double l1, double l2, double q0,
-                                             double q1, double q2, double q3, double logit, bool sh_finite,
-                                             double alpha_min, float depth_lo, float depth_hi, Proj &P)
+// The camera-independent transcendental values of one Gaussian: |q|, the scales, the
+// opacity and 2 ln(o / alpha_min).  ok is false for a Gaussian no camera keeps (non-finite
+// input, |q| = 0, opacity below alpha_min).
+struct ProjScalars {
+    bool ok;
+    double qnorm, s[3], o, lnr;
+};
+
+__device__ __forceinline__ void project_scalars(double mx, double my, double mz, double l0, double l1, double l2,
+                                                double q0, double q1, double q2, double q3, double logit,
+                                                bool sh_finite, double alpha_min, ProjScalars &S)
+{
+    S.ok = false;
+    if (!(finite_d(mx) && finite_d(my) && finite_d(mz) && finite_d(l0) && finite_d(l1) && finite_d(l2) &&
+          finite_d(q0) && finite_d(q1) && finite_d(q2) && finite_d(q3) && finite_d(logit) && sh_finite))
+        return;
+    S.qnorm = sqrt(q0 * q0 + q1 * q1 + q2 * q2 + q3 * q3);
+    if (!(S.qnorm > 0.0)) return;
+    S.s[0] = exp(l0); S.s[1] = exp(l1); S.s[2] = exp(l2);
+    S.o = 1.0 / (1.0 + exp(-logit));
+    const double o32 = (double)(float)S.o;
+    if (!(o32 >= alpha_min)) return;
+    S.lnr = 2.0 * log(o32 / alpha_min);
+    S.ok = true;
+}
+
+// The projection for one camera, from the Gaussian's parameters and its ProjScalars.
+__device__ __forceinline__ void project_view(const CamD &cam, double mx, double my, double mz, float fmx, float fmy,
+                                             float fmz, double q0, double q1, double q2, double q3,
+                                             const ProjScalars &S, float depth_lo, float depth_hi, Proj &P)
 {
     P.vis = false;
     P.rx = P.ry = 0;
     // camera-space depth as the float32 key: each step rounded explicitly
     P.key = __fadd_rn(__fmaf_rn(cam.r22, fmz, __fmaf_rn(cam.r21, fmy, __fmul_rn(cam.r20, fmx))), cam.t2);
-    if (!(finite_d(mx) && finite_d(my) && finite_d(mz) && finite_d(l0) && finite_d(l1) && finite_d(l2) &&
-          finite_d(q0) && finite_d(q1) && finite_d(q2) && finite_d(q3) && finite_d(logit) && sh_finite))
-        return;
-    P.qnorm = sqrt(q0 * q0 + q1 * q1 + q2 * q2 + q3 * q3);
-    if (!(P.qnorm > 0.0)) return;
+    if (!S.ok) return;
     if (!(P.key >= depth_lo && P.key < depth_hi)) return;
+    P.qnorm = S.qnorm;
     P.mu[0] = mx; P.mu[1] = my; P.mu[2] = mz;
     P.X = cam.R[0] * mx + cam.R[1] * my + cam.R[2] * mz + cam.t[0];
     P.Y = cam.R[3] * mx + cam.R[4] * my + cam.R[5] * mz + cam.t[1];
@@ -162,7 +185,7 @@ __device__ __forceinline__ void project_core(const CamD &cam, double mx, double 
     R[0] = 1.0 - 2.0 * (y * y + z * z); R[1] = 2.0 * (x * y - w * z);       R[2] = 2.0 * (x * z + w * y);
     R[3] = 2.0 * (x * y + w * z);       R[4] = 1.0 - 2.0 * (x * x + z * z); R[5] = 2.0 * (y * z - w * x);
     R[6] = 2.0 * (x * z - w * y);       R[7] = 2.0 * (y * z + w * x);       R[8] = 1.0 - 2.0 * (x * x + y * y);
-    P.s[0] = exp(l0); P.s[1] = exp(l1); P.s[2] = exp(l2);
+    P.s[0] = S.s[0]; P.s[1] = S.s[1]; P.s[2] = S.s[2];
     for (int r = 0; r < 3; ++r)
         for (int c = 0; c < 3; ++c) P.M[3 * r + c] = R[3 * r + c] * P.s[c];
     const double *M = P.M;
@@ -181,15 +204,15 @@ __device__ __forceinline__ void project_core(const CamD &cam, double mx, double 
         T[c] = j00 * cam.R[c] + j02 * cam.R[6 + c];
         T[3 + c] = j11 * cam.R[3 + c] + j12 * cam.R[6 + c];
     }
-    const double *S = P.Sig;
+    const double *Sg = P.Sig;
     // (T Sigma) rows
     double ts0[3], ts1[3];
-    ts0[0] = T[0] * S[0] + T[1] * S[1] + T[2] * S[2];
-    ts0[1] = T[0] * S[1] + T[1] * S[3] + T[2] * S[4];
-    ts0[2] = T[0] * S[2] + T[1] * S[4] + T[2] * S[5];
-    ts1[0] = T[3] * S[0] + T[4] * S[1] + T[5] * S[2];
-    ts1[1] = T[3] * S[1] + T[4] * S[3] + T[5] * S[4];
-    ts1[2] = T[3] * S[2] + T[4] * S[4] + T[5] * S[5];
+    ts0[0] = T[0] * Sg[0] + T[1] * Sg[1] + T[2] * Sg[2];
+    ts0[1] = T[0] * Sg[1] + T[1] * Sg[3] + T[2] * Sg[4];
+    ts0[2] = T[0] * Sg[2] + T[1] * Sg[4] + T[2] * Sg[5];
+    ts1[0] = T[3] * Sg[0] + T[4] * Sg[1] + T[5] * Sg[2];
+    ts1[1] = T[3] * Sg[1] + T[4] * Sg[3] + T[5] * Sg[4];
+    ts1[2] = T[3] * Sg[2] + T[4] * Sg[4] + T[5] * Sg[5];
     P.a = ts0[0] * T[0] + ts0[1] * T[1] + ts0[2] * T[2];
     P.b = ts0[0] * T[3] + ts0[1] * T[4] + ts0[2] * T[5];
     P.c = ts1[0] * T[3] + ts1[1] * T[4] + ts1[2] * T[5];
@@ -198,10 +221,8 @@ __device__ __forceinline__ void project_core(const CamD &cam, double mx, double 
     const double idet = 1.0 / P.det;
     P.A = P.c * idet; P.B = -P.b * idet; P.C = P.a * idet;
 
-    P.o = 1.0 / (1.0 + exp(-logit));
-    const double o32 = (double)(float)P.o;
-    if (!(o32 >= alpha_min)) return;
-    const double lnr = 2.0 * log(o32 / alpha_min);
+    P.o = S.o;
+    const double lnr = S.lnr;
     double ex = ceil(sqrt(lnr * P.a)), ey = ceil(sqrt(lnr * P.c));
     ex = fmin(fmax(ex, 1.0), (double)GS_RADIUS_CAP);
     ey = fmin(fmax(ey, 1.0), (double)GS_RADIUS_CAP);
@@ -212,6 +233,16 @@ __device__ __forceinline__ void project_core(const CamD &cam, double mx, double 
     const double id = 1.0 / P.dist;
     P.dir[0] = (float)(dx * id); P.dir[1] = (float)(dy * id); P.dir[2] = (float)(dz * id);
     P.vis = true;
+}
+
+__device__ __forceinline__ void project_core(const CamD &cam, double mx, double my, double mz, float fmx,
+                                             float fmy, float fmz, double l0, double l1, double l2, double q0,
+                                             double q1, double q2, double q3, double logit, bool sh_finite,
+                                             double alpha_min, float depth_lo, float depth_hi, Proj &P)
+{
+    ProjScalars S;
+    project_scalars(mx, my, mz, l0, l1, l2, q0, q1, q2, q3, logit, sh_finite, alpha_min, S);
+    project_view(cam, mx, my, mz, fmx, fmy, fmz, q0, q1, q2, q3, S, depth_lo, depth_hi, P);
 }
 
 // The conic and opacity of the raster record, as float: a = -A log2(e)/2, b = -B log2(e),
@@ -265,17 +296,38 @@ struct ProjOut {
 
 // Projects Gaussian i with parameters prm and stores its projected record: the one
 // definition both gs_project and the projection fused into the end of a step use.
+template <int K>
+__device__ __forceinline__ void params_scalars(const Params1<K> &prm, float alpha_min, ProjScalars &S)
+{
+    project_scalars(prm.means[0], prm.means[1], prm.means[2], prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1],
+                    prm.q[2], prm.q[3], prm.logit, sh_finite(prm), (double)alpha_min, S);
+}
+
+template <int DEG>
+__device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG + 1)> &prm, const ProjScalars &S,
+                                                const CamD &cam, float depth_lo, float depth_hi, int64_t i,
+                                                const ProjOut &po);
+
 template <int DEG>
 __device__ __forceinline__ void project_store(const Params1<(DEG + 1) * (DEG + 1)> &prm, const CamD &cam,
                                               float alpha_min, float depth_lo, float depth_hi, int64_t i,
                                               const ProjOut &po)
 {
+    ProjScalars S;
+    params_scalars(prm, alpha_min, S);
+    project_store_s<DEG>(prm, S, cam, depth_lo, depth_hi, i, po);
+}
+
+// project_store with the Gaussian's camera-independent values already computed.
+template <int DEG>
+__device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG + 1)> &prm, const ProjScalars &S,
+                                                const CamD &cam, float depth_lo, float depth_hi, int64_t i,
+                                                const ProjOut &po)
+{
     constexpr int K = (DEG + 1) * (DEG + 1);
-    const bool shf = sh_finite(prm);
     Proj P;
     const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
-    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
-                 prm.q[3], prm.logit, shf, (double)alpha_min, depth_lo, depth_hi, P);
+    project_view(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.q[0], prm.q[1], prm.q[2], prm.q[3], S, depth_lo, depth_hi, P);
     po.depth[i] = P.key;
     po.radii[i] = make_int2(P.rx, P.ry);
     if (!P.vis) return;
@@ -383,9 +435,9 @@ struct AdamSink {
     }
 
     // Updates and stores every parameter scalar of Gaussian i; P holds the updated values
-    // afterwards.
-    template <int K>
-    __device__ void flush(int64_t i, const Grad3<K> &g, Params1<K> &P) const
+    // afterwards.  Grad: Grad3 or GradSum (means, ls, q, logit and sh(plane)).
+    template <class Grad, int K>
+    __device__ void flush(int64_t i, const Grad &g, Params1<K> &P) const
     {
         {   // means, log_scales, quats, opacity: 11 scalars
             const int grp[11] = {0, 0, 0, 1, 1, 1, 2, 2, 2, 2, 3};
@@ -608,6 +660,130 @@ __global__ __launch_bounds__(256) void k_grad_adam(
                                      acc, grads2d, out, next_cam, next);
 }
 
+// -------------------------------------------------------------------- batches of views
+// A training step over a batch of views (ROCm blog, "Batching and Hyperparameter Scaling":
+// several camera views per optimiser step): the Gaussians are projected for every view of
+// the batch in one pass over the parameters, each view is binned and rasterized on its own,
+// and one pass per Gaussian sums each view's slots, takes each view's projection backward,
+// adds the 3D gradients over the views, applies one Adam update and projects the updated
+// Gaussian for the views of the next batch.
+constexpr int kMaxViews = 4;
+
+struct ViewBins {
+    const gsr::BinsHeader *hdr;
+    const uint32_t *qoff;
+    const float4 *qgrad;
+    const uint2 *qstamp;
+};
+
+struct BatchProj {
+    int views;
+    CamD cam[kMaxViews];
+    ProjOut out[kMaxViews];
+};
+
+struct BatchGrad {
+    int views;
+    float grad_scale;
+    CamD cam[kMaxViews];
+    ViewBins vb[kMaxViews];
+};
+
+// 3D gradients summed over views; the SH gradients as per-plane sums of Y_k(v^) dL/dc,
+// kept in LDS (one column per thread of the block) to leave the registers to the
+// projection backward.
+template <int K>
+struct GradSum {
+    float means[3], ls[3], q[4], logit;
+    float (*shg)[256];
+    int t;
+    __device__ float sh(int plane) const { return shg[plane][t]; }
+};
+
+template <int DEG>
+__global__ __launch_bounds__(256) void k_project_batch(const float *__restrict__ means,
+                                                       const float *__restrict__ log_scales,
+                                                       const float *__restrict__ quats, const float *__restrict__ logits,
+                                                       const float *__restrict__ sh, int64_t n, float alpha_min,
+                                                       float depth_lo, float depth_hi, BatchProj bp)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    Params1<K> prm;
+    load_params(means, log_scales, quats, logits, sh, n, i, prm);
+    ProjScalars S;
+    params_scalars(prm, alpha_min, S);
+    for (int v = 0; v < bp.views; ++v) project_store_s<DEG>(prm, S, bp.cam[v], depth_lo, depth_hi, i, bp.out[v]);
+}
+
+// Per Gaussian: for each view in order, the Eq. 4 sum over that view's slots, scaled by
+// grad_scale (the batch mean: 1 / views), and the projection backward for that view's
+// camera, added to the running 3D gradients; then the Adam update; with NEXT, the
+// projections of the updated Gaussian for the next batch's views.
+template <int DEG, bool NEXT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_grad_adam_batch(
+    const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, float alpha_min, float depth_lo,
+    float depth_hi, BatchGrad bg, AdamSink out, BatchProj next)
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    __shared__ gsr::SlotStage stage[4];
+    __shared__ float shacc[3 * K][256];
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = i < n;
+    Params1<K> prm;
+    ProjScalars PS;
+    PS.ok = false;
+    if (live) {
+        load_params(means, log_scales, quats, logits, sh, n, i, prm);
+        params_scalars(prm, alpha_min, PS);
+    }
+    GradSum<K> S;
+    for (int j = 0; j < 3; ++j) S.means[j] = S.ls[j] = 0.0f;
+    for (int j = 0; j < 4; ++j) S.q[j] = 0.0f;
+    S.logit = 0.0f;
+    S.shg = shacc;
+    S.t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) shacc[k][threadIdx.x] = 0.0f;
+    for (int v = 0; v < bg.views; ++v) {
+        float acc[9];
+        // every lane of the wave takes part in the slot sums
+        gsr::raw_slot_sums(bg.vb[v].hdr, bg.vb[v].qoff, bg.vb[v].qgrad, bg.vb[v].qstamp, i, n,
+                           stage[threadIdx.x >> 6], acc);
+        if (live) {
+            Proj P;
+            const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
+            project_view(bg.cam[v], fmx, fmy, fmz, fmx, fmy, fmz, prm.q[0], prm.q[1], prm.q[2], prm.q[3], PS, depth_lo,
+                         depth_hi, P);
+            if (P.vis) {
+                const RecConic rc = rec_conic(P);
+                float g2[9];
+                gsr::moments_to_grads(acc, rc.a, rc.b, rc.c, rc.l, g2);
+#pragma unroll
+                for (int f = 0; f < 9; ++f) g2[f] *= bg.grad_scale;
+                Grad3<K> G;
+                project_bwd_grads<DEG>(P, bg.cam[v], g2, prm, G);
+                for (int j = 0; j < 3; ++j) { S.means[j] += G.means[j]; S.ls[j] += G.ls[j]; }
+                for (int j = 0; j < 4; ++j) S.q[j] += G.q[j];
+                S.logit += G.logit;
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int c = 0; c < 3; ++c) shacc[3 * k + c][threadIdx.x] += G.Y[k] * G.gc[c];
+            }
+        }
+    }
+    if (!live) return;
+    out.flush(i, S, prm);
+    if constexpr (NEXT) {
+        params_scalars(prm, alpha_min, PS);   // of the updated Gaussian
+        for (int v = 0; v < next.views; ++v)
+            project_store_s<DEG>(prm, PS, next.cam[v], depth_lo, depth_hi, i, next.out[v]);
+    }
+}
+
 }  // namespace
 
 namespace gsi {
@@ -713,6 +889,51 @@ gs_status check_raster_inputs(const gs_bins *bins, const gs_camera *cam);
 
 namespace {
 
+gs_status make_adam_sink(const gs_gaussians *g, const gs_param_grads *m, const gs_param_grads *v,
+                         const gs_adam_lrs *lr, int32_t step, float beta1, float beta2, float eps, AdamSink &sink)
+{
+    using namespace gsi;
+    if (!m->means || !m->log_scales || !m->quats || !m->opacity_logits || !m->sh || !v->means || !v->log_scales ||
+        !v->quats || !v->opacity_logits || !v->sh)
+        return fail(GS_ERR_INVALID_ARGUMENT, "an Adam moment pointer is NULL");
+    float *params[5] = {const_cast<float *>(g->means), const_cast<float *>(g->log_scales), const_cast<float *>(g->quats),
+                        const_cast<float *>(g->opacity_logits), const_cast<float *>(g->sh)};
+    float *ms[5] = {m->means, m->log_scales, m->quats, m->opacity_logits, m->sh};
+    float *vs[5] = {v->means, v->log_scales, v->quats, v->opacity_logits, v->sh};
+    for (int a = 0; a < 5; ++a) { sink.p[a] = params[a]; sink.m[a] = ms[a]; sink.v[a] = vs[a]; }
+    sink.n = g->n;
+    // the same host arithmetic as gs_adam_step, so that both paths agree bit for bit
+    const double bc1 = 1.0 - std::pow((double)beta1, step), bc2 = 1.0 - std::pow((double)beta2, step);
+    const float lrs[6] = {lr->means, lr->log_scales, lr->quats, lr->opacity_logits, lr->sh_dc, lr->sh_rest};
+    for (int a = 0; a < 6; ++a) sink.st[a] = (float)((double)lrs[a] / bc1);
+    sink.b1 = beta1;
+    sink.b2 = beta2;
+    sink.inv_bc2 = (float)(1.0 / bc2);
+    sink.eps = eps;
+    return GS_OK;
+}
+
+gs_status check_adam_args(const gs_param_grads *m, const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step,
+                          float beta1, float beta2, float eps)
+{
+    using namespace gsi;
+    if (!m || !v || !lr) return fail(GS_ERR_INVALID_ARGUMENT, "m / v / lr is NULL");
+    if (step < 1) return fail(GS_ERR_INVALID_ARGUMENT, "step must be >= 1");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f && beta2 >= 0.0f && beta2 < 1.0f && eps >= 0.0f))
+        return fail(GS_ERR_INVALID_ARGUMENT, "bad Adam hyper-parameters");
+    return GS_OK;
+}
+
+ViewBins view_bins(const gs_bins *bins, const gs_camera *cam, int64_t n)
+{
+    const int T = gsi::tiles_x(cam->width) * gsi::tiles_y(cam->height);
+    const gsr::RasterLayout L = gsr::raster_layout(n, bins->capacity, T);
+    const char *rb = static_cast<const char *>(bins->raster);
+    return ViewBins{reinterpret_cast<const gsr::BinsHeader *>(rb + L.hdr),
+                    reinterpret_cast<const uint32_t *>(rb + L.qoff), reinterpret_cast<const float4 *>(rb + L.qgrad),
+                    reinterpret_cast<const uint2 *>(rb + L.qstamp)};
+}
+
 gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins, const gs_camera *cam,
                            const gs_raster_params *p, float *grads2d, const gs_param_grads *m,
                            const gs_param_grads *v, const gs_adam_lrs *lr, int32_t step, float beta1, float beta2,
@@ -736,24 +957,8 @@ gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, cons
         if ((s = check_proj_out(next_proj, n)) != GS_OK) return s;
     }
     if (n == 0) return GS_OK;
-    if (!m->means || !m->log_scales || !m->quats || !m->opacity_logits || !m->sh || !v->means || !v->log_scales ||
-        !v->quats || !v->opacity_logits || !v->sh)
-        return fail(GS_ERR_INVALID_ARGUMENT, "an Adam moment pointer is NULL");
     AdamSink sink;
-    float *params[5] = {const_cast<float *>(g->means), const_cast<float *>(g->log_scales), const_cast<float *>(g->quats),
-                        const_cast<float *>(g->opacity_logits), const_cast<float *>(g->sh)};
-    float *ms[5] = {m->means, m->log_scales, m->quats, m->opacity_logits, m->sh};
-    float *vs[5] = {v->means, v->log_scales, v->quats, v->opacity_logits, v->sh};
-    for (int a = 0; a < 5; ++a) { sink.p[a] = params[a]; sink.m[a] = ms[a]; sink.v[a] = vs[a]; }
-    sink.n = n;
-    // the same host arithmetic as gs_adam_step, so that both paths agree bit for bit
-    const double bc1 = 1.0 - std::pow((double)beta1, step), bc2 = 1.0 - std::pow((double)beta2, step);
-    const float lrs[6] = {lr->means, lr->log_scales, lr->quats, lr->opacity_logits, lr->sh_dc, lr->sh_rest};
-    for (int a = 0; a < 6; ++a) sink.st[a] = (float)((double)lrs[a] / bc1);
-    sink.b1 = beta1;
-    sink.b2 = beta2;
-    sink.inv_bc2 = (float)(1.0 / bc2);
-    sink.eps = eps;
+    if ((s = make_adam_sink(g, m, v, lr, step, beta1, beta2, eps, sink)) != GS_OK) return s;
     const int T = tiles_x(cam->width) * tiles_y(cam->height);
     const gsr::RasterLayout L = gsr::raster_layout(n, bins->capacity, T);
     const char *rb = static_cast<const char *>(bins->raster);
@@ -810,4 +1015,101 @@ extern "C" gs_status gs_grad_aggregate_adam_project(const gs_gaussians *g, const
     if (!next_cam) return gsi::fail(GS_ERR_INVALID_ARGUMENT, "next_cam is NULL");
     return grad_adam_launch(g, proj, bins, cam, p, grads2d, m, v, lr, step, beta1, beta2, eps, next_cam, next_proj,
                             stream);
+}
+
+extern "C" gs_status gs_project_batch(const gs_gaussians *g, int32_t views, const gs_camera *cams,
+                                      const gs_raster_params *p, gs_projected *out, hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if (views < 1 || views > kMaxViews) return fail(GS_ERR_INVALID_ARGUMENT, "views must lie in [1, %d]", kMaxViews);
+    if (!cams || !out) return fail(GS_ERR_INVALID_ARGUMENT, "cams / out is NULL");
+    if ((s = check_gaussians(g)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    BatchProj bp = {};
+    bp.views = views;
+    for (int v = 0; v < views; ++v) {
+        if ((s = check_camera(&cams[v])) != GS_OK) return s;
+        if ((s = check_proj_out(&out[v], g->n)) != GS_OK) return s;
+        bp.cam[v] = make_cam(&cams[v]);
+        bp.out[v] = proj_out(&out[v]);
+    }
+    const int64_t n = g->n;
+    if (n == 0) return GS_OK;
+    const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+#define GS_PB(D)                                                                                                    \
+    k_project_batch<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
+                                                   p->alpha_min, p->depth_lo, p->depth_hi, bp)
+    switch (p->sh_degree) {
+    case 0: GS_PB(0); break;
+    case 1: GS_PB(1); break;
+    case 2: GS_PB(2); break;
+    default: GS_PB(3); break;
+    }
+#undef GS_PB
+    GS_LAUNCH_CHECK("k_project_batch");
+    return GS_OK;
+}
+
+extern "C" gs_status gs_grad_aggregate_adam_batch(const gs_gaussians *g, int32_t views, const gs_bins *bins,
+                                                  const gs_camera *cams, const gs_raster_params *p, float grad_scale,
+                                                  const gs_param_grads *m, const gs_param_grads *v,
+                                                  const gs_adam_lrs *lr, int32_t step, float beta1, float beta2,
+                                                  float eps, const gs_camera *next_cams, gs_projected *next_proj,
+                                                  hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if (views < 1 || views > kMaxViews) return fail(GS_ERR_INVALID_ARGUMENT, "views must lie in [1, %d]", kMaxViews);
+    if (!bins || !cams) return fail(GS_ERR_INVALID_ARGUMENT, "bins / cams is NULL");
+    if ((s = check_gaussians(g)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    if ((s = check_adam_args(m, v, lr, step, beta1, beta2, eps)) != GS_OK) return s;
+    if (!(grad_scale > 0.0f) || !__builtin_isfinite(grad_scale))
+        return fail(GS_ERR_INVALID_ARGUMENT, "grad_scale must be positive and finite");
+    const int64_t n = g->n;
+    BatchGrad bg = {};
+    bg.views = views;
+    bg.grad_scale = grad_scale;
+    for (int k = 0; k < views; ++k) {
+        if ((s = check_camera(&cams[k])) != GS_OK) return s;
+        if ((s = check_raster_inputs(&bins[k], &cams[k])) != GS_OK) return s;
+        bg.cam[k] = make_cam(&cams[k]);
+        bg.vb[k] = view_bins(&bins[k], &cams[k], n);
+    }
+    BatchProj next = {};
+    if (next_cams) {
+        if (!next_proj) return fail(GS_ERR_INVALID_ARGUMENT, "next_proj is NULL");
+        next.views = views;
+        for (int k = 0; k < views; ++k) {
+            if ((s = check_camera(&next_cams[k])) != GS_OK) return s;
+            if ((s = check_proj_out(&next_proj[k], n)) != GS_OK) return s;
+            next.cam[k] = make_cam(&next_cams[k]);
+            next.out[k] = proj_out(&next_proj[k]);
+        }
+    }
+    if (n == 0) return GS_OK;
+    AdamSink sink;
+    if ((s = make_adam_sink(g, m, v, lr, step, beta1, beta2, eps, sink)) != GS_OK) return s;
+    const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+#define GS_GB(D)                                                                                                     \
+    do {                                                                                                             \
+        if (next_cams)                                                                                               \
+            k_grad_adam_batch<D, true><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,                \
+                                                                   g->opacity_logits, g->sh, n, p->alpha_min,        \
+                                                                   p->depth_lo, p->depth_hi, bg, sink, next);        \
+        else                                                                                                         \
+            k_grad_adam_batch<D, false><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,               \
+                                                                    g->opacity_logits, g->sh, n, p->alpha_min,       \
+                                                                    p->depth_lo, p->depth_hi, bg, sink, next);       \
+    } while (0)
+    switch (p->sh_degree) {
+    case 0: GS_GB(0); break;
+    case 1: GS_GB(1); break;
+    case 2: GS_GB(2); break;
+    default: GS_GB(3); break;
+    }
+#undef GS_GB
+    GS_LAUNCH_CHECK("k_grad_adam_batch");
+    return GS_OK;
 }

@@ -5,8 +5,8 @@ of the computation runs in libgsmi's kernels:
 
     gs_project -> gs_bin_sort -> gs_raster_fwd -> gs_loss_l1 -> gs_raster_bwd -> gs_adam_step
 
-and of one training step over depth slabs rendered separately and over-composited
-(PartitionedStep).
+of one training step over depth slabs rendered separately and over-composited
+(PartitionedStep), and of one training step over a batch of views (BatchTrainStep).
 
 Parameters, gradients and the two Adam moments each live in one contiguous
 [planes][N] float32 buffer (structure of arrays), so every kernel streams
@@ -235,6 +235,59 @@ class TrainStep:
         self.loss(target, stream)
         self.backward(cam, stream=stream)
         self.adam(stream)
+
+
+class BatchTrainStep:
+    """One optimiser step over a batch of views (ROCm blog, "Batching and Hyperparameter
+    Scaling": several camera views per step, learning rates times sqrt(BS), eps / sqrt(BS),
+    betas 1 - BS (1 - beta)).  The Gaussians are projected for all views of the batch in one
+    pass (gs_project_batch); each view is binned and runs the fused forward + L1 + backward
+    (the loss of the batch is the mean of the views' L1 losses); one pass per Gaussian then
+    adds the views' gradients, applies Adam and projects the updated Gaussians for the next
+    batch's views (gs_grad_aggregate_adam_batch)."""
+
+    MAX_VIEWS = 4
+
+    def __init__(self, params: GaussianParams, width, height, views, device="cuda", raster=None, lr=DEFAULT_LR,
+                 capacity=0):
+        if not 1 <= views <= self.MAX_VIEWS:
+            raise ValueError(f"views must lie in [1, {self.MAX_VIEWS}]")
+        self.params, self.views = params, views
+        self.raster = raster if raster is not None else B.make_params(params.sh_degree)
+        self.proj = [Projection(params.n, device) for _ in range(views)]
+        self.bins = [Binning(params.n, width, height, capacity=capacity, device=device) for _ in range(views)]
+        self.frame = [Frame(width, height, device) for _ in range(views)]
+        self.lrs, self.beta1, self.beta2, self.eps = B.gs_adam_batch_hparams(views, B.AdamLrs(**lr))
+
+    def project(self, cams, stream=None):
+        B.gs_project_batch(self.params.gaussians(), cams, self.raster, [p.abi() for p in self.proj], stream)
+
+    def sort(self, k, cam: B.Camera, stream=None):
+        self.bins[k].sort(self.proj[k], cam, self.raster, stream)
+
+    def render(self, k, cam: B.Camera, target, stream=None):
+        """View k: forward, L1 loss and the per-record backward in one kernel."""
+        f = self.frame[k]
+        B.gs_raster_fused_l1(self.params.gaussians(), self.bins[k].abi(), cam, self.raster, target, f.color,
+                             f.t_final, f.n_trav, f.loss, f.n_trav_sum, f.fused_ws, stream)
+
+    def update(self, cams, next_cams=None, stream=None):
+        """The views' gradients (mean over the batch), Adam and, with next_cams, the next
+        batch's projections into self.proj."""
+        self.params.step_count += 1
+        m, v = self.params.moments()
+        nxt = [p.abi() for p in self.proj] if next_cams is not None else None
+        B.gs_grad_aggregate_adam_batch(self.params.gaussians(), [b.abi() for b in self.bins], cams, self.raster,
+                                       1.0 / self.views, m, v, self.lrs, self.params.step_count, self.beta1,
+                                       self.beta2, self.eps, next_cams, nxt, stream)
+
+    def step(self, cams, targets, next_cams=None, stream=None):
+        """The batch's projections must be in self.proj (project(), or the previous step's
+        update with next_cams)."""
+        for k in range(self.views):
+            self.sort(k, cams[k], stream)
+            self.render(k, cams[k], targets[k], stream)
+        self.update(cams, next_cams, stream)
 
 
 class PartitionedStep:

@@ -23,6 +23,8 @@
  *   ByteSplat section 3 Insight 4 and section 6.1)
  *   owner-side decoding and atomic aggregation of those records -> gs_decode_grads
  *   (ByteSplat section 6.2)
+ *   batches of views per optimiser step -> gs_project_batch, gs_grad_aggregate_adam_batch,
+ *   gs_adam_batch_hparams  (ROCm blog, "Batching and Hyperparameter Scaling")
  *
  * Conventions (all entry points):
  *   - Every pointer argument that names device memory must be a device (or managed)
@@ -329,6 +331,42 @@ gs_status gs_grad_aggregate_adam_project(const gs_gaussians *g, const gs_project
                                          const gs_param_grads *m, const gs_param_grads *v, const gs_adam_lrs *lr,
                                          int32_t step, float beta1, float beta2, float eps,
                                          const gs_camera *next_cam, gs_projected *next_proj, hipStream_t stream);
+
+/* ---- batches of views (ROCm blog, "Batching and Hyperparameter Scaling": several camera
+ * views per optimiser step; gsplat's projection of C cameras x N Gaussians in one call).
+ * A batch holds 1 <= views <= 4 views; cams, bins, out and next_proj are host arrays of
+ * `views` structs. */
+
+/* Projects the Gaussians for every camera of the batch in one pass over the parameters:
+ * out[k] receives exactly what gs_project(g, &cams[k], p, &out[k]) writes. */
+gs_status gs_project_batch(const gs_gaussians *g, int32_t views, const gs_camera *cams,
+                           const gs_raster_params *p, gs_projected *out, hipStream_t stream);
+
+/* The end of a training step over a batch of views in one pass over the Gaussians: per
+ * Gaussian and for k = 0 .. views-1 in order, the per-Gaussian part of the ByteSplat Eq. 4
+ * sum over the slots of bins[k] (written by gs_raster_bwd_partials or gs_raster_fused_l1
+ * for camera cams[k]), its screen-space gradients multiplied by grad_scale (1/views for the
+ * mean of the views' losses), and the projection backward for cams[k], added to the 3D
+ * gradients of the views before it; then one Adam update with the sum (as
+ * gs_grad_aggregate_adam); then, if next_cams is non-NULL, the projection of the updated
+ * Gaussian for every next_cams[k] into next_proj[k] (as gs_project_batch).  For a
+ * power-of-two grad_scale the result equals, bit for bit, gs_grad_aggregate and
+ * gs_project_bwd per view, the 3D gradients scaled by grad_scale and added in view order,
+ * and gs_adam_step.  The 3D gradients are never stored.  Adam hyper-parameters for a batch:
+ * gs_adam_batch_hparams. */
+gs_status gs_grad_aggregate_adam_batch(const gs_gaussians *g, int32_t views, const gs_bins *bins,
+                                       const gs_camera *cams, const gs_raster_params *p, float grad_scale,
+                                       const gs_param_grads *m, const gs_param_grads *v, const gs_adam_lrs *lr,
+                                       int32_t step, float beta1, float beta2, float eps,
+                                       const gs_camera *next_cams, gs_projected *next_proj, hipStream_t stream);
+
+/* Adam hyper-parameters for a batch of `batch` views (ROCm blog, "Batching and
+ * Hyperparameter Scaling", with BS = batch on one GPU): every learning rate times
+ * sqrt(BS), eps / sqrt(BS), beta_i -> 1 - BS (1 - beta_i), in double precision and rounded
+ * to float once.  Host only (no device work).  GS_ERR_INVALID_ARGUMENT if batch < 1 or a
+ * scaled beta falls outside [0, 1) (beta1 = 0.9 reaches 0 at BS = 10). */
+gs_status gs_adam_batch_hparams(int32_t batch, double beta1, double beta2, double eps, const gs_adam_lrs *lr,
+                                gs_adam_lrs *lr_out, float *beta1_out, float *beta2_out, float *eps_out);
 
 /* Backward through projection and colour evaluation alone (ByteSplat section 2.1: the
  * aggregated screen-space gradients are propagated through projection and colour

@@ -320,6 +320,19 @@ def decode(parts, n_owner, out=None):
     return res, int(rej)
 
 
+def adam_batch_hparams(bs, lrs, beta1=0.9, beta2=0.999, eps=1e-15):
+    """(lrs [6], beta1, beta2, eps) scaled for BS views per step, or None if degenerate."""
+    L = lib()
+    lr = (ctypes.c_double * 6)(*[float(x) for x in lrs])
+    b1, b2, e = ctypes.c_double(beta1), ctypes.c_double(beta2), ctypes.c_double(eps)
+    f = L.orc_adam_batch_hparams
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    if f(int(bs), lr, ctypes.byref(b1), ctypes.byref(b2), ctypes.byref(e)) != 0:
+        return None
+    return list(lr), b1.value, b2.value, e.value
+
+
 def sh_basis(deg, dirs):
     """Y [m][(deg+1)^2] and dY [m][(deg+1)^2][3] at unit vectors dirs [m][3]."""
     L = lib()

@@ -1054,3 +1054,20 @@ int64_t orc_decode(int k, const uint32_t *const *records, const int64_t *r, cons
     }
     return rejected;
 }
+
+/* Adam hyper-parameters for BS views per optimiser step ["Scaling 3D Gaussian Splatting
+ * with Distributed Compute", section "Batching and Hyperparameter Scaling"]: learning
+ * rates grow with the square root of BS, eps shrinks by it, and each momentum coefficient
+ * is linearised as 1 - BS (1 - beta).  lr: 6 rates in, scaled in place.  Returns 0, or -1
+ * when a scaled beta leaves [0, 1). */
+int orc_adam_batch_hparams(int bs, double *lr, double *beta1, double *beta2, double *eps)
+{
+    const double root = sqrt((double)bs);
+    const double b1 = 1.0 - bs * (1.0 - *beta1), b2 = 1.0 - bs * (1.0 - *beta2);
+    if (bs < 1 || !(b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 && b2 < 1.0)) return -1;
+    for (int a = 0; a < 6; ++a) lr[a] *= root;
+    *beta1 = b1;
+    *beta2 = b2;
+    *eps /= root;
+    return 0;
+}

@@ -10,6 +10,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 from differentiable_rasterization_amd import binding as B
@@ -200,3 +201,37 @@ def test_decode_argument_errors_before_launch():
     empty = (B.GradRecords * 1)(B.GradRecords(None, 0, 0, None, 0))
     assert B._lib.gs_decode_grads(empty, 1, None, 0, None, None) == B.GS_OK
     assert B._lib.gs_decode_grads(one, 1, None, 0, None, None) == B.GS_OK
+
+
+def test_batch_hparams_match_oracle():
+    """gs_adam_batch_hparams (host only) rounds the oracle's double-precision values once."""
+    import oracle
+    lrs = [1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3, 1.25e-4]
+    lr = B.AdamLrs(*lrs)
+    names = ("means", "log_scales", "quats", "opacity_logits", "sh_dc", "sh_rest")
+    for bs in range(1, 11):
+        out, b1, b2, e = B.gs_adam_batch_hparams(bs, lr)
+        # the oracle scales the float32 rates the ABI receives
+        o_lr, o_b1, o_b2, o_e = oracle.adam_batch_hparams(bs, [getattr(lr, nm) for nm in names])
+        for nm, want in zip(names, o_lr):
+            assert getattr(out, nm) == float(np.float32(want)), (bs, nm)
+        assert b1 == float(np.float32(o_b1)) and b2 == float(np.float32(o_b2)) and e == float(np.float32(o_e))
+    for bad in (0, 11):
+        with pytest.raises(B.GsError):
+            B.gs_adam_batch_hparams(bad, lr)
+
+
+def test_batch_argument_errors_before_launch():
+    g = B.Gaussians(None, None, None, None, None, 0)
+    cams = (B.Camera * 5)(*([_cam()] * 5))
+    outs = (B.Projected * 5)()
+    p = B.make_params(3)
+    assert B._lib.gs_project_batch(ctypes.byref(g), 0, cams, ctypes.byref(p), outs, None) == B.GS_ERR_INVALID_ARGUMENT
+    assert B._lib.gs_project_batch(ctypes.byref(g), 5, cams, ctypes.byref(p), outs, None) == B.GS_ERR_INVALID_ARGUMENT
+    assert B._lib.gs_project_batch(ctypes.byref(g), 2, cams, ctypes.byref(p), outs, None) == B.GS_OK   # n = 0
+    bins = (B.Bins * 2)()
+    m = B.ParamGrads()
+    lr = B.AdamLrs()
+    st = B._lib.gs_grad_aggregate_adam_batch(ctypes.byref(g), 2, bins, cams, ctypes.byref(p), 0.5, ctypes.byref(m),
+                                             ctypes.byref(m), ctypes.byref(lr), 1, 0.9, 0.999, 1e-15, None, None, None)
+    assert st == B.GS_ERR_INVALID_ARGUMENT      # the bins have no tile lists

@@ -390,6 +390,139 @@ def test_fused_adam_projection_matches_separate_calls(name):
     assert int((pb[0][4][:, 0] > 0).sum()) > 0
 
 
+def _views(cam, k):
+    """k cameras: cam and copies moved sideways and back by growing amounts."""
+    out = [cam]
+    for j in range(1, k):
+        vm = cam.viewmat.clone().reshape(4, 4)
+        vm[0, 3] += 0.15 * j
+        vm[1, 3] -= 0.05 * j
+        vm[2, 3] += 0.3 * j
+        out.append(scenes._camera(vm.reshape(16).contiguous(), cam.width, cam.height))
+    return out
+
+
+@pytest.mark.parametrize("name,views", [("tiny", 1), ("tiny", 4), ("ragged_sh1", 3), ("ragged_sh2", 2),
+                                        ("offscreen_sh3", 4), ("100k", 4)])
+def test_project_batch_matches_project(name, views):
+    """gs_project_batch writes for every camera exactly what gs_project writes."""
+    sc = _scene(name)
+    cams = [B.camera_from(c) for c in _views(sc.cameras[0], views)]
+    rp = B.make_params(sc.sh_degree)
+    params = PL.GaussianParams.from_scene(sc, DEV)
+    batch = [PL.Projection(sc.n, DEV) for _ in cams]
+    B.gs_project_batch(params.gaussians(), cams, rp, [p.abi() for p in batch])
+    for c, pb in zip(cams, batch):
+        one = PL.Projection(sc.n, DEV)
+        B.gs_project(params.gaussians(), c, rp, one.abi())
+        torch.cuda.synchronize()
+        for a, b in zip(_proj_fields(one), _proj_fields(pb)):
+            assert torch.equal(a, b)
+
+
+def _batch_setup(sc, views, rp):
+    """A BatchTrainStep with every view projected, binned and rendered (fused L1)."""
+    cams = [B.camera_from(c) for c in _views(sc.cameras[0], views)]
+    params = PL.GaussianParams.from_scene(sc, DEV)
+    bt = PL.BatchTrainStep(params, sc.cameras[0].width, sc.cameras[0].height, views, DEV, raster=rp)
+    bt.project(cams)
+    tgt = sc.targets[0].to(DEV)
+    for k, c in enumerate(cams):
+        bt.sort(k, c)
+        bt.render(k, c, tgt)
+    torch.cuda.synchronize()
+    return bt, cams
+
+
+@pytest.mark.parametrize("name,views", [("tiny", 1), ("tiny", 4), ("ragged_sh1", 2), ("ragged_sh2", 4),
+                                        ("offscreen_sh3", 2), ("100k", 4)])
+def test_batch_end_of_step_matches_separate_calls(name, views):
+    """gs_grad_aggregate_adam_batch equals, bit for bit, gs_grad_aggregate + gs_project_bwd per
+    view, the 3D gradients scaled by 1/views and added in view order, gs_adam_step with the
+    batch hyper-parameters, and gs_project_batch of the updated Gaussians for the next views
+    (parameters, Adam moments and every projected field)."""
+    log(f"batch end of step {name} views={views}")
+    sc = _scene(name)
+    rp = B.make_params(sc.sh_degree)
+    bt, cams = _batch_setup(sc, views, rp)
+    nxt = [B.camera_from(c) for c in _views(_moved_camera(sc.cameras[0]), views)]
+    p0 = bt.params.data.clone()
+    # separate calls on a copy of the parameters, reading the same slots
+    ref = PL.GaussianParams.from_scene(sc, DEV)
+    acc = torch.zeros_like(ref.grad)
+    g2 = torch.zeros(9, max(sc.n, 1), device=DEV)
+    for k, c in enumerate(cams):
+        B.gs_grad_aggregate(ref.gaussians(), bt.proj[k].abi(), bt.bins[k].abi(), c, rp, g2, ref.param_grads())
+        acc = acc + ref.grad * (1.0 / views)
+    ref.grad.copy_(acc)
+    lr_dict = {nm: getattr(bt.lrs, nm) for nm in PL.DEFAULT_LR}
+    B.gs_adam_step(ref.adam_groups(lr_dict), 1, bt.beta1, bt.beta2, bt.eps)
+    ref_proj = [PL.Projection(sc.n, DEV) for _ in nxt]
+    B.gs_project_batch(ref.gaussians(), nxt, rp, [p.abi() for p in ref_proj])
+    # the batched pass
+    bt.update(cams, nxt)
+    torch.cuda.synchronize()
+    assert torch.equal(bt.params.data, ref.data)
+    assert torch.equal(bt.params.m, ref.m) and torch.equal(bt.params.v, ref.v)
+    assert not torch.equal(bt.params.data, p0)
+    for a, b in zip(bt.proj, ref_proj):
+        for x, y in zip(_proj_fields(a), _proj_fields(b)):
+            assert torch.equal(x, y)
+
+
+def test_batch_of_one_equals_single_view_pass():
+    """A batch of one view with grad_scale 1 is gs_grad_aggregate_adam_project."""
+    sc = _scene("ragged_sh2")
+    rp = B.make_params(sc.sh_degree)
+    bt, cams = _batch_setup(sc, 1, rp)
+    nc = B.camera_from(_moved_camera(sc.cameras[0]))
+    st = gpu_forward(sc, sc.cameras[0], rp)
+    st.fused_l1(cams[0], sc.targets[0].to(DEV))
+    st.aggregate_adam_project(cams[0], nc)
+    bt.update(cams, [nc])
+    torch.cuda.synchronize()
+    assert torch.equal(bt.params.data, st.params.data) and torch.equal(bt.params.m, st.params.m)
+    for x, y in zip(_proj_fields(bt.proj[0]), _proj_fields(st.proj)):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh2"])
+def test_batch_gradient_matches_oracle(name):
+    """The batch gradient is the mean of the views' gradients (each the oracle's backward of
+    its own view): after one step from zero moments, m = (1 - beta1) g with the batch's
+    beta1, so g is read back from m and compared with the oracle's mean."""
+    views = 2
+    sc = _scene(name)
+    rp = B.make_params(sc.sh_degree)
+    op = oracle_params(rp)
+    cams = _views(sc.cameras[0], views)
+    params = PL.GaussianParams.from_scene(sc, DEV)
+    bt = PL.BatchTrainStep(params, cams[0].width, cams[0].height, views, DEV, raster=rp)
+    bc = [B.camera_from(c) for c in cams]
+    bt.project(bc)
+    g3_sum = None
+    for k, c in enumerate(cams):
+        bt.sort(k, bc[k])
+        P = oracle.project(sc, c, op)
+        col, tf, nt, tie = oracle.render(P, op)
+        G = _oracle_G(col, sc.targets[0].numpy())
+        f = bt.frame[k]
+        B.gs_raster_fwd(bt.proj[k].abi(), bt.bins[k].abi(), bc[k], rp, f.color, f.t_final, f.n_trav, f.n_trav_sum)
+        B.gs_raster_bwd_partials(params.gaussians(), bt.bins[k].abi(), bc[k], rp, f.color, f.t_final, f.n_trav,
+                                 torch.from_numpy(G).to(DEV), None)
+        g3 = oracle.project_backward(sc, c, oracle.raster_backward(P, G.astype(np.float64), None, op), op)
+        g3_sum = g3 if g3_sum is None else {nm: g3_sum[nm] + g3[nm] for nm in g3}
+    bt.update(bc)
+    torch.cuda.synchronize()
+    g_batch = bt.params.m.cpu().numpy().astype(np.float64) / (1.0 - bt.beta1)
+    for nm in ("means", "log_scales", "quats", "opacity_logits", "sh"):
+        got = params.view(torch.from_numpy(g_batch), nm).numpy()
+        want = g3_sum[nm] / views
+        e = rel_l2(got, want)
+        log(f"  {name} {nm}: batch gradient vs oracle mean rel-L2 {e:.2e}")
+        assert e <= 1e-3
+
+
 # ------------------------------------------------------------------ Adam
 
 @pytest.mark.parametrize("n,step", [(1, 1), (1001, 1), (4096, 7), (250_001, 3)])

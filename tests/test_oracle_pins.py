@@ -663,6 +663,25 @@ def test_decode_rejects_out_of_range_records():
     assert rej == 1 and np.array_equal(lo[:, :199], dense[:, 1:])
 
 
+def test_batch_hparams_follow_the_page():
+    """ROCm blog, "Batching and Hyperparameter Scaling": learning rates scale as sqrt(BS),
+    eps as 1/sqrt(BS), and the linearised beta1 of 0.9 reaches zero at BS = 10; BS = 1
+    changes nothing."""
+    lrs = [1.6e-4, 5e-3, 1e-3, 5e-2, 2.5e-3, 1.25e-4]
+    one = oracle.adam_batch_hparams(1, lrs)
+    assert one == (lrs, 0.9, 0.999, 1e-15)
+    lr4, b1, b2, e = oracle.adam_batch_hparams(4, lrs)
+    assert all(abs(a - 2.0 * b) <= 1e-18 for a, b in zip(lr4, lrs))    # sqrt(4) = 2
+    assert abs(e - 0.5e-15) <= 1e-30
+    assert abs(b1 - 0.6) < 1e-12 and abs(b2 - 0.996) < 1e-12
+    lr9, _, _, e9 = oracle.adam_batch_hparams(9, lrs)
+    assert all(abs(a - 3.0 * b) <= 1e-18 for a, b in zip(lr9, lrs)) and abs(e9 - 1e-15 / 3) < 1e-30
+    _, b1_10, _, _ = oracle.adam_batch_hparams(10, lrs)
+    assert abs(b1_10) < 1e-12                                           # the page's degenerate limit
+    assert oracle.adam_batch_hparams(11, lrs) is None
+    assert oracle.adam_batch_hparams(0, lrs) is None
+
+
 # ------------------------------------------------------------------ golden values from the pages
 
 def test_golden_thresholds_fixture():
