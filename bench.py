@@ -212,6 +212,69 @@ def cpu_baseline(scene, rows):
                       f"compositing backward of {rows} rows x {W} px ({isect} intersections) in {dt:.1f} s"}
 
 
+def _band_worker(args):
+    """One process of the parallel oracle leg: compositing and compositing backward of a
+    band of rows (the projection is inherited from the parent)."""
+    import numpy as np
+    import oracle
+    ys, W = args
+    P, target = _PAR_STATE["P"], _PAR_STATE["target"]
+    ys = np.asarray(ys, dtype=np.int32)
+    pix = np.stack([np.tile(np.arange(W, dtype=np.int32), len(ys)), np.repeat(ys, W)], 1)
+    col, tf, nt, tie = oracle.render(P, pixels=pix)
+    _, G = oracle.loss_l1(col.astype(np.float32), target[ys].reshape(-1, 3))
+    oracle.raster_backward(P, G.reshape(-1, 3), None, pixels=pix)
+    return int(nt.sum())
+
+
+_PAR_STATE = {}
+
+
+def cpu_baseline_parallel(scene, rows):
+    """The same per-pixel work as cpu_baseline (compositing and its backward of `rows`
+    rows of view 0), the rows dealt round-robin to P forked processes (P = the CPU share,
+    at most 16), the projection done once beforehand and not timed.  Runs before the GPU
+    is used."""
+    import multiprocessing as mp
+    import oracle
+    cam = scene.cameras[0]
+    procs = max(1, min(16, len(os.sched_getaffinity(0))))
+    _PAR_STATE["P"] = oracle.project(scene, cam)
+    _PAR_STATE["target"] = scene.targets[0].numpy()
+    y0 = (cam.height - rows) // 2
+    bands = [(list(range(y0 + b, y0 + rows, procs)), cam.width) for b in range(min(procs, rows))]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(bands)) as pool:
+        isect = sum(pool.map(_band_worker, bands))
+    dt = time.perf_counter() - t0
+    _PAR_STATE.clear()
+    return {"value": isect / dt, "unit": "Gaussian-pixel intersections/s", "cores": len(bands), "kind": "oracle",
+            "sample": f"view 0: compositing and compositing backward of {rows} rows x {cam.width} px "
+                      f"({isect} intersections), rows dealt round-robin to {len(bands)} processes, in {dt:.2f} s "
+                      "(projection not timed)"}
+
+
+def device_info():
+    import torch
+    info = {"name": torch.cuda.get_device_name(0), "hip": getattr(torch.version, "hip", None)}
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        info["compute_units"] = pr.multi_processor_count
+        info["arch"] = getattr(pr, "gcnArchName", None)
+    except Exception:
+        pass
+    try:   # current shader clock from the driver's DPM table, where readable
+        import glob
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            cur = [ln for ln in open(f).read().splitlines() if ln.strip().endswith("*")]
+            if cur:
+                info["sclk"] = cur[0].split(":", 1)[1].strip(" *")
+                break
+    except Exception:
+        pass
+    return info
+
+
 class CallTimer:
     """Timing events around calls, summed by name after a synchronisation."""
 
@@ -489,6 +552,10 @@ def main():
 
     dev = "cuda"
     scene, desc = make_scene(args.workload)
+    # the parallel oracle leg forks, so it runs before anything touches the GPU
+    cpu_par = None
+    if not args.no_cpu_baseline:
+        cpu_par = cpu_baseline_parallel(scene, min(args.cpu_rows, scene.cameras[0].height))
     cams = [B.camera_from(c) for c in scene.cameras]
     targets = [t.to(dev) for t in scene.targets]
     nviews = len(cams)
@@ -687,9 +754,11 @@ def main():
                         "pass of the same steps with an event around every call",
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
+        "device_info": device_info(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, min(args.cpu_rows, H))
+        out["cpu_baseline_parallel"] = cpu_par
     print(json.dumps(out), flush=True)
 
 
