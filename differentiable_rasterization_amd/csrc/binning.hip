@@ -287,6 +287,9 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
                                                     const float4 *__restrict__ prec, float4 *__restrict__ qrec)
 {
     constexpr int kPadF4 = gsr::kRecPad * gsr::kRecF4;
+    // per wave: the records of one quadrant list, staged so that the wave writes them as
+    // one contiguous run of float4 (consecutive lanes, consecutive 16-byte words)
+    __shared__ float4 stage[4][64 * gsr::kRecF4];
     const int64_t kp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (kp < 2 * kPadF4) {
         // leading pad, then the pad after the last record (the scan's total)
@@ -297,25 +300,48 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
     const int64_t K = (int64_t)*klen;
     const int64_t blk = xcd_contiguous_block((K + 255) / 256);
     if (blk < 0) return;
+    const int lane = threadIdx.x & 63;
     const int64_t k = blk * 256 + threadIdx.x;
-    if (k >= K) return;
-    const uint32_t qm = tkeys[k] >> gsr::kMaskShift;
-    if (!qm) return;
-    const uint64_t tvk = tvals[k];
-    const uint32_t g = (uint32_t)tvk;
-    const float4 a = prec[gsr::kRecF4 * (size_t)g], b = prec[gsr::kRecF4 * (size_t)g + 1];
-    float4 c = prec[gsr::kRecF4 * (size_t)g + 2];
-    c.z = __uint_as_float((uint32_t)k);
-    uint32_t slot = (uint32_t)(tvk >> 32);
+    if (k - lane >= K) return;   // the whole wave lies past the lists
+    const uint32_t qm = k < K ? tkeys[k] >> gsr::kMaskShift : 0u;
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), b = a, c = a;
+    uint32_t slot = 0;
+    if (qm) {
+        const uint64_t tvk = tvals[k];
+        const uint32_t g = (uint32_t)tvk;
+        a = prec[gsr::kRecF4 * (size_t)g];
+        b = prec[gsr::kRecF4 * (size_t)g + 1];
+        c = prec[gsr::kRecF4 * (size_t)g + 2];
+        c.z = __uint_as_float((uint32_t)k);
+        slot = (uint32_t)(tvk >> 32);
+    }
+    float4 *st = stage[threadIdx.x >> 6];
+    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int q = 0; q < gsr::kQuads; ++q) {
-        if (!((qm >> q) & 1u)) continue;
-        const uint32_t pos = gsr::quad_prefix(bitmap + (int64_t)q * words, wpre + (int64_t)q * (words + 1), (uint32_t)k);
-        float4 *d = qrec + gsr::kRecF4 * (size_t)pos;
-        c.w = __uint_as_float(slot++);
-        d[0] = a;
-        d[1] = b;
-        d[2] = c;
+        const bool has = (qm >> q) & 1u;
+        const uint64_t bal = __ballot(has);
+        if (!bal) continue;
+        // the wave's entries are consecutive, so its records of list q are one run that
+        // starts where the first of them goes
+        const int first = __builtin_ctzll(bal);
+        uint32_t pos0 = 0;
+        if (lane == first) pos0 = gsr::quad_prefix(bitmap + (int64_t)q * words, wpre + (int64_t)q * (words + 1),
+                                                   (uint32_t)k);
+        pos0 = __shfl(pos0, first, 64);
+        if (has) {
+            const uint32_t r = (uint32_t)__popcll(bal & below);
+            float4 cc = c;
+            cc.w = __uint_as_float(slot++);
+            st[gsr::kRecF4 * r] = a;
+            st[gsr::kRecF4 * r + 1] = b;
+            st[gsr::kRecF4 * r + 2] = cc;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t n4 = gsr::kRecF4 * (uint32_t)__popcll(bal);
+        float4 *d = qrec + gsr::kRecF4 * (size_t)pos0;
+        for (uint32_t t = (uint32_t)lane; t < n4; t += 64u) d[t] = st[t];
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
