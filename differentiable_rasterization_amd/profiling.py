@@ -34,6 +34,7 @@ KERNEL_SOURCES = {
     "k_raster_fused_l1": ["raster_fused.hip", "raster_walk.h", "raster.h", "kernels.h", "common.h"],
     "k_adam": ["optim.hip", "kernels.h", "common.h"],
     "k_grad_adam": ["project.hip", "raster.h", "kernels.h", "common.h"],
+    "k_grad_adam_batch": ["project.hip", "raster.h", "kernels.h", "common.h"],
 }
 
 COPY_KERNEL = re.compile(r"vectorized_elementwise_kernel.*MulFunctor")
