@@ -136,6 +136,26 @@ __device__ __forceinline__ CoopEntry coop_round(Coop &S, uint32_t e0, uint32_t C
     return E;
 }
 
+// The counting half of coop_round: each entry adds its quadrant-record count to its
+// Gaussian's total (LDS atomics; the sum does not depend on their order, so no scan and no
+// barrier per round).  The caller synchronises before reading S.qacc.
+__device__ __forceinline__ void coop_count_round(Coop &S, uint32_t e0, uint32_t C, float log2_amin)
+{
+    const uint32_t e = e0 + (uint32_t)threadIdx.x;
+    if (e >= C) return;
+    int o = 0;
+#pragma unroll
+    for (int step = 128; step > 0; step >>= 1)
+        if (S.off[o + step] <= e) o += step;
+    const int4 R = S.rect[o];
+    const uint32_t local = e - S.off[o];
+    const uint32_t row = local / (uint32_t)R.z;
+    const int x = R.x + (int)(local - row * (uint32_t)R.z), y = R.y + (int)row;
+    const uint32_t qm =
+        gsr::quad_mask_rec(S.p0[o], S.p1[o], log2_amin, (float)(x * GS_TILE), (float)(y * GS_TILE));
+    if (qm) atomicAdd(&S.qacc[o], (uint32_t)__popc(qm));
+}
+
 // Depth keys (culled Gaussians last) in index order, with the values tile count << 32 |
 // index, each Gaussian's quadrant-record count (qcnt [n + 1], qcnt[n] = 0, so that its
 // exclusive scan ends with the total), optionally the tile counts for the caller
@@ -160,7 +180,8 @@ __global__ __launch_bounds__(256) void k_keys_count(const int2 *__restrict__ rad
     }
     uint32_t c;
     const uint32_t C = coop_load(S, vis, (uint32_t)i, rec, tx, ty, c);
-    for (uint32_t e0 = 0; e0 < C; e0 += 256u) coop_round(S, e0, C, log2_amin);
+    for (uint32_t e0 = 0; e0 < C; e0 += 256u) coop_count_round(S, e0, C, log2_amin);
+    __syncthreads();
     if (i < n) {
         vals[i] = ((uint64_t)c << 32) | (uint64_t)i;
         qcnt[i] = S.qacc[threadIdx.x];
