@@ -88,6 +88,8 @@ def parse():
                     help="separate gs_grad_aggregate, gs_project_bwd and gs_adam_step calls instead of the fused pass")
     ap.add_argument("--separate-raster", action="store_true",
                     help="gs_raster_fwd, gs_loss_l1 and gs_raster_bwd_partials instead of gs_raster_fused_l1")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the binning's kernels one by one instead of replaying its per-view HIP graph")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the untimed pass that times every call separately")
     ap.add_argument("--batch", type=int, default=1, help="views per optimiser step (BatchTrainStep for 2..4)")
@@ -579,6 +581,14 @@ def main():
         st.forward(c)
     st.bins._alloc(int(st.bins.capacity * 1.3) + 4096)
     torch.cuda.synchronize()
+    # the binning of each view as a HIP graph (about thirty launches replayed as one); each
+    # replay writes (K, required capacity or 0) to its view's counts and adds them to acc
+    view_counts = torch.zeros(nviews, 2, dtype=torch.int64, device=dev)
+    acc = torch.zeros(2, dtype=torch.int64, device=dev)
+    graphs = None
+    if not args.no_graph:
+        B.gs_project(params.gaussians(), cams[0], st.raster, st.proj.abi())
+        graphs = [PL.BinSortGraph(st.bins, st.proj, cams[v], st.raster, view_counts[v], acc) for v in range(nviews)]
 
     if args.unfused:
         names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
@@ -610,7 +620,9 @@ def main():
             B.gs_project(g, c, st.raster, st.proj.abi())
             k += 1
             rec(k)
-        if counts is None:
+        if graphs is not None:   # no host wait; acc collects the counts
+            graphs[i % nviews].replay()
+        elif counts is None:
             st.bins.sort(st.proj, c, st.raster)
         else:   # no host wait inside the step; the counts are checked after the timed steps
             st.bins.sort_async(st.proj, c, st.raster, counts)
@@ -660,6 +672,7 @@ def main():
     events = new_events()
     st.frame.n_trav_sum.zero_()
     counts = torch.zeros(args.steps, 2, dtype=torch.int64, device=dev)
+    acc.zero_()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -667,10 +680,16 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    cnt = counts.cpu()
-    if int(cnt[:, 1].max()) != 0:
-        raise RuntimeError(f"intersection lists overflowed during the timed steps (need {int(cnt[:, 1].max())})")
-    k_isect = [int(k) for k in cnt[:, 0]]
+    if graphs is not None:
+        k_sum, need = (int(x) for x in acc.cpu())
+        if need != 0:
+            raise RuntimeError("intersection lists overflowed during the timed steps")
+        k_isect = [k_sum / args.steps]
+    else:
+        cnt = counts.cpu()
+        if int(cnt[:, 1].max()) != 0:
+            raise RuntimeError(f"intersection lists overflowed during the timed steps (need {int(cnt[:, 1].max())})")
+        k_isect = [int(k) for k in cnt[:, 0]]
     # quadrant records of the last sort (the list header: entries, then quadrant records)
     q_last = int(st.bins.raster[:16].view(torch.int64)[1].item())
     isect_total = int(st.frame.n_trav_sum.item())
@@ -745,7 +764,8 @@ def main():
                    "views": nviews,
                    "step": "one view: projection + fwd + L1 + bwd + Adam" + (
                        "" if args.unfused else " (each view's projection fused into the previous step's Adam pass"
-                       + ("" if args.separate_raster else "; fwd + L1 + bwd in one kernel") + ")")},
+                       + ("" if args.separate_raster else "; fwd + L1 + bwd in one kernel") + ")"),
+                   "binning_launch": "eager" if args.no_graph else "HIP graph per view"},
         "roofline": roof,
         "roofline_next": roof_next,
         # from the untimed pass with an event around every call

@@ -134,6 +134,40 @@ class Binning:
         B.gs_bin_sort_async(proj.abi(), self.n, cam, params, self.abi(), counts, self.workspace, stream)
 
 
+class BinSortGraph:
+    """gs_bin_sort_async for one camera, captured once as a HIP graph and replayed.
+
+    The sort is about thirty small kernel launches; on a slow host their launch cost
+    exceeds their GPU time and the step waits for the host.  A replay is one launch.
+    The graph holds the buffers' addresses and the camera: it stays valid while bins,
+    proj and counts keep their storage (Binning._alloc replaces it).  Every kernel of
+    the sort clears what it needs with its own stores (no memset nodes).  With acc
+    (device int64[2]), each replay also adds counts to it (entries, required capacity):
+    acc[1] != 0 after a run means some sort overflowed."""
+
+    def __init__(self, bins: Binning, proj: Projection, cam: B.Camera, params: B.RasterParams, counts,
+                 acc=None):
+        self.bins, self.counts = bins, counts
+        self._storage = (bins.ids.data_ptr(), bins.workspace.data_ptr(), bins.raster.data_ptr())
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # one eager run first, off the capture
+            bins.sort_async(proj, cam, params, counts)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            bins.sort_async(proj, cam, params, counts)
+            if acc is not None:
+                acc.add_(counts)
+
+    def replay(self):
+        b = self.bins
+        if (b.ids.data_ptr(), b.workspace.data_ptr(), b.raster.data_ptr()) != self._storage:
+            raise RuntimeError("the binning buffers were reallocated after the graph was captured")
+        self.graph.replay()
+
+
 class Frame:
     """Per-image buffers: render, transmittance, traversal counts, loss gradient."""
 

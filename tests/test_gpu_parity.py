@@ -832,6 +832,54 @@ def test_fused_l1_then_fused_adam_projection_matches_separate_step():
         assert torch.equal(a, b)
 
 
+def test_bin_sort_graph_replays_match_eager():
+    """The binning captured as one HIP graph per view and replayed, with eager
+    rasterization and host synchronisations between the replays, gives the eager sort's
+    lists, counts and rendered images bit for bit on every replay."""
+    log("bin sort graph replays")
+    sc = _scene("ragged_sh2")
+    cams = [B.camera_from(c) for c in (sc.cameras[0], _moved_camera(sc.cameras[0]))]
+    rp = B.make_params(sc.sh_degree)
+    tgt = sc.targets[0].to(DEV)
+    st = gpu_forward(sc, sc.cameras[0], rp)
+    st.bins._alloc(int(st.bins.capacity * 1.5) + 1024)
+    projs = [st.proj, PL.Projection(sc.n, DEV)]
+    B.gs_project(st.params.gaussians(), cams[1], rp, projs[1].abi())
+    f = st.frame
+
+    def outputs(v):
+        k = int(st.bins.raster[:16].view(torch.int64)[0])
+        return [st.bins.ids[:k].clone(), st.bins.tile_ranges.clone(), f.color.clone(), f.t_final.clone(),
+                f.n_trav.clone(), f.loss.clone()]
+
+    want, ks = [], []
+    for v in range(2):
+        n = torch.zeros(2, dtype=torch.int64, device=DEV)
+        st.bins.sort_async(projs[v], cams[v], rp, n)
+        st.fused_l1(cams[v], tgt)
+        torch.cuda.synchronize()
+        assert int(n[1]) == 0 and int(n[0]) > 0
+        ks.append(int(n[0]))
+        want.append(outputs(v))
+    assert not torch.equal(want[0][2], want[1][2])
+    counts = torch.full((2, 2), -1, dtype=torch.int64, device=DEV)
+    acc = torch.zeros(2, dtype=torch.int64, device=DEV)
+    graphs = [PL.BinSortGraph(st.bins, projs[v], cams[v], rp, counts[v], acc) for v in range(2)]
+    acc.zero_()
+    replays = 0
+    for rnd in range(3):
+        for v in (1, 0) if rnd % 2 else (0, 1):
+            counts[v].fill_(-1)
+            graphs[v].replay()
+            st.fused_l1(cams[v], tgt)
+            torch.cuda.synchronize()
+            replays += 1
+            assert counts[v].tolist() == [ks[v], 0]
+            for a, b in zip(outputs(v), want[v]):
+                assert torch.equal(a, b), f"replay {replays} of view {v} differs from the eager sort"
+    assert acc.tolist() == [3 * (ks[0] + ks[1]), 0]
+
+
 def test_tile_budget_report():
     """ByteSplat Eq. 8 and Eq. 9 per tile against numpy on the tile lists of a sorted scene."""
     sc = _scene("100k")
