@@ -134,6 +134,19 @@ __device__ __forceinline__ int64_t elem_count(int64_t m, const unsigned long lon
     return m_dev ? (int64_t)min((unsigned long long)m, *m_dev) : m;
 }
 
+// The radix tile a block takes.  Blocks reach the 8 XCDs round-robin (block b on XCD
+// b % 8); the tiles that hold elements are renumbered so that each XCD takes one
+// contiguous run of them.  Neighbouring tiles write neighbouring words of the digit-major
+// histogram and neighbouring runs of each digit's output, so their partial cache lines
+// meet in one L2 instead of eight.  Tiles past the last element keep their own number.
+__device__ __forceinline__ int64_t rx_tile(int64_t m)
+{
+    const int64_t b = blockIdx.x, active = (m + kRxTile - 1) / kRxTile;
+    if (b >= active) return b;
+    const int64_t x = b % gsi::kXcds, per = active / gsi::kXcds, rem = active % gsi::kXcds;
+    return x * per + (x < rem ? x : rem) + b / gsi::kXcds;
+}
+
 __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restrict__ keys, int64_t m_max,
                                                          const unsigned long long *__restrict__ m_dev, int shift,
                                                          uint32_t *__restrict__ hist, int64_t nb)
@@ -141,9 +154,10 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
     __shared__ uint32_t h[4][256];
     const int64_t m = elem_count(m_max, m_dev);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t tile = rx_tile(m);
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&h[0][0])[i] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kRxTile + (int64_t)w * kRxWaveSpan + lane;
+    const int64_t base = tile * kRxTile + (int64_t)w * kRxWaveSpan + lane;
     // Consecutive lanes hold consecutive elements.  Each run of equal digits across the
     // lanes is counted by its first lane with one LDS add of the run length, so skewed or
     // presorted keys (long runs of one digit) do not serialise on one LDS address.
@@ -163,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
     }
     __syncthreads();
     const int d = threadIdx.x;
-    hist[(int64_t)d * nb + blockIdx.x] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+    hist[(int64_t)d * nb + tile] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
 }
 
 template <typename V>
@@ -180,9 +194,10 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
     __shared__ uint32_t skey[kRxTile];
     __shared__ V sval[kRxTile];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t tile = rx_tile(m), tile0 = tile * kRxTile;
+    if (tile0 >= m) return;   // the whole block: nothing to place
     for (int i = threadIdx.x; i < 4 * 256; i += kThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
-    const int64_t tile0 = (int64_t)blockIdx.x * kRxTile;
     const int64_t base = tile0 + (int64_t)w * kRxWaveSpan + lane;
     const uint64_t below_mask = (1ull << lane) - 1ull;
     uint32_t key[kRxItems], rank[kRxItems];
@@ -221,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
         wcnt[3][d] = c0 + c1 + c2;
         uint32_t tot;
         bstart[d] = block_exclusive_scan(c0 + c1 + c2 + c3, scratch, &tot);
-        gbase[d] = offs[(int64_t)d * nb + blockIdx.x];
+        gbase[d] = offs[(int64_t)d * nb + tile];
     }
     __syncthreads();
 #pragma unroll
