@@ -338,18 +338,26 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
     }
     float4 *st = stage[threadIdx.x >> 6];
     const uint64_t below = (1ull << lane) - 1ull;
+    // The wave's entries are consecutive, so its records of list q are one run that starts
+    // where the first of them goes.  Lane q looks that position up for list q: four
+    // independent lookups instead of a chain of four.
+    static_assert(gsr::kQuads == 4, "one lookup lane per quadrant");
+    uint64_t bals[gsr::kQuads];
+#pragma unroll
+    for (int q = 0; q < gsr::kQuads; ++q) bals[q] = __ballot((qm >> q) & 1u);
+    uint32_t start = 0;
+    {
+        const uint64_t mine = lane == 0 ? bals[0] : lane == 1 ? bals[1] : lane == 2 ? bals[2] : bals[3];
+        if (lane < gsr::kQuads && mine)
+            start = gsr::quad_prefix(bitmap + (int64_t)lane * words, wpre + (int64_t)lane * (words + 1),
+                                     (uint32_t)(k - lane + __builtin_ctzll(mine)));
+    }
 #pragma unroll
     for (int q = 0; q < gsr::kQuads; ++q) {
         const bool has = (qm >> q) & 1u;
-        const uint64_t bal = __ballot(has);
+        const uint64_t bal = bals[q];
         if (!bal) continue;
-        // the wave's entries are consecutive, so its records of list q are one run that
-        // starts where the first of them goes
-        const int first = __builtin_ctzll(bal);
-        uint32_t pos0 = 0;
-        if (lane == first) pos0 = gsr::quad_prefix(bitmap + (int64_t)q * words, wpre + (int64_t)q * (words + 1),
-                                                   (uint32_t)k);
-        pos0 = __shfl(pos0, first, 64);
+        const uint32_t pos0 = __shfl(start, q, 64);
         if (has) {
             const uint32_t r = (uint32_t)__popcll(bal & below);
             float4 cc = c;
