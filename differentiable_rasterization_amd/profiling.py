@@ -4,6 +4,8 @@
     python -m differentiable_rasterization_amd.profiling traffic --fetch <fetch counter csv>
         --write <write counter csv> --kernel k_raster_bwd --copy-bytes <bytes read by the copy kernel>
     python -m differentiable_rasterization_amd.profiling counters <counter csv> [kernel ...]
+    python -m differentiable_rasterization_amd.profiling rates --fetch <fetch counter csv>
+        --write <write counter csv> --stats <run_kernel_stats.csv> --copy-bytes <bytes> [kernel ...]
 
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch, as rocprofv3 reports them)
 into HBM bytes per launch of one kernel.  Each counter is first divided by what it
@@ -107,6 +109,37 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> str
     return "\n".join(lines)
 
 
+def rates(fetch_csv: str, write_csv: str, stats_csv: str, copy_bytes: int, kernels) -> str:
+    """Copy-normalised HBM bytes per dispatch of every kernel (or those matching the
+    patterns), with its mean duration from a kernel-trace run of the same command: the
+    achieved rate is counted bytes over time, all dispatches of a kernel together."""
+    fm, fc = counter_means(fetch_csv)
+    wm, _ = counter_means(write_csv)
+    f_copy = sum(fm[k]["FETCH_SIZE"] for k in _find(fm, COPY_KERNEL.pattern)) / len(_find(fm, COPY_KERNEL.pattern))
+    w_copy = sum(wm[k]["WRITE_SIZE"] for k in _find(wm, COPY_KERNEL.pattern)) / len(_find(wm, COPY_KERNEL.pattern))
+    f_copy *= 1024.0 / copy_bytes
+    w_copy *= 1024.0 / copy_bytes
+    dur = {short_name(r["Name"]): (int(r["Calls"]), float(r["AverageNs"])) for r in _rows(stats_csv)}
+    wsum = collections.defaultdict(list)
+    for k, c in wm.items():
+        wsum[short_name(k)].append(c["WRITE_SIZE"])
+    lines = [f"copy kernel: FETCH_SIZE reads {f_copy:.4f} x and WRITE_SIZE {w_copy:.4f} x the bytes it moves "
+             f"({copy_bytes} B each way)",
+             f"{'kernel':40s} {'dispatches':>10s} {'read_MB':>10s} {'write_MB':>10s} {'avg_us':>9s} {'GB/s':>8s}"]
+    for k in sorted(fm, key=lambda x: -fm[x]["FETCH_SIZE"]):
+        name = short_name(k)
+        if name not in dur or COPY_KERNEL.search(k):
+            continue
+        if kernels and not any(re.search(p, name) for p in kernels):
+            continue
+        rd = fm[k]["FETCH_SIZE"] * 1024.0 / f_copy
+        wr = sum(wsum[name]) / len(wsum[name]) * 1024.0 / w_copy if wsum.get(name) else 0.0
+        calls, avg_ns = dur[name]
+        lines.append(f"{name[:40]:40s} {fc[k]:10d} {rd / 1e6:10.1f} {wr / 1e6:10.1f} {avg_ns / 1e3:9.2f} "
+                     f"{(rd + wr) / avg_ns:8.1f}")
+    return "\n".join(lines)
+
+
 def counters(path: str, kernels) -> str:
     means, counts = counter_means(path)
     out = []
@@ -154,6 +187,12 @@ def main(argv=None):
     b.add_argument("--write", required=True)
     b.add_argument("--kernel", required=True)
     b.add_argument("--copy-bytes", type=int, required=True)
+    r = sub.add_parser("rates")
+    r.add_argument("--fetch", required=True)
+    r.add_argument("--write", required=True)
+    r.add_argument("--stats", required=True)
+    r.add_argument("--copy-bytes", type=int, required=True)
+    r.add_argument("kernels", nargs="*")
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("kernels", nargs="*")
@@ -162,6 +201,8 @@ def main(argv=None):
         print(stats(args.csv))
     elif args.cmd == "traffic":
         print(traffic(args.fetch, args.write, args.kernel, args.copy_bytes))
+    elif args.cmd == "rates":
+        print(rates(args.fetch, args.write, args.stats, args.copy_bytes, args.kernels))
     else:
         print(counters(args.csv, args.kernels))
 
