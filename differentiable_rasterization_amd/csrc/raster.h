@@ -185,16 +185,15 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
     const uint32_t w0 = __shfl(s0, 0, 64), w1 = __shfl(s1, 63, 64);   // the wave's run of slots
 #pragma unroll
     for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
-    // the stamps of chunk c0 + 64 are loaded while the slot data of chunk c0 is in flight,
-    // so that a chunk waits for one memory round trip rather than two
+    // Two-stage pipeline over the chunks of 64 slots: the stamps run two chunks ahead and the
+    // slot data one chunk ahead, so the data of chunk c0 + 64 loads while chunk c0 is summed.
     uint2 tn = make_uint2(0u, 0u);
     if (w0 + (uint32_t)lane < w1) tn = qstamp[w0 + (uint32_t)lane];
-    for (uint32_t c0 = w0; c0 < w1; c0 += 64u) {
-        const uint32_t sl = c0 + (uint32_t)lane;
-        const uint2 t = tn;
-        // slots the latest backward call did not write: not read
-        const bool w = sl < w1 && t.x == epoch && t.y == ~epoch;
-        float4 d0, d1, d2;
+    bool w;   // this lane's slot of the chunk in d0..d2 was written by the latest backward call
+    float4 d0, d1, d2;
+    {
+        const uint32_t sl = w0 + (uint32_t)lane;
+        w = sl < w1 && tn.x == epoch && tn.y == ~epoch;   // unwritten slots are not read
         if (w) {
             const float4 *p = qgrad + (size_t)sl * (kGradSlot / 4);
             d0 = p[0];
@@ -202,12 +201,23 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
             d2 = p[2];
         }
         if (sl + 64u < w1) tn = qstamp[sl + 64u];
+    }
+    for (uint32_t c0 = w0; c0 < w1; c0 += 64u) {
         if (w) {
             S.d[0][lane] = d0;
             S.d[1][lane] = d1;
             S.d[2][lane] = d2;
         }
         S.ok[lane] = w ? 1u : 0u;
+        const uint32_t sn = c0 + 64u + (uint32_t)lane;
+        w = sn < w1 && tn.x == epoch && tn.y == ~epoch;
+        if (w) {
+            const float4 *p = qgrad + (size_t)sn * (kGradSlot / 4);
+            d0 = p[0];
+            d1 = p[1];
+            d2 = p[2];
+        }
+        if (sn + 64u < w1) tn = qstamp[sn + 64u];
         __builtin_amdgcn_wave_barrier();
         const uint32_t lo = s0 > c0 ? s0 : c0, hi = s1 < c0 + 64u ? s1 : c0 + 64u;
         for (uint32_t x = lo; x < hi; ++x) {
