@@ -405,25 +405,32 @@ constexpr int sh_chunk(int planes)
 }
 
 // Adam over the parameter scalars of one Gaussian, a chunk of planes at a time: every
-// moment load of a chunk is issued before any store, so the loads overlap.
+// moment load of a chunk is issued before any store, so the loads overlap, and the moments
+// of the next chunk are loaded before the current chunk is updated and stored, so that a
+// chunk's loads are in flight during the previous chunk's arithmetic and stores.
 struct AdamSink {
     float *p[5], *m[5], *v[5];   // means, log_scales, quats, opacity_logits, sh
     int64_t n;
     float st[6];                 // lr / (1 - b1^t): means, log_scales, quats, opacity, sh DC, sh rest
     float b1, b2, inv_bc2, eps;
 
-    // pv: the parameter values in, the updated values out
     template <int N>
-    __device__ void chunk(const int (&grp)[N], const int (&plane)[N], const float (&g)[N], float (&pv)[N],
-                          const float (&step)[N], int64_t i) const
+    __device__ void load_mv(const int (&grp)[N], const int (&plane)[N], int64_t i, float (&mv)[N],
+                            float (&vv)[N]) const
     {
-        float mv[N], vv[N];
 #pragma unroll
         for (int c = 0; c < N; ++c) {
             const int64_t idx = (int64_t)plane[c] * n + i;
             mv[c] = __builtin_nontemporal_load(m[grp[c]] + idx);
             vv[c] = __builtin_nontemporal_load(v[grp[c]] + idx);
         }
+    }
+
+    // pv: the parameter values in, the updated values out
+    template <int N>
+    __device__ void update(const int (&grp)[N], const int (&plane)[N], const float (&g)[N], float (&pv)[N],
+                           const float (&step)[N], float (&mv)[N], float (&vv)[N], int64_t i) const
+    {
 #pragma unroll
         for (int c = 0; c < N; ++c) {
             gsd::adam_update(pv[c], g[c], mv[c], vv[c], b1, b2, inv_bc2, eps, step[c]);
@@ -439,37 +446,61 @@ struct AdamSink {
     template <class Grad, int K>
     __device__ void flush(int64_t i, const Grad &g, Params1<K> &P) const
     {
-        {   // means, log_scales, quats, opacity: 11 scalars
-            const int grp[11] = {0, 0, 0, 1, 1, 1, 2, 2, 2, 2, 3};
-            const int pl[11] = {0, 1, 2, 0, 1, 2, 0, 1, 2, 3, 0};
+        constexpr int kChunk = sh_chunk(3 * K);
+        static_assert((3 * K) % kChunk == 0, "the chunks must tile the SH planes exactly");
+        // means, log_scales, quats, opacity: 11 scalars
+        const int grp[11] = {0, 0, 0, 1, 1, 1, 2, 2, 2, 2, 3};
+        const int pl[11] = {0, 1, 2, 0, 1, 2, 0, 1, 2, 3, 0};
+        float m11[11], v11[11];
+        load_mv(grp, pl, i, m11, v11);
+        int sgrp[kChunk], spl[kChunk];
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            sgrp[c] = 4;
+            spl[c] = c;
+        }
+        float msh[kChunk], vsh[kChunk];
+        load_mv(sgrp, spl, i, msh, vsh);   // the first SH chunk
+        {
             const float gg[11] = {g.means[0], g.means[1], g.means[2], g.ls[0], g.ls[1], g.ls[2],
                                   g.q[0], g.q[1], g.q[2], g.q[3], g.logit};
             float pv[11] = {P.means[0], P.means[1], P.means[2], P.ls[0], P.ls[1], P.ls[2],
                             P.q[0], P.q[1], P.q[2], P.q[3], P.logit};
             const float sp[11] = {st[0], st[0], st[0], st[1], st[1], st[1], st[2], st[2], st[2], st[2], st[3]};
-            chunk(grp, pl, gg, pv, sp, i);
+            update(grp, pl, gg, pv, sp, m11, v11, i);
             P.means[0] = pv[0]; P.means[1] = pv[1]; P.means[2] = pv[2];
             P.ls[0] = pv[3]; P.ls[1] = pv[4]; P.ls[2] = pv[5];
             P.q[0] = pv[6]; P.q[1] = pv[7]; P.q[2] = pv[8]; P.q[3] = pv[9];
             P.logit = pv[10];
         }
-        constexpr int kChunk = sh_chunk(3 * K);
-        static_assert((3 * K) % kChunk == 0, "the chunks must tile the SH planes exactly");
 #pragma unroll
         for (int c0 = 0; c0 < 3 * K; c0 += kChunk) {
-            int grp[kChunk], pl[kChunk];
+            float mnx[kChunk], vnx[kChunk];
+            if (c0 + kChunk < 3 * K) {   // the next chunk's moments
+                int npl[kChunk];
+#pragma unroll
+                for (int c = 0; c < kChunk; ++c) npl[c] = c0 + kChunk + c;
+                load_mv(sgrp, npl, i, mnx, vnx);
+            }
+            int cpl[kChunk];
             float gg[kChunk], pv[kChunk], sp[kChunk];
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) {
-                grp[c] = 4;
-                pl[c] = c0 + c;
+                cpl[c] = c0 + c;
                 gg[c] = g.sh(c0 + c);
                 pv[c] = P.sh[c0 + c];
                 sp[c] = c0 + c < 3 ? st[4] : st[5];
             }
-            chunk(grp, pl, gg, pv, sp, i);
+            update(sgrp, cpl, gg, pv, sp, msh, vsh, i);
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) P.sh[c0 + c] = pv[c];
+            if (c0 + kChunk < 3 * K) {
+#pragma unroll
+                for (int c = 0; c < kChunk; ++c) {
+                    msh[c] = mnx[c];
+                    vsh[c] = vnx[c];
+                }
+            }
         }
     }
 };
