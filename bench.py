@@ -88,8 +88,9 @@ def parse():
                     help="separate gs_grad_aggregate, gs_project_bwd and gs_adam_step calls instead of the fused pass")
     ap.add_argument("--separate-raster", action="store_true",
                     help="gs_raster_fwd, gs_loss_l1 and gs_raster_bwd_partials instead of gs_raster_fused_l1")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="launch the binning's kernels one by one instead of replaying its per-view HIP graph")
+    ap.add_argument("--binning-launch", choices=["auto", "graph", "eager"], default="auto",
+                    help="replay the binning's per-view HIP graph, launch its kernels one by one, or (auto) time a few "
+                         "untimed steps each way after the warm-up and keep the faster")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the untimed pass that times every call separately")
     ap.add_argument("--batch", type=int, default=1, help="views per optimiser step (BatchTrainStep for 2..4)")
@@ -278,6 +279,31 @@ def device_info():
     return info
 
 
+def choose_binning_launch(one_step, use_graph, step0, n, slots):
+    """Runs n untimed training steps with the binning replayed as graphs and n with its
+    kernels launched one by one, twice each, and keeps the faster way in use_graph[0].
+    Which is faster depends on the host: a graph replay costs the GPU a few microseconds
+    more, eager launches cost the host ~30 launches per binning.  The steps are ordinary
+    training steps (step0, step0 + 1, ...); eager steps queue the sort without a host wait.
+    Returns the wall ms per step of each run and the number of steps taken ("steps")."""
+    import torch
+    counts = torch.zeros(slots, 2, dtype=torch.int64, device="cuda")
+    per = {"graph": [], "eager": []}
+    i = step0
+    for _ in range(2):
+        for mode in ("graph", "eager"):
+            use_graph[0] = mode == "graph"
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(n):
+                one_step(i, counts=counts if slots > 1 else counts[0])
+                i += 1
+            torch.cuda.synchronize()
+            per[mode].append(round((time.perf_counter() - t) * 1e3 / n, 4))
+    use_graph[0] = min(per["graph"]) <= min(per["eager"])
+    return {**per, "steps": i - step0}
+
+
 class CallTimer:
     """Timing events around calls, summed by name after a synchronisation."""
 
@@ -455,17 +481,18 @@ def main_batch(args):
     # each (batch slot, view) pair's binning as a HIP graph; each replay adds its counts to acc
     acc = torch.zeros(2, dtype=torch.int64, device=dev)
     graphs = None
-    if not args.no_graph:
+    if args.binning_launch != "eager":
         pairs = sorted({(k, v) for i in range(nviews) for k, v in enumerate(views_of(i))})
         pair_counts = torch.zeros(len(pairs), 2, dtype=torch.int64, device=dev)
         graphs = {(k, v): PL.BinSortGraph(bt.bins[k], bt.proj[k], cams[v], bt.raster, pair_counts[j], acc)
                   for j, (k, v) in enumerate(pairs)}
+    use_graph = [graphs is not None]
 
     def one_step(i, ev=None, counts=None):
         vs, nv = views_of(i), views_of(i + 1)
         rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
         for k, v in enumerate(vs):
-            if graphs is not None:
+            if use_graph[0]:
                 graphs[(k, v)].replay()
             elif counts is None:
                 bt.sort(k, cams[v])
@@ -490,6 +517,11 @@ def main_batch(args):
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
+    step0 = args.warmup
+    launch_trials = None
+    if args.binning_launch == "auto":
+        launch_trials = choose_binning_launch(one_step, use_graph, step0, 4, bs)
+        step0 += launch_trials.pop("steps")
     for f in bt.frame:
         f.n_trav_sum.zero_()
     events = [[TimingEvent() for _ in range(2 * bs + 2)] for _ in range(args.steps)]
@@ -498,10 +530,10 @@ def main_batch(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(args.warmup + i, events[i], counts[i])
+        one_step(step0 + i, events[i], counts[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if graphs is not None:
+    if use_graph[0]:
         k_sum, need = (int(x) for x in acc.cpu())
         if need != 0:
             raise RuntimeError("intersection lists overflowed during the timed steps")
@@ -550,7 +582,8 @@ def main_batch(args):
         "ms_per_view": round(wall * 1e3 / (args.steps * bs), 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
-                   "views": nviews, "batch": bs, "binning_launch": "eager" if args.no_graph else "HIP graph per view",
+                   "views": nviews, "batch": bs, "binning_launch": "HIP graph per view" if use_graph[0] else "eager",
+                   "binning_launch_trials_ms_per_step": launch_trials,
                    "step": f"one optimiser step over {bs} views: per view binning + fwd + L1 + bwd; one pass of "
                            "gradient mean, Adam (batch hyper-parameters) and the next batch's projections"},
         "roofline": roof,
@@ -603,9 +636,10 @@ def main():
     view_counts = torch.zeros(nviews, 2, dtype=torch.int64, device=dev)
     acc = torch.zeros(2, dtype=torch.int64, device=dev)
     graphs = None
-    if not args.no_graph:
+    if args.binning_launch != "eager":
         B.gs_project(params.gaussians(), cams[0], st.raster, st.proj.abi())
         graphs = [PL.BinSortGraph(st.bins, st.proj, cams[v], st.raster, view_counts[v], acc) for v in range(nviews)]
+    use_graph = [graphs is not None]
 
     if args.unfused:
         names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
@@ -637,7 +671,7 @@ def main():
             B.gs_project(g, c, st.raster, st.proj.abi())
             k += 1
             rec(k)
-        if graphs is not None:   # no host wait; acc collects the counts
+        if use_graph[0]:   # no host wait; acc collects the counts
             graphs[i % nviews].replay()
         elif counts is None:
             st.bins.sort(st.proj, c, st.raster)
@@ -684,6 +718,11 @@ def main():
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
+    step0 = args.warmup
+    launch_trials = None
+    if args.binning_launch == "auto":
+        launch_trials = choose_binning_launch(one_step, use_graph, step0, max(2 * nviews, 4), 1)
+        step0 += launch_trials.pop("steps")
     new_events = lambda: [[TimingEvent() for _ in range(len(names) + 1)]
                           for _ in range(args.steps)]
     events = new_events()
@@ -693,11 +732,11 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(args.warmup + i, events[i], counts[i])
+        one_step(step0 + i, events[i], counts[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    if graphs is not None:
+    if use_graph[0]:
         k_sum, need = (int(x) for x in acc.cpu())
         if need != 0:
             raise RuntimeError("intersection lists overflowed during the timed steps")
@@ -715,10 +754,10 @@ def main():
     per_kernel, step_ms = dict(timed_ms), None
     if not args.no_breakdown:
         # untimed: the same steps again with an event around every call
-        project_for(args.warmup)
+        project_for(step0)
         ev2 = new_events()
         for i in range(args.steps):
-            one_step(args.warmup + i, ev2[i], counts[i], every_call=True)
+            one_step(step0 + i, ev2[i], counts[i], every_call=True)
         torch.cuda.synchronize()
         per_kernel = {names[j]: sum(ev2[s][j].elapsed_time(ev2[s][j + 1]) for s in range(args.steps)) / args.steps
                       for j in range(len(names))}
@@ -782,7 +821,8 @@ def main():
                    "step": "one view: projection + fwd + L1 + bwd + Adam" + (
                        "" if args.unfused else " (each view's projection fused into the previous step's Adam pass"
                        + ("" if args.separate_raster else "; fwd + L1 + bwd in one kernel") + ")"),
-                   "binning_launch": "eager" if args.no_graph else "HIP graph per view"},
+                   "binning_launch": "HIP graph per view" if use_graph[0] else "eager",
+                   "binning_launch_trials_ms_per_step": launch_trials},
         "roofline": roof,
         "roofline_next": roof_next,
         # from the untimed pass with an event around every call
