@@ -781,7 +781,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int v = 0; v < bg.views; ++v) {
         float acc[9];
         // every lane of the wave takes part in the slot sums
-        gsr::raw_slot_sums(bg.vb[v].hdr, bg.vb[v].qoff, bg.vb[v].qgrad, bg.vb[v].qstamp, i, n,
+        gsr::raw_slot_sums<2>(bg.vb[v].hdr, bg.vb[v].qoff, bg.vb[v].qgrad, bg.vb[v].qstamp, i, n,
                            stage[threadIdx.x >> 6], acc);
         if (live) {
             Proj P;

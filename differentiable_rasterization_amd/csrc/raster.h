@@ -173,6 +173,10 @@ struct SlotStage {
     uint32_t ok[64];   // slot c0 + l was written by the latest backward call
 };
 
+// U: slots summed per step of a lane's loop.  With U > 1 the LDS reads of U slots are
+// issued together and then added in slot order (the same sums); measured faster in the
+// batch pass (two waves per SIMD by attribute), slower in k_grad_adam at 10 M.
+template <int U = 1>
 __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
                                               const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp,
                                               int64_t g, int64_t n, SlotStage &S, float (&acc)[9])
@@ -220,13 +224,36 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
         if (sn + 64u < w1) tn = qstamp[sn + 64u];
         __builtin_amdgcn_wave_barrier();
         const uint32_t lo = s0 > c0 ? s0 : c0, hi = s1 < c0 + 64u ? s1 : c0 + 64u;
-        for (uint32_t x = lo; x < hi; ++x) {
-            const uint32_t l = x - c0;
-            if (S.ok[l]) {
-                const float4 a = S.d[0][l], b = S.d[1][l], c = S.d[2][l];
-                acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-                acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-                acc[8] += c.x;
+        if constexpr (U == 1) {
+            for (uint32_t x = lo; x < hi; ++x) {
+                const uint32_t l = x - c0;
+                if (S.ok[l]) {
+                    const float4 a = S.d[0][l], b = S.d[1][l], c = S.d[2][l];
+                    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+                    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+                    acc[8] += c.x;
+                }
+            }
+        } else {
+            for (uint32_t x = lo; x < hi; x += (uint32_t)U) {
+                float4 a[U], b[U], c[U];
+                bool take[U];
+#pragma unroll
+                for (int j = 0; j < U; ++j) {
+                    const uint32_t l = min(x - c0 + (uint32_t)j, 63u);
+                    take[j] = x + (uint32_t)j < hi && S.ok[l] != 0u;
+                    a[j] = S.d[0][l];
+                    b[j] = S.d[1][l];
+                    c[j] = S.d[2][l];
+                }
+#pragma unroll
+                for (int j = 0; j < U; ++j) {
+                    if (take[j]) {
+                        acc[0] += a[j].x; acc[1] += a[j].y; acc[2] += a[j].z; acc[3] += a[j].w;
+                        acc[4] += b[j].x; acc[5] += b[j].y; acc[6] += b[j].z; acc[7] += b[j].w;
+                        acc[8] += c[j].x;
+                    }
+                }
             }
         }
         __builtin_amdgcn_wave_barrier();
