@@ -878,6 +878,11 @@ def test_bin_sort_graph_replays_match_eager():
             for a, b in zip(outputs(v), want[v]):
                 assert torch.equal(a, b), f"replay {replays} of view {v} differs from the eager sort"
     assert acc.tolist() == [3 * (ks[0] + ks[1]), 0]
+    # the graphs hold the buffers' addresses: after the binning buffers are replaced, a replay
+    # is refused instead of writing into freed memory
+    st.bins._alloc(st.bins.capacity + 4096)
+    with pytest.raises(RuntimeError, match="reallocated"):
+        graphs[0].replay()
 
 
 def test_tile_budget_report():
