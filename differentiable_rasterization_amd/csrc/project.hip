@@ -1000,7 +1000,8 @@ gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, cons
     const CamD cd = make_cam(cam);
     const CamD nd = next_cam ? make_cam(next_cam) : cd;
     const ProjOut po = next_cam ? proj_out(next_proj) : ProjOut{};
-    const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+    // 128-thread blocks: at two waves per SIMD the last round of blocks is half as coarse
+    const dim3 grid((unsigned)ceil_div(n, 128)), block(128);
 #define GS_GA(D)                                                                                                   \
     do {                                                                                                           \
         if (next_cam)                                                                                              \
