@@ -47,6 +47,7 @@ WRITE_SIZE.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -94,6 +95,9 @@ def parse():
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the untimed pass that times every call separately")
     ap.add_argument("--batch", type=int, default=1, help="views per optimiser step (BatchTrainStep for 2..4)")
+    ap.add_argument("--serial-views", action="store_true",
+                    help="with --batch: bin and rasterize the views one after another on one stream instead of one "
+                         "stream per view")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a copy-like kernel over this many MiB before timing (counter normalisation)")
     return ap.parse_args()
@@ -488,19 +492,29 @@ def main_batch(args):
                   for j, (k, v) in enumerate(pairs)}
     use_graph = [graphs is not None]
 
+    vstreams = None if args.serial_views else PL.ViewStreams(bs)
+
     def one_step(i, ev=None, counts=None):
+        """Each view's binning and rasterization on its own stream (vstreams), the update on
+        the current stream after them; ev[2k], ev[2k + 1] bracket view k's rasterization on
+        the stream it runs on."""
         vs, nv = views_of(i), views_of(i + 1)
         rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        if vstreams is not None:
+            vstreams.fork()
         for k, v in enumerate(vs):
-            if use_graph[0]:
-                graphs[(k, v)].replay()
-            elif counts is None:
-                bt.sort(k, cams[v])
-            else:
-                bt.bins[k].sort_async(bt.proj[k], cams[v], bt.raster, counts[k])
-            rec(2 * k)
-            bt.render(k, cams[v], targets[v])
-            rec(2 * k + 1)
+            with (torch.cuda.stream(vstreams.streams[k]) if vstreams is not None else contextlib.nullcontext()):
+                if use_graph[0]:
+                    graphs[(k, v)].replay()
+                elif counts is None:
+                    bt.sort(k, cams[v])
+                else:
+                    bt.bins[k].sort_async(bt.proj[k], cams[v], bt.raster, counts[k])
+                rec(2 * k)
+                bt.render(k, cams[v], targets[v])
+                rec(2 * k + 1)
+        if vstreams is not None:
+            vstreams.join()
         rec(2 * bs)
         bt.update([cams[v] for v in vs], [cams[v] for v in nv])
         rec(2 * bs + 1)
@@ -552,11 +566,18 @@ def main_batch(args):
     n_vis = int((bt.proj[0].radii[:, 0] > 0).sum().item())
     by = 36 * k_mean * bs + n * (11 + 3 * scene.k_sh) * 24 + bs * (n_vis * 96 + (n - n_vis) * 12)
     fl = FLOP_PER_PAIR["raster_fused"] * isect_view
+    if vstreams is None:
+        raster_entry = {"ms": round(raster_ms, 4), "bound": "alu", "algorithmic_flop": int(fl),
+                        "achieved_TFLOPs": round(fl / (raster_ms * 1e-3) / 1e12, 3),
+                        "frac": round(fl / (raster_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
+                        "note": "per view"}
+    else:   # the views overlap: the window on a view's stream is not the kernel's duration
+        raster_entry = {"window_ms": round(raster_ms, 4), "bound": "alu", "algorithmic_flop": int(fl),
+                        "note": "per view; window between events on the view's stream while the other views' "
+                                "binning and rasterization run beside it (not a kernel duration; --serial-views "
+                                "times the kernel alone)"}
     kernels = {
-        "raster_fused": {"ms": round(raster_ms, 4), "bound": "alu", "algorithmic_flop": int(fl),
-                         "achieved_TFLOPs": round(fl / (raster_ms * 1e-3) / 1e12, 3),
-                         "frac": round(fl / (raster_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
-                         "note": "per view"},
+        "raster_fused": raster_entry,
         "grad_adam_batch": {"ms": round(update_ms, 4), "bound": "hbm", "algorithmic_bytes": int(by),
                             "achieved_GBs": round(by / (update_ms * 1e-3) / 1e9, 1),
                             "frac": round(by / (update_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -564,7 +585,7 @@ def main_batch(args):
     }
     from differentiable_rasterization_amd.profiling import read_stored_traffic
     stored = lambda k: read_stored_traffic(TRAFFIC_SUMMARY[k], k) if args.workload == "1m" else None
-    if update_ms > raster_ms:
+    if update_ms > raster_ms or vstreams is not None:
         d = kernels["grad_adam_batch"]
         roof = {"kernel": "k_grad_adam_batch", "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": d["frac"], "traffic": stored("k_grad_adam_batch"),
@@ -584,6 +605,7 @@ def main_batch(args):
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
                    "views": nviews, "batch": bs, "binning_launch": "HIP graph per view" if use_graph[0] else "eager",
                    "binning_launch_trials_ms_per_step": launch_trials,
+                   "views_on": "one stream each" if vstreams is not None else "one stream",
                    "step": f"one optimiser step over {bs} views: per view binning + fwd + L1 + bwd; one pass of "
                            "gradient mean, Adam (batch hyper-parameters) and the next batch's projections"},
         "roofline": roof,

@@ -271,6 +271,28 @@ class TrainStep:
         self.adam(stream)
 
 
+class ViewStreams:
+    """One stream per view of a batch.  fork() makes each stream wait for everything queued
+    on the caller's stream so far; join() makes the caller's stream wait for all of them.
+    The views' binning and rasterization are independent (each has its own bins, frame and
+    gradient slots; the parameters are only read), and a binning is a chain of small
+    kernels that leaves most of the GPU idle, so the views' chains run side by side.  The
+    streams keep the default priority."""
+
+    def __init__(self, views):
+        self.streams = [torch.cuda.Stream() for _ in range(views)]
+
+    def fork(self):
+        main = torch.cuda.current_stream()
+        for s in self.streams:
+            s.wait_stream(main)
+
+    def join(self):
+        main = torch.cuda.current_stream()
+        for s in self.streams:
+            main.wait_stream(s)
+
+
 class BatchTrainStep:
     """One optimiser step over a batch of views (ROCm blog, "Batching and Hyperparameter
     Scaling": several camera views per step, learning rates times sqrt(BS), eps / sqrt(BS),
@@ -315,13 +337,24 @@ class BatchTrainStep:
                                        1.0 / self.views, m, v, self.lrs, self.params.step_count, self.beta1,
                                        self.beta2, self.eps, next_cams, nxt, stream)
 
-    def step(self, cams, targets, next_cams=None, stream=None):
+    def step(self, cams, targets, next_cams=None, view_streams: ViewStreams | None = None):
         """The batch's projections must be in self.proj (project(), or the previous step's
-        update with next_cams)."""
+        update with next_cams).  With view_streams, each view is binned and rasterized on
+        its own stream (on the current stream otherwise); the update runs on the current
+        stream after all of them."""
+        if view_streams is not None:
+            view_streams.fork()
         for k in range(self.views):
-            self.sort(k, cams[k], stream)
-            self.render(k, cams[k], targets[k], stream)
-        self.update(cams, next_cams, stream)
+            if view_streams is not None:
+                with torch.cuda.stream(view_streams.streams[k]):
+                    self.sort(k, cams[k])
+                    self.render(k, cams[k], targets[k])
+            else:
+                self.sort(k, cams[k])
+                self.render(k, cams[k], targets[k])
+        if view_streams is not None:
+            view_streams.join()
+        self.update(cams, next_cams)
 
 
 class PartitionedStep:

@@ -470,6 +470,32 @@ def test_batch_end_of_step_matches_separate_calls(name, views):
             assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("name", ["ragged_sh2", "100k"])
+def test_batch_step_on_view_streams_matches_one_stream(name):
+    """BatchTrainStep.step with each view binned and rasterized on its own stream gives, over
+    three steps, the parameters, moments, images and losses of the same steps on one stream,
+    bit for bit."""
+    log(f"batch step on view streams {name}")
+    sc = _scene(name)
+    rp = B.make_params(sc.sh_degree)
+    views = 4
+    cams = [B.camera_from(c) for c in _views(sc.cameras[0], views)]
+    tgt = sc.targets[0].to(DEV)
+    out = []
+    for concurrent in (False, True):
+        bt, _ = _batch_setup(sc, views, rp)   # sized bins; projections for cams
+        for b in bt.bins:
+            b._alloc(int(b.capacity * 1.5) + 1024)
+        vs = PL.ViewStreams(views) if concurrent else None
+        for _ in range(3):
+            bt.step(cams, [tgt] * views, next_cams=cams, view_streams=vs)
+        torch.cuda.synchronize()
+        out.append([bt.params.data.clone(), bt.params.m.clone(), bt.params.v.clone()]
+                   + [f.color.clone() for f in bt.frame] + [f.loss.clone() for f in bt.frame])
+    for a, b in zip(*out):
+        assert torch.equal(a, b)
+
+
 def test_batch_of_one_equals_single_view_pass():
     """A batch of one view with grad_scale 1 is gs_grad_aggregate_adam_project."""
     sc = _scene("ragged_sh2")
