@@ -268,12 +268,15 @@ __device__ __forceinline__ void load_params(const float *__restrict__ means, con
                                             const float *__restrict__ quats, const float *__restrict__ logits,
                                             const float *__restrict__ sh, int64_t n, int64_t i, Params1<K> &prm)
 {
-    prm.means[0] = means[i]; prm.means[1] = means[n + i]; prm.means[2] = means[2 * n + i];
-    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[n + i]; prm.ls[2] = log_scales[2 * n + i];
-    prm.q[0] = quats[i]; prm.q[1] = quats[n + i]; prm.q[2] = quats[2 * n + i]; prm.q[3] = quats[3 * n + i];
-    prm.logit = logits[i];
+    // streamed once per pass: non-temporal loads
+    const auto ld = [](const float *p) { return __builtin_nontemporal_load(p); };
+    prm.means[0] = ld(means + i); prm.means[1] = ld(means + n + i); prm.means[2] = ld(means + 2 * n + i);
+    prm.ls[0] = ld(log_scales + i); prm.ls[1] = ld(log_scales + n + i); prm.ls[2] = ld(log_scales + 2 * n + i);
+    prm.q[0] = ld(quats + i); prm.q[1] = ld(quats + n + i); prm.q[2] = ld(quats + 2 * n + i);
+    prm.q[3] = ld(quats + 3 * n + i);
+    prm.logit = ld(logits + i);
 #pragma unroll
-    for (int k = 0; k < 3 * K; ++k) prm.sh[k] = sh[(int64_t)k * n + i];
+    for (int k = 0; k < 3 * K; ++k) prm.sh[k] = ld(sh + (int64_t)k * n + i);
 }
 
 template <int K>
