@@ -12,6 +12,7 @@
 // The geometric chain runs in double (it is memory bound, so this costs no time on
 // MI355X) and is rounded once to the float32 record.  SH evaluation runs in float.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -263,13 +264,15 @@ struct Params1 {   // one Gaussian's parameters as loaded
     float means[3], ls[3], q[4], logit, sh[3 * K];
 };
 
-template <int K>
+// NT: non-temporal loads.  Measured faster in the end-of-step passes (whose parameter
+// stores are non-temporal too) and slower in the standalone projection and projection
+// backward, which keep ordinary loads.
+template <bool NT, int K>
 __device__ __forceinline__ void load_params(const float *__restrict__ means, const float *__restrict__ log_scales,
                                             const float *__restrict__ quats, const float *__restrict__ logits,
                                             const float *__restrict__ sh, int64_t n, int64_t i, Params1<K> &prm)
 {
-    // streamed once per pass: non-temporal loads
-    const auto ld = [](const float *p) { return __builtin_nontemporal_load(p); };
+    const auto ld = [](const float *p) { return NT ? __builtin_nontemporal_load(p) : *p; };
     prm.means[0] = ld(means + i); prm.means[1] = ld(means + n + i); prm.means[2] = ld(means + 2 * n + i);
     prm.ls[0] = ld(log_scales + i); prm.ls[1] = ld(log_scales + n + i); prm.ls[2] = ld(log_scales + 2 * n + i);
     prm.q[0] = ld(quats + i); prm.q[1] = ld(quats + n + i); prm.q[2] = ld(quats + 2 * n + i);
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     Params1<K> prm;
-    load_params(means, log_scales, quats, logits, sh, n, i, prm);
+    load_params<false>(means, log_scales, quats, logits, sh, n, i, prm);
     project_store<DEG>(prm, cam, alpha_min, depth_lo, depth_hi, i, po);
 }
 
@@ -626,7 +629,7 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     Params1<K> prm;
-    load_params(means, log_scales, quats, logits, sh, n, i, prm);
+    load_params<std::is_same<Sink, AdamSink>::value>(means, log_scales, quats, logits, sh, n, i, prm);
     const bool shf = sh_finite(prm);
     Proj P;
     const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
@@ -745,7 +748,7 @@ __global__ __launch_bounds__(256) void k_project_batch(const float *__restrict__
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     Params1<K> prm;
-    load_params(means, log_scales, quats, logits, sh, n, i, prm);
+    load_params<false>(means, log_scales, quats, logits, sh, n, i, prm);
     ProjScalars S;
     params_scalars(prm, alpha_min, S);
     for (int v = 0; v < bp.views; ++v) project_store_s<DEG>(prm, S, bp.cam[v], depth_lo, depth_hi, i, bp.out[v]);
@@ -770,7 +773,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     ProjScalars PS;
     PS.ok = false;
     if (live) {
-        load_params(means, log_scales, quats, logits, sh, n, i, prm);
+        load_params<true>(means, log_scales, quats, logits, sh, n, i, prm);
         params_scalars(prm, alpha_min, PS);
     }
     GradSum<K> S;
