@@ -79,6 +79,87 @@ def test_isotropic_gaussian_closed_form(round_record, tol):
     assert (alpha == 0).sum() > 100 and (alpha > 0).sum() > 20
 
 
+# ------------------------------------------------------------------ footprint radius (S12)
+
+def _boundary_half_extents(sig2d, thr, samples=2_000_001):
+    """Half-extents in x and y of the ellipse {d : d^T Sigma2D^-1 d <= thr}, by brute force
+    over its boundary: the points sqrt(thr) L (cos t, sin t) with Sigma2D = L L^T, on a fine
+    grid of angles (no closed form of the extent is used)."""
+    L = np.linalg.cholesky(sig2d)
+    t = np.linspace(0.0, 2.0 * math.pi, samples)
+    pts = math.sqrt(thr) * (L @ np.stack([np.cos(t), np.sin(t)]))
+    return float(np.abs(pts[0]).max()), float(np.abs(pts[1]).max())
+
+
+def _ewa_sigma2d(mu, s, q, f, z0):
+    """Sigma2D = J W Sigma W^T J^T for a camera at (0, 0, -z0) looking down +z (W = I),
+    Sigma = R diag(s^2) R^T with R from scipy ([Splaxel] sec. 2 'Projection')."""
+    from scipy.spatial.transform import Rotation
+    w, x, y, z = q
+    R = Rotation.from_quat([x, y, z, w]).as_matrix()
+    Sig = R @ np.diag(np.square(s)) @ R.T
+    X, Y, Z = mu[0], mu[1], mu[2] + z0
+    J = np.array([[f / Z, 0.0, -f * X / Z ** 2], [0.0, f / Z, -f * Y / Z ** 2]])
+    return J @ Sig @ J.T
+
+
+@pytest.mark.parametrize("case", ["isotropic", "rotated_anisotropic", "off_axis"])
+def test_footprint_radius_is_the_alpha_min_ellipse_box(case):
+    """[gsplat] walkthrough step 5 (two radii per projected Gaussian) and [ByteSplat] sec. 2.1
+    (the alpha-check): each radius is the half-extent of the region where
+    o exp(-d^T Sigma2D^-1 d / 2) >= alpha_min, rounded up to whole pixels.  The half-extents
+    come from a brute-force sweep of that ellipse's boundary, with Sigma2D built from the
+    3D parameters by the EWA formula in float64 (scipy's rotation); a radius one pixel too
+    large or too small fails."""
+    f, z0 = 200.0, 3.0
+    cases = {
+        "isotropic": ([0.0, 0.0, 0.0], [0.02, 0.02, 0.02], [1.0, 0.0, 0.0, 0.0], 0.5),
+        "rotated_anisotropic": ([0.0, 0.0, 0.0], [0.05, 0.012, 0.03], [0.8, 0.3, -0.4, 0.35], 1.2),
+        "off_axis": ([0.31, -0.22, 0.4], [0.04, 0.015, 0.025], [0.2, 0.9, 0.1, -0.3], -0.4),
+    }
+    mu, s, q, logit = cases[case]
+    qn = np.array(q) / np.linalg.norm(q)
+    sc = _single_scene([mu], [s], [logit], [[0.5, 0.5, 0.5]], quats=[list(qn)])
+    cam = _axis_camera(z0, f, 256, 256)
+    prm = oracle.Params()
+    P = oracle.project(sc, cam, prm, round_record=False)
+    assert P.vis[0] == 1
+    # the float32 inputs the oracle sees
+    s32 = np.exp(sc.log_scales[:, 0].double().numpy())
+    mu32 = sc.means[:, 0].double().numpy()
+    q32 = sc.quats[:, 0].double().numpy()
+    o = _sigmoid(float(sc.opacity_logits[0]))
+    sig2d = _ewa_sigma2d(mu32, s32, q32 / np.linalg.norm(q32), f, z0)
+    thr = 2.0 * math.log(o / prm.alpha_min)
+    hx, hy = _boundary_half_extents(sig2d, thr)
+    for h in (hx, hy):   # away from an integer, so that rounding up is decided
+        assert 1e-3 < h - math.floor(h) < 1.0 - 1e-3, h
+    want = [max(1, math.ceil(hx)), max(1, math.ceil(hy))]
+    assert P.radii[0].tolist() == want, (P.radii[0].tolist(), hx, hy)
+    if case != "isotropic":
+        assert want[0] != want[1]
+
+
+def test_footprint_tiles_and_traversal_hand_count():
+    """The isotropic Gaussian of the radius pin on the axis of a 64x64 camera: sigma_px =
+    200 * 0.02 / 3 = 1.3333 px, o = sigmoid(0.5) = 0.6225, so the alpha >= 1/255 disc has
+    radius 1.3333 * sqrt(2 ln(0.6225 * 255)) = 4.245 px and the box is u, v = 32 +- 5, i.e.
+    pixels [27, 37] x [27, 37]: tiles 1 and 2 in x and in y, 4 tiles.  Every pixel of those
+    4 tiles traverses exactly one list entry (T starts at 1), every other pixel none:
+    N_p summed over the image = 4 * 256 = 1024 ([ByteSplat] Eq. 1, N_p)."""
+    sc = _single_scene([[0.0, 0.0, 0.0]], [[0.02] * 3], [0.5], [[0.5, 0.5, 0.5]])
+    cam = _axis_camera(3.0, 200.0, 64, 64)
+    P = oracle.project(sc, cam, oracle.Params(), round_record=True)
+    assert P.radii[0].tolist() == [5, 5]
+    tt, keys, ids, ranges = oracle.bin_f32(P.rec[:, :2].astype(np.float32), P.radii, P.dkey, 64, 64)
+    assert tt.tolist() == [4]
+    assert ranges.tolist() == [0, 0, 0, 0, 0, 0, 1, 2, 2, 2, 3, 4, 4, 4, 4, 4, 4]
+    col, tf, nt, tie = oracle.render(P, oracle.Params())
+    want = np.zeros((64, 64), np.int32)
+    want[16:48, 16:48] = 1
+    assert np.array_equal(nt, want) and int(nt.sum()) == 1024
+
+
 def test_two_gaussians_blend_order():
     """[ByteSplat Eq. 1] front to back: C = a1 c1 + (1 - a1) a2 c2; swapping the depths swaps
     the roles (depth sort, [Splaxel sec. 2 'Sorting'])."""
