@@ -36,9 +36,12 @@ the batch hyper-parameters of the ROCm blog's "Batching and Hyperparameter Scali
 the next batch's projections).  ms_per_step is per optimiser step (B views).
 
 roofline: the longer of the backward raster kernel (k_raster_fused_l1 by default,
-k_raster_bwd with --separate-raster; bound by VALU arithmetic, its algorithmic work is
-FLOP_PER_PAIR floating-point operations per Gaussian-pixel pair) and k_grad_adam (bound by
-HBM; hbm_bytes), one launch each per step; roofline_next the other.  roofline.traffic is the HBM traffic of one launch
+k_raster_bwd with --separate-raster; bound by VALU arithmetic: FLOP_FWD floating-point
+operations per (pixel, record) pair the forward walk evaluates and FLOP_BWD per pair the
+backward walk evaluates, with the pairs counted on the device by the fused kernel's
+counting instance in an untimed call on each view's lists after the timed steps; peak: the
+non-packed fp32 VALU rate) and k_grad_adam (bound by HBM; hbm_bytes), one launch each per
+step; roofline_next the other.  roofline.traffic is the HBM traffic of one launch
 from the stored counter summary (profiles/), or null if the kernel's sources changed
 since those counters were taken.  --copy-calibration-mib runs a plain copy-like kernel of
 known size before the timed steps, for the counter runs that normalise FETCH_SIZE and
@@ -57,17 +60,63 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "Gaussian-pixel intersections/s (fwd+bwd); train-step ms at 1M Gaussians 1080p"
+METRIC_OF = {"1m": METRIC,
+             "100k": "Gaussian-pixel intersections/s (fwd+bwd); train-step ms at 100K Gaussians 512x512",
+             "10m": "Gaussian-pixel intersections/s (fwd+bwd); train-step ms at 10M Gaussians 4K (skewed)",
+             "20m": "Gaussian-pixel intersections/s (fwd+bwd); train-step ms at 20M Gaussians 4K in 4 depth slabs",
+             "tiny": "Gaussian-pixel intersections/s (fwd+bwd); train-step ms at 1K Gaussians 64x64"}
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3          # published MI355X vector fp32 (packed FMA)
-FP32_NONPACKED_TFLOPS = 78.6             # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+# fp32 VALU peak reachable without packed-FP32 instructions (the build excludes them):
+# 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz; the published 157.3 needs packed FMA
+FP32_VALU_PEAK_TFLOPS = 78.6
+FP32_PACKED_PUBLISHED_TFLOPS = 157.3
 
-# Algorithmic floating-point work per Gaussian-pixel pair, from the operation lists of
-# ByteSplat Eq. 1 (forward: offset, quadratic form, exp, clamp and alpha-check, blend,
-# transmittance update: 26 flop + 1 exp) and Eq. 3 / Eq. 4 (backward: the forward's alpha,
-# T recovery, colour and alpha gradients, colour-behind update, power / conic / mean /
-# opacity gradients and their per-Gaussian sums: 61 flop + 1 exp + 1 reciprocal).  The
-# kernels compute the same quantities with fewer instructions (per-wave moment sums).
-FLOP_PER_PAIR = {"raster_fwd": 27, "raster_bwd": 63, "raster_fused": 27 + 63}
+# Algorithmic floating-point work per evaluated (pixel, record) pair, from the operation
+# lists of ByteSplat Eq. 1 (forward: offset, quadratic form, exp, clamp and alpha-check,
+# blend, transmittance update: 26 flop + 1 exp) and Eq. 3 / Eq. 4 (backward: the forward's
+# alpha, T recovery, colour and alpha gradients, colour-behind update, power / conic / mean /
+# opacity gradients and their per-Gaussian sums: 61 flop + 1 exp + 1 reciprocal).  Every
+# record a quadrant wave walks is evaluated for all 64 of its lanes (branch-free), so the
+# pairs are 64 x the records walked, counted on the device (gs_raster_fused_l1 walk_counts).
+FLOP_FWD, FLOP_BWD = 27, 63
+ALU_KERNELS = ("raster_fwd", "raster_bwd", "raster_fused")
+
+
+def alu_flop(nm, walk):
+    """Algorithmic flop of one launch of raster kernel nm; walk = per-launch (forward
+    records, backward records, accepted pairs) of the quadrant waves."""
+    pf, pb = 64.0 * walk[0], 64.0 * walk[1]
+    return {"raster_fwd": FLOP_FWD * pf, "raster_bwd": FLOP_BWD * pb,
+            "raster_fused": FLOP_FWD * pf + FLOP_BWD * pb}[nm]
+
+
+def alu_entry(nm, ms, walk, isect):
+    fl = alu_flop(nm, walk)
+    tf = fl / (ms * 1e-3) / 1e12
+    return dict(bound="alu", algorithmic_flop=int(fl), achieved_TFLOPs=round(tf, 3),
+                frac=round(tf / FP32_VALU_PEAK_TFLOPS, 4), isect_per_s=round(isect / (ms * 1e-3), 1))
+
+
+def alu_roofline(kern, nm, d, walk, isect, traffic):
+    return {"kernel": kern, "bound": "alu", "achieved": d["achieved_TFLOPs"], "peak": FP32_VALU_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": d["frac"], "traffic": traffic,
+            "flop_per_pair": {"fwd": FLOP_FWD if nm != "raster_bwd" else 0, "bwd": FLOP_BWD if nm != "raster_fwd" else 0},
+            "pairs_per_launch": {"fwd_evaluated": round(64.0 * walk[0], 1) if nm != "raster_bwd" else 0,
+                                 "bwd_evaluated": round(64.0 * walk[1], 1) if nm != "raster_fwd" else 0,
+                                 "fwd_accepted": round(walk[2], 1), "sum_n_p": round(isect, 1)},
+            "launch_ms": d["ms"], "peak_packed_published": FP32_PACKED_PUBLISHED_TFLOPS}
+
+
+def count_walks(runs):
+    """runs: (callable(walk_counts)) per launch to count; each runs the fused kernel's counting
+    instance once.  Returns the (forward records, backward records, accepted pairs) of each."""
+    import torch
+    out = []
+    for run in runs:
+        wc = torch.zeros(3, dtype=torch.int64, device="cuda")
+        run(wc)
+        out.append([int(x) for x in wc.cpu()])
+    return out
 # stored counter traffic of the kernels that can dominate the step (1M / 1080p workload)
 TRAFFIC_SUMMARY = {"k_grad_adam_batch": os.path.join(ROOT, "profiles", "k_grad_adam_batch_1m_1080p_traffic.txt"),
                    "k_raster_bwd": os.path.join(ROOT, "profiles", "k_raster_bwd_1m_1080p_traffic.txt"),
@@ -197,12 +246,36 @@ class TimingEvent:
             self._hip.hipEventDestroy(self.ev)
 
 
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(scene, rows):
     """The oracle, single-threaded, on a bounded sample of view 0: projection of every
-    Gaussian, compositing and backward of `rows` image rows, projection backward."""
+    Gaussian, compositing and backward of `rows` image rows, projection backward.  Runs
+    pinned to one host core (os.sched_setaffinity of this thread, restored afterwards),
+    before the GPU is used."""
     import numpy as np
     import oracle
     cam = scene.cameras[0]
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[-1]
+    os.sched_setaffinity(0, {core})
+    try:
+        out = _cpu_baseline_pinned(scene, rows, oracle, np, cam)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    out.update(pinned_core=core, cpu_model=cpu_model())
+    return out
+
+
+def _cpu_baseline_pinned(scene, rows, oracle, np, cam):
     t0 = time.perf_counter()
     P = oracle.project(scene, cam)
     W = cam.width
@@ -259,7 +332,7 @@ def cpu_baseline_parallel(scene, rows):
     return {"value": isect / dt, "unit": "Gaussian-pixel intersections/s", "cores": len(bands), "kind": "oracle",
             "sample": f"view 0: compositing and compositing backward of {rows} rows x {cam.width} px "
                       f"({isect} intersections), rows dealt round-robin to {len(bands)} processes, in {dt:.2f} s "
-                      "(projection not timed)"}
+                      "(projection not timed)", "cpu_model": cpu_model()}
 
 
 def device_info():
@@ -404,6 +477,12 @@ def main_partitioned(args):
     wall = time.perf_counter() - t0
     per_kernel = {nm: ms / args.steps for nm, ms in timer.totals().items()}
     isect_step = sum(int(st.frame.n_trav_sum.item()) for st in ps.parts) / args.steps
+    # the raster walks of the last step's slab lists, counted by the fused kernel's counting
+    # instance (its forward and backward walks are those of the separate raster kernels;
+    # the target only sets dL/dC, which does not change which records are walked)
+    walks = count_walks([lambda wc, st=st: st.fused_l1(cam, st.frame.color.clone(), walk_counts=wc)
+                         for st in ps.parts])
+    walk_step = [sum(w[j] for w in walks) for j in range(3)]
     parts = len(ps.parts)
     n = sum(st.params.n for st in ps.parts)
     n_vis = sum(int((st.proj.radii[:, 0] > 0).sum().item()) for st in ps.parts)
@@ -419,26 +498,22 @@ def main_partitioned(args):
         if by is not None:
             entry.update(bound="hbm", algorithmic_bytes=int(by), achieved_GBs=round(by / (ms * 1e-3) / 1e9, 1),
                          frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
-        elif nm in FLOP_PER_PAIR:
-            fl = FLOP_PER_PAIR[nm] * isect_step
-            tf = fl / (ms * 1e-3) / 1e12
-            entry.update(bound="alu", algorithmic_flop=int(fl), achieved_TFLOPs=round(tf, 3),
-                         frac=round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
-                         isect_per_s=round(isect_step / (ms * 1e-3), 1))
+        elif nm in ALU_KERNELS:
+            entry.update(alu_entry(nm, ms, walk_step, isect_step))
         kernels[nm] = entry
     dom = max(per_kernel, key=per_kernel.get)
     d = kernels[dom]
     kern = {"raster_bwd": "k_raster_bwd", "raster_fwd": "k_raster_fwd", "bin_sort": "gs_bin_sort"}.get(dom, dom)
     if d.get("bound") == "alu":
-        roof = {"kernel": kern, "bound": "alu", "achieved": d["achieved_TFLOPs"], "peak": FP32_VECTOR_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": d["frac"], "traffic": None, "flop_per_pair": FLOP_PER_PAIR[dom],
-                "pairs_per_launch": round(isect_step / parts, 1), "launch_ms": round(d["ms"] / parts, 4)}
+        per_launch = dict(d, ms=round(d["ms"] / parts, 4))
+        roof = alu_roofline(kern, dom, per_launch, [w / parts for w in walk_step], isect_step / parts, None)
     else:
         roof = {"kernel": kern, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": d["frac"], "traffic": None, "algorithmic_bytes": d["algorithmic_bytes"],
                 "launch_ms": d["ms"]}
     out = {
-        "metric": METRIC, "value": round(isect_step * args.steps / wall, 1), "unit": "Gaussian-pixel intersections/s",
+        "metric": METRIC_OF["20m"], "value": round(isect_step * args.steps / wall, 1),
+        "unit": "Gaussian-pixel intersections/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H], "views": 1,
@@ -565,12 +640,17 @@ def main_batch(args):
     n = scene.n
     n_vis = int((bt.proj[0].radii[:, 0] > 0).sum().item())
     by = 36 * k_mean * bs + n * (11 + 3 * scene.k_sh) * 24 + bs * (n_vis * 96 + (n - n_vis) * 12)
-    fl = FLOP_PER_PAIR["raster_fused"] * isect_view
+    # the walks of each batch slot's last lists, counted by the fused kernel's counting instance
+    last_views = views_of(step0 + args.steps - 1)   # the views whose lists the bins hold now
+    walks = count_walks([lambda wc, k=k: B.gs_raster_fused_l1(
+        bt.params.gaussians(), bt.bins[k].abi(), cams[last_views[k]], bt.raster, targets[last_views[k]],
+        bt.frame[k].color, bt.frame[k].t_final, bt.frame[k].n_trav, None, None, bt.frame[k].fused_ws,
+        walk_counts=wc) for k in range(bs)])
+    walk_view = [sum(w[j] for w in walks) / bs for j in range(3)]
+    fl = alu_flop("raster_fused", walk_view)
     if vstreams is None:
-        raster_entry = {"ms": round(raster_ms, 4), "bound": "alu", "algorithmic_flop": int(fl),
-                        "achieved_TFLOPs": round(fl / (raster_ms * 1e-3) / 1e12, 3),
-                        "frac": round(fl / (raster_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
-                        "note": "per view"}
+        raster_entry = dict(ms=round(raster_ms, 4), **alu_entry("raster_fused", raster_ms, walk_view, isect_view),
+                            note="per view")
     else:   # the views overlap: the window on a view's stream is not the kernel's duration
         raster_entry = {"window_ms": round(raster_ms, 4), "bound": "alu", "algorithmic_flop": int(fl),
                         "note": "per view; window between events on the view's stream while the other views' "
@@ -592,13 +672,11 @@ def main_batch(args):
                 "algorithmic_bytes": d["algorithmic_bytes"], "launch_ms": d["ms"]}
     else:
         d = kernels["raster_fused"]
-        roof = {"kernel": "k_raster_fused_l1", "bound": "alu", "achieved": d["achieved_TFLOPs"],
-                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": d["frac"],
-                "traffic": stored("k_raster_fused_l1"),
-                "flop_per_pair": FLOP_PER_PAIR["raster_fused"], "pairs_per_launch": round(isect_view, 1),
-                "launch_ms": d["ms"]}
+        roof = alu_roofline("k_raster_fused_l1", "raster_fused", d, walk_view, isect_view,
+                            stored("k_raster_fused_l1"))
     out = {
-        "metric": METRIC, "value": round(isect_total / wall, 1), "unit": "Gaussian-pixel intersections/s",
+        "metric": METRIC_OF[args.workload], "value": round(isect_total / wall, 1),
+        "unit": "Gaussian-pixel intersections/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "ms_per_view": round(wall * 1e3 / (args.steps * bs), 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
@@ -638,10 +716,12 @@ def main():
 
     dev = "cuda"
     scene, desc = make_scene(args.workload)
-    # the parallel oracle leg forks, so it runs before anything touches the GPU
-    cpu_par = None
+    # both oracle legs run before anything touches the GPU: the parallel one forks, the
+    # single-core one pins this thread to one core
+    cpu_par = cpu_one = None
     if not args.no_cpu_baseline:
         cpu_par = cpu_baseline_parallel(scene, min(args.cpu_rows, scene.cameras[0].height))
+        cpu_one = cpu_baseline(scene, min(args.cpu_rows, scene.cameras[0].height))
     cams = [B.camera_from(c) for c in scene.cameras]
     targets = [t.to(dev) for t in scene.targets]
     nviews = len(cams)
@@ -785,6 +865,18 @@ def main():
                       for j in range(len(names))}
         per_kernel.update(timed_ms)
         step_ms = sorted(ev2[s][0].elapsed_time(ev2[s][-1]) for s in range(args.steps))
+    # the raster walks, counted on the device by the fused kernel's counting instance: one
+    # untimed call on each view's lists (projected and sorted from the current parameters),
+    # weighted by how often each view ran in the timed steps
+    def count_view(v):
+        def run(wc):
+            B.gs_project(g, cams[v], st.raster, st.proj.abi())
+            st.bins.sort(st.proj, cams[v], st.raster)
+            st.fused_l1(cams[v], targets[v], walk_counts=wc)
+        return run
+    walks = count_walks([count_view(v) for v in range(nviews)])
+    wts = [sum(1 for i in range(args.steps) if (step0 + i) % nviews == v) for v in range(nviews)]
+    walk_step = [sum(w * wk[j] for w, wk in zip(wts, walks)) / args.steps for j in range(3)]
     # ByteSplat Eq. 7-9 for the last step's tile lists: how many tiles a design that keeps a
     # tile's records on chip could hold (64 KiB of LDS per tile, 256 pixels x 32 B of pixel
     # state, 48-B records); the fused kernel streams records and runs every tile
@@ -809,23 +901,15 @@ def main():
         if by is not None:
             entry.update(bound="hbm", algorithmic_bytes=int(by), achieved_GBs=round(by / (ms * 1e-3) / 1e9, 1),
                          frac=round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
-        elif nm in FLOP_PER_PAIR:
-            fl = FLOP_PER_PAIR[nm] * isect_step
-            tf = fl / (ms * 1e-3) / 1e12
-            entry.update(bound="alu", algorithmic_flop=int(fl), achieved_TFLOPs=round(tf, 3),
-                         frac=round(tf / FP32_VECTOR_PEAK_TFLOPS, 4),
-                         frac_nonpacked=round(tf / FP32_NONPACKED_TFLOPS, 4),
-                         isect_per_s=round(isect_step / (ms * 1e-3), 1))
+        elif nm in ALU_KERNELS:
+            entry.update(alu_entry(nm, ms, walk_step, isect_step))
         kernels[nm] = entry
     def roofline(nm):
         d = kernels[nm]
         kern = KERNEL_OF[nm]
         traffic = read_stored_traffic(TRAFFIC_SUMMARY[kern], kern) if args.workload == "1m" else None
         if d["bound"] == "alu":
-            return {"kernel": kern, "bound": "alu", "achieved": d["achieved_TFLOPs"], "peak": FP32_VECTOR_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": d["frac"], "traffic": traffic,
-                    "flop_per_pair": FLOP_PER_PAIR[nm], "pairs_per_launch": round(isect_step, 1),
-                    "launch_ms": d["ms"], "frac_nonpacked_peak": d["frac_nonpacked"]}
+            return alu_roofline(kern, nm, d, walk_step, isect_step, traffic)
         return {"kernel": kern, "bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": d["frac"], "traffic": traffic, "algorithmic_bytes": d["algorithmic_bytes"],
                 "launch_ms": d["ms"]}
@@ -835,7 +919,8 @@ def main():
     roof = roofline(ranked[0])
     roof_next = roofline(ranked[1]) if len(ranked) > 1 else None
     out = {
-        "metric": METRIC, "value": round(isect_total / wall, 1), "unit": "Gaussian-pixel intersections/s",
+        "metric": METRIC_OF[args.workload], "value": round(isect_total / wall, 1),
+        "unit": "Gaussian-pixel intersections/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
@@ -868,7 +953,7 @@ def main():
         "device_info": device_info(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(scene, min(args.cpu_rows, H))
+        out["cpu_baseline"] = cpu_one
         out["cpu_baseline_parallel"] = cpu_par
     print(json.dumps(out), flush=True)
 

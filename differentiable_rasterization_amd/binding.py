@@ -117,7 +117,7 @@ _SIGS = {
                                               _vp, _P(ParamGrads), _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32,
                                               _f32, _P(Camera), _P(Projected), _vp]),
     "gs_raster_fused_l1": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp,
-                                  _vp, _vp, ctypes.c_size_t, _vp]),
+                                  _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "gs_raster_fused_l1_workspace_bytes": (ctypes.c_size_t, [_i32, _i32]),
     "gs_tile_budget": (_i64, [_i64, _i64, _i64]),
     "gs_tile_budget_report": (_i32, [_P(Bins), _P(Camera), _i64, _vp, _vp, _vp, _vp]),
@@ -294,10 +294,11 @@ def gs_raster_fused_l1_workspace_bytes(width, height) -> int:
 
 
 def gs_raster_fused_l1(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, target, color, t_final, n_trav,
-                       loss_out, n_trav_sum, workspace, stream=None):
+                       loss_out, n_trav_sum, workspace, stream=None, walk_counts=None):
     _check(_lib.gs_raster_fused_l1(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p), _ptr(target),
                                    _ptr(color), _ptr(t_final), _ptr(n_trav), _ptr(loss_out), _ptr(n_trav_sum),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+                                   _ptr(walk_counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
 
 
 def gs_tile_budget(lds_budget_bytes, fixed_bytes, bytes_per_gaussian) -> int:

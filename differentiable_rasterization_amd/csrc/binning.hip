@@ -219,6 +219,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals
         hdr->K = K;
         hdr->Q = Q;
         hdr->ok = ok ? 1u : 0u;
+        hdr->epoch = gsr::kSortEpoch;   // the qoff scan zeroed the stamps of slots 0 .. Q
         if (counts) {
             counts[0] = (int64_t)K;
             counts[1] = ok ? 0 : (int64_t)need_capacity(K, Q);
@@ -467,6 +468,7 @@ __global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restr
     hdr->K = 0;
     hdr->Q = 0;
     hdr->ok = 1u;
+    hdr->epoch = gsr::kSortEpoch;
     if (counts) {
         counts[0] = 0;
         counts[1] = 0;
@@ -606,11 +608,16 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     const unsigned gn = (unsigned)ceil_div(n, 256);
 
     // 1. depth keys, tile and quadrant-record counts in index order; the first gradient
-    //    slot of each Gaussian (exclusive scan of its record counts) and the total Q
+    //    slot of each Gaussian (exclusive scan of its record counts) and the total Q; the
+    //    same scan zeroes the stamps of the slots it gives out (those that fit), so no slot
+    //    of this sort carries a backward call's stamp before one writes it
     k_keys_count<<<gn, 256, 0, stream>>>(rr, proj->depth, prec, log2_amin, n, tx, ty, dkA, dvA, qcnt,
                                          bins->tiles_touched, (uint32_t *)(ws + L.zero), (int64_t)(L.zero_bytes / 4));
     GS_LAUNCH_CHECK("k_keys_count");
-    if ((s = lb_scan_u32(qcnt, qoff, n + 1, scQ, tickets + kTkQcnt, total + 1, stream)) != GS_OK) return s;
+    uint32_t *qstamp = reinterpret_cast<uint32_t *>(rb + RL.qstamp);
+    if ((s = lb_scan_u32(qcnt, qoff, n + 1, scQ, tickets + kTkQcnt, total + 1, stream, qstamp,
+                         (int64_t)gsr::kQuadFactor * RL.cap)) != GS_OK)
+        return s;
 
     // 2. Gaussians by depth key (stable, so equal keys stay in index order; the values
     //    carry the tile counts along), and the emit offsets: the exclusive scan of the tile

@@ -20,10 +20,12 @@ gs_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, uint3
 // Exclusive scan of m >= 1 uint32 values (in place allowed) in one launch, by look-back
 // over the published sums of earlier tiles.  status [lb_scan_tiles(m)] uint64 and *ticket
 // must be zero on entry (each scan needs its own).  If total != NULL the 64-bit sum is
-// written there.
+// written there.  With clear != NULL the scan also sets clear[x] = 0 for every x below
+// min(sum, clear_lim) (each tile zeroes its own output range, coalesced).
 int64_t lb_scan_tiles(int64_t m);
 gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
-                      unsigned long long *total, hipStream_t stream);
+                      unsigned long long *total, hipStream_t stream, uint32_t *clear = nullptr,
+                      int64_t clear_lim = 0);
 // The same over the high 32 bits of m uint64 values (in: 16-byte aligned).
 gs_status lb_scan_hi32(const uint64_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
                        unsigned long long *total, hipStream_t stream);

@@ -685,7 +685,7 @@ __global__ __launch_bounds__(256) void k_grad_adam(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
     const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
-    const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp, float *__restrict__ grads2d, AdamSink out,
+    const float4 *__restrict__ qgrad, const uint32_t *__restrict__ qstamp, float *__restrict__ grads2d, AdamSink out,
     CamD next_cam, ProjOut next)
 {
     __shared__ gsr::SlotStage stage[4];
@@ -710,7 +710,7 @@ struct ViewBins {
     const gsr::BinsHeader *hdr;
     const uint32_t *qoff;
     const float4 *qgrad;
-    const uint2 *qstamp;
+    const uint32_t *qstamp;
 };
 
 struct BatchProj {
@@ -968,7 +968,7 @@ ViewBins view_bins(const gs_bins *bins, const gs_camera *cam, int64_t n)
     const char *rb = static_cast<const char *>(bins->raster);
     return ViewBins{reinterpret_cast<const gsr::BinsHeader *>(rb + L.hdr),
                     reinterpret_cast<const uint32_t *>(rb + L.qoff), reinterpret_cast<const float4 *>(rb + L.qgrad),
-                    reinterpret_cast<const uint2 *>(rb + L.qstamp)};
+                    reinterpret_cast<const uint32_t *>(rb + L.qstamp)};
 }
 
 gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, const gs_bins *bins, const gs_camera *cam,
@@ -1002,7 +1002,7 @@ gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, cons
     const gsr::BinsHeader *hdr = reinterpret_cast<const gsr::BinsHeader *>(rb + L.hdr);
     const uint32_t *qoff = reinterpret_cast<const uint32_t *>(rb + L.qoff);
     const float4 *qg = reinterpret_cast<const float4 *>(rb + L.qgrad);
-    const uint2 *qs = reinterpret_cast<const uint2 *>(rb + L.qstamp);
+    const uint32_t *qs = reinterpret_cast<const uint32_t *>(rb + L.qstamp);
     const CamD cd = make_cam(cam);
     const CamD nd = next_cam ? make_cam(next_cam) : cd;
     const ProjOut po = next_cam ? proj_out(next_proj) : ProjOut{};

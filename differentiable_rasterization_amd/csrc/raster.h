@@ -24,9 +24,10 @@
 //   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
 //                                 padded to 48 bytes), one slot per quadrant record, at the
 //                                 slot index its record carries
-//   qstamp [2 * capacity] uint2   the stamp (epoch, ~epoch) of the backward call that wrote
-//                                 each slot, kept apart from the slots so that the
-//                                 per-Gaussian sums read only the slots that were written
+//   qstamp [2 * capacity] uint32  the epoch of the backward call that wrote each slot, kept
+//                                 apart from the slots so that the per-Gaussian sums read only
+//                                 the slots that were written; the sort sets the stamps of
+//                                 slots 0 .. Q to 0, which no epoch equals
 //
 // Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
 // (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of records with
@@ -56,7 +57,7 @@ struct Rec {
 };
 constexpr int kRecF4 = 3;   // float4 words per record
 constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
-constexpr int kStampWords = 2;  // uint32 words per slot stamp
+constexpr int kStampWords = 1;  // uint32 words per slot stamp
 // The record array has kRecPad spare records before and after the lists, so that a batch
 // of consecutive records, and the batch after it, can always be loaded from one base
 // address (records outside the lists are loaded but never used).
@@ -113,15 +114,21 @@ __device__ __forceinline__ uint32_t quad_mask(float u, float v, float A, float B
 
 // Counts of the last sort, in device memory (the first bytes of the raster buffer).  When
 // the lists did not fit (ok == 0) the sort leaves every tile list empty and the per-Gaussian
-// gradient reduction writes zeros.  epoch: advanced by every backward call (any start
-// value); the backward stamps each gradient slot it writes with (epoch, ~epoch) in qstamp,
-// and the per-Gaussian sums take only slots stamped by the latest call, so slots of records
-// no pixel reached are never written nor read (a stale or never-written stamp matches with
-// probability 2^-64).
+// gradient reduction writes zeros.  epoch: the sort sets it to 1 and every backward call
+// advances it (next_epoch: never 0); the backward stamps each gradient slot it writes with
+// the new epoch in qstamp, and the per-Gaussian sums take only slots whose stamp equals the
+// current epoch.  The sort sets the stamps of all its slots to 0, so a slot the backward
+// did not write since the sort (a record no pixel reached, a batch no pixel took) never
+// matches, whatever the buffer held before: the raster buffer may be uninitialised.
 struct BinsHeader {
     unsigned long long K, Q;   // tile entries and (entry, quadrant) records
     uint32_t ok, epoch;
 };
+
+constexpr uint32_t kSortEpoch = 1u;   // the epoch a sort leaves in the header
+
+// The epoch after e; 0 is skipped, since it is the stamp of a slot no backward wrote.
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1u == 0u ? 1u : e + 1u; }
 
 // The same test from a raster record (conic pre-scaled for exp2, l = log2 o):
 // alpha >= alpha_min  <=>  a dx^2 + b dx dy + c dy^2 >= log2(alpha_min) - l, i.e. the
@@ -178,7 +185,7 @@ struct SlotStage {
 // batch pass (two waves per SIMD by attribute), slower in k_grad_adam at 10 M.
 template <int U = 1>
 __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
-                                              const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp,
+                                              const float4 *__restrict__ qgrad, const uint32_t *__restrict__ qstamp,
                                               int64_t g, int64_t n, SlotStage &S, float (&acc)[9])
 {
     const int lane = threadIdx.x & 63;
@@ -191,13 +198,13 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
     for (int f = 0; f < 9; ++f) acc[f] = 0.0f;
     // Two-stage pipeline over the chunks of 64 slots: the stamps run two chunks ahead and the
     // slot data one chunk ahead, so the data of chunk c0 + 64 loads while chunk c0 is summed.
-    uint2 tn = make_uint2(0u, 0u);
+    uint32_t tn = 0u;
     if (w0 + (uint32_t)lane < w1) tn = qstamp[w0 + (uint32_t)lane];
     bool w;   // this lane's slot of the chunk in d0..d2 was written by the latest backward call
     float4 d0, d1, d2;
     {
         const uint32_t sl = w0 + (uint32_t)lane;
-        w = sl < w1 && tn.x == epoch && tn.y == ~epoch;   // unwritten slots are not read
+        w = sl < w1 && tn == epoch;   // unwritten slots are not read
         if (w) {
             const float4 *p = qgrad + (size_t)sl * (kGradSlot / 4);
             d0 = p[0];
@@ -214,7 +221,7 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
         }
         S.ok[lane] = w ? 1u : 0u;
         const uint32_t sn = c0 + 64u + (uint32_t)lane;
-        w = sn < w1 && tn.x == epoch && tn.y == ~epoch;
+        w = sn < w1 && tn == epoch;
         if (w) {
             const float4 *p = qgrad + (size_t)sn * (kGradSlot / 4);
             d0 = p[0];
@@ -284,7 +291,7 @@ __device__ __forceinline__ void moments_to_grads(const float (&acc)[9], float a,
 // Both steps, the record read from rec[g]; a Gaussian without records (culled) gets zeros
 // and its record is not read.  Called by all 64 lanes of the wave (see raw_slot_sums).
 __device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
-                                          const float4 *__restrict__ qgrad, const uint2 *__restrict__ qstamp,
+                                          const float4 *__restrict__ qgrad, const uint32_t *__restrict__ qstamp,
                                           const float4 *__restrict__ rec, int64_t g, int64_t n, SlotStage &S,
                                           float (&out)[9])
 {

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
 }
 
 // A new stamp for the gradient slots of this backward call.
-__global__ void k_new_epoch(BinsHeader *__restrict__ hdr) { hdr->epoch = hdr->epoch + 1u; }
+__global__ void k_new_epoch(BinsHeader *__restrict__ hdr) { hdr->epoch = next_epoch(hdr->epoch); }
 
 // Eq. 4: the gradient of Gaussian g is the sum of the slots of its quadrant records,
 // slots qoff[g] .. qoff[g + 1], added in order.  Every Gaussian is
@@ -92,7 +92,7 @@ __global__ void k_new_epoch(BinsHeader *__restrict__ hdr) { hdr->epoch = hdr->ep
 // so that the stores coalesce.
 __global__ __launch_bounds__(256) void k_grad_reduce(const BinsHeader *__restrict__ hdr,
                                                      const uint32_t *__restrict__ qoff, const float4 *__restrict__ qgrad,
-                                                     const uint2 *__restrict__ qstamp,
+                                                     const uint32_t *__restrict__ qstamp,
                                                      const float4 *__restrict__ rec, int64_t n,
                                                      float *__restrict__ grads2d)
 {
@@ -171,7 +171,7 @@ extern "C" gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_projected
         const char *rb = static_cast<const char *>(bins->raster);
         k_grad_reduce<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(
             reinterpret_cast<const BinsHeader *>(rb + L.hdr), reinterpret_cast<const uint32_t *>(rb + L.qoff),
-            reinterpret_cast<const float4 *>(rb + L.qgrad), reinterpret_cast<const uint2 *>(rb + L.qstamp),
+            reinterpret_cast<const float4 *>(rb + L.qgrad), reinterpret_cast<const uint32_t *>(rb + L.qstamp),
             reinterpret_cast<const float4 *>(proj->rec), n, grads2d);
         GS_LAUNCH_CHECK("k_grad_reduce");
     }

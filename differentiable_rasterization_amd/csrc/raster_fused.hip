@@ -52,13 +52,16 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 
 __device__ __forceinline__ float l1_sign(float d) { return d > 0.0f ? 1.0f : (d < 0.0f ? -1.0f : 0.0f); }
 
+// kCount: the counting instance (gs_raster_fused_l1 with walk_counts) also adds the wave's
+// walked records, forward and backward, and its accepted (pixel, record) pairs to counts.
+template <bool kCount>
 __global__ __launch_bounds__(64) void k_raster_fused_l1(
     const int32_t *__restrict__ ranges, const int32_t *__restrict__ order, const float4 *__restrict__ qrec,
     const uint64_t *__restrict__ bitmap, const uint32_t *__restrict__ wpre, int64_t words, int W, int H, int TX,
     int T, float alpha_min, float alpha_max, float t_min, const float *__restrict__ target, float inv,
     float *__restrict__ out_c, float *__restrict__ out_t, int32_t *__restrict__ out_n,
     FusedPartial *__restrict__ part, uint32_t *__restrict__ final_ticket, const BinsHeader *__restrict__ hdr,
-    float *__restrict__ qgrad, uint32_t *__restrict__ qstamp)
+    float *__restrict__ qgrad, uint32_t *__restrict__ qstamp, unsigned long long *__restrict__ counts)
 {
     int tile, q;
     raster_block(order, tile, q);
@@ -75,13 +78,14 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
     float Tr = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
     int np = 0;
     uint32_t j0 = 0, j1 = 0;
+    uint32_t walked = 0, taken = 0;
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     if (listed) {   // an empty list reads nothing (its quadrant prefix counts may be unset)
         j0 = quad_prefix(bq, wq, (uint32_t)start);
         j1 = quad_prefix(bq, wq, (uint32_t)end);
-        fwd_walk<kFusedFwdBatch>(qrec, j0, j1, fx, fy, start, end, inside, alpha_min, alpha_max, t_min, cr, cg, cb,
-                                 Tr, np);
+        fwd_walk<kFusedFwdBatch, kCount>(qrec, j0, j1, fx, fy, start, end, inside, alpha_min, alpha_max, t_min, cr,
+                                         cg, cb, Tr, np, &walked, &taken);
     }
     // 2. L1 loss and its gradient
     float G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, Z = 0.0f;
@@ -111,8 +115,17 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
     if (!listed) return;
     const int nmax = max(0, min(gsd::wave_max_i32(np), end - start));
     const uint32_t jb = quad_prefix(bq, wq, (uint32_t)(start + nmax));
-    // the stamp of this call: the header's epoch advanced by one (k_fused_final stores it)
-    bwd_walk(qrec, j0, jb, fx, fy, start, np, G0, G1, G2, Z, alpha_min, alpha_max, hdr->epoch + 1u, qgrad, qstamp);
+    if constexpr (kCount) {
+        const unsigned long long tk = wave_sum_u64((unsigned long long)taken);
+        if (lane == 0) {
+            atomicAdd(&counts[0], (unsigned long long)walked);
+            atomicAdd(&counts[1], (unsigned long long)(jb - j0));
+            atomicAdd(&counts[2], tk);
+        }
+    }
+    // the stamp of this call: the header's next epoch (k_fused_final stores it)
+    bwd_walk(qrec, j0, jb, fx, fy, start, np, G0, G1, G2, Z, alpha_min, alpha_max, next_epoch(hdr->epoch), qgrad,
+             qstamp);
 }
 
 // The loss and sum_p N_p from the per-wave partials.  Each block adds kFinalSpan partials
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
 // finishes last (by a ticket) adds the block sums in block order and writes the results,
 // so the result does not depend on which block finished last.  The ticket is cleared by
 // k_raster_fused_l1 of the same call.  The last block also advances the header's epoch to
-// the stamp k_raster_fused_l1 wrote (epoch + 1), so the per-Gaussian sums that follow read
+// the stamp k_raster_fused_l1 wrote (next_epoch), so the per-Gaussian sums that follow read
 // this call's slots.
 constexpr int kFinalSpan = 1024;
 
@@ -183,7 +196,7 @@ __global__ __launch_bounds__(256) void k_fused_final(const FusedPartial *__restr
     if (threadIdx.x == 0) {
         if (loss) *loss = (float)(l * inv);
         if (n_sum && c) atomicAdd(n_sum, c);
-        hdr->epoch = hdr->epoch + 1u;
+        hdr->epoch = next_epoch(hdr->epoch);
     }
 }
 
@@ -246,7 +259,8 @@ extern "C" size_t gs_raster_fused_l1_workspace_bytes(int32_t width, int32_t heig
 extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
                                         const gs_raster_params *p, const float *target, float *color, float *t_final,
                                         int32_t *n_trav, float *loss_out, unsigned long long *n_trav_sum,
-                                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+                                        unsigned long long *walk_counts, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream)
 {
     using namespace gsi;
     gs_status s;
@@ -268,13 +282,16 @@ extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bi
     FusedPartial *part = reinterpret_cast<FusedPartial *>(wsb + fw.part);
     FusedPartial *block_part = reinterpret_cast<FusedPartial *>(wsb + fw.block_part);
     uint32_t *ticket = reinterpret_cast<uint32_t *>(wsb + fw.ticket);
-    k_raster_fused_l1<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
+    if (walk_counts && !aligned(walk_counts, 8))
+        return fail(GS_ERR_INVALID_ARGUMENT, "walk_counts must be 8-byte aligned");
+    auto kern = walk_counts ? k_raster_fused_l1<true> : k_raster_fused_l1<false>;
+    kern<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
         bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order),
         reinterpret_cast<const float4 *>(rb + L.qrec) + kRecPad * kRecF4,
         reinterpret_cast<const uint64_t *>(rb + L.bitmap), reinterpret_cast<const uint32_t *>(rb + L.wpre), L.words,
         cam->width, cam->height, TX, T, p->alpha_min, p->alpha_max, p->t_min, target, (float)(1.0 / (double)m),
         color, t_final, n_trav, part, ticket, hdr, reinterpret_cast<float *>(rb + L.qgrad),
-        reinterpret_cast<uint32_t *>(rb + L.qstamp));
+        reinterpret_cast<uint32_t *>(rb + L.qstamp), walk_counts);
     GS_LAUNCH_CHECK("k_raster_fused_l1");
     k_fused_final<<<(unsigned)fw.blocks, 256, 0, stream>>>(part, fw.waves, 1.0 / (double)m, block_part, ticket, hdr,
                                                           loss_out, n_trav_sum);

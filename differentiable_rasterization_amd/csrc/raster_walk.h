@@ -44,10 +44,14 @@ struct Batch {
 // kFwdBatch (2 or 4) records per scalar-load batch, two batches in flight: 4 hides more
 // load latency, 2 needs 40 fewer scalar registers (the fused kernel's backward phase then
 // keeps more waves resident).  The batch size does not change the arithmetic.
-template <int kFwdBatch = 4>
+// With kCount, walked receives the number of records the wave evaluated (each for all 64
+// lanes) and taken the number of them this lane accepted (alpha-check passed while live);
+// without it both are left alone.
+template <int kFwdBatch = 4, bool kCount = false>
 __device__ __forceinline__ void fwd_walk(const float4 *__restrict__ qrec, uint32_t j0, uint32_t j1, float fx, float fy,
                                          int start, int end, bool inside, float alpha_min, float alpha_max,
-                                         float t_min, float &cr, float &cg, float &cb, float &Tr, int &np)
+                                         float t_min, float &cr, float &cg, float &cb, float &Tr, int &np,
+                                         uint32_t *walked = nullptr, uint32_t *taken = nullptr)
 {
     Tr = 1.0f;
     cr = 0.0f;
@@ -72,6 +76,7 @@ __device__ __forceinline__ void fwd_walk(const float4 *__restrict__ qrec, uint32
             const float dx = fx - R.p0[i].x, dy = fy - R.p0[i].y;
             const float alpha = fminf(alpha_max, exp2_fast(exponent(R.p0[i], R.p1[i], dx, dy)));
             const bool take = live && alpha >= alpha_min;
+            if constexpr (kCount) *taken += take ? 1u : 0u;
             const float a = take ? alpha : 0.0f;
             const float w = Tr * a;
             cr = fmaf(w, R.p1[i].z, cr);
@@ -89,18 +94,22 @@ __device__ __forceinline__ void fwd_walk(const float4 *__restrict__ qrec, uint32
             pend = prefetch_records(qrec, j + 64u, j1);
         }
     };
+    uint32_t jw = j0;   // end of the records blended so far
     for (uint32_t j = j0; j < j1; j += 2 * kFwdBatch) {
         prefetch(j);
         A.wait();
         B.load(qrec, j + kFwdBatch);   // past j1: spare records, loaded but unused
         blend(A, j);
+        if constexpr (kCount) jw = min(j + kFwdBatch, j1);
         if (j + kFwdBatch >= j1 || __ballot(live) == 0) break;
         prefetch(j + kFwdBatch);
         B.wait();
         A.load(qrec, j + 2 * kFwdBatch);
         blend(B, j + kFwdBatch);
+        if constexpr (kCount) jw = min(j + 2 * kFwdBatch, j1);
         if (__ballot(live) == 0) break;
     }
+    if constexpr (kCount) *walked = jw - j0;
     sink ^= pend;
     asm volatile("" ::"v"(sink));
 }
@@ -182,7 +191,7 @@ __device__ __forceinline__ void reduce_4x9(float (&v)[kBwdBatch * kFields], int 
 // ByteSplat Eq. 3 (and the per-record part of Eq. 4) over the quadrant's records j0 .. j1,
 // front to back, for the lane's pixel at (fx, fy) with dL/dC = (G0, G1, G2),
 // Z = C . G + G_T T_final and its N_p (np): the moment sums of every batch of 4 records
-// some pixel takes go to the records' gradient slots in qgrad, stamped (epoch, ~epoch) in
+// some pixel takes go to the records' gradient slots in qgrad, stamped with epoch in
 // qstamp.
 __device__ __forceinline__ void bwd_walk(const float4 *__restrict__ qrec, uint32_t j0, uint32_t j1, float fx, float fy,
                                          int start, int np, float G0, float G1, float G2, float Z, float alpha_min,
@@ -192,11 +201,10 @@ __device__ __forceinline__ void bwd_walk(const float4 *__restrict__ qrec, uint32
     const int lane = threadIdx.x & 63;
     const int row = lane >> 4, nl = lane & 15;
     // the reduced field each lane of a row holds (reduce_4x9): even lanes hold fields 0-7,
-    // lane 1 field 8; lane 3 writes the slot's stamp (epoch, ~epoch)
+    // lane 1 field 8; lane 3 writes the slot's stamp (the epoch)
     const bool stamp_lane = nl == 3;
     const int my_field = nl == 1 ? 8 : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
     const bool lane_writes = (nl & 1) == 0 || nl == 1 || stamp_lane;
-    const uint2 stamp = make_uint2(epoch, ~epoch);
     float Tr = 1.0f;
     // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
     uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
@@ -258,7 +266,7 @@ __device__ __forceinline__ void bwd_walk(const float4 *__restrict__ qrec, uint32
         // my_field (see reduce_4x9)
         const uint32_t my_slot = __float_as_uint(by_row(row, slot[0], slot[1], slot[2], slot[3]));
         float *dst = qgrad + (size_t)my_slot * kGradSlot + my_field;
-        uint2 *dst_stamp = reinterpret_cast<uint2 *>(qstamp) + my_slot;
+        uint32_t *dst_stamp = qstamp + my_slot;
         const bool writer = (uint32_t)row < cnt && lane_writes;
         jt += cnt;
         if (__ballot(any) == 0) continue;   // no pixel takes these records: slots left unstamped
@@ -266,7 +274,7 @@ __device__ __forceinline__ void bwd_walk(const float4 *__restrict__ qrec, uint32
         reduce_4x9(v, nl, fz, t8);
         if (writer) {
             if (stamp_lane)
-                *dst_stamp = stamp;
+                *dst_stamp = epoch;
             else
                 *dst = nl == 1 ? t8 : fz;
         }

@@ -297,11 +297,15 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 __host__ __device__ constexpr int lb_items(int64_t m) { return m <= 1500000 ? 16 : m <= 6000000 ? 32 : 64; }
 
 // HI32: the input is uint64 and the scan takes the high 32 bits of each value.
+// clear (nullable): the tile also sets clear[x] = 0 for x in its own output range
+// [prefix, prefix + tile sum) below clear_lim, so that one coalesced pass zeroes the
+// elements the scanned counts give out (each tile's range is contiguous).
 template <int ITEMS, bool HI32>
 __global__ __launch_bounds__(kThreads) void k_scan_lb(const void *in_v, uint32_t *out, int64_t m,
                                                       unsigned long long *__restrict__ status,
                                                       uint32_t *__restrict__ ticket,
-                                                      unsigned long long *__restrict__ total)
+                                                      unsigned long long *__restrict__ total,
+                                                      uint32_t *__restrict__ clear, int64_t clear_lim)
 {
     constexpr int kT = kThreads * ITEMS;
     __shared__ uint32_t scratch[4];
@@ -375,6 +379,10 @@ __global__ __launch_bounds__(kThreads) void k_scan_lb(const void *in_v, uint32_t
         }
     }
     __syncthreads();
+    if (clear) {
+        const int64_t c0 = (int64_t)s_excl, c1 = min((int64_t)(s_excl + tot), clear_lim);
+        for (int64_t x = c0 + threadIdx.x; x < c1; x += kThreads) clear[x] = 0u;
+    }
     uint32_t run = (uint32_t)s_excl + pre;
     if (full) {
         uint4 *p = reinterpret_cast<uint4 *>(out + base);
@@ -395,17 +403,18 @@ __global__ __launch_bounds__(kThreads) void k_scan_lb(const void *in_v, uint32_t
 
 template <bool HI32>
 gs_status launch_scan_lb(const void *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
-                         unsigned long long *total, hipStream_t stream)
+                         unsigned long long *total, hipStream_t stream, uint32_t *clear = nullptr,
+                         int64_t clear_lim = 0)
 {
     if (m <= 0) return gsi::fail(GS_ERR_UNSUPPORTED, "scan of an empty array");
     const int items = lb_items(m);
     const unsigned grid = (unsigned)gsi::ceil_div(m, (int64_t)kThreads * items);
     if (items == 16)
-        k_scan_lb<16, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total);
+        k_scan_lb<16, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total, clear, clear_lim);
     else if (items == 32)
-        k_scan_lb<32, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total);
+        k_scan_lb<32, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total, clear, clear_lim);
     else
-        k_scan_lb<64, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total);
+        k_scan_lb<64, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total, clear, clear_lim);
     GS_LAUNCH_CHECK("k_scan_lb");
     return GS_OK;
 }
@@ -454,9 +463,9 @@ int64_t radix_hist_len(int64_t m) { return 256 * ceil_div(m > 0 ? m : 1, kRxTile
 int64_t lb_scan_tiles(int64_t m) { return ceil_div(m > 0 ? m : 1, (int64_t)kThreads * lb_items(m)); }
 
 gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
-                      unsigned long long *total, hipStream_t stream)
+                      unsigned long long *total, hipStream_t stream, uint32_t *clear, int64_t clear_lim)
 {
-    return launch_scan_lb<false>(in, out, m, status, ticket, total, stream);
+    return launch_scan_lb<false>(in, out, m, status, ticket, total, stream, clear, clear_lim);
 }
 
 gs_status lb_scan_hi32(const uint64_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,

@@ -252,12 +252,14 @@ class TrainStep:
                                          v, B.AdamLrs(**self.lr), self.params.step_count, 0.9, 0.999, 1e-15,
                                          next_cam, pa, stream)
 
-    def fused_l1(self, cam: B.Camera, target, stream=None):
+    def fused_l1(self, cam: B.Camera, target, stream=None, walk_counts=None):
         """Forward rasterization, L1 loss and the per-record backward in one kernel (from the
-        current bins); equal to forward rasterization, loss and backward_partials."""
+        current bins); equal to forward rasterization, loss and backward_partials.  With
+        walk_counts (device int64[3]) the counting instance runs and adds the records walked
+        forward and backward and the accepted pairs."""
         f = self.frame
         B.gs_raster_fused_l1(self.params.gaussians(), self.bins.abi(), cam, self.raster, target, f.color, f.t_final,
-                             f.n_trav, f.loss, f.n_trav_sum, f.fused_ws, stream)
+                             f.n_trav, f.loss, f.n_trav_sum, f.fused_ws, stream, walk_counts=walk_counts)
 
     def backward_partials(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):
         f = self.frame

@@ -126,8 +126,12 @@ typedef struct {
  *                             entries whose box reaches it, the maps the backward needs to sum
  *                             each Gaussian's contributions, and the order in which tiles are
  *                             rasterized.  Its layout is private to the library; the caller
- *                             only owns the memory.  The raster calls must use the same n,
- *                             capacity and image size as the gs_bin_sort call that filled it.
+ *                             only owns the memory, which may be uninitialised (fresh or
+ *                             reused) before the first gs_bin_sort: the sort writes
+ *                             everything the raster calls read, including the stamps that
+ *                             mark which gradient slots a backward call has written.  The
+ *                             raster calls must use the same n, capacity and image size as
+ *                             the gs_bin_sort call that filled it.
  * tiles = ceil(W/16) * ceil(H/16), tile id = row * ceil(W/16) + column; capacity <= 2^30. */
 typedef struct {
     uint32_t *ids;
@@ -163,7 +167,7 @@ gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raste
                      gs_projected *out, hipStream_t stream);
 
 /* Bytes of the gs_bins.raster buffer for n Gaussians, `capacity` list entries and a W x H
- * image: 2 quadrant records (48 B), 2 gradient slots (48 B) with their stamps (8 B) and 4
+ * image: 2 quadrant records (48 B), 2 gradient slots (48 B) with their stamps (4 B) and 4
  * quadrant bits per entry, plus 4 B per Gaussian, 16 B per tile and a 256-byte header. */
 size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
 
@@ -274,14 +278,22 @@ gs_status gs_grad_aggregate(const gs_gaussians *g, const gs_projected *proj, con
  * target [H][W][3]: the reference image.  loss_out (device, may be NULL): the mean of
  * |C - target|, equal to gs_loss_l1's up to the order of its double-precision sum.
  * n_trav_sum (device, may be NULL): sum_p N_p is added to it, as in gs_raster_fwd.
+ * walk_counts (device, may be NULL, 8-byte aligned, 3 x uint64): when given, the call runs a
+ * counting instance of the same kernel, which also adds, over all 8x8 quadrant waves, the
+ * number of records the forward walk evaluated, the number the backward walk evaluated
+ * (each record is evaluated for the wave's 64 pixels, those outside the image included) and
+ * the number of (pixel, record) pairs the forward accepted (alpha-check passed before
+ * termination); its results are otherwise identical.  It costs one more vector instruction
+ * per pair, so timed calls pass NULL.
  * workspace: gs_raster_fused_l1_workspace_bytes(W, H) bytes (16-byte aligned) of per-wave
  * partial sums.  Every tile takes this path: records stream through registers in batches,
  * so no tile is too large for it. */
 size_t gs_raster_fused_l1_workspace_bytes(int32_t width, int32_t height);
 gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
                              const gs_raster_params *p, const float *target, float *color, float *t_final,
-                             int32_t *n_trav, float *loss_out, unsigned long long *n_trav_sum, void *workspace,
-                             size_t workspace_bytes, hipStream_t stream);
+                             int32_t *n_trav, float *loss_out, unsigned long long *n_trav_sum,
+                             unsigned long long *walk_counts, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Tile budget diagnostic (ByteSplat section 5.2, Eq. 7-9).  gs_tile_budget: B =
  * floor((lds_budget_bytes - fixed_bytes) / bytes_per_gaussian), the number of Gaussian

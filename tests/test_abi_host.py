@@ -103,10 +103,10 @@ def test_workspace_sizes():
     assert B.gs_compact_workspace_bytes(10**6) >= 4 * (10**6 // 256)
     assert B.gs_loss_workspace_bytes(100) >= 8
     # raster-ready lists: per entry 2 quadrant records (48 B), gradient slots (48 B) and slot
-    # stamps (8 B); 4 quadrant bits and 4 prefix counts per 64 entries; the first gradient
+    # stamps (4 B); 4 quadrant bits and 4 prefix counts per 64 entries; the first gradient
     # slot per Gaussian (+ the total); the raster order of the 4 quadrant waves per tile
     r0 = B.gs_bins_raster_bytes(5000, 64 * 1000, 1920, 1080)
-    lo = 2 * (48 + 48 + 8) * 64000 + 4 * 8 * 1000 + 4 * 4 * 1001 + 4 * 5001 + 4 * 4 * 8160
+    lo = 2 * (48 + 48 + 4) * 64000 + 4 * 8 * 1000 + 4 * 4 * 1001 + 4 * 5001 + 4 * 4 * 8160
     assert lo <= r0 <= lo + 8 * 256
     assert B.gs_bins_raster_bytes(0, 0, 16, 16) > 0 and B.gs_bins_raster_bytes(0, -1, 16, 16) == 0
 
@@ -166,7 +166,7 @@ def test_fused_l1_argument_errors_before_launch():
     with pytest.raises(B.GsError) as e:   # no tile lists
         B._check(B._lib.gs_raster_fused_l1(ctypes.byref(g), ctypes.byref(bins), ctypes.byref(_cam()),
                                            ctypes.byref(B.make_params(0)), None, None, None, None, None, None,
-                                           ws.ptr, 16, None))
+                                           None, ws.ptr, 16, None))
     assert e.value.status == B.GS_ERR_INVALID_ARGUMENT
     with pytest.raises(B.GsError) as e:
         B._check(B._lib.gs_tile_budget_report(ctypes.byref(bins), ctypes.byref(_cam()), -1, None, None, None, None))
