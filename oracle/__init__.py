@@ -231,6 +231,43 @@ def loss_l1(color, target):
     return loss, G
 
 
+def ssim(x, y, radius=5, sigma=1.5, c1=1e-4, c2=9e-4, want_map=False, want_grad=False):
+    """Mean SSIM of two [H][W][3] images (the reading in gs_oracle.c), optionally with the
+    per-pixel map and d SSIM / d x.  Returns (ssim, map or None, grad or None)."""
+    L = lib()
+    a = _np(x, np.float32)
+    b = _np(y, np.float32)
+    assert a.shape == b.shape and a.ndim == 3 and a.shape[2] == 3
+    H, W = a.shape[:2]
+    smap = np.zeros(a.shape) if want_map else None
+    grad = np.zeros(a.shape) if want_grad else None
+    f = L.orc_ssim
+    f.restype = ctypes.c_double
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double,
+                  ctypes.c_double, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
+    val = f(W, H, a.ctypes.data, b.ctypes.data, radius, sigma, c1, c2,
+            None if smap is None else smap.ctypes.data, None if grad is None else grad.ctypes.data)
+    return val, smap, grad
+
+
+def loss_l1_dssim(color, target, lam):
+    """(1 - lam) L1 + lam (1 - SSIM) / 2 of two [H][W][3] images.  Returns (loss, G [H][W][3]
+    float64 = dL/dcolor, ssim)."""
+    L = lib()
+    c = _np(color, np.float32)
+    t = _np(target, np.float32)
+    assert c.shape == t.shape and c.ndim == 3 and c.shape[2] == 3
+    H, W = c.shape[:2]
+    G = np.zeros(c.shape)
+    s = ctypes.c_double(0.0)
+    f = L.orc_loss_l1_dssim
+    f.restype = ctypes.c_double
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
+                  ctypes.POINTER(ctypes.c_double)]
+    loss = f(W, H, c.ctypes.data, t.ctypes.data, float(lam), G.ctypes.data, ctypes.byref(s))
+    return loss, G, s.value
+
+
 def adam(p, g, m, v, lr, b1, b2, eps, step):
     L = lib()
     p, g, m, v = (_np(x, np.float64).reshape(-1) for x in (p, g, m, v))

@@ -906,6 +906,137 @@ double orc_loss_l1(int64_t n_px, const float *color, const float *target, double
     return m > 0 ? s / (double)m : 0.0;
 }
 
+/* ------------------------------------------------------- structural loss */
+
+/*
+ * SSIM and the D-SSIM term of the objective.  The pages give the objective
+ * ("Scaling 3D Gaussian Splatting with Distributed Compute", section "Why gsplat
+ * Cannot Just Use DDP": L = (1 - lambda) L1 + lambda (1 - SSIM(I_r, I_gt)) / 2;
+ * Splaxel section 2 "Parameter Optimization": the structural dissimilarity derived
+ * from SSIM; ByteSplat Eq. 2) but not the SSIM window or constants.  Reading:
+ *   - per colour channel, a (2r+1) x (2r+1) window w(u, v) = g(u) g(v) with
+ *     g(u) = exp(-u^2 / (2 sigma^2)) normalised to sum 1 over |u| <= r
+ *     (r = 5, sigma = 1.5);
+ *   - pixels outside the image count as 0 (zero padding), every window keeps its
+ *     full weights;
+ *   - at pixel p: mu_x = sum w x, e_xx = sum w x^2, e_xy = sum w x y (and the same
+ *     for y), s_xx = e_xx - mu_x^2, s_xy = e_xy - mu_x mu_y,
+ *     S(p) = (2 mu_x mu_y + C1)(2 s_xy + C2) / ((mu_x^2 + mu_y^2 + C1)(s_xx + s_yy + C2))
+ *     with C1 = 0.01^2, C2 = 0.03^2 (unit dynamic range);
+ *   - SSIM = the mean of S over the H W pixels and 3 channels.
+ * Images are [H][W][3] float; everything is computed in double by direct sums
+ * over each window.  Returns the mean SSIM; smap [H][W][3] (nullable) receives S;
+ * grad [H][W][3] (nullable) receives d SSIM / d x (x = the first image), by the
+ * chain rule through mu_x, e_xx and e_xy of every window that holds the pixel.
+ */
+static void ssim_window(int r, double sigma, double *g)
+{
+    double sum = 0.0;
+    for (int u = -r; u <= r; ++u) {
+        g[u + r] = exp(-(double)(u * u) / (2.0 * sigma * sigma));
+        sum += g[u + r];
+    }
+    for (int u = -r; u <= r; ++u) g[u + r] /= sum;
+}
+
+double orc_ssim(int W, int H, const float *x, const float *y, int r, double sigma, double C1, double C2,
+                double *smap, double *grad)
+{
+    if (W <= 0 || H <= 0 || r < 0 || r > 64) return NAN;
+    double g[129];
+    ssim_window(r, sigma, g);
+    const int64_t np = (int64_t)W * H * 3;
+    /* per pixel and channel: dS/dmu_x (total, through s_xx and s_xy too), dS/de_xx, dS/de_xy */
+    double *dm = NULL, *dexx = NULL, *dexy = NULL;
+    if (grad) {
+        dm = (double *)calloc((size_t)np, sizeof(double));
+        dexx = (double *)calloc((size_t)np, sizeof(double));
+        dexy = (double *)calloc((size_t)np, sizeof(double));
+    }
+    double total = 0.0;
+    for (int py = 0; py < H; ++py)
+        for (int px = 0; px < W; ++px)
+            for (int c = 0; c < 3; ++c) {
+                double mx = 0, my = 0, exx = 0, eyy = 0, exy = 0;
+                for (int v = -r; v <= r; ++v)
+                    for (int u = -r; u <= r; ++u) {
+                        const int qx = px + u, qy = py + v;
+                        if (qx < 0 || qx >= W || qy < 0 || qy >= H) continue;   /* zero padding */
+                        const double w = g[u + r] * g[v + r];
+                        const int64_t q = ((int64_t)qy * W + qx) * 3 + c;
+                        const double a = x[q], b = y[q];
+                        mx += w * a; my += w * b;
+                        exx += w * a * a; eyy += w * b * b; exy += w * a * b;
+                    }
+                const double sxx = exx - mx * mx, syy = eyy - my * my, sxy = exy - mx * my;
+                const double n1 = 2.0 * mx * my + C1, n2 = 2.0 * sxy + C2;
+                const double d1 = mx * mx + my * my + C1, d2 = sxx + syy + C2;
+                const double S = (n1 * n2) / (d1 * d2);
+                const int64_t p = ((int64_t)py * W + px) * 3 + c;
+                if (smap) smap[p] = S;
+                total += S;
+                if (grad) {
+                    /* partials with mu_x, s_xx, s_xy as independent variables */
+                    const double dS_dmx = S * (2.0 * my / n1 - 2.0 * mx / d1);
+                    const double dS_dsxx = -S / d2;
+                    const double dS_dsxy = 2.0 * S / n2;
+                    /* s_xx = e_xx - mu_x^2, s_xy = e_xy - mu_x mu_y */
+                    dm[p] = dS_dmx + dS_dsxx * (-2.0 * mx) + dS_dsxy * (-my);
+                    dexx[p] = dS_dsxx;
+                    dexy[p] = dS_dsxy;
+                }
+            }
+    const double inv = 1.0 / (double)np;
+    if (grad) {
+        /* d mu_x(p)/d x(q) = w(q - p); d e_xx(p)/d x(q) = 2 w(q - p) x(q); d e_xy(p)/d x(q) = w(q - p) y(q) */
+        for (int qy = 0; qy < H; ++qy)
+            for (int qx = 0; qx < W; ++qx)
+                for (int c = 0; c < 3; ++c) {
+                    const int64_t q = ((int64_t)qy * W + qx) * 3 + c;
+                    double acc = 0.0;
+                    for (int v = -r; v <= r; ++v)
+                        for (int u = -r; u <= r; ++u) {
+                            const int px = qx - u, py = qy - v;   /* windows centred at p hold q */
+                            if (px < 0 || px >= W || py < 0 || py >= H) continue;
+                            const double w = g[u + r] * g[v + r];
+                            const int64_t p = ((int64_t)py * W + px) * 3 + c;
+                            acc += w * (dm[p] + 2.0 * (double)x[q] * dexx[p] + (double)y[q] * dexy[p]);
+                        }
+                    grad[q] = acc * inv;
+                }
+        free(dm);
+        free(dexx);
+        free(dexy);
+    }
+    return total * inv;
+}
+
+/* The objective with both terms ("Scaling 3D Gaussian Splatting with Distributed
+ * Compute", "Why gsplat Cannot Just Use DDP"; ByteSplat Eq. 2):
+ *   L = (1 - lambda) mean |C - C*| + lambda (1 - SSIM(C, C*)) / 2
+ * over the 3 H W colour values, with SSIM as orc_ssim (r = 5, sigma = 1.5,
+ * C1 = 0.01^2, C2 = 0.03^2; reading) and sign(0) = 0 in the L1 gradient.
+ * G [H][W][3] (nullable) receives dL/dC.  Returns L; *ssim_out (nullable) the SSIM. */
+double orc_loss_l1_dssim(int W, int H, const float *color, const float *target, double lambda, double *G,
+                         double *ssim_out)
+{
+    const int64_t np = (int64_t)W * H * 3;
+    double *gs = G ? (double *)calloc((size_t)np, sizeof(double)) : NULL;
+    const double ssim = orc_ssim(W, H, color, target, 5, 1.5, 1e-4, 9e-4, NULL, gs);
+    double l1 = 0.0;
+    for (int64_t i = 0; i < np; ++i) {
+        const double d = (double)color[i] - (double)target[i];
+        l1 += fabs(d);
+        if (G) {
+            const double sg = d > 0.0 ? 1.0 : (d < 0.0 ? -1.0 : 0.0);
+            G[i] = (1.0 - lambda) * sg / (double)np - 0.5 * lambda * gs[i];
+        }
+    }
+    free(gs);
+    if (ssim_out) *ssim_out = ssim;
+    return (1.0 - lambda) * l1 / (double)np + lambda * (1.0 - ssim) / 2.0;
+}
+
 /* ----------------------------------------------------------------- Adam */
 
 /* Textbook bias-corrected Adam (reading: the pages name Adam with betas

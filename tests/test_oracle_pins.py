@@ -656,6 +656,91 @@ def test_l1_loss_matches_torch():
 
 # ------------------------------------------------------------------ P16 compaction
 
+# ------------------------------------------------------------------ SSIM / D-SSIM (reading)
+
+def _rand_img(seed, h, w):
+    return np.random.default_rng(seed).uniform(0.0, 1.0, size=(h, w, 3)).astype(np.float32)
+
+
+def test_ssim_identity_symmetry_and_constant_images():
+    """[gsplat] "Why gsplat Cannot Just Use DDP" (L = (1 - lambda) L1 + lambda (1 - SSIM)/2)
+    with the SSIM reading of the oracle: SSIM(x, x) = 1 at every pixel with a zero gradient
+    there (the maximum); SSIM(x, y) = SSIM(y, x); for constant images a and b, every pixel
+    whose window lies inside the image has S = (2ab + C1) / (a^2 + b^2 + C1)."""
+    x, y = _rand_img(1, 17, 23), _rand_img(2, 17, 23)
+    s, smap, g = oracle.ssim(x, x, want_map=True, want_grad=True)
+    assert abs(s - 1.0) < 1e-12 and np.abs(smap - 1.0).max() < 1e-12
+    assert np.abs(g).max() < 1e-12
+    assert abs(oracle.ssim(x, y)[0] - oracle.ssim(y, x)[0]) < 1e-14
+    assert oracle.ssim(x, y)[0] < 0.5
+    a, b = 0.3, 0.8
+    ca = np.full((20, 20, 3), a, np.float32)
+    cb = np.full((20, 20, 3), b, np.float32)
+    _, smap, _ = oracle.ssim(ca, cb, want_map=True)
+    a32, b32 = float(np.float32(a)), float(np.float32(b))
+    want = (2 * a32 * b32 + 1e-4) / (a32 ** 2 + b32 ** 2 + 1e-4)
+    assert np.abs(smap[5:15, 5:15] - want).max() < 1e-12
+
+
+def test_ssim_window_and_zero_padding_against_scipy():
+    """The window reading (11 x 11 Gaussian, sigma 1.5, normalised over its support; zero
+    outside the image): for constant images a, b the window statistics reduce to the window
+    mass m(p) inside the image, mu_x = a m, s_xx = a^2 m (1 - m), s_xy = a b m (1 - m), and
+    m is what scipy's gaussian filter (sigma 1.5, radius 5, zero padding) gives for an image
+    of ones; S(p) must equal the closed form built from that m at every pixel."""
+    from scipy.ndimage import gaussian_filter
+    h, w = 14, 19
+    a, b = float(np.float32(0.25)), float(np.float32(0.7))
+    m = gaussian_filter(np.ones((h, w)), sigma=1.5, mode="constant", cval=0.0, truncate=5 / 1.5)
+    mx, my = a * m, b * m
+    sxx, syy, sxy = a * a * m * (1 - m), b * b * m * (1 - m), a * b * m * (1 - m)
+    C1, C2 = 1e-4, 9e-4
+    want = (2 * mx * my + C1) * (2 * sxy + C2) / ((mx ** 2 + my ** 2 + C1) * (sxx + syy + C2))
+    _, smap, _ = oracle.ssim(np.full((h, w, 3), a, np.float32), np.full((h, w, 3), b, np.float32), want_map=True)
+    for c in range(3):
+        assert np.abs(smap[..., c] - want).max() < 1e-12
+    assert want.min() < want.max() - 0.05     # the border pixels differ from the interior
+
+
+def test_ssim_gradient_finite_differences():
+    """d SSIM / d x by central differences in double (the oracle takes float images, so the
+    difference quotient is taken on the oracle's own exact function of the float inputs
+    through a perturbation of representable size)."""
+    h, w = 9, 11
+    x, y = _rand_img(3, h, w), _rand_img(4, h, w)
+    _, _, g = oracle.ssim(x, y, want_grad=True)
+    rng = np.random.default_rng(5)
+    checked = 0
+    for _ in range(40):
+        i, j, c = rng.integers(h), rng.integers(w), rng.integers(3)
+        eps = 2.0 ** -12
+        xp, xm = x.copy(), x.copy()
+        xp[i, j, c] += eps
+        xm[i, j, c] -= eps
+        num = (oracle.ssim(xp, y)[0] - oracle.ssim(xm, y)[0]) / (2 * eps)
+        assert abs(num - g[i, j, c]) <= 1e-6 * max(1e-3, abs(g[i, j, c])) + 1e-9, (i, j, c, num, g[i, j, c])
+        checked += 1
+    assert checked == 40
+
+
+def test_l1_dssim_loss_and_gradient():
+    """L = (1 - lambda) mean|C - C*| + lambda (1 - SSIM) / 2 and its gradient: lambda = 0 is
+    the L1 term (torch autograd of l1_loss, mean reduction); lambda = 1 is the D-SSIM term
+    (-1/2 d SSIM / dC); in between, the weighted sum."""
+    h, w = 8, 10
+    c, t = _rand_img(6, h, w), _rand_img(7, h, w)
+    s = oracle.ssim(c, t, want_grad=True)
+    ct = torch.tensor(c.astype(np.float64), requires_grad=True)
+    l1 = torch.nn.functional.l1_loss(ct, torch.tensor(t.astype(np.float64)))
+    l1.backward()
+    for lam in (0.0, 0.2, 1.0):
+        loss, G, ss = oracle.loss_l1_dssim(c, t, lam)
+        assert abs(ss - s[0]) < 1e-15
+        assert abs(loss - ((1 - lam) * float(l1.detach()) + lam * (1 - s[0]) / 2)) < 1e-14
+        want_G = (1 - lam) * ct.grad.numpy() - 0.5 * lam * s[2]
+        assert np.abs(G - want_G).max() < 1e-15
+
+
 def test_compaction_invariants():
     """[ByteSplat sec. 6]: records of Gaussians with any non-zero field, ascending index;
     scattering them back reproduces the dense gradients bit for bit (elision is exact)."""
