@@ -28,7 +28,8 @@ GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP 
 TILE = 16
 EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_bin_sort_async", "gs_raster_fwd", "gs_loss_workspace_bytes",
             "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project",
-            "gs_raster_fused_l1", "gs_raster_fused_l1_workspace_bytes", "gs_tile_budget", "gs_tile_budget_report",
+            "gs_raster_fused_l1", "gs_raster_fused_l1_workspace_bytes", "gs_raster_fused_l1_noalloc",
+            "gs_tile_budget", "gs_tile_budget_report",
             "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_decode_grads", "gs_project_batch",
             "gs_grad_aggregate_adam_batch", "gs_adam_batch_hparams", "gs_last_error")
@@ -119,6 +120,8 @@ _SIGS = {
     "gs_raster_fused_l1": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "gs_raster_fused_l1_workspace_bytes": (ctypes.c_size_t, [_i32, _i32]),
+    "gs_raster_fused_l1_noalloc": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp,
+                                          _vp, _vp, _vp, _vp, _vp]),
     "gs_tile_budget": (_i64, [_i64, _i64, _i64]),
     "gs_tile_budget_report": (_i32, [_P(Bins), _P(Camera), _i64, _vp, _vp, _vp, _vp]),
     "gs_project_bwd": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads), _vp]),
@@ -299,6 +302,16 @@ def gs_raster_fused_l1(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, targ
                                    _ptr(color), _ptr(t_final), _ptr(n_trav), _ptr(loss_out), _ptr(n_trav_sum),
                                    _ptr(walk_counts), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)))
+
+
+FUSED_NOALLOC_MAX_WAVES = 256 * 256 * 4
+
+
+def gs_raster_fused_l1_noalloc(g: Gaussians, b: Bins, cam: Camera, p: RasterParams, target, color, t_final, n_trav,
+                               loss_out, n_trav_sum, stream=None, walk_counts=None):
+    _check(_lib.gs_raster_fused_l1_noalloc(ctypes.byref(g), ctypes.byref(b), ctypes.byref(cam), ctypes.byref(p),
+                                           _ptr(target), _ptr(color), _ptr(t_final), _ptr(n_trav), _ptr(loss_out),
+                                           _ptr(n_trav_sum), _ptr(walk_counts), _stream(stream)))
 
 
 def gs_tile_budget(lds_budget_bytes, fixed_bytes, bytes_per_gaussian) -> int:

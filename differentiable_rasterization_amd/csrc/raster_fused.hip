@@ -18,6 +18,8 @@
 // chip, B = floor((M_budget - M_fixed) / M_g) records fit per tile, E_t = max(0, N_t - B)
 // would have to be pruned from tile t and P_t = E_t / N_t (0 for an empty tile).
 // k_tile_budget computes E_t and P_t from the tile lists and the totals.
+#include <mutex>
+
 #include "kernels.h"
 #include "raster_walk.h"
 
@@ -256,11 +258,12 @@ extern "C" size_t gs_raster_fused_l1_workspace_bytes(int32_t width, int32_t heig
     return fused_ws(width, height).bytes;
 }
 
-extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
-                                        const gs_raster_params *p, const float *target, float *color, float *t_final,
-                                        int32_t *n_trav, float *loss_out, unsigned long long *n_trav_sum,
-                                        unsigned long long *walk_counts, void *workspace, size_t workspace_bytes,
-                                        hipStream_t stream)
+namespace {
+
+// Both entry points: the checks, then the two launches with the workspace at wsb.
+gs_status fused_checks(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam, const gs_raster_params *p,
+                       const float *target, float *color, float *t_final, int32_t *n_trav,
+                       unsigned long long *walk_counts)
 {
     using namespace gsi;
     gs_status s;
@@ -269,21 +272,25 @@ extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bi
     if ((s = check_params(p)) != GS_OK) return s;
     if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
     if (!target || !color || !t_final || !n_trav) return fail(GS_ERR_INVALID_ARGUMENT, "an image pointer is NULL");
-    const size_t need = gs_raster_fused_l1_workspace_bytes(cam->width, cam->height);
-    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
-        return fail(GS_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, 16-byte aligned", need);
+    if (walk_counts && !aligned(walk_counts, 8))
+        return fail(GS_ERR_INVALID_ARGUMENT, "walk_counts must be 8-byte aligned");
+    return GS_OK;
+}
+
+gs_status fused_launch(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam, const gs_raster_params *p,
+                       const float *target, float *color, float *t_final, int32_t *n_trav, float *loss_out,
+                       unsigned long long *n_trav_sum, unsigned long long *walk_counts, char *wsb, hipStream_t stream)
+{
+    using namespace gsi;
     const int TX = tiles_x(cam->width), T = TX * tiles_y(cam->height);
     const RasterLayout L = raster_layout(g->n, bins->capacity, T);
     char *rb = static_cast<char *>(bins->raster);
     BinsHeader *hdr = reinterpret_cast<BinsHeader *>(rb + L.hdr);
     const int64_t m = 3 * (int64_t)cam->width * cam->height;
     const FusedWs fw = fused_ws(cam->width, cam->height);
-    char *wsb = static_cast<char *>(workspace);
     FusedPartial *part = reinterpret_cast<FusedPartial *>(wsb + fw.part);
     FusedPartial *block_part = reinterpret_cast<FusedPartial *>(wsb + fw.block_part);
     uint32_t *ticket = reinterpret_cast<uint32_t *>(wsb + fw.ticket);
-    if (walk_counts && !aligned(walk_counts, 8))
-        return fail(GS_ERR_INVALID_ARGUMENT, "walk_counts must be 8-byte aligned");
     auto kern = walk_counts ? k_raster_fused_l1<true> : k_raster_fused_l1<false>;
     kern<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
         bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order),
@@ -297,6 +304,80 @@ extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bi
                                                           loss_out, n_trav_sum);
     GS_LAUNCH_CHECK("k_fused_final");
     return GS_OK;
+}
+
+// ------------------------------------------------------------------ without allocation
+//
+// The workspace of gs_raster_fused_l1_noalloc: a file-scope device array, one copy per GPU
+// (the per-wave partials, the per-block sums and the ticket of an image of up to
+// kNoAllocMaxWaves quadrant waves, 4096 x 4096 pixels).  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, taken once per device with that device
+// current and kept in scratch_ptr.
+constexpr int kNoAllocMaxWaves = 256 * 256 * gsr::kQuads;
+constexpr size_t kNoAllocScratchBytes = ((size_t)kNoAllocMaxWaves * sizeof(FusedPartial) +
+                                         (size_t)((kNoAllocMaxWaves + kFinalSpan - 1) / kFinalSpan) *
+                                             sizeof(FusedPartial) + 16 + 255) & ~size_t(255);
+
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+char *scratch_ptr[kMaxDevices] = {};
+
+gs_status scratch_of_current_device(char **out)
+{
+    int dev = -1;
+    GS_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return gsi::fail(GS_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        GS_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) return gsi::fail(GS_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+        scratch_ptr[dev] = static_cast<char *>(ptr);
+    }
+    *out = scratch_ptr[dev];
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                        const gs_raster_params *p, const float *target, float *color, float *t_final,
+                                        int32_t *n_trav, float *loss_out, unsigned long long *n_trav_sum,
+                                        unsigned long long *walk_counts, void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if ((s = fused_checks(g, bins, cam, p, target, color, t_final, n_trav, walk_counts)) != GS_OK) return s;
+    const size_t need = gs_raster_fused_l1_workspace_bytes(cam->width, cam->height);
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < need)
+        return fail(GS_ERR_INVALID_ARGUMENT, "workspace needs %zu bytes, 16-byte aligned", need);
+    return fused_launch(g, bins, cam, p, target, color, t_final, n_trav, loss_out, n_trav_sum, walk_counts,
+                        static_cast<char *>(workspace), stream);
+}
+
+extern "C" gs_status gs_raster_fused_l1_noalloc(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                                const gs_raster_params *p, const float *target, float *color,
+                                                float *t_final, int32_t *n_trav, float *loss_out,
+                                                unsigned long long *n_trav_sum, unsigned long long *walk_counts,
+                                                hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if ((s = fused_checks(g, bins, cam, p, target, color, t_final, n_trav, walk_counts)) != GS_OK) return s;
+    const size_t need = gs_raster_fused_l1_workspace_bytes(cam->width, cam->height);
+    if (need > kNoAllocScratchBytes)
+        return fail(GS_ERR_UNSUPPORTED,
+                    "a %d x %d image needs %zu bytes of workspace; the static scratch holds %zu (at most %d quadrant "
+                    "waves, 4096 x 4096 pixels): use gs_raster_fused_l1 with a workspace",
+                    cam->width, cam->height, need, kNoAllocScratchBytes, kNoAllocMaxWaves);
+    char *wsb = nullptr;
+    if ((s = scratch_of_current_device(&wsb)) != GS_OK) return s;
+    return fused_launch(g, bins, cam, p, target, color, t_final, n_trav, loss_out, n_trav_sum, walk_counts, wsb,
+                        stream);
 }
 
 extern "C" int64_t gs_tile_budget(int64_t lds_budget_bytes, int64_t fixed_bytes, int64_t bytes_per_gaussian)

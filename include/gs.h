@@ -295,6 +295,21 @@ gs_status gs_raster_fused_l1(const gs_gaussians *g, const gs_bins *bins, const g
                              unsigned long long *walk_counts, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* gs_raster_fused_l1 for callers that cannot allocate device memory or be handed a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the per-wave partial sums in a
+ * file-scope device array of the library (GS_FUSED_NOALLOC_MAX_WAVES quadrant waves,
+ * i.e. images of up to 4096 x 4096 pixels; about 4 MiB held by each GPU the library runs
+ * on until the process ends).  Calls no allocation routine.  Larger images return
+ * GS_ERR_UNSUPPORTED.  Every call on one GPU uses that GPU's one array: calls that overlap
+ * on one GPU (other streams, other threads) race and must be serialised by the caller.
+ * The array's contents are not needed between calls (each call rewrites what it reads). */
+#define GS_FUSED_NOALLOC_MAX_WAVES (256 * 256 * 4)
+gs_status gs_raster_fused_l1_noalloc(const gs_gaussians *g, const gs_bins *bins, const gs_camera *cam,
+                                     const gs_raster_params *p, const float *target, float *color, float *t_final,
+                                     int32_t *n_trav, float *loss_out, unsigned long long *n_trav_sum,
+                                     unsigned long long *walk_counts, hipStream_t stream);
+
 /* Tile budget diagnostic (ByteSplat section 5.2, Eq. 7-9).  gs_tile_budget: B =
  * floor((lds_budget_bytes - fixed_bytes) / bytes_per_gaussian), the number of Gaussian
  * records a tile can keep on chip in a design that holds them there (Eq. 7); -1 for
