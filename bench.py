@@ -147,6 +147,9 @@ def parse():
     ap.add_argument("--serial-views", action="store_true",
                     help="with --batch: bin and rasterize the views one after another on one stream instead of one "
                          "stream per view")
+    ap.add_argument("--loss", choices=["l1", "l1_dssim"], default="l1",
+                    help="l1_dssim: (1 - lambda) L1 + lambda (1 - SSIM)/2 with lambda 0.2 (gs_loss_l1_dssim) between "
+                         "the separate forward and backward raster calls")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a copy-like kernel over this many MiB before timing (counter normalisation)")
     return ap.parse_args()
@@ -743,6 +746,8 @@ def main():
         graphs = [PL.BinSortGraph(st.bins, st.proj, cams[v], st.raster, view_counts[v], acc) for v in range(nviews)]
     use_graph = [graphs is not None]
 
+    if args.loss == "l1_dssim":
+        args.separate_raster = True   # the structural term needs the whole image before the backward
     if args.unfused:
         names = ["project", "bin_sort", "raster_fwd", "loss", "raster_bwd", "grad_aggregate", "project_bwd", "adam"]
     elif args.separate_raster:   # the projection of each step runs in the previous step's last pass
@@ -788,7 +793,10 @@ def main():
             return
         B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.n_trav_sum)
         rec(k + 2)
-        B.gs_loss_l1(f.color, t, f.n_px, f.loss, f.dL_dcolor, f.loss_ws)
+        if args.loss == "l1_dssim":
+            st.loss_dssim(t, 0.2)
+        else:
+            B.gs_loss_l1(f.color, t, f.n_px, f.loss, f.dL_dcolor, f.loss_ws)
         rec(k + 3)
         B.gs_raster_bwd_partials(g, st.bins.abi(), c, st.raster, f.color, f.t_final, f.n_trav, f.dL_dcolor, None)
         rec(k + 4)
@@ -925,6 +933,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H],
                    "views": nviews,
+                   "loss": "L1" if args.loss == "l1" else "(1 - 0.2) L1 + 0.2 (1 - SSIM) / 2",
                    "step": "one view: projection + fwd + L1 + bwd + Adam" + (
                        "" if args.unfused else " (each view's projection fused into the previous step's Adam pass"
                        + ("" if args.separate_raster else "; fwd + L1 + bwd in one kernel") + ")"),

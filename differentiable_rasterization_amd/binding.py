@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_UNSUPPORTED, GS_ERR_CAPACITY, GS_ERR_HIP = range(5)
 TILE = 16
 EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes", "gs_bin_sort", "gs_bin_sort_async", "gs_raster_fwd", "gs_loss_workspace_bytes",
-            "gs_loss_l1", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project",
+            "gs_loss_l1", "gs_loss_l1_dssim", "gs_loss_l1_dssim_workspace_bytes", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project",
             "gs_raster_fused_l1", "gs_raster_fused_l1_workspace_bytes", "gs_raster_fused_l1_noalloc",
             "gs_tile_budget", "gs_tile_budget_report",
             "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
@@ -105,6 +105,8 @@ _SIGS = {
     "gs_raster_fwd": (_i32, [_P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp]),
     "gs_loss_workspace_bytes": (_sz, [_i64]),
     "gs_loss_l1": (_i32, [_vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "gs_loss_l1_dssim_workspace_bytes": (_sz, [_i32, _i32]),
+    "gs_loss_l1_dssim": (_i32, [_vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gs_raster_bwd": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp,
                              _vp, _vp, _vp, _P(ParamGrads), _vp]),
     "gs_raster_bwd_partials": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp,
@@ -290,6 +292,16 @@ def gs_grad_aggregate_adam_project(g: Gaussians, proj: Projected, b: Bins, cam: 
                                                ctypes.byref(cam), ctypes.byref(p), _ptr(grads2d), ctypes.byref(m),
                                                ctypes.byref(v), ctypes.byref(lr), step, beta1, beta2, eps,
                                                ctypes.byref(next_cam), ctypes.byref(next_proj), _stream(stream)))
+
+
+def gs_loss_l1_dssim_workspace_bytes(width, height) -> int:
+    return int(_lib.gs_loss_l1_dssim_workspace_bytes(width, height))
+
+
+def gs_loss_l1_dssim(color, target, width, height, lam, loss_out, ssim_out, dL_dcolor, workspace, stream=None):
+    _check(_lib.gs_loss_l1_dssim(_ptr(color), _ptr(target), int(width), int(height), float(lam), _ptr(loss_out),
+                                 _ptr(ssim_out), _ptr(dL_dcolor), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def gs_raster_fused_l1_workspace_bytes(width, height) -> int:

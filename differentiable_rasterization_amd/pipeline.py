@@ -182,6 +182,8 @@ class Frame:
         # running sum of N_p (Gaussian-pixel evaluations) over forward passes; cleared by the caller
         self.n_trav_sum = torch.zeros(1, dtype=torch.int64, device=device)
         self.loss_ws = torch.empty(max(B.gs_loss_workspace_bytes(self.n_px), 8), dtype=torch.uint8, device=device)
+        self.ssim = torch.zeros(1, dtype=torch.float32, device=device)
+        self.ssim_ws = None   # allocated on the first D-SSIM loss
         # per-wave partial sums of the fused forward + L1 + backward
         self.fused_ws = torch.empty(max(B.gs_raster_fused_l1_workspace_bytes(width, height), 16),
                                     dtype=torch.uint8, device=device)
@@ -215,6 +217,15 @@ class TrainStep:
     def loss(self, target, stream=None):
         f = self.frame
         B.gs_loss_l1(f.color, target, f.n_px, f.loss, f.dL_dcolor, f.loss_ws, stream)
+
+    def loss_dssim(self, target, lam=0.2, stream=None):
+        """(1 - lam) L1 + lam (1 - SSIM) / 2 into frame.loss (and frame.ssim), its gradient into
+        frame.dL_dcolor; follow with backward_partials and the end-of-step pass."""
+        f = self.frame
+        if f.ssim_ws is None:
+            f.ssim_ws = torch.empty(B.gs_loss_l1_dssim_workspace_bytes(f.width, f.height), dtype=torch.uint8,
+                                    device=f.color.device)
+        B.gs_loss_l1_dssim(f.color, target, f.width, f.height, lam, f.loss, f.ssim, f.dL_dcolor, f.ssim_ws, stream)
 
     def backward_raster(self, cam: B.Camera, dL_dcolor=None, dL_dt=None, stream=None):
         f = self.frame
@@ -387,6 +398,8 @@ class PartitionedStep:
         self.color, self.t_final = z(height, width, 3), z(height, width)
         self.loss_value, self.dL_dcolor = z(1), z(height, width, 3)
         self.loss_ws = torch.empty(max(B.gs_loss_workspace_bytes(self.n_px), 8), dtype=torch.uint8, device=device)
+        self.ssim = torch.zeros(1, dtype=torch.float32, device=device)
+        self.ssim_ws = None   # allocated on the first D-SSIM loss
         self.dcs = [z(height, width, 3) for _ in self.parts]
         self.dts = [z(height, width) for _ in self.parts]
         self.records, self.bitmaps, self.compact_ws, self.owner_g2, self.r = [], [], [], [], []

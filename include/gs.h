@@ -15,6 +15,7 @@
  *                                             ("Projection", "Sorting")
  *   front-to-back compositing -> gs_raster_fwd  ByteSplat section 2.1, Eq. 1
  *   L1 loss                   -> gs_loss_l1      ByteSplat Eq. 2 (L1 term); ROCm blog, loss
+ *   L1 + D-SSIM loss          -> gs_loss_l1_dssim  ROCm blog, loss; Splaxel section 2
  *   backward rasterization    -> gs_raster_bwd   ByteSplat section 2.1, Eq. 3 and Eq. 4, then
  *                                                the backward through projection and colour
  *   parameter update          -> gs_adam_step    ROCm blog, create_splats_with_optimizers
@@ -229,6 +230,23 @@ size_t gs_loss_workspace_bytes(int64_t n_px);
  * double.  workspace: gs_loss_workspace_bytes(n_px) bytes of device memory. */
 gs_status gs_loss_l1(const float *color, const float *target, int64_t n_px, float *loss_out,
                      float *dL_dcolor, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The objective with its structural term (ROCm blog, "Why gsplat Cannot Just Use DDP":
+ * L = (1 - lambda) mean |C - C*| + lambda (1 - SSIM(C, C*)) / 2 over the 3 W H colour
+ * values; Splaxel section 2 "Parameter Optimization"; ByteSplat Eq. 2) and dL/dC.  The
+ * pages fix neither the SSIM window nor its constants; this library reads them as: per
+ * colour channel, an 11 x 11 Gaussian window (sigma 1.5, normalised over its support),
+ * zero padding outside the image, C1 = 0.01^2, C2 = 0.03^2, SSIM = the mean over pixels
+ * and channels of S = (2 mu_x mu_y + C1)(2 s_xy + C2) / ((mu_x^2 + mu_y^2 + C1)(s_xx + s_yy
+ * + C2)); sign(0) = 0 in the L1 term.  color, target, dL_dcolor: [H][W][3]; 0 <= lambda
+ * <= 1 (lambda = 0 is gs_loss_l1's objective); loss_out, ssim_out: device floats (each may
+ * be NULL), the sums taken in double in a fixed order.  workspace:
+ * gs_loss_l1_dssim_workspace_bytes(W, H) bytes (256-byte aligned): three coefficient maps
+ * per channel (36 B per pixel) and per-tile partial sums. */
+size_t gs_loss_l1_dssim_workspace_bytes(int32_t width, int32_t height);
+gs_status gs_loss_l1_dssim(const float *color, const float *target, int32_t width, int32_t height, float lambda,
+                           float *loss_out, float *ssim_out, float *dL_dcolor, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* Backward rasterization (ByteSplat Eq. 3 and Eq. 4): per tile, each pixel walks its
  * traversed entries front to back, recomputing T_i as the forward pass did, takes the

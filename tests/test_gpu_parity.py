@@ -197,6 +197,106 @@ def test_loss_l1_parity(h, w):
 
 # ------------------------------------------------------------------ backward
 
+def _ssim_pair(kind, h, w, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(0.0, 1.0, size=(h, w, 3)).astype(np.float32)
+    if kind == "random":
+        y = rng.uniform(0.0, 1.0, size=(h, w, 3)).astype(np.float32)
+    elif kind == "near":      # SSIM close to 1: small differences, small gradients
+        y = np.clip(x + rng.normal(0.0, 0.01, size=x.shape), 0.0, 1.0).astype(np.float32)
+    else:                     # smooth image with flat regions, against noise
+        yy, xx = np.mgrid[0:h, 0:w]
+        base = 0.5 + 0.4 * np.sin(xx / 13.0)[..., None] * np.cos(yy / 7.0)[..., None] * np.array([1.0, 0.6, 0.2])
+        x = np.where(((xx // 20 + yy // 20) % 2 == 0)[..., None], base, 0.0).astype(np.float32)
+        y = rng.uniform(0.0, 1.0, size=(h, w, 3)).astype(np.float32)
+    return x, y
+
+
+@pytest.mark.parametrize("h,w,lam,kind", [(64, 64, 0.2, "random"), (37, 41, 0.2, "near"), (1, 1, 0.2, "random"),
+                                          (5, 130, 1.0, "smooth"), (16, 64, 0.0, "random"),
+                                          (300, 257, 0.2, "smooth"), (1080, 1920, 0.2, "near")])
+def test_loss_l1_dssim_parity(h, w, lam, kind):
+    """(1 - lambda) L1 + lambda (1 - SSIM)/2 and dL/dC against the oracle's direct window sums
+    (ROCm blog, "Why gsplat Cannot Just Use DDP"), over tiles, ragged edges and the
+    one-pixel image.  Tolerances: the loss and SSIM within 2e-6; dL/dC within relative L2
+    1e-4 of the oracle's, every element within 1e-3 of the largest; the L1 part's sign is
+    decided in float32 on both sides."""
+    log(f"L1 + D-SSIM {h}x{w} lambda={lam} {kind}")
+    x, y = _ssim_pair(kind, h, w, h * 1000 + w)
+    loss_o, G_o, ssim_o = oracle.loss_l1_dssim(x, y, lam)
+    c, t = torch.from_numpy(x).to(DEV), torch.from_numpy(y).to(DEV)
+    out = torch.full((2,), float("nan"), device=DEV)
+    G = torch.full((h, w, 3), float("nan"), device=DEV)
+    ws = torch.empty(B.gs_loss_l1_dssim_workspace_bytes(w, h), dtype=torch.uint8, device=DEV)
+    B.gs_loss_l1_dssim(c, t, w, h, lam, out[0:1], out[1:2], G, ws)
+    torch.cuda.synchronize()
+    loss, ssim = float(out[0]), float(out[1])
+    g = G.cpu().numpy().astype(np.float64)
+    e = rel_l2(g, G_o)
+    emax = float(np.abs(g - G_o).max() / max(np.abs(G_o).max(), 1e-30))
+    log(f"  loss {loss:.8f} (oracle {loss_o:.8f}), SSIM {ssim:.8f} (oracle {ssim_o:.8f}), dL/dC rel-L2 {e:.2e}, "
+        f"max {emax:.2e}")
+    assert abs(loss - loss_o) <= 2e-6 and abs(ssim - ssim_o) <= 2e-6
+    assert e <= 1e-4 and emax <= 1e-3
+    # a second call gives the same bits (fixed summation order)
+    G2 = torch.empty_like(G)
+    out2 = torch.empty_like(out)
+    B.gs_loss_l1_dssim(c, t, w, h, lam, out2[0:1], out2[1:2], G2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(G, G2) and torch.equal(out, out2)
+
+
+def test_loss_l1_dssim_at_lambda_zero_is_the_l1_loss():
+    """lambda = 0 reduces the objective to the L1 term: the gradient equals gs_loss_l1's bit
+    for bit (sign(d) / (3 W H) either way)."""
+    h, w = 45, 70
+    x, y = _ssim_pair("random", h, w, 7)
+    c, t = torch.from_numpy(x).to(DEV), torch.from_numpy(y).to(DEV)
+    G0 = torch.empty(h, w, 3, device=DEV)
+    G1 = torch.empty(h, w, 3, device=DEV)
+    loss = torch.empty(2, device=DEV)
+    ws = torch.empty(B.gs_loss_l1_dssim_workspace_bytes(w, h), dtype=torch.uint8, device=DEV)
+    B.gs_loss_l1_dssim(c, t, w, h, 0.0, loss[0:1], None, G0, ws)
+    lws = torch.empty(max(B.gs_loss_workspace_bytes(h * w), 8), dtype=torch.uint8, device=DEV)
+    B.gs_loss_l1(c, t, h * w, loss[1:2], G1, lws)
+    torch.cuda.synchronize()
+    assert torch.equal(G0, G1)
+    assert abs(float(loss[0]) - float(loss[1])) <= 1e-6 * float(loss[1])
+
+
+@pytest.mark.parametrize("name", ["ragged_sh2", "100k"])
+def test_dssim_training_step_gradients(name):
+    """The training step with the structural term: forward, L1 + D-SSIM loss (lambda 0.2),
+    backward rasterization, per-Gaussian sum and projection backward, against the oracle's
+    render, orc_loss_l1_dssim gradient, raster backward and projection backward."""
+    log(f"D-SSIM training step {name}")
+    sc = _scene(name)
+    cam = sc.cameras[0]
+    rp = B.make_params(sc.sh_degree)
+    op = oracle_params(rp)
+    st = gpu_forward(sc, cam, rp)
+    tgt = sc.targets[0]
+    st.loss_dssim(tgt.to(DEV), 0.2)
+    st.backward_partials(B.camera_from(cam))
+    B.gs_grad_aggregate(st.params.gaussians(), st.proj.abi(), st.bins.abi(), B.camera_from(cam), rp, st.grads2d,
+                        st.params.param_grads())
+    torch.cuda.synchronize()
+    P = oracle.project(sc, cam, op)
+    c, tf, nt, tie = oracle.render(P, op)
+    loss_o, G, ssim_o = oracle.loss_l1_dssim(c.astype(np.float32), tgt.numpy(), 0.2)
+    assert abs(float(st.frame.loss) - loss_o) <= 1e-5 and abs(float(st.frame.ssim) - ssim_o) <= 1e-5
+    g2_o = oracle.raster_backward(P, G, None, op)
+    g3_o = oracle.project_backward(sc, cam, g2_o, op)
+    g2 = st.grads2d.cpu().numpy()
+    errs = {oracle.G_FIELDS[f]: rel_l2(g2[f], g2_o[f]) for f in range(9)}
+    gp = st.params
+    errs3 = {nm: rel_l2(gp.view(gp.grad, nm).cpu().numpy(), g3_o[nm]) for nm in
+             ("means", "log_scales", "quats", "opacity_logits", "sh")}
+    log(f"  loss {float(st.frame.loss):.6f} (oracle {loss_o:.6f}); grads2d rel-L2 max {max(errs.values()):.2e}; "
+        f"grads3d rel-L2 max {max(errs3.values()):.2e}")
+    assert max(errs.values()) <= 1e-3 and max(errs3.values()) <= 1e-3, (errs, errs3)
+
+
 def _oracle_G(c_orc, target):
     """dL/dC of the L1 loss on the oracle's image, as the float32 input both sides use."""
     _, G = oracle.loss_l1(c_orc.astype(np.float32), target)
