@@ -57,24 +57,30 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *wsum)
 
 // Loads Gaussian t of the block (valid: it is listed; otherwise it has no entries) into
 // the shared state and sets the block-local offsets.  Returns the block's entry count.
+// copy (may be NULL): receives the Gaussian's record (its three float4 words).
 __device__ __forceinline__ uint32_t coop_load(Coop &S, bool valid, uint32_t g, const float4 *__restrict__ rec,
-                                              int tx, int ty, uint32_t &c_out)
+                                              int tx, int ty, uint32_t &c_out, float4 *__restrict__ copy = nullptr)
 {
     const int t = threadIdx.x;
     uint32_t c = 0;
-    float4 p0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), p1 = p0;
+    float4 p0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), p1 = p0, p2 = p0;
     int x0 = 0, w = 1;
     int y0 = 0;
     if (valid) {
         p0 = rec[gsr::kRecF4 * (size_t)g];
         p1 = rec[gsr::kRecF4 * (size_t)g + 1];
-        const float4 p2 = rec[gsr::kRecF4 * (size_t)g + 2];
+        p2 = rec[gsr::kRecF4 * (size_t)g + 2];
         int x1, y1;
         gsd::tile_rect(p0.x, p0.y, __float_as_int(p2.z), __float_as_int(p2.w), tx, ty, x0, x1, y0, y1);
         if (x1 > x0 && y1 > y0) {
             c = (uint32_t)((x1 - x0) * (y1 - y0));
             w = x1 - x0;
         }
+    }
+    if (copy) {
+        copy[0] = p0;
+        copy[1] = p1;
+        copy[2] = p2;
     }
     const uint32_t incl = block_incl_scan(c, S.wsum);
     S.off[t] = incl - c;
@@ -159,14 +165,15 @@ __device__ __forceinline__ void coop_count_round(Coop &S, uint32_t e0, uint32_t 
 // Depth keys (culled Gaussians last) in index order, with the values tile count << 32 |
 // index, each Gaussian's quadrant-record count (qcnt [n + 1], qcnt[n] = 0, so that its
 // exclusive scan ends with the total), optionally the tile counts for the caller
-// (touched); also clears the scans' look-back state for this sort (zero: zero_words
-// uint32).
+// (touched), and the copy of every Gaussian's raster record that the raster calls read
+// (grec, 64-byte stride; zeros for culled ones); also clears the scans' look-back state
+// for this sort (zero: zero_words uint32).
 __global__ __launch_bounds__(256) void k_keys_count(const int2 *__restrict__ radii, const float *__restrict__ depth,
                                                     const float4 *__restrict__ rec, float log2_amin, int64_t n,
                                                     int tx, int ty, uint32_t *__restrict__ keys,
                                                     uint64_t *__restrict__ vals, uint32_t *__restrict__ qcnt,
                                                     int32_t *__restrict__ touched, uint32_t *__restrict__ zero,
-                                                    int64_t zero_words)
+                                                    int64_t zero_words, float4 *__restrict__ grec)
 {
     __shared__ Coop S;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -179,7 +186,8 @@ __global__ __launch_bounds__(256) void k_keys_count(const int2 *__restrict__ rad
         keys[i] = vis ? __float_as_uint(depth[i]) : kCulledKey;
     }
     uint32_t c;
-    const uint32_t C = coop_load(S, vis, (uint32_t)i, rec, tx, ty, c);
+    const uint32_t C = coop_load(S, vis, (uint32_t)i, rec, tx, ty, c,
+                                 i < n ? grec + gsr::kGRecF4 * (size_t)i : nullptr);
     for (uint32_t e0 = 0; e0 < C; e0 += 256u) coop_count_round(S, e0, C, log2_amin);
     __syncthreads();
     if (i < n) {
@@ -206,6 +214,7 @@ __device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned lo
 __global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals, const uint32_t *__restrict__ off, const uint32_t *__restrict__ qoff,
                                               const float4 *__restrict__ rec, float log2_amin, int64_t n, int tx,
                                               int ty, const unsigned long long *__restrict__ tot, int64_t cap,
+                                              unsigned long long grec_off,
                                               unsigned long long *__restrict__ klen, gsr::BinsHeader *__restrict__ hdr,
                                               int64_t *__restrict__ counts, uint32_t *__restrict__ tkeys,
                                               uint64_t *__restrict__ tvals)
@@ -220,6 +229,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals
         hdr->Q = Q;
         hdr->ok = ok ? 1u : 0u;
         hdr->epoch = gsr::kSortEpoch;   // the qoff scan zeroed the stamps of slots 0 .. Q
+        hdr->grec_off = grec_off;
         if (counts) {
             counts[0] = (int64_t)K;
             counts[1] = ok ? 0 : (int64_t)need_capacity(K, Q);
@@ -286,14 +296,12 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
     }
 }
 
-// Copies the projected record of every list entry into the record list of each quadrant
-// its box reaches, at the position given by the scanned bit counts, and stamps the entry
-// index and the record's gradient slot into it.  The spare records around the lists are
-// read (never used) by the raster kernels' batches: they are zeroed, so they stay finite.
+// Writes every list entry into the list of each quadrant its box reaches, at the position
+// given by the scanned bit counts: (Gaussian, gradient slot) to qent and the entry's
+// tile-list index to qk.
 // Blocks reach the 8 XCDs round-robin (block b on XCD b % 8).  The first `active` blocks
-// are renumbered so that each XCD takes one contiguous run of them: the entries of
-// neighbouring tiles, which gather the records of largely the same Gaussians, then share
-// one L2.  Returns -1 for blocks past `active`.
+// are renumbered so that each XCD takes one contiguous run of them: neighbouring tiles'
+// entries then share one L2.  Returns -1 for blocks past `active`.
 __device__ __forceinline__ int64_t xcd_contiguous_block(int64_t active)
 {
     const int64_t b = blockIdx.x;
@@ -305,20 +313,9 @@ __device__ __forceinline__ int64_t xcd_contiguous_block(int64_t active)
 __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint64_t *__restrict__ tvals,
                                                     const unsigned long long *__restrict__ klen, int64_t words,
                                                     const uint64_t *__restrict__ bitmap,
-                                                    const uint32_t *__restrict__ wpre,
-                                                    const float4 *__restrict__ prec, float4 *__restrict__ qrec)
+                                                    const uint32_t *__restrict__ wpre, uint2 *__restrict__ qent,
+                                                    uint32_t *__restrict__ qk)
 {
-    constexpr int kPadF4 = gsr::kRecPad * gsr::kRecF4;
-    // per wave: the records of one quadrant list, staged so that the wave writes them as
-    // one contiguous run of float4 (consecutive lanes, consecutive 16-byte words)
-    __shared__ float4 stage[4][64 * gsr::kRecF4];
-    const int64_t kp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (kp < 2 * kPadF4) {
-        // leading pad, then the pad after the last record (the scan's total)
-        const int64_t q_total = wpre[(int64_t)gsr::kQuads * (words + 1) - 1];
-        const int64_t at = kp < kPadF4 ? kp - kPadF4 : gsr::kRecF4 * q_total + (kp - kPadF4);
-        qrec[at] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
     const int64_t K = (int64_t)*klen;
     const int64_t blk = xcd_contiguous_block((K + 255) / 256);
     if (blk < 0) return;
@@ -326,20 +323,14 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
     const int64_t k = blk * 256 + threadIdx.x;
     if (k - lane >= K) return;   // the whole wave lies past the lists
     const uint32_t qm = k < K ? tkeys[k] >> gsr::kMaskShift : 0u;
-    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), b = a, c = a;
-    uint32_t slot = 0;
+    uint32_t g = 0, slot = 0;
     if (qm) {
         const uint64_t tvk = tvals[k];
-        const uint32_t g = (uint32_t)tvk;
-        a = prec[gsr::kRecF4 * (size_t)g];
-        b = prec[gsr::kRecF4 * (size_t)g + 1];
-        c = prec[gsr::kRecF4 * (size_t)g + 2];
-        c.z = __uint_as_float((uint32_t)k);
+        g = (uint32_t)tvk;
         slot = (uint32_t)(tvk >> 32);
     }
-    float4 *st = stage[threadIdx.x >> 6];
     const uint64_t below = (1ull << lane) - 1ull;
-    // The wave's entries are consecutive, so its records of list q are one run that starts
+    // The wave's entries are consecutive, so its entries of list q are one run that starts
     // where the first of them goes.  Lane q looks that position up for list q: four
     // independent lookups instead of a chain of four.
     static_assert(gsr::kQuads == 4, "one lookup lane per quadrant");
@@ -355,23 +346,14 @@ __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__
     }
 #pragma unroll
     for (int q = 0; q < gsr::kQuads; ++q) {
-        const bool has = (qm >> q) & 1u;
         const uint64_t bal = bals[q];
         if (!bal) continue;
         const uint32_t pos0 = __shfl(start, q, 64);
-        if (has) {
-            const uint32_t r = (uint32_t)__popcll(bal & below);
-            float4 cc = c;
-            cc.w = __uint_as_float(slot++);
-            st[gsr::kRecF4 * r] = a;
-            st[gsr::kRecF4 * r + 1] = b;
-            st[gsr::kRecF4 * r + 2] = cc;
+        if ((qm >> q) & 1u) {
+            const uint32_t pos = pos0 + (uint32_t)__popcll(bal & below);
+            qent[pos] = make_uint2(g, slot++);
+            qk[pos] = (uint32_t)k;
         }
-        __builtin_amdgcn_wave_barrier();
-        const uint32_t n4 = gsr::kRecF4 * (uint32_t)__popcll(bal);
-        float4 *d = qrec + gsr::kRecF4 * (size_t)pos0;
-        for (uint32_t t = (uint32_t)lane; t < n4; t += 64u) d[t] = st[t];
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -463,12 +445,14 @@ __global__ __launch_bounds__(256) void k_wave_identity(uint32_t waves, int32_t *
 }
 
 // Counts of an empty scene (n = 0).
-__global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restrict__ counts)
+__global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restrict__ counts,
+                             unsigned long long grec_off)
 {
     hdr->K = 0;
     hdr->Q = 0;
     hdr->ok = 1u;
     hdr->epoch = gsr::kSortEpoch;
+    hdr->grec_off = grec_off;
     if (counts) {
         counts[0] = 0;
         counts[1] = 0;
@@ -580,7 +564,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
         if ((s = fill_i32(reinterpret_cast<int32_t *>(wpre0), nw0, 0, stream)) != GS_OK) return s;
         k_wave_identity<<<(unsigned)ceil_div(waves, 256), 256, 0, stream>>>((uint32_t)waves, order);
         GS_LAUNCH_CHECK("k_wave_identity");
-        k_bins_empty<<<1, 1, 0, stream>>>(hdr, counts);
+        k_bins_empty<<<1, 1, 0, stream>>>(hdr, counts, (unsigned long long)RL.grec);
         GS_LAUNCH_CHECK("k_bins_empty");
         return GS_OK;
     }
@@ -612,7 +596,8 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     //    same scan zeroes the stamps of the slots it gives out (those that fit), so no slot
     //    of this sort carries a backward call's stamp before one writes it
     k_keys_count<<<gn, 256, 0, stream>>>(rr, proj->depth, prec, log2_amin, n, tx, ty, dkA, dvA, qcnt,
-                                         bins->tiles_touched, (uint32_t *)(ws + L.zero), (int64_t)(L.zero_bytes / 4));
+                                         bins->tiles_touched, (uint32_t *)(ws + L.zero), (int64_t)(L.zero_bytes / 4),
+                                         reinterpret_cast<float4 *>(rb + RL.grec));
     GS_LAUNCH_CHECK("k_keys_count");
     uint32_t *qstamp = reinterpret_cast<uint32_t *>(rb + RL.qstamp);
     if ((s = lb_scan_u32(qcnt, qoff, n + 1, scQ, tickets + kTkQcnt, total + 1, stream, qstamp,
@@ -631,8 +616,8 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     // 3. emit entries in depth order (nothing if the lists do not fit), then a stable sort
     //    of (tile key, emit position) by tile
     const int tbits = L.tbits;
-    k_emit<<<gn, 256, 0, stream>>>(sv, doff, qoff, prec, log2_amin, n, tx, ty, total, cap, klen, hdr, counts, tkA,
-                                   tvA);
+    k_emit<<<gn, 256, 0, stream>>>(sv, doff, qoff, prec, log2_amin, n, tx, ty, total, cap,
+                                   (unsigned long long)RL.grec, klen, hdr, counts, tkA, tvA);
     GS_LAUNCH_CHECK("k_emit");
     if (cap == 0) {
         if ((s = fill_i32(bins->tile_ranges, (int64_t)T + 1, 0, stream)) != GS_OK) return s;
@@ -657,8 +642,8 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
         tk, tv, klen, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
     GS_LAUNCH_CHECK("k_finish");
     if ((s = lb_scan_u32(wpre, wpre, nw, scW, tickets + kTkWpre, nullptr, stream)) != GS_OK) return s;
-    k_quad_lists<<<gk, 256, 0, stream>>>(tk, tv, klen, RL.words, bm, wpre,
-                                         prec, reinterpret_cast<float4 *>(rb + RL.qrec) + gsr::kRecPad * gsr::kRecF4);
+    k_quad_lists<<<gk, 256, 0, stream>>>(tk, tv, klen, RL.words, bm, wpre, reinterpret_cast<uint2 *>(rb + RL.qent),
+                                         reinterpret_cast<uint32_t *>(rb + RL.qk));
     GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {
         k_keys64<<<gk, 256, 0, stream>>>(tk, bins->ids, proj->depth, klen, bins->keys);

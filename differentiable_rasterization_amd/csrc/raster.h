@@ -4,16 +4,16 @@
 // Raster-ready lists (the gs_bins.raster buffer, written by gs_bin_sort):
 //   hdr    BinsHeader             the counts of the last sort: entries K, quadrant records
 //                                 Q, and whether the lists fit the capacity
-//   qrec   [2 * capacity] Rec     (plus kRecPad spare records at each end)
-//                                 for each 8x8 quadrant q of every tile (qx = q & 1,
-//                                 qy = q >> 1), the records of the tile's entries whose
-//                                 alpha >= alpha_min box reaches the quadrant, in list
-//                                 order; quadrant 0's lists of all tiles in tile order, then
-//                                 quadrant 1's, ...
+//   qent   [2 * capacity] uint2   for each 8x8 quadrant q of every tile (qx = q & 1,
+//                                 qy = q >> 1), the entries of the tile's list whose
+//                                 alpha >= alpha_min box reaches the quadrant, in list order,
+//                                 as (Gaussian, gradient slot); quadrant 0's lists of all
+//                                 tiles in tile order, then quadrant 1's, ...
+//   qk     [2 * capacity] uint32  the tile-list index of each of those entries
 //   bitmap [4][words] uint64      bit k of bitmap q is set if list entry k is in quadrant q
 //   wpre   [4][words + 1] uint32  exclusive prefix count over all four bitmaps, word by
-//                                 word, so the records of tile t in quadrant q are
-//                                 qrec[P_q(start_t) .. P_q(end_t)), P_q(x) = wpre[q][x / 64]
+//                                 word, so the entries of tile t in quadrant q are
+//                                 qent[P_q(start_t) .. P_q(end_t)), P_q(x) = wpre[q][x / 64]
 //                                 + set bits of bitmap q below entry x in its word
 //   order  [4 * tiles] int32      the (tile, quadrant) waves, w = tile * 4 + quadrant, by
 //                                 decreasing quadrant record count (heaviest first)
@@ -24,16 +24,20 @@
 //   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
 //                                 padded to 48 bytes), one slot per quadrant record, at the
 //                                 slot index its record carries
+//   grec   [n][4] float4          (last, at hdr.grec_off) the projected raster record of every
+//                                 Gaussian (its three float4 words, then a fourth, unused),
+//                                 copied at sort time (zeros for culled ones), so that the
+//                                 raster calls read nothing outside this buffer
 //   qstamp [2 * capacity] uint32  the epoch of the backward call that wrote each slot, kept
 //                                 apart from the slots so that the per-Gaussian sums read only
 //                                 the slots that were written; the sort sets the stamps of
 //                                 slots 0 .. Q to 0, which no epoch equals
 //
 // Execution: one 64-lane wave per 8x8 quadrant of a 16x16 tile, one pixel per lane
-// (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of records with
-// scalar loads, several records per load batch: the records are uniform across the wave,
-// so they live in SGPRs and feed the vector ALU as operands, with no LDS traffic and no
-// per-entry relevance test.
+// (lane & 7 = column, lane >> 3 = row).  A wave reads its contiguous run of list entries
+// with vector loads and each entry's record with scalar loads, several records per load
+// batch: the records are uniform across the wave, so they live in SGPRs and feed the vector
+// ALU as operands, with no LDS traffic and no per-entry relevance test.
 #pragma once
 
 #include "common.h"
@@ -43,25 +47,23 @@ namespace gsr {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQuads = 4;
 
-// Record layout (48 bytes; written per Gaussian by the projection, copied per quadrant
-// list entry by the binning).  With (dx, dy) = pixel centre - mean, the alpha exponent is
-// evaluated base 2:  o exp(-A dx^2/2 - B dx dy - C dy^2/2) = exp2(a dx^2 + b dx dy + c dy^2 + l)
+// Record layout (48 bytes; written per Gaussian by the projection, copied to grec by the
+// binning).  With (dx, dy) = pixel centre - mean, the alpha exponent is evaluated base 2:
+// o exp(-A dx^2/2 - B dx dy - C dy^2/2) = exp2(a dx^2 + b dx dy + c dy^2 + l)
 // with a = -log2(e) A / 2, b = -log2(e) B, c = -log2(e) C / 2, l = log2(o).
-//   p0 = (u, v, a, b)   p1 = (c, l, red, green)   p2 = (blue, index bits, entry bits, slot bits)
-// "entry" is the record's position k in the 16x16 tile lists and "slot" the index of its
-// gradient slot (both set by the binning; in the per-Gaussian records the projection writes,
-// those two words hold the box half-extents rx, ry as int32 bits).
+//   p0 = (u, v, a, b)   p1 = (c, l, red, green)   p2 = (blue, index bits, rx bits, ry bits)
+// with rx, ry the box half-extents as int32 bits.
 // The backward recovers A = -2 ln(2) a, B = -ln(2) b, C = -2 ln(2) c and 1/o = exp2(-l).
 struct Rec {
     float4 p0, p1, p2;
 };
 constexpr int kRecF4 = 3;   // float4 words per record
+// The binning's copy of the records (grec) uses a 64-byte stride, so that the raster's
+// gather of a record's first 36 bytes touches one 64-byte line (at a 48-byte stride half of
+// them straddled two).
+constexpr int kGRecF4 = 4;
 constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
 constexpr int kStampWords = 1;  // uint32 words per slot stamp
-// The record array has kRecPad spare records before and after the lists, so that a batch
-// of consecutive records, and the batch after it, can always be loaded from one base
-// address (records outside the lists are loaded but never used).
-constexpr int kRecPad = 8;
 // Quadrant records are stored for up to kQuadFactor * capacity (entry, quadrant) pairs
 // (an entry reaches 1.4 - 2 quadrants on average); more is reported as a capacity error.
 constexpr int kQuadFactor = 2;
@@ -120,9 +122,12 @@ __device__ __forceinline__ uint32_t quad_mask(float u, float v, float A, float B
 // current epoch.  The sort sets the stamps of all its slots to 0, so a slot the backward
 // did not write since the sort (a record no pixel reached, a batch no pixel took) never
 // matches, whatever the buffer held before: the raster buffer may be uninitialised.
+// grec_off: the byte offset of grec in the raster buffer (it depends on n, which the
+// forward raster call is not given).
 struct BinsHeader {
     unsigned long long K, Q;   // tile entries and (entry, quadrant) records
     uint32_t ok, epoch;
+    unsigned long long grec_off;
 };
 
 constexpr uint32_t kSortEpoch = 1u;   // the epoch a sort leaves in the header
@@ -140,7 +145,7 @@ __device__ __forceinline__ uint32_t quad_mask_rec(const float4 &p0, const float4
 }
 
 struct RasterLayout {
-    size_t hdr, qrec, bitmap, wpre, order, qoff, qgrad, qstamp, bytes;
+    size_t hdr, grec, qent, qk, bitmap, wpre, order, qoff, qgrad, qstamp, bytes;
     int64_t cap, words;
 };
 
@@ -154,13 +159,15 @@ inline RasterLayout raster_layout(int64_t n, int64_t capacity, int tiles)
     const size_t nn = (size_t)(n > 0 ? n : 1), q4 = (size_t)kQuadFactor * (size_t)L.cap;
     size_t o = 0;
     L.hdr = o;    o += align256(sizeof(BinsHeader));
-    L.qrec = o;   o += align256((q4 + 2 * kRecPad) * sizeof(Rec));   // kRecPad spare records at each end
+    L.qent = o;   o += align256(q4 * 8);
+    L.qk = o;     o += align256(q4 * 4);
     L.bitmap = o; o += align256((size_t)kQuads * (size_t)L.words * 8);
     L.wpre = o;   o += align256((size_t)kQuads * (size_t)(L.words + 1) * 4);
     L.order = o;  o += align256((size_t)kQuads * (size_t)(tiles > 0 ? tiles : 1) * 4);
     L.qoff = o;   o += align256((nn + 1) * 4);
     L.qgrad = o;  o += align256(q4 * kGradSlot * 4);
     L.qstamp = o; o += align256(q4 * kStampWords * 4);
+    L.grec = o;   o += align256(nn * (size_t)kGRecF4 * 16);
     L.bytes = o;
     return L;
 }
@@ -305,7 +312,7 @@ __device__ __forceinline__ void sum_slots(const BinsHeader *__restrict__ hdr, co
 }
 
 // Number of entries below x (0 <= x <= K) that belong to quadrant q: the position in
-// qrec[q] of the first record at or after entry x.  bq = bitmap + q * words,
+// quadrant q's lists (qent) of the first record at or after entry x.  bq = bitmap + q * words,
 // wq = wpre + q * (words + 1).
 __device__ __forceinline__ uint32_t quad_prefix(const uint64_t *__restrict__ bq, const uint32_t *__restrict__ wq,
                                                 uint32_t x)
@@ -327,17 +334,6 @@ __device__ __forceinline__ void raster_block(const int32_t *__restrict__ order, 
     const int w = order[blockIdx.x];
     tile = w >> 2;
     quad = w & 3;
-}
-
-// Pulls the cache lines of records [j, min(j + 64, jlim)) into L2 with one vector load
-// (lane l touches record j + l), so that the wave's scalar loads of those records hit L2
-// rather than memory.  The loaded word is only folded into a sink one chunk later (by
-// then the load has landed, so that wait costs nothing) and the sink is consumed once at
-// the end of the kernel: an ordinary load the compiler tracks, kept in flight meanwhile.
-__device__ __forceinline__ uint32_t prefetch_records(const float4 *__restrict__ qrec, uint32_t j, uint32_t jlim)
-{
-    const uint32_t r = j + (uint32_t)threadIdx.x;
-    return r < jlim ? __float_as_uint(qrec[kRecF4 * (size_t)r].x) : 0u;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

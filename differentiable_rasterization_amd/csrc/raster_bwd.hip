@@ -44,7 +44,8 @@ constexpr int kFields = 9;
 
 template <bool HAS_GT>
 __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ ranges, const int32_t *__restrict__ order,
-                                                   const float4 *__restrict__ qrec, const uint64_t *__restrict__ bitmap,
+                                                   const uint2 *__restrict__ qent, const float4 *__restrict__ grec,
+                                                   const uint64_t *__restrict__ bitmap,
                                                    const uint32_t *__restrict__ wpre, int64_t words, int W, int H,
                                                    int TX, int T, float alpha_min, float alpha_max,
                                                    const float *__restrict__ color, const float *__restrict__ t_final,
@@ -79,7 +80,9 @@ __global__ __launch_bounds__(64) void k_raster_bwd(const int32_t *__restrict__ r
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)(start + nmax));
-    bwd_walk(qrec, j0, j1, fx, fy, start, np, G0, G1, G2, Z, alpha_min, alpha_max, hdr->epoch, qgrad, qstamp);
+    // this pixel's records: those before the first entry beyond its N_p
+    const uint32_t jend = quad_prefix(bq, wq, (uint32_t)(start + max(0, min(np, end - start))));
+    bwd_walk(qent, grec, j0, j1, fx, fy, jend, G0, G1, G2, Z, alpha_min, alpha_max, hdr->epoch, qgrad, qstamp);
 }
 
 // A new stamp for the gradient slots of this backward call.
@@ -130,7 +133,8 @@ extern "C" gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins
     const RasterLayout L = raster_layout(n, bins->capacity, T);
     char *rb = static_cast<char *>(bins->raster);
     const int32_t *order = reinterpret_cast<const int32_t *>(rb + L.order);
-    const float4 *rc = reinterpret_cast<const float4 *>(rb + L.qrec) + kRecPad * kRecF4;
+    const uint2 *qe = reinterpret_cast<const uint2 *>(rb + L.qent);
+    const float4 *gr = reinterpret_cast<const float4 *>(rb + L.grec);
     const uint64_t *bm = reinterpret_cast<const uint64_t *>(rb + L.bitmap);
     const uint32_t *wp = reinterpret_cast<const uint32_t *>(rb + L.wpre);
     float *qg = reinterpret_cast<float *>(rb + L.qgrad);
@@ -140,11 +144,11 @@ extern "C" gs_status gs_raster_bwd_partials(const gs_gaussians *g, const gs_bins
     k_new_epoch<<<1, 1, 0, stream>>>(hdr);
     GS_LAUNCH_CHECK("k_new_epoch");
     if (dL_dt)
-        k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
+        k_raster_bwd<true><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, qe, gr, bm, wp, L.words, cam->width,
                                                     cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
                                                     n_trav, dL_dcolor, dL_dt, hdr, qg, qs);
     else
-        k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, rc, bm, wp, L.words, cam->width,
+        k_raster_bwd<false><<<grid, 64, 0, stream>>>(bins->tile_ranges, order, qe, gr, bm, wp, L.words, cam->width,
                                                      cam->height, TX, T, p->alpha_min, p->alpha_max, color, t_final,
                                                      n_trav, dL_dcolor, nullptr, hdr, qg, qs);
     GS_LAUNCH_CHECK("k_raster_bwd");

@@ -58,7 +58,8 @@ __device__ __forceinline__ float l1_sign(float d) { return d > 0.0f ? 1.0f : (d 
 // walked records, forward and backward, and its accepted (pixel, record) pairs to counts.
 template <bool kCount>
 __global__ __launch_bounds__(64) void k_raster_fused_l1(
-    const int32_t *__restrict__ ranges, const int32_t *__restrict__ order, const float4 *__restrict__ qrec,
+    const int32_t *__restrict__ ranges, const int32_t *__restrict__ order, const uint2 *__restrict__ qent,
+    const uint32_t *__restrict__ qk, const float4 *__restrict__ grec,
     const uint64_t *__restrict__ bitmap, const uint32_t *__restrict__ wpre, int64_t words, int W, int H, int TX,
     int T, float alpha_min, float alpha_max, float t_min, const float *__restrict__ target, float inv,
     float *__restrict__ out_c, float *__restrict__ out_t, int32_t *__restrict__ out_n,
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
     if (listed) {   // an empty list reads nothing (its quadrant prefix counts may be unset)
         j0 = quad_prefix(bq, wq, (uint32_t)start);
         j1 = quad_prefix(bq, wq, (uint32_t)end);
-        fwd_walk<kFusedFwdBatch, kCount>(qrec, j0, j1, fx, fy, start, end, inside, alpha_min, alpha_max, t_min, cr,
-                                         cg, cb, Tr, np, &walked, &taken);
+        fwd_walk<kFusedFwdBatch, kCount>(qent, qk, grec, j0, j1, fx, fy, start, end, inside, alpha_min, alpha_max,
+                                         t_min, cr, cg, cb, Tr, np, &walked, &taken);
     }
     // 2. L1 loss and its gradient
     float G0 = 0.0f, G1 = 0.0f, G2 = 0.0f, Z = 0.0f;
@@ -117,6 +118,8 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
     if (!listed) return;
     const int nmax = max(0, min(gsd::wave_max_i32(np), end - start));
     const uint32_t jb = quad_prefix(bq, wq, (uint32_t)(start + nmax));
+    // this pixel's records: those before the first entry beyond its N_p
+    const uint32_t jend = quad_prefix(bq, wq, (uint32_t)(start + np));
     if constexpr (kCount) {
         const unsigned long long tk = wave_sum_u64((unsigned long long)taken);
         if (lane == 0) {
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(64) void k_raster_fused_l1(
         }
     }
     // the stamp of this call: the header's next epoch (k_fused_final stores it)
-    bwd_walk(qrec, j0, jb, fx, fy, start, np, G0, G1, G2, Z, alpha_min, alpha_max, next_epoch(hdr->epoch), qgrad,
+    bwd_walk(qent, grec, j0, jb, fx, fy, jend, G0, G1, G2, Z, alpha_min, alpha_max, next_epoch(hdr->epoch), qgrad,
              qstamp);
 }
 
@@ -294,7 +297,8 @@ gs_status fused_launch(const gs_gaussians *g, const gs_bins *bins, const gs_came
     auto kern = walk_counts ? k_raster_fused_l1<true> : k_raster_fused_l1<false>;
     kern<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
         bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order),
-        reinterpret_cast<const float4 *>(rb + L.qrec) + kRecPad * kRecF4,
+        reinterpret_cast<const uint2 *>(rb + L.qent), reinterpret_cast<const uint32_t *>(rb + L.qk),
+        reinterpret_cast<const float4 *>(rb + L.grec),
         reinterpret_cast<const uint64_t *>(rb + L.bitmap), reinterpret_cast<const uint32_t *>(rb + L.wpre), L.words,
         cam->width, cam->height, TX, T, p->alpha_min, p->alpha_max, p->t_min, target, (float)(1.0 / (double)m),
         color, t_final, n_trav, part, ticket, hdr, reinterpret_cast<float *>(rb + L.qgrad),

@@ -15,7 +15,8 @@ namespace {
 using namespace gsr;
 
 __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ ranges, const int32_t *__restrict__ order,
-                                                   const float4 *__restrict__ qrec, const uint64_t *__restrict__ bitmap,
+                                                   const uint2 *__restrict__ qent, const uint32_t *__restrict__ qk,
+                                                   const char *__restrict__ rb, const uint64_t *__restrict__ bitmap,
                                                    const uint32_t *__restrict__ wpre, int64_t words, int W, int H,
                                                    int TX, int T, float alpha_min, float alpha_max, float t_min,
                                                    float *__restrict__ out_c, float *__restrict__ out_t,
@@ -44,9 +45,10 @@ __global__ __launch_bounds__(64) void k_raster_fwd(const int32_t *__restrict__ r
     const uint64_t *bq = bitmap + (int64_t)q * words;
     const uint32_t *wq = wpre + (int64_t)q * (words + 1);
     const uint32_t j0 = quad_prefix(bq, wq, (uint32_t)start), j1 = quad_prefix(bq, wq, (uint32_t)end);
+    const float4 *grec = reinterpret_cast<const float4 *>(rb + reinterpret_cast<const BinsHeader *>(rb)->grec_off);
     float Tr, cr, cg, cb;
     int np;
-    fwd_walk(qrec, j0, j1, fx, fy, start, end, inside, alpha_min, alpha_max, t_min, cr, cg, cb, Tr, np);
+    fwd_walk(qent, qk, grec, j0, j1, fx, fy, start, end, inside, alpha_min, alpha_max, t_min, cr, cg, cb, Tr, np);
     if (inside) {
         const size_t idx = (size_t)py * W + px;
         out_c[3 * idx] = cr;
@@ -120,18 +122,19 @@ extern "C" gs_status gs_raster_fwd(const gs_projected *proj, const gs_bins *bins
                                    unsigned long long *n_trav_sum, hipStream_t stream)
 {
     using namespace gsi;
-    (void)proj;   // the lists carry raster-ready copies of the projected records
+    (void)proj;   // the raster buffer carries copies of the projected records
     gs_status s;
     if ((s = check_camera(cam)) != GS_OK) return s;
     if ((s = check_params(p)) != GS_OK) return s;
     if ((s = check_raster_inputs(bins, cam)) != GS_OK) return s;
     if (!color || !t_final || !n_trav) return fail(GS_ERR_INVALID_ARGUMENT, "an output pointer is NULL");
     const int TX = tiles_x(cam->width), T = TX * tiles_y(cam->height);
-    const RasterLayout L = raster_layout(0, bins->capacity, T);   // the fields read here do not depend on n
+    // the fields read here come before the n-dependent ones; grec's offset is in the header
+    const RasterLayout L = raster_layout(0, bins->capacity, T);
     const char *rb = static_cast<const char *>(bins->raster);
     k_raster_fwd<<<(unsigned)raster_grid(T), 64, 0, stream>>>(
         bins->tile_ranges, reinterpret_cast<const int32_t *>(rb + L.order),
-        reinterpret_cast<const float4 *>(rb + L.qrec) + kRecPad * kRecF4,
+        reinterpret_cast<const uint2 *>(rb + L.qent), reinterpret_cast<const uint32_t *>(rb + L.qk), rb,
         reinterpret_cast<const uint64_t *>(rb + L.bitmap), reinterpret_cast<const uint32_t *>(rb + L.wpre), L.words,
         cam->width, cam->height, TX, T, p->alpha_min, p->alpha_max, p->t_min, color, t_final, n_trav);
     GS_LAUNCH_CHECK("k_raster_fwd");

@@ -8,22 +8,106 @@
 
 namespace gsr {
 
+// The quadrant lists hold per record its Gaussian g and gradient slot (qent); the record
+// itself (centre, pre-scaled conic, log2 opacity, colour) is the Gaussian's raster record
+// in grec, fetched by g with scalar loads.  A wave reads the entries of its list 64
+// at a time with one vector load (lane l: entry c + l), one chunk ahead, and takes each
+// record's g and slot out of those registers (v_readlane).
+struct Chunks {
+    uint2 e0, e1;   // entries of chunks base and base + 64
+    uint32_t base, last;
+    const uint2 *qent;
+    const float4 *grec;
+    // Lane l loads entry c + l, clamped to the list's last entry: the loads are unconditional
+    // (no divergent branch, so the compiler's waits on them stay exact), and a lane past the
+    // list names a real Gaussian, whose record is loaded and never used.
+    __device__ __forceinline__ uint2 load(uint32_t c) const { return qent[min(c + (uint32_t)threadIdx.x, last)]; }
+    // e0 is always written by an explicit move (of a loaded value that has arrived), never
+    // straight by a load: the compiler's wait placement then knows that reading e0 needs no
+    // wait, also where vector stores are in flight (they share the load counter on this GPU).
+    __device__ __forceinline__ static uint2 moved(uint2 v)
+    {
+        uint32_t x, y;
+        asm volatile("v_mov_b32 %0, %2\n\tv_mov_b32 %1, %3" : "=v"(x), "=v"(y) : "v"(v.x), "v"(v.y));
+        return make_uint2(x, y);
+    }
+    // for a non-empty list j0 .. j1
+    __device__ __forceinline__ void init(const uint2 *q, const float4 *g, uint32_t j0, uint32_t j1)
+    {
+        qent = q;
+        grec = g;
+        base = j0;
+        last = j1 - 1u;
+        const uint2 first = load(j0);
+        e1 = load(j0 + 64u);
+        e0 = moved(first);
+    }
+    // at the first record of the next chunk (its entries were loaded one chunk ago).  The
+    // move of e1 into e0 is ordered before the next load, so that the load can write e1's
+    // registers directly: as a plain assignment, the compiler issued the load into
+    // temporaries and copied them afterwards, which waits for the load just issued.
+    __device__ __forceinline__ void advance()
+    {
+        base += 64u;
+        e0 = moved(e1);
+        __builtin_amdgcn_sched_barrier(0);
+        e1 = load(base + 64u);
+    }
+    // entries of records j .. j + kN - 1 (all in one chunk: base <= j, j + kN <= base + 128,
+    // j - base a multiple of kN), uniform across the wave; the chunk is chosen by a uniform
+    // branch, so a batch reads only its own chunk's registers
+    template <int kN>
+    __device__ __forceinline__ void at(uint32_t j, uint32_t (&g)[kN], uint32_t (&slot)[kN]) const
+    {
+        const uint32_t l = j - base;
+        const int ln = (int)(l & 63u);
+        if (l < 64u) {
+#pragma unroll
+            for (int i = 0; i < kN; ++i) {
+                g[i] = (uint32_t)__builtin_amdgcn_readlane((int)e0.x, ln + i);
+                slot[i] = (uint32_t)__builtin_amdgcn_readlane((int)e0.y, ln + i);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kN; ++i) {
+                g[i] = (uint32_t)__builtin_amdgcn_readlane((int)e1.x, ln + i);
+                slot[i] = (uint32_t)__builtin_amdgcn_readlane((int)e1.y, ln + i);
+            }
+        }
+    }
+    template <int kN>
+    __device__ __forceinline__ void at(uint32_t j, uint32_t (&g)[kN]) const
+    {
+        const uint32_t l = j - base;
+        const int ln = (int)(l & 63u);
+        if (l < 64u) {
+#pragma unroll
+            for (int i = 0; i < kN; ++i) g[i] = (uint32_t)__builtin_amdgcn_readlane((int)e0.x, ln + i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kN; ++i) g[i] = (uint32_t)__builtin_amdgcn_readlane((int)e1.x, ln + i);
+        }
+    }
+    __device__ __forceinline__ void finish() const {}
+};
 
 // One batch of records in scalar registers.
 template <int kFwdBatch>
 struct Batch {
     float4 p0[kFwdBatch], p1[kFwdBatch];
-    float blue[kFwdBatch], kent[kFwdBatch];
-    __device__ __forceinline__ void load(const float4 *__restrict__ qrec, uint32_t j)
+    float blue[kFwdBatch];
+    // records j .. j + kFwdBatch - 1 of the list (entries past its end repeat the last one,
+    // loaded and never used)
+    __device__ __forceinline__ void load(const Chunks &C, uint32_t j)
     {
-        const float4 *rb = qrec + kRecF4 * (size_t)j;
+        uint32_t g[kFwdBatch];
+        C.at<kFwdBatch>(j, g);
 #pragma unroll
         for (int i = 0; i < kFwdBatch; ++i) {
-            p0[i] = rb[kRecF4 * i];
-            p1[i] = rb[kRecF4 * i + 1];
-            const float4 p2 = rb[kRecF4 * i + 2];
-            blue[i] = p2.x;
-            kent[i] = p2.z;
+            const float4 *rb = C.grec + kGRecF4 * (size_t)g[i];
+            p0[i] = rb[0];
+            p1[i] = rb[1];
+            blue[i] = rb[2].x;
         }
     }
     // Makes the loaded values available here: the compiler waits for the scalar loads at
@@ -33,14 +117,16 @@ struct Batch {
 #pragma unroll
         for (int i = 0; i < kFwdBatch; ++i)
             asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
-                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i])
+                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i])
                          : "memory");
     }
 };
 
 // ByteSplat Eq. 1 over the quadrant's records j0 .. j1 (tile list entries start .. end):
 // front-to-back compositing of the lane's pixel at (fx, fy), stopping once T < t_min.
-// Outputs the colour (cr, cg, cb), T_final and N_p (entries of the tile list traversed).
+// Outputs the colour (cr, cg, cb), T_final and N_p (entries of the tile list traversed: the
+// tile-list index qk of the record at which the pixel stopped, minus start, plus one; the
+// whole list if it never stopped).
 // kFwdBatch (2 or 4) records per scalar-load batch, two batches in flight: 4 hides more
 // load latency, 2 needs 40 fewer scalar registers (the fused kernel's backward phase then
 // keeps more waves resident).  The batch size does not change the arithmetic.
@@ -48,8 +134,9 @@ struct Batch {
 // lanes) and taken the number of them this lane accepted (alpha-check passed while live);
 // without it both are left alone.
 template <int kFwdBatch = 4, bool kCount = false>
-__device__ __forceinline__ void fwd_walk(const float4 *__restrict__ qrec, uint32_t j0, uint32_t j1, float fx, float fy,
-                                         int start, int end, bool inside, float alpha_min, float alpha_max,
+__device__ __forceinline__ void fwd_walk(const uint2 *__restrict__ qent, const uint32_t *__restrict__ qk,
+                                         const float4 *__restrict__ grec, uint32_t j0, uint32_t j1, float fx,
+                                         float fy, int start, int end, bool inside, float alpha_min, float alpha_max,
                                          float t_min, float &cr, float &cg, float &cb, float &Tr, int &np,
                                          uint32_t *walked = nullptr, uint32_t *taken = nullptr)
 {
@@ -58,15 +145,18 @@ __device__ __forceinline__ void fwd_walk(const float4 *__restrict__ qrec, uint32
     cg = 0.0f;
     cb = 0.0f;
     np = end - start;
+    uint32_t jstop = 0xFFFFFFFFu;   // the record at which this lane's pixel stopped
     bool live = inside;
-    // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
-    uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
+    if constexpr (kCount) *walked = 0u;
+    if (j0 >= j1) return;   // no record reaches the quadrant: the pixels traverse the whole list
+    Chunks C;
+    C.init(qent, grec, j0, j1);
     // Records come in batches of kFwdBatch through scalar loads.  Scalar loads complete out
     // of order, so the only wait is for all of them: the loop waits for batch b, issues the
     // loads of batch b + 1 and then blends batch b, so that the loads of b + 1 land while b
     // is blended.  Two register sets, alternating (the loop body is unrolled twice).
     Batch<kFwdBatch> A, B;
-    if (j0 < j1) A.load(qrec, j0);
+    A.load(C, j0);
     auto blend = [&](const Batch<kFwdBatch> &R, uint32_t j) {
         // branch-free per entry: lanes that do not take it blend with alpha = 0 (T and C
         // unchanged exactly); termination is a mask update
@@ -84,34 +174,31 @@ __device__ __forceinline__ void fwd_walk(const float4 *__restrict__ qrec, uint32
             cb = fmaf(w, R.blue[i], cb);
             Tr = Tr * (1.0f - a);
             const bool stop = take && Tr < t_min;
-            np = stop ? (int)__float_as_uint(R.kent[i]) - start + 1 : np;
+            jstop = stop ? j + (uint32_t)i : jstop;
             live = live && !stop;
         }
     };
-    auto prefetch = [&](uint32_t j) {
-        if (((j - j0) & 63u) == 0u && j > j0) {
-            sink ^= pend;
-            pend = prefetch_records(qrec, j + 64u, j1);
-        }
+    auto chunk = [&](uint32_t j) {
+        if (((j - j0) & 63u) == 0u && j > j0) C.advance();
     };
     uint32_t jw = j0;   // end of the records blended so far
     for (uint32_t j = j0; j < j1; j += 2 * kFwdBatch) {
-        prefetch(j);
+        chunk(j);
         A.wait();
-        B.load(qrec, j + kFwdBatch);   // past j1: spare records, loaded but unused
+        B.load(C, j + kFwdBatch);   // past j1: the last entry again, loaded but unused
         blend(A, j);
         if constexpr (kCount) jw = min(j + kFwdBatch, j1);
         if (j + kFwdBatch >= j1 || __ballot(live) == 0) break;
-        prefetch(j + kFwdBatch);
+        chunk(j + kFwdBatch);
         B.wait();
-        A.load(qrec, j + 2 * kFwdBatch);
+        A.load(C, j + 2 * kFwdBatch);
         blend(B, j + kFwdBatch);
         if constexpr (kCount) jw = min(j + 2 * kFwdBatch, j1);
         if (__ballot(live) == 0) break;
     }
+    C.finish();
+    if (jstop != 0xFFFFFFFFu) np = (int)qk[jstop] - start + 1;
     if constexpr (kCount) *walked = jw - j0;
-    sink ^= pend;
-    asm volatile("" ::"v"(sink));
 }
 
 constexpr int kBwdBatch = 4;   // entries per transpose-reduction (4 x 9 values -> 4 rows of 16 lanes)
@@ -190,13 +277,14 @@ __device__ __forceinline__ void reduce_4x9(float (&v)[kBwdBatch * kFields], int 
 
 // ByteSplat Eq. 3 (and the per-record part of Eq. 4) over the quadrant's records j0 .. j1,
 // front to back, for the lane's pixel at (fx, fy) with dL/dC = (G0, G1, G2),
-// Z = C . G + G_T T_final and its N_p (np): the moment sums of every batch of 4 records
-// some pixel takes go to the records' gradient slots in qgrad, stamped with epoch in
-// qstamp.
-__device__ __forceinline__ void bwd_walk(const float4 *__restrict__ qrec, uint32_t j0, uint32_t j1, float fx, float fy,
-                                         int start, int np, float G0, float G1, float G2, float Z, float alpha_min,
-                                         float alpha_max, uint32_t epoch, float *__restrict__ qgrad,
-                                         uint32_t *__restrict__ qstamp)
+// Z = C . G + G_T T_final; the pixel takes records j < jend (jend: the quadrant position of
+// the first entry beyond its N_p, quad_prefix(start + N_p)).  The moment sums of every
+// batch of 4 records some pixel takes go to the records' gradient slots in qgrad, stamped
+// with epoch in qstamp.
+__device__ __forceinline__ void bwd_walk(const uint2 *__restrict__ qent, const float4 *__restrict__ grec, uint32_t j0,
+                                         uint32_t j1, float fx, float fy, uint32_t jend, float G0, float G1, float G2,
+                                         float Z, float alpha_min, float alpha_max, uint32_t epoch,
+                                         float *__restrict__ qgrad, uint32_t *__restrict__ qstamp)
 {
     const int lane = threadIdx.x & 63;
     const int row = lane >> 4, nl = lane & 15;
@@ -206,42 +294,39 @@ __device__ __forceinline__ void bwd_walk(const float4 *__restrict__ qrec, uint32
     const int my_field = nl == 1 ? 8 : 4 * ((nl >> 1) & 1) + 2 * ((nl >> 2) & 1) + ((nl >> 3) & 1);
     const bool lane_writes = (nl & 1) == 0 || nl == 1 || stamp_lane;
     float Tr = 1.0f;
-    // L2 prefetch of the next chunk of 64 records ahead of the scalar reads
-    uint32_t sink = prefetch_records(qrec, j0, j1), pend = prefetch_records(qrec, j0 + 64u, j1);
+    if (j0 >= j1) return;
+    Chunks C;
+    C.init(qent, grec, j0, j1);
     for (uint32_t jt = j0; jt < j1;) {
-        if (((jt - j0) & 63u) == 0u && jt > j0) {
-            sink ^= pend;
-            pend = prefetch_records(qrec, jt + 64u, j1);
-        }
-        // records jt .. jt+3 (past j1: spare, unused); one wait per batch
+        if (((jt - j0) & 63u) == 0u && jt > j0) C.advance();
+        // records jt .. jt+3 (past j1: the last entry again, unused); one wait per batch
         float4 p0[kBwdBatch], p1[kBwdBatch];
-        float blue[kBwdBatch], kent[kBwdBatch], slot[kBwdBatch];
-        const float4 *rb = qrec + kRecF4 * (size_t)jt;
+        float blue[kBwdBatch], slot[kBwdBatch];
+        uint32_t gi[kBwdBatch], si[kBwdBatch];
+        C.at<kBwdBatch>(jt, gi, si);
 #pragma unroll
         for (int i = 0; i < kBwdBatch; ++i) {
-            p0[i] = rb[kRecF4 * i];
-            p1[i] = rb[kRecF4 * i + 1];
-            const float4 p2 = rb[kRecF4 * i + 2];
-            blue[i] = p2.x;
-            kent[i] = p2.z;
-            slot[i] = p2.w;
+            const float4 *rb = grec + kGRecF4 * (size_t)gi[i];
+            p0[i] = rb[0];
+            p1[i] = rb[1];
+            blue[i] = rb[2].x;
+            slot[i] = __uint_as_float(si[i]);
         }
 #pragma unroll
         for (int i = 0; i < kBwdBatch; ++i)
             asm volatile("" ::"s"(p0[i].x), "s"(p0[i].y), "s"(p0[i].z), "s"(p0[i].w), "s"(p1[i].x), "s"(p1[i].y),
-                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(kent[i]), "s"(slot[i]));
+                         "s"(p1[i].z), "s"(p1[i].w), "s"(blue[i]), "s"(slot[i]));
         const uint32_t cnt = min((uint32_t)kBwdBatch, j1 - jt);
         float v[kBwdBatch * kFields];
         bool any = false;
 #pragma unroll
         for (int i = 0; i < kBwdBatch; ++i) {
             float *o = v + kFields * i;
-            const int rel = (int)__float_as_uint(kent[i]) - start;
             const float dx = fx - p0[i].x, dy = fy - p0[i].y;
             const float raw = exp2_fast(exponent(p0[i], p1[i], dx, dy));
             // the forward pass's alpha and T, bit for bit
             const float alpha = fminf(alpha_max, raw);
-            const bool take = (uint32_t)i < cnt && rel < np && alpha >= alpha_min;
+            const bool take = (uint32_t)i < cnt && jt + (uint32_t)i < jend && alpha >= alpha_min;
             const float a = take ? alpha : 0.0f;
             const float om = 1.0f - a;
             const float ro = __builtin_amdgcn_rcpf(om);
@@ -279,8 +364,7 @@ __device__ __forceinline__ void bwd_walk(const float4 *__restrict__ qrec, uint32
                 *dst = nl == 1 ? t8 : fz;
         }
     }
-    sink ^= pend;
-    asm volatile("" ::"v"(sink));
+    C.finish();
 }
 
 }  // namespace gsr

@@ -168,8 +168,9 @@ gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, const gs_raste
                      gs_projected *out, hipStream_t stream);
 
 /* Bytes of the gs_bins.raster buffer for n Gaussians, `capacity` list entries and a W x H
- * image: 2 quadrant records (48 B), 2 gradient slots (48 B) with their stamps (4 B) and 4
- * quadrant bits per entry, plus 4 B per Gaussian, 16 B per tile and a 256-byte header. */
+ * image: 2 quadrant entries (12 B), 2 gradient slots (48 B) with their stamps (4 B) and 4
+ * quadrant bits per entry, plus 68 B per Gaussian (a copy of its 48-byte raster record at a
+ * 64-byte stride and its first gradient slot), 16 B per tile and a 256-byte header. */
 size_t gs_bins_raster_bytes(int64_t n, int64_t capacity, int32_t width, int32_t height);
 
 /* Workspace bytes gs_bin_sort needs for n Gaussians, `capacity` list entries and the
@@ -184,8 +185,9 @@ size_t gs_bin_sort_workspace_bytes(int64_t n, int64_t capacity, int32_t width, i
  * radix sort of the Gaussians by depth key, a scan of their tile counts in that order,
  * emission, and a stable radix sort of the entries by tile id.  Then fills bins->raster
  * from the projected records (proj->depth, radii and rec are read; u, v, rx, ry as stored in
- * rec): an entry joins the list of an 8x8 quadrant of its tile if its alpha >= p->alpha_min
- * ellipse can reach one of the quadrant's pixel centres.  p must be the parameters given
+ * rec; the records themselves are copied in): an entry joins the list of an 8x8 quadrant
+ * of its tile if its alpha >= p->alpha_min ellipse can reach one of the quadrant's pixel
+ * centres.  p must be the parameters given
  * to gs_project.
  * Reads the total K back to the host (synchronises `stream`) and stores it in
  * *n_isect_out (host).  The quadrant records take up to 2 * capacity slots, so a capacity
