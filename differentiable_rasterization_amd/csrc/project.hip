@@ -291,13 +291,14 @@ __device__ __forceinline__ bool sh_finite(const Params1<K> &prm)
     return f;
 }
 
-// The projection's outputs (gs_projected).
+// The projection's outputs (gs_projected): the depth key, the radii and the raster record of
+// every Gaussian, and optionally the plain record fields as planes of n floats.
 struct ProjOut {
-    float2 *means2d;
-    float4 *conic_o;
-    float *color, *depth;
+    float *means2d, *conic_o, *color;   // [2][n], [4][n], [3][n]; NULL: that group is not written
+    float *depth;
     int2 *radii;
     float4 *rec;
+    int64_t n;
 };
 
 // Projects Gaussian i with parameters prm and stores its projected record: the one
@@ -324,11 +325,13 @@ __device__ __forceinline__ void project_store(const Params1<(DEG + 1) * (DEG + 1
     project_store_s<DEG>(prm, S, cam, depth_lo, depth_hi, i, po);
 }
 
-// project_store with the Gaussian's camera-independent values already computed.
+// The projected record of Gaussian i as three float4 of the raster record; depth, radii and
+// the plain fields (where requested) are stored on the way.  A culled Gaussian's record is
+// zero apart from its index (its radii are (0, 0)).
 template <int DEG>
-__device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG + 1)> &prm, const ProjScalars &S,
-                                                const CamD &cam, float depth_lo, float depth_hi, int64_t i,
-                                                const ProjOut &po)
+__device__ __forceinline__ void project_record(const Params1<(DEG + 1) * (DEG + 1)> &prm, const ProjScalars &S,
+                                               const CamD &cam, float depth_lo, float depth_hi, int64_t i,
+                                               const ProjOut &po, float4 (&rec)[3])
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     Proj P;
@@ -336,9 +339,9 @@ __device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG +
     project_view(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.q[0], prm.q[1], prm.q[2], prm.q[3], S, depth_lo, depth_hi, P);
     po.depth[i] = P.key;
     po.radii[i] = make_int2(P.rx, P.ry);
+    rec[0] = rec[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    rec[2] = make_float4(0.0f, __uint_as_float((uint32_t)i), 0.0f, 0.0f);
     if (!P.vis) return;
-    po.means2d[i] = make_float2((float)P.u, (float)P.v);
-    po.conic_o[i] = make_float4((float)P.A, (float)P.B, (float)P.C, (float)P.o);
     float Y[K];
     sh_basis<DEG>(P.dir[0], P.dir[1], P.dir[2], Y);
     float r = 0.0f, g = 0.0f, b = 0.0f;
@@ -348,14 +351,42 @@ __device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG +
         g = fmaf(prm.sh[3 * k + 1], Y[k], g);
         b = fmaf(prm.sh[3 * k + 2], Y[k], b);
     }
-    po.color[3 * i + 0] = r;
-    po.color[3 * i + 1] = g;
-    po.color[3 * i + 2] = b;
-    // raster-ready copy: conic scaled for exp2, log2 of the stored opacity
+    const int64_t n = po.n;
+    if (po.means2d) {
+        po.means2d[i] = (float)P.u;
+        po.means2d[n + i] = (float)P.v;
+    }
+    if (po.conic_o) {
+        po.conic_o[i] = (float)P.A;
+        po.conic_o[n + i] = (float)P.B;
+        po.conic_o[2 * n + i] = (float)P.C;
+        po.conic_o[3 * n + i] = (float)P.o;
+    }
+    if (po.color) {
+        po.color[i] = r;
+        po.color[n + i] = g;
+        po.color[2 * n + i] = b;
+    }
+    // raster-ready: conic scaled for exp2, log2 of the stored opacity
     const RecConic rc = rec_conic(P);
-    po.rec[3 * i + 0] = make_float4((float)P.u, (float)P.v, rc.a, rc.b);
-    po.rec[3 * i + 1] = make_float4(rc.c, rc.l, r, g);
-    po.rec[3 * i + 2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(P.rx), __int_as_float(P.ry));
+    rec[0] = make_float4((float)P.u, (float)P.v, rc.a, rc.b);
+    rec[1] = make_float4(rc.c, rc.l, r, g);
+    rec[2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(P.rx), __int_as_float(P.ry));
+}
+
+// project_store with the Gaussian's camera-independent values already computed.  The record
+// goes straight from registers (three 16-byte stores 48 bytes apart per lane; staging a
+// block's records through LDS for contiguous stores measured no faster).
+template <int DEG>
+__device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG + 1)> &prm, const ProjScalars &S,
+                                                const CamD &cam, float depth_lo, float depth_hi, int64_t i,
+                                                const ProjOut &po)
+{
+    float4 rec[3];
+    project_record<DEG>(prm, S, cam, depth_lo, depth_hi, i, po, rec);
+    po.rec[3 * i + 0] = rec[0];
+    po.rec[3 * i + 1] = rec[1];
+    po.rec[3 * i + 2] = rec[2];
 }
 
 template <int DEG>
@@ -839,18 +870,17 @@ gs_status check_proj_out(const gs_projected *out, int64_t n)
 {
     if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "projected output is NULL");
     if (n == 0) return GS_OK;
-    if (!out->means2d || !out->conic_opacity || !out->color || !out->depth || !out->radii || !out->rec)
-        return fail(GS_ERR_INVALID_ARGUMENT, "a projected-record pointer is NULL");
-    if (!aligned(out->conic_opacity, 16) || !aligned(out->rec, 16) || !aligned(out->means2d, 8) ||
-        !aligned(out->radii, 8))
-        return fail(GS_ERR_INVALID_ARGUMENT, "conic_opacity/rec must be 16-byte, means2d/radii 8-byte aligned");
+    if (!out->depth || !out->radii || !out->rec)
+        return fail(GS_ERR_INVALID_ARGUMENT, "projected depth / radii / rec is NULL");
+    if (!aligned(out->rec, 16) || !aligned(out->radii, 8))
+        return fail(GS_ERR_INVALID_ARGUMENT, "rec must be 16-byte, radii 8-byte aligned");
     return GS_OK;
 }
 
-ProjOut proj_out(const gs_projected *out)
+ProjOut proj_out(const gs_projected *out, int64_t n)
 {
-    return ProjOut{reinterpret_cast<float2 *>(out->means2d), reinterpret_cast<float4 *>(out->conic_opacity),
-                   out->color, out->depth, reinterpret_cast<int2 *>(out->radii), reinterpret_cast<float4 *>(out->rec)};
+    return ProjOut{out->means2d, out->conic_opacity, out->color, out->depth, reinterpret_cast<int2 *>(out->radii),
+                   reinterpret_cast<float4 *>(out->rec), n};
 }
 
 gs_status launch_project_bwd(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
@@ -892,7 +922,7 @@ extern "C" gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, con
     if (n == 0) return GS_OK;
     const CamD cd = make_cam(cam);
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
-    const ProjOut po = proj_out(out);
+    const ProjOut po = proj_out(out, n);
 #define GS_PF(D)                                                                                        \
     k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
                                              cd, p->alpha_min, p->depth_lo, p->depth_hi, po)
@@ -1005,7 +1035,7 @@ gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, cons
     const uint32_t *qs = reinterpret_cast<const uint32_t *>(rb + L.qstamp);
     const CamD cd = make_cam(cam);
     const CamD nd = next_cam ? make_cam(next_cam) : cd;
-    const ProjOut po = next_cam ? proj_out(next_proj) : ProjOut{};
+    const ProjOut po = next_cam ? proj_out(next_proj, n) : ProjOut{};
     // Small blocks: at two waves per SIMD the last round of blocks is the coarser the larger
     // they are.  Measured on MI355X: 64 threads fastest at 1M Gaussians, 128 at 10M.
     const int bt = n <= (int64_t(1) << 22) ? 64 : 128;
@@ -1072,7 +1102,7 @@ extern "C" gs_status gs_project_batch(const gs_gaussians *g, int32_t views, cons
         if ((s = check_camera(&cams[v])) != GS_OK) return s;
         if ((s = check_proj_out(&out[v], g->n)) != GS_OK) return s;
         bp.cam[v] = make_cam(&cams[v]);
-        bp.out[v] = proj_out(&out[v]);
+        bp.out[v] = proj_out(&out[v], g->n);
     }
     const int64_t n = g->n;
     if (n == 0) return GS_OK;
@@ -1125,7 +1155,7 @@ extern "C" gs_status gs_grad_aggregate_adam_batch(const gs_gaussians *g, int32_t
             if ((s = check_camera(&next_cams[k])) != GS_OK) return s;
             if ((s = check_proj_out(&next_proj[k], n)) != GS_OK) return s;
             next.cam[k] = make_cam(&next_cams[k]);
-            next.out[k] = proj_out(&next_proj[k]);
+            next.out[k] = proj_out(&next_proj[k], n);
         }
     }
     if (n == 0) return GS_OK;

@@ -24,19 +24,21 @@ def bytes_per_gaussian(sh_degree: int, adam: bool = True, grads: bool = False) -
 
 def step_bytes_per_gaussian(sh_degree: int) -> int:
     """Everything this library keeps per Gaussian during a training step: parameters,
-    gradients, Adam moments, the projected record (means2d 8, conic+opacity 16, colour 12,
-    depth 4, radii 8), its 48-byte raster-ready copy, screen-space gradients (36) and the
-    binning's per-Gaussian buffers (36: 32-bit depth keys and 64-bit values (tile count,
-    index) twice, quadrant-record counts, emit offsets, first gradient slot)."""
-    return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 48 + 48 + 36 + 36
+    gradients, Adam moments, the projection's depth key (4), radii (8) and 48-byte raster
+    record (the plain record planes are optional and not counted), screen-space gradients
+    (36), the binning's per-Gaussian buffers (36: 32-bit depth keys and 64-bit values (tile
+    count, index) twice, quadrant-record counts, emit offsets, first gradient slot) and the
+    raster buffer's per-Gaussian part (68: the record copied at a 64-byte stride, the first
+    gradient slot)."""
+    return bytes_per_gaussian(sh_degree, adam=True, grads=True) + 60 + 36 + 36 + 68
 
 
 def step_bytes_per_intersection() -> int:
-    """Intersection lists: ids (4); the raster-ready lists with room for two 8x8-quadrant
-    records per entry (2 x 48), their gradient slots (2 x 48) and slot stamps (2 x 8) and
-    quadrant bits (1); and the sort workspace's key, value, Gaussian and first-slot buffers
-    (24)."""
-    return 4 + 2 * (48 + 48 + 8) + 1 + 24
+    """Intersection lists: ids (4); the raster lists with room for two 8x8-quadrant entries
+    per tile entry (2 x 12: Gaussian, gradient slot, tile-list position), their gradient
+    slots (2 x 48) and slot stamps (2 x 4), and 4 quadrant bits (0.5, counted as 1); and the
+    sort workspace's key, value, Gaussian and first-slot buffers (24)."""
+    return 4 + 2 * (12 + 48 + 4) + 1 + 24
 
 
 def max_gaussians(hbm_bytes: float, sh_degree: int, adam: bool = True) -> int:

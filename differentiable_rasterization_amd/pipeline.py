@@ -82,14 +82,19 @@ class GaussianParams:
 
 
 class Projection:
-    def __init__(self, n, device="cuda"):
+    """Projected records of n Gaussians: depth keys, radii and the raster records, and with
+    plain=True also the plain record fields as planes (means2d [2][n], conic_opacity [4][n],
+    color [3][n]), which the training step itself never reads."""
+
+    def __init__(self, n, device="cuda", plain=False):
         n = max(n, 1)   # the raster entry points take the record pointers even for an empty scene
-        self.means2d = torch.zeros(n, 2, dtype=torch.float32, device=device)
-        self.conic_opacity = torch.zeros(n, 4, dtype=torch.float32, device=device)
-        self.color = torch.zeros(n, 3, dtype=torch.float32, device=device)
-        self.depth = torch.zeros(n, dtype=torch.float32, device=device)
+        z = lambda *shape: torch.zeros(*shape, dtype=torch.float32, device=device)
+        self.means2d = z(2, n) if plain else None
+        self.conic_opacity = z(4, n) if plain else None
+        self.color = z(3, n) if plain else None
+        self.depth = z(n)
         self.radii = torch.zeros(n, 2, dtype=torch.int32, device=device)
-        self.rec = torch.zeros(n, 12, dtype=torch.float32, device=device)   # raster-ready copy
+        self.rec = z(n, 12)   # raster record
 
     def abi(self) -> B.Projected:
         return B.projected(self.means2d, self.conic_opacity, self.color, self.depth, self.radii, self.rec)
@@ -193,10 +198,10 @@ class TrainStep:
     """One-view training step on one GPU: forward, L1 loss, backward, Adam."""
 
     def __init__(self, params: GaussianParams, width, height, device="cuda", raster=None, lr=DEFAULT_LR,
-                 capacity=0):
+                 capacity=0, plain=False):
         self.params = params
         self.raster = raster if raster is not None else B.make_params(params.sh_degree)
-        self.proj = Projection(params.n, device)
+        self.proj = Projection(params.n, device, plain)
         self.bins = Binning(params.n, width, height, capacity=capacity, device=device)
         self.frame = Frame(width, height, device)
         self.grads2d = torch.zeros(9, max(params.n, 1), dtype=torch.float32, device=device)

@@ -94,21 +94,23 @@ typedef struct {
 } gs_gaussians;
 
 /* Projected 2D records, one per Gaussian.
- *   means2d [n][2]        pixel coordinates (u, v) of the mean
- *   conic_opacity [n][4]  (A, B, C, o): inverse 2D covariance [[A, B], [B, C]] and opacity
- *                         (16-byte aligned)
- *   color [n][3]          RGB from the SH coefficients (no offset, no clamp)
  *   depth [n]             camera-space depth as a float32 key:
  *                         fma(R22, z, fma(R21, y, R20 * x)) + t2, each step rounded
  *   radii [n][2]          half-extents in pixels of the alpha >= alpha_min ellipse box,
- *                         rounded up, >= 1; (0, 0) marks a culled Gaussian.
- *   rec [n][12]           raster-ready copy of the same record (16-byte aligned): u, v, the
- *                         conic pre-scaled for a base-2 exponential (-A log2(e)/2,
- *                         -B log2(e), -C log2(e)/2), log2(o), red, green, blue, the index as
- *                         uint32 bits, rx and ry as int32 bits.  gs_bin_sort takes each
- *                         Gaussian's tile box and quadrant test from it and copies it per
- *                         list entry.
- * For culled Gaussians only radii and depth are written. */
+ *                         rounded up, >= 1; (0, 0) marks a culled Gaussian (8-byte aligned)
+ *   rec [n][12]           the raster record (16-byte aligned): u, v (pixel coordinates of
+ *                         the mean), the conic pre-scaled for a base-2 exponential
+ *                         (-A log2(e)/2, -B log2(e), -C log2(e)/2), log2(o), red, green,
+ *                         blue, the index as uint32 bits, rx and ry as int32 bits.
+ *                         gs_bin_sort takes each Gaussian's tile box and quadrant test from
+ *                         it and the raster entry points read it.  A culled Gaussian's
+ *                         record is zero apart from its index.
+ * Optional plain copies of the same record, planes of n floats; each pointer may be NULL,
+ * and then that group is not written:
+ *   means2d [2][n]        u, v
+ *   conic_opacity [4][n]  A, B, C, o: inverse 2D covariance [[A, B], [B, C]] and opacity
+ *   color [3][n]          RGB from the SH coefficients (no offset, no clamp)
+ * They are written for visible Gaussians only. */
 typedef struct {
     float *means2d, *conic_opacity, *color, *depth;
     int32_t *radii;

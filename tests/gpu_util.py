@@ -35,7 +35,6 @@ def synthetic_projection(m2, r, d):
     n = d.numel()
     proj = PL.Projection(max(n, 1), DEV)
     if n:
-        proj.means2d[:n].copy_(m2.to(DEV))
         proj.radii[:n].copy_(r.to(DEV))
         proj.depth[:n].copy_(d.to(DEV))
         proj.rec[:n, 0:2].copy_(m2.to(DEV))
@@ -58,14 +57,8 @@ def oracle_projection(P, n):
     rec[:, 9] = np.arange(n, dtype=np.uint32).view(np.float32)
     rec[:, 10:12] = np.ascontiguousarray(P.radii, np.int32).view(np.float32)
     proj = PL.Projection(n, DEV)
-    proj.means2d.copy_(torch.from_numpy(P.rec[:, :2].astype(np.float32)))
     proj.radii.copy_(torch.from_numpy(np.ascontiguousarray(P.radii, np.int32)))
     proj.depth.copy_(torch.from_numpy(P.dkey))
-    co = np.zeros((n, 4), np.float32)
-    co[:, :3] = P.rec[:, 2:5]
-    co[:, 3] = P.rec[:, 5]
-    proj.conic_opacity.copy_(torch.from_numpy(co))
-    proj.color.copy_(torch.from_numpy(P.rec[:, 6:9].astype(np.float32)))
     proj.rec.copy_(torch.from_numpy(rec))
     return proj
 
@@ -73,7 +66,7 @@ def oracle_projection(P, n):
 def gpu_forward(scene, cam, rp=None, capacity=0):
     """Project, bin and render one view on the GPU.  Returns the TrainStep holding the buffers."""
     params = PL.GaussianParams.from_scene(scene, DEV)
-    step = PL.TrainStep(params, cam.width, cam.height, DEV, raster=rp, capacity=capacity)
+    step = PL.TrainStep(params, cam.width, cam.height, DEV, raster=rp, capacity=capacity, plain=True)
     step.forward(B.camera_from(cam))
     torch.cuda.synchronize()
     return step
@@ -147,8 +140,10 @@ def compare_images(gpu_c, gpu_t, orc_c, orc_t, tie, gpu_n=None, orc_n=None, tol=
 def compare_projection(proj, P, ulps=2):
     """GPU projected records against the oracle's float32 record: cull decisions and
     depth keys bit-identical (outside marginal culls), radii equal, means within `ulps`
-    float32 ulps, opacity within 1 ulp, conic within 1e-6 of its largest entry, colour
-    within 2e-6."""
+    float32 ulps, conic within 1e-6 of its largest entry, colour within 2e-6, opacity within
+    1 ulp (its log2 in the raster record within what that ulp and one rounding allow).  Checked in the raster record, which
+    also carries the index and the radii (a culled Gaussian's record is zero apart from its
+    index), and in the plain record planes where the projection holds them."""
     radii = proj.radii.cpu().numpy()
     vis_g = (radii[:, 0] > 0) & (radii[:, 1] > 0)
     marg = P.marginal.astype(bool)
@@ -157,16 +152,37 @@ def compare_projection(proj, P, ulps=2):
     assert np.array_equal(dk.view(np.uint32), P.dkey.view(np.uint32)), "depth keys must be bit-identical"
     v = vis_g & P.vis.astype(bool)
     assert np.array_equal(radii[v], P.radii[v])
-    m2 = proj.means2d.cpu().numpy()[v]
-    co = proj.conic_opacity.cpu().numpy()[v]
-    col = proj.color.cpu().numpy()[v]
+    n = radii.shape[0]
+    grec = proj.rec.cpu().numpy()
+    bits = grec.view(np.uint32)
+    assert np.array_equal(bits[:, 9], np.arange(n, dtype=np.uint32)), "record index"
+    assert np.array_equal(bits[:, 10:12].view(np.int32), radii), "record radii"
+    culled = ~vis_g
+    assert not bits[culled][:, [0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 11]].any(), "a culled record must be zero"
     rec = P.rec[v]
+    g = grec[v]
     stats = dict(visible=int(v.sum()), marginal=int(marg.sum()),
-                 mean_ulps=int(ulp_diff(m2, rec[:, :2].astype(np.float32)).max()) if v.any() else 0)
+                 mean_ulps=int(ulp_diff(g[:, :2], rec[:, :2].astype(np.float32)).max()) if v.any() else 0)
     assert stats["mean_ulps"] <= ulps, stats
-    assert ulp_diff(co[:, 3], rec[:, 5].astype(np.float32)).max() <= 1
-    # conic: both sides invert Sigma2D in double; allow a few ulps of the larger entry
-    scale = np.abs(rec[:, 2:5]).max(axis=1, keepdims=True)
-    assert (np.abs(co[:, :3] - rec[:, 2:5]) / scale).max() < 1e-6
-    assert np.abs(col - rec[:, 6:9]).max() < 2e-6 * max(1.0, np.abs(rec[:, 6:9]).max())
+    if v.any():
+        # conic: both sides invert Sigma2D in double; allow a few ulps of the larger entry
+        l2e = 1.4426950408889634
+        want = rec[:, 2:5] * np.array([-0.5 * l2e, -l2e, -0.5 * l2e])
+        scale = np.abs(want).max(axis=1, keepdims=True)
+        assert (np.abs(g[:, 2:5] - want) / scale).max() < 1e-6
+        # log2 of the float32 opacity, rounded to float32: one ulp of o moves it by at most
+        # 1.8e-7, its own rounding by half an ulp of the result
+        lo = np.log2(rec[:, 5].astype(np.float32).astype(np.float64))
+        tol = 1.8e-7 + 2 * np.spacing(np.abs(lo).astype(np.float32)).astype(np.float64)
+        assert (np.abs(g[:, 5] - lo) <= tol).all()
+        assert np.abs(g[:, 6:9] - rec[:, 6:9]).max() < 2e-6 * max(1.0, np.abs(rec[:, 6:9]).max())
+    if proj.means2d is not None:
+        m2 = proj.means2d.cpu().numpy().T[v]
+        co = proj.conic_opacity.cpu().numpy().T[v]
+        col = proj.color.cpu().numpy().T[v]
+        assert np.array_equal(m2, g[:, :2]), "plain means equal the record's"
+        assert np.array_equal(col, g[:, 6:9]), "plain colour equals the record's"
+        assert ulp_diff(co[:, 3], rec[:, 5].astype(np.float32)).max() <= 1
+        scale = np.abs(rec[:, 2:5]).max(axis=1, keepdims=True)
+        assert (np.abs(co[:, :3] - rec[:, 2:5]) / scale).max() < 1e-6
     return stats

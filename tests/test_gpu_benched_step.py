@@ -133,9 +133,8 @@ def test_1m_1080p_benched_step_against_oracle():
         c, t, nc = cams[i], targets[i], cams[(i + 1) % nviews]
         before = dict(p=cpu(params.data), m=cpu(params.m), v=cpu(params.v),
                       proj=PL.Projection(sc.n, DEV))
-        for a, b in zip((before["proj"].means2d, before["proj"].conic_opacity, before["proj"].color,
-                         before["proj"].depth, before["proj"].radii),
-                        (st.proj.means2d, st.proj.conic_opacity, st.proj.color, st.proj.depth, st.proj.radii)):
+        for a, b in zip((before["proj"].depth, before["proj"].radii, before["proj"].rec),
+                        (st.proj.depth, st.proj.radii, st.proj.rec)):
             a.copy_(b)
         graphs[i].replay()
         st.fused_l1(c, t)

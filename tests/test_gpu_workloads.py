@@ -325,7 +325,7 @@ def test_tile_band_renderers_decode_to_full_gradients():
     st.backward(c, dL_dcolor=G, grads3d=False)
     full = st.grads2d.clone()
     n = params.n
-    m2 = st.proj.means2d.cpu().numpy().astype(np.float64)
+    m2 = st.proj.rec[:, :2].cpu().numpy().astype(np.float64)
     radii = st.proj.radii.cpu().numpy()
     vis = (radii > 0).all(axis=1)
     # rows a footprint can reach (one pixel of slack around the bounding box)
