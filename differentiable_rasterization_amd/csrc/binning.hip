@@ -57,7 +57,9 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *wsum)
 
 // Loads Gaussian t of the block (valid: it is listed; otherwise it has no entries) into
 // the shared state and sets the block-local offsets.  Returns the block's entry count.
-// copy (may be NULL): receives the Gaussian's record (its three float4 words).
+// STRIDE: float4 words per record in rec (the projection's 3, or 4 for the binning's 64-byte
+// copy).  copy (may be NULL): receives the Gaussian's record (its three float4 words).
+template <int STRIDE>
 __device__ __forceinline__ uint32_t coop_load(Coop &S, bool valid, uint32_t g, const float4 *__restrict__ rec,
                                               int tx, int ty, uint32_t &c_out, float4 *__restrict__ copy = nullptr)
 {
@@ -67,9 +69,9 @@ __device__ __forceinline__ uint32_t coop_load(Coop &S, bool valid, uint32_t g, c
     int x0 = 0, w = 1;
     int y0 = 0;
     if (valid) {
-        p0 = rec[gsr::kRecF4 * (size_t)g];
-        p1 = rec[gsr::kRecF4 * (size_t)g + 1];
-        p2 = rec[gsr::kRecF4 * (size_t)g + 2];
+        p0 = rec[STRIDE * (size_t)g];
+        p1 = rec[STRIDE * (size_t)g + 1];
+        p2 = rec[STRIDE * (size_t)g + 2];
         int x1, y1;
         gsd::tile_rect(p0.x, p0.y, __float_as_int(p2.z), __float_as_int(p2.w), tx, ty, x0, x1, y0, y1);
         if (x1 > x0 && y1 > y0) {
@@ -186,8 +188,8 @@ __global__ __launch_bounds__(256) void k_keys_count(const int2 *__restrict__ rad
         keys[i] = vis ? __float_as_uint(depth[i]) : kCulledKey;
     }
     uint32_t c;
-    const uint32_t C = coop_load(S, vis, (uint32_t)i, rec, tx, ty, c,
-                                 i < n ? grec + gsr::kGRecF4 * (size_t)i : nullptr);
+    const uint32_t C = coop_load<gsr::kRecF4>(S, vis, (uint32_t)i, rec, tx, ty, c,
+                                              i < n ? grec + gsr::kGRecF4 * (size_t)i : nullptr);
     for (uint32_t e0 = 0; e0 < C; e0 += 256u) coop_count_round(S, e0, C, log2_amin);
     __syncthreads();
     if (i < n) {
@@ -210,9 +212,11 @@ __device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned lo
 // tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at) and the
 // value (gradient slot of its first quadrant record) << 32 | its Gaussian, carried through
 // the tile sort.  Gaussian g's quadrant records own slots qoff[g] .. qoff[g + 1], in the
-// order of its entries and, within an entry, of the quadrants.
-__global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals, const uint32_t *__restrict__ off, const uint32_t *__restrict__ qoff,
-                                              const float4 *__restrict__ rec, float log2_amin, int64_t n, int tx,
+// order of its entries and, within an entry, of the quadrants.  The records are gathered in
+// depth order from the 64-byte-aligned copy grec (one aligned run per Gaussian).
+__global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals, const uint32_t *__restrict__ off,
+                                              const uint32_t *__restrict__ qoff, const float4 *__restrict__ grec,
+                                              float log2_amin, int64_t n, int tx,
                                               int ty, const unsigned long long *__restrict__ tot, int64_t cap,
                                               unsigned long long grec_off,
                                               unsigned long long *__restrict__ klen, gsr::BinsHeader *__restrict__ hdr,
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals
     const bool listed = (sv >> 32) != 0u;   // culled Gaussians and those off the image have no tiles
     const uint32_t g = (uint32_t)sv;
     uint32_t c;
-    const uint32_t C = coop_load(S, listed, g, rec, tx, ty, c);
+    const uint32_t C = coop_load<gsr::kGRecF4>(S, listed, g, grec, tx, ty, c);
     if (C == 0) return;
     S.qbase[threadIdx.x] = listed ? qoff[g] : 0u;
     const uint64_t base = off[j0];
@@ -257,41 +261,58 @@ __global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals
     }
 }
 
+// Each wave of the two passes below takes kWaveWords consecutive 64-entry words, with all
+// of its loads issued before any use (the passes are latency-bound).
+constexpr int kWaveWords = 4;
+
 // Finishes the sorted lists in one pass over the entries: the Gaussian index of each
 // entry, tile_ranges[t] = first entry of tile t (entries are sorted by tile; ranges[T] =
-// K), and the quadrant bitmaps with their per-word bit counts (one 64-bit word per wave and
-// quadrant; block bases are multiples of 64).  Every word of the bitmaps and of `wcnt`
-// [4][words + 1] is written (zero past the entries); the exclusive scan of wcnt gives the
-// positions of the quadrant records.  The launch covers max(capacity, T + 1) threads (all
-// `words` words); K is read on the device.
+// K), and the quadrant bitmaps with their per-word bit counts (one 64-bit word per 64
+// entries and quadrant).  Every word of the bitmaps and of `wcnt` [4][words + 1] is written
+// (zero past the entries); the exclusive scan of wcnt gives the positions of the quadrant
+// records.  The launch covers max(words, ceil((T + 1) / 64)) words; K is read on the device.
 __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tkeys, const uint64_t *__restrict__ tvals,
                                                 const unsigned long long *__restrict__ klen, int32_t T,
                                                 uint32_t *__restrict__ ids, int32_t *__restrict__ ranges,
                                                 int64_t words, uint64_t *__restrict__ bitmap,
                                                 uint32_t *__restrict__ wcnt)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t w0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kWaveWords;   // first word of the wave
     const int64_t K = (int64_t)*klen;
-    if (k < gsr::kQuads) wcnt[(int64_t)k * (words + 1) + words] = 0u;
-    if (K == 0 && k <= T) ranges[k] = 0;   // no entries (or lists that did not fit): all lists empty
-    uint32_t qm = 0;
-    if (k < K) {
-        const uint32_t key = tkeys[k];
-        const int32_t t = (int32_t)(key & gsr::kTileMask);
-        qm = key >> gsr::kMaskShift;
-        ids[k] = (uint32_t)tvals[k];
-        const int32_t prev = k > 0 ? (int32_t)(tkeys[k - 1] & gsr::kTileMask) : -1;
-        for (int32_t u = prev + 1; u <= t; ++u) ranges[u] = (int32_t)k;
-        if (k == K - 1)
-            for (int32_t u = t + 1; u <= T; ++u) ranges[u] = (int32_t)K;
-    }
-    const int64_t wbase = k - (threadIdx.x & 63);
+    if (w0 == 0 && lane < gsr::kQuads) wcnt[(int64_t)lane * (words + 1) + words] = 0u;
+    uint32_t key[kWaveWords], prev[kWaveWords];
+    uint64_t tv[kWaveWords];
 #pragma unroll
-    for (int q = 0; q < gsr::kQuads; ++q) {
-        const uint64_t b = __ballot((qm >> q) & 1u);
-        if ((threadIdx.x & 63) == 0 && (wbase >> 6) < words) {
-            bitmap[(int64_t)q * words + (wbase >> 6)] = b;
-            wcnt[(int64_t)q * (words + 1) + (wbase >> 6)] = (uint32_t)__popcll(b);
+    for (int i = 0; i < kWaveWords; ++i) {
+        const int64_t k = (w0 + i) * 64 + lane;
+        const int64_t kc = k < K ? k : K - 1, kp = kc > 0 ? kc - 1 : 0;   // clamped: loads stay in range
+        key[i] = K > 0 ? tkeys[kc] : 0u;
+        prev[i] = K > 0 ? tkeys[kp] : 0u;
+        tv[i] = K > 0 ? tvals[kc] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < kWaveWords; ++i) {
+        const int64_t k = (w0 + i) * 64 + lane;
+        if (K == 0 && k <= T) ranges[k] = 0;   // no entries (or lists that did not fit): all lists empty
+        uint32_t qm = 0;
+        if (k < K) {
+            const int32_t t = (int32_t)(key[i] & gsr::kTileMask);
+            qm = key[i] >> gsr::kMaskShift;
+            ids[k] = (uint32_t)tv[i];
+            const int32_t pt = k > 0 ? (int32_t)(prev[i] & gsr::kTileMask) : -1;
+            for (int32_t u = pt + 1; u <= t; ++u) ranges[u] = (int32_t)k;
+            if (k == K - 1)
+                for (int32_t u = t + 1; u <= T; ++u) ranges[u] = (int32_t)K;
+        }
+        const int64_t wd = w0 + i;
+#pragma unroll
+        for (int q = 0; q < gsr::kQuads; ++q) {
+            const uint64_t b = __ballot((qm >> q) & 1u);
+            if (lane == 0 && wd < words) {
+                bitmap[(int64_t)q * words + wd] = b;
+                wcnt[(int64_t)q * (words + 1) + wd] = (uint32_t)__popcll(b);
+            }
         }
     }
 }
@@ -312,47 +333,47 @@ __device__ __forceinline__ int64_t xcd_contiguous_block(int64_t active)
 
 __global__ __launch_bounds__(256) void k_quad_lists(const uint32_t *__restrict__ tkeys, const uint64_t *__restrict__ tvals,
                                                     const unsigned long long *__restrict__ klen, int64_t words,
-                                                    const uint64_t *__restrict__ bitmap,
                                                     const uint32_t *__restrict__ wpre, uint2 *__restrict__ qent,
                                                     uint32_t *__restrict__ qk)
 {
+    constexpr int64_t kBlockEntries = 4 * 64 * kWaveWords;
     const int64_t K = (int64_t)*klen;
-    const int64_t blk = xcd_contiguous_block((K + 255) / 256);
+    const int64_t blk = xcd_contiguous_block((K + kBlockEntries - 1) / kBlockEntries);
     if (blk < 0) return;
     const int lane = threadIdx.x & 63;
-    const int64_t k = blk * 256 + threadIdx.x;
-    if (k - lane >= K) return;   // the whole wave lies past the lists
-    const uint32_t qm = k < K ? tkeys[k] >> gsr::kMaskShift : 0u;
-    uint32_t g = 0, slot = 0;
-    if (qm) {
-        const uint64_t tvk = tvals[k];
-        g = (uint32_t)tvk;
-        slot = (uint32_t)(tvk >> 32);
+    const int64_t w0 = (blk * 4 + (threadIdx.x >> 6)) * kWaveWords;   // first word of the wave
+    if (w0 * 64 >= K) return;   // the whole wave lies past the lists
+    // The entries of one 64-entry word that belong to list q are one run that starts at the
+    // scanned count of that word: lane 4 i + q loads it for word w0 + i and list q.
+    static_assert(gsr::kQuads == 4 && 4 * kWaveWords <= 64, "one lookup lane per word and quadrant");
+    uint32_t start = 0;
+    if (lane < 4 * kWaveWords && w0 + (lane >> 2) < words)
+        start = wpre[(int64_t)(lane & 3) * (words + 1) + w0 + (lane >> 2)];
+    uint32_t key[kWaveWords];
+    uint64_t tv[kWaveWords];
+#pragma unroll
+    for (int i = 0; i < kWaveWords; ++i) {
+        const int64_t k = (w0 + i) * 64 + lane;
+        const int64_t kc = k < K ? k : K - 1;   // clamped: loads stay in range
+        key[i] = tkeys[kc];
+        tv[i] = tvals[kc];
     }
     const uint64_t below = (1ull << lane) - 1ull;
-    // The wave's entries are consecutive, so its entries of list q are one run that starts
-    // where the first of them goes.  Lane q looks that position up for list q: four
-    // independent lookups instead of a chain of four.
-    static_assert(gsr::kQuads == 4, "one lookup lane per quadrant");
-    uint64_t bals[gsr::kQuads];
 #pragma unroll
-    for (int q = 0; q < gsr::kQuads; ++q) bals[q] = __ballot((qm >> q) & 1u);
-    uint32_t start = 0;
-    {
-        const uint64_t mine = lane == 0 ? bals[0] : lane == 1 ? bals[1] : lane == 2 ? bals[2] : bals[3];
-        if (lane < gsr::kQuads && mine)
-            start = gsr::quad_prefix(bitmap + (int64_t)lane * words, wpre + (int64_t)lane * (words + 1),
-                                     (uint32_t)(k - lane + __builtin_ctzll(mine)));
-    }
+    for (int i = 0; i < kWaveWords; ++i) {
+        const int64_t k = (w0 + i) * 64 + lane;
+        const uint32_t qm = k < K ? key[i] >> gsr::kMaskShift : 0u;
+        const uint32_t g = (uint32_t)tv[i];
+        uint32_t slot = (uint32_t)(tv[i] >> 32);
 #pragma unroll
-    for (int q = 0; q < gsr::kQuads; ++q) {
-        const uint64_t bal = bals[q];
-        if (!bal) continue;
-        const uint32_t pos0 = __shfl(start, q, 64);
-        if ((qm >> q) & 1u) {
-            const uint32_t pos = pos0 + (uint32_t)__popcll(bal & below);
-            qent[pos] = make_uint2(g, slot++);
-            qk[pos] = (uint32_t)k;
+        for (int q = 0; q < gsr::kQuads; ++q) {
+            const uint64_t bal = __ballot((qm >> q) & 1u);
+            const uint32_t pos0 = __shfl(start, 4 * i + q, 64);
+            if ((qm >> q) & 1u) {
+                const uint32_t pos = pos0 + (uint32_t)__popcll(bal & below);
+                qent[pos] = make_uint2(g, slot++);
+                qk[pos] = (uint32_t)k;
+            }
         }
     }
 }
@@ -595,9 +616,10 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     //    slot of each Gaussian (exclusive scan of its record counts) and the total Q; the
     //    same scan zeroes the stamps of the slots it gives out (those that fit), so no slot
     //    of this sort carries a backward call's stamp before one writes it
+    float4 *grec = reinterpret_cast<float4 *>(rb + RL.grec);
     k_keys_count<<<gn, 256, 0, stream>>>(rr, proj->depth, prec, log2_amin, n, tx, ty, dkA, dvA, qcnt,
                                          bins->tiles_touched, (uint32_t *)(ws + L.zero), (int64_t)(L.zero_bytes / 4),
-                                         reinterpret_cast<float4 *>(rb + RL.grec));
+                                         grec);
     GS_LAUNCH_CHECK("k_keys_count");
     uint32_t *qstamp = reinterpret_cast<uint32_t *>(rb + RL.qstamp);
     if ((s = lb_scan_u32(qcnt, qoff, n + 1, scQ, tickets + kTkQcnt, total + 1, stream, qstamp,
@@ -616,7 +638,7 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     // 3. emit entries in depth order (nothing if the lists do not fit), then a stable sort
     //    of (tile key, emit position) by tile
     const int tbits = L.tbits;
-    k_emit<<<gn, 256, 0, stream>>>(sv, doff, qoff, prec, log2_amin, n, tx, ty, total, cap,
+    k_emit<<<gn, 256, 0, stream>>>(sv, doff, qoff, grec, log2_amin, n, tx, ty, total, cap,
                                    (unsigned long long)RL.grec, klen, hdr, counts, tkA, tvA);
     GS_LAUNCH_CHECK("k_emit");
     if (cap == 0) {
@@ -638,12 +660,13 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     uint64_t *bm = reinterpret_cast<uint64_t *>(rb + RL.bitmap);
     uint32_t *wpre = reinterpret_cast<uint32_t *>(rb + RL.wpre);
     const int64_t nw = gsr::kQuads * (RL.words + 1);
-    k_finish<<<(unsigned)ceil_div(std::max<int64_t>(cap, (int64_t)T + 1), 256), 256, 0, stream>>>(
-        tk, tv, klen, T, bins->ids, bins->tile_ranges, RL.words, bm, wpre);
+    const int64_t fwords = std::max<int64_t>(RL.words, ceil_div((int64_t)T + 1, 64));
+    k_finish<<<(unsigned)ceil_div(fwords, 4 * kWaveWords), 256, 0, stream>>>(tk, tv, klen, T, bins->ids,
+                                                                            bins->tile_ranges, RL.words, bm, wpre);
     GS_LAUNCH_CHECK("k_finish");
     if ((s = lb_scan_u32(wpre, wpre, nw, scW, tickets + kTkWpre, nullptr, stream)) != GS_OK) return s;
-    k_quad_lists<<<gk, 256, 0, stream>>>(tk, tv, klen, RL.words, bm, wpre, reinterpret_cast<uint2 *>(rb + RL.qent),
-                                         reinterpret_cast<uint32_t *>(rb + RL.qk));
+    k_quad_lists<<<(unsigned)ceil_div(cap, 4 * 64 * kWaveWords), 256, 0, stream>>>(
+        tk, tv, klen, RL.words, wpre, reinterpret_cast<uint2 *>(rb + RL.qent), reinterpret_cast<uint32_t *>(rb + RL.qk));
     GS_LAUNCH_CHECK("k_quad_lists");
     if (bins->keys) {
         k_keys64<<<gk, 256, 0, stream>>>(tk, bins->ids, proj->depth, klen, bins->keys);
