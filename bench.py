@@ -385,21 +385,33 @@ def choose_binning_launch(one_step, use_graph, step0, n, slots):
 
 
 class CallTimer:
-    """Timing events around calls, summed by name after a synchronisation."""
+    """Timing events around calls, summed by name after a synchronisation.  The events come
+    from a pool created up front (n_events of them), so that no event is created between
+    the calls being timed: creating HIP events inside a timed loop left one-time host stalls
+    of tens of ms in the partitioned step's trace, with the GPU idle.  `created_late` counts
+    events the pool could not supply."""
 
-    def __init__(self):
+    def __init__(self, n_events=0):
         self.marks = []
+        self.pool = [TimingEvent() for _ in range(n_events)]
+        self.created_late = 0
+
+    def _event(self):
+        if self.pool:
+            return self.pool.pop()
+        self.created_late += 1
+        return TimingEvent()
 
     def __call__(self, name):
         timer = self
 
         class _Ctx:
             def __enter__(self):
-                self.a = TimingEvent()
+                self.a = timer._event()
                 self.a.record()
 
             def __exit__(self, *exc):
-                b = TimingEvent()
+                b = timer._event()
                 b.record()
                 timer.marks.append((name, self.a, b))
         return _Ctx()
@@ -471,7 +483,12 @@ def main_partitioned(args):
     torch.cuda.synchronize()
     for st in ps.parts:
         st.frame.n_trav_sum.zero_()
-    timer = CallTimer()
+    probe = CallTimer()
+    one_step(probe)   # one more untimed step, to count the timed calls of a step
+    torch.cuda.synchronize()
+    for st in ps.parts:
+        st.frame.n_trav_sum.zero_()
+    timer = CallTimer(2 * len(probe.marks) * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -529,6 +546,7 @@ def main_partitioned(args):
         "records_per_step": records,
         "visible_gaussians": n_vis,
         "kernels_note": "every call timed with events in the timed steps; summed over the slabs",
+        "timing_events_created_in_timed_steps": timer.created_late,
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
         "cpu_baseline": None,

@@ -11,10 +11,14 @@ namespace gsr {
 // The quadrant lists hold per record its Gaussian g and gradient slot (qent); the record
 // itself (centre, pre-scaled conic, log2 opacity, colour) is the Gaussian's raster record
 // in grec, fetched by g with scalar loads.  A wave reads the entries of its list 64
-// at a time with one vector load (lane l: entry c + l), one chunk ahead, and takes each
-// record's g and slot out of those registers (v_readlane).
+// at a time with one vector load (lane l: entry c + l), two chunks ahead, and takes each
+// record's g and slot out of those registers (v_readlane).  One chunk ahead, each lane
+// also loads one word of its entry's record, so that the records a chunk's scalar loads
+// fetch are in L2 by then (the records are scattered over the Gaussian array; without it
+// each batch waited for HBM).
 struct Chunks {
-    uint2 e0, e1;   // entries of chunks base and base + 64
+    uint2 e0, e1, e2;   // entries of chunks base, base + 64 and base + 128
+    float pf;           // the record word loaded to warm L2 (consumed one chunk later)
     uint32_t base, last;
     const uint2 *qent;
     const float4 *grec;
@@ -31,6 +35,8 @@ struct Chunks {
         asm volatile("v_mov_b32 %0, %2\n\tv_mov_b32 %1, %3" : "=v"(x), "=v"(y) : "v"(v.x), "v"(v.y));
         return make_uint2(x, y);
     }
+    // one word of the record of this lane's entry of chunk base + 64 (e1, arrived)
+    __device__ __forceinline__ void warm() { pf = grec[kGRecF4 * (size_t)e1.x].x; }
     // for a non-empty list j0 .. j1
     __device__ __forceinline__ void init(const uint2 *q, const float4 *g, uint32_t j0, uint32_t j1)
     {
@@ -39,19 +45,27 @@ struct Chunks {
         base = j0;
         last = j1 - 1u;
         const uint2 first = load(j0);
-        e1 = load(j0 + 64u);
+        const uint2 second = load(j0 + 64u);
         e0 = moved(first);
+        e1 = moved(second);
+        __builtin_amdgcn_sched_barrier(0);
+        warm();
+        e2 = load(j0 + 128u);
     }
-    // at the first record of the next chunk (its entries were loaded one chunk ago).  The
-    // move of e1 into e0 is ordered before the next load, so that the load can write e1's
-    // registers directly: as a plain assignment, the compiler issued the load into
-    // temporaries and copied them afterwards, which waits for the load just issued.
+    // at the first record of the next chunk (its entries were loaded two chunks ago, those
+    // of the chunk after it one chunk ago).  The moves are ordered before the next loads, so
+    // that the loads can write their registers directly: as plain assignments, the compiler
+    // issued the loads into temporaries and copied them afterwards, which waits for the
+    // loads just issued.
     __device__ __forceinline__ void advance()
     {
         base += 64u;
+        asm volatile("" ::"v"(pf));   // the previous warming load (long arrived)
         e0 = moved(e1);
+        e1 = moved(e2);
         __builtin_amdgcn_sched_barrier(0);
-        e1 = load(base + 64u);
+        warm();
+        e2 = load(base + 128u);
     }
     // entries of records j .. j + kN - 1 (all in one chunk: base <= j, j + kN <= base + 128,
     // j - base a multiple of kN), uniform across the wave; the chunk is chosen by a uniform
@@ -88,7 +102,7 @@ struct Chunks {
             for (int i = 0; i < kN; ++i) g[i] = (uint32_t)__builtin_amdgcn_readlane((int)e1.x, ln + i);
         }
     }
-    __device__ __forceinline__ void finish() const {}
+    __device__ __forceinline__ void finish() const { asm volatile("" ::"v"(pf)); }
 };
 
 // One batch of records in scalar registers.

@@ -236,3 +236,49 @@ def test_batch_argument_errors_before_launch():
     st = B._lib.gs_grad_aggregate_adam_batch(ctypes.byref(g), 2, bins, cams, ctypes.byref(p), 0.5, ctypes.byref(m),
                                              ctypes.byref(m), ctypes.byref(lr), 1, 0.9, 0.999, 1e-15, None, None, None)
     assert st == B.GS_ERR_INVALID_ARGUMENT      # the bins have no tile lists
+
+
+def _signature(name):
+    text = open(os.path.join(ROOT, "include", "gs.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    return [" ".join(a.split()) for a in m.group(1).split(",")]
+
+
+def _struct_fields(name):
+    text = open(os.path.join(ROOT, "include", "gs.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    m = re.search(r"typedef struct \{([^}]*)\}\s*" + name + r"\s*;", text)
+    assert m, name
+    return " ".join(m.group(1).split())
+
+
+def test_boundary_departures_from_the_planned_abi_are_the_recorded_ones():
+    """Where the C ABI differs from the planned boundary, it differs exactly as recorded:
+    gs_bin_sort takes the raster parameters (alpha_min decides the quadrant lists);
+    gs_raster_fwd reports the traversed entries per pixel (n_trav) and their sum instead of
+    taking n_isect; gs_raster_bwd writes grads2d (no accumulation) and takes color and
+    n_trav from the forward pass; gs_loss_l1 takes a workspace for its deterministic
+    two-level sum; gs_adam_step reads the gradients without zeroing them; gs_projected holds
+    the raster record, with the plain fields as optional planes and the radii interleaved;
+    gs_bins holds the raster buffer, with keys and tiles_touched optional."""
+    assert "const gs_raster_params *p" in _signature("gs_bin_sort")
+    fwd = _signature("gs_raster_fwd")
+    assert "int32_t *n_trav" in fwd and "unsigned long long *n_trav_sum" in fwd
+    assert not any("n_isect" in a for a in fwd)
+    bwd = _signature("gs_raster_bwd")
+    assert "float *grads2d" in bwd and "const int32_t *n_trav" in bwd and "const float *color" in bwd
+    loss = _signature("gs_loss_l1")
+    assert "void *workspace" in loss and "size_t workspace_bytes" in loss
+    adam = _signature("gs_adam_step")
+    assert adam[0] == "const gs_adam_group *groups"
+    assert "const float *g;" in _struct_fields("gs_adam_group")   # the gradients are an input only
+    proj = _struct_fields("gs_projected")
+    assert proj == "float *means2d, *conic_opacity, *color, *depth; int32_t *radii; float *rec;"
+    bins = _struct_fields("gs_bins")
+    assert "void *raster" in bins and "tiles_touched" in bins and "keys" in bins
+    header = open(os.path.join(ROOT, "include", "gs.h")).read()
+    assert "The gradients are read, not modified." in header
+    assert "Every entry of\n * grads2d is written" in header
+    assert "each pointer may be NULL,\n * and then that group is not written" in header

@@ -333,9 +333,12 @@ def test_backward_parity(name, with_gt):
              ("means", "log_scales", "quats", "opacity_logits", "sh")}
     log(f"  grads3d rel-L2 {errs3}")
     assert max(errs3.values()) <= 1e-3, errs3
-    # repeat: the per-Gaussian sums run in a fixed order, so the gradients are bit-identical
+    # repeat: the per-Gaussian sums run in a fixed order, so the gradients are bit-identical;
+    # grads2d and grads3d are written, not accumulated, so what they held before is irrelevant
     first = st.grads2d.clone()
     first3 = gp.grad.clone()
+    st.grads2d.fill_(7.0)
+    gp.grad.fill_(-3.0)
     st.backward(B.camera_from(cam), dL_dcolor=Gd, dL_dt=GTd)
     torch.cuda.synchronize()
     assert torch.equal(st.grads2d, first) and torch.equal(gp.grad, first3)
@@ -643,7 +646,8 @@ def test_adam_parity(n, step):
     dev = [([t.to(DEV).contiguous() for t in st], lr) for st, lr in host]
     B.gs_adam_step([(p, g, m, v, lr) for (p, g, m, v), lr in dev], step, 0.9, 0.999, 1e-15)
     torch.cuda.synchronize()
-    for ((p, g, m, v), lr), ((dp, _, dm, dv), _) in zip(host, dev):
+    for ((p, g, m, v), lr), ((dp, dg, dm, dv), _) in zip(host, dev):
+        assert torch.equal(dg.cpu(), g), "the gradients are read, not modified"
         po, mo, vo = oracle.adam(p, g, m, v, float(np.float32(lr)), float(np.float32(0.9)),
                                  float(np.float32(0.999)), float(np.float32(1e-15)), step)
         assert rel_l2(dp.cpu().numpy(), po) <= 1e-6
