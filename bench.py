@@ -183,8 +183,8 @@ def hbm_bytes(kernel, n, n_vis, k_sh, n_isect, n_px):
         return 36 * n_isect + 36 * n                                # one partial per (tile, Gaussian); grads2d
     if kernel == "grad_adam":                                       # partials; p, m, v read and written
         return 36 * n_isect + n * (11 + 3 * k_sh) * 24
-    if kernel == "grad_adam_project":                               # the same + the next view's records
-        return 36 * n_isect + n * (11 + 3 * k_sh) * 24 + n_vis * 96 + (n - n_vis) * 12
+    if kernel == "grad_adam_project":                               # the same + the next view's projection
+        return 36 * n_isect + n * (11 + 3 * k_sh) * 24 + n_vis * 60 + (n - n_vis) * 12
     return None
 
 
