@@ -246,7 +246,8 @@ gs_status gs_loss_l1(const float *color, const float *target, int64_t n_px, floa
  * <= 1 (lambda = 0 is gs_loss_l1's objective); loss_out, ssim_out: device floats (each may
  * be NULL), the sums taken in double in a fixed order.  workspace:
  * gs_loss_l1_dssim_workspace_bytes(W, H) bytes (256-byte aligned): three coefficient maps
- * per channel (36 B per pixel) and per-tile partial sums. */
+ * per channel (36 B per pixel) and per-tile partial sums.  Images of 12 W H >= 2^32 bytes
+ * (the kernels index in 32 bits) return GS_ERR_UNSUPPORTED, and their workspace size is 0. */
 size_t gs_loss_l1_dssim_workspace_bytes(int32_t width, int32_t height);
 gs_status gs_loss_l1_dssim(const float *color, const float *target, int32_t width, int32_t height, float lambda,
                            float *loss_out, float *ssim_out, float *dL_dcolor, void *workspace,

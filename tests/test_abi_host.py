@@ -81,6 +81,24 @@ def test_argument_errors_before_launch():
     assert st == B.GS_ERR_INVALID_ARGUMENT and "k must" in B.last_error()
 
 
+def test_dssim_argument_errors_before_launch():
+    """gs_loss_l1_dssim rejects sizes, NULL buffers, lambda outside [0, 1], images whose
+    12 W H bytes need more than 32-bit offsets and short workspaces before any launch (the
+    non-NULL addresses below are never dereferenced)."""
+    fake = ctypes.c_void_p(256)
+    call = lambda w, h, lam, ws_bytes, color=fake: B._lib.gs_loss_l1_dssim(
+        color, fake, w, h, lam, None, None, fake, fake, ws_bytes, None)
+    assert call(0, 10, 0.2, 1 << 30) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(70000, 10, 0.2, 1 << 30) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(16, 16, 0.2, 1 << 30, color=None) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(16, 16, 1.5, 1 << 30) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(16, 16, float("nan"), 1 << 30) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(20000, 20000, 0.2, 1 << 62) == B.GS_ERR_UNSUPPORTED and "2^32" in B.last_error()
+    assert B.gs_loss_l1_dssim_workspace_bytes(20000, 20000) == 0
+    assert B.gs_loss_l1_dssim_workspace_bytes(16384, 16384) >= 36 * 16384 * 16384
+    assert call(16, 16, 0.2, B.gs_loss_l1_dssim_workspace_bytes(16, 16) - 1) == B.GS_ERR_INVALID_ARGUMENT
+
+
 class _NullStream:
     cuda_stream = 0
 
