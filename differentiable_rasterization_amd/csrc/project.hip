@@ -115,20 +115,39 @@ __device__ __forceinline__ void sh_grad(float x, float y, float z, const float *
 }
 
 // Everything the forward computes for one Gaussian, kept for the backward.
+// What the projection backward needs of the forward; the matrices R(q^), M, Sigma and T are
+// recomputed from these by the same code (rot_q, cov3d, jw), so they need not stay live.
 struct Proj {
     bool vis;
     float key;
-    double mu[3], s[3], q[4], qnorm, o;
-    double Rq[9];        // rotation of q^
-    double M[9];         // Rq diag(s)
-    double Sig[6];       // xx, xy, xz, yy, yz, zz
+    double s[3], q[4], qnorm, o;
     double X, Y, Z, u, v;
-    double T[6];         // J W, 2x3
-    double a, b, c, det, A, B, C;
+    double a, b, c, A, B, C;
     double dist;
     float dir[3];        // unit view direction
     int rx, ry;
 };
+
+// R(q^) of the unit quaternion (w, x, y, z), row-major.
+__device__ __forceinline__ void rot_q(double w, double x, double y, double z, double (&R)[9])
+{
+    R[0] = 1.0 - 2.0 * (y * y + z * z); R[1] = 2.0 * (x * y - w * z);       R[2] = 2.0 * (x * z + w * y);
+    R[3] = 2.0 * (x * y + w * z);       R[4] = 1.0 - 2.0 * (x * x + z * z); R[5] = 2.0 * (y * z - w * x);
+    R[6] = 2.0 * (x * z - w * y);       R[7] = 2.0 * (y * z + w * x);       R[8] = 1.0 - 2.0 * (x * x + y * y);
+}
+
+// M = R diag(s) and Sigma = M M^T (xx, xy, xz, yy, yz, zz).
+__device__ __forceinline__ void cov3d(const double (&R)[9], const double (&s)[3], double (&M)[9], double (&Sig)[6])
+{
+    for (int r = 0; r < 3; ++r)
+        for (int c = 0; c < 3; ++c) M[3 * r + c] = R[3 * r + c] * s[c];
+    Sig[0] = M[0] * M[0] + M[1] * M[1] + M[2] * M[2];
+    Sig[1] = M[0] * M[3] + M[1] * M[4] + M[2] * M[5];
+    Sig[2] = M[0] * M[6] + M[1] * M[7] + M[2] * M[8];
+    Sig[3] = M[3] * M[3] + M[4] * M[4] + M[5] * M[5];
+    Sig[4] = M[3] * M[6] + M[4] * M[7] + M[5] * M[8];
+    Sig[5] = M[6] * M[6] + M[7] * M[7] + M[8] * M[8];
+}
 
 __device__ __forceinline__ bool finite_d(double x) { return __builtin_isfinite(x); }
 
@@ -158,6 +177,18 @@ __device__ __forceinline__ void project_scalars(double mx, double my, double mz,
     S.ok = true;
 }
 
+// T = J W (2 x 3): the projection's Jacobian at camera-space (X, Y, Z) times the rotation.
+__device__ __forceinline__ void jw(const CamD &cam, double X, double Y, double Z, double (&T)[6])
+{
+    const double iz = 1.0 / Z;
+    const double j00 = cam.fx * iz, j02 = -cam.fx * X * iz * iz;
+    const double j11 = cam.fy * iz, j12 = -cam.fy * Y * iz * iz;
+    for (int c = 0; c < 3; ++c) {
+        T[c] = j00 * cam.R[c] + j02 * cam.R[6 + c];
+        T[3 + c] = j11 * cam.R[3 + c] + j12 * cam.R[6 + c];
+    }
+}
+
 // The projection for one camera, from the Gaussian's parameters and its ProjScalars.
 __device__ __forceinline__ void project_view(const CamD &cam, double mx, double my, double mz, float fmx, float fmy,
                                              float fmz, double q0, double q1, double q2, double q3,
@@ -170,7 +201,6 @@ __device__ __forceinline__ void project_view(const CamD &cam, double mx, double 
     if (!S.ok) return;
     if (!(P.key >= depth_lo && P.key < depth_hi)) return;
     P.qnorm = S.qnorm;
-    P.mu[0] = mx; P.mu[1] = my; P.mu[2] = mz;
     P.X = cam.R[0] * mx + cam.R[1] * my + cam.R[2] * mz + cam.t[0];
     P.Y = cam.R[3] * mx + cam.R[4] * my + cam.R[5] * mz + cam.t[1];
     P.Z = cam.R[6] * mx + cam.R[7] * my + cam.R[8] * mz + cam.t[2];
@@ -182,30 +212,11 @@ __device__ __forceinline__ void project_view(const CamD &cam, double mx, double 
     const double iq = 1.0 / P.qnorm;
     const double w = q0 * iq, x = q1 * iq, y = q2 * iq, z = q3 * iq;
     P.q[0] = w; P.q[1] = x; P.q[2] = y; P.q[3] = z;
-    double *R = P.Rq;
-    R[0] = 1.0 - 2.0 * (y * y + z * z); R[1] = 2.0 * (x * y - w * z);       R[2] = 2.0 * (x * z + w * y);
-    R[3] = 2.0 * (x * y + w * z);       R[4] = 1.0 - 2.0 * (x * x + z * z); R[5] = 2.0 * (y * z - w * x);
-    R[6] = 2.0 * (x * z - w * y);       R[7] = 2.0 * (y * z + w * x);       R[8] = 1.0 - 2.0 * (x * x + y * y);
     P.s[0] = S.s[0]; P.s[1] = S.s[1]; P.s[2] = S.s[2];
-    for (int r = 0; r < 3; ++r)
-        for (int c = 0; c < 3; ++c) P.M[3 * r + c] = R[3 * r + c] * P.s[c];
-    const double *M = P.M;
-    P.Sig[0] = M[0] * M[0] + M[1] * M[1] + M[2] * M[2];
-    P.Sig[1] = M[0] * M[3] + M[1] * M[4] + M[2] * M[5];
-    P.Sig[2] = M[0] * M[6] + M[1] * M[7] + M[2] * M[8];
-    P.Sig[3] = M[3] * M[3] + M[4] * M[4] + M[5] * M[5];
-    P.Sig[4] = M[3] * M[6] + M[4] * M[7] + M[5] * M[8];
-    P.Sig[5] = M[6] * M[6] + M[7] * M[7] + M[8] * M[8];
-
-    const double iz = 1.0 / P.Z;
-    const double j00 = cam.fx * iz, j02 = -cam.fx * P.X * iz * iz;
-    const double j11 = cam.fy * iz, j12 = -cam.fy * P.Y * iz * iz;
-    double *T = P.T;
-    for (int c = 0; c < 3; ++c) {
-        T[c] = j00 * cam.R[c] + j02 * cam.R[6 + c];
-        T[3 + c] = j11 * cam.R[3 + c] + j12 * cam.R[6 + c];
-    }
-    const double *Sg = P.Sig;
+    double R[9], M[9], Sg[6], T[6];
+    rot_q(w, x, y, z, R);
+    cov3d(R, P.s, M, Sg);
+    jw(cam, P.X, P.Y, P.Z, T);
     // (T Sigma) rows
     double ts0[3], ts1[3];
     ts0[0] = T[0] * Sg[0] + T[1] * Sg[1] + T[2] * Sg[2];
@@ -217,9 +228,9 @@ __device__ __forceinline__ void project_view(const CamD &cam, double mx, double 
     P.a = ts0[0] * T[0] + ts0[1] * T[1] + ts0[2] * T[2];
     P.b = ts0[0] * T[3] + ts0[1] * T[4] + ts0[2] * T[5];
     P.c = ts1[0] * T[3] + ts1[1] * T[4] + ts1[2] * T[5];
-    P.det = P.a * P.c - P.b * P.b;
-    if (!(P.det > 0.0)) return;
-    const double idet = 1.0 / P.det;
+    const double det = P.a * P.c - P.b * P.b;
+    if (!(det > 0.0)) return;
+    const double idet = 1.0 / det;
     P.A = P.c * idet; P.B = -P.b * idet; P.C = P.a * idet;
 
     P.o = S.o;
@@ -267,19 +278,22 @@ struct Params1 {   // one Gaussian's parameters as loaded
 // NT: non-temporal loads.  Measured faster in the end-of-step passes (whose parameter
 // stores are non-temporal too) and slower in the standalone projection and projection
 // backward, which keep ordinary loads.
-template <bool NT, int K>
+// NT_SH: the SH coefficients too (false: ordinary loads, so that a second read soon after
+// finds them in L2).
+template <bool NT, int K, bool NT_SH = NT>
 __device__ __forceinline__ void load_params(const float *__restrict__ means, const float *__restrict__ log_scales,
                                             const float *__restrict__ quats, const float *__restrict__ logits,
                                             const float *__restrict__ sh, int64_t n, int64_t i, Params1<K> &prm)
 {
     const auto ld = [](const float *p) { return NT ? __builtin_nontemporal_load(p) : *p; };
+    const auto ld_sh = [](const float *p) { return NT_SH ? __builtin_nontemporal_load(p) : *p; };
     prm.means[0] = ld(means + i); prm.means[1] = ld(means + n + i); prm.means[2] = ld(means + 2 * n + i);
     prm.ls[0] = ld(log_scales + i); prm.ls[1] = ld(log_scales + n + i); prm.ls[2] = ld(log_scales + 2 * n + i);
     prm.q[0] = ld(quats + i); prm.q[1] = ld(quats + n + i); prm.q[2] = ld(quats + 2 * n + i);
     prm.q[3] = ld(quats + 3 * n + i);
     prm.logit = ld(logits + i);
 #pragma unroll
-    for (int k = 0; k < 3 * K; ++k) prm.sh[k] = ld(sh + (int64_t)k * n + i);
+    for (int k = 0; k < 3 * K; ++k) prm.sh[k] = ld_sh(sh + (int64_t)k * n + i);
 }
 
 template <int K>
@@ -325,6 +339,44 @@ __device__ __forceinline__ void project_store(const Params1<(DEG + 1) * (DEG + 1
     project_store_s<DEG>(prm, S, cam, depth_lo, depth_hi, i, po);
 }
 
+// The float fields of a visible Gaussian's outputs, as rounded from its projection.
+struct RecFields {
+    float u, v, A, B, C, o;
+    RecConic rc;   // raster-ready: conic scaled for exp2, log2 of the stored opacity
+    int rx, ry;
+};
+
+__device__ __forceinline__ RecFields rec_fields(const Proj &P)
+{
+    return {(float)P.u, (float)P.v, (float)P.A, (float)P.B, (float)P.C, (float)P.o, rec_conic(P), P.rx, P.ry};
+}
+
+// The record of a visible Gaussian with colour (r, g, b); its plain fields (where requested)
+// are stored on the way.
+__device__ __forceinline__ void record_visible(const RecFields &F, float r, float g, float b, int64_t i,
+                                               const ProjOut &po, float4 (&rec)[3])
+{
+    const int64_t n = po.n;
+    if (po.means2d) {
+        po.means2d[i] = F.u;
+        po.means2d[n + i] = F.v;
+    }
+    if (po.conic_o) {
+        po.conic_o[i] = F.A;
+        po.conic_o[n + i] = F.B;
+        po.conic_o[2 * n + i] = F.C;
+        po.conic_o[3 * n + i] = F.o;
+    }
+    if (po.color) {
+        po.color[i] = r;
+        po.color[n + i] = g;
+        po.color[2 * n + i] = b;
+    }
+    rec[0] = make_float4(F.u, F.v, F.rc.a, F.rc.b);
+    rec[1] = make_float4(F.rc.c, F.rc.l, r, g);
+    rec[2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(F.rx), __int_as_float(F.ry));
+}
+
 // The projected record of Gaussian i as three float4 of the raster record; depth, radii and
 // the plain fields (where requested) are stored on the way.  A culled Gaussian's record is
 // zero apart from its index (its radii are (0, 0)).
@@ -351,27 +403,7 @@ __device__ __forceinline__ void project_record(const Params1<(DEG + 1) * (DEG + 
         g = fmaf(prm.sh[3 * k + 1], Y[k], g);
         b = fmaf(prm.sh[3 * k + 2], Y[k], b);
     }
-    const int64_t n = po.n;
-    if (po.means2d) {
-        po.means2d[i] = (float)P.u;
-        po.means2d[n + i] = (float)P.v;
-    }
-    if (po.conic_o) {
-        po.conic_o[i] = (float)P.A;
-        po.conic_o[n + i] = (float)P.B;
-        po.conic_o[2 * n + i] = (float)P.C;
-        po.conic_o[3 * n + i] = (float)P.o;
-    }
-    if (po.color) {
-        po.color[i] = r;
-        po.color[n + i] = g;
-        po.color[2 * n + i] = b;
-    }
-    // raster-ready: conic scaled for exp2, log2 of the stored opacity
-    const RecConic rc = rec_conic(P);
-    rec[0] = make_float4((float)P.u, (float)P.v, rc.a, rc.b);
-    rec[1] = make_float4(rc.c, rc.l, r, g);
-    rec[2] = make_float4(b, __uint_as_float((uint32_t)i), __int_as_float(P.rx), __int_as_float(P.ry));
+    record_visible(rec_fields(P), r, g, b, i, po, rec);
 }
 
 // project_store with the Gaussian's camera-independent values already computed.  The record
@@ -437,6 +469,15 @@ struct GradSink {
 constexpr int sh_chunk(int planes)
 {
     for (int c = 12; c > 1; --c)
+        if (planes % c == 0) return c;
+    return 1;
+}
+
+// The same for the single-view update, which also holds each chunk's parameter values:
+// chunks of at most 4 planes.
+constexpr int view_chunk(int planes)
+{
+    for (int c = 4; c > 1; --c)
         if (planes % c == 0) return c;
     return 1;
 }
@@ -540,19 +581,158 @@ struct AdamSink {
             }
         }
     }
+
+    // The update of the single-view end of step, shaped to keep few values live: the SH
+    // coefficients are read back from the wave's LDS copy a chunk at a time,
+    // the SH gradients Y_k(dir) dc are formed from the view direction (vis false: zero), and
+    // with NEXT the updated Gaussian is projected for next_cam on the way: its geometry right
+    // after the 11 other scalars, its colour summed over the updated SH chunks in the order
+    // project_record takes, and a non-finite updated coefficient culls it as there.  Every
+    // value equals what flush followed by project_store gives.
+    template <int DEG, bool NEXT>
+    __device__ void flush_view(int64_t i, const Grad3<(DEG + 1) * (DEG + 1)> &g, bool vis, const float (&dir)[3],
+                               Params1<(DEG + 1) * (DEG + 1)> &P, float (*shs)[64], float alpha_min, float depth_lo,
+                               float depth_hi, const CamD &next_cam, const ProjOut &next) const
+    {
+        constexpr int K = (DEG + 1) * (DEG + 1);
+        constexpr int kC = view_chunk(3 * K);
+        const int grp[11] = {0, 0, 0, 1, 1, 1, 2, 2, 2, 2, 3};
+        const int pl[11] = {0, 1, 2, 0, 1, 2, 0, 1, 2, 3, 0};
+        float m11[11], v11[11];
+        load_mv(grp, pl, i, m11, v11);
+        int sgrp[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) sgrp[c] = 4;
+        float msh[kC], vsh[kC], psh[kC];
+        {
+            const float gg[11] = {g.means[0], g.means[1], g.means[2], g.ls[0], g.ls[1], g.ls[2],
+                                  g.q[0], g.q[1], g.q[2], g.q[3], g.logit};
+            float pv[11] = {P.means[0], P.means[1], P.means[2], P.ls[0], P.ls[1], P.ls[2],
+                            P.q[0], P.q[1], P.q[2], P.q[3], P.logit};
+            const float sp[11] = {st[0], st[0], st[0], st[1], st[1], st[1], st[2], st[2], st[2], st[2], st[3]};
+            update(grp, pl, gg, pv, sp, m11, v11, i);
+            P.means[0] = pv[0]; P.means[1] = pv[1]; P.means[2] = pv[2];
+            P.ls[0] = pv[3]; P.ls[1] = pv[4]; P.ls[2] = pv[5];
+            P.q[0] = pv[6]; P.q[1] = pv[7]; P.q[2] = pv[8]; P.q[3] = pv[9];
+            P.logit = pv[10];
+        }
+        float Yn[K];
+        RecFields F{};
+        float key = 0.0f;
+        bool nvis = false;
+        if constexpr (NEXT) {   // the geometry of project_store, its SH finiteness settled below
+            ProjScalars S;
+            project_scalars(P.means[0], P.means[1], P.means[2], P.ls[0], P.ls[1], P.ls[2], P.q[0], P.q[1], P.q[2],
+                            P.q[3], P.logit, true, (double)alpha_min, S);
+            const float fmx = P.means[0], fmy = P.means[1], fmz = P.means[2];
+            Proj Pn;
+            project_view(next_cam, fmx, fmy, fmz, fmx, fmy, fmz, P.q[0], P.q[1], P.q[2], P.q[3], S, depth_lo, depth_hi,
+                         Pn);
+            key = Pn.key;
+            nvis = Pn.vis;
+#pragma unroll
+            for (int k = 0; k < K; ++k) Yn[k] = 0.0f;
+            if (nvis) {
+                sh_basis<DEG>(Pn.dir[0], Pn.dir[1], Pn.dir[2], Yn);
+                F = rec_fields(Pn);
+            }
+        }
+        load_pmv<kC>(0, i, shs, psh, msh, vsh);   // the first SH chunk (after the fp64 geometry: fewer live values)
+        float Y[K];
+        sh_basis<DEG>(dir[0], dir[1], dir[2], Y);
+        float col[3] = {0.0f, 0.0f, 0.0f};
+        bool fin = true;
+#pragma unroll
+        for (int c0 = 0; c0 < 3 * K; c0 += kC) {
+            float pnx[kC], mnx[kC], vnx[kC];
+            if (c0 + kC < 3 * K) load_pmv<kC>(c0 + kC, i, shs, pnx, mnx, vnx);   // the next chunk
+            int cpl[kC];
+            float gg[kC], sp[kC];
+#pragma unroll
+            for (int c = 0; c < kC; ++c) {
+                const int plane = c0 + c;
+                cpl[c] = plane;
+                gg[c] = vis ? Y[plane / 3] * g.gc[plane % 3] : 0.0f;
+                sp[c] = plane < 3 ? st[4] : st[5];
+            }
+            update(sgrp, cpl, gg, psh, sp, msh, vsh, i);
+            if constexpr (NEXT) {
+#pragma unroll
+                for (int c = 0; c < kC; ++c) {
+                    const int plane = c0 + c;
+                    fin = fin && __builtin_isfinite(psh[c]);
+                    col[plane % 3] = fmaf(psh[c], Yn[plane / 3], col[plane % 3]);
+                }
+            }
+            if (c0 + kC < 3 * K) {
+#pragma unroll
+                for (int c = 0; c < kC; ++c) {
+                    psh[c] = pnx[c];
+                    msh[c] = mnx[c];
+                    vsh[c] = vnx[c];
+                }
+            }
+        }
+        if constexpr (NEXT) {
+            nvis = nvis && fin;   // a non-finite coefficient: culled, as project_view's scalars reject it
+            next.depth[i] = key;
+            next.radii[i] = nvis ? make_int2(F.rx, F.ry) : make_int2(0, 0);
+            float4 rec[3];
+            rec[0] = rec[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            rec[2] = make_float4(0.0f, __uint_as_float((uint32_t)i), 0.0f, 0.0f);
+            if (nvis) record_visible(F, col[0], col[1], col[2], i, next, rec);
+            next.rec[3 * i + 0] = rec[0];
+            next.rec[3 * i + 1] = rec[1];
+            next.rec[3 * i + 2] = rec[2];
+        }
+    }
+
+    // Chunk [c0, c0 + N) of the SH planes: parameter values (from the wave's LDS copy
+    // shs[plane][lane]) and moments.
+    template <int N>
+    __device__ void load_pmv(int c0, int64_t i, float (*shs)[64], float (&pv)[N], float (&mv)[N],
+                             float (&vv)[N]) const
+    {
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+            const int64_t idx = (int64_t)(c0 + c) * n + i;
+            pv[c] = shs[c0 + c][threadIdx.x & 63];
+            mv[c] = __builtin_nontemporal_load(m[4] + idx);
+            vv[c] = __builtin_nontemporal_load(v[4] + idx);
+        }
+    }
 };
 
-// The chain rule for a Gaussian the projection keeps.
+// The colour's part of the chain rule through the view direction: d v^ = sum_k (sh_k . dc)
+// grad Y_k, and its share of dL/dmu (dsh).
+template <int DEG>
+__device__ __forceinline__ void project_bwd_sh(const Proj &P, const float (&gc)[3], const float *shc, double (&dsh)[3])
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = shc[3 * k] * gc[0] + shc[3 * k + 1] * gc[1] + shc[3 * k + 2] * gc[2];
+    float gx, gy, gz;
+    sh_grad<DEG>(P.dir[0], P.dir[1], P.dir[2], wk, gx, gy, gz);
+    const double vd = (double)P.dir[0] * gx + (double)P.dir[1] * gy + (double)P.dir[2] * gz;
+    const double idist = 1.0 / P.dist;
+    dsh[0] = (gx - P.dir[0] * vd) * idist;
+    dsh[1] = (gy - P.dir[1] * vd) * idist;
+    dsh[2] = (gz - P.dir[2] * vd) * idist;
+}
+
+// The chain rule for a Gaussian the projection keeps.  The colour's part comes first, so
+// that the SH coefficients are no longer needed during the geometric part.
 template <int DEG>
 __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam, const float (&g2)[9],
                                                   const Params1<(DEG + 1) * (DEG + 1)> &prm,
                                                   Grad3<(DEG + 1) * (DEG + 1)> &G)
 {
-    constexpr int K = (DEG + 1) * (DEG + 1);
-    const float *shc = prm.sh;
     const double gu = g2[0], gv = g2[1], gA = g2[2], gB = g2[3], gC = g2[4];
     const double go = g2[5];
     const float gc[3] = {g2[6], g2[7], g2[8]};
+    double dsh[3];
+    project_bwd_sh<DEG>(P, gc, prm.sh, dsh);
 
     // conic = Sigma2D^-1:  G_S2 = -Q G_Q Q with G_Q = [[gA, gB/2], [gB/2, gC]]
     const double A = P.A, B = P.B, C = P.C;
@@ -564,7 +744,10 @@ __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam
     const double s11 = -(p10 * B + p11 * C);
 
     // Sigma2D = T Sigma T^T:  G_T = 2 G_S2 T Sigma,  G_Sigma = T^T G_S2 T
-    const double *T = P.T, *S = P.Sig;
+    double R[9], M[9], S[6], T[6];
+    rot_q(P.q[0], P.q[1], P.q[2], P.q[3], R);
+    cov3d(R, P.s, M, S);
+    jw(cam, P.X, P.Y, P.Z, T);
     double ts[6];
     for (int r = 0; r < 2; ++r) {
         const double *t = T + 3 * r;
@@ -602,7 +785,6 @@ __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam
     for (int j = 0; j < 3; ++j) dmu[j] = W[j] * dX + W[3 + j] * dY + W[6 + j] * dZ;
 
     // Sigma = M M^T: G_M = 2 G_Sigma M;  M = R diag(s)
-    const double *M = P.M, *R = P.Rq;
     double GR[9];
     for (int k = 0; k < 3; ++k) {
         double ds = 0.0;
@@ -629,20 +811,10 @@ __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam
 
     G.logit = (float)(go * P.o * (1.0 - P.o));
 
-    // colour: d sh_k = Y_k dc;  d v^ = sum_k (sh_k . dc) grad Y_k
-    float wk[K];
+    // colour: d sh_k = Y_k dc
     sh_basis<DEG>(P.dir[0], P.dir[1], P.dir[2], G.Y);
     G.gc[0] = gc[0]; G.gc[1] = gc[1]; G.gc[2] = gc[2];
-#pragma unroll
-    for (int k = 0; k < K; ++k) wk[k] = shc[3 * k] * gc[0] + shc[3 * k + 1] * gc[1] + shc[3 * k + 2] * gc[2];
-    float gx, gy, gz;
-    sh_grad<DEG>(P.dir[0], P.dir[1], P.dir[2], wk, gx, gy, gz);
-    const double vd = (double)P.dir[0] * gx + (double)P.dir[1] * gy + (double)P.dir[2] * gz;
-    const double idist = 1.0 / P.dist;
-    dmu[0] += (gx - P.dir[0] * vd) * idist;
-    dmu[1] += (gy - P.dir[1] * vd) * idist;
-    dmu[2] += (gz - P.dir[2] * vd) * idist;
-    for (int j = 0; j < 3; ++j) G.means[j] = (float)dmu[j];
+    for (int j = 0; j < 3; ++j) G.means[j] = (float)(dmu[j] + dsh[j]);
 }
 
 // in: the screen-space gradients (u, v, A, B, C, o, r, g, b), or with RAW the per-Gaussian
@@ -692,6 +864,49 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
     if constexpr (NEXT) project_store<DEG>(prm, next_cam, alpha_min, depth_lo, depth_hi, i, next);
 }
 
+// k_grad_adam's Gaussian: the per-Gaussian moment sums in (as project_bwd_one with RAW), the
+// projection backward and AdamSink::flush_view.  The SH coefficients are kept in the wave's
+// LDS (shs[plane][lane]) from the load to the update, not in registers.
+template <int DEG, bool NEXT>
+__device__ __forceinline__ void grad_adam_one(const float *__restrict__ means, const float *__restrict__ log_scales,
+                                              const float *__restrict__ quats, const float *__restrict__ logits,
+                                              const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
+                                              float alpha_min, float depth_lo, float depth_hi, const float (&in)[9],
+                                              float *__restrict__ grads2d, const AdamSink &out, const CamD &next_cam,
+                                              const ProjOut &next, float (*shs)[64])
+{
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    const int lane = threadIdx.x & 63;
+    Params1<K> prm;
+    load_params<true>(means, log_scales, quats, logits, sh, n, i, prm);
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) shs[k][lane] = prm.sh[k];
+    const bool shf = sh_finite(prm);
+    Proj P;
+    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
+    project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
+                 prm.q[3], prm.logit, shf, (double)alpha_min, depth_lo, depth_hi, P);
+    Grad3<K> G;
+    for (int j = 0; j < 3; ++j) G.means[j] = G.ls[j] = 0.0f;
+    for (int j = 0; j < 4; ++j) G.q[j] = 0.0f;
+    G.logit = 0.0f;
+    G.gc[0] = G.gc[1] = G.gc[2] = 0.0f;
+    float g2[9];
+    RecConic rc{0.0f, 0.0f, 0.0f, 0.0f};
+    if (P.vis) rc = rec_conic(P);
+    gsr::moments_to_grads(in, rc.a, rc.b, rc.c, rc.l, g2);
+    if (grads2d) {
+#pragma unroll
+        for (int f = 0; f < 9; ++f) grads2d[(int64_t)f * n + i] = g2[f];
+    }
+    float dir[3] = {0.0f, 0.0f, 1.0f};
+    if (P.vis) {
+        project_bwd_grads<DEG>(P, cam, g2, prm, G);
+        dir[0] = P.dir[0]; dir[1] = P.dir[1]; dir[2] = P.dir[2];
+    }
+    out.flush_view<DEG, NEXT>(i, G, P.vis, dir, prm, shs, alpha_min, depth_lo, depth_hi, next_cam, next);
+}
+
 template <int DEG>
 __global__ __launch_bounds__(256) void k_project_bwd(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
@@ -711,21 +926,32 @@ __global__ __launch_bounds__(256) void k_project_bwd(
 // quadrant-record slots (as k_grad_reduce; optionally stored in grads2d), the projection
 // backward, and the Adam update of every parameter scalar; with NEXT also the projection
 // of the updated Gaussian for the next camera (into next).
+// LDS of one wave of k_grad_adam: its slot-sum stage, then (once the sums are done) its
+// lanes' SH coefficients between the projection backward and the update.
+__host__ __device__ constexpr size_t grad_adam_wave_lds(int deg)
+{
+    const size_t shb = (size_t)3 * (deg + 1) * (deg + 1) * 64 * sizeof(float);
+    return shb > sizeof(gsr::SlotStage) ? shb : sizeof(gsr::SlotStage);
+}
+
 template <int DEG, bool NEXT>
-__global__ __launch_bounds__(256) void k_grad_adam(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_grad_adam(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
     const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
     const float4 *__restrict__ qgrad, const uint32_t *__restrict__ qstamp, float *__restrict__ grads2d, AdamSink out,
     CamD next_cam, ProjOut next)
 {
-    __shared__ gsr::SlotStage stage[4];
+    extern __shared__ __align__(16) unsigned char ga_lds[];   // grad_adam_wave_lds(DEG) per wave
+    unsigned char *wl = ga_lds + (threadIdx.x >> 6) * grad_adam_wave_lds(DEG);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     float acc[9];
-    gsr::raw_slot_sums(hdr, qoff, qgrad, qstamp, i, n, stage[threadIdx.x >> 6], acc);
+    gsr::raw_slot_sums(hdr, qoff, qgrad, qstamp, i, n, *reinterpret_cast<gsr::SlotStage *>(wl), acc);
     if (i >= n) return;
-    project_bwd_one<DEG, true, NEXT>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi,
-                                     acc, grads2d, out, next_cam, next);
+    // the wave's stage is no longer read (each wave reads only its own; the sums end with a
+    // wave barrier): its bytes now hold the lanes' SH coefficients
+    grad_adam_one<DEG, NEXT>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, acc,
+                             grads2d, out, next_cam, next, reinterpret_cast<float(*)[64]>(wl));
 }
 
 // -------------------------------------------------------------------- batches of views
@@ -1042,15 +1268,17 @@ gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, cons
     const dim3 grid((unsigned)ceil_div(n, (int64_t)bt)), block((unsigned)bt);
 #define GS_GA(D)                                                                                                   \
     do {                                                                                                           \
+        const size_t lds = (size_t)(bt / 64) * grad_adam_wave_lds(D);                                              \
         if (next_cam)                                                                                              \
-            k_grad_adam<D, true><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, \
-                                                             g->sh, n, cd, p->alpha_min, p->depth_lo, p->depth_hi, \
-                                                             hdr, qoff, qg, qs, grads2d, sink, nd, po);            \
+            k_grad_adam<D, true><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,                  \
+                                                               g->opacity_logits, g->sh, n, cd, p->alpha_min,      \
+                                                               p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,        \
+                                                               grads2d, sink, nd, po);                             \
         else                                                                                                       \
-            k_grad_adam<D, false><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,                   \
-                                                              g->opacity_logits, g->sh, n, cd, p->alpha_min,       \
-                                                              p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,         \
-                                                              grads2d, sink, nd, po);                              \
+            k_grad_adam<D, false><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,                 \
+                                                                g->opacity_logits, g->sh, n, cd, p->alpha_min,     \
+                                                                p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,       \
+                                                                grads2d, sink, nd, po);                            \
     } while (0)
     switch (p->sh_degree) {
     case 0: GS_GA(0); break;
