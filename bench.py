@@ -27,7 +27,9 @@ without the system-scope fence, see TimingEvent).
 over-composited, L1 on the composite, the composite backward, each slab's backward
 rasterization and per-Gaussian sum, compaction of its non-zero gradient records, their
 decoding into the slab owner's gradient planes, and the owner's projection backward and
-Adam; every call is timed with events and reported in `kernels`.
+Adam.  The timed steps run each slab's calls on a stream of its own (the slabs share
+nothing between the composites); `kernels` times every call with events in as many
+serial steps afterwards, whose wall time is serial_ms_per_step.
 
 --batch B (2..4) measures BatchTrainStep instead: one optimiser step over B views (the
 workload's views in turn), each binned and rasterized with the fused forward + L1 +
@@ -478,25 +480,40 @@ def main_partitioned(args):
             with t("adam"):
                 st.adam()
 
+    # The timed steps run the slabs side by side (PartitionedStep.step_overlapped: each slab
+    # on a stream of its own, binning without host waits); the per-call breakdown comes from
+    # the same number of serial steps afterwards, every call between HIP events (events
+    # around overlapped calls would not time the calls).
+    tgt = target
     for _ in range(args.warmup):
-        one_step(CallTimer())
+        ps.step_overlapped(cam, tgt, join=False)
+    ps.join()
     torch.cuda.synchronize()
+    if not ps.check_capacity():
+        raise RuntimeError("a slab's lists outgrew their buffers during the warm-up; rerun")
     for st in ps.parts:
         st.frame.n_trav_sum.zero_()
-    probe = CallTimer()
-    one_step(probe)   # one more untimed step, to count the timed calls of a step
-    torch.cuda.synchronize()
-    for st in ps.parts:
-        st.frame.n_trav_sum.zero_()
-    timer = CallTimer(2 * len(probe.marks) * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        one_step(timer)
+        ps.step_overlapped(cam, tgt, join=False)   # a slab's update overlaps the next step's binning
+    ps.join()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_kernel = {nm: ms / args.steps for nm, ms in timer.totals().items()}
+    if not ps.check_capacity():
+        raise RuntimeError("a slab's lists outgrew their buffers during the timed steps; rerun")
     isect_step = sum(int(st.frame.n_trav_sum.item()) for st in ps.parts) / args.steps
+    probe = CallTimer()
+    one_step(probe)   # one untimed serial step, to count the calls of a step
+    torch.cuda.synchronize()
+    timer = CallTimer(2 * len(probe.marks) * args.steps)
+    torch.cuda.synchronize()
+    ts0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(timer)
+    torch.cuda.synchronize()
+    serial_wall = time.perf_counter() - ts0
+    per_kernel = {nm: ms / args.steps for nm, ms in timer.totals().items()}
     # the raster walks of the last step's slab lists, counted by the fused kernel's counting
     # instance (its forward and backward walks are those of the separate raster kernels;
     # the target only sets dL/dC, which does not change which records are walked)
@@ -539,14 +556,17 @@ def main_partitioned(args):
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H], "views": 1,
                    "slabs": parts, "slab_gaussians": [st.params.n for st in ps.parts],
                    "step": "per slab projection + binning + forward; composite; L1; composite backward; per slab "
-                           "backward raster + per-Gaussian sum + compaction + decoding + projection backward + Adam"},
+                           "backward raster + per-Gaussian sum + compaction + decoding + projection backward + Adam",
+                   "schedule": "each slab's calls on a stream of its own (PartitionedStep.step_overlapped)"},
         "roofline": roof,
         "intersections_per_step": round(isect_step, 1),
         "tile_entries_per_step": k_isect,
         "records_per_step": records,
         "visible_gaussians": n_vis,
-        "kernels_note": "every call timed with events in the timed steps; summed over the slabs",
-        "timing_events_created_in_timed_steps": timer.created_late,
+        "serial_ms_per_step": round(serial_wall * 1e3 / args.steps, 4),
+        "kernels_note": "every call timed with events in as many serial steps after the timed ones; summed over "
+                        "the slabs",
+        "breakdown_events_created_late": timer.created_late,
         "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
         "cpu_baseline": None,

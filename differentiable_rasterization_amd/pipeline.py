@@ -416,6 +416,9 @@ class PartitionedStep:
                                                device=device))
             self.owner_g2.append(z(9, n))
             self.r.append(0)
+        self.streams = None   # ViewStreams of the overlapped schedule, made on first use
+        # (K, required capacity or 0) of each slab's binning in the overlapped schedule
+        self.counts = torch.zeros(len(self.parts), 2, dtype=torch.int64, device=device)
 
     # -- forward
     def render_part(self, k, cam: B.Camera, stream=None):
@@ -477,3 +480,86 @@ class PartitionedStep:
         self.backward(cam, stream)
         for k in range(len(self.parts)):
             self.update_part(k, cam, stream)
+
+    # -- the same step with the slabs side by side
+    #
+    # The slabs share nothing until the composite and nothing again after the composite
+    # backward.  Each slab's projection and binning, and later its compaction, decoding and
+    # update (projection backward and Adam: HBM-bound), run on a stream of its own; the
+    # rasterizations (VALU-bound) run in slab order on one more stream, each after its
+    # slab's binning, so that one slab's rasterization overlaps the other slabs' binning
+    # and updates rather than the other rasterizations.  The binning does not wait for the
+    # host (the lists must fit the buffers' capacity: self.counts[k] = (K, required
+    # capacity or 0) tells after the step, check_capacity grows them); the whole backward
+    # chain is queued before the first compaction reads its record count, so the later
+    # slabs run while the host waits.  Every call is the serial step's, on the same data:
+    # the results are the same bit for bit.
+
+    def _slab_streams(self):
+        if self.streams is None:
+            self.streams = ViewStreams(len(self.parts) + 1)   # one per slab, then the raster stream
+        return self.streams
+
+    def forward_overlapped(self, cam: B.Camera):
+        vs = self._slab_streams()
+        rs = vs.streams[-1]
+        vs.fork()
+        for k, st in enumerate(self.parts):
+            with torch.cuda.stream(vs.streams[k]):
+                B.gs_project(st.params.gaussians(), cam, st.raster, st.proj.abi())
+                st.bins.sort_async(st.proj, cam, st.raster, self.counts[k])
+        for k, st in enumerate(self.parts):
+            rs.wait_stream(vs.streams[k])   # slab k's lists
+            with torch.cuda.stream(rs):
+                f = st.frame
+                B.gs_raster_fwd(st.proj.abi(), st.bins.abi(), cam, st.raster, f.color, f.t_final, f.n_trav,
+                                f.n_trav_sum)
+        vs.join()
+        self.composite()
+
+    def backward_overlapped(self, cam: B.Camera, join=True):
+        """Composite backward, then each slab's backward rasterization and per-Gaussian sum
+        on the raster stream, and its compaction, decoding and update on its own stream.
+        join=False leaves the updates running: the next step_overlapped orders each slab's
+        projection after its own update (same stream) and everything else after those, so
+        one slab's update overlaps the next step's binning of the others; call join() (or
+        synchronize) before reading the parameters."""
+        vs = self._slab_streams()
+        rs = vs.streams[-1]
+        self.composite_backward()
+        vs.fork()
+        for k in range(len(self.parts)):
+            with torch.cuda.stream(rs):
+                self.backward_part(k, cam)
+            vs.streams[k].wait_stream(rs)   # slab k's gradients
+        for k in range(len(self.parts)):
+            with torch.cuda.stream(vs.streams[k]):
+                self.compact_part(k)   # waits for this slab's stream only
+                self.decode_part(k)
+                self.update_part(k, cam)
+        if join:
+            vs.join()
+
+    def join(self):
+        """Makes the current stream wait for the slabs' streams."""
+        if self.streams is not None:
+            self.streams.join()
+
+    def step_overlapped(self, cam: B.Camera, target, join=True):
+        self.forward_overlapped(cam)
+        self.loss(target)
+        self.backward_overlapped(cam, join)
+
+    def check_capacity(self) -> bool:
+        """After overlapped steps: True if every slab's lists fit; otherwise the short
+        buffers are grown (the steps since the last check must be repeated)."""
+        c = self.counts.cpu()
+        ok = True
+        for k, st in enumerate(self.parts):
+            need = int(c[k, 1])
+            if need:
+                ok = False
+                st.bins._alloc(int(math.ceil(need * 1.25)) + 1024)
+            else:
+                st.bins.n_isect = int(c[k, 0])
+        return ok

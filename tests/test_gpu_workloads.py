@@ -414,3 +414,40 @@ def test_partitioned_step_matches_unpartitioned():
         e3 = rel_l2(st.params.grad.cpu().numpy(), g3[:, idx[k]].numpy())
         log(f"  slab {k}: {ps.r[k]} records of {st.params.n}; grads2d rel-L2 {e2:.2e}, 3D grads rel-L2 {e3:.2e}")
         assert e2 <= 1e-4 and e3 <= 1e-4
+
+
+def test_partitioned_overlapped_step_matches_serial():
+    """PartitionedStep.step_overlapped (each slab's calls on a stream of its own, the binning
+    without host waits, a step's updates running into the next step) gives the serial
+    step's results bit for bit: the composite, the loss, each slab's records, and the
+    parameters and Adam moments after the updates, after step 1 (joined) and step 3 (step
+    2's updates left running into it); 200K Gaussians, 960x540, 4 depth slabs,
+    theta_T = 1e-4."""
+    log("PartitionedStep overlapped vs serial, 200K 960x540, 4 slabs, 3 steps")
+    sc = scenes.scene_partitioned_4k(n=200_000, width=960, height=540)
+    subs = scenes.slab_scenes(sc)
+    cam = B.camera_from(sc.cameras[0])
+    W, H = sc.cameras[0].width, sc.cameras[0].height
+    tgt = sc.targets[0].to(DEV)
+    mk = lambda: PL.PartitionedStep([PL.GaussianParams.from_scene(s, DEV) for s in subs], [(0.0, math.inf)] * 4,
+                                    W, H, DEV, t_min=1e-4)
+    serial, over = mk(), mk()
+    over.forward(cam)   # sizes each slab's lists (the overlapped binning does not grow them)
+    for st in over.parts:
+        st.bins._alloc(int(st.bins.capacity * 1.3) + 4096)
+    for step in range(3):
+        serial.step(cam, tgt)
+        over.step_overlapped(cam, tgt, join=step != 1)   # step 1's updates run into step 2
+        if step == 1:
+            continue   # compared after step 2, which is ordered after them
+        torch.cuda.synchronize()
+        assert over.check_capacity()
+        assert torch.equal(serial.color, over.color) and torch.equal(serial.t_final, over.t_final)
+        assert torch.equal(serial.loss_value, over.loss_value)
+        assert serial.r == over.r
+        for a, b in zip(serial.parts, over.parts):
+            assert torch.equal(a.params.data, b.params.data)
+            assert torch.equal(a.params.m, b.params.m) and torch.equal(a.params.v, b.params.v)
+        for a, b in zip(serial.owner_g2, over.owner_g2):
+            assert torch.equal(a, b)
+        log(f"  step {step}: equal; records {over.r}")
