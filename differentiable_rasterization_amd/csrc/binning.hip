@@ -206,15 +206,16 @@ __device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned lo
     return K > qc ? K : qc;
 }
 
-// Entries of the Gaussians in depth order (block b: depth ranks 256 b ..; svals: tile
-// count << 32 | Gaussian), tiles row-major; off: exclusive scan of the tile counts in depth
+// Entries of the Gaussians in depth order (block b: depth ranks 256 b ..; svals, or
+// svals_b when *sel != 0: tile count << 32 | Gaussian), tiles row-major; off: exclusive scan of the tile counts in depth
 // order.  Entry p gets the key
 // tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at) and the
 // value (gradient slot of its first quadrant record) << 32 | its Gaussian, carried through
 // the tile sort.  Gaussian g's quadrant records own slots qoff[g] .. qoff[g + 1], in the
 // order of its entries and, within an entry, of the quadrants.  The records are gathered in
 // depth order from the 64-byte-aligned copy grec (one aligned run per Gaussian).
-__global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals, const uint32_t *__restrict__ off,
+__global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals, const uint64_t *__restrict__ svals_b,
+                                              const uint32_t *__restrict__ sel, const uint32_t *__restrict__ off,
                                               const uint32_t *__restrict__ qoff, const float4 *__restrict__ grec,
                                               float log2_amin, int64_t n, int tx,
                                               int ty, const unsigned long long *__restrict__ tot, int64_t cap,
@@ -241,6 +242,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals
     }
     if (!ok) return;   // the whole block agrees
     const int64_t j0 = (int64_t)blockIdx.x * blockDim.x;
+    if (sel && *sel) svals = svals_b;
     const uint64_t sv = j < n ? svals[j] : 0ull;
     const bool listed = (sv >> 32) != 0u;   // culled Gaussians and those off the image have no tiles
     const uint32_t g = (uint32_t)sv;
@@ -483,7 +485,7 @@ __global__ void k_bins_empty(gsr::BinsHeader *__restrict__ hdr, int64_t *__restr
 struct Layout {
     // zero region (cleared by k_keys_count at the start of every sort): tickets and
     // look-back status words of the scans
-    size_t zero, tickets, whist, stD, stT, scC, scQ, scW, zero_bytes;
+    size_t zero, tickets, xf, whist, stD, stT, scC, scQ, scW, zero_bytes;
     size_t dkA, dvA, dkB, dvB, qcnt, doff, total, klen, tkA, tkB, tvA, tvB, hist, wb, bytes;
     int tbits;
 };
@@ -506,6 +508,7 @@ Layout layout(int64_t n, int64_t cap, int32_t tiles)
     const int64_t nw = gsr::kQuads * (gsr::raster_layout(n, cap, 1).words + 1);
     L.zero = o;
     L.tickets = take(16 * 4);
+    L.xf = take(4 * gsi::kRadixXfWords);   // the depth sort's key range reduction
     L.whist = take(2 * 4 * kWaveBuckets);   // wave-order histogram, then placement cursors
     L.stD = take(8 * (size_t)gsi::radix_scan_status_len((int64_t)nn, 32));
     L.stT = take(8 * (size_t)gsi::radix_scan_status_len((int64_t)cc, L.tbits));
@@ -629,16 +632,21 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     // 2. Gaussians by depth key (stable, so equal keys stay in index order; the values
     //    carry the tile counts along), and the emit offsets: the exclusive scan of the tile
     //    counts in that order, with the total K
+    //    It takes three passes instead of four when the visible depth keys span less than
+    //    about 2^24 (decided on the device); the result is then in (dkB, dvB), which
+    //    xf[1] != 0 tells the scan and the emit pass
+    uint32_t *xf = (uint32_t *)(ws + L.xf);   // zeroed by k_keys_count
     bool in_b = false;
-    if ((s = radix_sort_u32_u64(dkA, dvA, dkB, dvB, n, 32, hist, stD, tickets + kTkDepth, &in_b, stream)) != GS_OK)
+    if ((s = radix_sort_u32_u64(dkA, dvA, dkB, dvB, n, 32, hist, stD, tickets + kTkDepth, &in_b, stream, nullptr,
+                                xf)) != GS_OK)
         return s;
-    const uint64_t *sv = in_b ? dvB : dvA;
-    if ((s = lb_scan_hi32(sv, doff, n, scC, tickets + kTkCnt, total, stream)) != GS_OK) return s;
+    const uint32_t *sel = xf + 1;
+    if ((s = lb_scan_hi32(dvA, doff, n, scC, tickets + kTkCnt, total, stream, dvB, sel)) != GS_OK) return s;
 
     // 3. emit entries in depth order (nothing if the lists do not fit), then a stable sort
     //    of (tile key, emit position) by tile
     const int tbits = L.tbits;
-    k_emit<<<gn, 256, 0, stream>>>(sv, doff, qoff, grec, log2_amin, n, tx, ty, total, cap,
+    k_emit<<<gn, 256, 0, stream>>>(dvA, dvB, sel, doff, qoff, grec, log2_amin, n, tx, ty, total, cap,
                                    (unsigned long long)RL.grec, klen, hdr, counts, tkA, tvA);
     GS_LAUNCH_CHECK("k_emit");
     if (cap == 0) {

@@ -26,9 +26,11 @@ int64_t lb_scan_tiles(int64_t m);
 gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
                       unsigned long long *total, hipStream_t stream, uint32_t *clear = nullptr,
                       int64_t clear_lim = 0);
-// The same over the high 32 bits of m uint64 values (in: 16-byte aligned).
+// The same over the high 32 bits of m uint64 values (in: 16-byte aligned).  With sel !=
+// NULL, the input is in_alt instead of in when *sel != 0 (read on the device).
 gs_status lb_scan_hi32(const uint64_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
-                       unsigned long long *total, hipStream_t stream);
+                       unsigned long long *total, hipStream_t stream, const uint64_t *in_alt = nullptr,
+                       const uint32_t *sel = nullptr);
 
 // Stable LSD radix sort of (key, value) uint32 pairs on the low `bits` bits of the key,
 // 8 bits per pass, ping-ponging between (ka, va) and (kb, vb).  Returns in *in_b whether
@@ -41,10 +43,16 @@ int64_t radix_scan_status_len(int64_t m, int bits);
 gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb, int64_t m, int bits,
                          uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
                          hipStream_t stream, const unsigned long long *m_dev = nullptr);
-// The same with 64-bit values.
+// The same with 64-bit values.  xf (device, may be NULL; 32-bit sorts only): kRadixXfWords
+// words, zero before the call.  With xf, the sort finds the range of the keys other than 0xFFFFFFFF
+// on the device; when they lie within about 2^24 of each other (the exact test is in
+// sort.hip), it takes three passes instead of four and the result ends in (kb, vb): then
+// xf[1] != 0 after the sort (read it on the device; *in_b reports the four-pass case).
+constexpr int kRadixXfWords = 32 * 33;
 gs_status radix_sort_u32_u64(uint32_t *ka, uint64_t *va, uint32_t *kb, uint64_t *vb, int64_t m, int bits,
                              uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
-                             hipStream_t stream, const unsigned long long *m_dev = nullptr);
+                             hipStream_t stream, const unsigned long long *m_dev = nullptr,
+                             uint32_t *xf = nullptr);
 
 // Fills n int32 values with `value` (a kernel, not a memset, so it may be captured in graphs).
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream);

@@ -134,6 +134,48 @@ __device__ __forceinline__ int64_t elem_count(int64_t m, const unsigned long lon
     return m_dev ? (int64_t)min((unsigned long long)m, *m_dev) : m;
 }
 
+// Key range reduction of a 32-bit sort.  xf: kRadixXfWords device words, zero before the
+// sort.  The first pass's histogram also gathers the largest key and the largest
+// complement of a key over the keys other than 0xFFFFFFFF, each block into one of kXfSlots
+// slots (one 128-byte line each, so that the blocks' atomics spread over the memory
+// channels); from them the first scatter derives the offset o (the smallest key with its
+// low byte cleared) and whether every such key k has k - o < 0xFFFFFF, and stores both in
+// xf[0], xf[1].  If it does, that scatter writes every key k as k - o, and 0xFFFFFFFF (an
+// element whose place among the other keys does not matter, as a culled Gaussian's, but
+// which sorts last) as 0xFFFFFF: the order is unchanged, the fourth digit is then zero for
+// every key, and the fourth pass skips itself.  The first digit is the same before and
+// after the change (o's low byte is zero), so the first histogram is taken before o is
+// known.  Modes of a pass (a template argument): 0 plain, 1 the first pass, 2 the fourth
+// pass.
+constexpr int kXfSlots = 32, kXfSlotWords = 32;
+static_assert(gsi::kRadixXfWords == kXfSlotWords * (1 + kXfSlots), "xf layout");
+
+__device__ __forceinline__ uint32_t *xf_slot(uint32_t *xf, int s) { return xf + kXfSlotWords * (1 + s); }
+
+// Every lane of the calling wave gets o and fits (lanes 0 .. kXfSlots - 1 read one slot each).
+__device__ __forceinline__ void xf_range(uint32_t *xf, uint32_t &o, bool &fits)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t mx = 0u, ninv = 0u;
+    if (lane < kXfSlots) {
+        const uint32_t *sl = xf_slot(xf, lane);
+        mx = sl[0];
+        ninv = sl[1];
+    }
+    for (int d = 32; d > 0; d >>= 1) {   // over all 64 lanes: every lane needs the result
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, 64));
+        ninv = max(ninv, (uint32_t)__shfl_xor((int)ninv, d, 64));
+    }
+    o = ninv ? ~ninv & ~0xFFu : 0u;   // ninv == 0: no key other than 0xFFFFFFFF
+    fits = ninv == 0u || mx - o < 0xFFFFFFu;
+}
+
+template <int MODE>
+__device__ __forceinline__ bool xf_skip(const uint32_t *__restrict__ xf)
+{
+    return MODE == 2 && xf[1] != 0u;
+}
+
 // The radix tile a block takes.  Blocks reach the 8 XCDs round-robin (block b on XCD
 // b % 8); the tiles that hold elements are renumbered so that each XCD takes one
 // contiguous run of them.  Neighbouring tiles write neighbouring words of the digit-major
@@ -147,11 +189,15 @@ __device__ __forceinline__ int64_t rx_tile(int64_t m)
     return x * per + (x < rem ? x : rem) + b / gsi::kXcds;
 }
 
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restrict__ keys, int64_t m_max,
                                                          const unsigned long long *__restrict__ m_dev, int shift,
-                                                         uint32_t *__restrict__ hist, int64_t nb)
+                                                         uint32_t *__restrict__ hist, int64_t nb,
+                                                         uint32_t *__restrict__ xf)
 {
     __shared__ uint32_t h[4][256];
+    __shared__ uint32_t red[2][4];
+    if (xf_skip<MODE>(xf)) return;   // the whole grid
     const int64_t m = elem_count(m_max, m_dev);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t tile = rx_tile(m);
@@ -161,11 +207,17 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
     // Consecutive lanes hold consecutive elements.  Each run of equal digits across the
     // lanes is counted by its first lane with one LDS add of the run length, so skewed or
     // presorted keys (long runs of one digit) do not serialise on one LDS address.
+    uint32_t kmax = 0u, kninv = 0u;   // over the keys other than 0xFFFFFFFF (MODE 1)
 #pragma unroll 4
     for (int r = 0; r < kRxItems; ++r) {
         const int64_t e = base + r * 64;
         const bool valid = e < m;
-        const uint32_t d = valid ? (keys[e] >> shift) & 255u : 0x100u;   // 0x100: no element
+        const uint32_t kv = valid ? keys[e] : 0xFFFFFFFFu;
+        if (MODE == 1 && kv != 0xFFFFFFFFu) {
+            kmax = max(kmax, kv);
+            kninv = max(kninv, ~kv);
+        }
+        const uint32_t d = valid ? (kv >> shift) & 255u : 0x100u;   // 0x100: no element
         const uint32_t dp = __shfl_up(d, 1, 64);
         const bool head = lane == 0 || d != dp;
         const uint64_t heads = __ballot(head);
@@ -175,17 +227,43 @@ __global__ __launch_bounds__(kThreads) void k_radix_hist(const uint32_t *__restr
             atomicAdd(&h[w][d], (uint32_t)(next - lane));
         }
     }
+    if (MODE == 1) {
+        for (int o = 32; o > 0; o >>= 1) {
+            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+            kninv = max(kninv, (uint32_t)__shfl_xor((int)kninv, o, 64));
+        }
+        if (lane == 0) {
+            red[0][w] = kmax;
+            red[1][w] = kninv;
+        }
+    }
     __syncthreads();
     const int d = threadIdx.x;
     hist[(int64_t)d * nb + tile] = h[0][d] + h[1][d] + h[2][d] + h[3][d];
+    if (MODE == 1 && threadIdx.x < 2) {
+        const uint32_t *r4 = red[threadIdx.x];
+        const uint32_t v = max(max(r4[0], r4[1]), max(r4[2], r4[3]));
+        if (v) atomicMax(xf_slot(xf, (int)(blockIdx.x % kXfSlots)) + threadIdx.x, v);
+    }
 }
 
-template <typename V>
+template <typename V, int MODE>
 __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__restrict__ kin, const V *__restrict__ vin,
                                                             uint32_t *__restrict__ kout, V *__restrict__ vout,
                                                             int64_t m_max, const unsigned long long *__restrict__ m_dev,
-                                                            int shift, const uint32_t *__restrict__ offs, int64_t nb)
+                                                            int shift, const uint32_t *__restrict__ offs, int64_t nb,
+                                                            uint32_t *__restrict__ xf)
 {
+    if (xf_skip<MODE>(xf)) return;   // the whole grid
+    uint32_t xo = 0u;
+    bool tf = false;
+    if (MODE == 1) {
+        xf_range(xf, xo, tf);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            xf[0] = xo;
+            xf[1] = tf ? 1u : 0u;
+        }
+    }
     const int64_t m = elem_count(m_max, m_dev);
     __shared__ uint32_t wcnt[4][256];
     __shared__ uint32_t bstart[256];
@@ -206,7 +284,8 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
     for (int r = 0; r < kRxItems; ++r) {
         const int64_t e = base + r * 64;
         const bool valid = e < m;
-        const uint32_t k = valid ? kin[e] : 0u;
+        uint32_t k = valid ? kin[e] : 0u;
+        if (tf) k = k == 0xFFFFFFFFu ? 0xFFFFFFu : k - xo;
         const V v = valid ? vin[e] : V(0);
         const uint32_t d = (k >> shift) & 255u;
         uint64_t same = __ballot(valid);
@@ -300,17 +379,25 @@ __host__ __device__ constexpr int lb_items(int64_t m) { return m <= 1500000 ? 16
 // clear (nullable): the tile also sets clear[x] = 0 for x in its own output range
 // [prefix, prefix + tile sum) below clear_lim, so that one coalesced pass zeroes the
 // elements the scanned counts give out (each tile's range is contiguous).
-template <int ITEMS, bool HI32>
+// DEV only: skip (nullable): when *skip != 0 the whole scan does nothing (no block takes a
+// ticket); in_alt, sel (nullable): when *sel != 0 the input is in_alt instead of in_v.
+template <int ITEMS, bool HI32, bool DEV>
 __global__ __launch_bounds__(kThreads) void k_scan_lb(const void *in_v, uint32_t *out, int64_t m,
                                                       unsigned long long *__restrict__ status,
                                                       uint32_t *__restrict__ ticket,
                                                       unsigned long long *__restrict__ total,
-                                                      uint32_t *__restrict__ clear, int64_t clear_lim)
+                                                      uint32_t *__restrict__ clear, int64_t clear_lim,
+                                                      const uint32_t *__restrict__ skip, const void *in_alt,
+                                                      const uint32_t *__restrict__ sel)
 {
     constexpr int kT = kThreads * ITEMS;
     __shared__ uint32_t scratch[4];
     __shared__ uint32_t s_tile;
     __shared__ unsigned long long s_excl;
+    if (DEV) {
+        if (skip && *skip) return;   // uniform over the grid
+        if (sel && *sel) in_v = in_alt;
+    }
     if (threadIdx.x == 0) s_tile = atomicAdd(ticket, 1u);
     __syncthreads();
     const int64_t tile = s_tile;
@@ -404,17 +491,24 @@ __global__ __launch_bounds__(kThreads) void k_scan_lb(const void *in_v, uint32_t
 template <bool HI32>
 gs_status launch_scan_lb(const void *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
                          unsigned long long *total, hipStream_t stream, uint32_t *clear = nullptr,
-                         int64_t clear_lim = 0)
+                         int64_t clear_lim = 0, const uint32_t *skip = nullptr, const void *in_alt = nullptr,
+                         const uint32_t *sel = nullptr)
 {
     if (m <= 0) return gsi::fail(GS_ERR_UNSUPPORTED, "scan of an empty array");
     const int items = lb_items(m);
     const unsigned grid = (unsigned)gsi::ceil_div(m, (int64_t)kThreads * items);
-    if (items == 16)
-        k_scan_lb<16, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total, clear, clear_lim);
-    else if (items == 32)
-        k_scan_lb<32, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total, clear, clear_lim);
-    else
-        k_scan_lb<64, HI32><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total, clear, clear_lim);
+    const bool dev = skip || sel;
+#define GS_SCAN_LB(IT, D)                                                                                           \
+    k_scan_lb<IT, HI32, D><<<grid, kThreads, 0, stream>>>(in, out, m, status, ticket, total, clear, clear_lim, skip, \
+                                                          in_alt, sel)
+    if (items == 16) {
+        if (dev) GS_SCAN_LB(16, true); else GS_SCAN_LB(16, false);
+    } else if (items == 32) {
+        if (dev) GS_SCAN_LB(32, true); else GS_SCAN_LB(32, false);
+    } else {
+        if (dev) GS_SCAN_LB(64, true); else GS_SCAN_LB(64, false);
+    }
+#undef GS_SCAN_LB
     GS_LAUNCH_CHECK("k_scan_lb");
     return GS_OK;
 }
@@ -469,10 +563,11 @@ gs_status lb_scan_u32(const uint32_t *in, uint32_t *out, int64_t m, unsigned lon
 }
 
 gs_status lb_scan_hi32(const uint64_t *in, uint32_t *out, int64_t m, unsigned long long *status, uint32_t *ticket,
-                       unsigned long long *total, hipStream_t stream)
+                       unsigned long long *total, hipStream_t stream, const uint64_t *in_alt, const uint32_t *sel)
 {
-    if (!aligned(in, 16)) return fail(GS_ERR_INVALID_ARGUMENT, "scan input must be 16-byte aligned");
-    return launch_scan_lb<true>(in, out, m, status, ticket, total, stream);
+    if (!aligned(in, 16) || (in_alt && !aligned(in_alt, 16)))
+        return fail(GS_ERR_INVALID_ARGUMENT, "scan input must be 16-byte aligned");
+    return launch_scan_lb<true>(in, out, m, status, ticket, total, stream, nullptr, 0, nullptr, in_alt, sel);
 }
 
 int64_t radix_scan_status_len(int64_t m, int bits)
@@ -483,8 +578,9 @@ int64_t radix_scan_status_len(int64_t m, int bits)
 template <typename V>
 gs_status radix_sort_kv(uint32_t *ka, V *va, uint32_t *kb, V *vb, int64_t m, int bits, uint32_t *hist,
                         unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b, hipStream_t stream,
-                        const unsigned long long *m_dev)
+                        const unsigned long long *m_dev, uint32_t *xf)
 {
+    if (xf && bits != 32) return fail(GS_ERR_INVALID_ARGUMENT, "key range reduction needs a 32-bit sort");
     *in_b = false;
     if (m <= 1 || bits <= 0) return GS_OK;
     const int64_t nb = ceil_div(m, kRxTile);
@@ -493,12 +589,24 @@ gs_status radix_sort_kv(uint32_t *ka, V *va, uint32_t *kb, V *vb, int64_t m, int
     V *sv = va, *dv = vb;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
-        k_radix_hist<<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb);
+        const int mode = !xf ? 0 : p == 0 ? 1 : p == 3 ? 2 : 0;
+        if (mode == 1)
+            k_radix_hist<1><<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb, xf);
+        else if (mode == 2)
+            k_radix_hist<2><<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb, xf);
+        else
+            k_radix_hist<0><<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb, xf);
         GS_LAUNCH_CHECK("k_radix_hist");
-        gs_status s = lb_scan_u32(hist, hist, 256 * nb, scan_status + p * lb_scan_tiles(256 * nb), scan_tickets + p,
-                                  nullptr, stream);
+        gs_status s = launch_scan_lb<false>(hist, hist, 256 * nb, scan_status + p * lb_scan_tiles(256 * nb),
+                                            scan_tickets + p, nullptr, stream, nullptr, 0,
+                                            mode == 2 ? xf + 1 : nullptr);
         if (s != GS_OK) return s;
-        k_radix_scatter<V><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb);
+        if (mode == 1)
+            k_radix_scatter<V, 1><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf);
+        else if (mode == 2)
+            k_radix_scatter<V, 2><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf);
+        else
+            k_radix_scatter<V, 0><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf);
         GS_LAUNCH_CHECK("k_radix_scatter");
         std::swap(sk, dk);
         std::swap(sv, dv);
@@ -511,14 +619,14 @@ gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb,
                          uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
                          hipStream_t stream, const unsigned long long *m_dev)
 {
-    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev);
+    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev, nullptr);
 }
 
 gs_status radix_sort_u32_u64(uint32_t *ka, uint64_t *va, uint32_t *kb, uint64_t *vb, int64_t m, int bits,
                              uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
-                             hipStream_t stream, const unsigned long long *m_dev)
+                             hipStream_t stream, const unsigned long long *m_dev, uint32_t *xf)
 {
-    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev);
+    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev, xf);
 }
 
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream)

@@ -103,6 +103,36 @@ def test_bin_sort_bit_exact(n, W, H, maxr, seed):
         assert np.array_equal(bins.keys[:k].cpu().numpy().view(np.uint64), keys)
 
 
+@pytest.mark.parametrize("n,span,seed", [
+    (2, 0, 11), (3000, 0, 12), (20000, 0xFFFFFE, 13), (20000, 0xFFFFFF, 14), (20000, 0x1000000, 15),
+    (200000, 0x7FFFFF, 16),
+])
+def test_bin_sort_depth_key_span(n, span, seed):
+    """The depth sort orders by the float bits of the depth; visible depths whose keys span
+    at most 2^24 - 2 take a shorter path than wider ones.  Depths here are built from their
+    bit patterns at the edges of that range (the smallest and the largest key both present,
+    repeated keys included); the lists must equal the oracle's either way."""
+    log(f"bin sort depth key span n={n} span={span:#x}")
+    W, H = 640, 360
+    m2, r, _ = scenes.projected_for_binning(seed, n, W, H, max_radius=20)
+    g = np.random.default_rng(seed)
+    base = np.uint32(np.float32(20.0).view(np.uint32))
+    off = g.integers(0, span + 1, size=n, dtype=np.int64)
+    off[g.random(n) < 0.1] = span // 3
+    vis = np.flatnonzero((r[:, 0] > 0).numpy())
+    if len(vis) >= 2:
+        off[vis[0]], off[vis[-1]] = span, 0
+    d = torch.from_numpy((base + off.astype(np.uint32)).view(np.float32).copy())
+    k, bins = _bin_gpu(m2, r, d, W, H)
+    tt, keys, ids, ranges = oracle.bin_f32(m2, r, d, W, H)
+    assert k == len(ids)
+    assert np.array_equal(bins.tile_ranges.cpu().numpy(), ranges)
+    assert np.array_equal(bins.tiles_touched.cpu().numpy(), tt)
+    if k:
+        assert np.array_equal(bins.ids[:k].cpu().numpy().view(np.uint32), ids)
+        assert np.array_equal(bins.keys[:k].cpu().numpy().view(np.uint64), keys)
+
+
 def test_bin_sort_all_culled_and_capacity():
     m2, r, d = scenes.projected_for_binning(9, 4000, 200, 150, max_radius=20)
     r0 = torch.zeros_like(r)
