@@ -27,7 +27,8 @@ without the system-scope fence, see TimingEvent).
 over-composited, L1 on the composite, the composite backward, each slab's backward
 rasterization and per-Gaussian sum, compaction of its non-zero gradient records, their
 decoding into the slab owner's gradient planes, and the owner's projection backward and
-Adam.  The timed steps run each slab's calls on a stream of its own (the slabs share
+Adam in one pass, which also projects the updated slab for the next step (so a step
+starts at the binning).  The timed steps run each slab's calls on a stream of its own (the slabs share
 nothing between the composites); `kernels` times every call with events in as many
 serial steps afterwards, whose wall time is serial_ms_per_step.
 
@@ -53,6 +54,7 @@ from __future__ import annotations
 
 import argparse
 import contextlib
+import gc
 import json
 import os
 import sys
@@ -60,6 +62,17 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+
+def quiet_gc():
+    """Collects once, then switches Python's cyclic garbage collector off for the timed
+    loops, so that no collection pauses the host inside a timed call.  Without the
+    collection up front, one pause of tens of milliseconds (with the GPU idle) landed
+    inside a single call of the 20M step's per-call breakdown, presumably the collection
+    that freed the scene's multi-gigabyte host tensors."""
+    gc.collect()
+    gc.disable()
+
 
 METRIC = "Gaussian-pixel intersections/s (fwd+bwd); train-step ms at 1M Gaussians 1080p"
 METRIC_OF = {"1m": METRIC,
@@ -187,6 +200,8 @@ def hbm_bytes(kernel, n, n_vis, k_sh, n_isect, n_px):
         return 36 * n_isect + n * (11 + 3 * k_sh) * 24
     if kernel == "grad_adam_project":                               # the same + the next view's projection
         return 36 * n_isect + n * (11 + 3 * k_sh) * 24 + n_vis * 60 + (n - n_vis) * 12
+    if kernel == "update":                                          # grads2d read; p, m, v; the next projection
+        return 36 * n + n * (11 + 3 * k_sh) * 24 + n_vis * 60 + (n - n_vis) * 12
     return None
 
 
@@ -449,10 +464,10 @@ def main_partitioned(args):
         st.bins._alloc(int(st.bins.capacity * 1.3) + 4096)
     torch.cuda.synchronize()
 
+    # Each slab's update (projection backward + Adam) also projects the updated slab for the
+    # next step's camera, so a step after the first starts at the binning.
     def one_step(t):
         for k, st in enumerate(ps.parts):
-            with t("project"):
-                B.gs_project(st.params.gaussians(), cam, st.raster, st.proj.abi())
             with t("bin_sort"):
                 st.bins.sort(st.proj, cam, st.raster)
             with t("raster_fwd"):
@@ -475,18 +490,17 @@ def main_partitioned(args):
                 ps.compact_part(k)
             with t("decode"):
                 ps.decode_part(k)
-            with t("project_bwd"):
-                B.gs_project_bwd(st.params.gaussians(), cam, st.raster, ps.owner_g2[k], st.params.param_grads())
-            with t("adam"):
-                st.adam()
+            with t("update"):
+                ps.update_part(k, cam, next_cam=cam)
 
     # The timed steps run the slabs side by side (PartitionedStep.step_overlapped: each slab
     # on a stream of its own, binning without host waits); the per-call breakdown comes from
     # the same number of serial steps afterwards, every call between HIP events (events
     # around overlapped calls would not time the calls).
     tgt = target
-    for _ in range(args.warmup):
-        ps.step_overlapped(cam, tgt, join=False)
+    quiet_gc()
+    for _ in range(args.warmup):   # ps.forward above projected every slab for cam
+        ps.step_overlapped(cam, tgt, join=False, next_cam=cam, projected=True)
     ps.join()
     torch.cuda.synchronize()
     if not ps.check_capacity():
@@ -496,7 +510,8 @@ def main_partitioned(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        ps.step_overlapped(cam, tgt, join=False)   # a slab's update overlaps the next step's binning
+        # a slab's update overlaps the next step's binning of the others
+        ps.step_overlapped(cam, tgt, join=False, next_cam=cam, projected=True)
     ps.join()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -540,7 +555,8 @@ def main_partitioned(args):
         kernels[nm] = entry
     dom = max(per_kernel, key=per_kernel.get)
     d = kernels[dom]
-    kern = {"raster_bwd": "k_raster_bwd", "raster_fwd": "k_raster_fwd", "bin_sort": "gs_bin_sort"}.get(dom, dom)
+    kern = {"raster_bwd": "k_raster_bwd", "raster_fwd": "k_raster_fwd", "bin_sort": "gs_bin_sort",
+            "update": "k_proj_bwd_adam"}.get(dom, dom)
     if d.get("bound") == "alu":
         per_launch = dict(d, ms=round(d["ms"] / parts, 4))
         roof = alu_roofline(kern, dom, per_launch, [w / parts for w in walk_step], isect_step / parts, None)
@@ -555,8 +571,9 @@ def main_partitioned(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": desc, "gaussians": n, "sh_degree": scene.sh_degree, "image": [W, H], "views": 1,
                    "slabs": parts, "slab_gaussians": [st.params.n for st in ps.parts],
-                   "step": "per slab projection + binning + forward; composite; L1; composite backward; per slab "
-                           "backward raster + per-Gaussian sum + compaction + decoding + projection backward + Adam",
+                   "step": "per slab binning + forward; composite; L1; composite backward; per slab backward "
+                           "raster + per-Gaussian sum + compaction + decoding + projection backward + Adam + the "
+                           "next step's projection (the last three in one pass)",
                    "schedule": "each slab's calls on a stream of its own (PartitionedStep.step_overlapped)"},
         "roofline": roof,
         "intersections_per_step": round(isect_step, 1),
@@ -644,6 +661,7 @@ def main_batch(args):
         torch.cuda.synchronize()
         del src, dst
     bt.project([cams[v] for v in views_of(0)])
+    quiet_gc()
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
@@ -863,6 +881,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     project_for(0)
+    quiet_gc()
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()

@@ -30,7 +30,7 @@ EXPORTED = ("gs_project", "gs_bins_raster_bytes", "gs_bin_sort_workspace_bytes",
             "gs_loss_l1", "gs_loss_l1_dssim", "gs_loss_l1_dssim_workspace_bytes", "gs_raster_bwd", "gs_raster_bwd_partials", "gs_grad_aggregate", "gs_grad_aggregate_adam", "gs_grad_aggregate_adam_project",
             "gs_raster_fused_l1", "gs_raster_fused_l1_workspace_bytes", "gs_raster_fused_l1_noalloc",
             "gs_tile_budget", "gs_tile_budget_report",
-            "gs_project_bwd", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
+            "gs_project_bwd", "gs_project_bwd_adam", "gs_adam_step", "gs_composite_over", "gs_composite_over_bwd",
             "gs_compact_workspace_bytes", "gs_compact_grads", "gs_decode_grads", "gs_project_batch",
             "gs_grad_aggregate_adam_batch", "gs_adam_batch_hparams", "gs_last_error")
 
@@ -62,7 +62,8 @@ class RasterParams(ctypes.Structure):
 
 class Gaussians(ctypes.Structure):
     _fields_ = [("means", ctypes.c_void_p), ("log_scales", ctypes.c_void_p), ("quats", ctypes.c_void_p),
-                ("opacity_logits", ctypes.c_void_p), ("sh", ctypes.c_void_p), ("n", ctypes.c_int64)]
+                ("opacity_logits", ctypes.c_void_p), ("sh", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("ld", ctypes.c_int64)]
 
 
 class Projected(ctypes.Structure):
@@ -77,7 +78,7 @@ class Bins(ctypes.Structure):
 
 class ParamGrads(ctypes.Structure):
     _fields_ = [("means", ctypes.c_void_p), ("log_scales", ctypes.c_void_p), ("quats", ctypes.c_void_p),
-                ("opacity_logits", ctypes.c_void_p), ("sh", ctypes.c_void_p)]
+                ("opacity_logits", ctypes.c_void_p), ("sh", ctypes.c_void_p), ("ld", ctypes.c_int64)]
 
 
 class AdamLrs(ctypes.Structure):
@@ -119,6 +120,9 @@ _SIGS = {
     "gs_grad_aggregate_adam_project": (_i32, [_P(Gaussians), _P(Projected), _P(Bins), _P(Camera), _P(RasterParams),
                                               _vp, _P(ParamGrads), _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32,
                                               _f32, _P(Camera), _P(Projected), _vp]),
+    "gs_project_bwd_adam": (_i32, [_P(Gaussians), _P(Camera), _P(RasterParams), _vp, _P(ParamGrads),
+                                   _P(ParamGrads), _P(AdamLrs), _i32, _f32, _f32, _f32, _P(Camera), _P(Projected),
+                                   _vp]),
     "gs_raster_fused_l1": (_i32, [_P(Gaussians), _P(Bins), _P(Camera), _P(RasterParams), _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "gs_raster_fused_l1_workspace_bytes": (ctypes.c_size_t, [_i32, _i32]),
@@ -166,6 +170,12 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _plane_ptr(t):
+    """The address of a [planes][n] parameter view whose rows are contiguous (the plane
+    stride is checked by _plane_stride)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -189,9 +199,29 @@ def make_params(sh_degree, alpha_min=1.0 / 255.0, alpha_max=0.99, t_min=1e-4, de
     return RasterParams(int(sh_degree), alpha_min, alpha_max, t_min, depth_lo, depth_hi)
 
 
+def _plane_stride(groups, n):
+    """The one plane stride of [planes][n] views (rows contiguous), 0 for plain [planes][n]."""
+    ld = None
+    for t in groups:
+        if t.dim() == 2 and t.shape[0] > 1:
+            if t.stride(1) != 1:
+                raise ValueError("parameter planes must be contiguous rows")
+            if ld is None:
+                ld = t.stride(0)
+            elif t.stride(0) != ld:
+                raise ValueError("every parameter group must have the same plane stride")
+        elif t.dim() >= 1 and t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError("parameter planes must be contiguous rows")
+    return 0 if ld is None or ld == n else ld
+
+
 def gaussians(means, log_scales, quats, opacity_logits, sh) -> Gaussians:
+    """[planes][n] tensors (views of [planes][ld] storage allowed: the plane stride is
+    taken from them and must be the same for every group)."""
     n = means.shape[-1]
-    return Gaussians(_ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh), n)
+    ld = _plane_stride((means, log_scales, quats, opacity_logits, sh), n)
+    return Gaussians(_plane_ptr(means), _plane_ptr(log_scales), _plane_ptr(quats), _plane_ptr(opacity_logits),
+                     _plane_ptr(sh), n, ld)
 
 
 def projected(means2d, conic_opacity, color, depth, radii, rec) -> Projected:
@@ -205,7 +235,10 @@ def bins(ids, tile_ranges, raster, keys=None, tiles_touched=None) -> Bins:
 
 
 def param_grads(means, log_scales, quats, opacity_logits, sh) -> ParamGrads:
-    return ParamGrads(_ptr(means), _ptr(log_scales), _ptr(quats), _ptr(opacity_logits), _ptr(sh))
+    n = means.shape[-1]
+    ld = _plane_stride((means, log_scales, quats, opacity_logits, sh), n)
+    return ParamGrads(_plane_ptr(means), _plane_ptr(log_scales), _plane_ptr(quats), _plane_ptr(opacity_logits),
+                      _plane_ptr(sh), ld)
 
 
 # ------------------------------------------------------------------ entry points (same names as the C ABI)
@@ -292,6 +325,15 @@ def gs_grad_aggregate_adam_project(g: Gaussians, proj: Projected, b: Bins, cam: 
                                                ctypes.byref(cam), ctypes.byref(p), _ptr(grads2d), ctypes.byref(m),
                                                ctypes.byref(v), ctypes.byref(lr), step, beta1, beta2, eps,
                                                ctypes.byref(next_cam), ctypes.byref(next_proj), _stream(stream)))
+
+
+def gs_project_bwd_adam(g: Gaussians, cam: Camera, p: RasterParams, grads2d, m: ParamGrads, v: ParamGrads,
+                        lr: "AdamLrs", step, beta1, beta2, eps, next_cam: Camera = None, next_proj: Projected = None,
+                        stream=None):
+    _check(_lib.gs_project_bwd_adam(ctypes.byref(g), ctypes.byref(cam), ctypes.byref(p), _ptr(grads2d),
+                                    ctypes.byref(m), ctypes.byref(v), ctypes.byref(lr), step, beta1, beta2, eps,
+                                    ctypes.byref(next_cam) if next_cam is not None else None,
+                                    ctypes.byref(next_proj) if next_proj is not None else None, _stream(stream)))
 
 
 def gs_loss_l1_dssim_workspace_bytes(width, height) -> int:

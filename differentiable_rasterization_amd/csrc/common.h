@@ -32,6 +32,10 @@ inline int tiles_y(int h) { return (h + GS_TILE - 1) / GS_TILE; }
 constexpr int kXcds = 8;
 inline int xcd_per(int tiles) { return (tiles + kXcds - 1) / kXcds; }
 
+// Plane strides of the parameter groups and of gradient / moment sets (0 in the struct: n).
+inline int64_t param_ld(const gs_gaussians *g) { return g->ld ? g->ld : g->n; }
+inline int64_t grads_ld(const gs_param_grads *pg, int64_t n) { return pg->ld ? pg->ld : n; }
+
 gs_status check_camera(const gs_camera *cam);
 gs_status check_params(const gs_raster_params *p);
 

@@ -285,6 +285,7 @@ __device__ __forceinline__ void load_params(const float *__restrict__ means, con
                                             const float *__restrict__ quats, const float *__restrict__ logits,
                                             const float *__restrict__ sh, int64_t n, int64_t i, Params1<K> &prm)
 {
+    // n: the plane stride of the parameter groups
     const auto ld = [](const float *p) { return NT ? __builtin_nontemporal_load(p) : *p; };
     const auto ld_sh = [](const float *p) { return NT_SH ? __builtin_nontemporal_load(p) : *p; };
     prm.means[0] = ld(means + i); prm.means[1] = ld(means + n + i); prm.means[2] = ld(means + 2 * n + i);
@@ -424,14 +425,14 @@ __device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG +
 template <int DEG>
 __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means, const float *__restrict__ log_scales,
                                                  const float *__restrict__ quats, const float *__restrict__ logits,
-                                                 const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+                                                 const float *__restrict__ sh, int64_t n, int64_t ldp, CamD cam, float alpha_min,
                                                  float depth_lo, float depth_hi, ProjOut po)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     Params1<K> prm;
-    load_params<false>(means, log_scales, quats, logits, sh, n, i, prm);
+    load_params<false>(means, log_scales, quats, logits, sh, ldp, i, prm);
     project_store<DEG>(prm, cam, alpha_min, depth_lo, depth_hi, i, po);
 }
 
@@ -451,7 +452,7 @@ struct Grad3 {
 
 struct GradSink {
     float *d_means, *d_ls, *d_q, *d_logit, *d_sh;
-    int64_t n;
+    int64_t n;   // the plane stride of the gradient planes
     template <int K>
     __device__ void flush(int64_t i, const Grad3<K> &g, const Params1<K> &) const
     {
@@ -488,7 +489,7 @@ constexpr int view_chunk(int planes)
 // chunk's loads are in flight during the previous chunk's arithmetic and stores.
 struct AdamSink {
     float *p[5], *m[5], *v[5];   // means, log_scales, quats, opacity_logits, sh
-    int64_t n;
+    int64_t n;                   // the plane stride of p, m and v
     float st[6];                 // lr / (1 - b1^t): means, log_scales, quats, opacity, sh DC, sh rest
     float b1, b2, inv_bc2, eps;
 
@@ -825,14 +826,14 @@ __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam
 template <int DEG, bool RAW, bool NEXT, class Sink>
 __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means, const float *__restrict__ log_scales,
                                                 const float *__restrict__ quats, const float *__restrict__ logits,
-                                                const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
+                                                const float *__restrict__ sh, int64_t n, int64_t ldp, int64_t i, const CamD &cam,
                                                 float alpha_min, float depth_lo, float depth_hi, const float (&in)[9],
                                                 float *__restrict__ grads2d, const Sink &out, const CamD &next_cam,
                                                 const ProjOut &next)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     Params1<K> prm;
-    load_params<std::is_same<Sink, AdamSink>::value>(means, log_scales, quats, logits, sh, n, i, prm);
+    load_params<std::is_same<Sink, AdamSink>::value>(means, log_scales, quats, logits, sh, ldp, i, prm);
     const bool shf = sh_finite(prm);
     Proj P;
     const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
@@ -864,13 +865,14 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
     if constexpr (NEXT) project_store<DEG>(prm, next_cam, alpha_min, depth_lo, depth_hi, i, next);
 }
 
-// k_grad_adam's Gaussian: the per-Gaussian moment sums in (as project_bwd_one with RAW), the
-// projection backward and AdamSink::flush_view.  The SH coefficients are kept in the wave's
-// LDS (shs[plane][lane]) from the load to the update, not in registers.
-template <int DEG, bool NEXT>
+// k_grad_adam's Gaussian: the per-Gaussian moment sums in (as project_bwd_one with RAW; without
+// RAW, the screen-space gradients themselves), the projection backward and
+// AdamSink::flush_view.  The SH coefficients are kept in the wave's LDS (shs[plane][lane])
+// from the load to the update, not in registers.
+template <int DEG, bool NEXT, bool RAW = true>
 __device__ __forceinline__ void grad_adam_one(const float *__restrict__ means, const float *__restrict__ log_scales,
                                               const float *__restrict__ quats, const float *__restrict__ logits,
-                                              const float *__restrict__ sh, int64_t n, int64_t i, const CamD &cam,
+                                              const float *__restrict__ sh, int64_t n, int64_t ldp, int64_t i, const CamD &cam,
                                               float alpha_min, float depth_lo, float depth_hi, const float (&in)[9],
                                               float *__restrict__ grads2d, const AdamSink &out, const CamD &next_cam,
                                               const ProjOut &next, float (*shs)[64])
@@ -878,7 +880,7 @@ __device__ __forceinline__ void grad_adam_one(const float *__restrict__ means, c
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int lane = threadIdx.x & 63;
     Params1<K> prm;
-    load_params<true>(means, log_scales, quats, logits, sh, n, i, prm);
+    load_params<true>(means, log_scales, quats, logits, sh, ldp, i, prm);
 #pragma unroll
     for (int k = 0; k < 3 * K; ++k) shs[k][lane] = prm.sh[k];
     const bool shf = sh_finite(prm);
@@ -892,12 +894,17 @@ __device__ __forceinline__ void grad_adam_one(const float *__restrict__ means, c
     G.logit = 0.0f;
     G.gc[0] = G.gc[1] = G.gc[2] = 0.0f;
     float g2[9];
-    RecConic rc{0.0f, 0.0f, 0.0f, 0.0f};
-    if (P.vis) rc = rec_conic(P);
-    gsr::moments_to_grads(in, rc.a, rc.b, rc.c, rc.l, g2);
-    if (grads2d) {
+    if constexpr (RAW) {
+        RecConic rc{0.0f, 0.0f, 0.0f, 0.0f};
+        if (P.vis) rc = rec_conic(P);
+        gsr::moments_to_grads(in, rc.a, rc.b, rc.c, rc.l, g2);
+        if (grads2d) {
 #pragma unroll
-        for (int f = 0; f < 9; ++f) grads2d[(int64_t)f * n + i] = g2[f];
+            for (int f = 0; f < 9; ++f) grads2d[(int64_t)f * n + i] = g2[f];
+        }
+    } else {
+#pragma unroll
+        for (int f = 0; f < 9; ++f) g2[f] = in[f];
     }
     float dir[3] = {0.0f, 0.0f, 1.0f};
     if (P.vis) {
@@ -910,7 +917,7 @@ __device__ __forceinline__ void grad_adam_one(const float *__restrict__ means, c
 template <int DEG>
 __global__ __launch_bounds__(256) void k_project_bwd(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
-    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, int64_t ldp, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const float *__restrict__ g2, GradSink out)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -918,7 +925,7 @@ __global__ __launch_bounds__(256) void k_project_bwd(
     float g[9];
 #pragma unroll
     for (int f = 0; f < 9; ++f) g[f] = g2[(int64_t)f * n + i];
-    project_bwd_one<DEG, false, false>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo,
+    project_bwd_one<DEG, false, false>(means, log_scales, quats, logits, sh, n, ldp, i, cam, alpha_min, depth_lo,
                                        depth_hi, g, nullptr, out, cam, ProjOut{});
 }
 
@@ -937,7 +944,7 @@ __host__ __device__ constexpr size_t grad_adam_wave_lds(int deg)
 template <int DEG, bool NEXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_grad_adam(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
-    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, CamD cam, float alpha_min,
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, int64_t ldp, CamD cam, float alpha_min,
     float depth_lo, float depth_hi, const gsr::BinsHeader *__restrict__ hdr, const uint32_t *__restrict__ qoff,
     const float4 *__restrict__ qgrad, const uint32_t *__restrict__ qstamp, float *__restrict__ grads2d, AdamSink out,
     CamD next_cam, ProjOut next)
@@ -950,8 +957,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     if (i >= n) return;
     // the wave's stage is no longer read (each wave reads only its own; the sums end with a
     // wave barrier): its bytes now hold the lanes' SH coefficients
-    grad_adam_one<DEG, NEXT>(means, log_scales, quats, logits, sh, n, i, cam, alpha_min, depth_lo, depth_hi, acc,
+    grad_adam_one<DEG, NEXT>(means, log_scales, quats, logits, sh, n, ldp, i, cam, alpha_min, depth_lo, depth_hi, acc,
                              grads2d, out, next_cam, next, reinterpret_cast<float(*)[64]>(wl));
+}
+
+// The owner's update from screen-space gradients already summed per Gaussian (g2 [9][n],
+// e.g. decoded from other renderers' records): the projection backward, Adam and, with
+// NEXT, the projection of the updated Gaussian for the next camera, per Gaussian in one
+// pass, as k_grad_adam after its slot sums.
+__host__ __device__ constexpr size_t proj_bwd_adam_wave_lds(int deg)
+{
+    return (size_t)3 * (deg + 1) * (deg + 1) * 64 * sizeof(float);
+}
+
+template <int DEG, bool NEXT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_proj_bwd_adam(
+    const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, int64_t ldp, CamD cam, float alpha_min,
+    float depth_lo, float depth_hi, const float *__restrict__ g2, AdamSink out, CamD next_cam, ProjOut next)
+{
+    extern __shared__ __align__(16) unsigned char pba_lds[];   // proj_bwd_adam_wave_lds(DEG) per wave
+    float(*shs)[64] = reinterpret_cast<float(*)[64]>(pba_lds + (threadIdx.x >> 6) * proj_bwd_adam_wave_lds(DEG));
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float g[9];
+#pragma unroll
+    for (int f = 0; f < 9; ++f) g[f] = __builtin_nontemporal_load(g2 + (int64_t)f * n + i);
+    grad_adam_one<DEG, NEXT, false>(means, log_scales, quats, logits, sh, n, ldp, i, cam, alpha_min, depth_lo, depth_hi, g,
+                                    nullptr, out, next_cam, next, shs);
 }
 
 // -------------------------------------------------------------------- batches of views
@@ -998,14 +1031,14 @@ template <int DEG>
 __global__ __launch_bounds__(256) void k_project_batch(const float *__restrict__ means,
                                                        const float *__restrict__ log_scales,
                                                        const float *__restrict__ quats, const float *__restrict__ logits,
-                                                       const float *__restrict__ sh, int64_t n, float alpha_min,
-                                                       float depth_lo, float depth_hi, BatchProj bp)
+                                                       const float *__restrict__ sh, int64_t n, int64_t ldp,
+                                                       float alpha_min, float depth_lo, float depth_hi, BatchProj bp)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     Params1<K> prm;
-    load_params<false>(means, log_scales, quats, logits, sh, n, i, prm);
+    load_params<false>(means, log_scales, quats, logits, sh, ldp, i, prm);
     ProjScalars S;
     params_scalars(prm, alpha_min, S);
     for (int v = 0; v < bp.views; ++v) project_store_s<DEG>(prm, S, bp.cam[v], depth_lo, depth_hi, i, bp.out[v]);
@@ -1018,8 +1051,8 @@ __global__ __launch_bounds__(256) void k_project_batch(const float *__restrict__
 template <int DEG, bool NEXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_grad_adam_batch(
     const float *__restrict__ means, const float *__restrict__ log_scales, const float *__restrict__ quats,
-    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, float alpha_min, float depth_lo,
-    float depth_hi, BatchGrad bg, AdamSink out, BatchProj next)
+    const float *__restrict__ logits, const float *__restrict__ sh, int64_t n, int64_t ldp, float alpha_min,
+    float depth_lo, float depth_hi, BatchGrad bg, AdamSink out, BatchProj next)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     __shared__ gsr::SlotStage stage[4];
@@ -1030,7 +1063,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     ProjScalars PS;
     PS.ok = false;
     if (live) {
-        load_params<true>(means, log_scales, quats, logits, sh, n, i, prm);
+        load_params<true>(means, log_scales, quats, logits, sh, ldp, i, prm);
         params_scalars(prm, alpha_min, PS);
     }
     GradSum<K> S;
@@ -1089,6 +1122,7 @@ gs_status check_gaussians(const gs_gaussians *g)
     if (g->n > (int64_t(1) << 31) - 1) return fail(GS_ERR_UNSUPPORTED, "n >= 2^31");
     if (g->n > 0 && (!g->means || !g->log_scales || !g->quats || !g->opacity_logits || !g->sh))
         return fail(GS_ERR_INVALID_ARGUMENT, "a parameter pointer is NULL");
+    if (g->ld != 0 && g->ld < g->n) return fail(GS_ERR_INVALID_ARGUMENT, "plane stride ld < n");
     return GS_OK;
 }
 
@@ -1116,12 +1150,13 @@ gs_status launch_project_bwd(const gs_gaussians *g, const gs_camera *cam, const 
     if (n == 0) return GS_OK;
     if (!out->means || !out->log_scales || !out->quats || !out->opacity_logits || !out->sh)
         return fail(GS_ERR_INVALID_ARGUMENT, "a grads3d pointer is NULL");
+    if (out->ld != 0 && out->ld < n) return fail(GS_ERR_INVALID_ARGUMENT, "grads3d plane stride ld < n");
     const CamD cd = make_cam(cam);
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
-    const GradSink sink{out->means, out->log_scales, out->quats, out->opacity_logits, out->sh, n};
+    const GradSink sink{out->means, out->log_scales, out->quats, out->opacity_logits, out->sh, grads_ld(out, n)};
 #define GS_PB(D)                                                                                              \
     k_project_bwd<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, \
-                                                 n, cd, p->alpha_min, p->depth_lo, p->depth_hi, grads2d, sink)
+                                                 n, param_ld(g), cd, p->alpha_min, p->depth_lo, p->depth_hi, grads2d, sink)
     switch (p->sh_degree) {
     case 0: GS_PB(0); break;
     case 1: GS_PB(1); break;
@@ -1150,7 +1185,7 @@ extern "C" gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, con
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
     const ProjOut po = proj_out(out, n);
 #define GS_PF(D)                                                                                        \
-    k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
+    k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, param_ld(g), \
                                              cd, p->alpha_min, p->depth_lo, p->depth_hi, po)
     switch (p->sh_degree) {
     case 0: GS_PF(0); break;
@@ -1194,7 +1229,11 @@ gs_status make_adam_sink(const gs_gaussians *g, const gs_param_grads *m, const g
     float *ms[5] = {m->means, m->log_scales, m->quats, m->opacity_logits, m->sh};
     float *vs[5] = {v->means, v->log_scales, v->quats, v->opacity_logits, v->sh};
     for (int a = 0; a < 5; ++a) { sink.p[a] = params[a]; sink.m[a] = ms[a]; sink.v[a] = vs[a]; }
-    sink.n = g->n;
+    // p, m and v share one plane stride
+    const int64_t ld = param_ld(g);
+    if (grads_ld(m, g->n) != ld || grads_ld(v, g->n) != ld)
+        return fail(GS_ERR_INVALID_ARGUMENT, "the Adam moments must have the parameters' plane stride");
+    sink.n = ld;
     // the same host arithmetic as gs_adam_step, so that both paths agree bit for bit
     const double bc1 = 1.0 - std::pow((double)beta1, step), bc2 = 1.0 - std::pow((double)beta2, step);
     const float lrs[6] = {lr->means, lr->log_scales, lr->quats, lr->opacity_logits, lr->sh_dc, lr->sh_rest};
@@ -1271,12 +1310,12 @@ gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, cons
         const size_t lds = (size_t)(bt / 64) * grad_adam_wave_lds(D);                                              \
         if (next_cam)                                                                                              \
             k_grad_adam<D, true><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,                  \
-                                                               g->opacity_logits, g->sh, n, cd, p->alpha_min,      \
+                                                               g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min,      \
                                                                p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,        \
                                                                grads2d, sink, nd, po);                             \
         else                                                                                                       \
             k_grad_adam<D, false><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,                 \
-                                                                g->opacity_logits, g->sh, n, cd, p->alpha_min,     \
+                                                                g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min,     \
                                                                 p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,       \
                                                                 grads2d, sink, nd, po);                            \
     } while (0)
@@ -1315,6 +1354,55 @@ extern "C" gs_status gs_grad_aggregate_adam_project(const gs_gaussians *g, const
                             stream);
 }
 
+extern "C" gs_status gs_project_bwd_adam(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                                        const float *grads2d, const gs_param_grads *m, const gs_param_grads *v,
+                                        const gs_adam_lrs *lr, int32_t step, float beta1, float beta2, float eps,
+                                        const gs_camera *next_cam, gs_projected *next_proj, hipStream_t stream)
+{
+    using namespace gsi;
+    gs_status s;
+    if ((s = check_gaussians(g)) != GS_OK) return s;
+    if ((s = check_camera(cam)) != GS_OK) return s;
+    if ((s = check_params(p)) != GS_OK) return s;
+    if ((s = check_adam_args(m, v, lr, step, beta1, beta2, eps)) != GS_OK) return s;
+    const int64_t n = g->n;
+    if (n > 0 && !grads2d) return fail(GS_ERR_INVALID_ARGUMENT, "grads2d is NULL");
+    if (next_cam) {
+        if ((s = check_camera(next_cam)) != GS_OK) return s;
+        if ((s = check_proj_out(next_proj, n)) != GS_OK) return s;
+    }
+    if (n == 0) return GS_OK;
+    AdamSink sink;
+    if ((s = make_adam_sink(g, m, v, lr, step, beta1, beta2, eps, sink)) != GS_OK) return s;
+    const CamD cd = make_cam(cam);
+    const CamD nd = next_cam ? make_cam(next_cam) : cd;
+    const ProjOut po = next_cam ? proj_out(next_proj, n) : ProjOut{};
+    const int bt = n <= (int64_t(1) << 22) ? 64 : 128;   // as k_grad_adam
+    const dim3 grid((unsigned)ceil_div(n, (int64_t)bt)), block((unsigned)bt);
+#define GS_PBA(D)                                                                                                  \
+    do {                                                                                                           \
+        const size_t lds = (size_t)(bt / 64) * proj_bwd_adam_wave_lds(D);                                          \
+        if (next_cam)                                                                                              \
+            k_proj_bwd_adam<D, true><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,              \
+                                                                   g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min,  \
+                                                                   p->depth_lo, p->depth_hi, grads2d, sink, nd, po); \
+        else                                                                                                       \
+            k_proj_bwd_adam<D, false><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,             \
+                                                                    g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min, \
+                                                                    p->depth_lo, p->depth_hi, grads2d, sink, nd,   \
+                                                                    po);                                           \
+    } while (0)
+    switch (p->sh_degree) {
+    case 0: GS_PBA(0); break;
+    case 1: GS_PBA(1); break;
+    case 2: GS_PBA(2); break;
+    default: GS_PBA(3); break;
+    }
+#undef GS_PBA
+    GS_LAUNCH_CHECK("k_proj_bwd_adam");
+    return GS_OK;
+}
+
 extern "C" gs_status gs_project_batch(const gs_gaussians *g, int32_t views, const gs_camera *cams,
                                       const gs_raster_params *p, gs_projected *out, hipStream_t stream)
 {
@@ -1336,7 +1424,7 @@ extern "C" gs_status gs_project_batch(const gs_gaussians *g, int32_t views, cons
     if (n == 0) return GS_OK;
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
 #define GS_PB(D)                                                                                                    \
-    k_project_batch<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
+    k_project_batch<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, param_ld(g), \
                                                    p->alpha_min, p->depth_lo, p->depth_hi, bp)
     switch (p->sh_degree) {
     case 0: GS_PB(0); break;
@@ -1394,11 +1482,11 @@ extern "C" gs_status gs_grad_aggregate_adam_batch(const gs_gaussians *g, int32_t
     do {                                                                                                             \
         if (next_cams)                                                                                               \
             k_grad_adam_batch<D, true><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,                \
-                                                                   g->opacity_logits, g->sh, n, p->alpha_min,        \
+                                                                   g->opacity_logits, g->sh, n, param_ld(g), p->alpha_min,        \
                                                                    p->depth_lo, p->depth_hi, bg, sink, next);        \
         else                                                                                                         \
             k_grad_adam_batch<D, false><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,               \
-                                                                    g->opacity_logits, g->sh, n, p->alpha_min,       \
+                                                                    g->opacity_logits, g->sh, n, param_ld(g), p->alpha_min,       \
                                                                     p->depth_lo, p->depth_hi, bg, sink, next);       \
     } while (0)
     switch (p->sh_degree) {

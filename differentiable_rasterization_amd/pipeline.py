@@ -8,9 +8,10 @@ of the computation runs in libgsmi's kernels:
 of one training step over depth slabs rendered separately and over-composited
 (PartitionedStep), and of one training step over a batch of views (BatchTrainStep).
 
-Parameters, gradients and the two Adam moments each live in one contiguous
-[planes][N] float32 buffer (structure of arrays), so every kernel streams
-coalesced planes and Adam runs as one launch over six parameter groups.
+Parameters, gradients and the two Adam moments each live in one [planes][LD]
+float32 buffer (structure of arrays, LD = N rounded up to 64), so every kernel
+streams coalesced planes whose 64-Gaussian segments cover whole cache lines, and
+Adam runs as one launch over six parameter groups.
 """
 from __future__ import annotations
 
@@ -26,16 +27,23 @@ DEFAULT_LR = dict(means=1.6e-4, log_scales=5e-3, quats=1e-3, opacity_logits=5e-2
 
 
 class GaussianParams:
-    """Learnable parameters plus gradients and Adam moments, structure of arrays."""
+    """Learnable parameters plus gradients and Adam moments, structure of arrays.
+
+    Each set is stored as [planes][ld] with ld = n rounded up to 64 (a plane stride whose
+    64-Gaussian segments start on 256-byte boundaries; the per-Gaussian kernels run up to
+    twice as long on planes that straddle cache lines).  data, grad, m and v are the
+    [planes][n] views; the padding stays zero (Adam leaves zero entries at zero)."""
+
+    LD_ALIGN = 64
 
     def __init__(self, n: int, sh_degree: int, device="cuda"):
         self.n, self.sh_degree = n, sh_degree
         self.k_sh = (sh_degree + 1) ** 2
         self.planes = 11 + 3 * self.k_sh
-        self.data = torch.zeros(self.planes, n, dtype=torch.float32, device=device)
-        self.grad = torch.zeros_like(self.data)
-        self.m = torch.zeros_like(self.data)
-        self.v = torch.zeros_like(self.data)
+        self.ld = -(-n // self.LD_ALIGN) * self.LD_ALIGN
+        z = lambda: torch.zeros(self.planes, self.ld, dtype=torch.float32, device=device)
+        self.store = dict(data=z(), grad=z(), m=z(), v=z())
+        self.data, self.grad, self.m, self.v = (self.store[k][:, :n] for k in ("data", "grad", "m", "v"))
         self.step_count = 0
 
     _SLICES = (("means", 0, 3), ("log_scales", 3, 6), ("quats", 6, 10), ("opacity_logits", 10, 11))
@@ -71,13 +79,16 @@ class GaussianParams:
         return ps(self.m), ps(self.v)
 
     def adam_groups(self, lr=DEFAULT_LR):
+        """Six flat groups over the padded rows (the padding has zero gradients and moments,
+        so Adam leaves it at zero)."""
         bounds = [("means", 0, 3), ("log_scales", 3, 6), ("quats", 6, 10), ("opacity_logits", 10, 11),
                   ("sh_dc", 11, 14), ("sh_rest", 14, self.planes)]
+        st = self.store
         out = []
         for name, a, b in bounds:
             if b <= a:
                 continue
-            out.append((self.data[a:b], self.grad[a:b], self.m[a:b], self.v[a:b], lr[name]))
+            out.append((st["data"][a:b], st["grad"][a:b], st["m"][a:b], st["v"][a:b], lr[name]))
         return out
 
 
@@ -387,7 +398,9 @@ class PartitionedStep:
     which are compacted to the records of non-zero Gaussians (ByteSplat section 6.1) and
     decoded into the owner's gradient planes (section 6.2).  On one GPU a slab's renderer
     and owner are the same; the exchange between them is left out.  The owner then runs
-    the projection backward and Adam for its Gaussians.
+    the projection backward and Adam for its Gaussians in one pass (gs_project_bwd_adam),
+    which with next_cam also projects the updated slab for the next step's camera, so that
+    the next step (projected=True) starts at the binning.
 
     slabs: one GaussianParams per slab (disjoint Gaussians); windows: the slabs' depth
     windows [lo, hi) of the projection (Gaussians outside are culled)."""
@@ -428,9 +441,14 @@ class PartitionedStep:
         B.gs_composite_over([st.frame.color for st in self.parts], [st.frame.t_final for st in self.parts],
                             self.n_px, self.t_min, self.color, self.t_final, stream)
 
-    def forward(self, cam: B.Camera, stream=None):
-        for k in range(len(self.parts)):
-            self.render_part(k, cam, stream)
+    def forward(self, cam: B.Camera, stream=None, projected=False):
+        """projected: each slab's projection buffers already hold its projection for cam
+        (written by the previous step's update with next_cam = cam)."""
+        for k, st in enumerate(self.parts):
+            if projected:
+                st.forward_projected(cam, stream)
+            else:
+                self.render_part(k, cam, stream)
         self.composite(stream)
 
     def loss(self, target, stream=None):
@@ -461,8 +479,20 @@ class PartitionedStep:
         self.owner_g2[k].zero_()
         B.gs_decode_grads([(self.records[k], self.r[k], 0, None, n)], self.owner_g2[k], n, None, stream)
 
-    def update_part(self, k, cam: B.Camera, stream=None):
-        """The owner's projection backward from the decoded gradients, then Adam."""
+    def update_part(self, k, cam: B.Camera, stream=None, next_cam: B.Camera = None):
+        """The owner's projection backward from the decoded gradients and Adam in one pass;
+        with next_cam, also the projection of the updated slab for next_cam into the slab's
+        projection buffers.  The 3D gradients are not stored."""
+        st = self.parts[k]
+        st.params.step_count += 1
+        m, v = st.params.moments()
+        B.gs_project_bwd_adam(st.params.gaussians(), cam, st.raster, self.owner_g2[k], m, v, B.AdamLrs(**st.lr),
+                              st.params.step_count, 0.9, 0.999, 1e-15, next_cam,
+                              st.proj.abi() if next_cam is not None else None, stream)
+
+    def update_part_separate(self, k, cam: B.Camera, stream=None):
+        """update_part without next_cam as two calls: the projection backward into the
+        slab's 3D gradients, then Adam (the same result, bit for bit)."""
         st = self.parts[k]
         B.gs_project_bwd(st.params.gaussians(), cam, st.raster, self.owner_g2[k], st.params.param_grads(), stream)
         st.adam(stream)
@@ -474,12 +504,12 @@ class PartitionedStep:
             self.compact_part(k, stream)
             self.decode_part(k, stream)
 
-    def step(self, cam: B.Camera, target, stream=None):
-        self.forward(cam, stream)
+    def step(self, cam: B.Camera, target, stream=None, next_cam: B.Camera = None, projected=False):
+        self.forward(cam, stream, projected)
         self.loss(target, stream)
         self.backward(cam, stream)
         for k in range(len(self.parts)):
-            self.update_part(k, cam, stream)
+            self.update_part(k, cam, stream, next_cam)
 
     # -- the same step with the slabs side by side
     #
@@ -500,13 +530,14 @@ class PartitionedStep:
             self.streams = ViewStreams(len(self.parts) + 1)   # one per slab, then the raster stream
         return self.streams
 
-    def forward_overlapped(self, cam: B.Camera):
+    def forward_overlapped(self, cam: B.Camera, projected=False):
         vs = self._slab_streams()
         rs = vs.streams[-1]
         vs.fork()
         for k, st in enumerate(self.parts):
             with torch.cuda.stream(vs.streams[k]):
-                B.gs_project(st.params.gaussians(), cam, st.raster, st.proj.abi())
+                if not projected:
+                    B.gs_project(st.params.gaussians(), cam, st.raster, st.proj.abi())
                 st.bins.sort_async(st.proj, cam, st.raster, self.counts[k])
         for k, st in enumerate(self.parts):
             rs.wait_stream(vs.streams[k])   # slab k's lists
@@ -517,13 +548,14 @@ class PartitionedStep:
         vs.join()
         self.composite()
 
-    def backward_overlapped(self, cam: B.Camera, join=True):
+    def backward_overlapped(self, cam: B.Camera, join=True, next_cam: B.Camera = None):
         """Composite backward, then each slab's backward rasterization and per-Gaussian sum
         on the raster stream, and its compaction, decoding and update on its own stream.
         join=False leaves the updates running: the next step_overlapped orders each slab's
-        projection after its own update (same stream) and everything else after those, so
-        one slab's update overlaps the next step's binning of the others; call join() (or
-        synchronize) before reading the parameters."""
+        projection (with projected=True, its binning) after its own update (same stream)
+        and everything else after those, so one slab's update overlaps the next step's
+        binning of the others; call join() (or synchronize) before reading the parameters.
+        next_cam: as in update_part."""
         vs = self._slab_streams()
         rs = vs.streams[-1]
         self.composite_backward()
@@ -536,7 +568,7 @@ class PartitionedStep:
             with torch.cuda.stream(vs.streams[k]):
                 self.compact_part(k)   # waits for this slab's stream only
                 self.decode_part(k)
-                self.update_part(k, cam)
+                self.update_part(k, cam, next_cam=next_cam)
         if join:
             vs.join()
 
@@ -545,10 +577,10 @@ class PartitionedStep:
         if self.streams is not None:
             self.streams.join()
 
-    def step_overlapped(self, cam: B.Camera, target, join=True):
-        self.forward_overlapped(cam)
+    def step_overlapped(self, cam: B.Camera, target, join=True, next_cam: B.Camera = None, projected=False):
+        self.forward_overlapped(cam, projected)
         self.loss(target)
-        self.backward_overlapped(cam, join)
+        self.backward_overlapped(cam, join, next_cam)
 
     def check_capacity(self) -> bool:
         """After overlapped steps: True if every slab's lists fit; otherwise the short

@@ -23,7 +23,8 @@
  *   gradient records -> gs_composite_over(_bwd), gs_compact_grads  (Splaxel sections 4.2-4.3;
  *   ByteSplat section 3 Insight 4 and section 6.1)
  *   owner-side decoding and atomic aggregation of those records -> gs_decode_grads
- *   (ByteSplat section 6.2)
+ *   (ByteSplat section 6.2); the owner's update from the decoded gradients ->
+ *   gs_project_bwd_adam
  *   batches of views per optimiser step -> gs_project_batch, gs_grad_aggregate_adam_batch,
  *   gs_adam_batch_hparams  (ROCm blog, "Batching and Hyperparameter Scaling")
  *
@@ -87,10 +88,18 @@ typedef struct {
  *   means [3][n], log_scales [3][n] (scale = exp), quats [4][n] (w, x, y, z; normalised
  *   in the forward), opacity_logits [n] (opacity = sigmoid), sh [K*3][n] with
  *   K = (sh_degree+1)^2 and plane k*3 + c holding coefficient k of channel c
- *   (k = l*l + l + m, real orthonormal basis without Condon-Shortley phase). */
+ *   (k = l*l + l + m, real orthonormal basis without Condon-Shortley phase).
+ * ld: floats from one plane of a group to the next, the same for every group (0: n;
+ *   otherwise >= n).  Plane f of means is means[f * ld .. f * ld + n).  The kernels read
+ *   and write one plane segment per 64 Gaussians: with ld a multiple of 32 every segment
+ *   of a 256-byte-aligned group covers whole 128-byte lines; otherwise most segments
+ *   straddle lines that neighbouring waves write too, which on MI355X costs the
+ *   per-Gaussian passes up to twice their time (a padded ld of 64 is the recommended
+ *   layout). */
 typedef struct {
     const float *means, *log_scales, *quats, *opacity_logits, *sh;
     int64_t n;
+    int64_t ld;
 } gs_gaussians;
 
 /* Projected 2D records, one per Gaussian.
@@ -145,9 +154,11 @@ typedef struct {
     void *raster;
 } gs_bins;
 
-/* Gradients of the learnable parameters, same shapes as gs_gaussians. */
+/* Gradients of the learnable parameters (or Adam moments), same shapes as gs_gaussians;
+ * ld: their plane stride (0: the Gaussians' n; otherwise >= n). */
 typedef struct {
     float *means, *log_scales, *quats, *opacity_logits, *sh;
+    int64_t ld;
 } gs_param_grads;
 
 /* One Adam parameter group: n scalars of parameters p, gradients g, moments m, v. */
@@ -486,6 +497,20 @@ typedef struct {
  * whose partitions are decoded into the same grads2d may overlap on different streams. */
 gs_status gs_decode_grads(const gs_grad_records *parts, int32_t k, float *grads2d, int64_t n_owner,
                           uint32_t *rejected, hipStream_t stream);
+
+/* The owner's update from screen-space gradients already summed per Gaussian (grads2d
+ * [9][n], same field order as gs_raster_bwd; e.g. rebuilt by gs_decode_grads, ByteSplat
+ * section 6.2): per Gaussian in one pass, the projection backward of gs_project_bwd, the
+ * Adam update of gs_adam_step with those 3D gradients (which are never stored) and, if
+ * next_cam is non-NULL, the projection of the updated Gaussian for next_cam into next_proj
+ * (as gs_project(g, next_cam, p, next_proj) would write it afterwards; Splaxel section 2
+ * "Projection").  The result equals gs_project_bwd, gs_adam_step and gs_project in
+ * sequence, bit for bit.  grads2d is read only.  m, v, lr, step, beta1, beta2, eps: as
+ * gs_grad_aggregate_adam.  Errors as gs_project_bwd, gs_adam_step and gs_project. */
+gs_status gs_project_bwd_adam(const gs_gaussians *g, const gs_camera *cam, const gs_raster_params *p,
+                              const float *grads2d, const gs_param_grads *m, const gs_param_grads *v,
+                              const gs_adam_lrs *lr, int32_t step, float beta1, float beta2, float eps,
+                              const gs_camera *next_cam, gs_projected *next_proj, hipStream_t stream);
 
 /* Message describing the last non-OK status returned on the calling thread. */
 const char *gs_last_error(void);

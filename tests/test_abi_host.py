@@ -39,7 +39,9 @@ def test_struct_layouts_match_header():
     # sizes of the by-value structs the header defines (x86-64 SysV layout)
     assert ctypes.sizeof(B.Camera) == 16 * 4 + 4 * 4 + 2 * 4 + 4
     assert ctypes.sizeof(B.RasterParams) == 24
-    assert ctypes.sizeof(B.Gaussians) == 5 * 8 + 8
+    assert ctypes.sizeof(B.Gaussians) == 5 * 8 + 8 + 8
+    assert B.Gaussians.ld.offset == 48
+    assert ctypes.sizeof(B.ParamGrads) == 5 * 8 + 8
     assert ctypes.sizeof(B.Projected) == 6 * 8
     assert ctypes.sizeof(B.Bins) == 4 * 8 + 8 + 8
     assert ctypes.sizeof(B.AdamGroup) == 4 * 8 + 8 + 8
@@ -192,6 +194,67 @@ def test_fused_l1_argument_errors_before_launch():
     assert e.value.status == B.GS_ERR_INVALID_ARGUMENT
 
 
+def test_owner_update_argument_errors_before_launch():
+    """gs_project_bwd_adam rejects a NULL gradient array, a step below 1, bad Adam
+    hyper-parameters, NULL moments and a next camera without projection buffers before any
+    launch, and returns OK without a launch when there are no Gaussians (the non-NULL
+    addresses below are never dereferenced)."""
+    fake = 256
+    g = B.Gaussians(fake, fake, fake, fake, fake, 10)
+    m = B.ParamGrads(fake, fake, fake, fake, fake)
+    lr = B.AdamLrs(1e-3, 1e-3, 1e-3, 1e-3, 1e-3, 1e-3)
+    p = B.make_params(3)
+    empty = B.Projected(None, None, None, None, None, None)
+
+    def call(gs=g, grads2d=fake, mm=m, step=1, b1=0.9, nc=None, np_=None):
+        return B._lib.gs_project_bwd_adam(ctypes.byref(gs), ctypes.byref(_cam()), ctypes.byref(p), grads2d,
+                                          ctypes.byref(mm) if mm is not None else None, ctypes.byref(m),
+                                          ctypes.byref(lr), step, b1, 0.999, 1e-15,
+                                          ctypes.byref(nc) if nc is not None else None,
+                                          ctypes.byref(np_) if np_ is not None else None, None)
+    assert call(grads2d=None) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(step=0) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(b1=1.0) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(mm=None) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(mm=B.ParamGrads(fake, None, fake, fake, fake)) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(nc=_cam()) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(nc=_cam(), np_=empty) == B.GS_ERR_INVALID_ARGUMENT
+    assert call(gs=B.Gaussians(None, None, None, None, None, 0), grads2d=None) == B.GS_OK
+
+
+def test_plane_stride_from_views_and_checks():
+    """The binding takes the plane stride of [planes][n] views of padded [planes][ld]
+    storage (0 for unpadded planes), rejects groups with different strides, and the library
+    rejects a stride below n before any launch."""
+    import torch
+    store = torch.zeros(59, 128)
+    v = store[:, :100]
+    g = B.gaussians(v[0:3], v[3:6], v[6:10], v[10], v[11:])
+    assert (g.n, g.ld) == (100, 128)
+    pg = B.param_grads(v[0:3], v[3:6], v[6:10], v[10], v[11:])
+    assert pg.ld == 128
+    plain = torch.zeros(59, 100)
+    assert B.gaussians(plain[0:3], plain[3:6], plain[6:10], plain[10], plain[11:]).ld == 0
+    with pytest.raises(ValueError):
+        B.gaussians(v[0:3], plain[3:6], v[6:10], v[10], v[11:])
+    fake = 256
+    bad = B.Gaussians(fake, fake, fake, fake, fake, 10, 8)
+    out = B.Projected(fake, fake, fake, fake, fake, fake)
+    with pytest.raises(B.GsError) as e:
+        B.gs_project(bad, _cam(), B.make_params(3), out, _NullStream())
+    assert e.value.status == B.GS_ERR_INVALID_ARGUMENT and "ld" in B.last_error()
+    good = B.Gaussians(fake, fake, fake, fake, fake, 10, 64)
+    m = B.ParamGrads(fake, fake, fake, fake, fake, 32)   # a moment stride other than the parameters'
+    lr = B.AdamLrs(1e-3, 1e-3, 1e-3, 1e-3, 1e-3, 1e-3)
+    st = B._lib.gs_project_bwd_adam(ctypes.byref(good), ctypes.byref(_cam()), ctypes.byref(B.make_params(3)), fake,
+                                    ctypes.byref(m), ctypes.byref(m), ctypes.byref(lr), 1, 0.9, 0.999, 1e-15, None,
+                                    None, None)
+    assert st == B.GS_ERR_INVALID_ARGUMENT and "stride" in B.last_error()
+    g3 = B.ParamGrads(fake, fake, fake, fake, fake, 5)
+    assert B._lib.gs_project_bwd(ctypes.byref(good), ctypes.byref(_cam()), ctypes.byref(B.make_params(3)), fake,
+                                 ctypes.byref(g3), None) == B.GS_ERR_INVALID_ARGUMENT
+
+
 class _Buf:
     """A host buffer standing in for a device pointer in argument checks (never dereferenced)."""
 
@@ -300,3 +363,6 @@ def test_boundary_departures_from_the_planned_abi_are_the_recorded_ones():
     assert "The gradients are read, not modified." in header
     assert "Every entry of\n * grads2d is written" in header
     assert "each pointer may be NULL,\n * and then that group is not written" in header
+    # B9: the parameter, gradient and moment groups carry a plane stride
+    assert _struct_fields("gs_gaussians").endswith("int64_t n; int64_t ld;")
+    assert _struct_fields("gs_param_grads").endswith("int64_t ld;")

@@ -509,6 +509,95 @@ def test_fused_adam_projection_matches_separate_calls(name):
     assert int((pb[0][1][:, 0] > 0).sum()) > 0
 
 
+def _owner_update_runs(sc, cams, rp, g2s, modes):
+    """Two steps of the owner's update from the given screen-space gradients g2s[step] on the
+    cameras cams[step % 2], each projecting for the other camera afterwards, per mode:
+    "separate" (gs_project_bwd, gs_adam_step, gs_project), "fused_next" (gs_project_bwd_adam
+    with next_cam) or "fused" (without; the projection then by gs_project).  Returns per mode
+    the projections after each step, the parameters and moments, and m after the first step."""
+    out = {}
+    for mode in modes:
+        params = PL.GaussianParams.from_scene(sc, DEV)
+        st = PL.TrainStep(params, cams[0].width, cams[0].height, DEV, raster=rp, plain=True)
+        projs, m_first = [], None
+        for step in range(2):
+            c, nc = B.camera_from(cams[step % 2]), B.camera_from(cams[(step + 1) % 2])
+            g2 = g2s[step].to(DEV)
+            for t in (st.proj.means2d, st.proj.conic_opacity, st.proj.color, st.proj.depth, st.proj.rec):
+                t.fill_(-123.0)
+            st.proj.radii.fill_(-5)
+            if mode == "separate":
+                B.gs_project_bwd(params.gaussians(), c, rp, g2, params.param_grads())
+                st.adam()
+            else:
+                params.step_count += 1
+                m, v = params.moments()
+                nxt = mode == "fused_next"
+                B.gs_project_bwd_adam(params.gaussians(), c, rp, g2, m, v, B.AdamLrs(**st.lr), params.step_count,
+                                      0.9, 0.999, 1e-15, nc if nxt else None, st.proj.abi() if nxt else None)
+            if mode != "fused_next":
+                B.gs_project(params.gaussians(), nc, rp, st.proj.abi())
+            torch.cuda.synchronize()
+            assert torch.equal(g2.cpu(), g2s[step]), "the screen-space gradients are read, not modified"
+            projs.append(_proj_fields(st.proj))
+            if step == 0:
+                m_first = params.m.clone()
+        out[mode] = (projs, params.data.clone(), params.m.clone(), params.v.clone(), m_first, params)
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_sh1", "ragged_sh2", "offscreen_sh3", "100k"])
+def test_owner_update_matches_separate_calls(name):
+    """gs_project_bwd_adam (the owner's projection backward and Adam from decoded
+    screen-space gradients, with or without the next camera's projection) equals
+    gs_project_bwd, gs_adam_step and gs_project bit for bit: every projected field, the
+    parameters and the moments, over two steps on two views.  Its 3D gradient, read back
+    from m after the first step from zero moments (m = (1 - beta1) g), matches the oracle's
+    projection backward of the same screen-space gradients."""
+    log(f"owner update {name}")
+    sc = _scene(name)
+    cams = [sc.cameras[0], _moved_camera(sc.cameras[0])]
+    rp = B.make_params(sc.sh_degree)
+    gen = torch.Generator().manual_seed(len(name))
+    g2s = [(torch.randn(9, sc.n, generator=gen) * 1e-3).contiguous() for _ in range(2)]
+    runs = _owner_update_runs(sc, cams, rp, g2s, ("separate", "fused_next", "fused"))
+    ref = runs["separate"]
+    for mode in ("fused_next", "fused"):
+        got = runs[mode]
+        for sa, sb in zip(ref[0], got[0]):
+            for a, b in zip(sa, sb):
+                assert torch.equal(a, b), mode
+        for a, b in zip(ref[1:5], got[1:5]):
+            assert torch.equal(a, b), mode
+    assert int((ref[0][0][1][:, 0] > 0).sum()) > 0
+    g3 = oracle.project_backward(sc, cams[0], g2s[0].double().numpy(), oracle_params(rp))
+    params = runs["fused_next"][5]
+    g_dev = runs["fused_next"][4].cpu().numpy().astype(np.float64) / (1.0 - np.float32(0.9))
+    for nm in ("means", "log_scales", "quats", "opacity_logits", "sh"):
+        e = rel_l2(params.view(torch.from_numpy(g_dev), nm).numpy(), g3[nm])
+        log(f"  {name} {nm}: owner-update gradient vs oracle rel-L2 {e:.2e}")
+        assert e <= 1e-3
+
+
+def test_owner_update_large_blocks_match_separate_calls():
+    """gs_project_bwd_adam above 2^22 Gaussians (the launch with 128-thread blocks): equal to
+    gs_project_bwd, gs_adam_step and gs_project bit for bit; 2^22 + 4097 Gaussians, SH3."""
+    n = (1 << 22) + 4097
+    log(f"owner update, large blocks, n={n}")
+    sc = scenes.scene_small_random(21, n, 320, 200, 3, extent=1.5, distance=3.0, log_scale_mean=-4.0)
+    cams = [sc.cameras[0], _moved_camera(sc.cameras[0])]
+    rp = B.make_params(sc.sh_degree)
+    gen = torch.Generator().manual_seed(5)
+    g2s = [(torch.randn(9, n, generator=gen) * 1e-3).contiguous() for _ in range(2)]
+    runs = _owner_update_runs(sc, cams, rp, g2s, ("separate", "fused_next"))
+    ref, got = runs["separate"], runs["fused_next"]
+    for sa, sb in zip(ref[0], got[0]):
+        for a, b in zip(sa, sb):
+            assert torch.equal(a, b)
+    for a, b in zip(ref[1:5], got[1:5]):
+        assert torch.equal(a, b)
+
+
 def _views(cam, k):
     """k cameras: cam and copies moved sideways and back by growing amounts."""
     out = [cam]

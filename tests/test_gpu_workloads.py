@@ -418,11 +418,12 @@ def test_partitioned_step_matches_unpartitioned():
 
 def test_partitioned_overlapped_step_matches_serial():
     """PartitionedStep.step_overlapped (each slab's calls on a stream of its own, the binning
-    without host waits, a step's updates running into the next step) gives the serial
-    step's results bit for bit: the composite, the loss, each slab's records, and the
-    parameters and Adam moments after the updates, after step 1 (joined) and step 3 (step
-    2's updates left running into it); 200K Gaussians, 960x540, 4 depth slabs,
-    theta_T = 1e-4."""
+    without host waits, a step's updates running into the next step, each update projecting
+    its slab for the next step) gives the serial step's results bit for bit: the composite,
+    the loss, each slab's records, and the parameters and Adam moments after the updates,
+    after step 1 (joined) and step 3 (step 2's updates left running into it).  Both equal a
+    serial step made of separate calls (gs_project at the start, gs_project_bwd and
+    gs_adam_step at the end); 200K Gaussians, 960x540, 4 depth slabs, theta_T = 1e-4."""
     log("PartitionedStep overlapped vs serial, 200K 960x540, 4 slabs, 3 steps")
     sc = scenes.scene_partitioned_4k(n=200_000, width=960, height=540)
     subs = scenes.slab_scenes(sc)
@@ -431,23 +432,29 @@ def test_partitioned_overlapped_step_matches_serial():
     tgt = sc.targets[0].to(DEV)
     mk = lambda: PL.PartitionedStep([PL.GaussianParams.from_scene(s, DEV) for s in subs], [(0.0, math.inf)] * 4,
                                     W, H, DEV, t_min=1e-4)
-    serial, over = mk(), mk()
+    serial, over, sep = mk(), mk(), mk()
     over.forward(cam)   # sizes each slab's lists (the overlapped binning does not grow them)
     for st in over.parts:
         st.bins._alloc(int(st.bins.capacity * 1.3) + 4096)
     for step in range(3):
-        serial.step(cam, tgt)
-        over.step_overlapped(cam, tgt, join=step != 1)   # step 1's updates run into step 2
+        sep.forward(cam)
+        sep.loss(tgt)
+        sep.backward(cam)
+        for k in range(len(sep.parts)):
+            sep.update_part_separate(k, cam)
+        serial.step(cam, tgt, next_cam=cam, projected=step > 0)
+        over.step_overlapped(cam, tgt, join=step != 1, next_cam=cam, projected=step > 0)   # step 1 runs into 2
         if step == 1:
             continue   # compared after step 2, which is ordered after them
         torch.cuda.synchronize()
         assert over.check_capacity()
-        assert torch.equal(serial.color, over.color) and torch.equal(serial.t_final, over.t_final)
-        assert torch.equal(serial.loss_value, over.loss_value)
-        assert serial.r == over.r
-        for a, b in zip(serial.parts, over.parts):
-            assert torch.equal(a.params.data, b.params.data)
-            assert torch.equal(a.params.m, b.params.m) and torch.equal(a.params.v, b.params.v)
-        for a, b in zip(serial.owner_g2, over.owner_g2):
-            assert torch.equal(a, b)
+        for other in (over, sep):
+            assert torch.equal(serial.color, other.color) and torch.equal(serial.t_final, other.t_final)
+            assert torch.equal(serial.loss_value, other.loss_value)
+            assert serial.r == other.r
+            for a, b in zip(serial.parts, other.parts):
+                assert torch.equal(a.params.data, b.params.data)
+                assert torch.equal(a.params.m, b.params.m) and torch.equal(a.params.v, b.params.v)
+            for a, b in zip(serial.owner_g2, other.owner_g2):
+                assert torch.equal(a, b)
         log(f"  step {step}: equal; records {over.r}")
