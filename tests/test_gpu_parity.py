@@ -598,6 +598,66 @@ def test_owner_update_large_blocks_match_separate_calls():
         assert torch.equal(a, b)
 
 
+class _PlainParams(PL.GaussianParams):
+    """The parameter store with plane stride n (no padding)."""
+    LD_ALIGN = 1
+
+
+@pytest.mark.parametrize("name", ["ragged_sh1", "ragged_sh2", "offscreen_sh3"])
+def test_padded_plane_stride_equals_unpadded(name):
+    """The padded parameter store (plane stride n rounded up to 64) and the plain one
+    (stride n) give the same results bit for bit through every entry point that reads or
+    writes parameter, gradient or moment planes: the one-view step with the fused end of step
+    and the next projection, the projection backward into 3D gradients, the owner update
+    and the batch step; ragged n, two steps."""
+    log(f"padded vs plain plane stride {name}")
+    sc = _scene(name)
+    assert sc.n % 64 != 0
+    cams = [sc.cameras[0], _moved_camera(sc.cameras[0])]
+    bc = [B.camera_from(c) for c in cams]
+    rp = B.make_params(sc.sh_degree)
+    tgt = sc.targets[0].to(DEV)
+    gen = torch.Generator().manual_seed(3)
+    g2 = (torch.randn(9, sc.n, generator=gen) * 1e-3).contiguous().to(DEV)
+    out = {}
+    for cls in (PL.GaussianParams, _PlainParams):
+        params = cls.from_scene(sc, DEV)
+        assert params.ld == (sc.n if cls is _PlainParams else -(-sc.n // 64) * 64)
+        st = PL.TrainStep(params, cams[0].width, cams[0].height, DEV, raster=rp, plain=True)
+        st.forward(bc[0])
+        res = []
+        for step in range(2):
+            if step:
+                st.forward_projected(bc[step % 2])
+            st.loss(tgt)
+            st.backward_partials(bc[step % 2])
+            st.aggregate_adam_project(bc[step % 2], bc[(step + 1) % 2])
+            torch.cuda.synchronize()
+            res += _proj_fields(st.proj)
+        B.gs_project_bwd(params.gaussians(), bc[0], rp, g2, params.param_grads())
+        params.step_count += 1
+        m, v = params.moments()
+        B.gs_project_bwd_adam(params.gaussians(), bc[1], rp, g2, m, v, B.AdamLrs(**st.lr), params.step_count, 0.9,
+                              0.999, 1e-15, bc[0], st.proj.abi())
+        torch.cuda.synchronize()
+        res += [params.grad.clone()] + _proj_fields(st.proj)
+        bt = PL.BatchTrainStep(params, cams[0].width, cams[0].height, 2, DEV, raster=rp)
+        bt.project(bc)
+        for k in range(2):
+            bt.sort(k, bc[k])
+            bt.render(k, bc[k], tgt)
+        bt.update(bc, next_cams=bc)
+        torch.cuda.synchronize()
+        res += [params.data.clone(), params.m.clone(), params.v.clone()] + _proj_fields(bt.proj[1])
+        pad = [params.store[k][:, params.n:] for k in ("data", "grad", "m", "v")]
+        assert all(int((t != 0).sum()) == 0 for t in pad), "the padding stays zero"
+        out[cls] = res
+    a, b = out[PL.GaussianParams], out[_PlainParams]
+    assert len(a) == len(b)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 def _views(cam, k):
     """k cameras: cam and copies moved sideways and back by growing amounts."""
     out = [cam]
