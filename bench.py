@@ -953,6 +953,16 @@ def main():
     tile_budget = {"B": budget, "lds_budget_bytes": lds_budget, "fixed_bytes": fixed_bytes, "bytes_per_gaussian": rec_bytes,
                    "tiles": st.bins.tiles, "tiles_over_budget": tiles_over,
                    "frac_tiles_within": round(1.0 - tiles_over / st.bins.tiles, 4), "sum_excess": excess}
+    # the realized skew of the last step's tile lists: longest over mean list, and the share of
+    # the entries in the longest 1 % of tiles; for the clustered 10M scene also the share of
+    # the means inside the dense central sub-cube (10 % of the 20 m cube's volume)
+    lens = (st.bins.tile_ranges[1:] - st.bins.tile_ranges[:-1]).to(torch.float64)
+    top = max(1, lens.numel() // 100)
+    skew = {"tile_list_max_over_mean": round(float(lens.max()) / max(float(lens.mean()), 1e-30), 2),
+            "top1pct_tiles_share_of_entries": round(float(lens.topk(top).values.sum()) / max(float(lens.sum()), 1.0), 4)}
+    if args.workload == "10m":
+        sub_half = 10.0 * 0.1 ** (1.0 / 3.0)
+        skew["means_in_dense_subcube"] = round(float((scene.means.abs() <= sub_half).all(dim=0).double().mean()), 4)
     ms_step = wall * 1e3 / args.steps
     isect_step = isect_total / args.steps
     n = scene.n
@@ -1007,6 +1017,7 @@ def main():
         "quadrant_records_last_step": q_last,
         "visible_gaussians": n_vis,
         "tile_budget": tile_budget,
+        "skew": skew,
         # Gaussian-pixel intersections over the two raster kernels' time (forward compositing
         # and the per-pixel backward with its per-quadrant sums)
         "raster_isect_per_s": round(isect_step / ((per_kernel["raster_fwd"] + per_kernel["raster_bwd"]) * 1e-3), 1)
