@@ -268,8 +268,9 @@ __global__ __launch_bounds__(256) void k_emit(const uint64_t *__restrict__ svals
 constexpr int kWaveWords = 4;
 
 // Finishes the sorted lists in one pass over the entries: the Gaussian index of each
-// entry, tile_ranges[t] = first entry of tile t (entries are sorted by tile; ranges[T] =
-// K), and the quadrant bitmaps with their per-word bit counts (one 64-bit word per 64
+// entry (only with tvals != NULL; the tile sort's last pass writes them otherwise),
+// tile_ranges[t] = first entry of tile t (entries are sorted by tile; ranges[T] = K), and
+// the quadrant bitmaps with their per-word bit counts (one 64-bit word per 64
 // entries and quadrant).  Every word of the bitmaps and of `wcnt` [4][words + 1] is written
 // (zero past the entries); the exclusive scan of wcnt gives the positions of the quadrant
 // records.  The launch covers max(words, ceil((T + 1) / 64)) words; K is read on the device.
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
         const int64_t kc = k < K ? k : K - 1, kp = kc > 0 ? kc - 1 : 0;   // clamped: loads stay in range
         key[i] = K > 0 ? tkeys[kc] : 0u;
         prev[i] = K > 0 ? tkeys[kp] : 0u;
-        tv[i] = K > 0 ? tvals[kc] : 0ull;
+        tv[i] = K > 0 && tvals ? tvals[kc] : 0ull;
     }
 #pragma unroll
     for (int i = 0; i < kWaveWords; ++i) {
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(256) void k_finish(const uint32_t *__restrict__ tke
         if (k < K) {
             const int32_t t = (int32_t)(key[i] & gsr::kTileMask);
             qm = key[i] >> gsr::kMaskShift;
-            ids[k] = (uint32_t)tv[i];
+            if (tvals) ids[k] = (uint32_t)tv[i];
             const int32_t pt = k > 0 ? (int32_t)(prev[i] & gsr::kTileMask) : -1;
             for (int32_t u = pt + 1; u <= t; ++u) ranges[u] = (int32_t)k;
             if (k == K - 1)
@@ -656,8 +657,11 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
         GS_LAUNCH_CHECK("k_wave_identity");
         return GS_OK;
     }
-    if ((s = radix_sort_u32_u64(tkA, tvA, tkB, tvB, cap, tbits, hist, stT, tickets + kTkTile, &in_b, stream, klen)) !=
-        GS_OK)
+    // the last pass also writes the Gaussian of each sorted entry to ids (no pass runs for a
+    // capacity of 1; k_finish writes them then)
+    const bool ids_in_sort = cap > 1;
+    if ((s = radix_sort_u32_u64(tkA, tvA, tkB, tvB, cap, tbits, hist, stT, tickets + kTkTile, &in_b, stream, klen,
+                                nullptr, ids_in_sort ? bins->ids : nullptr)) != GS_OK)
         return s;
     const uint32_t *tk = in_b ? tkB : tkA;
     const uint64_t *tv = in_b ? tvB : tvA;
@@ -669,7 +673,8 @@ gs_status bin_sort_launch(const gs_projected *proj, int64_t n, const gs_camera *
     uint32_t *wpre = reinterpret_cast<uint32_t *>(rb + RL.wpre);
     const int64_t nw = gsr::kQuads * (RL.words + 1);
     const int64_t fwords = std::max<int64_t>(RL.words, ceil_div((int64_t)T + 1, 64));
-    k_finish<<<(unsigned)ceil_div(fwords, 4 * kWaveWords), 256, 0, stream>>>(tk, tv, klen, T, bins->ids,
+    k_finish<<<(unsigned)ceil_div(fwords, 4 * kWaveWords), 256, 0, stream>>>(tk, ids_in_sort ? nullptr : tv, klen, T,
+                                                                            bins->ids,
                                                                             bins->tile_ranges, RL.words, bm, wpre);
     GS_LAUNCH_CHECK("k_finish");
     if ((s = lb_scan_u32(wpre, wpre, nw, scW, tickets + kTkWpre, nullptr, stream)) != GS_OK) return s;

@@ -48,11 +48,13 @@ gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb,
 // on the device; when they lie within about 2^24 of each other (the exact test is in
 // sort.hip), it takes three passes instead of four and the result ends in (kb, vb): then
 // xf[1] != 0 after the sort (read it on the device; *in_b reports the four-pass case).
+// low_out (device, may be NULL; not with xf): the last pass also writes the low 32 bits of
+// each sorted value there; nothing is written when m <= 1 (no pass runs).
 constexpr int kRadixXfWords = 32 * 33;
 gs_status radix_sort_u32_u64(uint32_t *ka, uint64_t *va, uint32_t *kb, uint64_t *vb, int64_t m, int bits,
                              uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
                              hipStream_t stream, const unsigned long long *m_dev = nullptr,
-                             uint32_t *xf = nullptr);
+                             uint32_t *xf = nullptr, uint32_t *low_out = nullptr);
 
 // Fills n int32 values with `value` (a kernel, not a memset, so it may be captured in graphs).
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream);

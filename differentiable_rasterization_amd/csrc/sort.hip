@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
                                                             uint32_t *__restrict__ kout, V *__restrict__ vout,
                                                             int64_t m_max, const unsigned long long *__restrict__ m_dev,
                                                             int shift, const uint32_t *__restrict__ offs, int64_t nb,
-                                                            uint32_t *__restrict__ xf)
+                                                            uint32_t *__restrict__ xf, uint32_t *__restrict__ low_out)
 {
     if (xf_skip<MODE>(xf)) return;   // the whole grid
     uint32_t xo = 0u;
@@ -337,6 +337,7 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(const uint32_t *__re
         if (dst < (uint64_t)m) {   // always true for a consistent ranking; keeps a bug from writing out of bounds
             kout[dst] = k;
             vout[dst] = sval[i];
+            if (low_out) low_out[dst] = (uint32_t)sval[i];
         }
     }
 }
@@ -578,9 +579,10 @@ int64_t radix_scan_status_len(int64_t m, int bits)
 template <typename V>
 gs_status radix_sort_kv(uint32_t *ka, V *va, uint32_t *kb, V *vb, int64_t m, int bits, uint32_t *hist,
                         unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b, hipStream_t stream,
-                        const unsigned long long *m_dev, uint32_t *xf)
+                        const unsigned long long *m_dev, uint32_t *xf, uint32_t *low_out)
 {
     if (xf && bits != 32) return fail(GS_ERR_INVALID_ARGUMENT, "key range reduction needs a 32-bit sort");
+    if (xf && low_out) return fail(GS_ERR_INVALID_ARGUMENT, "low_out with key range reduction");
     *in_b = false;
     if (m <= 1 || bits <= 0) return GS_OK;
     const int64_t nb = ceil_div(m, kRxTile);
@@ -590,6 +592,7 @@ gs_status radix_sort_kv(uint32_t *ka, V *va, uint32_t *kb, V *vb, int64_t m, int
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
         const int mode = !xf ? 0 : p == 0 ? 1 : p == 3 ? 2 : 0;
+        uint32_t *lo = p == passes - 1 ? low_out : nullptr;
         if (mode == 1)
             k_radix_hist<1><<<(unsigned)nb, kThreads, 0, stream>>>(sk, m, m_dev, shift, hist, nb, xf);
         else if (mode == 2)
@@ -602,11 +605,14 @@ gs_status radix_sort_kv(uint32_t *ka, V *va, uint32_t *kb, V *vb, int64_t m, int
                                             mode == 2 ? xf + 1 : nullptr);
         if (s != GS_OK) return s;
         if (mode == 1)
-            k_radix_scatter<V, 1><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf);
+            k_radix_scatter<V, 1><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf,
+                                                                         lo);
         else if (mode == 2)
-            k_radix_scatter<V, 2><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf);
+            k_radix_scatter<V, 2><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf,
+                                                                         lo);
         else
-            k_radix_scatter<V, 0><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf);
+            k_radix_scatter<V, 0><<<(unsigned)nb, kThreads, 0, stream>>>(sk, sv, dk, dv, m, m_dev, shift, hist, nb, xf,
+                                                                         lo);
         GS_LAUNCH_CHECK("k_radix_scatter");
         std::swap(sk, dk);
         std::swap(sv, dv);
@@ -619,14 +625,15 @@ gs_status radix_sort_u32(uint32_t *ka, uint32_t *va, uint32_t *kb, uint32_t *vb,
                          uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
                          hipStream_t stream, const unsigned long long *m_dev)
 {
-    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev, nullptr);
+    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev, nullptr,
+                         nullptr);
 }
 
 gs_status radix_sort_u32_u64(uint32_t *ka, uint64_t *va, uint32_t *kb, uint64_t *vb, int64_t m, int bits,
                              uint32_t *hist, unsigned long long *scan_status, uint32_t *scan_tickets, bool *in_b,
-                             hipStream_t stream, const unsigned long long *m_dev, uint32_t *xf)
+                             hipStream_t stream, const unsigned long long *m_dev, uint32_t *xf, uint32_t *low_out)
 {
-    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev, xf);
+    return radix_sort_kv(ka, va, kb, vb, m, bits, hist, scan_status, scan_tickets, in_b, stream, m_dev, xf, low_out);
 }
 
 gs_status fill_i32(int32_t *p, int64_t n, int32_t value, hipStream_t stream)
