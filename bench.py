@@ -758,7 +758,7 @@ def main_batch(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
     if args.workload == "20m":

@@ -87,8 +87,8 @@ def rel_l2(a, b):
 
 
 # Where one comparison's statistics are appended (one JSON object per line), so that a GPU
-# run reports the tie and mismatch counts of every image it compared.
-TIE_LOG = os.environ.get("GS_TIE_LOG", os.path.join(ROOT, "gpurun_out", "image_compare_stats.jsonl"))
+# run reports the tie and mismatch counts of every image it compared (GS_TIE_LOG overrides).
+TIE_LOG = os.environ.get("GS_TIE_LOG", os.path.join(ROOT, "tests", "logs", "image_compare_stats.jsonl"))
 
 
 def _record(stats):
