@@ -207,8 +207,8 @@ __device__ __host__ __forceinline__ unsigned long long need_capacity(unsigned lo
 }
 
 // Entries of the Gaussians in depth order (block b: depth ranks 256 b ..; svals, or
-// svals_b when *sel != 0: tile count << 32 | Gaussian), tiles row-major; off: exclusive scan of the tile counts in depth
-// order.  Entry p gets the key
+// svals_b when *sel != 0: tile count << 32 | Gaussian), tiles row-major; off: exclusive
+// scan of the tile counts in depth order.  Entry p gets the key
 // tile | quadrant mask << 24 (the mask rides in bits the tile sort never looks at) and the
 // value (gradient slot of its first quadrant record) << 32 | its Gaussian, carried through
 // the tile sort.  Gaussian g's quadrant records own slots qoff[g] .. qoff[g + 1], in the

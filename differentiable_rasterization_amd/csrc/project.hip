@@ -425,8 +425,8 @@ __device__ __forceinline__ void project_store_s(const Params1<(DEG + 1) * (DEG +
 template <int DEG>
 __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means, const float *__restrict__ log_scales,
                                                  const float *__restrict__ quats, const float *__restrict__ logits,
-                                                 const float *__restrict__ sh, int64_t n, int64_t ldp, CamD cam, float alpha_min,
-                                                 float depth_lo, float depth_hi, ProjOut po)
+                                                 const float *__restrict__ sh, int64_t n, int64_t ldp, CamD cam,
+                                                 float alpha_min, float depth_lo, float depth_hi, ProjOut po)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -826,10 +826,10 @@ __device__ __forceinline__ void project_bwd_grads(const Proj &P, const CamD &cam
 template <int DEG, bool RAW, bool NEXT, class Sink>
 __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means, const float *__restrict__ log_scales,
                                                 const float *__restrict__ quats, const float *__restrict__ logits,
-                                                const float *__restrict__ sh, int64_t n, int64_t ldp, int64_t i, const CamD &cam,
-                                                float alpha_min, float depth_lo, float depth_hi, const float (&in)[9],
-                                                float *__restrict__ grads2d, const Sink &out, const CamD &next_cam,
-                                                const ProjOut &next)
+                                                const float *__restrict__ sh, int64_t n, int64_t ldp, int64_t i,
+                                                const CamD &cam, float alpha_min, float depth_lo, float depth_hi,
+                                                const float (&in)[9], float *__restrict__ grads2d, const Sink &out,
+                                                const CamD &next_cam, const ProjOut &next)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     Params1<K> prm;
@@ -872,10 +872,10 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
 template <int DEG, bool NEXT, bool RAW = true>
 __device__ __forceinline__ void grad_adam_one(const float *__restrict__ means, const float *__restrict__ log_scales,
                                               const float *__restrict__ quats, const float *__restrict__ logits,
-                                              const float *__restrict__ sh, int64_t n, int64_t ldp, int64_t i, const CamD &cam,
-                                              float alpha_min, float depth_lo, float depth_hi, const float (&in)[9],
-                                              float *__restrict__ grads2d, const AdamSink &out, const CamD &next_cam,
-                                              const ProjOut &next, float (*shs)[64])
+                                              const float *__restrict__ sh, int64_t n, int64_t ldp, int64_t i,
+                                              const CamD &cam, float alpha_min, float depth_lo, float depth_hi,
+                                              const float (&in)[9], float *__restrict__ grads2d, const AdamSink &out,
+                                              const CamD &next_cam, const ProjOut &next, float (*shs)[64])
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int lane = threadIdx.x & 63;
@@ -983,8 +983,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     float g[9];
 #pragma unroll
     for (int f = 0; f < 9; ++f) g[f] = __builtin_nontemporal_load(g2 + (int64_t)f * n + i);
-    grad_adam_one<DEG, NEXT, false>(means, log_scales, quats, logits, sh, n, ldp, i, cam, alpha_min, depth_lo, depth_hi, g,
-                                    nullptr, out, next_cam, next, shs);
+    grad_adam_one<DEG, NEXT, false>(means, log_scales, quats, logits, sh, n, ldp, i, cam, alpha_min, depth_lo,
+                                    depth_hi, g, nullptr, out, next_cam, next, shs);
 }
 
 // -------------------------------------------------------------------- batches of views
@@ -1156,7 +1156,8 @@ gs_status launch_project_bwd(const gs_gaussians *g, const gs_camera *cam, const 
     const GradSink sink{out->means, out->log_scales, out->quats, out->opacity_logits, out->sh, grads_ld(out, n)};
 #define GS_PB(D)                                                                                              \
     k_project_bwd<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, \
-                                                 n, param_ld(g), cd, p->alpha_min, p->depth_lo, p->depth_hi, grads2d, sink)
+                                                 n, param_ld(g), cd, p->alpha_min, p->depth_lo, p->depth_hi,   \
+                                                 grads2d, sink)
     switch (p->sh_degree) {
     case 0: GS_PB(0); break;
     case 1: GS_PB(1); break;
@@ -1185,8 +1186,8 @@ extern "C" gs_status gs_project(const gs_gaussians *g, const gs_camera *cam, con
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
     const ProjOut po = proj_out(out, n);
 #define GS_PF(D)                                                                                        \
-    k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, param_ld(g), \
-                                             cd, p->alpha_min, p->depth_lo, p->depth_hi, po)
+    k_project<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
+                                             param_ld(g), cd, p->alpha_min, p->depth_lo, p->depth_hi, po)
     switch (p->sh_degree) {
     case 0: GS_PF(0); break;
     case 1: GS_PF(1); break;
@@ -1310,14 +1311,14 @@ gs_status grad_adam_launch(const gs_gaussians *g, const gs_projected *proj, cons
         const size_t lds = (size_t)(bt / 64) * grad_adam_wave_lds(D);                                              \
         if (next_cam)                                                                                              \
             k_grad_adam<D, true><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,                  \
-                                                               g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min,      \
-                                                               p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,        \
-                                                               grads2d, sink, nd, po);                             \
+                                                               g->opacity_logits, g->sh, n, param_ld(g), cd,       \
+                                                               p->alpha_min, p->depth_lo, p->depth_hi, hdr, qoff,  \
+                                                               qg, qs, grads2d, sink, nd, po);                     \
         else                                                                                                       \
             k_grad_adam<D, false><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,                 \
-                                                                g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min,     \
-                                                                p->depth_lo, p->depth_hi, hdr, qoff, qg, qs,       \
-                                                                grads2d, sink, nd, po);                            \
+                                                                g->opacity_logits, g->sh, n, param_ld(g), cd,      \
+                                                                p->alpha_min, p->depth_lo, p->depth_hi, hdr, qoff, \
+                                                                qg, qs, grads2d, sink, nd, po);                    \
     } while (0)
     switch (p->sh_degree) {
     case 0: GS_GA(0); break;
@@ -1384,13 +1385,14 @@ extern "C" gs_status gs_project_bwd_adam(const gs_gaussians *g, const gs_camera 
         const size_t lds = (size_t)(bt / 64) * proj_bwd_adam_wave_lds(D);                                          \
         if (next_cam)                                                                                              \
             k_proj_bwd_adam<D, true><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,              \
-                                                                   g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min,  \
-                                                                   p->depth_lo, p->depth_hi, grads2d, sink, nd, po); \
+                                                                   g->opacity_logits, g->sh, n, param_ld(g), cd,   \
+                                                                   p->alpha_min, p->depth_lo, p->depth_hi, grads2d, \
+                                                                   sink, nd, po);                                  \
         else                                                                                                       \
             k_proj_bwd_adam<D, false><<<grid, block, lds, stream>>>(g->means, g->log_scales, g->quats,             \
-                                                                    g->opacity_logits, g->sh, n, param_ld(g), cd, p->alpha_min, \
-                                                                    p->depth_lo, p->depth_hi, grads2d, sink, nd,   \
-                                                                    po);                                           \
+                                                                    g->opacity_logits, g->sh, n, param_ld(g), cd,  \
+                                                                    p->alpha_min, p->depth_lo, p->depth_hi,        \
+                                                                    grads2d, sink, nd, po);                        \
     } while (0)
     switch (p->sh_degree) {
     case 0: GS_PBA(0); break;
@@ -1424,8 +1426,8 @@ extern "C" gs_status gs_project_batch(const gs_gaussians *g, int32_t views, cons
     if (n == 0) return GS_OK;
     const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
 #define GS_PB(D)                                                                                                    \
-    k_project_batch<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, param_ld(g), \
-                                                   p->alpha_min, p->depth_lo, p->depth_hi, bp)
+    k_project_batch<D><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats, g->opacity_logits, g->sh, n, \
+                                                   param_ld(g), p->alpha_min, p->depth_lo, p->depth_hi, bp)
     switch (p->sh_degree) {
     case 0: GS_PB(0); break;
     case 1: GS_PB(1); break;
@@ -1482,12 +1484,14 @@ extern "C" gs_status gs_grad_aggregate_adam_batch(const gs_gaussians *g, int32_t
     do {                                                                                                             \
         if (next_cams)                                                                                               \
             k_grad_adam_batch<D, true><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,                \
-                                                                   g->opacity_logits, g->sh, n, param_ld(g), p->alpha_min,        \
-                                                                   p->depth_lo, p->depth_hi, bg, sink, next);        \
+                                                                   g->opacity_logits, g->sh, n, param_ld(g),         \
+                                                                   p->alpha_min, p->depth_lo, p->depth_hi, bg, sink, \
+                                                                   next);                                            \
         else                                                                                                         \
             k_grad_adam_batch<D, false><<<grid, block, 0, stream>>>(g->means, g->log_scales, g->quats,               \
-                                                                    g->opacity_logits, g->sh, n, param_ld(g), p->alpha_min,       \
-                                                                    p->depth_lo, p->depth_hi, bg, sink, next);       \
+                                                                    g->opacity_logits, g->sh, n, param_ld(g),        \
+                                                                    p->alpha_min, p->depth_lo, p->depth_hi, bg,      \
+                                                                    sink, next);                                     \
     } while (0)
     switch (p->sh_degree) {
     case 0: GS_GB(0); break;
