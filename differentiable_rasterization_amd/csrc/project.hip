@@ -382,14 +382,10 @@ __device__ __forceinline__ void record_visible(const RecFields &F, float r, floa
 // the plain fields (where requested) are stored on the way.  A culled Gaussian's record is
 // zero apart from its index (its radii are (0, 0)).
 template <int DEG>
-__device__ __forceinline__ void project_record(const Params1<(DEG + 1) * (DEG + 1)> &prm, const ProjScalars &S,
-                                               const CamD &cam, float depth_lo, float depth_hi, int64_t i,
-                                               const ProjOut &po, float4 (&rec)[3])
+__device__ __forceinline__ void record_from(const Params1<(DEG + 1) * (DEG + 1)> &prm, const Proj &P, int64_t i,
+                                            const ProjOut &po, float4 (&rec)[3])
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    Proj P;
-    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
-    project_view(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.q[0], prm.q[1], prm.q[2], prm.q[3], S, depth_lo, depth_hi, P);
     po.depth[i] = P.key;
     po.radii[i] = make_int2(P.rx, P.ry);
     rec[0] = rec[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -405,6 +401,17 @@ __device__ __forceinline__ void project_record(const Params1<(DEG + 1) * (DEG + 
         b = fmaf(prm.sh[3 * k + 2], Y[k], b);
     }
     record_visible(rec_fields(P), r, g, b, i, po, rec);
+}
+
+template <int DEG>
+__device__ __forceinline__ void project_record(const Params1<(DEG + 1) * (DEG + 1)> &prm, const ProjScalars &S,
+                                               const CamD &cam, float depth_lo, float depth_hi, int64_t i,
+                                               const ProjOut &po, float4 (&rec)[3])
+{
+    Proj P;
+    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
+    project_view(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.q[0], prm.q[1], prm.q[2], prm.q[3], S, depth_lo, depth_hi, P);
+    record_from<DEG>(prm, P, i, po, rec);
 }
 
 // project_store with the Gaussian's camera-independent values already computed.  The record
@@ -431,9 +438,33 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
     constexpr int K = (DEG + 1) * (DEG + 1);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
+    // The geometry decides visibility first (with the SH taken as finite); only the visible
+    // lanes load their SH coefficients, and non-finite ones cull the Gaussian then, which
+    // gives what project_store gives (a culled Gaussian's depth key does not depend on them).
     Params1<K> prm;
-    load_params<false>(means, log_scales, quats, logits, sh, ldp, i, prm);
-    project_store<DEG>(prm, cam, alpha_min, depth_lo, depth_hi, i, po);
+    prm.means[0] = means[i]; prm.means[1] = means[ldp + i]; prm.means[2] = means[2 * ldp + i];
+    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[ldp + i]; prm.ls[2] = log_scales[2 * ldp + i];
+    prm.q[0] = quats[i]; prm.q[1] = quats[ldp + i]; prm.q[2] = quats[2 * ldp + i]; prm.q[3] = quats[3 * ldp + i];
+    prm.logit = logits[i];
+    ProjScalars S;
+    project_scalars(prm.means[0], prm.means[1], prm.means[2], prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1],
+                    prm.q[2], prm.q[3], prm.logit, true, (double)alpha_min, S);
+    Proj P;
+    const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
+    project_view(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.q[0], prm.q[1], prm.q[2], prm.q[3], S, depth_lo, depth_hi, P);
+    if (P.vis) {
+#pragma unroll
+        for (int k = 0; k < 3 * K; ++k) prm.sh[k] = sh[(int64_t)k * ldp + i];
+        if (!sh_finite(prm)) {
+            P.vis = false;
+            P.rx = P.ry = 0;
+        }
+    }
+    float4 rec[3];
+    record_from<DEG>(prm, P, i, po, rec);
+    po.rec[3 * i + 0] = rec[0];
+    po.rec[3 * i + 1] = rec[1];
+    po.rec[3 * i + 2] = rec[2];
 }
 
 // Backward through projection and colour evaluation (ByteSplat, section 2.1: the
