@@ -297,6 +297,26 @@ __device__ __forceinline__ void load_params(const float *__restrict__ means, con
     for (int k = 0; k < 3 * K; ++k) prm.sh[k] = ld_sh(sh + (int64_t)k * n + i);
 }
 
+// The 11 scalars other than the SH coefficients (n: the plane stride), and the coefficients
+// on their own, for kernels that load the latter only for visible Gaussians.
+template <int K>
+__device__ __forceinline__ void load_geometry(const float *__restrict__ means, const float *__restrict__ log_scales,
+                                              const float *__restrict__ quats, const float *__restrict__ logits,
+                                              int64_t n, int64_t i, Params1<K> &prm)
+{
+    prm.means[0] = means[i]; prm.means[1] = means[n + i]; prm.means[2] = means[2 * n + i];
+    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[n + i]; prm.ls[2] = log_scales[2 * n + i];
+    prm.q[0] = quats[i]; prm.q[1] = quats[n + i]; prm.q[2] = quats[2 * n + i]; prm.q[3] = quats[3 * n + i];
+    prm.logit = logits[i];
+}
+
+template <int K>
+__device__ __forceinline__ void load_sh(const float *__restrict__ sh, int64_t n, int64_t i, Params1<K> &prm)
+{
+#pragma unroll
+    for (int k = 0; k < 3 * K; ++k) prm.sh[k] = sh[(int64_t)k * n + i];
+}
+
 template <int K>
 __device__ __forceinline__ bool sh_finite(const Params1<K> &prm)
 {
@@ -442,10 +462,7 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
     // lanes load their SH coefficients, and non-finite ones cull the Gaussian then, which
     // gives what project_store gives (a culled Gaussian's depth key does not depend on them).
     Params1<K> prm;
-    prm.means[0] = means[i]; prm.means[1] = means[ldp + i]; prm.means[2] = means[2 * ldp + i];
-    prm.ls[0] = log_scales[i]; prm.ls[1] = log_scales[ldp + i]; prm.ls[2] = log_scales[2 * ldp + i];
-    prm.q[0] = quats[i]; prm.q[1] = quats[ldp + i]; prm.q[2] = quats[2 * ldp + i]; prm.q[3] = quats[3 * ldp + i];
-    prm.logit = logits[i];
+    load_geometry(means, log_scales, quats, logits, ldp, i, prm);
     ProjScalars S;
     project_scalars(prm.means[0], prm.means[1], prm.means[2], prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1],
                     prm.q[2], prm.q[3], prm.logit, true, (double)alpha_min, S);
@@ -453,8 +470,7 @@ __global__ __launch_bounds__(256) void k_project(const float *__restrict__ means
     const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
     project_view(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.q[0], prm.q[1], prm.q[2], prm.q[3], S, depth_lo, depth_hi, P);
     if (P.vis) {
-#pragma unroll
-        for (int k = 0; k < 3 * K; ++k) prm.sh[k] = sh[(int64_t)k * ldp + i];
+        load_sh(sh, ldp, i, prm);
         if (!sh_finite(prm)) {
             P.vis = false;
             P.rx = P.ry = 0;
@@ -863,13 +879,26 @@ __device__ __forceinline__ void project_bwd_one(const float *__restrict__ means,
                                                 const CamD &next_cam, const ProjOut &next)
 {
     constexpr int K = (DEG + 1) * (DEG + 1);
+    // A gradient sink needs no SH coefficients of a culled Gaussian (its gradients are zero):
+    // they are loaded after the geometry has decided visibility, and non-finite ones cull
+    // then, which gives the same result as checking them first.
+    constexpr bool kLazySH = std::is_same<Sink, GradSink>::value && !NEXT;
     Params1<K> prm;
-    load_params<std::is_same<Sink, AdamSink>::value>(means, log_scales, quats, logits, sh, ldp, i, prm);
-    const bool shf = sh_finite(prm);
+    if constexpr (kLazySH)
+        load_geometry(means, log_scales, quats, logits, ldp, i, prm);
+    else
+        load_params<std::is_same<Sink, AdamSink>::value>(means, log_scales, quats, logits, sh, ldp, i, prm);
+    const bool shf = kLazySH ? true : sh_finite(prm);
     Proj P;
     const float fmx = prm.means[0], fmy = prm.means[1], fmz = prm.means[2];
     project_core(cam, fmx, fmy, fmz, fmx, fmy, fmz, prm.ls[0], prm.ls[1], prm.ls[2], prm.q[0], prm.q[1], prm.q[2],
                  prm.q[3], prm.logit, shf, (double)alpha_min, depth_lo, depth_hi, P);
+    if constexpr (kLazySH) {
+        if (P.vis) {
+            load_sh(sh, ldp, i, prm);
+            if (!sh_finite(prm)) P.vis = false;
+        }
+    }
     // culled Gaussians get zero gradients; every lane reaches the one flush at the end, so
     // a wave issues the sink's memory traffic once
     Grad3<K> G;
