@@ -48,7 +48,10 @@ step; roofline_next the other.  roofline.traffic is the HBM traffic of one launc
 from the stored counter summary (profiles/), or null if the kernel's sources changed
 since those counters were taken.  --copy-calibration-mib runs a plain copy-like kernel of
 known size before the timed steps, for the counter runs that normalise FETCH_SIZE and
-WRITE_SIZE.
+WRITE_SIZE.  skew: the last step's longest tile list over the mean and the share of the
+entries in the longest 1 % of tiles (and at 10M the share of the means inside the dense
+central sub-cube of the clustered recipe).  The timed loops run with Python's cyclic
+garbage collector off (quiet_gc).
 """
 from __future__ import annotations
 
