@@ -21,8 +21,8 @@
 //                                 own slots qoff[g] .. qoff[g + 1], in the order of its
 //                                 entries and, within an entry, of the quadrants (qoff[n] =
 //                                 the number of quadrant records)
-//   qgrad  [2 * capacity][12] f32 the backward's per-record partial gradients (9 fields,
-//                                 padded to 48 bytes), one slot per quadrant record, at the
+//   qgrad  [2 * capacity][9] f32  the backward's per-record partial gradients (9 fields,
+//                                 36 bytes, packed), one slot per quadrant record, at the
 //                                 slot index its record carries
 //   grec   [n][4] float4          (last, at hdr.grec_off) the projected raster record of every
 //                                 Gaussian (its three float4 words, then a fourth, unused),
@@ -62,7 +62,7 @@ constexpr int kRecF4 = 3;   // float4 words per record
 // gather of a record's first 36 bytes touches one 64-byte line (at a 48-byte stride half of
 // them straddled two).
 constexpr int kGRecF4 = 4;
-constexpr int kGradSlot = 12;   // floats per per-record gradient slot (9 used)
+constexpr int kGradSlot = 9;    // floats per per-record gradient slot (the 9 moment sums, packed)
 constexpr int kStampWords = 1;  // uint32 words per slot stamp
 // Quadrant records are stored for up to kQuadFactor * capacity (entry, quadrant) pairs
 // (an entry reaches 1.4 - 2 quadrants on average); more is reported as a capacity error.
@@ -213,10 +213,10 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
         const uint32_t sl = w0 + (uint32_t)lane;
         w = sl < w1 && tn == epoch;   // unwritten slots are not read
         if (w) {
-            const float4 *p = qgrad + (size_t)sl * (kGradSlot / 4);
-            d0 = p[0];
-            d1 = p[1];
-            d2 = p[2];
+            const float *p = reinterpret_cast<const float *>(qgrad) + (size_t)sl * kGradSlot;
+            d0 = make_float4(p[0], p[1], p[2], p[3]);
+            d1 = make_float4(p[4], p[5], p[6], p[7]);
+            d2 = make_float4(p[8], 0.0f, 0.0f, 0.0f);
         }
         if (sl + 64u < w1) tn = qstamp[sl + 64u];
     }
@@ -230,10 +230,10 @@ __device__ __forceinline__ bool raw_slot_sums(const BinsHeader *__restrict__ hdr
         const uint32_t sn = c0 + 64u + (uint32_t)lane;
         w = sn < w1 && tn == epoch;
         if (w) {
-            const float4 *p = qgrad + (size_t)sn * (kGradSlot / 4);
-            d0 = p[0];
-            d1 = p[1];
-            d2 = p[2];
+            const float *p = reinterpret_cast<const float *>(qgrad) + (size_t)sn * kGradSlot;
+            d0 = make_float4(p[0], p[1], p[2], p[3]);
+            d1 = make_float4(p[4], p[5], p[6], p[7]);
+            d2 = make_float4(p[8], 0.0f, 0.0f, 0.0f);
         }
         if (sn + 64u < w1) tn = qstamp[sn + 64u];
         __builtin_amdgcn_wave_barrier();

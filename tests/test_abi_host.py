@@ -123,11 +123,11 @@ def test_workspace_sizes():
     assert B.gs_compact_workspace_bytes(10**6) >= 4 * (10**6 // 256)
     assert B.gs_loss_workspace_bytes(100) >= 8
     # raster-ready lists: per entry 2 quadrant entries (Gaussian and slot, 8 B; tile-list
-    # index, 4 B), gradient slots (48 B) and slot stamps (4 B); 4 quadrant bits and 4 prefix
+    # index, 4 B), gradient slots (36 B) and slot stamps (4 B); 4 quadrant bits and 4 prefix
     # counts per 64 entries; the first gradient slot and the raster record (64-B stride) per
     # Gaussian (+ the total); the raster order of the 4 quadrant waves per tile
     r0 = B.gs_bins_raster_bytes(5000, 64 * 1000, 1920, 1080)
-    lo = 2 * (8 + 4 + 48 + 4) * 64000 + 4 * 8 * 1000 + 4 * 4 * 1001 + 4 * 5001 + 64 * 5000 + 4 * 4 * 8160
+    lo = 2 * (8 + 4 + 36 + 4) * 64000 + 4 * 8 * 1000 + 4 * 4 * 1001 + 4 * 5001 + 64 * 5000 + 4 * 4 * 8160
     assert lo <= r0 <= lo + 8 * 256
     assert B.gs_bins_raster_bytes(0, 0, 16, 16) > 0 and B.gs_bins_raster_bytes(0, -1, 16, 16) == 0
 
